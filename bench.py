@@ -1,0 +1,278 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X SSD layer (chunked forward + recurrent decode).
+
+One step = one full forward (all four stages) of the Mamba-2 130M-shaped SSD
+layer -- batch 4, seqlen 2048, 24 heads, headdim 64, state 128, 1 group,
+chunk 256, bf16 X/B/C with fp32 a -- over one batch of seeded synthetic
+inputs already resident in HBM.  Several distinct input batches are cycled so
+that the working set of the timed loop (> 256 MB) does not sit in the 256 MB
+Infinity Cache.
+
+Prints ONE JSON line.  Besides the contract fields it carries:
+  roofline      the dominant kernel (the MFMA full pass) against the HBM peak,
+                from algorithmic bytes and that kernel's own launch duration,
+                measured with HIP events on the launch stream;
+  mfma          algorithmic MFMA flops of the step against the bf16 dense peak;
+  cpu_baseline  the fp64 CPU oracle on the same workload (host cores);
+  secondary     the other workloads of the metric: the 2.7B-shaped layer,
+                the state-64 sweep at seqlen 32K, and the decode step's
+                HBM bandwidth.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+
+
+def fwd_algo_bytes_per_token(sh):
+    """Minimum HBM bytes per token: X in, Y out, B and C, a (fp32)."""
+    es = 2 if sh.dtype == "bf16" else 4
+    return sh.nheads * sh.headdim * 2 * es + 2 * sh.ngroups * sh.dstate * es + 4 * sh.nheads
+
+
+def fwd_algo_flops_per_token(sh):
+    """Algorithmic MFMA flops per token: causal half of C B^T once per group,
+    causal half of (L o S) X per head, chunk state and state-to-output per head."""
+    Q, N, P, H, G = sh.chunk, sh.dstate, sh.headdim, sh.nheads, sh.ngroups
+    return (Q + 1) * (N * G + P * H) + 4 * N * P * H
+
+
+def stored_traffic():
+    """HBM bytes per launch of the full-pass kernel from the committed
+    rocprofv3 FETCH_SIZE/WRITE_SIZE summary (calibrated on a plain copy), or
+    None when that summary was taken on a different kernel source."""
+    import hashlib
+    src = os.path.join(ROOT, "ssd_chunked_scan_chunk_amd", "csrc", "kernels_mfma.hip")
+    prof = os.path.join(ROOT, "profiles", "k_mfma_seg_full_m2_130m_hbm_traffic.md")
+    try:
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        fields = dict(l.split(":", 1) for l in open(prof) if l.startswith(("traffic_bytes", "kernel_source")))
+    except OSError:
+        return None
+    if fields.get("kernel_source_sha256_16", "").strip() != sha:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
+def upload(d):
+    import torch
+    dt = d["shape"].dtype
+    out = {}
+    for k in ("X", "B", "C"):
+        arr = d[k]
+        t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.uint16)).view(torch.bfloat16) \
+            if dt == "bf16" else torch.from_numpy(arr)
+        out[k] = t.to("cuda")
+    out["a"] = torch.from_numpy(d["a"]).to("cuda")
+    return out
+
+
+def time_events(fn, steps):
+    import torch
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(steps):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / 1e3  # seconds
+
+
+def bench_forward(sh, steps, warmup, nbatch, seed0=0):
+    """Time `steps` forwards cycling over `nbatch` seeded batches.
+    Returns (seconds per step, seconds per launch of the full-pass kernel, plan)."""
+    import torch
+    import ssd_chunked_scan_chunk_amd as ssd
+    import ssd_inputs as si
+    batches = [upload(si.make_fwd(sh, seed=seed0 + i)) for i in range(nbatch)]
+    Ys = [torch.empty_like(b["X"]) for b in batches]
+    fin = torch.empty((sh.batch, sh.nheads, sh.headdim, sh.dstate), dtype=torch.float32, device="cuda")
+    X0 = batches[0]["X"]
+    plan = ssd.fwd_plan(X0, batches[0]["B"], sh.chunk)
+    nws = ssd.workspace_bytes(X0, batches[0]["B"], sh.chunk)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        g = batches[i % nbatch]
+        ssd.chunk_scan_fwd(g["X"], g["a"], g["B"], g["C"], sh.chunk, Y=Ys[i % nbatch],
+                           final_state=fin if sh.final_state else None, workspace=ws)
+
+    for i in range(warmup):
+        step(i)
+    t_step = time_events(step, steps) / steps
+
+    # the dominant kernel alone, in the launch configuration the step uses
+    algo, seg_chunks, nseg = plan
+    if nseg == 1:
+        t_kernel = t_step               # the step is that single launch
+    elif seg_chunks == 1:
+        # full pass with one chunk per workgroup, fed the entering states
+        states = []
+        for g in batches:
+            dS = ssd.chunk_state(g["X"], g["a"], g["B"], sh.chunk)
+            _, lam = ssd.chunk_cumsum(g["a"], sh.chunk)
+            Sin, _ = ssd.state_passing(dS, lam, sh.chunk, sh.seqlen, return_final_state=False)
+            states.append(Sin)
+
+        def kern(i):
+            g = batches[i % nbatch]
+            ssd.chunk_scan(g["X"], g["a"], g["B"], g["C"], sh.chunk, states_in=states[i % nbatch])
+
+        for i in range(warmup):
+            kern(i)
+        t_kernel = time_events(kern, steps) / steps
+        del states
+    else:
+        t_kernel = None
+    del batches, Ys
+    torch.cuda.empty_cache()
+    return t_step, t_kernel, plan
+
+
+def bench_decode(steps, warmup):
+    import torch
+    import ssd_chunked_scan_chunk_amd as ssd
+    import ssd_inputs as si
+    sh = si.DECODE_CONFIG
+    T = 16  # distinct per-step inputs, cycled (same bytes per step as fresh ones)
+    d = si.make_decode(sh, seed=0, steps=T)
+    state = torch.from_numpy(d["state"]).cuda()
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16)).view(torch.bfloat16).cuda()
+    x, B, C = bf(d["x"]), bf(d["B"]), bf(d["C"])
+    a = torch.from_numpy(d["a"]).cuda()
+    y = torch.empty_like(x[0])
+
+    def step(i):
+        t = i % T
+        ssd.step(state, x[t], a[t], B[t], C[t], y=y)
+
+    for i in range(warmup):
+        step(i)
+    t = time_events(step, steps) / steps
+    Bz, H, P, N, G = sh.batch, sh.nheads, sh.headdim, sh.dstate, sh.ngroups
+    nbytes = 2 * Bz * H * P * N * 4 + 2 * Bz * H * P * 2 + 2 * Bz * G * N * 2 + Bz * H * 4
+    del state, x, B, C, a, y
+    torch.cuda.empty_cache()
+    return t, nbytes
+
+
+def cpu_baseline(sh):
+    """The fp64 oracle (never tuned) on the same workload, on the host cores."""
+    import oracle
+    import ssd_inputs as si
+    d = si.make_fwd(sh, seed=0)
+    w = {k: si.widen(d[k], sh.dtype) for k in ("X", "B", "C")}
+    a = d["a"].astype(np.float64)
+    threads = os.cpu_count() or 1
+    reps, t0 = 0, time.perf_counter()
+    while True:   # repeat the batch until ~10 CPU-seconds of work are timed
+        oracle.fwd(w["X"], a, w["B"], w["C"], nthreads=threads)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt * threads >= 10.0 or dt >= 30.0:
+            break
+    tokens = sh.batch * sh.seqlen * reps
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "the full %dx%d-token batch (%d heads), %d times, through the sequential "
+                      "fp64 recurrence with (batch, head) slices spread over %d threads; %.2f s wall"
+                      % (sh.batch, sh.seqlen, sh.nheads, reps, threads, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device copy of 512 MiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: there is no multi-GPU path (the layer would "
+              "shard over (batch, head) with no exchange); run it with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.calibrate_copy:
+        # a plain copy of known size: FETCH_SIZE / WRITE_SIZE per dispatch of
+        # this kernel, divided by 512 MiB, calibrates the HBM byte counters
+        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy_bytes": 512 << 20, "copies": 5}))
+        return
+    import ssd_inputs as si
+    import ssd_chunked_scan_chunk_amd as ssd  # noqa: F401  (fails loudly if libssd.so is missing)
+
+    sh = si.FWD_CONFIGS["m2_130m"]
+    tokens = sh.batch * sh.seqlen
+    per_batch = tokens * fwd_algo_bytes_per_token(sh)
+    nbatch = max(2, int(np.ceil(2 * 256e6 / per_batch)))   # > 2x the Infinity Cache
+    t_step, t_kernel, plan = bench_forward(sh, args.steps, args.warmup, nbatch)
+
+    algo_bytes = tokens * fwd_algo_bytes_per_token(sh)
+    algo_flops = tokens * fwd_algo_flops_per_token(sh)
+    achieved = algo_bytes / t_kernel / 1e9 if t_kernel else None
+    out = {
+        "metric": "SSD fwd tokens/s + MFMA% of bf16 peak at N=64/128; decode GB/s % of HBM peak",
+        "value": tokens / t_step,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": t_step * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) X/B/C, a = dt*A with Mamba-2 dt recipe; %d batches cycled)" % nbatch,
+        "config": {"workload": "m2_130m SSD layer fwd: batch 4, seqlen 2048, 24 heads, headdim 64, "
+                               "dstate 128, 1 group, chunk 256",
+                   "plan": {"algo": plan[0], "seg_chunks": plan[1], "nseg": plan[2]}},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": (achieved / HBM_PEAK_GBS) if achieved else None, "traffic": stored_traffic(),
+                     "kernel": "k_mfma_seg full pass", "kernel_ms": t_kernel * 1e3 if t_kernel else None,
+                     "algo_bytes_per_launch": algo_bytes},
+        "mfma": {"achieved": algo_flops / t_step / 1e12, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                 "frac": algo_flops / t_step / 1e12 / BF16_PEAK_TFLOPS,
+                 "algo_flops_per_step": algo_flops},
+    }
+
+    if not args.no_secondary:
+        sec = {}
+        for name, shp in (("m2_2p7b", si.FWD_CONFIGS["m2_2p7b"]), ("sweep_n64_L32768", si.sweep_shape(32768))):
+            tok = shp.batch * shp.seqlen
+            nb = max(1, int(np.ceil(2 * 256e6 / (tok * fwd_algo_bytes_per_token(shp)))))
+            ts, tk, pl = bench_forward(shp, max(5, args.steps // 5), 2, nb)
+            fl = tok * fwd_algo_flops_per_token(shp)
+            sec[name] = {"tokens_per_s": tok / ts, "ms_per_step": ts * 1e3,
+                         "hbm_frac": tok * fwd_algo_bytes_per_token(shp) / ts / 1e9 / HBM_PEAK_GBS,
+                         "mfma_frac": fl / ts / 1e12 / BF16_PEAK_TFLOPS, "plan": list(pl)}
+        td, nbytes = bench_decode(max(20, args.steps), 5)
+        sec["decode_step"] = {"workload": "batch 256, 80 heads, headdim 64, dstate 128, fp32 state in place",
+                              "us_per_step": td * 1e6, "GB_per_s": nbytes / td / 1e9,
+                              "hbm_frac": nbytes / td / 1e9 / HBM_PEAK_GBS, "tokens_per_s": 256 / td}
+        out["secondary"] = sec
+
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(sh)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,162 @@
+/*
+ * ssd.h -- C ABI of the MI355X (gfx950) SSD layer library (libssd.so).
+ *
+ * The layer evaluates, for every batch b and head h, the selective state
+ * space model with a scalar decay per step -- a 1-semiseparable SSM, which
+ * the CiteArk page of "Transformers are SSMs" (section "AI research summary")
+ * says is computed by a block-decomposed matrix-multiplication algorithm,
+ * and which the same page (section "what this means") identifies with
+ * structured masked attention and constant-memory inference:
+ *
+ *     S_t = exp(a_t) * S_{t-1} + X_t (x) B_t        (S is P x N, S_{-1} = S0)
+ *     Y_t = S_t C_t                                  (Y_t[p] = sum_n S_t[p][n] C_t[n])
+ *
+ * i.e. Y = (Lmask o (C B^T)) X with Lmask[t][s] = exp(a_{s+1} + ... + a_t)
+ * for t >= s and 0 above the diagonal (the semiseparable matrix of the wiki
+ * review's "Core concepts").  Head h reads B/C group g = h * ngroups / nheads.
+ *
+ * Data layout (dense, row-major, last index fastest):
+ *   X, Y           [batch][seqlen][nheads][headdim]     dtype of the call
+ *   a              [batch][seqlen][nheads]              float32
+ *   B, C           [batch][seqlen][ngroups][dstate]     dtype of the call
+ *   states         [batch][nheads][headdim][dstate]     float32
+ *   per-chunk data [batch][nchunks][nheads][headdim][dstate] float32
+ * nchunks = ceil(seqlen / chunk); the last chunk may be shorter.
+ *
+ * Ownership: the caller allocates every buffer (device memory) and the
+ * workspace; the library never allocates, keeps no state between calls and
+ * never synchronises.  Every call validates all arguments on the host before
+ * touching the GPU; on any error nothing is enqueued and no output is
+ * written.  Work is enqueued on `stream` (a hipStream_t passed as void*;
+ * NULL = the null stream) and is complete only once that stream has been
+ * synchronised.  Asynchronous device faults surface at that synchronisation,
+ * not as a return code.  Values are not inspected: NaN/Inf propagate within
+ * their (batch, head) slice and a_t > 0 is computed as written.
+ * Calls are thread-safe; ssd_last_error() is per calling thread.
+ */
+#ifndef SSD_H
+#define SSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ssd_status {
+    SSD_OK = 0,
+    SSD_ERR_NULL = 1,        /* a required pointer is NULL                   */
+    SSD_ERR_SHAPE = 2,       /* negative size, nheads % ngroups != 0, chunk<1 */
+    SSD_ERR_DTYPE = 3,       /* dtype is not one of ssd_dtype                 */
+    SSD_ERR_ALIGN = 4,       /* a buffer is not 16-byte aligned               */
+    SSD_ERR_UNSUPPORTED = 5, /* valid shape outside the compiled kernels      */
+    SSD_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required       */
+    SSD_ERR_HIP = 7,         /* a HIP launch failed (see ssd_last_error)      */
+    SSD_ERR_ALIAS = 8        /* an output overlaps an input it must not       */
+} ssd_status;
+
+typedef enum ssd_dtype {
+    SSD_F32 = 0,  /* float32 X, B, C, Y                                       */
+    SSD_BF16 = 1  /* bfloat16 X, B, C, Y; accumulation is always float32;     */
+                  /* Y is rounded to nearest even                             */
+} ssd_dtype;
+
+typedef enum ssd_algo {
+    SSD_ALGO_AUTO = 0,    /* MFMA path when compiled for the shape, else VALU  */
+    SSD_ALGO_VALU = 1,    /* per-(b,h) sequential VALU kernel, fp32 math, any  */
+                          /* dtype; exact segment sums (the fp32 path)         */
+    SSD_ALGO_MFMA = 2     /* bf16 MFMA segmented kernels only                  */
+} ssd_algo;
+
+/* Forward problem.  chunk is the block size Q of the decomposition: the
+ * diagonal Q x Q blocks are evaluated in the quadratic (masked attention)
+ * form and everything across blocks through the carried state.  The result
+ * does not depend on chunk beyond rounding.  seg_chunks (MFMA path) is the
+ * number of consecutive chunks one workgroup walks while carrying the state
+ * in registers; 0 lets the library choose from the shape. */
+typedef struct ssd_fwd_desc {
+    int64_t batch, seqlen, nheads, headdim, dstate, ngroups, chunk;
+    int32_t dtype;      /* ssd_dtype */
+    int32_t algo;       /* ssd_algo  */
+    int64_t seg_chunks; /* 0 = automatic */
+} ssd_fwd_desc;
+
+typedef struct ssd_step_desc {
+    int64_t batch, nheads, headdim, dstate, ngroups;
+    int32_t dtype;      /* ssd_dtype of x, B, C, y */
+    int32_t reserved;   /* must be 0 */
+} ssd_step_desc;
+
+/* Bytes of device workspace ssd_chunk_scan_fwd needs for *desc (0 is
+ * possible).  Errors as for ssd_chunk_scan_fwd's validation. */
+ssd_status ssd_fwd_workspace_bytes(const ssd_fwd_desc* desc, size_t* bytes);
+
+/* The chunk/segment plan the library uses for *desc: *algo receives the
+ * ssd_algo that runs, *seg_chunks the chunks per segment (MFMA path) and
+ * *nseg the number of segments.  Host only. */
+ssd_status ssd_fwd_plan(const ssd_fwd_desc* desc, int32_t* algo, int64_t* seg_chunks,
+                        int64_t* nseg);
+
+/* Full forward: the four stages (segment sums, intra-chunk masked product,
+ * chunk states with the inter-chunk state scan, state-to-output) over the
+ * whole sequence.  Reads X, a, B, C and the optional initial_state (NULL =
+ * zero state); writes Y and, if final_state != NULL, the state after the
+ * last step.  Y and final_state must not overlap any input.
+ * workspace: device buffer of at least ssd_fwd_workspace_bytes() bytes
+ * (may be NULL when that is 0); its contents on entry are ignored. */
+ssd_status ssd_chunk_scan_fwd(const ssd_fwd_desc* desc, const void* X, const float* a,
+                              const void* B, const void* C, const float* initial_state,
+                              void* Y, float* final_state, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* Single-token recurrent decode step for every (b, h) (constant-memory
+ * inference): state <- exp(a) * state + x (x) B, then y = state C.
+ * state [batch][nheads][headdim][dstate] float32 is updated in place;
+ * x, y [batch][nheads][headdim] and B, C [batch][ngroups][dstate] in the
+ * call's dtype; a [batch][nheads] float32.  y must not overlap state or the
+ * inputs. */
+ssd_status ssd_step(const ssd_step_desc* desc, float* state, const void* x, const float* a,
+                    const void* B, const void* C, void* y, void* stream);
+
+/* ---- Stage entry points (the same kernels' building blocks, exposed so
+ * each stage can be checked on its own).  bf16 MFMA path only, except
+ * ssd_chunk_cumsum which takes any dtype descriptor. ---- */
+
+/* Stage 1, segment sums: cs[b][h][c][i] = a_{cQ} + ... + a_{cQ+i} (fp32
+ * wavefront prefix sums; entries past a ragged end are 0) and
+ * lam[b][h][c] = the chunk's total. */
+ssd_status ssd_chunk_cumsum(const ssd_fwd_desc* desc, const float* a, float* cs, float* lam,
+                            void* stream);
+
+/* Stage 3, chunk states: dstates[b][c][h][p][n] =
+ * sum_j exp(a_{j+1} + ... + a_{end of chunk}) X_j[p] B_j[n] over the chunk. */
+ssd_status ssd_chunk_state(const ssd_fwd_desc* desc, const void* X, const float* a,
+                           const void* B, float* dstates, void* stream);
+
+/* Stage 4, inter-chunk state scan: states_in[b][0][h] = initial_state (or 0),
+ * states_in[b][c+1][h] = exp(lam[b][h][c]) states_in[b][c][h] + dstates[b][c][h];
+ * final_state (optional) receives the state after the last chunk.
+ * states_in may alias dstates exactly (in-place scan). */
+ssd_status ssd_state_passing(const ssd_fwd_desc* desc, const float* dstates, const float* lam,
+                             const float* initial_state, float* states_in, float* final_state,
+                             void* stream);
+
+/* Stages 2 and 5, chunk output: Y = intra-chunk masked product + exp(cs) *
+ * (C states_in^T) per chunk, written once.  states_in NULL means zero states
+ * (Y is then the intra-chunk part alone). */
+ssd_status ssd_chunk_scan(const ssd_fwd_desc* desc, const void* X, const float* a,
+                          const void* B, const void* C, const float* states_in, void* Y,
+                          void* stream);
+
+/* Static description of a status code. */
+const char* ssd_status_str(ssd_status s);
+/* Detail of the calling thread's most recent error ("" if none). */
+const char* ssd_last_error(void);
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t ssd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SSD_H */

@@ -1,0 +1,161 @@
+"""MI355X (gfx950) SSD layer: chunked forward and recurrent decode step.
+
+A thin torch binding over libssd.so's C ABI (include/ssd.h).  This module
+only marshals arguments -- checks devices/dtypes/contiguity, allocates
+outputs and workspace with torch, and passes raw device pointers plus the
+current HIP stream.  Every step of the computation runs in the library's HIP
+kernels; there is no fallback of any kind, and every function raises if the
+library is not built.
+
+Layouts (contiguous): X, Y [batch, seqlen, nheads, headdim]; a [batch, seqlen,
+nheads] float32; B, C [batch, seqlen, ngroups, dstate]; states [batch, nheads,
+headdim, dstate] float32.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import (SSD_ALGO_AUTO, SSD_ALGO_MFMA, SSD_ALGO_VALU, SSD_BF16, SSD_F32,
+                   SSDError)
+
+__all__ = ["chunk_scan_fwd", "step", "chunk_cumsum", "chunk_state", "state_passing",
+           "chunk_scan", "fwd_plan", "workspace_bytes", "SSDError", "SSD_ALGO_AUTO",
+           "SSD_ALGO_MFMA", "SSD_ALGO_VALU", "library_path"]
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def _L():
+    return _lib.load()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SSD_BF16
+    if t.dtype == torch.float32:
+        return SSD_F32
+    raise TypeError("X/B/C must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _desc(X, B, chunk, algo, seg_chunks):
+    Bz, L, H, P = X.shape
+    G, N = B.shape[2], B.shape[3]
+    return _lib.fwd_desc(Bz, L, H, P, N, G, int(chunk), _dtype_code(X), int(algo), int(seg_chunks))
+
+
+def fwd_plan(X, B, chunk, algo=SSD_ALGO_AUTO, seg_chunks=0):
+    """(algo, seg_chunks, nseg) the library would use for these shapes."""
+    d = _desc(X, B, chunk, algo, seg_chunks)
+    a = ctypes.c_int32()
+    k = ctypes.c_int64()
+    n = ctypes.c_int64()
+    _lib.check(_L().ssd_fwd_plan(ctypes.byref(d), ctypes.byref(a), ctypes.byref(k), ctypes.byref(n)))
+    return a.value, k.value, n.value
+
+
+def workspace_bytes(X, B, chunk, algo=SSD_ALGO_AUTO, seg_chunks=0) -> int:
+    d = _desc(X, B, chunk, algo, seg_chunks)
+    n = ctypes.c_size_t()
+    _lib.check(_L().ssd_fwd_workspace_bytes(ctypes.byref(d), ctypes.byref(n)))
+    return n.value
+
+
+def chunk_scan_fwd(X, a, B, C, chunk, initial_state=None, return_final_state=False,
+                   algo=SSD_ALGO_AUTO, seg_chunks=0, Y=None, final_state=None, workspace=None):
+    """Full SSD forward.  Returns (Y, final_state or None)."""
+    d = _desc(X, B, chunk, algo, seg_chunks)
+    dev = X.device
+    if Y is None:
+        Y = torch.empty_like(X)
+    if final_state is None and return_final_state:
+        final_state = torch.empty((X.shape[0], X.shape[2], X.shape[3], B.shape[3]),
+                                  dtype=torch.float32, device=dev)
+    nws = ctypes.c_size_t()
+    _lib.check(_L().ssd_fwd_workspace_bytes(ctypes.byref(d), ctypes.byref(nws)))
+    if workspace is None and nws.value > 0:
+        workspace = torch.empty(nws.value, dtype=torch.uint8, device=dev)
+    wsz = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _lib.check(_L().ssd_chunk_scan_fwd(
+        ctypes.byref(d), _ptr(X), _ptr(a), _ptr(B), _ptr(C), _ptr(initial_state), _ptr(Y),
+        _ptr(final_state), _ptr(workspace), wsz, _stream(dev)))
+    return Y, final_state
+
+
+def step(state, x, a, B, C, y=None):
+    """One recurrent decode step; ``state`` is updated in place.  Returns y.
+
+    state [Bz,H,P,N] f32, x [Bz,H,P], a [Bz,H] f32, B/C [Bz,G,N]."""
+    Bz, H, P, N = state.shape
+    G = B.shape[1]
+    if y is None:
+        y = torch.empty_like(x)
+    d = _lib.StepDesc(Bz, H, P, N, G, _dtype_code(x), 0)
+    _lib.check(_L().ssd_step(ctypes.byref(d), _ptr(state), _ptr(x), _ptr(a), _ptr(B), _ptr(C),
+                             _ptr(y), _stream(state.device)))
+    return y
+
+
+# ---- stage entry points ------------------------------------------------------
+def chunk_cumsum(a, chunk):
+    """Stage 1: (cs [Bz,H,nc,Q], lam [Bz,H,nc]) from a [Bz,L,H]."""
+    Bz, L, H = a.shape
+    Q = int(chunk)
+    nc = (L + Q - 1) // Q
+    d = _lib.fwd_desc(Bz, L, H, 4, 4, 1, Q, SSD_F32)
+    cs = torch.empty((Bz, H, nc, Q), dtype=torch.float32, device=a.device)
+    lam = torch.empty((Bz, H, nc), dtype=torch.float32, device=a.device)
+    _lib.check(_L().ssd_chunk_cumsum(ctypes.byref(d), _ptr(a), _ptr(cs), _ptr(lam), _stream(a.device)))
+    return cs, lam
+
+
+def chunk_state(X, a, B, chunk):
+    """Stage 3: per-chunk states dS [Bz,nc,H,P,N] f32."""
+    Bz, L, H, P = X.shape
+    N = B.shape[3]
+    nc = (L + int(chunk) - 1) // int(chunk)
+    d = _desc(X, B, chunk, SSD_ALGO_MFMA, 1)
+    out = torch.empty((Bz, nc, H, P, N), dtype=torch.float32, device=X.device)
+    _lib.check(_L().ssd_chunk_state(ctypes.byref(d), _ptr(X), _ptr(a), _ptr(B), _ptr(out),
+                                    _stream(X.device)))
+    return out
+
+
+def state_passing(dstates, lam, chunk, seqlen, initial_state=None, return_final_state=True,
+                  out=None):
+    """Stage 4: states entering each chunk [Bz,nc,H,P,N] (+ final state)."""
+    Bz, nc, H, P, N = dstates.shape
+    d = _lib.fwd_desc(Bz, seqlen, H, P, N, 1, int(chunk), SSD_F32)
+    if out is None:
+        out = torch.empty_like(dstates)
+    fin = torch.empty((Bz, H, P, N), dtype=torch.float32, device=dstates.device) if return_final_state else None
+    _lib.check(_L().ssd_state_passing(ctypes.byref(d), _ptr(dstates), _ptr(lam), _ptr(initial_state),
+                                      _ptr(out), _ptr(fin), _stream(dstates.device)))
+    return out, fin
+
+
+def chunk_scan(X, a, B, C, chunk, states_in=None):
+    """Stages 2 + 5: Y from the chunk inputs and the entering states (None = zero)."""
+    d = _desc(X, B, chunk, SSD_ALGO_MFMA, 1)
+    Y = torch.empty_like(X)
+    _lib.check(_L().ssd_chunk_scan(ctypes.byref(d), _ptr(X), _ptr(a), _ptr(B), _ptr(C),
+                                   _ptr(states_in), _ptr(Y), _stream(X.device)))
+    return Y

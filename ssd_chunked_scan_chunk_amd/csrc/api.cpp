@@ -1,0 +1,458 @@
+// api.cpp -- the C ABI of libssd.so (declared in include/ssd.h).
+//
+// Every entry point validates all of its arguments on the host before the
+// first HIP call; a rejected call enqueues nothing and writes no output.
+// Accepted calls only enqueue work on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "ssd.h"
+#include "ssd_launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+ssd_status fail(ssd_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+ssd_status ok() {
+    g_err[0] = '\0';
+    return SSD_OK;
+}
+
+ssd_status hip_fail(hipError_t e, const char* what) {
+    return fail(SSD_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+struct Range {
+    const char* name;
+    uintptr_t lo, hi;  // [lo, hi)
+};
+Range rng(const char* name, const void* p, int64_t bytes) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{name, lo, p ? lo + (uintptr_t)(bytes > 0 ? bytes : 0) : lo};
+}
+bool overlap(const Range& a, const Range& b) {
+    if (a.lo == a.hi || b.lo == b.hi) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+constexpr int64_t kNumCU = 256;          // MI355X compute units
+constexpr int64_t kLdsPerCU = 160 * 1024;
+
+// LDS of the MFMA kernel's full pass for (Q, P, N): used to estimate how many
+// workgroups share a CU when planning segments.
+int64_t mfma_lds_bytes(int64_t Q, int64_t P, int64_t N) {
+    return 2 * (Q * (N + 8) + 2 * P * (Q + 8) + P * (N + 8)) + 4 * Q + 32;
+}
+
+struct Plan {
+    int32_t algo;
+    int64_t seg_chunks, nseg;
+    size_t ws;
+    ssd::FwdShape s;
+    bool bf16;
+};
+
+ssd_status check_desc(const ssd_fwd_desc* d, bool need_chunk_le_256) {
+    if (!d) return fail(SSD_ERR_NULL, "desc is NULL");
+    if (d->batch < 0 || d->seqlen < 0 || d->nheads < 1 || d->headdim < 1 || d->dstate < 1 ||
+        d->ngroups < 1)
+        return fail(SSD_ERR_SHAPE,
+                    "sizes must be batch>=0, seqlen>=0, nheads,headdim,dstate,ngroups>=1 "
+                    "(got %lld,%lld,%lld,%lld,%lld,%lld)",
+                    (long long)d->batch, (long long)d->seqlen, (long long)d->nheads,
+                    (long long)d->headdim, (long long)d->dstate, (long long)d->ngroups);
+    if (d->nheads % d->ngroups != 0)
+        return fail(SSD_ERR_SHAPE, "nheads (%lld) must be a multiple of ngroups (%lld)",
+                    (long long)d->nheads, (long long)d->ngroups);
+    if (d->chunk < 1) return fail(SSD_ERR_SHAPE, "chunk must be >= 1 (got %lld)", (long long)d->chunk);
+    if (d->seg_chunks < 0) return fail(SSD_ERR_SHAPE, "seg_chunks must be >= 0");
+    if (d->dtype != SSD_F32 && d->dtype != SSD_BF16)
+        return fail(SSD_ERR_DTYPE, "dtype %d is not SSD_F32 or SSD_BF16", (int)d->dtype);
+    if (d->algo < SSD_ALGO_AUTO || d->algo > SSD_ALGO_MFMA)
+        return fail(SSD_ERR_UNSUPPORTED, "unknown algo %d", (int)d->algo);
+    if (need_chunk_le_256 && d->chunk > 256)
+        return fail(SSD_ERR_UNSUPPORTED, "chunk %lld > 256", (long long)d->chunk);
+    // grid limits (dims are launched as unsigned grid sizes) and 32-bit in-slice indexing
+    if (d->nheads > 65535 || d->batch > 65535 || d->headdim * d->dstate > (1 << 24) ||
+        d->seqlen > ((int64_t)1 << 40))
+        return fail(SSD_ERR_UNSUPPORTED, "sizes beyond the supported range");
+    if ((d->headdim * d->dstate) % 4 != 0)
+        return fail(SSD_ERR_UNSUPPORTED, "headdim*dstate must be a multiple of 4");
+    return SSD_OK;
+}
+
+ssd::FwdShape shape_of(const ssd_fwd_desc* d) {
+    ssd::FwdShape s;
+    s.Bz = d->batch; s.L = d->seqlen; s.H = d->nheads; s.P = d->headdim; s.N = d->dstate;
+    s.G = d->ngroups; s.Q = d->chunk;
+    s.nc = (s.L + s.Q - 1) / s.Q;
+    return s;
+}
+
+// Segment plan of the MFMA path.  A workgroup walks k consecutive chunks;
+// nseg = ceil(nc / k) segments per (b, h).  Cost in "chunk passes per CU":
+// the full pass takes ceil(WG / slots) rounds of k chunks, and when nseg > 1
+// the state-only pass (about 0.4 of a full chunk) and the segment scan are
+// added.  For each segment count only the most balanced k is tried; the
+// cheapest wins, ties going to fewer segments (less traffic).
+int64_t auto_seg_chunks(const ssd::FwdShape& s) {
+    const int64_t per_cu = kLdsPerCU / mfma_lds_bytes(s.Q, s.P, s.N);
+    const int64_t slots = kNumCU * (per_cu > 0 ? per_cu : 1);
+    const int64_t bh = s.Bz * s.H;
+    const int64_t max_seg = s.nc < 65535 ? s.nc : 65535;
+    double best = 1e300;
+    int64_t best_k = s.nc;
+    int64_t prev_k = -1;
+    for (int64_t want = 1; want <= max_seg; ++want) {
+        const int64_t k = (s.nc + want - 1) / want;   // longest segment
+        if (k == prev_k) continue;
+        prev_k = k;
+        const int64_t nseg = (s.nc + k - 1) / k;
+        const double rounds_c = (double)((bh * nseg + slots - 1) / slots);
+        double cost = rounds_c * (double)k;
+        if (nseg > 1) {
+            const double rounds_a = (double)((bh * (nseg - 1) + slots - 1) / slots);
+            cost += rounds_a * (double)k * 0.4 + 1.5;
+        }
+        if (cost < best - 1e-9) {
+            best = cost;
+            best_k = k;
+        }
+    }
+    return best_k;
+}
+
+ssd_status make_plan(const ssd_fwd_desc* d, Plan* p) {
+    ssd_status st = check_desc(d, false);
+    if (st != SSD_OK) return st;
+    p->s = shape_of(d);
+    p->bf16 = d->dtype == SSD_BF16;
+    const ssd::FwdShape& s = p->s;
+    const bool mfma_ok = p->bf16 && ssd::mfma_supported(s.Q, s.P, s.N) && s.Q <= 256;
+    const bool valu_ok = ssd::valu_fwd_supported(s);
+    if (d->algo == SSD_ALGO_MFMA) {
+        if (!mfma_ok)
+            return fail(SSD_ERR_UNSUPPORTED,
+                        "no MFMA kernel for dtype=%d chunk=%lld headdim=%lld dstate=%lld "
+                        "(bf16, chunk in {64,128,256}, headdim in {32,64}, dstate in {64,128})",
+                        (int)d->dtype, (long long)s.Q, (long long)s.P, (long long)s.N);
+        p->algo = SSD_ALGO_MFMA;
+    } else if (d->algo == SSD_ALGO_VALU) {
+        if (!valu_ok)
+            return fail(SSD_ERR_UNSUPPORTED, "VALU kernel needs chunk<=256 and headdim*dstate<=16384");
+        p->algo = SSD_ALGO_VALU;
+    } else {
+        if (mfma_ok) p->algo = SSD_ALGO_MFMA;
+        else if (valu_ok) p->algo = SSD_ALGO_VALU;
+        else
+            return fail(SSD_ERR_UNSUPPORTED, "no kernel for chunk=%lld headdim=%lld dstate=%lld",
+                        (long long)s.Q, (long long)s.P, (long long)s.N);
+    }
+    p->seg_chunks = 0;
+    p->nseg = 1;
+    p->ws = 0;
+    if (p->algo == SSD_ALGO_MFMA && s.nc > 0 && s.Bz > 0) {
+        int64_t k = d->seg_chunks > 0 ? d->seg_chunks : auto_seg_chunks(s);
+        if (k > s.nc) k = s.nc;
+        p->seg_chunks = k;
+        p->nseg = (s.nc + k - 1) / k;
+        if (p->nseg > 65535) return fail(SSD_ERR_UNSUPPORTED, "too many segments (%lld)", (long long)p->nseg);
+        if (p->nseg > 1) {
+            const size_t states = (size_t)s.Bz * p->nseg * s.H * s.P * s.N * sizeof(float);
+            const size_t lams = (size_t)s.Bz * s.H * p->nseg * sizeof(float);
+            p->ws = ((states + 255) / 256) * 256 + ((lams + 255) / 256) * 256;
+        }
+    }
+    return SSD_OK;
+}
+
+ssd_status check_fwd_io(const Plan& p, const void* X, const float* a, const void* B,
+                        const void* C, const float* S0, const void* Y, const float* Sfin) {
+    const ssd::FwdShape& s = p.s;
+    if (s.Bz > 0 && s.L > 0 && (!X || !a || !B || !C || !Y))
+        return fail(SSD_ERR_NULL, "X, a, B, C and Y are required");
+    const void* v[] = {X, B, C, Y, S0, Sfin};
+    const char* nm[] = {"X", "B", "C", "Y", "initial_state", "final_state"};
+    for (int i = 0; i < 6; ++i)
+        if (v[i] && !aligned(v[i], 16)) return fail(SSD_ERR_ALIGN, "%s is not 16-byte aligned", nm[i]);
+    if (a && !aligned(a, 4)) return fail(SSD_ERR_ALIGN, "a is not 4-byte aligned");
+    const int64_t es = p.bf16 ? 2 : 4;
+    const int64_t nX = s.Bz * s.L * s.H * s.P, nBC = s.Bz * s.L * s.G * s.N;
+    const int64_t nS = s.Bz * s.H * s.P * s.N;
+    const Range in[] = {rng("X", X, nX * es), rng("a", a, s.Bz * s.L * s.H * 4), rng("B", B, nBC * es),
+                        rng("C", C, nBC * es), rng("initial_state", S0, S0 ? nS * 4 : 0)};
+    const Range outs[] = {rng("Y", Y, nX * es), rng("final_state", Sfin, Sfin ? nS * 4 : 0)};
+    for (const Range& o : outs)
+        for (const Range& i : in)
+            if (overlap(o, i)) return fail(SSD_ERR_ALIAS, "%s overlaps input %s", o.name, i.name);
+    if (overlap(outs[0], outs[1])) return fail(SSD_ERR_ALIAS, "Y overlaps final_state");
+    return SSD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ssd_status_str(ssd_status s) {
+    switch (s) {
+    case SSD_OK: return "SSD_OK: success";
+    case SSD_ERR_NULL: return "SSD_ERR_NULL: a required pointer is NULL";
+    case SSD_ERR_SHAPE: return "SSD_ERR_SHAPE: invalid sizes";
+    case SSD_ERR_DTYPE: return "SSD_ERR_DTYPE: unknown dtype";
+    case SSD_ERR_ALIGN: return "SSD_ERR_ALIGN: misaligned buffer";
+    case SSD_ERR_UNSUPPORTED: return "SSD_ERR_UNSUPPORTED: no kernel compiled for this shape";
+    case SSD_ERR_WORKSPACE: return "SSD_ERR_WORKSPACE: workspace missing or too small";
+    case SSD_ERR_HIP: return "SSD_ERR_HIP: HIP runtime error";
+    case SSD_ERR_ALIAS: return "SSD_ERR_ALIAS: an output overlaps an input";
+    }
+    return "unknown ssd_status";
+}
+
+const char* ssd_last_error(void) { return g_err; }
+
+int32_t ssd_version(void) { return 100; }
+
+ssd_status ssd_fwd_workspace_bytes(const ssd_fwd_desc* desc, size_t* bytes) {
+    if (!bytes) return fail(SSD_ERR_NULL, "bytes is NULL");
+    Plan p;
+    ssd_status st = make_plan(desc, &p);
+    if (st != SSD_OK) return st;
+    *bytes = p.ws;
+    return ok();
+}
+
+ssd_status ssd_fwd_plan(const ssd_fwd_desc* desc, int32_t* algo, int64_t* seg_chunks, int64_t* nseg) {
+    Plan p;
+    ssd_status st = make_plan(desc, &p);
+    if (st != SSD_OK) return st;
+    if (algo) *algo = p.algo;
+    if (seg_chunks) *seg_chunks = p.seg_chunks;
+    if (nseg) *nseg = p.nseg;
+    return ok();
+}
+
+ssd_status ssd_chunk_scan_fwd(const ssd_fwd_desc* desc, const void* X, const float* a,
+                              const void* B, const void* C, const float* initial_state,
+                              void* Y, float* final_state, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    Plan p;
+    ssd_status st = make_plan(desc, &p);
+    if (st != SSD_OK) return st;
+    st = check_fwd_io(p, X, a, B, C, initial_state, Y, final_state);
+    if (st != SSD_OK) return st;
+    if (p.ws > 0) {
+        if (!workspace || workspace_bytes < p.ws)
+            return fail(SSD_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", p.ws,
+                        workspace_bytes, workspace ? "" : ", NULL");
+        if (!aligned(workspace, 16)) return fail(SSD_ERR_ALIGN, "workspace is not 16-byte aligned");
+        const int64_t es = p.bf16 ? 2 : 4;
+        const ssd::FwdShape& s = p.s;
+        const Range w = rng("workspace", workspace, (int64_t)p.ws);
+        const Range others[] = {
+            rng("X", X, s.Bz * s.L * s.H * s.P * es), rng("a", a, s.Bz * s.L * s.H * 4),
+            rng("B", B, s.Bz * s.L * s.G * s.N * es), rng("C", C, s.Bz * s.L * s.G * s.N * es),
+            rng("Y", Y, s.Bz * s.L * s.H * s.P * es),
+            rng("initial_state", initial_state, initial_state ? s.Bz * s.H * s.P * s.N * 4 : 0),
+            rng("final_state", final_state, final_state ? s.Bz * s.H * s.P * s.N * 4 : 0)};
+        for (const Range& o : others)
+            if (overlap(w, o)) return fail(SSD_ERR_ALIAS, "workspace overlaps %s", o.name);
+    }
+    const ssd::FwdShape& s = p.s;
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    const int64_t PN = s.P * s.N;
+    hipError_t e = hipSuccess;
+    if (s.Bz == 0) return ok();
+    if (s.L == 0) {
+        if (final_state) {
+            e = initial_state ? ssd::launch_copy_f32(final_state, initial_state, s.Bz * s.H * PN, hs)
+                              : ssd::launch_fill_zero(final_state, s.Bz * s.H * PN, hs);
+            if (e != hipSuccess) return hip_fail(e, "empty-sequence final state");
+        }
+        return ok();
+    }
+    if (p.algo == SSD_ALGO_VALU) {
+        e = ssd::launch_valu_fwd(s, p.bf16, X, a, B, C, initial_state, Y, final_state, hs);
+        if (e != hipSuccess) return hip_fail(e, "VALU forward launch");
+        return ok();
+    }
+    if (p.nseg == 1) {
+        ssd::StateSrc src{initial_state, s.H * PN, 0};
+        e = ssd::launch_mfma_out(s, p.seg_chunks, 1, X, a, B, C, src, Y, final_state, hs);
+        if (e != hipSuccess) return hip_fail(e, "MFMA forward launch");
+        return ok();
+    }
+    float* Sbuf = static_cast<float*>(workspace);
+    const size_t states = (size_t)s.Bz * p.nseg * s.H * PN * sizeof(float);
+    float* lamseg = reinterpret_cast<float*>(static_cast<char*>(workspace) + ((states + 255) / 256) * 256);
+    e = ssd::launch_mfma_state(s, p.seg_chunks, p.nseg - 1, p.nseg, X, a, B, Sbuf, lamseg, hs);
+    if (e != hipSuccess) return hip_fail(e, "MFMA segment-state launch");
+    e = ssd::launch_state_scan(s, p.nseg - 1, p.nseg, Sbuf, lamseg, s.H * p.nseg, p.nseg,
+                               initial_state, Sbuf, Sbuf + (p.nseg - 1) * s.H * PN,
+                               p.nseg * s.H * PN, hs);
+    if (e != hipSuccess) return hip_fail(e, "segment scan launch");
+    ssd::StateSrc src{Sbuf, p.nseg * s.H * PN, s.H * PN};
+    e = ssd::launch_mfma_out(s, p.seg_chunks, p.nseg, X, a, B, C, src, Y, final_state, hs);
+    if (e != hipSuccess) return hip_fail(e, "MFMA forward launch");
+    return ok();
+}
+
+ssd_status ssd_step(const ssd_step_desc* d, float* state, const void* x, const float* a,
+                    const void* B, const void* C, void* y, void* stream) {
+    if (!d) return fail(SSD_ERR_NULL, "desc is NULL");
+    if (d->batch < 0 || d->nheads < 1 || d->headdim < 1 || d->dstate < 1 || d->ngroups < 1)
+        return fail(SSD_ERR_SHAPE, "sizes must be batch>=0 and nheads,headdim,dstate,ngroups>=1");
+    if (d->nheads % d->ngroups != 0)
+        return fail(SSD_ERR_SHAPE, "nheads (%lld) must be a multiple of ngroups (%lld)",
+                    (long long)d->nheads, (long long)d->ngroups);
+    if (d->dtype != SSD_F32 && d->dtype != SSD_BF16)
+        return fail(SSD_ERR_DTYPE, "dtype %d is not SSD_F32 or SSD_BF16", (int)d->dtype);
+    if (d->reserved != 0) return fail(SSD_ERR_SHAPE, "reserved must be 0");
+    if (d->batch * d->nheads > ((int64_t)1 << 31) - 1 || d->headdim * d->dstate > (1 << 24))
+        return fail(SSD_ERR_UNSUPPORTED, "sizes beyond the supported range");
+    if (d->batch == 0) return ok();
+    if (!state || !x || !a || !B || !C || !y) return fail(SSD_ERR_NULL, "state, x, a, B, C and y are required");
+    const int64_t es = d->dtype == SSD_BF16 ? 2 : 4;
+    if (!aligned(state, 16) || !aligned(B, 8) || !aligned(C, 8))
+        return fail(SSD_ERR_ALIGN, "state must be 16-byte and B, C 8-byte aligned");
+    if (!aligned(x, es) || !aligned(y, es) || !aligned(a, 4))
+        return fail(SSD_ERR_ALIGN, "x, y, a must be element aligned");
+    const int64_t BH = d->batch * d->nheads;
+    const Range ins[] = {rng("state", state, BH * d->headdim * d->dstate * 4),
+                         rng("x", x, BH * d->headdim * es), rng("a", a, BH * 4),
+                         rng("B", B, d->batch * d->ngroups * d->dstate * es),
+                         rng("C", C, d->batch * d->ngroups * d->dstate * es)};
+    const Range yo = rng("y", y, BH * d->headdim * es);
+    for (const Range& i : ins)
+        if (overlap(yo, i)) return fail(SSD_ERR_ALIAS, "y overlaps %s", i.name);
+    for (int i = 1; i < 5; ++i)
+        if (overlap(ins[0], ins[i])) return fail(SSD_ERR_ALIAS, "state overlaps %s", ins[i].name);
+    hipError_t e = ssd::launch_step(d->batch, d->nheads, d->headdim, d->dstate, d->ngroups,
+                                    d->dtype == SSD_BF16, state, x, a, B, C, y,
+                                    reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "decode step launch");
+    return ok();
+}
+
+ssd_status ssd_chunk_cumsum(const ssd_fwd_desc* desc, const float* a, float* cs, float* lam,
+                            void* stream) {
+    ssd_status st = check_desc(desc, true);
+    if (st != SSD_OK) return st;
+    const ssd::FwdShape s = shape_of(desc);
+    if (s.Bz == 0 || s.L == 0) return ok();
+    if (!a || !cs || !lam) return fail(SSD_ERR_NULL, "a, cs and lam are required");
+    if (!aligned(a, 4) || !aligned(cs, 4) || !aligned(lam, 4)) return fail(SSD_ERR_ALIGN, "misaligned");
+    const Range ra = rng("a", a, s.Bz * s.L * s.H * 4);
+    const Range rc = rng("cs", cs, s.Bz * s.H * s.nc * s.Q * 4), rl = rng("lam", lam, s.Bz * s.H * s.nc * 4);
+    if (overlap(ra, rc) || overlap(ra, rl) || overlap(rc, rl)) return fail(SSD_ERR_ALIAS, "outputs overlap");
+    hipError_t e = ssd::launch_chunk_cumsum(s, a, cs, lam, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "cumsum launch");
+    return ok();
+}
+
+ssd_status ssd_chunk_state(const ssd_fwd_desc* desc, const void* X, const float* a, const void* B,
+                           float* dstates, void* stream) {
+    ssd_fwd_desc d1;
+    if (!desc) return fail(SSD_ERR_NULL, "desc is NULL");
+    d1 = *desc;
+    d1.algo = SSD_ALGO_MFMA;
+    d1.seg_chunks = 1;
+    Plan p;
+    ssd_status st = make_plan(&d1, &p);
+    if (st != SSD_OK) return st;
+    const ssd::FwdShape& s = p.s;
+    if (s.Bz == 0 || s.L == 0) return ok();
+    if (!X || !a || !B || !dstates) return fail(SSD_ERR_NULL, "X, a, B and dstates are required");
+    if (!aligned(X, 16) || !aligned(B, 16) || !aligned(dstates, 16) || !aligned(a, 4))
+        return fail(SSD_ERR_ALIGN, "misaligned buffer");
+    const Range out = rng("dstates", dstates, s.Bz * s.nc * s.H * s.P * s.N * 4);
+    const Range ins[] = {rng("X", X, s.Bz * s.L * s.H * s.P * 2), rng("a", a, s.Bz * s.L * s.H * 4),
+                         rng("B", B, s.Bz * s.L * s.G * s.N * 2)};
+    for (const Range& i : ins)
+        if (overlap(out, i)) return fail(SSD_ERR_ALIAS, "dstates overlaps %s", i.name);
+    hipError_t e = ssd::launch_mfma_state(s, 1, s.nc, s.nc, X, a, B, dstates, nullptr,
+                                          reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "chunk state launch");
+    return ok();
+}
+
+ssd_status ssd_state_passing(const ssd_fwd_desc* desc, const float* dstates, const float* lam,
+                             const float* initial_state, float* states_in, float* final_state,
+                             void* stream) {
+    ssd_status st = check_desc(desc, false);
+    if (st != SSD_OK) return st;
+    const ssd::FwdShape s = shape_of(desc);
+    if (s.Bz == 0) return ok();
+    const int64_t PN = s.P * s.N;
+    if (s.L == 0) {
+        if (final_state) {
+            if (!aligned(final_state, 16)) return fail(SSD_ERR_ALIGN, "final_state misaligned");
+            hipError_t e = initial_state
+                ? ssd::launch_copy_f32(final_state, initial_state, s.Bz * s.H * PN, reinterpret_cast<hipStream_t>(stream))
+                : ssd::launch_fill_zero(final_state, s.Bz * s.H * PN, reinterpret_cast<hipStream_t>(stream));
+            if (e != hipSuccess) return hip_fail(e, "empty state passing");
+        }
+        return ok();
+    }
+    if (!dstates || !lam || !states_in) return fail(SSD_ERR_NULL, "dstates, lam and states_in are required");
+    const void* v16[] = {dstates, initial_state, states_in, final_state};
+    for (const void* q : v16)
+        if (q && !aligned(q, 16)) return fail(SSD_ERR_ALIGN, "state buffers must be 16-byte aligned");
+    if (!aligned(lam, 4)) return fail(SSD_ERR_ALIGN, "lam misaligned");
+    const int64_t nst = s.Bz * s.nc * s.H * PN * 4;
+    const Range rd = rng("dstates", dstates, nst), ro = rng("states_in", states_in, nst);
+    if (overlap(rd, ro) && dstates != states_in)
+        return fail(SSD_ERR_ALIAS, "states_in overlaps dstates without being identical");
+    const Range rl = rng("lam", lam, s.Bz * s.H * s.nc * 4);
+    const Range ri = rng("initial_state", initial_state, initial_state ? s.Bz * s.H * PN * 4 : 0);
+    const Range rf = rng("final_state", final_state, final_state ? s.Bz * s.H * PN * 4 : 0);
+    if (overlap(ro, rl) || overlap(ro, ri) || overlap(rf, rl) || overlap(rf, ri) || overlap(rf, rd) ||
+        overlap(rf, ro))
+        return fail(SSD_ERR_ALIAS, "an output overlaps an input");
+    hipError_t e = ssd::launch_state_scan(s, s.nc, s.nc, dstates, lam, s.H * s.nc, s.nc,
+                                          initial_state, states_in, final_state, s.H * PN,
+                                          reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "state passing launch");
+    return ok();
+}
+
+ssd_status ssd_chunk_scan(const ssd_fwd_desc* desc, const void* X, const float* a, const void* B,
+                          const void* C, const float* states_in, void* Y, void* stream) {
+    if (!desc) return fail(SSD_ERR_NULL, "desc is NULL");
+    ssd_fwd_desc d1 = *desc;
+    d1.algo = SSD_ALGO_MFMA;
+    d1.seg_chunks = 1;
+    Plan p;
+    ssd_status st = make_plan(&d1, &p);
+    if (st != SSD_OK) return st;
+    const ssd::FwdShape& s = p.s;
+    if (s.Bz == 0 || s.L == 0) return ok();
+    st = check_fwd_io(p, X, a, B, C, nullptr, Y, nullptr);
+    if (st != SSD_OK) return st;
+    if (states_in) {
+        if (!aligned(states_in, 16)) return fail(SSD_ERR_ALIGN, "states_in misaligned");
+        const Range rs = rng("states_in", states_in, s.Bz * s.nc * s.H * s.P * s.N * 4);
+        if (overlap(rs, rng("Y", Y, s.Bz * s.L * s.H * s.P * 2))) return fail(SSD_ERR_ALIAS, "Y overlaps states_in");
+    }
+    const int64_t PN = s.P * s.N;
+    ssd::StateSrc src{states_in, s.nc * s.H * PN, s.H * PN};
+    hipError_t e = ssd::launch_mfma_out(s, 1, s.nc, X, a, B, C, src, Y, nullptr,
+                                        reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "chunk scan launch");
+    return ok();
+}
+
+}  // extern "C"

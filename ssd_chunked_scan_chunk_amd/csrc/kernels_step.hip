@@ -1,0 +1,149 @@
+// kernels_step.hip -- single-token recurrent decode step on gfx950.
+//
+// The constant-memory inference mode of the layer (CiteArk page of
+// "Transformers are SSMs", section "what this means"): the fp32 P x N state of
+// every (batch, head) is read once, decayed and given the rank-1 update, written
+// back in place, and contracted with C for the output:
+//     S <- exp(a) S + x (x) B ;   y[p] = sum_n S[p][n] C[n]
+// 0.5 flop per byte: a pure HBM stream, no MFMA.  Each workgroup owns one
+// (b, h): thread t covers 4 consecutive n of rows p = t / (N/4) + k * (256 /
+// (N/4)), so every wave-wide access is one contiguous 1 KiB run; all of a
+// thread's state loads are issued before any arithmetic, and the row sums over
+// n finish with lane shuffles inside groups of N/4 lanes.
+#include "ssd_device.hpp"
+#include "ssd_launch.hpp"
+
+namespace ssd {
+
+template <typename T> __device__ __forceinline__ float4 load4(const T* p);
+template <> __device__ __forceinline__ float4 load4<float>(const float* p) {
+    return *reinterpret_cast<const float4*>(p);
+}
+template <> __device__ __forceinline__ float4 load4<u16>(const u16* p) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                       __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
+}
+
+template <typename T> struct AccOf;
+template <> struct AccOf<float> {
+    typedef double type;
+    __device__ __forceinline__ static double exp(float a) { return ::exp((double)a); }
+};
+template <> struct AccOf<u16> {
+    typedef float type;
+    __device__ __forceinline__ static float exp(float a) { return expf(a); }
+};
+
+// Fast path: N/4 lanes per state row (N in {16, 32, 64, 128, 256}), P a
+// multiple of 256 / (N/4); ROWS = rows handled per thread.
+template <typename T, int N, int ROWS>
+__global__ __launch_bounds__(256) void k_step(float* __restrict__ state, const T* __restrict__ x,
+                                              const float* __restrict__ a, const T* __restrict__ B,
+                                              const T* __restrict__ C, T* __restrict__ y, int H, int G)
+{
+    constexpr int LPR = N / 4;           // lanes per row
+    constexpr int RPP = 256 / LPR;       // rows per pass of the workgroup
+    constexpr int P = RPP * ROWS;
+    const int bh = blockIdx.x;
+    const int b = bh / H, h = bh - b * H, g = h * G / H;
+    const int tid = threadIdx.x;
+    const int nq = tid % LPR, r0 = tid / LPR;
+
+    float* Sb = state + (int64_t)bh * P * N;
+    f32x4 s[ROWS];
+#pragma unroll
+    for (int k = 0; k < ROWS; ++k)
+        s[k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Sb + (r0 + k * RPP) * N) + nq);
+
+    // fp32 inputs update and contract in fp64 (free here: the kernel is HBM
+    // bound) so a dot product that cancels does not lose the fp32 digits;
+    // bf16 inputs use fp32 arithmetic.
+    using Acc = typename AccOf<T>::type;
+    const float4 Bf = load4<T>(B + ((int64_t)b * G + g) * N + 4 * nq);
+    const float4 Cf = load4<T>(C + ((int64_t)b * G + g) * N + 4 * nq);
+    const Acc Bn[4] = {Bf.x, Bf.y, Bf.z, Bf.w}, Cn[4] = {Cf.x, Cf.y, Cf.z, Cf.w};
+    const Acc e = AccOf<T>::exp(a[bh]);
+    const T* xb = x + (int64_t)bh * P;
+    T* yb = y + (int64_t)bh * P;
+
+#pragma unroll
+    for (int k = 0; k < ROWS; ++k) {
+        const int p = r0 + k * RPP;
+        const Acc xp = Elem<T>::load(xb + p);
+        f32x4 v;
+        Acc acc = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const Acc nv = e * (Acc)s[k][c] + xp * Bn[c];
+            v[c] = (float)nv;
+            acc += nv * Cn[c];
+        }
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(Sb + p * N) + nq);
+#pragma unroll
+        for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+        if (nq == 0) Elem<T>::store(yb + p, (float)acc);
+    }
+}
+
+// General path: one thread per state row, any P and N.
+template <typename T>
+__global__ __launch_bounds__(256) void k_step_any(float* __restrict__ state, const T* __restrict__ x,
+                                                  const float* __restrict__ a, const T* __restrict__ B,
+                                                  const T* __restrict__ C, T* __restrict__ y,
+                                                  int64_t rows, int H, int P, int N, int G)
+{
+    const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (row >= rows) return;
+    const int64_t bh = row / P;
+    const int b = (int)(bh / H), h = (int)(bh - (int64_t)b * H), g = h * G / H;
+    using Acc = typename AccOf<T>::type;
+    const Acc e = AccOf<T>::exp(a[bh]);
+    const Acc xp = Elem<T>::load(x + row);
+    const T* Bt = B + ((int64_t)b * G + g) * N;
+    const T* Ct = C + ((int64_t)b * G + g) * N;
+    float* S = state + row * N;
+    Acc acc = 0;
+    for (int n = 0; n < N; ++n) {
+        const Acc v = e * (Acc)S[n] + xp * (Acc)Elem<T>::load(Bt + n);
+        S[n] = (float)v;
+        acc += v * (Acc)Elem<T>::load(Ct + n);
+    }
+    Elem<T>::store(y + row, (float)acc);
+}
+
+template <typename T>
+static hipError_t launch_step_t(int64_t Bz, int64_t H, int64_t P, int64_t N, int64_t G,
+                                float* state, const T* x, const float* a, const T* B,
+                                const T* C, T* y, hipStream_t st)
+{
+    const dim3 grid((unsigned)(Bz * H)), blk(256);
+#define SSD_STEP_CASE(NN, PP)                                                              \
+    if (N == NN && P == PP) {                                                              \
+        constexpr int rows = PP / (256 / (NN / 4));                                        \
+        hipLaunchKernelGGL((k_step<T, NN, rows>), grid, blk, 0, st, state, x, a, B, C, y,  \
+                           (int)H, (int)G);                                                \
+        return hipGetLastError();                                                          \
+    }
+    SSD_STEP_CASE(128, 64)
+    SSD_STEP_CASE(64, 64)
+    SSD_STEP_CASE(128, 128)
+#undef SSD_STEP_CASE
+    const int64_t rows = Bz * H * P;
+    hipLaunchKernelGGL(k_step_any<T>, dim3((unsigned)((rows + 255) / 256)), blk, 0, st, state, x,
+                       a, B, C, y, rows, (int)H, (int)P, (int)N, (int)G);
+    return hipGetLastError();
+}
+
+hipError_t launch_step(int64_t Bz, int64_t H, int64_t P, int64_t N, int64_t G, bool bf16,
+                       float* state, const void* x, const float* a, const void* B,
+                       const void* C, void* y, hipStream_t st)
+{
+    if (bf16)
+        return launch_step_t<u16>(Bz, H, P, N, G, state, (const u16*)x, a, (const u16*)B,
+                                  (const u16*)C, (u16*)y, st);
+    return launch_step_t<float>(Bz, H, P, N, G, state, (const float*)x, a, (const float*)B,
+                                (const float*)C, (float*)y, st);
+}
+
+}  // namespace ssd

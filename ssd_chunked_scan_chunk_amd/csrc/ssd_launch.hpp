@@ -1,0 +1,66 @@
+// ssd_launch.hpp -- host-side launchers of the gfx950 kernels.  Arguments are
+// already validated by the C ABI layer (api.cpp); these only enqueue.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+struct FwdShape {
+    int64_t Bz, L, H, P, N, G, Q;
+    int64_t nc;  // ceil(L / Q)
+};
+
+// Entering-state source for a segment: Sin + b*bstride + s*sstride + h*P*N,
+// or zeros when Sin is null.
+struct StateSrc {
+    const float* Sin;
+    int64_t bstride, sstride;
+};
+
+// ---- VALU path (any dtype; fp32 arithmetic, exact segment sums) -------------
+hipError_t launch_valu_fwd(const FwdShape& s, bool bf16, const void* X, const float* a,
+                           const void* B, const void* C, const float* S0, void* Y,
+                           float* S_fin, hipStream_t st);
+bool valu_fwd_supported(const FwdShape& s);
+
+// ---- stage 1: in-chunk prefix sums ---------------------------------------------
+hipError_t launch_chunk_cumsum(const FwdShape& s, const float* a, float* cs, float* lam,
+                               hipStream_t st);
+
+// ---- stage 4 / segment scan: S_{u+1} = exp(lam_u) S_u + D_u ---------------------
+// D, Sout: [Bz][ustride][H][P*N] (units 0..nu-1 used);
+// lam: lam[b*lam_bstride + h*lam_hstride + u];
+// Sout[u] receives the state entering unit u; final (optional) the state after
+// the last unit at final + b*final_bstride + h*P*N.  D may equal Sout.
+hipError_t launch_state_scan(const FwdShape& s, int64_t nu, int64_t ustride, const float* D,
+                             const float* lam,
+                             int64_t lam_bstride, int64_t lam_hstride, const float* S0,
+                             float* Sout, float* final_, int64_t final_bstride,
+                             hipStream_t st);
+
+// ---- MFMA segmented path (bf16) ----------------------------------------------------
+bool mfma_supported(int64_t Q, int64_t P, int64_t N);
+// Pass A: for segments [0, nseg_run) of seg_chunks chunks each, the state at
+// the end of the segment starting from zero -> Sseg [Bz][nseg_total][H][P][N]
+// (slot s), and the segment's total log-decay -> lamseg [Bz][H][nseg_total]
+// (lamseg may be null).
+hipError_t launch_mfma_state(const FwdShape& s, int64_t seg_chunks, int64_t nseg_run,
+                             int64_t nseg_total, const void* X, const float* a,
+                             const void* B, float* Sseg, float* lamseg, hipStream_t st);
+// Pass C: for every segment, starting from its entering state, write Y and
+// (last segment) the final state.
+hipError_t launch_mfma_out(const FwdShape& s, int64_t seg_chunks, int64_t nseg,
+                           const void* X, const float* a, const void* B, const void* C,
+                           StateSrc src, void* Y, float* S_fin, hipStream_t st);
+
+// ---- decode step ---------------------------------------------------------------------
+hipError_t launch_step(int64_t Bz, int64_t H, int64_t P, int64_t N, int64_t G, bool bf16,
+                       float* state, const void* x, const float* a, const void* B,
+                       const void* C, void* y, hipStream_t st);
+
+// zero-fill (used for empty sequences: final state = 0)
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
+hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t st);
+
+}  // namespace ssd

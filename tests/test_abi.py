@@ -1,0 +1,135 @@
+"""The C ABI on the host: the library loads, exports every symbol the header
+declares, and rejects bad arguments on the CPU before any HIP call (so these
+run without a GPU and never launch a kernel: every call here fails
+validation or is host-only)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from ssd_chunked_scan_chunk_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def declared_symbols():
+    hdr = open(os.path.join(ROOT, "include", "ssd.h")).read()
+    return sorted(set(re.findall(r"\b(ssd_[a-z_0-9]+)\s*\(", hdr)))
+
+
+def test_header_and_binding_agree():
+    assert declared_symbols() == sorted(_lib.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    assert lib.ssd_version() >= 100
+
+
+def test_status_strings(lib):
+    for code, name in _lib.STATUS_NAMES.items():
+        assert lib.ssd_status_str(code).decode().startswith(name)
+    assert b"unknown" in lib.ssd_status_str(99)
+
+
+FAKE = ctypes.c_void_p(1 << 20)          # 16-byte aligned, never dereferenced
+FAKE2 = ctypes.c_void_p(1 << 30)
+
+
+def desc(**kw):
+    base = dict(batch=2, seqlen=512, nheads=4, headdim=64, dstate=128, ngroups=1, chunk=256,
+                dtype=_lib.SSD_BF16)
+    base.update(kw)
+    return _lib.fwd_desc(**base)
+
+
+def fwd(lib, d, X=FAKE, a=FAKE, B=FAKE, C=FAKE, S0=None, Y=FAKE2, fin=None, ws=None, wsz=0):
+    return lib.ssd_chunk_scan_fwd(ctypes.byref(d), X, a, B, C, S0, Y, fin, ws, wsz, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(nheads=6, ngroups=4), _lib.SSD_ERR_SHAPE),
+    (dict(chunk=0), _lib.SSD_ERR_SHAPE),
+    (dict(batch=-1), _lib.SSD_ERR_SHAPE),
+    (dict(seqlen=-5), _lib.SSD_ERR_SHAPE),
+    (dict(headdim=0), _lib.SSD_ERR_SHAPE),
+    (dict(dtype=7), _lib.SSD_ERR_DTYPE),
+    (dict(chunk=300), _lib.SSD_ERR_UNSUPPORTED),
+    (dict(headdim=128, dstate=256), _lib.SSD_ERR_UNSUPPORTED),
+])
+def test_fwd_rejects_bad_shapes(lib, kw, code):
+    assert fwd(lib, desc(**kw)) == code
+    assert lib.ssd_last_error() != b""
+
+
+def test_fwd_rejects_nulls_alignment_alias_workspace(lib):
+    d = desc()
+    assert fwd(lib, d, X=None) == _lib.SSD_ERR_NULL
+    assert fwd(lib, d, Y=None) == _lib.SSD_ERR_NULL
+    assert fwd(lib, d, X=ctypes.c_void_p((1 << 20) + 2)) == _lib.SSD_ERR_ALIGN
+    # Y overlapping X
+    assert fwd(lib, d, Y=FAKE) == _lib.SSD_ERR_ALIAS
+    # a plan with several segments needs a workspace
+    d2 = desc(batch=1, seqlen=16384, nheads=2, headdim=64, dstate=64)
+    n = ctypes.c_size_t()
+    assert lib.ssd_fwd_workspace_bytes(ctypes.byref(d2), ctypes.byref(n)) == 0
+    assert n.value > 0
+    assert fwd(lib, d2) == _lib.SSD_ERR_WORKSPACE
+    assert fwd(lib, d2, ws=ctypes.c_void_p(1 << 34), wsz=n.value - 1) == _lib.SSD_ERR_WORKSPACE
+    # forcing the MFMA path on fp32 or an uncompiled shape
+    assert fwd(lib, desc(dtype=_lib.SSD_F32, algo=_lib.SSD_ALGO_MFMA)) == _lib.SSD_ERR_UNSUPPORTED
+    assert fwd(lib, desc(headdim=48, algo=_lib.SSD_ALGO_MFMA)) == _lib.SSD_ERR_UNSUPPORTED
+
+
+def plan(lib, d):
+    a, k, n = ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int64()
+    assert lib.ssd_fwd_plan(ctypes.byref(d), ctypes.byref(a), ctypes.byref(k), ctypes.byref(n)) == 0
+    return a.value, k.value, n.value
+
+
+def test_plans(lib):
+    # fp32 -> VALU; bf16 compiled shapes -> MFMA with a balanced segment plan
+    assert plan(lib, desc(dtype=_lib.SSD_F32))[0] == _lib.SSD_ALGO_VALU
+    assert plan(lib, desc(headdim=16, dstate=16))[0] == _lib.SSD_ALGO_VALU
+    a, k, n = plan(lib, desc(batch=8, seqlen=4096, nheads=80))
+    assert (a, k, n) == (_lib.SSD_ALGO_MFMA, 16, 1)      # 640 sequences fill the GPU
+    a, k, n = plan(lib, desc(batch=1, seqlen=524288, nheads=32, dstate=64))
+    assert a == _lib.SSD_ALGO_MFMA and n > 1 and k * n >= 2048
+    a, k, n = plan(lib, desc(seg_chunks=3, seqlen=256 * 10))
+    assert (k, n) == (3, 4)
+    # workspace is zero for a single segment
+    n0 = ctypes.c_size_t(123)
+    assert lib.ssd_fwd_workspace_bytes(ctypes.byref(desc(batch=8, seqlen=4096, nheads=80)), ctypes.byref(n0)) == 0
+    assert n0.value == 0
+
+
+def test_step_validation(lib):
+    def st(**kw):
+        base = dict(batch=4, nheads=8, headdim=64, dstate=128, ngroups=1, dtype=_lib.SSD_BF16, reserved=0)
+        base.update(kw)
+        return _lib.StepDesc(**base)
+    F = [ctypes.c_void_p(1 << k) for k in (20, 24, 26, 28, 30, 32)]
+    call = lambda d, *p: lib.ssd_step(ctypes.byref(d), *p, None)
+    assert call(st(nheads=6, ngroups=4), *F) == _lib.SSD_ERR_SHAPE
+    assert call(st(dtype=9), *F) == _lib.SSD_ERR_DTYPE
+    assert call(st(reserved=1), *F) == _lib.SSD_ERR_SHAPE
+    assert call(st(), None, *F[1:]) == _lib.SSD_ERR_NULL
+    assert call(st(), ctypes.c_void_p((1 << 20) + 4), *F[1:]) == _lib.SSD_ERR_ALIGN
+    assert call(st(), F[0], F[1], F[2], F[3], F[4], F[0]) == _lib.SSD_ERR_ALIAS
+
+
+def test_stage_validation(lib):
+    d = desc(dtype=_lib.SSD_F32)
+    # stage kernels 2/3/5 are the bf16 MFMA building blocks
+    assert lib.ssd_chunk_state(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE2, None) == _lib.SSD_ERR_UNSUPPORTED
+    assert lib.ssd_chunk_scan(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, FAKE2, None) == _lib.SSD_ERR_UNSUPPORTED
+    assert lib.ssd_chunk_cumsum(ctypes.byref(desc(chunk=512)), FAKE, FAKE2, FAKE2, None) == _lib.SSD_ERR_UNSUPPORTED
+    assert lib.ssd_chunk_cumsum(ctypes.byref(desc()), None, FAKE2, FAKE2, None) == _lib.SSD_ERR_NULL
+    assert lib.ssd_state_passing(ctypes.byref(desc()), FAKE, FAKE, None, None, None, None) == _lib.SSD_ERR_NULL
