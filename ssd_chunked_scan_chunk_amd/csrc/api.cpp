@@ -52,10 +52,12 @@ bool overlap(const Range& a, const Range& b) {
 constexpr int64_t kNumCU = 256;          // MI355X compute units
 constexpr int64_t kLdsPerCU = 160 * 1024;
 
-// LDS of the MFMA kernel's full pass for (Q, P, N): used to estimate how many
-// workgroups share a CU when planning segments.
+// LDS of the MFMA kernel's full pass for (Q, P, N) -- double-buffered X and B
+// halves, one C row half, the bf16 entering state and three per-step float
+// vectors -- used to estimate how many workgroups share a CU when planning
+// segments.
 int64_t mfma_lds_bytes(int64_t Q, int64_t P, int64_t N) {
-    return 2 * (Q * (N + 8) + 2 * P * (Q + 8) + P * (N + 8)) + 4 * Q + 32;
+    return 3 * Q * N + 2 * Q * P + 2 * P * N + 12 * Q + 32;
 }
 
 struct Plan {
@@ -148,7 +150,8 @@ ssd_status make_plan(const ssd_fwd_desc* d, Plan* p) {
         if (!mfma_ok)
             return fail(SSD_ERR_UNSUPPORTED,
                         "no MFMA kernel for dtype=%d chunk=%lld headdim=%lld dstate=%lld "
-                        "(bf16, chunk in {64,128,256}, headdim in {32,64}, dstate in {64,128})",
+                        "(bf16, chunk in {64,128,256}, headdim in {32,64}, dstate in {64,128}, "
+                        "not chunk=256 with headdim=32 and dstate=64)",
                         (int)d->dtype, (long long)s.Q, (long long)s.P, (long long)s.N);
         p->algo = SSD_ALGO_MFMA;
     } else if (d->algo == SSD_ALGO_VALU) {
@@ -171,6 +174,10 @@ ssd_status make_plan(const ssd_fwd_desc* d, Plan* p) {
         p->seg_chunks = k;
         p->nseg = (s.nc + k - 1) / k;
         if (p->nseg > 65535) return fail(SSD_ERR_UNSUPPORTED, "too many segments (%lld)", (long long)p->nseg);
+        // one-dimensional grid of (batch, segment, head) workgroups of Q threads
+        if ((s.Bz * p->nseg * s.H + 8) * s.Q >= ((int64_t)1 << 32))
+            return fail(SSD_ERR_UNSUPPORTED, "batch*segments*heads (%lld) too large for one launch",
+                        (long long)(s.Bz * p->nseg * s.H));
         if (p->nseg > 1) {
             const size_t states = (size_t)s.Bz * p->nseg * s.H * s.P * s.N * sizeof(float);
             const size_t lams = (size_t)s.Bz * s.H * p->nseg * sizeof(float);
