@@ -52,12 +52,12 @@ bool overlap(const Range& a, const Range& b) {
 constexpr int64_t kNumCU = 256;          // MI355X compute units
 constexpr int64_t kLdsPerCU = 160 * 1024;
 
-// LDS of the MFMA kernel's full pass for (Q, P, N) -- double-buffered X and B
-// halves, one C row half, the bf16 entering state and three per-step float
-// vectors -- used to estimate how many workgroups share a CU when planning
-// segments.
-int64_t mfma_lds_bytes(int64_t Q, int64_t P, int64_t N) {
-    return 3 * Q * N + 2 * Q * P + 2 * P * N + 12 * Q + 32;
+// LDS of the MFMA kernel's full pass for (P, N): double-buffered 64-step
+// blocks of X for four heads, B and C, plus the per-step vectors -- used to
+// estimate how many workgroups share a CU when planning segments.
+int64_t mfma_lds_bytes(int64_t P, int64_t N) {
+    const int64_t T = 64, HW = 4;
+    return 2 * (HW * T * P * 2 + 2 * T * N * 2 + T * HW * 4) + 3 * HW * T * 4;
 }
 
 struct Plan {
@@ -105,16 +105,18 @@ ssd::FwdShape shape_of(const ssd_fwd_desc* d) {
     return s;
 }
 
-// Segment plan of the MFMA path.  A workgroup walks k consecutive chunks;
-// nseg = ceil(nc / k) segments per (b, h).  Cost in "chunk passes per CU":
-// the full pass takes ceil(WG / slots) rounds of k chunks, and when nseg > 1
-// the state-only pass (about 0.4 of a full chunk) and the segment scan are
-// added.  For each segment count only the most balanced k is tried; the
-// cheapest wins, ties going to fewer segments (less traffic).
+// Segment plan of the MFMA path.  A workgroup (four heads of one group) walks
+// k consecutive chunks; nseg = ceil(nc / k) segments per (b, head quad).  Cost
+// in "chunk passes per CU": the full pass takes ceil(WG / slots) rounds of k
+// chunks, and when nseg > 1 the state-only pass (about 0.35 of a full chunk)
+// and the segment scan are added.  For each segment count only the most
+// balanced k is tried; the cheapest wins, ties going to fewer segments (less
+// traffic).
 int64_t auto_seg_chunks(const ssd::FwdShape& s) {
-    const int64_t per_cu = kLdsPerCU / mfma_lds_bytes(s.Q, s.P, s.N);
+    const int64_t per_cu = kLdsPerCU / mfma_lds_bytes(s.P, s.N);
     const int64_t slots = kNumCU * (per_cu > 0 ? per_cu : 1);
-    const int64_t bh = s.Bz * s.H;
+    const int64_t hw = ssd::mfma_heads_per_workgroup();
+    const int64_t wg = s.Bz * s.G * ((s.H / s.G + hw - 1) / hw);  // workgroups per segment
     const int64_t max_seg = s.nc < 65535 ? s.nc : 65535;
     double best = 1e300;
     int64_t best_k = s.nc;
@@ -124,11 +126,11 @@ int64_t auto_seg_chunks(const ssd::FwdShape& s) {
         if (k == prev_k) continue;
         prev_k = k;
         const int64_t nseg = (s.nc + k - 1) / k;
-        const double rounds_c = (double)((bh * nseg + slots - 1) / slots);
+        const double rounds_c = (double)((wg * nseg + slots - 1) / slots);
         double cost = rounds_c * (double)k;
         if (nseg > 1) {
-            const double rounds_a = (double)((bh * (nseg - 1) + slots - 1) / slots);
-            cost += rounds_a * (double)k * 0.4 + 1.5;
+            const double rounds_a = (double)((wg * (nseg - 1) + slots - 1) / slots);
+            cost += rounds_a * (double)k * 0.35 + 1.5;
         }
         if (cost < best - 1e-9) {
             best = cost;
@@ -150,8 +152,7 @@ ssd_status make_plan(const ssd_fwd_desc* d, Plan* p) {
         if (!mfma_ok)
             return fail(SSD_ERR_UNSUPPORTED,
                         "no MFMA kernel for dtype=%d chunk=%lld headdim=%lld dstate=%lld "
-                        "(bf16, chunk in {64,128,256}, headdim in {32,64}, dstate in {64,128}, "
-                        "not chunk=256 with headdim=32 and dstate=64)",
+                        "(bf16, chunk in {64,128,256}, headdim in {32,64}, dstate in {64,128})",
                         (int)d->dtype, (long long)s.Q, (long long)s.P, (long long)s.N);
         p->algo = SSD_ALGO_MFMA;
     } else if (d->algo == SSD_ALGO_VALU) {
@@ -174,8 +175,8 @@ ssd_status make_plan(const ssd_fwd_desc* d, Plan* p) {
         p->seg_chunks = k;
         p->nseg = (s.nc + k - 1) / k;
         if (p->nseg > 65535) return fail(SSD_ERR_UNSUPPORTED, "too many segments (%lld)", (long long)p->nseg);
-        // one-dimensional grid of (batch, segment, head) workgroups of Q threads
-        if ((s.Bz * p->nseg * s.H + 8) * s.Q >= ((int64_t)1 << 32))
+        // one-dimensional grid of (batch, segment, head quad) workgroups of 256 threads
+        if ((s.Bz * p->nseg * s.H + 8) * 256 >= ((int64_t)1 << 32))
             return fail(SSD_ERR_UNSUPPORTED, "batch*segments*heads (%lld) too large for one launch",
                         (long long)(s.Bz * p->nseg * s.H));
         if (p->nseg > 1) {

@@ -4,54 +4,62 @@
 // applied to X (wiki review of "Transformers are SSMs", section "Core
 // concepts"; CiteArk page, section "AI research summary": a block-decomposed
 // matrix-multiplication algorithm over that matrix).  Blocking the sequence
-// into chunks of Q steps gives, per chunk c:
-//   1. in-chunk prefix sums cs of a (wavefront scans, fp32);
+// into blocks of T steps gives, per block c:
+//   1. in-block prefix sums cs of a (wavefront scan, fp32);
 //   2. diagonal block:   Ydiag = (Lmask_cc o C_c B_c^T) X_c               (MFMA)
-//   3. chunk state:      dS_c  = X_c^T diag(w) B_c, w_j = exp(Lam_c - cs_j) (MFMA)
+//   3. block state:      dS_c  = X_c^T diag(w) B_c, w_j = exp(Lam_c - cs_j) (MFMA)
 //   4. state passing:    S_{c+1} = exp(Lam_c) S_c + dS_c   (fp32, in registers)
 //   5. state to output:  Yoff = diag(exp(cs)) C_c S_c^T                    (MFMA)
+// Y and the final state do not depend on the block length (every blocking is
+// the same sum, only rounded differently), so the fused kernels block at
+// T = 64 whatever chunk length the caller names: on gfx950 the causal
+// quadratic work of longer blocks costs more MFMA and exponential work than
+// the extra state passes it saves.  A caller's chunk still sets segment
+// boundaries (segments are whole chunks).
 //
-// One workgroup walks `seg_chunks` consecutive chunks of one (batch, head),
-// carrying the fp32 P x N state in MFMA accumulators, so states never
-// round-trip HBM inside a segment.  When a launch would leave CUs idle the
-// sequence is split into segments: a state-only pass (stages 1, 3, 4) gives
-// each segment's end state from zero, a scan over segments (kernels_scan.hip)
-// gives every segment's entering state, and the full pass starts from it.
-//
-// Mapping onto gfx950.
-//  * Workgroup = Q/64 wavefronts.  32-step row blocks are dealt to waves in
-//    pairs (w, Q/32-1-w) so every wave owns the same number of causal 32x32
-//    score tiles.  Every product is v_mfma_f32_32x32x16_bf16 (operand lane l
-//    holds row/column l%32 and the 8 k values of group l/32; the accumulator
-//    holds column l%32, rows 8(r/4) + 4(l/32) + r%4).
-//  * Every input reaches LDS through asynchronous global_load_lds copies
-//    (lane L of a wave-wide copy lands at LDS base + L * size), issued one
-//    phase ahead of use, so HBM traffic overlaps the MFMA work and no register
-//    holds prefetched data.  A chunk is consumed in two halves of Q/2 steps
-//    (the contraction index j of stages 2 and 3); X and B halves are double
-//    buffered, a and C single buffered (C in two row halves, moved into
-//    operand registers as soon as they land).  Each buffer is guarded by an
-//    explicit vmcnt wait (vector-memory operations complete in issue order)
-//    followed by an LDS-only barrier.  The copies are written in inline
-//    assembly: they have no register result, and keeping them out of the
-//    compiler's view stops it from inserting full vmcnt waits before every
-//    LDS access, which would serialise the prefetch.
-//  * LDS tiles are unpadded row-major with the 16-byte pieces of row r stored
-//    at piece ^ (r mod pieces-per-row), so the 16-byte row reads and the
-//    transposing reads below touch distinct banks.
-//  * Scores are formed transposed, S^T = B C^T, so lane = step i and the
-//    registers hold steps j: after the decay mask they are directly the
-//    B operand of Y^T = X^T (Lmask o S)^T.  Operands that need j along a
-//    lane's registers (X^T for stage 2; B^T and X for stage 3) come from
-//    ds_read_b64_tr_b16: in each 16-lane group, source lane m names row
-//    R(m/4), columns 4(m%4)..+3, and output lane i receives column i of rows
-//    R(0..3).  Outputs are Y^T tiles: a lane holds 4 consecutive head-dim
-//    entries of one step, an 8-byte store.
+// Decomposition on gfx950.
+//  * A workgroup is four wavefronts; wavefront w owns head w of a group of
+//    four heads that share B and C.  The workgroup walks the blocks of one
+//    (batch, segment) and each wave carries its head's fp32 P x N state in
+//    MFMA accumulators, so states never round-trip HBM inside a segment.  All
+//    four waves do identical work: the only synchronisation is one barrier
+//    per block, which publishes the block's copies and frees the other
+//    buffer.  When a launch would leave CUs idle the sequence is split into
+//    segments: a state-only pass (stages 1, 3, 4) gives each segment's end
+//    state from zero, a scan over segments (kernels_scan.hip) gives every
+//    segment's entering state, and the full pass starts from it.
+//  * Inputs reach LDS through asynchronous global_load_lds copies (lane L of a
+//    wave-wide copy lands at LDS base + L * size), double buffered one block
+//    ahead, so HBM traffic overlaps the MFMA work and no register holds
+//    prefetched data.  The copies are written in inline assembly: they have no
+//    register result, and keeping them out of the compiler's view stops it
+//    from inserting full vmcnt waits before every LDS access, which would
+//    serialise the prefetch.  A block's Y is stored from registers at the top
+//    of the next block, so the one vmcnt(0) wait per block never waits on
+//    fresh stores.
+//  * Every product is v_mfma_f32_32x32x16_bf16 (operand lane l holds row or
+//    column l%32 and 8 k values of group l/32; the accumulator holds column
+//    l%32, rows 8(r/4) + 4(l/32) + r%4 in register r).  Contractions use the
+//    k order {4g..4g+3, 8+4g..8+4g+3} within each 16-wide k step (g = l/32),
+//    which is exactly the row order of an accumulator's registers: the fp32
+//    scores and the fp32 state become MFMA operands in place (rounded to
+//    bf16), with no LDS round trip.  Operands with the contraction along
+//    memory rows (X^T, B^T) come from ds_read_b64_tr_b16: in each 16-lane
+//    group, source lane m names row R(m/4), columns 4(m%4)..+3, and output
+//    lane i receives column i of rows R(0..3).
+//  * Scores are formed transposed, S^T = B C^T, so lane = step i; outputs are
+//    Y^T tiles, a lane holding 4 consecutive head-dim entries of one step.
+//  * LDS tiles are row-major with the 16-byte pieces of row r stored at
+//    piece ^ (r mod pieces-per-row), so row reads and transposing reads touch
+//    distinct banks.
 //  * Workgroups are dealt to the 8 XCDs in contiguous ranges of (batch,
-//    segment, head) items, so the heads that share a batch's B and C run on
-//    one XCD and read them through one L2.
-// Operand rounding: (Lmask o S), w o X, exp(cs) C and the entering state are
-// rounded to bf16 for the MFMA; every accumulation is fp32.
+//    segment, group, head-quad) items, so the workgroups sharing B and C run
+//    on one XCD and read them through one L2.
+// Decay factors: within the diagonal 32x32 tiles exp(cs_i - cs_j) is taken
+// directly; for the off-diagonal tile it is exp(cs_i - cs_31) exp(cs_31 - cs_j),
+// both factors at most 1 for a <= 0.  Operand rounding: (Lmask o S), w o X and
+// the entering state are rounded to bf16 for the MFMA; every accumulation and
+// the exp(cs_i) output scaling are fp32.
 #include "ssd_device.hpp"
 #include "ssd_launch.hpp"
 
@@ -59,31 +67,25 @@ namespace ssd {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));  // register-friendly 16-byte piece
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-constexpr int kXcds = 8;  // MI355X accelerator complex dies; workgroups alternate over them
+constexpr int kXcds = 8;     // MI355X accelerator complex dies; workgroups alternate over them
+constexpr int kT = 64;       // steps per block
+constexpr int kHW = 4;       // heads (= wavefronts) per workgroup
+constexpr int kThreads = 64 * kHW;
 
-template <int Q, int P, int N>
+template <int P, int N>
 struct MfmaCfg {
-    static constexpr int NW = Q / 64;        // wavefronts
-    static constexpr int NT = Q;             // threads: one per step of the chunk
-    static constexpr int RB = Q / 32;        // 32-step row blocks
-    static constexpr int RBH = RB / 2;       // row blocks per half
-    static constexpr int JH = Q / 2;         // steps per half
-    static constexpr int KN = N / 16;        // k steps over the state dim
-    static constexpr int KJH = JH / 16;      // k steps over one half of the chunk
-    static constexpr int PT = P / 32;        // 32-wide head-dim tiles
-    static constexpr int TT = PT * (N / 32); // state tiles
-    static constexpr int TPW = TT / NW;      // state tiles per wave
-    static constexpr int XPR = P / 8;        // 16-byte pieces per X row
-    static constexpr int BPR = N / 8;        // 16-byte pieces per B, C and state row
-    static constexpr int XPH = JH * XPR / NT;  // X copies per thread per half
-    static constexpr int BPH = JH * BPR / NT;  // B (or C) copies per thread per half
-    static constexpr int NH = XPH + BPH;       // copies of one X+B half
-    static_assert(Q % 64 == 0 && P % 32 == 0 && N % 32 == 0, "tile shape");
-    static_assert(TT % NW == 0, "state tiles must split evenly over waves");
-    static_assert(XPH >= 1 && BPH >= 1, "half tiles must cover the workgroup");
+    static constexpr int PT = P / 32;          // 32-wide head-dim tiles
+    static constexpr int NTL = N / 32;         // 32-wide state-dim tiles
+    static constexpr int XPR = P / 8;          // 16-byte pieces per X row
+    static constexpr int BPR = N / 8;          // 16-byte pieces per B / C row
+    static constexpr int XOPS = kHW * kT * XPR / kThreads;  // X copies per thread per block
+    static constexpr int BOPS = kT * BPR / kThreads;        // B (or C) copies per thread per block
+    static_assert(P % 32 == 0 && N % 32 == 0, "tile shape");
+    static_assert(XOPS >= 1 && BOPS >= 1, "a block must cover the workgroup");
 };
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
@@ -99,6 +101,9 @@ __device__ __forceinline__ bf16x8 join8(i16x4 lo, i16x4 hi) {
     i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(bf16x8, v);
 }
+__device__ __forceinline__ bf16x8 join8(u32x2 lo, u32x2 hi) {
+    return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     return (uint32_t)f32_to_bf_bits(lo) | ((uint32_t)f32_to_bf_bits(hi) << 16);
 }
@@ -107,6 +112,11 @@ __device__ __forceinline__ f32x16 zero16() {
 #pragma unroll
     for (int r = 0; r < 16; ++r) z[r] = 0.f;
     return z;
+}
+// registers 8h .. 8h+7 of an accumulator as a bf16 operand
+__device__ __forceinline__ bf16x8 acc_half(const f32x16& v, int h) {
+    return as_bf16x8(u32x4{pack2(v[8 * h + 0], v[8 * h + 1]), pack2(v[8 * h + 2], v[8 * h + 3]),
+                           pack2(v[8 * h + 4], v[8 * h + 5]), pack2(v[8 * h + 6], v[8 * h + 7])});
 }
 // bf16x8 scaled elementwise in fp32 and rounded back
 __device__ __forceinline__ bf16x8 scale8(bf16x8 v, const float (&s)[8]) {
@@ -117,412 +127,407 @@ __device__ __forceinline__ bf16x8 scale8(bf16x8 v, const float (&s)[8]) {
         o[e] = pack2(s[2 * e] * __uint_as_float(u[e] << 16), s[2 * e + 1] * __uint_as_float(u[e] & 0xffff0000u));
     return as_bf16x8(o);
 }
-__device__ __forceinline__ bf16x8 scale8(bf16x8 v, float s) {
-    const u32x4 u = as_u32x4(v);
-    u32x4 o;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-        o[e] = pack2(s * __uint_as_float(u[e] << 16), s * __uint_as_float(u[e] & 0xffff0000u));
-    return as_bf16x8(o);
-}
 
 // Element offset of (row, col) in a swizzled row-major tile of PR 16-byte
-// pieces per row (col a multiple of 4 for 8-byte accesses, of 8 for 16-byte).
+// pieces per row (col a multiple of 4 for 8-byte accesses).
 template <int PR>
 __device__ __forceinline__ int swz(int row, int col) {
     return row * (PR * 8) + ((((col >> 3) ^ (row & (PR - 1))) << 3) | (col & 7));
 }
 
+// Inclusive prefix sum over the 64 lanes: shifts of 1, 2, 4, 8 within each row
+// of 16 lanes (DPP row_shr, zero shifted in), then the row totals.
+__device__ __forceinline__ float wave_scan64(float v, int lane) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xf, 0xf, true));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xf, 0xf, true));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xf, 0xf, true));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xf, 0xf, true));
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 15));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 31));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 47));
+    if (lane >= 16) v += r0;
+    if (lane >= 32) v += r1;
+    if (lane >= 48) v += r2;
+    return v;
+}
+
 // ---- asynchronous HBM -> LDS copies and their synchronisation -----------------
+// (M0 is named as clobbered so the compiler re-initialises it before any use
+// of its own; clang warns that reserved registers are not preserved.)
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char*)p);
 }
-// 16 (or 4) bytes per lane from `g`; lane L writes LDS byte lds + 16 L (4 L).
-// `lds` must be wave-uniform (it is moved into M0).
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :: "v"(g), "s"(lds) : "memory", "m0");
+// 16 (or 4) bytes per lane from base + off (base wave-uniform, off a 32-bit
+// byte offset per lane); lane L writes LDS byte lds + 16 L (4 L).  `lds` must
+// be wave-uniform (it is moved into M0).
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(off), "s"(base), "s"(lds) : "memory", "m0");
 }
-__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-                 :: "v"(g), "s"(lds) : "memory", "m0");
+__device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+                 :: "v"(off), "s"(base), "s"(lds) : "memory", "m0");
 }
-// at most N of this wave's vector-memory operations outstanding
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
-}
+// no vector-memory operation of this wave outstanding
+__device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // workgroup barrier ordering LDS only (no wait on HBM traffic)
 __device__ __forceinline__ void sync_lds() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Copy rows [j0, j0 + ROWS) of a chunk tile (HBM row stride `stride`
-// elements, PR pieces per row) into a swizzled LDS tile.  Wave w, step k
-// fills LDS pieces (k*NT + 64w) .. +63.  Rows past the end of the sequence
-// are clamped to the last valid row: their data never reaches an output
-// (their scores are masked, their chunk-state weight and C rows are zero).
-template <int NT, int PR, int ROWS>
-__device__ __forceinline__ void dma_tile(const u16* lds, const u16* __restrict__ gbase, int stride, int j0,
-                                         int lastc, int wave, int lane) {
-    const uint32_t base = lds_addr(lds);
-#pragma unroll
-    for (int k = 0; k < ROWS * PR / NT; ++k) {
-        const int slot = k * NT + wave * 64 + lane;
-        const int r = slot / PR, pp = slot % PR;
-        const int lp = pp ^ (r & (PR - 1));
-        const int jr = j0 + r <= lastc ? j0 + r : lastc;
-        dma16(gbase + (uint32_t)(jr * stride + lp * 8), base + (uint32_t)((k * NT + wave * 64) * 16));
-    }
-}
-
-// Inclusive prefix sum over the workgroup (one value per thread).  s_tot may
-// be reused only after a later barrier.
-__device__ __forceinline__ float block_scan(float v, float* s_tot, int nwaves, int lane, int wave) {
-    v = wave_inclusive_scan(v);
-    if (lane == 63) s_tot[wave] = v;
-    sync_lds();
-    float add = 0.f;
-    for (int w = 0; w < wave && w < nwaves; ++w) add += s_tot[w];
-    return v + add;
-}
-
-template <int Q, int P, int N, bool FULL>
-__global__ __launch_bounds__(Q) void k_mfma_seg(
+template <int P, int N, bool FULL>
+__global__ __launch_bounds__(kThreads) void k_mfma_seg(
     const u16* __restrict__ X, const float* __restrict__ a, const u16* __restrict__ B,
     const u16* __restrict__ C, StateSrc src, u16* __restrict__ Y, float* __restrict__ S_fin,
     float* __restrict__ Sseg, float* __restrict__ lamseg, int64_t nseg_total, int64_t L,
-    int H, int G, int64_t nc, int64_t seg_chunks, int nseg_grid, int Bz)
+    int H, int G, int64_t blocks_per_seg, int nseg_grid, int Bz)
 {
-    using Cfg = MfmaCfg<Q, P, N>;
-    constexpr int NW = Cfg::NW, NT = Cfg::NT, RB = Cfg::RB, RBH = Cfg::RBH, JH = Cfg::JH;
-    constexpr int KN = Cfg::KN, KJH = Cfg::KJH, PT = Cfg::PT, TPW = Cfg::TPW;
-    constexpr int XPR = Cfg::XPR, BPR = Cfg::BPR, NHV = Cfg::NH;
+    using Cfg = MfmaCfg<P, N>;
+    constexpr int PT = Cfg::PT, NTL = Cfg::NTL, XPR = Cfg::XPR, BPR = Cfg::BPR;
+    constexpr int XOPS = Cfg::XOPS, BOPS = Cfg::BOPS;
 
-    __shared__ __attribute__((aligned(16))) u16 sB0[JH * N];   // B rows of half 0 (swizzled)
-    __shared__ __attribute__((aligned(16))) u16 sB1[JH * N];   // B rows of half 1
-    __shared__ __attribute__((aligned(16))) u16 sX0[JH * P];   // X rows of half 0
-    __shared__ __attribute__((aligned(16))) u16 sX1[JH * P];   // X rows of half 1
-    __shared__ __attribute__((aligned(16))) u16 sC[FULL ? JH * N : 8];  // one row half of C
-    __shared__ __attribute__((aligned(16))) u16 sS[FULL ? P * N : 8];   // entering state, bf16 [p][n]
-    __shared__ __attribute__((aligned(16))) float sA[Q];       // a of the chunk
-    __shared__ __attribute__((aligned(16))) float sCs[Q];      // cs * log2(e)
-    __shared__ __attribute__((aligned(16))) float sW[Q];       // exp(Lam - cs_j), 0 past the end
-    __shared__ float sTot[8];
+    __shared__ __attribute__((aligned(16))) u16 sX[2][kHW * kT * P];   // [buf][head][step][p]
+    __shared__ __attribute__((aligned(16))) u16 sB[2][kT * N];         // [buf][step][n]
+    __shared__ __attribute__((aligned(16))) u16 sC[FULL ? 2 : 1][FULL ? kT * N : 8];
+    __shared__ __attribute__((aligned(16))) float sA[2][kT * kHW];     // [buf][step][head]
+    __shared__ __attribute__((aligned(16))) float sCs[kHW][kT];        // per wave: cs * log2(e)
+    __shared__ __attribute__((aligned(16))) float sW[kHW][kT];         // per wave: exp(Lam - cs_j), 0 past the end
+    __shared__ __attribute__((aligned(16))) float sV[kHW][kT];         // per wave: exp(cs_31 - cs_j), j < 32
 
-    // ---- work item: contiguous item ranges per XCD (heads fastest) ----
-    const int64_t items = (int64_t)Bz * nseg_grid * H;
+    // ---- work item: contiguous item ranges per XCD (head quads fastest) ----
+    const int HPG = H / G;
+    const int HQ = (HPG + kHW - 1) / kHW;
+    const int64_t items = (int64_t)Bz * nseg_grid * G * HQ;
     const int64_t per_xcd = gridDim.x / kXcds;
     const int64_t item = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
     if (item >= items) return;
-    const int h = (int)(item % H);
-    const int64_t seg = (item / H) % nseg_grid;
-    const int b = (int)(item / H / nseg_grid);
+    const int hq = (int)(item % HQ);
+    const int grp = (int)((item / HQ) % G);
+    const int64_t seg = (item / HQ / G) % nseg_grid;
+    const int b = (int)(item / HQ / G / nseg_grid);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, g2 = lane >> 5;
     const int trow = (lane & 15) >> 2, tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    const int grp = h * G / H;
+    const int hl0 = hq * kHW;                    // first head of the quad within the group
+    const int hlw = hl0 + wave;
+    const bool hvalid = hlw < HPG;
+    const int h = grp * HPG + (hvalid ? hlw : HPG - 1);  // this wave's head (clamped)
     const int64_t PN = (int64_t)P * N;
-    const int64_t c_begin = seg * seg_chunks;
-    const int64_t c_end = (c_begin + seg_chunks < nc) ? c_begin + seg_chunks : nc;
-    const int Ib = RB - 1 - wave, Is = wave;  // this wave's two row blocks
-    const int GN = G * N, HP = H * P;
+    const int64_t nblk = (L + kT - 1) / kT;
+    const int64_t c_begin = seg * blocks_per_seg;
+    const int64_t c_end = (c_begin + blocks_per_seg < nblk) ? c_begin + blocks_per_seg : nblk;
+    const int GN = G * N;
 
-    auto chunk_last = [&](int64_t c) -> int {
-        const int64_t last = L - 1 - c * Q;
-        return (int)(last < Q - 1 ? last : Q - 1);
+    auto block_last = [&](int64_t c) -> int {
+        const int64_t last = L - 1 - c * kT;
+        return (int)(last < kT - 1 ? last : kT - 1);
     };
-    auto dma_a = [&](int64_t c) {
-        const int lc = chunk_last(c);
-        const float* ab = a + ((int64_t)b * L + c * Q) * H + h;
-        dma4(ab + (uint32_t)((tid <= lc ? tid : lc) * H), lds_addr(sA) + (uint32_t)(wave * 256));
-    };
-    auto dma_c = [&](int64_t c, int half) {  // C rows [half*JH, half*JH + JH)
-        dma_tile<NT, BPR, JH>(sC, C + (((int64_t)b * L + c * Q) * G + grp) * N, GN, half * JH,
-                              chunk_last(c), wave, lane);
-    };
-    auto dma_half = [&](int64_t c, int half) {
-        const int lc = chunk_last(c);
-        dma_tile<NT, XPR, JH>(half ? sX1 : sX0, X + (((int64_t)b * L + c * Q) * H + h) * P, HP,
-                              half * JH, lc, wave, lane);
-        dma_tile<NT, BPR, JH>(half ? sB1 : sB0, B + (((int64_t)b * L + c * Q) * G + grp) * N, GN,
-                              half * JH, lc, wave, lane);
-    };
-
-    // ---- carried state: this wave's 32x32 tiles of S^T (rows n, columns p) ----
-    f32x16 Sacc[TPW];
-    bool has_state = false;
+    // all copies of block c into buffer bf; rows past the end of the sequence
+    // are clamped to the last valid row (their scores are masked, their state
+    // weight is zero and their outputs are not stored)
+    auto dma_block = [&](int64_t c, int bf) {
+        const int lc = block_last(c);
+        const int64_t row0 = (int64_t)b * L + c * kT;
+        {   // a: thread -> (step, head)
+            const int t = tid >> 2, hh = tid & 3;
+            const int tr = t <= lc ? t : lc;
+            const int hx = hl0 + hh < HPG ? hl0 + hh : HPG - 1;
+            dma4(a + row0 * H + grp * HPG, (uint32_t)((tr * H + hx) * 4),
+                 lds_addr(&sA[bf][0]) + (uint32_t)(wave * 256));
+        }
+        const u16* Xg = X + (row0 * H + grp * HPG) * P;
 #pragma unroll
-    for (int s = 0; s < TPW; ++s) Sacc[s] = zero16();
+        for (int k = 0; k < XOPS; ++k) {
+            const int slot = k * kThreads + wave * 64 + lane;
+            const int hh = slot / (kT * XPR), r = (slot / XPR) % kT, pp = slot % XPR;
+            const int lp = pp ^ (r & (XPR - 1));
+            const int tr = r <= lc ? r : lc;
+            const int hx = hl0 + hh < HPG ? hl0 + hh : HPG - 1;
+            dma16(Xg, (uint32_t)(((tr * H + hx) * P + lp * 8) * 2),
+                  lds_addr(&sX[bf][0]) + (uint32_t)((k * kThreads + wave * 64) * 16));
+        }
+        const u16* Bg = B + (row0 * G + grp) * N;
+        const u16* Cg = FULL ? C + (row0 * G + grp) * N : nullptr;
+#pragma unroll
+        for (int k = 0; k < BOPS; ++k) {
+            const int slot = k * kThreads + wave * 64 + lane;
+            const int r = slot / BPR, pp = slot % BPR;
+            const int lp = pp ^ (r & (BPR - 1));
+            const int tr = r <= lc ? r : lc;
+            const uint32_t off = (uint32_t)((tr * GN + lp * 8) * 2);
+            const uint32_t ldo = (uint32_t)((k * kThreads + wave * 64) * 16);
+            dma16(Bg, off, lds_addr(&sB[bf][0]) + ldo);
+            if constexpr (FULL) dma16(Cg, off, lds_addr(&sC[bf][0]) + ldo);
+        }
+    };
+
+    // ---- carried state: S^T tiles (rows n, columns p), tile (nt, pt) ----
+    f32x16 Sacc[NTL][PT];
+#pragma unroll
+    for (int nt = 0; nt < NTL; ++nt)
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) Sacc[nt][pt] = zero16();
     if constexpr (FULL) {
         if (src.Sin) {
             const float* S0 = src.Sin + b * src.bstride + seg * src.sstride + (int64_t)h * PN;
 #pragma unroll
-            for (int s = 0; s < TPW; ++s) {
-                const int tile = wave * TPW + s, pt = tile % PT, nt = tile / PT;
-                const float* row = S0 + (int64_t)(pt * 32 + l32) * N + nt * 32 + 4 * g2;
+            for (int nt = 0; nt < NTL; ++nt)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float4 v = *reinterpret_cast<const float4*>(row + 8 * q);
-                    Sacc[s][4 * q + 0] = v.x;
-                    Sacc[s][4 * q + 1] = v.y;
-                    Sacc[s][4 * q + 2] = v.z;
-                    Sacc[s][4 * q + 3] = v.w;
+                for (int pt = 0; pt < PT; ++pt) {
+                    const float* row = S0 + (int64_t)(pt * 32 + l32) * N + nt * 32 + 4 * g2;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float4 v = *reinterpret_cast<const float4*>(row + 8 * q);
+                        Sacc[nt][pt][4 * q + 0] = v.x;
+                        Sacc[nt][pt][4 * q + 1] = v.y;
+                        Sacc[nt][pt][4 * q + 2] = v.z;
+                        Sacc[nt][pt][4 * q + 3] = v.w;
+                    }
                 }
-            }
-            has_state = true;
         }
     }
     float lam2_total = 0.f;
-
-    // prologue copies, in the order the loop expects: a, C (upper rows), X+B half 0, half 1
-    dma_a(c_begin);
-    if constexpr (FULL) dma_c(c_begin, 1);
-    dma_half(c_begin, 0);
-    dma_half(c_begin, 1);
-
-    for (int64_t c = c_begin; c < c_end; ++c) {
-        const int64_t t0 = c * Q;
-        const int last = chunk_last(c);
-        const bool has_next = c + 1 < c_end;
-
-        vm_wait<NHV>();  // a, upper C and half 0 of this chunk have landed (half 1 may fly)
-        sync_lds();
-
-        // ---- stage 1: prefix sums of a, chunk-state weights ----
-        const float cs = block_scan(tid <= last ? sA[tid] : 0.f, sTot, NW, lane, wave);
-        sCs[tid] = cs * kLog2e;
-        sync_lds();
-        const float lam2 = sCs[Q - 1];
-        sW[tid] = tid <= last ? fast_exp2(lam2 - sCs[tid]) : 0.f;
-        bf16x8 Cc[2][KN];
-        float csi[2] = {0.f, 0.f};
-        if constexpr (FULL) {
-            csi[0] = sCs[Ib * 32 + l32];
-            csi[1] = sCs[Is * 32 + l32];
-            const bool ok = Ib * 32 + l32 <= last;
+    // previous block's Y^T in bf16: [row block][p tile][4-entry group]
+    uint2 Yb[2][PT][4];
+    auto store_y = [&](int64_t c) {
+        if (!hvalid) return;
+        const int lc = block_last(c);
 #pragma unroll
-            for (int kk = 0; kk < KN; ++kk)
-                Cc[0][kk] = ok ? as_bf16x8(*reinterpret_cast<const u32x4*>(
-                                     sC + swz<BPR>((Ib - RBH) * 32 + l32, 16 * kk + 8 * g2)))
-                               : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
-            if (has_state) {  // entering state, bf16, for stage 5
+        for (int I = 0; I < 2; ++I) {
+            const int i = 32 * I + l32;
+            if (i <= lc) {
+                u16* yrow = Y + (((int64_t)b * L + c * kT + i) * H + h) * P + 4 * g2;
 #pragma unroll
-                for (int s = 0; s < TPW; ++s) {
-                    const int tile = wave * TPW + s, pt = tile % PT, nt = tile / PT;
-                    const int p = pt * 32 + l32;
+                for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        *reinterpret_cast<uint2*>(sS + swz<BPR>(p, nt * 32 + 8 * q + 4 * g2)) =
-                            make_uint2(pack2(Sacc[s][4 * q], Sacc[s][4 * q + 1]),
-                                       pack2(Sacc[s][4 * q + 2], Sacc[s][4 * q + 3]));
-                }
+                    for (int q = 0; q < 4; ++q) *reinterpret_cast<uint2*>(yrow + pt * 32 + 8 * q) = Yb[I][pt][q];
             }
         }
-        sync_lds();  // sA and the upper C rows are consumed; sW, sS visible
-        if constexpr (FULL) dma_c(c, 0);    // lower C rows
-        else if (has_next) dma_a(c + 1);
+    };
 
-        f32x16 Yt[2][PT];
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-            for (int pt = 0; pt < PT; ++pt) Yt[rb][pt] = zero16();
+    if (c_begin < c_end) dma_block(c_begin, 0);
+
+    for (int64_t c = c_begin; c < c_end; ++c) {
+        const int bf = (int)((c - c_begin) & 1);
+        const int last = block_last(c);
+
+        vm_wait_all();  // this wave's copies of block c (and earlier stores) are done
+        sync_lds();     // ... and every wave's; buffer bf^1 is free
+        if (c + 1 < c_end) dma_block(c + 1, bf ^ 1);
+        if constexpr (FULL) {
+            if (c > c_begin) store_y(c - 1);
+        }
+
+        const u16* xT = &sX[bf][wave * kT * P];
+        const u16* bT = &sB[bf][0];
+
+        // ---- stage 1: prefix sums of a (lane = step), weights ----
+        const float av = lane <= last ? sA[bf][lane * kHW + wave] : 0.f;
+        const float cs2 = wave_scan64(av, lane) * kLog2e;
+        const float lam2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs2), 63));
+        const float ref2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs2), 31));
+        sCs[wave][lane] = cs2;
+        sW[wave][lane] = lane <= last ? fast_exp2(lam2 - cs2) : 0.f;
+        sV[wave][lane] = lane < 32 ? fast_exp2(ref2 - cs2) : 0.f;
+        lam2_total += lam2;
         const float dec = fast_exp2(lam2);
-#pragma unroll
-        for (int s = 0; s < TPW; ++s) Sacc[s] *= dec;
 
-        // one causal 32x32 tile (I, J): Y^T[rb] += X_J^T (Lmask o S)^T
-        auto tile = [&](const u16* sBh, const u16* sXh, int rb, int I, int J, int J0) {
-            const int rJ = (J - J0) * 32;
-            f32x16 St = zero16();
+        // X^T fragments (lane = p, k = step in the accumulator row order)
+        bf16x8 Xa[2][2][PT];
 #pragma unroll
-            for (int kk = 0; kk < KN; ++kk) {
-                const bf16x8 Bf = as_bf16x8(*reinterpret_cast<const u32x4*>(
-                    sBh + swz<BPR>(rJ + l32, 16 * kk + 8 * g2)));
-                St = mfma32(Bf, Cc[rb][kk], St);
-            }
-            bf16x8 Xa[2][PT];
+        for (int J = 0; J < 2; ++J)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
                 for (int pt = 0; pt < PT; ++pt) {
-                    const int r1 = rJ + 16 * ks + 4 * g2 + trow;
-                    Xa[ks][pt] = join8(lds_tr4(sXh + swz<XPR>(r1, pt * 32 + tcol)),
-                                       lds_tr4(sXh + swz<XPR>(r1 + 8, pt * 32 + tcol)));
+                    const int r1 = 32 * J + 16 * ks + 4 * g2 + trow;
+                    Xa[J][ks][pt] = join8(lds_tr4(xT + swz<XPR>(r1, pt * 32 + tcol)),
+                                          lds_tr4(xT + swz<XPR>(r1 + 8, pt * 32 + tcol)));
                 }
-            float csj[16];
+
+        if constexpr (FULL) {
+            const u16* cT = &sC[bf][0];
+            // C fragments of both row blocks (lane = step i, k = n in accumulator row order)
+            bf16x8 Cf[2][NTL][2];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const f32x4 v = *reinterpret_cast<const f32x4*>(sCs + J * 32 + 8 * q + 4 * g2);
-                csj[4 * q] = v[0]; csj[4 * q + 1] = v[1]; csj[4 * q + 2] = v[2]; csj[4 * q + 3] = v[3];
-            }
-            const bool diag = (J == I);
-            bf16x8 Pf[2];
+            for (int I = 0; I < 2; ++I)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                // row j = 8(r/4) + 4*g2 + r%4 of the tile, column i = l32;
-                // masked entries (j > i) are replaced, never multiplied
-                const int jl = 8 * (r >> 2) + 4 * g2 + (r & 3);
-                float v = St[r] * fast_exp2(csi[rb] - csj[r]);
-                if (diag && jl > l32) v = 0.f;
-                Pf[r >> 3][r & 7] = f32_to_bf(v);
-            }
+                for (int nt = 0; nt < NTL; ++nt)
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                for (int pt = 0; pt < PT; ++pt) Yt[rb][pt] = mfma32(Xa[ks][pt], Pf[ks], Yt[rb][pt]);
-        };
-        // stages 3 + 4 over one half: S^T += B^T diag(w) X
-        auto chunk_state_half = [&](const u16* sBh, const u16* sXh, int half) {
-#pragma unroll
-            for (int kj = 0; kj < KJH; ++kj) {
-                const int r0 = kj * 16 + 8 * g2 + trow;
-                float w[8];
-                const f32x4 w0 = *reinterpret_cast<const f32x4*>(sW + half * JH + kj * 16 + 8 * g2);
-                const f32x4 w1 = *reinterpret_cast<const f32x4*>(sW + half * JH + kj * 16 + 8 * g2 + 4);
-                w[0] = w0[0]; w[1] = w0[1]; w[2] = w0[2]; w[3] = w0[3];
-                w[4] = w1[0]; w[5] = w1[1]; w[6] = w1[2]; w[7] = w1[3];
-                bf16x8 Af, Bx;
-                int cur_nt = -1, cur_pt = -1;
-#pragma unroll
-                for (int s = 0; s < TPW; ++s) {
-                    const int tl = wave * TPW + s, pt = tl % PT, nt = tl / PT;
-                    if (nt != cur_nt) {
-                        Af = join8(lds_tr4(sBh + swz<BPR>(r0, nt * 32 + tcol)),
-                                   lds_tr4(sBh + swz<BPR>(r0 + 4, nt * 32 + tcol)));
-                        cur_nt = nt;
+                    for (int hf = 0; hf < 2; ++hf) {
+                        const int row = 32 * I + l32, col = nt * 32 + 16 * hf + 4 * g2;
+                        Cf[I][nt][hf] = join8(*reinterpret_cast<const u32x2*>(cT + swz<BPR>(row, col)),
+                                              *reinterpret_cast<const u32x2*>(cT + swz<BPR>(row, col + 8)));
                     }
-                    if (pt != cur_pt) {
-                        Bx = scale8(join8(lds_tr4(sXh + swz<XPR>(r0, pt * 32 + tcol)),
-                                          lds_tr4(sXh + swz<XPR>(r0 + 4, pt * 32 + tcol))), w);
-                        cur_pt = pt;
-                    }
-                    Sacc[s] = mfma32(Af, Bx, Sacc[s]);
-                }
-            }
-        };
-
-        // ================= half 0: steps [0, Q/2) of the chunk =================
-        if constexpr (FULL) {
-            for (int J = 0; J < RBH; ++J) tile(sB0, sX0, 0, Ib, J, 0);  // upper row block
-            vm_wait<0>();  // the lower C rows have landed (and half 1 with them)
-            sync_lds();
-            const bool ok = Is * 32 + l32 <= last;
+            // ---- stage 5: Y^T = S_c C^T for both row blocks, then exp(cs_i) ----
+            f32x16 Yt[2][PT];
 #pragma unroll
-            for (int kk = 0; kk < KN; ++kk)
-                Cc[1][kk] = ok ? as_bf16x8(*reinterpret_cast<const u32x4*>(
-                                     sC + swz<BPR>(Is * 32 + l32, 16 * kk + 8 * g2)))
-                               : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
-            sync_lds();  // every wave has its C rows: sC and sA are free
-            if (has_next) {
-                dma_a(c + 1);
-                dma_c(c + 1, 1);
-            }
-            for (int J = 0; J <= Is; ++J) tile(sB0, sX0, 1, Is, J, 0);  // lower row block
-        }
-        chunk_state_half(sB0, sX0, 0);
-
-        sync_lds();  // every wave is done with buffer 0
-        if (has_next) {
-            dma_half(c + 1, 0);
-            vm_wait<NHV>();  // half 1 of this chunk has landed (the copies just issued may fly)
-        } else {
-            vm_wait<0>();
-        }
-        sync_lds();
-
-        // ================= half 1: steps [Q/2, Q) =================
-        if constexpr (FULL) {
-            for (int J = RBH; J <= Ib; ++J) tile(sB1, sX1, 0, Ib, J, RBH);
-        }
-        chunk_state_half(sB1, sX1, 1);
-        if constexpr (FULL) {
-            // ---- stage 5: Y^T += S (diag(exp(cs)) C)^T ----
-            if (has_state) {
+            for (int I = 0; I < 2; ++I)
 #pragma unroll
-                for (int rb = 0; rb < 2; ++rb) {
-                    const float sc = fast_exp2(csi[rb]);
+                for (int pt = 0; pt < PT; ++pt) Yt[I][pt] = zero16();
 #pragma unroll
-                    for (int kk = 0; kk < KN; ++kk) Cc[rb][kk] = scale8(Cc[rb][kk], sc);
-                }
+            for (int nt = 0; nt < NTL; ++nt)
 #pragma unroll
                 for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
-                    for (int kk = 0; kk < KN; ++kk) {
-                        const bf16x8 Sf = as_bf16x8(*reinterpret_cast<const u32x4*>(
-                            sS + swz<BPR>(pt * 32 + l32, 16 * kk + 8 * g2)));
+                    for (int hf = 0; hf < 2; ++hf) {
+                        const bf16x8 Sf = acc_half(Sacc[nt][pt], hf);
 #pragma unroll
-                        for (int rb = 0; rb < 2; ++rb) Yt[rb][pt] = mfma32(Sf, Cc[rb][kk], Yt[rb][pt]);
+                        for (int I = 0; I < 2; ++I) Yt[I][pt] = mfma32(Sf, Cf[I][nt][hf], Yt[I][pt]);
                     }
-            }
-            // ---- write Y: lane = step i, 4 consecutive head-dim entries per store ----
+            const float csi0 = sCs[wave][l32], csi1 = sCs[wave][32 + l32];
+            {
+                const float e0 = fast_exp2(csi0), e1 = fast_exp2(csi1);
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
-                const int i = (rb == 0 ? Ib : Is) * 32 + l32;
-                if (i <= last) {
-                    u16* yrow = Y + (((int64_t)b * L + t0 + i) * H + h) * P + 4 * g2;
-#pragma unroll
-                    for (int pt = 0; pt < PT; ++pt)
-#pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            *reinterpret_cast<uint2*>(yrow + pt * 32 + 8 * q) =
-                                make_uint2(pack2(Yt[rb][pt][4 * q], Yt[rb][pt][4 * q + 1]),
-                                           pack2(Yt[rb][pt][4 * q + 2], Yt[rb][pt][4 * q + 3]));
+                for (int pt = 0; pt < PT; ++pt) {
+                    Yt[0][pt] *= e0;
+                    Yt[1][pt] *= e1;
                 }
             }
+
+            // ---- stage 2: scores S^T = B C^T per 32x32 tile, decay, Y^T += X^T (L o S)^T ----
+            auto scores = [&](int I, int J) {
+                f32x16 St = zero16();
+#pragma unroll
+                for (int nt = 0; nt < NTL; ++nt)
+#pragma unroll
+                    for (int hf = 0; hf < 2; ++hf) {
+                        const int row = 32 * J + l32, col = nt * 32 + 16 * hf + 4 * g2;
+                        const bf16x8 Bf = join8(*reinterpret_cast<const u32x2*>(bT + swz<BPR>(row, col)),
+                                                *reinterpret_cast<const u32x2*>(bT + swz<BPR>(row, col + 8)));
+                        St = mfma32(Bf, Cf[I][nt][hf], St);
+                    }
+                return St;
+            };
+            const f32x16 S00 = scores(0, 0), S10 = scores(1, 0), S11 = scores(1, 1);
+            // row j of accumulator register r: 8(r/4) + 4*g2 + r%4
+            auto diag_apply = [&](const f32x16& St, int I, float csi) {
+                float csj[16];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4 v = *reinterpret_cast<const f32x4*>(&sCs[wave][32 * I + 8 * q + 4 * g2]);
+                    csj[4 * q] = v[0]; csj[4 * q + 1] = v[1]; csj[4 * q + 2] = v[2]; csj[4 * q + 3] = v[3];
+                }
+                u32x4 pk[2];
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) {
+                    const int j0 = 8 * (r >> 2) + 4 * g2 + (r & 3);
+                    // masked entries (j > i) are replaced, never multiplied
+                    const float v0 = j0 <= l32 ? St[r] * fast_exp2(csi - csj[r]) : 0.f;
+                    const float v1 = j0 + 1 <= l32 ? St[r + 1] * fast_exp2(csi - csj[r + 1]) : 0.f;
+                    pk[r >> 3][(r & 7) >> 1] = pack2(v0, v1);
+                }
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int pt = 0; pt < PT; ++pt) Yt[I][pt] = mfma32(Xa[I][ks][pt], as_bf16x8(pk[ks]), Yt[I][pt]);
+            };
+            diag_apply(S00, 0, csi0);
+            diag_apply(S11, 1, csi1);
+            {   // off-diagonal tile (I = 1, J = 0)
+                const float ui = fast_exp2(csi1 - ref2);
+                float vj[16];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4 v = *reinterpret_cast<const f32x4*>(&sV[wave][8 * q + 4 * g2]);
+                    vj[4 * q] = v[0] * ui; vj[4 * q + 1] = v[1] * ui;
+                    vj[4 * q + 2] = v[2] * ui; vj[4 * q + 3] = v[3] * ui;
+                }
+                u32x4 pk[2];
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) pk[r >> 3][(r & 7) >> 1] = pack2(S10[r] * vj[r], S10[r + 1] * vj[r + 1]);
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int pt = 0; pt < PT; ++pt) Yt[1][pt] = mfma32(Xa[0][ks][pt], as_bf16x8(pk[ks]), Yt[1][pt]);
+            }
+            // Y^T to bf16, stored at the top of the next block (or after the loop)
+#pragma unroll
+            for (int I = 0; I < 2; ++I)
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        Yb[I][pt][q] = make_uint2(pack2(Yt[I][pt][4 * q], Yt[I][pt][4 * q + 1]),
+                                                  pack2(Yt[I][pt][4 * q + 2], Yt[I][pt][4 * q + 3]));
         }
 
-        sync_lds();  // every wave is done with buffer 1, sCs, sW and sS
-        if (has_next) dma_half(c + 1, 1);
-        has_state = true;
-        lam2_total += lam2;
+        // ---- stages 3 + 4: S^T = exp(Lam) S^T + B^T diag(w) X ----
+#pragma unroll
+        for (int nt = 0; nt < NTL; ++nt)
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) Sacc[nt][pt] *= dec;
+#pragma unroll
+        for (int J = 0; J < 2; ++J)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const int k0 = 32 * J + 16 * ks + 4 * g2;
+                float w[8];
+                const f32x4 w0 = *reinterpret_cast<const f32x4*>(&sW[wave][k0]);
+                const f32x4 w1 = *reinterpret_cast<const f32x4*>(&sW[wave][k0 + 8]);
+                w[0] = w0[0]; w[1] = w0[1]; w[2] = w0[2]; w[3] = w0[3];
+                w[4] = w1[0]; w[5] = w1[1]; w[6] = w1[2]; w[7] = w1[3];
+                bf16x8 Wx[PT];
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt) Wx[pt] = scale8(Xa[J][ks][pt], w);
+                const int r1 = k0 + trow;
+#pragma unroll
+                for (int nt = 0; nt < NTL; ++nt) {
+                    const bf16x8 Af = join8(lds_tr4(bT + swz<BPR>(r1, nt * 32 + tcol)),
+                                            lds_tr4(bT + swz<BPR>(r1 + 8, nt * 32 + tcol)));
+#pragma unroll
+                    for (int pt = 0; pt < PT; ++pt) Sacc[nt][pt] = mfma32(Af, Wx[pt], Sacc[nt][pt]);
+                }
+            }
+    }
+    if constexpr (FULL) {
+        if (c_begin < c_end) store_y(c_end - 1);
     }
 
     // ---- epilogue: final state (full pass, last segment) or segment summary ----
+    if (!hvalid) return;
     float* Sdst = nullptr;
     if constexpr (FULL) {
         if (S_fin && seg == nseg_grid - 1) Sdst = S_fin + ((int64_t)b * H + h) * PN;
     } else {
         Sdst = Sseg + (((int64_t)b * nseg_total + seg) * H + h) * PN;
-        if (lamseg && tid == 0) lamseg[((int64_t)b * H + h) * nseg_total + seg] = lam2_total * 0.69314718055994531f;
+        if (lamseg && lane == 0) lamseg[((int64_t)b * H + h) * nseg_total + seg] = lam2_total * 0.69314718055994531f;
     }
     if (Sdst) {
 #pragma unroll
-        for (int s = 0; s < TPW; ++s) {
-            const int tl = wave * TPW + s, pt = tl % PT, nt = tl / PT;
-            float* row = Sdst + (int64_t)(pt * 32 + l32) * N + nt * 32 + 4 * g2;
+        for (int nt = 0; nt < NTL; ++nt)
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                *reinterpret_cast<float4*>(row + 8 * q) =
-                    make_float4(Sacc[s][4 * q], Sacc[s][4 * q + 1], Sacc[s][4 * q + 2], Sacc[s][4 * q + 3]);
-        }
+            for (int pt = 0; pt < PT; ++pt) {
+                float* row = Sdst + (int64_t)(pt * 32 + l32) * N + nt * 32 + 4 * g2;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<float4*>(row + 8 * q) =
+                        make_float4(Sacc[nt][pt][4 * q], Sacc[nt][pt][4 * q + 1], Sacc[nt][pt][4 * q + 2],
+                                    Sacc[nt][pt][4 * q + 3]);
+            }
     }
 }
 
 bool mfma_supported(int64_t Q, int64_t P, int64_t N) {
-    if (!((Q == 64 || Q == 128 || Q == 256) && (P == 32 || P == 64) && (N == 64 || N == 128))) return false;
-    return ((P / 32) * (N / 32)) % (Q / 64) == 0;
+    return (Q == 64 || Q == 128 || Q == 256) && (P == 32 || P == 64) && (N == 64 || N == 128);
 }
 
-#define SSD_MFMA_DISPATCH(MACRO)                                        \
-    if (s.Q == 256 && s.P == 64 && s.N == 128) MACRO(256, 64, 128)      \
-    else if (s.Q == 256 && s.P == 64 && s.N == 64) MACRO(256, 64, 64)   \
-    else if (s.Q == 256 && s.P == 32 && s.N == 128) MACRO(256, 32, 128) \
-    else if (s.Q == 128 && s.P == 64 && s.N == 128) MACRO(128, 64, 128) \
-    else if (s.Q == 128 && s.P == 64 && s.N == 64) MACRO(128, 64, 64)   \
-    else if (s.Q == 128 && s.P == 32 && s.N == 128) MACRO(128, 32, 128) \
-    else if (s.Q == 128 && s.P == 32 && s.N == 64) MACRO(128, 32, 64)   \
-    else if (s.Q == 64 && s.P == 64 && s.N == 128) MACRO(64, 64, 128)   \
-    else if (s.Q == 64 && s.P == 64 && s.N == 64) MACRO(64, 64, 64)     \
-    else if (s.Q == 64 && s.P == 32 && s.N == 128) MACRO(64, 32, 128)   \
-    else if (s.Q == 64 && s.P == 32 && s.N == 64) MACRO(64, 32, 64)     \
+int64_t mfma_heads_per_workgroup() { return kHW; }
+
+#define SSD_MFMA_DISPATCH(MACRO)                     \
+    if (s.P == 64 && s.N == 128) MACRO(64, 128)      \
+    else if (s.P == 64 && s.N == 64) MACRO(64, 64)   \
+    else if (s.P == 32 && s.N == 128) MACRO(32, 128) \
+    else if (s.P == 32 && s.N == 64) MACRO(32, 64)   \
     else return hipErrorInvalidValue;
 
-// one workgroup per (batch, segment, head) item, padded to a multiple of the XCD count
-static unsigned grid_for(int64_t items) {
+// one workgroup per (batch, segment, group, head quad) item, padded to a multiple of the XCD count
+static unsigned grid_for(const FwdShape& s, int64_t nseg) {
+    const int64_t hq = (s.H / s.G + kHW - 1) / kHW;
+    const int64_t items = s.Bz * nseg * s.G * hq;
     return (unsigned)(((items + kXcds - 1) / kXcds) * kXcds);
 }
 
@@ -531,13 +536,14 @@ hipError_t launch_mfma_state(const FwdShape& s, int64_t seg_chunks, int64_t nseg
                              const void* B, float* Sseg, float* lamseg, hipStream_t st)
 {
     if (nseg_run <= 0) return hipSuccess;
-    const dim3 grid(grid_for(s.Bz * nseg_run * s.H));
+    const dim3 grid(grid_for(s, nseg_run));
     const StateSrc none{nullptr, 0, 0};
-#define SSD_LAUNCH_STATE(QQ, PP, NN)                                                          \
-    hipLaunchKernelGGL((k_mfma_seg<QQ, PP, NN, false>), grid, dim3(QQ), 0, st,              \
+    const int64_t bps = seg_chunks * (s.Q / kT);
+#define SSD_LAUNCH_STATE(PP, NN)                                                              \
+    hipLaunchKernelGGL((k_mfma_seg<PP, NN, false>), grid, dim3(kThreads), 0, st,             \
                        (const u16*)X, a, (const u16*)B, (const u16*)nullptr, none,          \
                        (u16*)nullptr, (float*)nullptr, Sseg, lamseg, nseg_total, s.L,       \
-                       (int)s.H, (int)s.G, s.nc, seg_chunks, (int)nseg_run, (int)s.Bz);
+                       (int)s.H, (int)s.G, bps, (int)nseg_run, (int)s.Bz);
     SSD_MFMA_DISPATCH(SSD_LAUNCH_STATE)
 #undef SSD_LAUNCH_STATE
     return hipGetLastError();
@@ -547,12 +553,13 @@ hipError_t launch_mfma_out(const FwdShape& s, int64_t seg_chunks, int64_t nseg,
                            const void* X, const float* a, const void* B, const void* C,
                            StateSrc src, void* Y, float* S_fin, hipStream_t st)
 {
-    const dim3 grid(grid_for(s.Bz * nseg * s.H));
-#define SSD_LAUNCH_OUT(QQ, PP, NN)                                                            \
-    hipLaunchKernelGGL((k_mfma_seg<QQ, PP, NN, true>), grid, dim3(QQ), 0, st,               \
+    const dim3 grid(grid_for(s, nseg));
+    const int64_t bps = seg_chunks * (s.Q / kT);
+#define SSD_LAUNCH_OUT(PP, NN)                                                                \
+    hipLaunchKernelGGL((k_mfma_seg<PP, NN, true>), grid, dim3(kThreads), 0, st,              \
                        (const u16*)X, a, (const u16*)B, (const u16*)C, src, (u16*)Y, S_fin, \
                        (float*)nullptr, (float*)nullptr, (int64_t)0, s.L, (int)s.H,          \
-                       (int)s.G, s.nc, seg_chunks, (int)nseg, (int)s.Bz);
+                       (int)s.G, bps, (int)nseg, (int)s.Bz);
     SSD_MFMA_DISPATCH(SSD_LAUNCH_OUT)
 #undef SSD_LAUNCH_OUT
     return hipGetLastError();

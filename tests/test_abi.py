@@ -98,15 +98,17 @@ def test_plans(lib):
     # fp32 -> VALU; bf16 compiled shapes -> MFMA with a balanced segment plan
     assert plan(lib, desc(dtype=_lib.SSD_F32))[0] == _lib.SSD_ALGO_VALU
     assert plan(lib, desc(headdim=16, dstate=16))[0] == _lib.SSD_ALGO_VALU
+    a, k, n = plan(lib, desc(batch=64, seqlen=4096, nheads=80))
+    assert (a, k, n) == (_lib.SSD_ALGO_MFMA, 16, 1)      # 1280 head quads fill the GPU
     a, k, n = plan(lib, desc(batch=8, seqlen=4096, nheads=80))
-    assert (a, k, n) == (_lib.SSD_ALGO_MFMA, 16, 1)      # 640 sequences fill the GPU
+    assert a == _lib.SSD_ALGO_MFMA and k * n >= 16 and k * (n - 1) < 16
     a, k, n = plan(lib, desc(batch=1, seqlen=524288, nheads=32, dstate=64))
     assert a == _lib.SSD_ALGO_MFMA and n > 1 and k * n >= 2048
     a, k, n = plan(lib, desc(seg_chunks=3, seqlen=256 * 10))
     assert (k, n) == (3, 4)
     # workspace is zero for a single segment
     n0 = ctypes.c_size_t(123)
-    assert lib.ssd_fwd_workspace_bytes(ctypes.byref(desc(batch=8, seqlen=4096, nheads=80)), ctypes.byref(n0)) == 0
+    assert lib.ssd_fwd_workspace_bytes(ctypes.byref(desc(batch=64, seqlen=4096, nheads=80)), ctypes.byref(n0)) == 0
     assert n0.value == 0
 
 
