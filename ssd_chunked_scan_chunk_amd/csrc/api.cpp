@@ -53,11 +53,11 @@ constexpr int64_t kNumCU = 256;          // MI355X compute units
 constexpr int64_t kLdsPerCU = 160 * 1024;
 
 // LDS of the MFMA kernel's full pass for (P, N): double-buffered 64-step
-// blocks of X for four heads, B and C, plus the per-step vectors -- used to
-// estimate how many workgroups share a CU when planning segments.
+// blocks of X for the workgroup's heads, B and C, plus the per-step vectors --
+// used to estimate how many workgroups share a CU when planning segments.
 int64_t mfma_lds_bytes(int64_t P, int64_t N) {
-    const int64_t T = 64, HW = 4;
-    return 2 * (HW * T * P * 2 + 2 * T * N * 2 + T * HW * 4) + 3 * HW * T * 4;
+    const int64_t T = 64, HW = ssd::mfma_heads_per_workgroup(P, N);
+    return 2 * (HW * T * P * 2 + 2 * T * N * 2 + T * HW * 4) + 2 * 4 * T * 4;
 }
 
 struct Plan {
@@ -105,8 +105,8 @@ ssd::FwdShape shape_of(const ssd_fwd_desc* d) {
     return s;
 }
 
-// Segment plan of the MFMA path.  A workgroup (four heads of one group) walks
-// k consecutive chunks; nseg = ceil(nc / k) segments per (b, head quad).  Cost
+// Segment plan of the MFMA path.  A workgroup (two or four heads of one group) walks
+// k consecutive chunks; nseg = ceil(nc / k) segments per (b, head set).  Cost
 // in "chunk passes per CU": the full pass takes ceil(WG / slots) rounds of k
 // chunks, and when nseg > 1 the state-only pass (about 0.35 of a full chunk)
 // and the segment scan are added.  For each segment count only the most
@@ -115,7 +115,7 @@ ssd::FwdShape shape_of(const ssd_fwd_desc* d) {
 int64_t auto_seg_chunks(const ssd::FwdShape& s) {
     const int64_t per_cu = kLdsPerCU / mfma_lds_bytes(s.P, s.N);
     const int64_t slots = kNumCU * (per_cu > 0 ? per_cu : 1);
-    const int64_t hw = ssd::mfma_heads_per_workgroup();
+    const int64_t hw = ssd::mfma_heads_per_workgroup(s.P, s.N);
     const int64_t wg = s.Bz * s.G * ((s.H / s.G + hw - 1) / hw);  // workgroups per segment
     const int64_t max_seg = s.nc < 65535 ? s.nc : 65535;
     double best = 1e300;
@@ -175,7 +175,7 @@ ssd_status make_plan(const ssd_fwd_desc* d, Plan* p) {
         p->seg_chunks = k;
         p->nseg = (s.nc + k - 1) / k;
         if (p->nseg > 65535) return fail(SSD_ERR_UNSUPPORTED, "too many segments (%lld)", (long long)p->nseg);
-        // one-dimensional grid of (batch, segment, head quad) workgroups of 256 threads
+        // one-dimensional grid of (batch, segment, head set) workgroups of 256 threads
         if ((s.Bz * p->nseg * s.H + 8) * 256 >= ((int64_t)1 << 32))
             return fail(SSD_ERR_UNSUPPORTED, "batch*segments*heads (%lld) too large for one launch",
                         (long long)(s.Bz * p->nseg * s.H));

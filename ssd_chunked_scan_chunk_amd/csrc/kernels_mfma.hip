@@ -8,7 +8,8 @@
 //   1. in-block prefix sums cs of a (wavefront scan, fp32);
 //   2. diagonal block:   Ydiag = (Lmask_cc o C_c B_c^T) X_c               (MFMA)
 //   3. block state:      dS_c  = X_c^T diag(w) B_c, w_j = exp(Lam_c - cs_j) (MFMA)
-//   4. state passing:    S_{c+1} = exp(Lam_c) S_c + dS_c   (fp32, in registers)
+//   4. state passing:    S_{c+1} = exp(Lam_c) S_c + dS_c   (fp32, in registers,
+//                        the decay kept as a separate power-of-two scale)
 //   5. state to output:  Yoff = diag(exp(cs)) C_c S_c^T                    (MFMA)
 // Y and the final state do not depend on the block length (every blocking is
 // the same sum, only rounded differently), so the fused kernels block at
@@ -73,18 +74,26 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kXcds = 8;     // MI355X accelerator complex dies; workgroups alternate over them
 constexpr int kT = 64;       // steps per block
-constexpr int kHW = 4;       // heads (= wavefronts) per workgroup
-constexpr int kThreads = 64 * kHW;
+constexpr int kWaves = 4;    // wavefronts per workgroup
+constexpr int kThreads = 64 * kWaves;
 
+// A workgroup holds HW heads of one group; wave w owns head w % HW and the
+// head-dim tiles [(w / HW) * PTW, +PTW).  Four heads per workgroup while a
+// head's fp32 state fits one wave comfortably (P*N <= 4096: 64 accumulator
+// registers); for larger states two heads, each split over two waves by head
+// dim, which halves the accumulators a wave carries.
 template <int P, int N>
 struct MfmaCfg {
-    static constexpr int PT = P / 32;          // 32-wide head-dim tiles
-    static constexpr int NTL = N / 32;         // 32-wide state-dim tiles
-    static constexpr int XPR = P / 8;          // 16-byte pieces per X row
-    static constexpr int BPR = N / 8;          // 16-byte pieces per B / C row
-    static constexpr int XOPS = kHW * kT * XPR / kThreads;  // X copies per thread per block
-    static constexpr int BOPS = kT * BPR / kThreads;        // B (or C) copies per thread per block
-    static_assert(P % 32 == 0 && N % 32 == 0, "tile shape");
+    static constexpr int HW = P * N > 4096 ? 2 : 4;    // heads per workgroup
+    static constexpr int PS = kWaves / HW;               // waves per head
+    static constexpr int PT = P / 32;                    // 32-wide head-dim tiles
+    static constexpr int PTW = PT / PS;                  // ... per wave
+    static constexpr int NTL = N / 32;                   // 32-wide state-dim tiles
+    static constexpr int XPR = P / 8;                    // 16-byte pieces per X row
+    static constexpr int BPR = N / 8;                    // 16-byte pieces per B / C row
+    static constexpr int XOPS = HW * kT * XPR / kThreads;  // X copies per thread per block
+    static constexpr int BOPS = kT * BPR / kThreads;       // B (or C) copies per thread per block
+    static_assert(P % 32 == 0 && N % 32 == 0 && PTW >= 1, "tile shape");
     static_assert(XOPS >= 1 && BOPS >= 1, "a block must cover the workgroup");
 };
 
@@ -104,8 +113,11 @@ __device__ __forceinline__ bf16x8 join8(i16x4 lo, i16x4 hi) {
 __device__ __forceinline__ bf16x8 join8(u32x2 lo, u32x2 hi) {
     return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
 }
+// two floats rounded (to nearest even) into one packed bf16 pair: one v_cvt_pk_bf16_f32
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-    return (uint32_t)f32_to_bf_bits(lo) | ((uint32_t)f32_to_bf_bits(hi) << 16);
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 __device__ __forceinline__ f32x16 zero16() {
     f32x16 z;
@@ -163,11 +175,11 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // be wave-uniform (it is moved into M0).
 __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-                 :: "v"(off), "s"(base), "s"(lds) : "memory", "m0");
+                 :: "v"(off), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
-                 :: "v"(off), "s"(base), "s"(lds) : "memory", "m0");
+                 :: "v"(off), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
 }
 // no vector-memory operation of this wave outstanding
 __device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -184,20 +196,19 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
     int H, int G, int64_t blocks_per_seg, int nseg_grid, int Bz)
 {
     using Cfg = MfmaCfg<P, N>;
-    constexpr int PT = Cfg::PT, NTL = Cfg::NTL, XPR = Cfg::XPR, BPR = Cfg::BPR;
+    constexpr int HW = Cfg::HW, PTW = Cfg::PTW, NTL = Cfg::NTL, XPR = Cfg::XPR, BPR = Cfg::BPR;
     constexpr int XOPS = Cfg::XOPS, BOPS = Cfg::BOPS;
 
-    __shared__ __attribute__((aligned(16))) u16 sX[2][kHW * kT * P];   // [buf][head][step][p]
+    __shared__ __attribute__((aligned(16))) u16 sX[2][HW * kT * P];    // [buf][head][step][p]
     __shared__ __attribute__((aligned(16))) u16 sB[2][kT * N];         // [buf][step][n]
     __shared__ __attribute__((aligned(16))) u16 sC[FULL ? 2 : 1][FULL ? kT * N : 8];
-    __shared__ __attribute__((aligned(16))) float sA[2][kT * kHW];     // [buf][step][head]
-    __shared__ __attribute__((aligned(16))) float sCs[kHW][kT];        // per wave: cs * log2(e)
-    __shared__ __attribute__((aligned(16))) float sW[kHW][kT];         // per wave: exp(Lam - cs_j), 0 past the end
-    __shared__ __attribute__((aligned(16))) float sV[kHW][kT];         // per wave: exp(cs_31 - cs_j), j < 32
+    __shared__ __attribute__((aligned(16))) float sA[2][kT * HW];      // [buf][step][head]
+    __shared__ __attribute__((aligned(16))) float sCs[kWaves][kT];     // per wave: cs * log2(e)
+    __shared__ __attribute__((aligned(16))) float sW[kWaves][kT];      // per wave: state weights, 0 past the end
 
-    // ---- work item: contiguous item ranges per XCD (head quads fastest) ----
+    // ---- work item: contiguous item ranges per XCD (head sets fastest) ----
     const int HPG = H / G;
-    const int HQ = (HPG + kHW - 1) / kHW;
+    const int HQ = (HPG + HW - 1) / HW;
     const int64_t items = (int64_t)Bz * nseg_grid * G * HQ;
     const int64_t per_xcd = gridDim.x / kXcds;
     const int64_t item = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
@@ -211,8 +222,9 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, g2 = lane >> 5;
     const int trow = (lane & 15) >> 2, tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    const int hl0 = hq * kHW;                    // first head of the quad within the group
-    const int hlw = hl0 + wave;
+    const int hl0 = hq * HW;                     // first head of the set within the group
+    const int hlw = hl0 + wave % HW;
+    const int pt0 = (wave / HW) * PTW;           // this wave's first head-dim tile
     const bool hvalid = hlw < HPG;
     const int h = grp * HPG + (hvalid ? hlw : HPG - 1);  // this wave's head (clamped)
     const int64_t PN = (int64_t)P * N;
@@ -225,39 +237,46 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
         const int64_t last = L - 1 - c * kT;
         return (int)(last < kT - 1 ? last : kT - 1);
     };
-    // all copies of block c into buffer bf; rows past the end of the sequence
-    // are clamped to the last valid row (their scores are masked, their state
-    // weight is zero and their outputs are not stored)
+    // All copies of block c into buffer bf.  Copy k of thread tid fills LDS
+    // slot k*256 + tid (16 bytes).  An X copy covers 256/XPR whole rows of one
+    // head and a B/C copy 256/BPR rows, so a thread's row within its copy and
+    // its (swizzled) piece are fixed; only a per-copy uniform row base
+    // changes.  Rows past the end of the sequence are clamped to the last
+    // valid row (their scores are masked, their state weight is zero and
+    // their outputs are not stored).
+    constexpr unsigned XROWS = kThreads / XPR, XCOPIES_PER_HEAD = kT / XROWS;
+    constexpr unsigned BROWS = kThreads / BPR;
+    static_assert(XROWS % XPR == 0 && BROWS % BPR == 0 && XOPS == HW * XCOPIES_PER_HEAD, "copy shape");
+    const unsigned utid = (unsigned)tid;
+    const unsigned xr = utid / XPR, xlp = (utid % XPR) ^ (xr % XPR);   // row in copy, global piece
+    const unsigned br = utid / BPR, blp = (utid % BPR) ^ (br % BPR);
     auto dma_block = [&](int64_t c, int bf) {
-        const int lc = block_last(c);
+        const unsigned lc = (unsigned)block_last(c);
         const int64_t row0 = (int64_t)b * L + c * kT;
-        {   // a: thread -> (step, head)
-            const int t = tid >> 2, hh = tid & 3;
-            const int tr = t <= lc ? t : lc;
-            const int hx = hl0 + hh < HPG ? hl0 + hh : HPG - 1;
-            dma4(a + row0 * H + grp * HPG, (uint32_t)((tr * H + hx) * 4),
+        if (wave < HW) {   // a: thread -> (step, head), 64 * HW values
+            const unsigned t = utid / HW, hh = utid % HW;
+            const unsigned tr = t <= lc ? t : lc;
+            const unsigned hx = hl0 + hh < (unsigned)HPG ? hl0 + hh : HPG - 1;
+            dma4(a + row0 * H + grp * HPG, (tr * (unsigned)H + hx) * 4u,
                  lds_addr(&sA[bf][0]) + (uint32_t)(wave * 256));
         }
         const u16* Xg = X + (row0 * H + grp * HPG) * P;
 #pragma unroll
         for (int k = 0; k < XOPS; ++k) {
-            const int slot = k * kThreads + wave * 64 + lane;
-            const int hh = slot / (kT * XPR), r = (slot / XPR) % kT, pp = slot % XPR;
-            const int lp = pp ^ (r & (XPR - 1));
-            const int tr = r <= lc ? r : lc;
-            const int hx = hl0 + hh < HPG ? hl0 + hh : HPG - 1;
-            dma16(Xg, (uint32_t)(((tr * H + hx) * P + lp * 8) * 2),
+            const unsigned hh = k / XCOPIES_PER_HEAD;
+            const unsigned rr = (k % XCOPIES_PER_HEAD) * XROWS + xr;
+            const unsigned tr = rr <= lc ? rr : lc;
+            const unsigned hx = hl0 + hh < (unsigned)HPG ? hl0 + hh : HPG - 1;
+            dma16(Xg, ((tr * (unsigned)H + hx) * P + xlp * 8) * 2u,
                   lds_addr(&sX[bf][0]) + (uint32_t)((k * kThreads + wave * 64) * 16));
         }
         const u16* Bg = B + (row0 * G + grp) * N;
         const u16* Cg = FULL ? C + (row0 * G + grp) * N : nullptr;
 #pragma unroll
         for (int k = 0; k < BOPS; ++k) {
-            const int slot = k * kThreads + wave * 64 + lane;
-            const int r = slot / BPR, pp = slot % BPR;
-            const int lp = pp ^ (r & (BPR - 1));
-            const int tr = r <= lc ? r : lc;
-            const uint32_t off = (uint32_t)((tr * GN + lp * 8) * 2);
+            const unsigned rr = k * BROWS + br;
+            const unsigned tr = rr <= lc ? rr : lc;
+            const uint32_t off = (tr * (unsigned)GN + blp * 8) * 2u;
             const uint32_t ldo = (uint32_t)((k * kThreads + wave * 64) * 16);
             dma16(Bg, off, lds_addr(&sB[bf][0]) + ldo);
             if constexpr (FULL) dma16(Cg, off, lds_addr(&sC[bf][0]) + ldo);
@@ -265,19 +284,19 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
     };
 
     // ---- carried state: S^T tiles (rows n, columns p), tile (nt, pt) ----
-    f32x16 Sacc[NTL][PT];
+    f32x16 Sacc[NTL][PTW];
 #pragma unroll
     for (int nt = 0; nt < NTL; ++nt)
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt) Sacc[nt][pt] = zero16();
+        for (int pt = 0; pt < PTW; ++pt) Sacc[nt][pt] = zero16();
     if constexpr (FULL) {
         if (src.Sin) {
             const float* S0 = src.Sin + b * src.bstride + seg * src.sstride + (int64_t)h * PN;
 #pragma unroll
             for (int nt = 0; nt < NTL; ++nt)
 #pragma unroll
-                for (int pt = 0; pt < PT; ++pt) {
-                    const float* row = S0 + (int64_t)(pt * 32 + l32) * N + nt * 32 + 4 * g2;
+                for (int pt = 0; pt < PTW; ++pt) {
+                    const float* row = S0 + (int64_t)((pt0 + pt) * 32 + l32) * N + nt * 32 + 4 * g2;
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const float4 v = *reinterpret_cast<const float4*>(row + 8 * q);
@@ -290,8 +309,20 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
         }
     }
     float lam2_total = 0.f;
+    // The true state is 2^ld * Sacc (|ld| <= kRange).  In a block whose
+    // log2-decays stay within kRange of the state scale (the common case) the
+    // decay is never applied to the accumulators: with X~_j = 2^(-ld - cs2_j) X_j
+    //   Y_i     = 2^(cs2_i + ld) * (C_i Sacc + sum_{j<=i} (C_i . B_j) X~_j)
+    //   Sacc'   = Sacc + B^T X~,   ld' = ld + Lam2,
+    // so stages 2 and 5 share one accumulator, the scores need only the causal
+    // mask, and one per-step factor scales the output (every factor stays
+    // within 2^+-kRange).  A block with a larger decay range takes the direct
+    // form: per-element decay of the scores, then Sacc' = 2^(ld + Lam2) Sacc
+    // + B^T (w o X) with ld' = 0.
+    constexpr float kRange = 64.f;
+    float ld = 0.f;
     // previous block's Y^T in bf16: [row block][p tile][4-entry group]
-    uint2 Yb[2][PT][4];
+    uint2 Yb[2][PTW][4];
     auto store_y = [&](int64_t c) {
         if (!hvalid) return;
         const int lc = block_last(c);
@@ -299,9 +330,9 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
         for (int I = 0; I < 2; ++I) {
             const int i = 32 * I + l32;
             if (i <= lc) {
-                u16* yrow = Y + (((int64_t)b * L + c * kT + i) * H + h) * P + 4 * g2;
+                u16* yrow = Y + (((int64_t)b * L + c * kT + i) * H + h) * P + pt0 * 32 + 4 * g2;
 #pragma unroll
-                for (int pt = 0; pt < PT; ++pt)
+                for (int pt = 0; pt < PTW; ++pt)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) *reinterpret_cast<uint2*>(yrow + pt * 32 + 8 * q) = Yb[I][pt][q];
             }
@@ -321,145 +352,38 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
             if (c > c_begin) store_y(c - 1);
         }
 
-        const u16* xT = &sX[bf][wave * kT * P];
+        const u16* xT = &sX[bf][(wave % HW) * kT * P];
         const u16* bT = &sB[bf][0];
 
-        // ---- stage 1: prefix sums of a (lane = step), weights ----
-        const float av = lane <= last ? sA[bf][lane * kHW + wave] : 0.f;
+        // ---- stage 1: prefix sums of a (lane = step), weights (log2 units) ----
+        const float av = lane <= last ? sA[bf][lane * HW + wave % HW] : 0.f;
         const float cs2 = wave_scan64(av, lane) * kLog2e;
         const float lam2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs2), 63));
-        const float ref2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs2), 31));
-        sCs[wave][lane] = cs2;
-        sW[wave][lane] = lane <= last ? fast_exp2(lam2 - cs2) : 0.f;
-        sV[wave][lane] = lane < 32 ? fast_exp2(ref2 - cs2) : 0.f;
+        // sum of |a| bounds every |cs2_j| of the block
+        const float abs2 = __int_as_float(__builtin_amdgcn_readlane(
+                               __float_as_int(wave_scan64(fabsf(av), lane)), 63)) * kLog2e;
         lam2_total += lam2;
-        const float dec = fast_exp2(lam2);
-
-        // X^T fragments (lane = p, k = step in the accumulator row order)
-        bf16x8 Xa[2][2][PT];
-#pragma unroll
-        for (int J = 0; J < 2; ++J)
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                for (int pt = 0; pt < PT; ++pt) {
-                    const int r1 = 32 * J + 16 * ks + 4 * g2 + trow;
-                    Xa[J][ks][pt] = join8(lds_tr4(xT + swz<XPR>(r1, pt * 32 + tcol)),
-                                          lds_tr4(xT + swz<XPR>(r1 + 8, pt * 32 + tcol)));
-                }
-
-        if constexpr (FULL) {
-            const u16* cT = &sC[bf][0];
-            // C fragments of both row blocks (lane = step i, k = n in accumulator row order)
-            bf16x8 Cf[2][NTL][2];
-#pragma unroll
-            for (int I = 0; I < 2; ++I)
-#pragma unroll
-                for (int nt = 0; nt < NTL; ++nt)
-#pragma unroll
-                    for (int hf = 0; hf < 2; ++hf) {
-                        const int row = 32 * I + l32, col = nt * 32 + 16 * hf + 4 * g2;
-                        Cf[I][nt][hf] = join8(*reinterpret_cast<const u32x2*>(cT + swz<BPR>(row, col)),
-                                              *reinterpret_cast<const u32x2*>(cT + swz<BPR>(row, col + 8)));
-                    }
-            // ---- stage 5: Y^T = S_c C^T for both row blocks, then exp(cs_i) ----
-            f32x16 Yt[2][PT];
-#pragma unroll
-            for (int I = 0; I < 2; ++I)
-#pragma unroll
-                for (int pt = 0; pt < PT; ++pt) Yt[I][pt] = zero16();
+        const bool fast = abs2 <= kRange;                    // wave-uniform
+        if (fast && fabsf(ld) + abs2 > kRange) {             // rare: fold the scale into Sacc
+            const float f = fast_exp2(ld);
 #pragma unroll
             for (int nt = 0; nt < NTL; ++nt)
 #pragma unroll
-                for (int pt = 0; pt < PT; ++pt)
-#pragma unroll
-                    for (int hf = 0; hf < 2; ++hf) {
-                        const bf16x8 Sf = acc_half(Sacc[nt][pt], hf);
-#pragma unroll
-                        for (int I = 0; I < 2; ++I) Yt[I][pt] = mfma32(Sf, Cf[I][nt][hf], Yt[I][pt]);
-                    }
-            const float csi0 = sCs[wave][l32], csi1 = sCs[wave][32 + l32];
-            {
-                const float e0 = fast_exp2(csi0), e1 = fast_exp2(csi1);
-#pragma unroll
-                for (int pt = 0; pt < PT; ++pt) {
-                    Yt[0][pt] *= e0;
-                    Yt[1][pt] *= e1;
+                for (int pt = 0; pt < PTW; ++pt) {
+                    Sacc[nt][pt] *= f;
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-            }
-
-            // ---- stage 2: scores S^T = B C^T per 32x32 tile, decay, Y^T += X^T (L o S)^T ----
-            auto scores = [&](int I, int J) {
-                f32x16 St = zero16();
-#pragma unroll
-                for (int nt = 0; nt < NTL; ++nt)
-#pragma unroll
-                    for (int hf = 0; hf < 2; ++hf) {
-                        const int row = 32 * J + l32, col = nt * 32 + 16 * hf + 4 * g2;
-                        const bf16x8 Bf = join8(*reinterpret_cast<const u32x2*>(bT + swz<BPR>(row, col)),
-                                                *reinterpret_cast<const u32x2*>(bT + swz<BPR>(row, col + 8)));
-                        St = mfma32(Bf, Cf[I][nt][hf], St);
-                    }
-                return St;
-            };
-            const f32x16 S00 = scores(0, 0), S10 = scores(1, 0), S11 = scores(1, 1);
-            // row j of accumulator register r: 8(r/4) + 4*g2 + r%4
-            auto diag_apply = [&](const f32x16& St, int I, float csi) {
-                float csj[16];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const f32x4 v = *reinterpret_cast<const f32x4*>(&sCs[wave][32 * I + 8 * q + 4 * g2]);
-                    csj[4 * q] = v[0]; csj[4 * q + 1] = v[1]; csj[4 * q + 2] = v[2]; csj[4 * q + 3] = v[3];
-                }
-                u32x4 pk[2];
-#pragma unroll
-                for (int r = 0; r < 16; r += 2) {
-                    const int j0 = 8 * (r >> 2) + 4 * g2 + (r & 3);
-                    // masked entries (j > i) are replaced, never multiplied
-                    const float v0 = j0 <= l32 ? St[r] * fast_exp2(csi - csj[r]) : 0.f;
-                    const float v1 = j0 + 1 <= l32 ? St[r + 1] * fast_exp2(csi - csj[r + 1]) : 0.f;
-                    pk[r >> 3][(r & 7) >> 1] = pack2(v0, v1);
-                }
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                    for (int pt = 0; pt < PT; ++pt) Yt[I][pt] = mfma32(Xa[I][ks][pt], as_bf16x8(pk[ks]), Yt[I][pt]);
-            };
-            diag_apply(S00, 0, csi0);
-            diag_apply(S11, 1, csi1);
-            {   // off-diagonal tile (I = 1, J = 0)
-                const float ui = fast_exp2(csi1 - ref2);
-                float vj[16];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const f32x4 v = *reinterpret_cast<const f32x4*>(&sV[wave][8 * q + 4 * g2]);
-                    vj[4 * q] = v[0] * ui; vj[4 * q + 1] = v[1] * ui;
-                    vj[4 * q + 2] = v[2] * ui; vj[4 * q + 3] = v[3] * ui;
-                }
-                u32x4 pk[2];
-#pragma unroll
-                for (int r = 0; r < 16; r += 2) pk[r >> 3][(r & 7) >> 1] = pack2(S10[r] * vj[r], S10[r + 1] * vj[r + 1]);
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                    for (int pt = 0; pt < PT; ++pt) Yt[1][pt] = mfma32(Xa[0][ks][pt], as_bf16x8(pk[ks]), Yt[1][pt]);
-            }
-            // Y^T to bf16, stored at the top of the next block (or after the loop)
-#pragma unroll
-            for (int I = 0; I < 2; ++I)
-#pragma unroll
-                for (int pt = 0; pt < PT; ++pt)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        Yb[I][pt][q] = make_uint2(pack2(Yt[I][pt][4 * q], Yt[I][pt][4 * q + 1]),
-                                                  pack2(Yt[I][pt][4 * q + 2], Yt[I][pt][4 * q + 3]));
+            ld = 0.f;
         }
+        const float ld_in = ld;
+        const float wsh = fast ? -ld_in : lam2;              // state weights 2^(wsh - cs2_j)
+        ld = fast ? ld_in + lam2 : 0.f;
+        sCs[wave][lane] = cs2;
+        sW[wave][lane] = lane <= last ? fast_exp2(wsh - cs2) : 0.f;
 
-        // ---- stages 3 + 4: S^T = exp(Lam) S^T + B^T diag(w) X ----
-#pragma unroll
-        for (int nt = 0; nt < NTL; ++nt)
-#pragma unroll
-            for (int pt = 0; pt < PT; ++pt) Sacc[nt][pt] *= dec;
+        // X^T fragments (lane = p, k = step in the accumulator row order) and
+        // the same fragments weighted by sW (the X~ of the state update)
+        bf16x8 Xa[2][2][PTW], Xw[2][2][PTW];
 #pragma unroll
         for (int J = 0; J < 2; ++J)
 #pragma unroll
@@ -470,16 +394,156 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
                 const f32x4 w1 = *reinterpret_cast<const f32x4*>(&sW[wave][k0 + 8]);
                 w[0] = w0[0]; w[1] = w0[1]; w[2] = w0[2]; w[3] = w0[3];
                 w[4] = w1[0]; w[5] = w1[1]; w[6] = w1[2]; w[7] = w1[3];
-                bf16x8 Wx[PT];
 #pragma unroll
-                for (int pt = 0; pt < PT; ++pt) Wx[pt] = scale8(Xa[J][ks][pt], w);
-                const int r1 = k0 + trow;
+                for (int pt = 0; pt < PTW; ++pt) {
+                    const int r1 = k0 + trow;
+                    Xa[J][ks][pt] = join8(lds_tr4(xT + swz<XPR>(r1, (pt0 + pt) * 32 + tcol)),
+                                          lds_tr4(xT + swz<XPR>(r1 + 8, (pt0 + pt) * 32 + tcol)));
+                    Xw[J][ks][pt] = scale8(Xa[J][ks][pt], w);
+                }
+            }
+
+        if constexpr (FULL) {
+            const u16* cT = &sC[bf][0];
+            f32x16 Yt[2][PTW], S00 = zero16(), S10 = zero16(), S11 = zero16();
+#pragma unroll
+            for (int I = 0; I < 2; ++I)
+#pragma unroll
+                for (int pt = 0; pt < PTW; ++pt) Yt[I][pt] = zero16();
+            // Stage 5 (unscaled: Y^T = Sacc C^T) and the stage-2 scores S^T = B C^T
+            // of the three causal 32x32 tiles, one 32-wide slice of the state
+            // dimension at a time, so each C and B fragment is loaded once and
+            // used at once (lane = step, k = n in accumulator row order).
+#pragma unroll
+            for (int nt = 0; nt < NTL; ++nt) {
+                bf16x8 Cf[2][2], Bf[2][2];
+#pragma unroll
+                for (int I = 0; I < 2; ++I)
+#pragma unroll
+                    for (int hf = 0; hf < 2; ++hf) {
+                        const int row = 32 * I + l32, col = nt * 32 + 16 * hf + 4 * g2;
+                        Cf[I][hf] = join8(*reinterpret_cast<const u32x2*>(cT + swz<BPR>(row, col)),
+                                          *reinterpret_cast<const u32x2*>(cT + swz<BPR>(row, col + 8)));
+                        Bf[I][hf] = join8(*reinterpret_cast<const u32x2*>(bT + swz<BPR>(row, col)),
+                                          *reinterpret_cast<const u32x2*>(bT + swz<BPR>(row, col + 8)));
+                    }
+#pragma unroll
+                for (int pt = 0; pt < PTW; ++pt)
+#pragma unroll
+                    for (int hf = 0; hf < 2; ++hf) {
+                        const bf16x8 Sf = acc_half(Sacc[nt][pt], hf);
+#pragma unroll
+                        for (int I = 0; I < 2; ++I) Yt[I][pt] = mfma32(Sf, Cf[I][hf], Yt[I][pt]);
+                    }
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    S00 = mfma32(Bf[0][hf], Cf[0][hf], S00);
+                    S10 = mfma32(Bf[0][hf], Cf[1][hf], S10);
+                    S11 = mfma32(Bf[1][hf], Cf[1][hf], S11);
+                }
+            }
+            const float csi0 = sCs[wave][l32], csi1 = sCs[wave][32 + l32];
+            const float e0 = fast_exp2(csi0 + ld_in), e1 = fast_exp2(csi1 + ld_in);   // output factors
+            // row j of accumulator register r: 8(r/4) + 4*g2 + r%4; masked
+            // entries (j > i) are replaced, never multiplied
+            if (fast) {
+                auto masked = [&](const f32x16& St, int ks) {
+                    u32x4 pk;
+#pragma unroll
+                    for (int e = 0; e < 8; e += 2) {
+                        const int r = 8 * ks + e;
+                        const int j0 = 8 * (r >> 2) + 4 * g2 + (r & 3);
+                        pk[e >> 1] = pack2(j0 <= l32 ? St[r] : 0.f, j0 + 1 <= l32 ? St[r + 1] : 0.f);
+                    }
+                    return as_bf16x8(pk);
+                };
+                auto plain = [&](const f32x16& St, int ks) {
+                    u32x4 pk;
+#pragma unroll
+                    for (int e = 0; e < 8; e += 2) pk[e >> 1] = pack2(St[8 * ks + e], St[8 * ks + e + 1]);
+                    return as_bf16x8(pk);
+                };
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const bf16x8 P00 = masked(S00, ks), P11 = masked(S11, ks), P10 = plain(S10, ks);
+#pragma unroll
+                    for (int pt = 0; pt < PTW; ++pt) {
+                        Yt[0][pt] = mfma32(Xw[0][ks][pt], P00, Yt[0][pt]);
+                        Yt[1][pt] = mfma32(Xw[1][ks][pt], P11, Yt[1][pt]);
+                        Yt[1][pt] = mfma32(Xw[0][ks][pt], P10, Yt[1][pt]);
+                    }
+                }
+#pragma unroll
+                for (int pt = 0; pt < PTW; ++pt) {
+                    Yt[0][pt] *= e0;
+                    Yt[1][pt] *= e1;
+                }
+            } else {
+#pragma unroll
+                for (int pt = 0; pt < PTW; ++pt) {
+                    Yt[0][pt] *= e0;
+                    Yt[1][pt] *= e1;
+                }
+                // decay 2^(cs2_i - cs2_j) applied per element
+                auto decayed = [&](const f32x16& St, int I, int J, float csi) {
+                    float csj[16];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const f32x4 v = *reinterpret_cast<const f32x4*>(&sCs[wave][32 * J + 8 * q + 4 * g2]);
+                        csj[4 * q] = v[0]; csj[4 * q + 1] = v[1]; csj[4 * q + 2] = v[2]; csj[4 * q + 3] = v[3];
+                    }
+                    u32x4 pk[2];
+#pragma unroll
+                    for (int r = 0; r < 16; r += 2) {
+                        const int j0 = 8 * (r >> 2) + 4 * g2 + (r & 3);
+                        const bool diag = I == J;
+                        const float v0 = (!diag || j0 <= l32) ? St[r] * fast_exp2(csi - csj[r]) : 0.f;
+                        const float v1 = (!diag || j0 + 1 <= l32) ? St[r + 1] * fast_exp2(csi - csj[r + 1]) : 0.f;
+                        pk[r >> 3][(r & 7) >> 1] = pack2(v0, v1);
+                    }
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                        for (int pt = 0; pt < PTW; ++pt)
+                            Yt[I][pt] = mfma32(Xa[J][ks][pt], as_bf16x8(pk[ks]), Yt[I][pt]);
+                };
+                decayed(S00, 0, 0, csi0);
+                decayed(S11, 1, 1, csi1);
+                decayed(S10, 1, 0, csi1);
+            }
+            // Y^T to bf16, stored at the top of the next block (or after the loop)
+#pragma unroll
+            for (int I = 0; I < 2; ++I)
+#pragma unroll
+                for (int pt = 0; pt < PTW; ++pt)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        Yb[I][pt][q] = make_uint2(pack2(Yt[I][pt][4 * q], Yt[I][pt][4 * q + 1]),
+                                                  pack2(Yt[I][pt][4 * q + 2], Yt[I][pt][4 * q + 3]));
+        }
+
+        // ---- stages 3 + 4: Sacc' = (direct form: 2^(ld + Lam2)) Sacc + B^T X~ ----
+        if (!fast) {
+            const float f = fast_exp2(ld_in + lam2);
+#pragma unroll
+            for (int nt = 0; nt < NTL; ++nt)
+#pragma unroll
+                for (int pt = 0; pt < PTW; ++pt) {
+                    Sacc[nt][pt] *= f;
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+        }
+#pragma unroll
+        for (int J = 0; J < 2; ++J)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const int r1 = 32 * J + 16 * ks + 4 * g2 + trow;
 #pragma unroll
                 for (int nt = 0; nt < NTL; ++nt) {
                     const bf16x8 Af = join8(lds_tr4(bT + swz<BPR>(r1, nt * 32 + tcol)),
                                             lds_tr4(bT + swz<BPR>(r1 + 8, nt * 32 + tcol)));
 #pragma unroll
-                    for (int pt = 0; pt < PT; ++pt) Sacc[nt][pt] = mfma32(Af, Wx[pt], Sacc[nt][pt]);
+                    for (int pt = 0; pt < PTW; ++pt) Sacc[nt][pt] = mfma32(Af, Xw[J][ks][pt], Sacc[nt][pt]);
                 }
             }
     }
@@ -497,16 +561,17 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
         if (lamseg && lane == 0) lamseg[((int64_t)b * H + h) * nseg_total + seg] = lam2_total * 0.69314718055994531f;
     }
     if (Sdst) {
+        const float f = fast_exp2(ld);
 #pragma unroll
         for (int nt = 0; nt < NTL; ++nt)
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt) {
-                float* row = Sdst + (int64_t)(pt * 32 + l32) * N + nt * 32 + 4 * g2;
+            for (int pt = 0; pt < PTW; ++pt) {
+                float* row = Sdst + (int64_t)((pt0 + pt) * 32 + l32) * N + nt * 32 + 4 * g2;
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
                     *reinterpret_cast<float4*>(row + 8 * q) =
-                        make_float4(Sacc[nt][pt][4 * q], Sacc[nt][pt][4 * q + 1], Sacc[nt][pt][4 * q + 2],
-                                    Sacc[nt][pt][4 * q + 3]);
+                        make_float4(f * Sacc[nt][pt][4 * q], f * Sacc[nt][pt][4 * q + 1],
+                                    f * Sacc[nt][pt][4 * q + 2], f * Sacc[nt][pt][4 * q + 3]);
             }
     }
 }
@@ -515,7 +580,7 @@ bool mfma_supported(int64_t Q, int64_t P, int64_t N) {
     return (Q == 64 || Q == 128 || Q == 256) && (P == 32 || P == 64) && (N == 64 || N == 128);
 }
 
-int64_t mfma_heads_per_workgroup() { return kHW; }
+int64_t mfma_heads_per_workgroup(int64_t P, int64_t N) { return P * N > 4096 ? 2 : 4; }
 
 #define SSD_MFMA_DISPATCH(MACRO)                     \
     if (s.P == 64 && s.N == 128) MACRO(64, 128)      \
@@ -524,9 +589,10 @@ int64_t mfma_heads_per_workgroup() { return kHW; }
     else if (s.P == 32 && s.N == 64) MACRO(32, 64)   \
     else return hipErrorInvalidValue;
 
-// one workgroup per (batch, segment, group, head quad) item, padded to a multiple of the XCD count
+// one workgroup per (batch, segment, group, head set) item, padded to a multiple of the XCD count
 static unsigned grid_for(const FwdShape& s, int64_t nseg) {
-    const int64_t hq = (s.H / s.G + kHW - 1) / kHW;
+    const int64_t hw = mfma_heads_per_workgroup(s.P, s.N);
+    const int64_t hq = (s.H / s.G + hw - 1) / hw;
     const int64_t items = s.Bz * nseg * s.G * hq;
     return (unsigned)(((items + kXcds - 1) / kXcds) * kXcds);
 }

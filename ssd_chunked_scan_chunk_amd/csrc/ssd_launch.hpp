@@ -41,8 +41,8 @@ hipError_t launch_state_scan(const FwdShape& s, int64_t nu, int64_t ustride, con
 
 // ---- MFMA segmented path (bf16) ----------------------------------------------------
 bool mfma_supported(int64_t Q, int64_t P, int64_t N);
-// heads (one per wavefront) sharing B and C in one MFMA workgroup
-int64_t mfma_heads_per_workgroup();
+// heads sharing B and C in one MFMA workgroup (four wavefronts)
+int64_t mfma_heads_per_workgroup(int64_t P, int64_t N);
 // Pass A: for segments [0, nseg_run) of seg_chunks chunks each, the state at
 // the end of the segment starting from zero -> Sseg [Bz][nseg_total][H][P][N]
 // (slot s), and the segment's total log-decay -> lamseg [Bz][H][nseg_total]
