@@ -53,11 +53,12 @@ constexpr int64_t kNumCU = 256;          // MI355X compute units
 constexpr int64_t kLdsPerCU = 160 * 1024;
 
 // LDS of the MFMA kernel's full pass for (P, N): double-buffered 64-step
-// blocks of X for the workgroup's heads, B and C, plus the per-step vectors --
+// blocks of X for the workgroup's heads, B and C, the shared score tiles and
+// the per-step vectors --
 // used to estimate how many workgroups share a CU when planning segments.
 int64_t mfma_lds_bytes(int64_t P, int64_t N) {
     const int64_t T = 64, HW = ssd::mfma_heads_per_workgroup(P, N);
-    return 2 * (HW * T * P * 2 + 2 * T * N * 2 + T * HW * 4) + 2 * 4 * T * 4;
+    return 2 * (HW * T * P * 2 + 2 * T * N * 2 + T * HW * 4) + 3 * 32 * 36 * 2 + 2 * 8 * T * 4;
 }
 
 struct Plan {

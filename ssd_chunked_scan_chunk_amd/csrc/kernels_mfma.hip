@@ -14,21 +14,24 @@
 // Y and the final state do not depend on the block length (every blocking is
 // the same sum, only rounded differently), so the fused kernels block at
 // T = 64 whatever chunk length the caller names: on gfx950 the causal
-// quadratic work of longer blocks costs more MFMA and exponential work than
-// the extra state passes it saves.  A caller's chunk still sets segment
+// quadratic work of longer blocks costs more MFMA and VALU work than the
+// extra state passes it saves.  A caller's chunk still sets segment
 // boundaries (segments are whole chunks).
 //
 // Decomposition on gfx950.
-//  * A workgroup is four wavefronts; wavefront w owns head w of a group of
-//    four heads that share B and C.  The workgroup walks the blocks of one
-//    (batch, segment) and each wave carries its head's fp32 P x N state in
-//    MFMA accumulators, so states never round-trip HBM inside a segment.  All
-//    four waves do identical work: the only synchronisation is one barrier
-//    per block, which publishes the block's copies and frees the other
-//    buffer.  When a launch would leave CUs idle the sequence is split into
-//    segments: a state-only pass (stages 1, 3, 4) gives each segment's end
-//    state from zero, a scan over segments (kernels_scan.hip) gives every
-//    segment's entering state, and the full pass starts from it.
+//  * A workgroup is eight wavefronts, two per SIMD, over the heads of one
+//    group that share B and C.  Each wavefront owns one 32-wide head-dim tile
+//    of one head (P/32 waves per head, 256/P heads per workgroup) and carries
+//    that slice of the head's fp32 state in MFMA accumulators, so states never
+//    round-trip HBM inside a segment and the two waves of a SIMD hide each
+//    other's MFMA, LDS and exponential latencies.  When a launch would leave
+//    CUs idle the sequence is split into segments: a state-only pass (stages
+//    1, 3, 4) gives each segment's end state from zero, a scan over segments
+//    (kernels_scan.hip) gives every segment's entering state, and the full
+//    pass starts from it.
+//  * The masked scores of a block do not depend on the head (the decay is
+//    moved onto X and the output, below), so waves 0-2 form the three causal
+//    32x32 score tiles once per workgroup and share them in LDS as bf16.
 //  * Inputs reach LDS through asynchronous global_load_lds copies (lane L of a
 //    wave-wide copy lands at LDS base + L * size), double buffered one block
 //    ahead, so HBM traffic overlaps the MFMA work and no register holds
@@ -37,30 +40,31 @@
 //    from inserting full vmcnt waits before every LDS access, which would
 //    serialise the prefetch.  A block's Y is stored from registers at the top
 //    of the next block, so the one vmcnt(0) wait per block never waits on
-//    fresh stores.
+//    fresh stores.  Two barriers per block: one publishes the block's copies
+//    (and frees the other buffer), one publishes the shared scores.
 //  * Every product is v_mfma_f32_32x32x16_bf16 (operand lane l holds row or
 //    column l%32 and 8 k values of group l/32; the accumulator holds column
 //    l%32, rows 8(r/4) + 4(l/32) + r%4 in register r).  Contractions use the
 //    k order {4g..4g+3, 8+4g..8+4g+3} within each 16-wide k step (g = l/32),
 //    which is exactly the row order of an accumulator's registers: the fp32
-//    scores and the fp32 state become MFMA operands in place (rounded to
-//    bf16), with no LDS round trip.  Operands with the contraction along
-//    memory rows (X^T, B^T) come from ds_read_b64_tr_b16: in each 16-lane
-//    group, source lane m names row R(m/4), columns 4(m%4)..+3, and output
-//    lane i receives column i of rows R(0..3).
+//    state becomes the stage-5 operand in place (rounded to bf16).  Operands
+//    with the contraction along memory rows (X^T, B^T) come from
+//    ds_read_b64_tr_b16: in each 16-lane group, source lane m names row
+//    R(m/4), columns 4(m%4)..+3, and output lane i receives column i of rows
+//    R(0..3).
 //  * Scores are formed transposed, S^T = B C^T, so lane = step i; outputs are
 //    Y^T tiles, a lane holding 4 consecutive head-dim entries of one step.
 //  * LDS tiles are row-major with the 16-byte pieces of row r stored at
 //    piece ^ (r mod pieces-per-row), so row reads and transposing reads touch
 //    distinct banks.
 //  * Workgroups are dealt to the 8 XCDs in contiguous ranges of (batch,
-//    segment, group, head-quad) items, so the workgroups sharing B and C run
+//    segment, group, head-set) items, so the workgroups sharing B and C run
 //    on one XCD and read them through one L2.
-// Decay factors: within the diagonal 32x32 tiles exp(cs_i - cs_j) is taken
-// directly; for the off-diagonal tile it is exp(cs_i - cs_31) exp(cs_31 - cs_j),
-// both factors at most 1 for a <= 0.  Operand rounding: (Lmask o S), w o X and
-// the entering state are rounded to bf16 for the MFMA; every accumulation and
-// the exp(cs_i) output scaling are fp32.
+// Operand rounding: masked scores, X weighted by the state weights, and the
+// entering state are rounded to bf16 for the MFMA; every accumulation and the
+// per-step output factor are fp32.
+#include <type_traits>
+
 #include "ssd_device.hpp"
 #include "ssd_launch.hpp"
 
@@ -74,27 +78,22 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kXcds = 8;     // MI355X accelerator complex dies; workgroups alternate over them
 constexpr int kT = 64;       // steps per block
-constexpr int kWaves = 4;    // wavefronts per workgroup
+constexpr int kWaves = 8;    // wavefronts per workgroup (two per SIMD)
 constexpr int kThreads = 64 * kWaves;
+constexpr int kPRow = 36;    // padded row (elements) of a shared 32x32 bf16 score tile
 
-// A workgroup holds HW heads of one group; wave w owns head w % HW and the
-// head-dim tiles [(w / HW) * PTW, +PTW).  Four heads per workgroup while a
-// head's fp32 state fits one wave comfortably (P*N <= 4096: 64 accumulator
-// registers); for larger states two heads, each split over two waves by head
-// dim, which halves the accumulators a wave carries.
 template <int P, int N>
 struct MfmaCfg {
-    static constexpr int HW = P * N > 4096 ? 2 : 4;    // heads per workgroup
-    static constexpr int PS = kWaves / HW;               // waves per head
-    static constexpr int PT = P / 32;                    // 32-wide head-dim tiles
-    static constexpr int PTW = PT / PS;                  // ... per wave
+    static constexpr int PS = P / 32;                    // waves per head (one head-dim tile each)
+    static constexpr int HW = kWaves / PS;               // heads per workgroup
     static constexpr int NTL = N / 32;                   // 32-wide state-dim tiles
     static constexpr int XPR = P / 8;                    // 16-byte pieces per X row
     static constexpr int BPR = N / 8;                    // 16-byte pieces per B / C row
     static constexpr int XOPS = HW * kT * XPR / kThreads;  // X copies per thread per block
     static constexpr int BOPS = kT * BPR / kThreads;       // B (or C) copies per thread per block
-    static_assert(P % 32 == 0 && N % 32 == 0 && PTW >= 1, "tile shape");
+    static_assert(P % 32 == 0 && N % 32 == 0 && kWaves % PS == 0, "tile shape");
     static_assert(XOPS >= 1 && BOPS >= 1, "a block must cover the workgroup");
+    static_assert(kThreads % (kT * XPR) == 0 || (kT * XPR) % kThreads == 0, "X copy shape");
 };
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
@@ -196,15 +195,15 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
     int H, int G, int64_t blocks_per_seg, int nseg_grid, int Bz)
 {
     using Cfg = MfmaCfg<P, N>;
-    constexpr int HW = Cfg::HW, PTW = Cfg::PTW, NTL = Cfg::NTL, XPR = Cfg::XPR, BPR = Cfg::BPR;
+    constexpr int HW = Cfg::HW, NTL = Cfg::NTL, XPR = Cfg::XPR, BPR = Cfg::BPR;
     constexpr int XOPS = Cfg::XOPS, BOPS = Cfg::BOPS;
 
     __shared__ __attribute__((aligned(16))) u16 sX[2][HW * kT * P];    // [buf][head][step][p]
     __shared__ __attribute__((aligned(16))) u16 sB[2][kT * N];         // [buf][step][n]
     __shared__ __attribute__((aligned(16))) u16 sC[FULL ? 2 : 1][FULL ? kT * N : 8];
+    __shared__ __attribute__((aligned(16))) u16 sP[FULL ? 3 : 1][FULL ? 32 * kPRow : 8];  // masked scores [i][j]
     __shared__ __attribute__((aligned(16))) float sA[2][kT * HW];      // [buf][step][head]
     __shared__ __attribute__((aligned(16))) float sCs[kWaves][kT];     // per wave: cs * log2(e)
-    __shared__ __attribute__((aligned(16))) float sW[kWaves][kT];      // per wave: state weights, 0 past the end
 
     // ---- work item: contiguous item ranges per XCD (head sets fastest) ----
     const int HPG = H / G;
@@ -223,10 +222,11 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
     const int l32 = lane & 31, g2 = lane >> 5;
     const int trow = (lane & 15) >> 2, tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     const int hl0 = hq * HW;                     // first head of the set within the group
-    const int hlw = hl0 + wave % HW;
-    const int pt0 = (wave / HW) * PTW;           // this wave's first head-dim tile
+    const int hw = wave % HW;                    // this wave's head within the set
+    const int hlw = hl0 + hw;
     const bool hvalid = hlw < HPG;
     const int h = grp * HPG + (hvalid ? hlw : HPG - 1);  // this wave's head (clamped)
+    const int pc = (wave / HW) * 32;             // this wave's first head-dim column
     const int64_t PN = (int64_t)P * N;
     const int64_t nblk = (L + kT - 1) / kT;
     const int64_t c_begin = seg * blocks_per_seg;
@@ -237,18 +237,45 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
         const int64_t last = L - 1 - c * kT;
         return (int)(last < kT - 1 ? last : kT - 1);
     };
+    // Per-lane element offsets into the swizzled LDS tiles, loop invariant.
+    // Tile row bases that are multiples of 16 rows (and so of the swizzle
+    // period) are added per use as immediates.
+    //  roff: row reads of B / C (lane = row l32, 8 bytes at column
+    //        nt*32 + 16hf + 8sec + 4*g2);
+    //  toff: transposing reads of B (source row 4*g2 + trow + 8s, columns
+    //        nt*32 + tcol);  xoff: the same of this wave's X head-dim tile.
+    uint32_t roff[NTL][2][2], toff[NTL][2], xoff[2];
+#pragma unroll
+    for (int nt = 0; nt < NTL; ++nt)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int sec = 0; sec < 2; ++sec)
+                roff[nt][hf][sec] = (uint32_t)swz<BPR>(l32, nt * 32 + 16 * hf + 8 * sec + 4 * g2);
+#pragma unroll
+    for (int sh = 0; sh < 2; ++sh) {
+        const int r = 4 * g2 + trow + 8 * sh;
+#pragma unroll
+        for (int nt = 0; nt < NTL; ++nt) toff[nt][sh] = (uint32_t)swz<BPR>(r, nt * 32 + tcol);
+        xoff[sh] = (uint32_t)swz<XPR>(r, pc + tcol);
+    }
+    auto rowfrag = [&](const u16* tile, int I, int nt, int hf) {   // rows 32I + lane
+        const u16* t = tile + 32 * I * N;
+        return join8(*reinterpret_cast<const u32x2*>(t + roff[nt][hf][0]),
+                     *reinterpret_cast<const u32x2*>(t + roff[nt][hf][1]));
+    };
     // All copies of block c into buffer bf.  Copy k of thread tid fills LDS
-    // slot k*256 + tid (16 bytes).  An X copy covers 256/XPR whole rows of one
-    // head and a B/C copy 256/BPR rows, so a thread's row within its copy and
-    // its (swizzled) piece are fixed; only a per-copy uniform row base
-    // changes.  Rows past the end of the sequence are clamped to the last
-    // valid row (their scores are masked, their state weight is zero and
-    // their outputs are not stored).
-    constexpr unsigned XROWS = kThreads / XPR, XCOPIES_PER_HEAD = kT / XROWS;
-    constexpr unsigned BROWS = kThreads / BPR;
-    static_assert(XROWS % XPR == 0 && BROWS % BPR == 0 && XOPS == HW * XCOPIES_PER_HEAD, "copy shape");
+    // slot k*512 + tid (16 bytes).  A thread's row and (swizzled) piece within
+    // a copy are fixed; only a per-copy uniform row or head base changes.
+    // Rows past the end of the sequence are clamped to the last valid row
+    // (their scores are masked, their state weight is zero and their outputs
+    // are not stored).
+    constexpr unsigned XHT = kT * XPR;                   // slots per head tile
     const unsigned utid = (unsigned)tid;
-    const unsigned xr = utid / XPR, xlp = (utid % XPR) ^ (xr % XPR);   // row in copy, global piece
+    const unsigned xh = utid / XHT, xr = (utid / XPR) % kT;
+    const unsigned xlp = (utid % XPR) ^ (xr % XPR);
+    constexpr unsigned BROWS = kThreads / BPR;
+    static_assert(BROWS % BPR == 0, "copy shape");
     const unsigned br = utid / BPR, blp = (utid % BPR) ^ (br % BPR);
     auto dma_block = [&](int64_t c, int bf) {
         const unsigned lc = (unsigned)block_last(c);
@@ -261,13 +288,12 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
                  lds_addr(&sA[bf][0]) + (uint32_t)(wave * 256));
         }
         const u16* Xg = X + (row0 * H + grp * HPG) * P;
+        const unsigned xtr = xr <= lc ? xr : lc;
 #pragma unroll
         for (int k = 0; k < XOPS; ++k) {
-            const unsigned hh = k / XCOPIES_PER_HEAD;
-            const unsigned rr = (k % XCOPIES_PER_HEAD) * XROWS + xr;
-            const unsigned tr = rr <= lc ? rr : lc;
+            const unsigned hh = (unsigned)(k * kThreads) / XHT + xh;
             const unsigned hx = hl0 + hh < (unsigned)HPG ? hl0 + hh : HPG - 1;
-            dma16(Xg, ((tr * (unsigned)H + hx) * P + xlp * 8) * 2u,
+            dma16(Xg, ((xtr * (unsigned)H + hx) * P + xlp * 8) * 2u,
                   lds_addr(&sX[bf][0]) + (uint32_t)((k * kThreads + wave * 64) * 16));
         }
         const u16* Bg = B + (row0 * G + grp) * N;
@@ -283,29 +309,25 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
         }
     };
 
-    // ---- carried state: S^T tiles (rows n, columns p), tile (nt, pt) ----
-    f32x16 Sacc[NTL][PTW];
+    // ---- carried state: S^T tiles (rows n, columns p of this wave's tile) ----
+    f32x16 Sacc[NTL];
 #pragma unroll
-    for (int nt = 0; nt < NTL; ++nt)
-#pragma unroll
-        for (int pt = 0; pt < PTW; ++pt) Sacc[nt][pt] = zero16();
+    for (int nt = 0; nt < NTL; ++nt) Sacc[nt] = zero16();
     if constexpr (FULL) {
         if (src.Sin) {
             const float* S0 = src.Sin + b * src.bstride + seg * src.sstride + (int64_t)h * PN;
 #pragma unroll
-            for (int nt = 0; nt < NTL; ++nt)
+            for (int nt = 0; nt < NTL; ++nt) {
+                const float* row = S0 + (int64_t)(pc + l32) * N + nt * 32 + 4 * g2;
 #pragma unroll
-                for (int pt = 0; pt < PTW; ++pt) {
-                    const float* row = S0 + (int64_t)((pt0 + pt) * 32 + l32) * N + nt * 32 + 4 * g2;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const float4 v = *reinterpret_cast<const float4*>(row + 8 * q);
-                        Sacc[nt][pt][4 * q + 0] = v.x;
-                        Sacc[nt][pt][4 * q + 1] = v.y;
-                        Sacc[nt][pt][4 * q + 2] = v.z;
-                        Sacc[nt][pt][4 * q + 3] = v.w;
-                    }
+                for (int q = 0; q < 4; ++q) {
+                    const float4 v = *reinterpret_cast<const float4*>(row + 8 * q);
+                    Sacc[nt][4 * q + 0] = v.x;
+                    Sacc[nt][4 * q + 1] = v.y;
+                    Sacc[nt][4 * q + 2] = v.z;
+                    Sacc[nt][4 * q + 3] = v.w;
                 }
+            }
         }
     }
     float lam2_total = 0.f;
@@ -315,26 +337,26 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
     //   Y_i     = 2^(cs2_i + ld) * (C_i Sacc + sum_{j<=i} (C_i . B_j) X~_j)
     //   Sacc'   = Sacc + B^T X~,   ld' = ld + Lam2,
     // so stages 2 and 5 share one accumulator, the scores need only the causal
-    // mask, and one per-step factor scales the output (every factor stays
-    // within 2^+-kRange).  A block with a larger decay range takes the direct
-    // form: per-element decay of the scores, then Sacc' = 2^(ld + Lam2) Sacc
-    // + B^T (w o X) with ld' = 0.
+    // mask (and so are the same for every head), and one per-step factor
+    // scales the output (every factor stays within 2^+-kRange).  A block with a
+    // larger decay range takes the direct form: per-element decay of the shared
+    // scores, then Sacc' = 2^(ld + Lam2) Sacc + B^T (w o X) with ld' = 0.
     constexpr float kRange = 64.f;
     float ld = 0.f;
-    // previous block's Y^T in bf16: [row block][p tile][4-entry group]
-    uint2 Yb[2][PTW][4];
+    // previous block's Y^T in bf16: [row block][4-entry group]
+    uint2 Yb[2][4];
+    // Y of block c: wave-uniform block base plus a 32-bit per-lane offset
+    const uint32_t yoff = (uint32_t)((l32 * H + h) * P + pc + 4 * g2);
     auto store_y = [&](int64_t c) {
         if (!hvalid) return;
         const int lc = block_last(c);
+        u16* yblk = Y + ((int64_t)b * L + c * kT) * H * P;
 #pragma unroll
         for (int I = 0; I < 2; ++I) {
-            const int i = 32 * I + l32;
-            if (i <= lc) {
-                u16* yrow = Y + (((int64_t)b * L + c * kT + i) * H + h) * P + pt0 * 32 + 4 * g2;
+            if (32 * I + l32 <= lc) {
+                u16* yrow = yblk + (yoff + (uint32_t)(32 * I * H * P));
 #pragma unroll
-                for (int pt = 0; pt < PTW; ++pt)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) *reinterpret_cast<uint2*>(yrow + pt * 32 + 8 * q) = Yb[I][pt][q];
+                for (int q = 0; q < 4; ++q) *reinterpret_cast<uint2*>(yrow + 8 * q) = Yb[I][q];
             }
         }
     };
@@ -346,17 +368,17 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
         const int last = block_last(c);
 
         vm_wait_all();  // this wave's copies of block c (and earlier stores) are done
-        sync_lds();     // ... and every wave's; buffer bf^1 is free
+        sync_lds();     // ... and every wave's; buffer bf^1 and the score tiles are free
         if (c + 1 < c_end) dma_block(c + 1, bf ^ 1);
         if constexpr (FULL) {
             if (c > c_begin) store_y(c - 1);
         }
 
-        const u16* xT = &sX[bf][(wave % HW) * kT * P];
+        const u16* xT = &sX[bf][hw * kT * P];
         const u16* bT = &sB[bf][0];
 
         // ---- stage 1: prefix sums of a (lane = step), weights (log2 units) ----
-        const float av = lane <= last ? sA[bf][lane * HW + wave % HW] : 0.f;
+        const float av = lane <= last ? sA[bf][lane * HW + hw] : 0.f;
         const float cs2 = wave_scan64(av, lane) * kLog2e;
         const float lam2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs2), 63));
         // sum of |a| bounds every |cs2_j| of the block
@@ -367,183 +389,158 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
         if (fast && fabsf(ld) + abs2 > kRange) {             // rare: fold the scale into Sacc
             const float f = fast_exp2(ld);
 #pragma unroll
-            for (int nt = 0; nt < NTL; ++nt)
-#pragma unroll
-                for (int pt = 0; pt < PTW; ++pt) {
-                    Sacc[nt][pt] *= f;
-                    __builtin_amdgcn_sched_barrier(0);
-                }
+            for (int nt = 0; nt < NTL; ++nt) Sacc[nt] *= f;
             ld = 0.f;
         }
         const float ld_in = ld;
         const float wsh = fast ? -ld_in : lam2;              // state weights 2^(wsh - cs2_j)
         ld = fast ? ld_in + lam2 : 0.f;
         sCs[wave][lane] = cs2;
-        sW[wave][lane] = lane <= last ? fast_exp2(wsh - cs2) : 0.f;
+        // The state weight of step j is applied to X in place: lane j scales row
+        // j of this wave's head-dim tile (its own 32 columns, 4 pieces), so the
+        // transposing reads that follow yield w o X directly.
+        u16* xTm = &sX[bf][hw * kT * P];
+        auto weight_rows = [&](float wr) {
+            u16* rowp = xTm + lane * P;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int piece = ((pc >> 3) + k) ^ (lane & (XPR - 1));
+                u32x4* q = reinterpret_cast<u32x4*>(rowp + piece * 8);
+                const u32x4 u = *q;
+                u32x4 o;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    o[e] = pack2(wr * __uint_as_float(u[e] << 16), wr * __uint_as_float(u[e] & 0xffff0000u));
+                *q = o;
+            }
+        };
+        const float wrow = lane <= last ? fast_exp2(wsh - cs2) : 0.f;
+        if (fast) weight_rows(wrow);
 
-        // X^T fragments (lane = p, k = step in the accumulator row order) and
-        // the same fragments weighted by sW (the X~ of the state update)
-        bf16x8 Xa[2][2][PTW], Xw[2][2][PTW];
+        if constexpr (FULL) {
+            // ---- shared masked scores: wave t < 3 forms tile t = (I, J) in
+            // {(0,0), (1,0), (1,1)} as S^T = B_J C_I^T, stored [i][j] in bf16 ----
+            if (wave < 3) {
+                const int I = wave > 0 ? 1 : 0, J = wave == 2 ? 1 : 0;
+                const u16* cT = &sC[bf][0];
+                f32x16 St = zero16();
 #pragma unroll
-        for (int J = 0; J < 2; ++J)
+                for (int nt = 0; nt < NTL; ++nt)
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const int k0 = 32 * J + 16 * ks + 4 * g2;
-                float w[8];
-                const f32x4 w0 = *reinterpret_cast<const f32x4*>(&sW[wave][k0]);
-                const f32x4 w1 = *reinterpret_cast<const f32x4*>(&sW[wave][k0 + 8]);
-                w[0] = w0[0]; w[1] = w0[1]; w[2] = w0[2]; w[3] = w0[3];
-                w[4] = w1[0]; w[5] = w1[1]; w[6] = w1[2]; w[7] = w1[3];
+                    for (int hf = 0; hf < 2; ++hf) {
+                        St = mfma32(rowfrag(bT, J, nt, hf), rowfrag(cT, I, nt, hf), St);
+                    }
+                // row j of accumulator register r: 8(r/4) + 4*g2 + r%4; lane = i.
+                // Masked entries (j > i on the diagonal) are replaced, never multiplied.
+                const bool diag = I == J;
+                u16* prow = &sP[wave][l32 * kPRow];
 #pragma unroll
-                for (int pt = 0; pt < PTW; ++pt) {
-                    const int r1 = k0 + trow;
-                    Xa[J][ks][pt] = join8(lds_tr4(xT + swz<XPR>(r1, (pt0 + pt) * 32 + tcol)),
-                                          lds_tr4(xT + swz<XPR>(r1 + 8, (pt0 + pt) * 32 + tcol)));
-                    Xw[J][ks][pt] = scale8(Xa[J][ks][pt], w);
+                for (int q = 0; q < 4; ++q) {
+                    const int j0 = 8 * q + 4 * g2;
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = (!diag || j0 + e <= l32) ? St[4 * q + e] : 0.f;
+                    *reinterpret_cast<uint2*>(prow + j0) = make_uint2(pack2(v[0], v[1]), pack2(v[2], v[3]));
                 }
             }
+        }
+
+        // X^T fragments of this wave's head-dim tile (lane = p, k = step in the
+        // accumulator row order); after weight_rows they are X~ = w o X.
+        auto xfrag = [&](int J, int ks) {
+            const u16* t = xT + (32 * J + 16 * ks) * P;
+            return join8(lds_tr4(t + xoff[0]), lds_tr4(t + xoff[1]));
+        };
 
         if constexpr (FULL) {
             const u16* cT = &sC[bf][0];
-            f32x16 Yt[2][PTW], S00 = zero16(), S10 = zero16(), S11 = zero16();
+            // ---- stage 5 (unscaled): Y^T = Sacc C^T for both row blocks ----
+            f32x16 Yt[2] = {zero16(), zero16()};
 #pragma unroll
-            for (int I = 0; I < 2; ++I)
-#pragma unroll
-                for (int pt = 0; pt < PTW; ++pt) Yt[I][pt] = zero16();
-            // Stage 5 (unscaled: Y^T = Sacc C^T) and the stage-2 scores S^T = B C^T
-            // of the three causal 32x32 tiles, one 32-wide slice of the state
-            // dimension at a time, so each C and B fragment is loaded once and
-            // used at once (lane = step, k = n in accumulator row order).
-#pragma unroll
-            for (int nt = 0; nt < NTL; ++nt) {
-                bf16x8 Cf[2][2], Bf[2][2];
-#pragma unroll
-                for (int I = 0; I < 2; ++I)
-#pragma unroll
-                    for (int hf = 0; hf < 2; ++hf) {
-                        const int row = 32 * I + l32, col = nt * 32 + 16 * hf + 4 * g2;
-                        Cf[I][hf] = join8(*reinterpret_cast<const u32x2*>(cT + swz<BPR>(row, col)),
-                                          *reinterpret_cast<const u32x2*>(cT + swz<BPR>(row, col + 8)));
-                        Bf[I][hf] = join8(*reinterpret_cast<const u32x2*>(bT + swz<BPR>(row, col)),
-                                          *reinterpret_cast<const u32x2*>(bT + swz<BPR>(row, col + 8)));
-                    }
-#pragma unroll
-                for (int pt = 0; pt < PTW; ++pt)
-#pragma unroll
-                    for (int hf = 0; hf < 2; ++hf) {
-                        const bf16x8 Sf = acc_half(Sacc[nt][pt], hf);
-#pragma unroll
-                        for (int I = 0; I < 2; ++I) Yt[I][pt] = mfma32(Sf, Cf[I][hf], Yt[I][pt]);
-                    }
+            for (int nt = 0; nt < NTL; ++nt)
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf) {
-                    S00 = mfma32(Bf[0][hf], Cf[0][hf], S00);
-                    S10 = mfma32(Bf[0][hf], Cf[1][hf], S10);
-                    S11 = mfma32(Bf[1][hf], Cf[1][hf], S11);
-                }
-            }
-            const float csi0 = sCs[wave][l32], csi1 = sCs[wave][32 + l32];
-            const float e0 = fast_exp2(csi0 + ld_in), e1 = fast_exp2(csi1 + ld_in);   // output factors
-            // row j of accumulator register r: 8(r/4) + 4*g2 + r%4; masked
-            // entries (j > i) are replaced, never multiplied
-            if (fast) {
-                auto masked = [&](const f32x16& St, int ks) {
-                    u32x4 pk;
+                    const bf16x8 Sf = acc_half(Sacc[nt], hf);
 #pragma unroll
-                    for (int e = 0; e < 8; e += 2) {
-                        const int r = 8 * ks + e;
-                        const int j0 = 8 * (r >> 2) + 4 * g2 + (r & 3);
-                        pk[e >> 1] = pack2(j0 <= l32 ? St[r] : 0.f, j0 + 1 <= l32 ? St[r + 1] : 0.f);
+                    for (int I = 0; I < 2; ++I) {
+                        Yt[I] = mfma32(Sf, rowfrag(cT, I, nt, hf), Yt[I]);
                     }
-                    return as_bf16x8(pk);
-                };
-                auto plain = [&](const f32x16& St, int ks) {
-                    u32x4 pk;
-#pragma unroll
-                    for (int e = 0; e < 8; e += 2) pk[e >> 1] = pack2(St[8 * ks + e], St[8 * ks + e + 1]);
-                    return as_bf16x8(pk);
-                };
+                }
+            const float e0 = fast_exp2(sCs[wave][l32] + ld_in);        // output factors
+            const float e1 = fast_exp2(sCs[wave][32 + l32] + ld_in);
+
+            sync_lds();  // the shared score tiles are complete
+            // P tile t as the B operand of k step ks (lane = i, k = j)
+            auto ptile = [&](int t, int ks) {
+                const u16* prow = &sP[t][l32 * kPRow + 16 * ks + 4 * g2];
+                return join8(*reinterpret_cast<const u32x2*>(prow), *reinterpret_cast<const u32x2*>(prow + 8));
+            };
+            if (fast) {
+                // ---- stage 2: Y^T += X~^T P, then the per-step factor ----
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
-                    const bf16x8 P00 = masked(S00, ks), P11 = masked(S11, ks), P10 = plain(S10, ks);
-#pragma unroll
-                    for (int pt = 0; pt < PTW; ++pt) {
-                        Yt[0][pt] = mfma32(Xw[0][ks][pt], P00, Yt[0][pt]);
-                        Yt[1][pt] = mfma32(Xw[1][ks][pt], P11, Yt[1][pt]);
-                        Yt[1][pt] = mfma32(Xw[0][ks][pt], P10, Yt[1][pt]);
-                    }
+                    const bf16x8 xw0 = xfrag(0, ks), xw1 = xfrag(1, ks);
+                    Yt[0] = mfma32(xw0, ptile(0, ks), Yt[0]);
+                    Yt[1] = mfma32(xw0, ptile(1, ks), Yt[1]);
+                    Yt[1] = mfma32(xw1, ptile(2, ks), Yt[1]);
                 }
-#pragma unroll
-                for (int pt = 0; pt < PTW; ++pt) {
-                    Yt[0][pt] *= e0;
-                    Yt[1][pt] *= e1;
-                }
+                Yt[0] *= e0;
+                Yt[1] *= e1;
             } else {
+                Yt[0] *= e0;
+                Yt[1] *= e1;
+                // ---- stage 2, direct form: decay 2^(cs2_i - cs2_j) on the shared scores ----
+                // (masked entries stay replaced by zero: their exponent may overflow)
+                auto decayed = [&](int t, int J, int ks, float csi) {
+                    const u32x4 u = as_u32x4(ptile(t, ks));
+                    const int jl = 16 * ks + 4 * g2;              // j within the tile, element 0
+                    const f32x4 c0 = *reinterpret_cast<const f32x4*>(&sCs[wave][32 * J + jl]);
+                    const f32x4 c1 = *reinterpret_cast<const f32x4*>(&sCs[wave][32 * J + jl + 8]);
+                    const float cj[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+                    const bool diag = t != 1;
+                    float v[8];
 #pragma unroll
-                for (int pt = 0; pt < PTW; ++pt) {
-                    Yt[0][pt] *= e0;
-                    Yt[1][pt] *= e1;
-                }
-                // decay 2^(cs2_i - cs2_j) applied per element
-                auto decayed = [&](const f32x16& St, int I, int J, float csi) {
-                    float csj[16];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const f32x4 v = *reinterpret_cast<const f32x4*>(&sCs[wave][32 * J + 8 * q + 4 * g2]);
-                        csj[4 * q] = v[0]; csj[4 * q + 1] = v[1]; csj[4 * q + 2] = v[2]; csj[4 * q + 3] = v[3];
+                    for (int e = 0; e < 8; ++e) {
+                        const int j = jl + (e < 4 ? e : 4 + e);
+                        const float x = __uint_as_float(e & 1 ? (u[e >> 1] & 0xffff0000u) : (u[e >> 1] << 16));
+                        v[e] = (!diag || j <= l32) ? x * fast_exp2(csi - cj[e]) : 0.f;
                     }
-                    u32x4 pk[2];
-#pragma unroll
-                    for (int r = 0; r < 16; r += 2) {
-                        const int j0 = 8 * (r >> 2) + 4 * g2 + (r & 3);
-                        const bool diag = I == J;
-                        const float v0 = (!diag || j0 <= l32) ? St[r] * fast_exp2(csi - csj[r]) : 0.f;
-                        const float v1 = (!diag || j0 + 1 <= l32) ? St[r + 1] * fast_exp2(csi - csj[r + 1]) : 0.f;
-                        pk[r >> 3][(r & 7) >> 1] = pack2(v0, v1);
-                    }
-#pragma unroll
-                    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                        for (int pt = 0; pt < PTW; ++pt)
-                            Yt[I][pt] = mfma32(Xa[J][ks][pt], as_bf16x8(pk[ks]), Yt[I][pt]);
+                    return as_bf16x8(u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])});
                 };
-                decayed(S00, 0, 0, csi0);
-                decayed(S11, 1, 1, csi1);
-                decayed(S10, 1, 0, csi1);
+                const float csi0 = sCs[wave][l32], csi1 = sCs[wave][32 + l32];
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const bf16x8 xa0 = xfrag(0, ks), xa1 = xfrag(1, ks);
+                    Yt[0] = mfma32(xa0, decayed(0, 0, ks, csi0), Yt[0]);
+                    Yt[1] = mfma32(xa0, decayed(1, 0, ks, csi1), Yt[1]);
+                    Yt[1] = mfma32(xa1, decayed(2, 1, ks, csi1), Yt[1]);
+                }
             }
             // Y^T to bf16, stored at the top of the next block (or after the loop)
 #pragma unroll
             for (int I = 0; I < 2; ++I)
 #pragma unroll
-                for (int pt = 0; pt < PTW; ++pt)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        Yb[I][pt][q] = make_uint2(pack2(Yt[I][pt][4 * q], Yt[I][pt][4 * q + 1]),
-                                                  pack2(Yt[I][pt][4 * q + 2], Yt[I][pt][4 * q + 3]));
+                for (int q = 0; q < 4; ++q)
+                    Yb[I][q] = make_uint2(pack2(Yt[I][4 * q], Yt[I][4 * q + 1]), pack2(Yt[I][4 * q + 2], Yt[I][4 * q + 3]));
         }
 
         // ---- stages 3 + 4: Sacc' = (direct form: 2^(ld + Lam2)) Sacc + B^T X~ ----
         if (!fast) {
+            weight_rows(wrow);   // after the direct-form stage 2, which reads X unweighted
             const float f = fast_exp2(ld_in + lam2);
 #pragma unroll
-            for (int nt = 0; nt < NTL; ++nt)
-#pragma unroll
-                for (int pt = 0; pt < PTW; ++pt) {
-                    Sacc[nt][pt] *= f;
-                    __builtin_amdgcn_sched_barrier(0);
-                }
+            for (int nt = 0; nt < NTL; ++nt) Sacc[nt] *= f;
         }
 #pragma unroll
         for (int J = 0; J < 2; ++J)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const int r1 = 32 * J + 16 * ks + 4 * g2 + trow;
+                const bf16x8 xw = xfrag(J, ks);
 #pragma unroll
                 for (int nt = 0; nt < NTL; ++nt) {
-                    const bf16x8 Af = join8(lds_tr4(bT + swz<BPR>(r1, nt * 32 + tcol)),
-                                            lds_tr4(bT + swz<BPR>(r1 + 8, nt * 32 + tcol)));
-#pragma unroll
-                    for (int pt = 0; pt < PTW; ++pt) Sacc[nt][pt] = mfma32(Af, Xw[J][ks][pt], Sacc[nt][pt]);
+                    const u16* t = bT + (32 * J + 16 * ks) * N;
+                    const bf16x8 Af = join8(lds_tr4(t + toff[nt][0]), lds_tr4(t + toff[nt][1]));
+                    Sacc[nt] = mfma32(Af, xw, Sacc[nt]);
                 }
             }
     }
@@ -558,21 +555,20 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
         if (S_fin && seg == nseg_grid - 1) Sdst = S_fin + ((int64_t)b * H + h) * PN;
     } else {
         Sdst = Sseg + (((int64_t)b * nseg_total + seg) * H + h) * PN;
-        if (lamseg && lane == 0) lamseg[((int64_t)b * H + h) * nseg_total + seg] = lam2_total * 0.69314718055994531f;
+        if (lamseg && lane == 0 && pc == 0)
+            lamseg[((int64_t)b * H + h) * nseg_total + seg] = lam2_total * 0.69314718055994531f;
     }
     if (Sdst) {
         const float f = fast_exp2(ld);
 #pragma unroll
-        for (int nt = 0; nt < NTL; ++nt)
+        for (int nt = 0; nt < NTL; ++nt) {
+            float* row = Sdst + (int64_t)(pc + l32) * N + nt * 32 + 4 * g2;
 #pragma unroll
-            for (int pt = 0; pt < PTW; ++pt) {
-                float* row = Sdst + (int64_t)((pt0 + pt) * 32 + l32) * N + nt * 32 + 4 * g2;
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    *reinterpret_cast<float4*>(row + 8 * q) =
-                        make_float4(f * Sacc[nt][pt][4 * q], f * Sacc[nt][pt][4 * q + 1],
-                                    f * Sacc[nt][pt][4 * q + 2], f * Sacc[nt][pt][4 * q + 3]);
-            }
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<float4*>(row + 8 * q) =
+                    make_float4(f * Sacc[nt][4 * q], f * Sacc[nt][4 * q + 1], f * Sacc[nt][4 * q + 2],
+                                f * Sacc[nt][4 * q + 3]);
+        }
     }
 }
 
@@ -580,7 +576,7 @@ bool mfma_supported(int64_t Q, int64_t P, int64_t N) {
     return (Q == 64 || Q == 128 || Q == 256) && (P == 32 || P == 64) && (N == 64 || N == 128);
 }
 
-int64_t mfma_heads_per_workgroup(int64_t P, int64_t N) { return P * N > 4096 ? 2 : 4; }
+int64_t mfma_heads_per_workgroup(int64_t P, int64_t N) { (void)N; return kWaves / (P / 32); }
 
 #define SSD_MFMA_DISPATCH(MACRO)                     \
     if (s.P == 64 && s.N == 128) MACRO(64, 128)      \
