@@ -277,36 +277,48 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
     constexpr unsigned BROWS = kThreads / BPR;
     static_assert(BROWS % BPR == 0, "copy shape");
     const unsigned br = utid / BPR, blp = (utid % BPR) ^ (br % BPR);
-    auto dma_block = [&](int64_t c, int bf) {
+    // The copies of a block are issued in four parts spread over the previous
+    // block's work (a and the first half of X; the rest of X; B; C): issued
+    // together they fill the CU's memory queue and stall every wave until the
+    // transfer drains, while spread out they overlap the MFMA and VALU work.
+    auto dma_part = [&](int64_t c, int bf, int part) {
         const unsigned lc = (unsigned)block_last(c);
         const int64_t row0 = (int64_t)b * L + c * kT;
-        if (wave < HW) {   // a: thread -> (step, head), 64 * HW values
+        if (part == 0 && wave < HW) {   // a: thread -> (step, head), 64 * HW values
             const unsigned t = utid / HW, hh = utid % HW;
             const unsigned tr = t <= lc ? t : lc;
             const unsigned hx = hl0 + hh < (unsigned)HPG ? hl0 + hh : HPG - 1;
             dma4(a + row0 * H + grp * HPG, (tr * (unsigned)H + hx) * 4u,
                  lds_addr(&sA[bf][0]) + (uint32_t)(wave * 256));
         }
-        const u16* Xg = X + (row0 * H + grp * HPG) * P;
-        const unsigned xtr = xr <= lc ? xr : lc;
+        if (part <= 1) {
+            const u16* Xg = X + (row0 * H + grp * HPG) * P;
+            const unsigned xtr = xr <= lc ? xr : lc;
 #pragma unroll
-        for (int k = 0; k < XOPS; ++k) {
-            const unsigned hh = (unsigned)(k * kThreads) / XHT + xh;
-            const unsigned hx = hl0 + hh < (unsigned)HPG ? hl0 + hh : HPG - 1;
-            dma16(Xg, ((xtr * (unsigned)H + hx) * P + xlp * 8) * 2u,
-                  lds_addr(&sX[bf][0]) + (uint32_t)((k * kThreads + wave * 64) * 16));
-        }
-        const u16* Bg = B + (row0 * G + grp) * N;
-        const u16* Cg = FULL ? C + (row0 * G + grp) * N : nullptr;
+            for (int k = 0; k < XOPS; ++k) {
+                if ((k < (XOPS + 1) / 2) != (part == 0)) continue;
+                const unsigned hh = (unsigned)(k * kThreads) / XHT + xh;
+                const unsigned hx = hl0 + hh < (unsigned)HPG ? hl0 + hh : HPG - 1;
+                dma16(Xg, ((xtr * (unsigned)H + hx) * P + xlp * 8) * 2u,
+                      lds_addr(&sX[bf][0]) + (uint32_t)((k * kThreads + wave * 64) * 16));
+            }
+        } else {
+            const u16* Tg = (part == 2 ? B : C) + (row0 * G + grp) * N;
+            const u16* tile = part == 2 ? &sB[bf][0] : &sC[FULL ? bf : 0][0];
 #pragma unroll
-        for (int k = 0; k < BOPS; ++k) {
-            const unsigned rr = k * BROWS + br;
-            const unsigned tr = rr <= lc ? rr : lc;
-            const uint32_t off = (tr * (unsigned)GN + blp * 8) * 2u;
-            const uint32_t ldo = (uint32_t)((k * kThreads + wave * 64) * 16);
-            dma16(Bg, off, lds_addr(&sB[bf][0]) + ldo);
-            if constexpr (FULL) dma16(Cg, off, lds_addr(&sC[bf][0]) + ldo);
+            for (int k = 0; k < BOPS; ++k) {
+                const unsigned rr = k * BROWS + br;
+                const unsigned tr = rr <= lc ? rr : lc;
+                dma16(Tg, (tr * (unsigned)GN + blp * 8) * 2u,
+                      lds_addr(tile) + (uint32_t)((k * kThreads + wave * 64) * 16));
+            }
         }
+    };
+    auto dma_block = [&](int64_t c, int bf) {
+        dma_part(c, bf, 0);
+        dma_part(c, bf, 1);
+        dma_part(c, bf, 2);
+        if constexpr (FULL) dma_part(c, bf, 3);
     };
 
     // ---- carried state: S^T tiles (rows n, columns p of this wave's tile) ----
@@ -343,22 +355,21 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
     // scores, then Sacc' = 2^(ld + Lam2) Sacc + B^T (w o X) with ld' = 0.
     constexpr float kRange = 64.f;
     float ld = 0.f;
-    // previous block's Y^T in bf16: [row block][4-entry group]
+    // This block's Y^T in bf16 ([row block][4-entry group]; lane = step), and
+    // the previous block's Y re-laid out through LDS so that copy k of a lane
+    // holds 16 contiguous bytes of step 16k + lane/4: a store then covers 16
+    // steps x 64 bytes instead of 64 scattered 8-byte pieces.
     uint2 Yb[2][4];
-    // Y of block c: wave-uniform block base plus a 32-bit per-lane offset
-    const uint32_t yoff = (uint32_t)((l32 * H + h) * P + pc + 4 * g2);
+    u32x4 Yr[4];
+    const uint32_t yoff = (uint32_t)(((lane >> 2) * H + h) * P + pc + 8 * (lane & 3));
     auto store_y = [&](int64_t c) {
         if (!hvalid) return;
         const int lc = block_last(c);
         u16* yblk = Y + ((int64_t)b * L + c * kT) * H * P;
 #pragma unroll
-        for (int I = 0; I < 2; ++I) {
-            if (32 * I + l32 <= lc) {
-                u16* yrow = yblk + (yoff + (uint32_t)(32 * I * H * P));
-#pragma unroll
-                for (int q = 0; q < 4; ++q) *reinterpret_cast<uint2*>(yrow + 8 * q) = Yb[I][q];
-            }
-        }
+        for (int k = 0; k < 4; ++k)
+            if (16 * k + (lane >> 2) <= lc)
+                *reinterpret_cast<u32x4*>(yblk + (yoff + (uint32_t)(16 * k * H * P))) = Yr[k];
     };
 
     if (c_begin < c_end) dma_block(c_begin, 0);
@@ -369,7 +380,8 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
 
         vm_wait_all();  // this wave's copies of block c (and earlier stores) are done
         sync_lds();     // ... and every wave's; buffer bf^1 and the score tiles are free
-        if (c + 1 < c_end) dma_block(c + 1, bf ^ 1);
+        const bool has_next = c + 1 < c_end;
+        if (has_next) dma_part(c + 1, bf ^ 1, 0);
         if constexpr (FULL) {
             if (c > c_begin) store_y(c - 1);
         }
@@ -416,6 +428,7 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
         };
         const float wrow = lane <= last ? fast_exp2(wsh - cs2) : 0.f;
         if (fast) weight_rows(wrow);
+        if (has_next) dma_part(c + 1, bf ^ 1, 1);
 
         if constexpr (FULL) {
             // ---- shared masked scores: wave t < 3 forms tile t = (I, J) in
@@ -469,7 +482,9 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
             const float e0 = fast_exp2(sCs[wave][l32] + ld_in);        // output factors
             const float e1 = fast_exp2(sCs[wave][32 + l32] + ld_in);
 
+            if (has_next) dma_part(c + 1, bf ^ 1, 2);
             sync_lds();  // the shared score tiles are complete
+            if (has_next) dma_part(c + 1, bf ^ 1, 3);
             // P tile t as the B operand of k step ks (lane = i, k = j)
             auto ptile = [&](int t, int ks) {
                 const u16* prow = &sP[t][l32 * kPRow + 16 * ks + 4 * g2];
@@ -524,6 +539,9 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
                     Yb[I][q] = make_uint2(pack2(Yt[I][4 * q], Yt[I][4 * q + 1]), pack2(Yt[I][4 * q + 2], Yt[I][4 * q + 3]));
         }
 
+        if constexpr (!FULL) {
+            if (has_next) dma_part(c + 1, bf ^ 1, 2);
+        }
         // ---- stages 3 + 4: Sacc' = (direct form: 2^(ld + Lam2)) Sacc + B^T X~ ----
         if (!fast) {
             weight_rows(wrow);   // after the direct-form stage 2, which reads X unweighted
@@ -543,6 +561,17 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
                     Sacc[nt] = mfma32(Af, xw, Sacc[nt]);
                 }
             }
+        if constexpr (FULL) {
+            // Y^T through this wave's own X slice, which is dead after stage 3
+#pragma unroll
+            for (int I = 0; I < 2; ++I)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<uint2*>(xTm + swz<XPR>(32 * I + l32, pc + 8 * q + 4 * g2)) = Yb[I][q];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                Yr[k] = *reinterpret_cast<const u32x4*>(xTm + swz<XPR>(16 * k + (lane >> 2), pc + 8 * (lane & 3)));
+        }
     }
     if constexpr (FULL) {
         if (c_begin < c_end) store_y(c_end - 1);
