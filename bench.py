@@ -11,8 +11,12 @@ Infinity Cache.
 Prints ONE JSON line.  Besides the contract fields it carries:
   roofline      the dominant kernel (the MFMA full pass) against the HBM peak,
                 from algorithmic bytes and that kernel's own launch duration,
-                measured with HIP events on the launch stream;
-  mfma          algorithmic MFMA flops of the step against the bf16 dense peak;
+                measured with HIP events on the launch stream (the pass is
+                launched alone through the stage entry point, in the same
+                segment configuration the step uses);
+  passes        the step's three launches timed one by one the same way;
+  mfma          MFMA flops of the step (the 64-step blocking the kernels run)
+                against the bf16 dense peak;
   cpu_baseline  the fp64 CPU oracle on the same workload (host cores);
   secondary     the other workloads of the metric: the 2.7B-shaped layer,
                 the state-64 sweep at seqlen 32K, and the decode step's
@@ -39,10 +43,14 @@ def fwd_algo_bytes_per_token(sh):
     return sh.nheads * sh.headdim * 2 * es + 2 * sh.ngroups * sh.dstate * es + 4 * sh.nheads
 
 
-def fwd_algo_flops_per_token(sh):
-    """Algorithmic MFMA flops per token: causal half of C B^T once per group,
-    causal half of (L o S) X per head, chunk state and state-to-output per head."""
-    Q, N, P, H, G = sh.chunk, sh.dstate, sh.headdim, sh.nheads, sh.ngroups
+KERNEL_BLOCK = 64   # the fused kernels' block length (the output does not depend on it)
+
+
+def fwd_algo_flops_per_token(sh, block=KERNEL_BLOCK):
+    """MFMA flops per token of the blocked form with blocks of `block` steps:
+    causal half of C B^T once per group, causal half of (L o S) X per head,
+    block state and state-to-output per head."""
+    Q, N, P, H, G = block, sh.dstate, sh.headdim, sh.nheads, sh.ngroups
     return (Q + 1) * (N * G + P * H) + 4 * N * P * H
 
 
@@ -112,32 +120,46 @@ def bench_forward(sh, steps, warmup, nbatch, seed0=0):
         step(i)
     t_step = time_events(step, steps) / steps
 
-    # the dominant kernel alone, in the launch configuration the step uses
+    # the step's launches one by one, in the configuration the step uses: the
+    # state-only pass over the segments, the segment scan, and the full pass
+    # (the dominant kernel) fed entering states (their values do not change
+    # the work)
     algo, seg_chunks, nseg = plan
-    if nseg == 1:
-        t_kernel = t_step               # the step is that single launch
-    elif seg_chunks == 1:
-        # full pass with one chunk per workgroup, fed the entering states
-        states = []
-        for g in batches:
-            dS = ssd.chunk_state(g["X"], g["a"], g["B"], sh.chunk)
-            _, lam = ssd.chunk_cumsum(g["a"], sh.chunk)
-            Sin, _ = ssd.state_passing(dS, lam, sh.chunk, sh.seqlen, return_final_state=False)
-            states.append(Sin)
+    passes = {}
+    if algo == ssd.SSD_ALGO_MFMA:
+        Bz, H, P, N = sh.batch, sh.nheads, sh.headdim, sh.dstate
+        Sin = torch.zeros((Bz, nseg, H, P, N), dtype=torch.float32, device="cuda")
 
-        def kern(i):
+        def full(i):
             g = batches[i % nbatch]
-            ssd.chunk_scan(g["X"], g["a"], g["B"], g["C"], sh.chunk, states_in=states[i % nbatch])
+            ssd.chunk_scan(g["X"], g["a"], g["B"], g["C"], sh.chunk, states_in=Sin,
+                           seg_chunks=seg_chunks, Y=Ys[i % nbatch])
 
         for i in range(warmup):
-            kern(i)
-        t_kernel = time_events(kern, steps) / steps
-        del states
-    else:
-        t_kernel = None
+            full(i)
+        passes["full_pass_ms"] = time_events(full, steps) / steps * 1e3
+        if nseg > 1:
+            dS = torch.empty((Bz, nseg, H, P, N), dtype=torch.float32, device="cuda")
+            lam_u = torch.zeros((Bz, H, nseg), dtype=torch.float32, device="cuda")
+
+            def state(i):
+                g = batches[i % nbatch]
+                ssd.chunk_state(g["X"], g["a"], g["B"], sh.chunk, seg_chunks=seg_chunks, out=dS)
+
+            def scan(i):
+                ssd.state_passing(dS, lam_u, sh.chunk, sh.seqlen, out=Sin, return_final_state=False,
+                                  seg_chunks=seg_chunks)
+
+            for fn, key in ((state, "state_pass_ms"), (scan, "segment_scan_ms")):
+                for i in range(warmup):
+                    fn(i)
+                passes[key] = time_events(fn, steps) / steps * 1e3
+            del dS, lam_u
+        del Sin
+    t_kernel = passes.get("full_pass_ms", 0.0) / 1e3 or None
     del batches, Ys
     torch.cuda.empty_cache()
-    return t_step, t_kernel, plan
+    return t_step, t_kernel, plan, passes
 
 
 def bench_decode(steps, warmup):
@@ -223,7 +245,7 @@ def main():
     tokens = sh.batch * sh.seqlen
     per_batch = tokens * fwd_algo_bytes_per_token(sh)
     nbatch = max(2, int(np.ceil(2 * 256e6 / per_batch)))   # > 2x the Infinity Cache
-    t_step, t_kernel, plan = bench_forward(sh, args.steps, args.warmup, nbatch)
+    t_step, t_kernel, plan, passes = bench_forward(sh, args.steps, args.warmup, nbatch)
 
     algo_bytes = tokens * fwd_algo_bytes_per_token(sh)
     algo_flops = tokens * fwd_algo_flops_per_token(sh)
@@ -248,6 +270,7 @@ def main():
                      "frac": (achieved / HBM_PEAK_GBS) if achieved else None, "traffic": stored_traffic(),
                      "kernel": "k_mfma_seg full pass", "kernel_ms": t_kernel * 1e3 if t_kernel else None,
                      "algo_bytes_per_launch": algo_bytes},
+        "passes": passes,
         "mfma": {"achieved": algo_flops / t_step / 1e12, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                  "frac": algo_flops / t_step / 1e12 / BF16_PEAK_TFLOPS,
                  "algo_flops_per_step": algo_flops},
@@ -258,11 +281,13 @@ def main():
         for name, shp in (("m2_2p7b", si.FWD_CONFIGS["m2_2p7b"]), ("sweep_n64_L32768", si.sweep_shape(32768))):
             tok = shp.batch * shp.seqlen
             nb = max(1, int(np.ceil(2 * 256e6 / (tok * fwd_algo_bytes_per_token(shp)))))
-            ts, tk, pl = bench_forward(shp, max(5, args.steps // 5), 2, nb)
+            ts, tk, pl, ps = bench_forward(shp, max(5, args.steps // 5), 2, nb)
             fl = tok * fwd_algo_flops_per_token(shp)
             sec[name] = {"tokens_per_s": tok / ts, "ms_per_step": ts * 1e3,
                          "hbm_frac": tok * fwd_algo_bytes_per_token(shp) / ts / 1e9 / HBM_PEAK_GBS,
-                         "mfma_frac": fl / ts / 1e12 / BF16_PEAK_TFLOPS, "plan": list(pl)}
+                         "mfma_frac": fl / ts / 1e12 / BF16_PEAK_TFLOPS, "plan": list(pl),
+                         "full_pass_hbm_frac": (tok * fwd_algo_bytes_per_token(shp) / tk / 1e9 / HBM_PEAK_GBS
+                                                if tk else None), "passes": ps}
         td, nbytes = bench_decode(max(20, args.steps), 5)
         sec["decode_step"] = {"workload": "batch 256, 80 heads, headdim 64, dstate 128, fp32 state in place",
                               "us_per_step": td * 1e6, "GB_per_s": nbytes / td / 1e9,

@@ -120,8 +120,12 @@ ssd_status ssd_step(const ssd_step_desc* desc, float* state, const void* x, cons
                     const void* B, const void* C, void* y, void* stream);
 
 /* ---- Stage entry points (the same kernels' building blocks, exposed so
- * each stage can be checked on its own).  bf16 MFMA path only, except
- * ssd_chunk_cumsum which takes any dtype descriptor. ---- */
+ * each stage can be checked and timed on its own).  bf16 MFMA path only,
+ * except ssd_chunk_cumsum which takes any dtype descriptor.  Stages 3-5 work
+ * on units of desc->seg_chunks consecutive chunks (0 or 1: one chunk per
+ * unit; the last unit may be shorter): U = ceil(nchunks / units) units, the
+ * grouping the full forward's segments use.  Per-unit arrays are indexed by
+ * the unit u in place of the chunk c. ---- */
 
 /* Stage 1, segment sums: cs[b][h][c][i] = a_{cQ} + ... + a_{cQ+i} (fp32
  * wavefront prefix sums; entries past a ragged end are 0) and
@@ -129,22 +133,24 @@ ssd_status ssd_step(const ssd_step_desc* desc, float* state, const void* x, cons
 ssd_status ssd_chunk_cumsum(const ssd_fwd_desc* desc, const float* a, float* cs, float* lam,
                             void* stream);
 
-/* Stage 3, chunk states: dstates[b][c][h][p][n] =
- * sum_j exp(a_{j+1} + ... + a_{end of chunk}) X_j[p] B_j[n] over the chunk. */
+/* Stage 3, chunk states: dstates[b][u][h][p][n] =
+ * sum_j exp(a_{j+1} + ... + a_{end of unit}) X_j[p] B_j[n] over the unit. */
 ssd_status ssd_chunk_state(const ssd_fwd_desc* desc, const void* X, const float* a,
                            const void* B, float* dstates, void* stream);
 
 /* Stage 4, inter-chunk state scan: states_in[b][0][h] = initial_state (or 0),
- * states_in[b][c+1][h] = exp(lam[b][h][c]) states_in[b][c][h] + dstates[b][c][h];
- * final_state (optional) receives the state after the last chunk.
+ * states_in[b][u+1][h] = exp(lam[b][h][u]) states_in[b][u][h] + dstates[b][u][h],
+ * with lam[b][h][u] the unit's total log-decay (the sum of its chunks' lam);
+ * final_state (optional) receives the state after the last unit.
  * states_in may alias dstates exactly (in-place scan). */
 ssd_status ssd_state_passing(const ssd_fwd_desc* desc, const float* dstates, const float* lam,
                              const float* initial_state, float* states_in, float* final_state,
                              void* stream);
 
-/* Stages 2 and 5, chunk output: Y = intra-chunk masked product + exp(cs) *
- * (C states_in^T) per chunk, written once.  states_in NULL means zero states
- * (Y is then the intra-chunk part alone). */
+/* Stages 2 and 5, chunk output: Y = masked product inside the unit + exp(cs) *
+ * (C states_in^T) per unit, written once, with states_in[b][u][h] the state
+ * entering unit u.  states_in NULL means zero states (Y is then the part
+ * from inside each unit alone). */
 ssd_status ssd_chunk_scan(const ssd_fwd_desc* desc, const void* X, const float* a,
                           const void* B, const void* C, const float* states_in, void* Y,
                           void* stream);

@@ -127,23 +127,28 @@ def chunk_cumsum(a, chunk):
     return cs, lam
 
 
-def chunk_state(X, a, B, chunk):
-    """Stage 3: per-chunk states dS [Bz,nc,H,P,N] f32."""
+def chunk_state(X, a, B, chunk, seg_chunks=1, out=None):
+    """Stage 3: states built inside each unit of `seg_chunks` chunks from a
+    zero state, dS [Bz,U,H,P,N] f32 (U = number of units)."""
     Bz, L, H, P = X.shape
     N = B.shape[3]
     nc = (L + int(chunk) - 1) // int(chunk)
-    d = _desc(X, B, chunk, SSD_ALGO_MFMA, 1)
-    out = torch.empty((Bz, nc, H, P, N), dtype=torch.float32, device=X.device)
+    k = max(1, int(seg_chunks))
+    d = _desc(X, B, chunk, SSD_ALGO_MFMA, k)
+    if out is None:
+        out = torch.empty((Bz, (nc + k - 1) // k, H, P, N), dtype=torch.float32, device=X.device)
     _lib.check(_L().ssd_chunk_state(ctypes.byref(d), _ptr(X), _ptr(a), _ptr(B), _ptr(out),
                                     _stream(X.device)))
     return out
 
 
 def state_passing(dstates, lam, chunk, seqlen, initial_state=None, return_final_state=True,
-                  out=None):
-    """Stage 4: states entering each chunk [Bz,nc,H,P,N] (+ final state)."""
-    Bz, nc, H, P, N = dstates.shape
+                  out=None, seg_chunks=1):
+    """Stage 4: states entering each unit of `seg_chunks` chunks [Bz,U,H,P,N]
+    (+ final state); lam [Bz,H,U] holds each unit's total log-decay."""
+    Bz, nu, H, P, N = dstates.shape
     d = _lib.fwd_desc(Bz, seqlen, H, P, N, 1, int(chunk), SSD_F32)
+    d.seg_chunks = max(1, int(seg_chunks))
     if out is None:
         out = torch.empty_like(dstates)
     fin = torch.empty((Bz, H, P, N), dtype=torch.float32, device=dstates.device) if return_final_state else None
@@ -152,10 +157,12 @@ def state_passing(dstates, lam, chunk, seqlen, initial_state=None, return_final_
     return out, fin
 
 
-def chunk_scan(X, a, B, C, chunk, states_in=None):
-    """Stages 2 + 5: Y from the chunk inputs and the entering states (None = zero)."""
-    d = _desc(X, B, chunk, SSD_ALGO_MFMA, 1)
-    Y = torch.empty_like(X)
+def chunk_scan(X, a, B, C, chunk, states_in=None, seg_chunks=1, Y=None):
+    """Stages 2 + 5: Y from the inputs and the states entering each unit of
+    `seg_chunks` chunks ([Bz,U,H,P,N]; None = zero)."""
+    d = _desc(X, B, chunk, SSD_ALGO_MFMA, max(1, int(seg_chunks)))
+    if Y is None:
+        Y = torch.empty_like(X)
     _lib.check(_L().ssd_chunk_scan(ctypes.byref(d), _ptr(X), _ptr(a), _ptr(B), _ptr(C),
                                    _ptr(states_in), _ptr(Y), _stream(X.device)))
     return Y

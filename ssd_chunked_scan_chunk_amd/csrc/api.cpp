@@ -378,7 +378,7 @@ ssd_status ssd_chunk_state(const ssd_fwd_desc* desc, const void* X, const float*
     if (!desc) return fail(SSD_ERR_NULL, "desc is NULL");
     d1 = *desc;
     d1.algo = SSD_ALGO_MFMA;
-    d1.seg_chunks = 1;
+    if (d1.seg_chunks < 1) d1.seg_chunks = 1;
     Plan p;
     ssd_status st = make_plan(&d1, &p);
     if (st != SSD_OK) return st;
@@ -387,12 +387,12 @@ ssd_status ssd_chunk_state(const ssd_fwd_desc* desc, const void* X, const float*
     if (!X || !a || !B || !dstates) return fail(SSD_ERR_NULL, "X, a, B and dstates are required");
     if (!aligned(X, 16) || !aligned(B, 16) || !aligned(dstates, 16) || !aligned(a, 4))
         return fail(SSD_ERR_ALIGN, "misaligned buffer");
-    const Range out = rng("dstates", dstates, s.Bz * s.nc * s.H * s.P * s.N * 4);
+    const Range out = rng("dstates", dstates, s.Bz * p.nseg * s.H * s.P * s.N * 4);
     const Range ins[] = {rng("X", X, s.Bz * s.L * s.H * s.P * 2), rng("a", a, s.Bz * s.L * s.H * 4),
                          rng("B", B, s.Bz * s.L * s.G * s.N * 2)};
     for (const Range& i : ins)
         if (overlap(out, i)) return fail(SSD_ERR_ALIAS, "dstates overlaps %s", i.name);
-    hipError_t e = ssd::launch_mfma_state(s, 1, s.nc, s.nc, X, a, B, dstates, nullptr,
+    hipError_t e = ssd::launch_mfma_state(s, p.seg_chunks, p.nseg, p.nseg, X, a, B, dstates, nullptr,
                                           reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "chunk state launch");
     return ok();
@@ -406,6 +406,8 @@ ssd_status ssd_state_passing(const ssd_fwd_desc* desc, const float* dstates, con
     const ssd::FwdShape s = shape_of(desc);
     if (s.Bz == 0) return ok();
     const int64_t PN = s.P * s.N;
+    const int64_t k = desc->seg_chunks > 1 ? desc->seg_chunks : 1;
+    const int64_t nu = (s.nc + k - 1) / k;   // units of k chunks
     if (s.L == 0) {
         if (final_state) {
             if (!aligned(final_state, 16)) return fail(SSD_ERR_ALIGN, "final_state misaligned");
@@ -421,17 +423,17 @@ ssd_status ssd_state_passing(const ssd_fwd_desc* desc, const float* dstates, con
     for (const void* q : v16)
         if (q && !aligned(q, 16)) return fail(SSD_ERR_ALIGN, "state buffers must be 16-byte aligned");
     if (!aligned(lam, 4)) return fail(SSD_ERR_ALIGN, "lam misaligned");
-    const int64_t nst = s.Bz * s.nc * s.H * PN * 4;
+    const int64_t nst = s.Bz * nu * s.H * PN * 4;
     const Range rd = rng("dstates", dstates, nst), ro = rng("states_in", states_in, nst);
     if (overlap(rd, ro) && dstates != states_in)
         return fail(SSD_ERR_ALIAS, "states_in overlaps dstates without being identical");
-    const Range rl = rng("lam", lam, s.Bz * s.H * s.nc * 4);
+    const Range rl = rng("lam", lam, s.Bz * s.H * nu * 4);
     const Range ri = rng("initial_state", initial_state, initial_state ? s.Bz * s.H * PN * 4 : 0);
     const Range rf = rng("final_state", final_state, final_state ? s.Bz * s.H * PN * 4 : 0);
     if (overlap(ro, rl) || overlap(ro, ri) || overlap(rf, rl) || overlap(rf, ri) || overlap(rf, rd) ||
         overlap(rf, ro))
         return fail(SSD_ERR_ALIAS, "an output overlaps an input");
-    hipError_t e = ssd::launch_state_scan(s, s.nc, s.nc, dstates, lam, s.H * s.nc, s.nc,
+    hipError_t e = ssd::launch_state_scan(s, nu, nu, dstates, lam, s.H * nu, nu,
                                           initial_state, states_in, final_state, s.H * PN,
                                           reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "state passing launch");
@@ -443,7 +445,7 @@ ssd_status ssd_chunk_scan(const ssd_fwd_desc* desc, const void* X, const float* 
     if (!desc) return fail(SSD_ERR_NULL, "desc is NULL");
     ssd_fwd_desc d1 = *desc;
     d1.algo = SSD_ALGO_MFMA;
-    d1.seg_chunks = 1;
+    if (d1.seg_chunks < 1) d1.seg_chunks = 1;
     Plan p;
     ssd_status st = make_plan(&d1, &p);
     if (st != SSD_OK) return st;
@@ -453,12 +455,12 @@ ssd_status ssd_chunk_scan(const ssd_fwd_desc* desc, const void* X, const float* 
     if (st != SSD_OK) return st;
     if (states_in) {
         if (!aligned(states_in, 16)) return fail(SSD_ERR_ALIGN, "states_in misaligned");
-        const Range rs = rng("states_in", states_in, s.Bz * s.nc * s.H * s.P * s.N * 4);
+        const Range rs = rng("states_in", states_in, s.Bz * p.nseg * s.H * s.P * s.N * 4);
         if (overlap(rs, rng("Y", Y, s.Bz * s.L * s.H * s.P * 2))) return fail(SSD_ERR_ALIAS, "Y overlaps states_in");
     }
     const int64_t PN = s.P * s.N;
-    ssd::StateSrc src{states_in, s.nc * s.H * PN, s.H * PN};
-    hipError_t e = ssd::launch_mfma_out(s, 1, s.nc, X, a, B, C, src, Y, nullptr,
+    ssd::StateSrc src{states_in, p.nseg * s.H * PN, s.H * PN};
+    hipError_t e = ssd::launch_mfma_out(s, p.seg_chunks, p.nseg, X, a, B, C, src, Y, nullptr,
                                         reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "chunk scan launch");
     return ok();

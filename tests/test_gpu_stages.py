@@ -90,3 +90,35 @@ def test_stages_compose_to_forward(case):
     torch.cuda.synchronize()
     assert y_err(host_f64(Y), ref["Y"]) < 2e-2
     assert slice_rel_err(host_f64(fin), ref["S_fin"], (0, 1)) < 2e-2
+
+
+@pytest.mark.parametrize("k", [2, 4])
+def test_stages_in_units_of_several_chunks(case, k):
+    """Stages 3-5 on units of k chunks (the full forward's segments; the last
+    unit is shorter): unit states from the oracle's chunk states, and the
+    composed output."""
+    d, g, ref = case
+    log("stages in units of %d chunks" % k)
+    nc = ref["dS"].shape[1]
+    nu = (nc + k - 1) // k
+    dS = ssd.chunk_state(g["X"], g["a"], g["B"], SHAPE.chunk, seg_chunks=k)
+    assert dS.shape[1] == nu
+    # the unit state is the chunk states combined by the chunk decays (fp64)
+    lam_c = ref["lam"]                              # [b][h][c]
+    want = np.zeros_like(ref["dS"][:, :nu])
+    for u in range(nu):
+        for c in range(u * k, min(nc, (u + 1) * k)):
+            dec = np.exp(lam_c[:, :, c])[:, :, None, None]
+            want[:, u] = want[:, u] * dec + ref["dS"][:, c]
+    torch.cuda.synchronize()
+    assert slice_rel_err(host_f64(dS), want, (0, 1, 2)) < 2e-2
+    # unit totals, summed from the per-chunk ones; the scan and the output
+    _, lam = ssd.chunk_cumsum(g["a"], SHAPE.chunk)
+    pad = nu * k - nc
+    lam_u = torch.nn.functional.pad(lam, (0, pad)).view(lam.shape[0], lam.shape[1], nu, k).sum(-1).contiguous()
+    Sin, fin = ssd.state_passing(dS, lam_u, SHAPE.chunk, SHAPE.seqlen, seg_chunks=k)
+    Y = ssd.chunk_scan(g["X"], g["a"], g["B"], g["C"], SHAPE.chunk, states_in=Sin, seg_chunks=k)
+    torch.cuda.synchronize()
+    assert slice_rel_err(host_f64(Sin), ref["S_in"][:, ::k], (0, 1, 2)) < 2e-2
+    assert y_err(host_f64(Y), ref["Y"]) < 2e-2
+    assert slice_rel_err(host_f64(fin), ref["S_fin"], (0, 1)) < 2e-2
