@@ -106,18 +106,23 @@ ssd::FwdShape shape_of(const ssd_fwd_desc* d) {
     return s;
 }
 
-// Segment plan of the MFMA path.  A workgroup (two or four heads of one group) walks
-// k consecutive chunks; nseg = ceil(nc / k) segments per (b, head set).  Cost
-// in "chunk passes per CU": the full pass takes ceil(WG / slots) rounds of k
-// chunks, and when nseg > 1 the state-only pass (about 0.35 of a full chunk)
-// and the segment scan are added.  For each segment count only the most
-// balanced k is tried; the cheapest wins, ties going to fewer segments (less
-// traffic).
+// Segment plan of the MFMA path.  A workgroup (the heads of one group that
+// share it) walks k consecutive chunks; nseg = ceil(nc / k) segments per
+// (b, head set).  Estimated time in microseconds, from measurements of the
+// kernels on MI355X: a full-pass block of 64 steps takes about kBlockUs on
+// one CU, a state-only block about kStateFrac of that, and more than one
+// segment adds the state round trips through HBM (written by the state
+// pass, read and written by the segment scan, read by the full pass) and
+// two launches.  For each segment count only the most balanced k is tried;
+// the cheapest wins, ties going to fewer segments.
 int64_t auto_seg_chunks(const ssd::FwdShape& s) {
+    constexpr double kBlockUs = 6.5, kStateFrac = 0.45, kStateBytesPerUs = 4.0e6, kLaunchUs = 4.0;
     const int64_t per_cu = kLdsPerCU / mfma_lds_bytes(s.P, s.N);
     const int64_t slots = kNumCU * (per_cu > 0 ? per_cu : 1);
     const int64_t hw = ssd::mfma_heads_per_workgroup(s.P, s.N);
     const int64_t wg = s.Bz * s.G * ((s.H / s.G + hw - 1) / hw);  // workgroups per segment
+    const double blocks_per_chunk = (double)((s.Q + 63) / 64);
+    const double state_bytes = 4.0 * (double)(s.Bz * s.H * s.P * s.N) * 4.0;  // per segment boundary
     const int64_t max_seg = s.nc < 65535 ? s.nc : 65535;
     double best = 1e300;
     int64_t best_k = s.nc;
@@ -127,11 +132,11 @@ int64_t auto_seg_chunks(const ssd::FwdShape& s) {
         if (k == prev_k) continue;
         prev_k = k;
         const int64_t nseg = (s.nc + k - 1) / k;
-        const double rounds_c = (double)((wg * nseg + slots - 1) / slots);
-        double cost = rounds_c * (double)k;
+        const double blocks = (double)k * blocks_per_chunk;
+        double cost = (double)((wg * nseg + slots - 1) / slots) * blocks * kBlockUs;
         if (nseg > 1) {
-            const double rounds_a = (double)((wg * (nseg - 1) + slots - 1) / slots);
-            cost += rounds_a * (double)k * 0.35 + 1.5;
+            cost += (double)((wg * (nseg - 1) + slots - 1) / slots) * blocks * kBlockUs * kStateFrac;
+            cost += (double)nseg * state_bytes / kStateBytesPerUs + 2.0 * kLaunchUs;
         }
         if (cost < best - 1e-9) {
             best = cost;
