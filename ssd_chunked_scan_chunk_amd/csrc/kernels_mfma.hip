@@ -54,9 +54,9 @@
 //    R(0..3).
 //  * Scores are formed transposed, S^T = B C^T, so lane = step i; outputs are
 //    Y^T tiles, a lane holding 4 consecutive head-dim entries of one step.
-//  * LDS tiles are row-major with the 16-byte pieces of row r stored at
-//    piece ^ (r mod pieces-per-row), so row reads and transposing reads touch
-//    distinct banks.
+//  * LDS tiles are row-major with their 16-byte pieces permuted per row
+//    (swzbits below) so that row reads and transposing reads spread over the
+//    banks.
 //  * Workgroups are dealt to the 8 XCDs in contiguous ranges of (batch,
 //    segment, group, head-set) items, so the workgroups sharing B and C run
 //    on one XCD and read them through one L2.
@@ -139,11 +139,24 @@ __device__ __forceinline__ bf16x8 scale8(bf16x8 v, const float (&s)[8]) {
     return as_bf16x8(o);
 }
 
-// Element offset of (row, col) in a swizzled row-major tile of PR 16-byte
-// pieces per row (col a multiple of 4 for 8-byte accesses).
+// Swizzle of a row-major LDS tile with PR 16-byte pieces per row: piece q of
+// row r is stored at q ^ swzbits<PR>(r).  swzbits is a bijection of the row's
+// low bits chosen for the two access patterns of these tiles with 64 banks of
+// 4 bytes: 16 consecutive rows read at one column land on distinct 16-byte
+// slots of the 256-byte bank window, and the 8 rows of one transposing read
+// (64 bytes each) fill the window's four 64-byte quarters two rows apiece.
+template <int PR>
+__device__ __forceinline__ int swzbits(int r) {
+    static_assert(PR == 4 || PR == 8 || PR == 16, "pieces per row");
+    if constexpr (PR == 16) return (((r >> 1) & 3) << 2) | (((r >> 3) & 1) << 1) | (r & 1);
+    else if constexpr (PR == 8) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+    else return (r >> 2) & 3;
+}
+// Element offset of (row, col) in such a tile (col a multiple of 4 for 8-byte
+// accesses, of 8 for 16-byte ones).
 template <int PR>
 __device__ __forceinline__ int swz(int row, int col) {
-    return row * (PR * 8) + ((((col >> 3) ^ (row & (PR - 1))) << 3) | (col & 7));
+    return row * (PR * 8) + ((((col >> 3) ^ swzbits<PR>(row)) << 3) | (col & 7));
 }
 
 // Inclusive prefix sum over the 64 lanes: shifts of 1, 2, 4, 8 within each row
@@ -273,10 +286,10 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
     constexpr unsigned XHT = kT * XPR;                   // slots per head tile
     const unsigned utid = (unsigned)tid;
     const unsigned xh = utid / XHT, xr = (utid / XPR) % kT;
-    const unsigned xlp = (utid % XPR) ^ (xr % XPR);
+    const unsigned xlp = (utid % XPR) ^ (unsigned)swzbits<XPR>((int)xr);
     constexpr unsigned BROWS = kThreads / BPR;
     static_assert(BROWS % BPR == 0, "copy shape");
-    const unsigned br = utid / BPR, blp = (utid % BPR) ^ (br % BPR);
+    const unsigned br = utid / BPR, blp = (utid % BPR) ^ (unsigned)swzbits<BPR>((int)br);
     // The copies of a block are issued in four parts spread over the previous
     // block's work (a and the first half of X; the rest of X; B; C): issued
     // together they fill the CU's memory queue and stall every wave until the
@@ -416,7 +429,7 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
             u16* rowp = xTm + lane * P;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const int piece = ((pc >> 3) + k) ^ (lane & (XPR - 1));
+                const int piece = ((pc >> 3) + k) ^ swzbits<XPR>(lane);
                 u32x4* q = reinterpret_cast<u32x4*>(rowp + piece * 8);
                 const u32x4 u = *q;
                 u32x4 o;
