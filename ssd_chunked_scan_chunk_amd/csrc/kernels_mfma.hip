@@ -356,17 +356,33 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
         }
     }
     float lam2_total = 0.f;
-    // The true state is 2^ld * Sacc (|ld| <= kRange).  In a block whose
-    // log2-decays stay within kRange of the state scale (the common case) the
-    // decay is never applied to the accumulators: with X~_j = 2^(-ld - cs2_j) X_j
+    // The true state is 2^ld * Sacc.  In a block whose log2-decays stay within
+    // range of the state scale (the common case) the decay is never applied to
+    // the accumulators: with X~_j = 2^(-ld - cs2_j) X_j
     //   Y_i     = 2^(cs2_i + ld) * (C_i Sacc + sum_{j<=i} (C_i . B_j) X~_j)
     //   Sacc'   = Sacc + B^T X~,   ld' = ld + Lam2,
     // so stages 2 and 5 share one accumulator, the scores need only the causal
     // mask (and so are the same for every head), and one per-step factor
-    // scales the output (every factor stays within 2^+-kRange).  A block with a
-    // larger decay range takes the direct form: per-element decay of the shared
-    // scores, then Sacc' = 2^(ld + Lam2) Sacc + B^T (w o X) with ld' = 0.
+    // scales the output.  Each 32-step half of the block is checked on its own:
+    // a half whose prefix sums (relative to its start) lie in [-neg, pos] keeps
+    // every weight exponent -ld - cs2_j and output exponent cs2_i + ld within
+    // +-kRange exactly when ld lies in [neg - kRange, kRange - pos] (neg and
+    // pos follow from the half's total and its sum of |a|).  When the scale
+    // reached at a half's start falls outside that interval it is re-based to
+    // the interval's centre, -Lam_h / 2: at the block start by multiplying
+    // Sacc, half-way by multiplying Sacc between the halves of stage 3 and the
+    // second row block's accumulator between the first and second column tiles
+    // of stage 2, after which the second half's X~ and output factors use its
+    // own prefix sums.  Such a scale exists when the half's spread neg + pos
+    // is at most 2 kRange (kSpan keeps a margin so the factor between the two
+    // halves' references stays below 2^127).  Only a block with a wider half
+    // takes the direct form: per-element decay of the shared scores, then
+    // Sacc' = 2^(ld + Lam2) Sacc + B^T (w o X), ld' = 0.
     constexpr float kRange = 64.f;
+    constexpr float kSpan = 2.f * kRange - 8.f;
+    auto fits = [](float l, float absh, float lamh_) {
+        return l >= 0.5f * (absh - lamh_) - kRange && l <= kRange - 0.5f * (absh + lamh_);
+    };
     float ld = 0.f;
     // This block's Y^T in bf16 ([row block][4-entry group]; lane = step), and
     // the previous block's Y re-laid out through LDS so that copy k of a lane
@@ -406,20 +422,28 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
         const float av = lane <= last ? sA[bf][lane * HW + hw] : 0.f;
         const float cs2 = wave_scan64(av, lane) * kLog2e;
         const float lam2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs2), 63));
-        // sum of |a| bounds every |cs2_j| of the block
-        const float abs2 = __int_as_float(__builtin_amdgcn_readlane(
-                               __float_as_int(wave_scan64(fabsf(av), lane)), 63)) * kLog2e;
+        const float lamh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs2), 31));
+        // sums of |a| over each half bound the spread of cs2 within the half
+        const float absc = wave_scan64(fabsf(av), lane) * kLog2e;
+        const float abs_h0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(absc), 31));
+        const float abs_h1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(absc), 63)) - abs_h0;
+        const float lam_h1 = lam2 - lamh;
         lam2_total += lam2;
-        const bool fast = abs2 <= kRange;                    // wave-uniform
-        if (fast && fabsf(ld) + abs2 > kRange) {             // rare: fold the scale into Sacc
-            const float f = fast_exp2(ld);
+        const bool fast = abs_h0 <= kSpan && abs_h1 <= kSpan;   // wave-uniform
+        if (fast && !fits(ld, abs_h0, lamh)) {               // re-base the state scale
+            const float target = -0.5f * lamh;
+            const float f = fast_exp2(ld - target);
 #pragma unroll
             for (int nt = 0; nt < NTL; ++nt) Sacc[nt] *= f;
-            ld = 0.f;
+            ld = target;
         }
-        const float ld_in = ld;
-        const float wsh = fast ? -ld_in : lam2;              // state weights 2^(wsh - cs2_j)
-        ld = fast ? ld_in + lam2 : 0.f;
+        const float ld_in = ld;                               // reference of the first half
+        const float ld_mid = ld_in + lamh;                    // scale reached half-way
+        const bool fold_mid = fast && !fits(ld_mid, abs_h1, lam_h1);
+        const float ld_h1 = fold_mid ? -0.5f * lam_h1 : ld_mid;   // reference of the second half
+        // state weights 2^(wsh - cs2_j)
+        const float wsh = fast ? (lane < 32 ? -ld_in : lamh - ld_h1) : lam2;
+        ld = fast ? ld_h1 + lam_h1 : 0.f;
         sCs[wave][lane] = cs2;
         // The state weight of step j is applied to X in place: lane j scales row
         // j of this wave's head-dim tile (its own 32 columns, 4 pieces), so the
@@ -493,7 +517,7 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
                     }
                 }
             const float e0 = fast_exp2(sCs[wave][l32] + ld_in);        // output factors
-            const float e1 = fast_exp2(sCs[wave][32 + l32] + ld_in);
+            const float e1 = fast_exp2(sCs[wave][32 + l32] - lamh + ld_h1);
 
             if (has_next) dma_part(c + 1, bf ^ 1, 2);
             sync_lds();  // the shared score tiles are complete
@@ -507,11 +531,13 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
                 // ---- stage 2: Y^T += X~^T P, then the per-step factor ----
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
-                    const bf16x8 xw0 = xfrag(0, ks), xw1 = xfrag(1, ks);
+                    const bf16x8 xw0 = xfrag(0, ks);
                     Yt[0] = mfma32(xw0, ptile(0, ks), Yt[0]);
                     Yt[1] = mfma32(xw0, ptile(1, ks), Yt[1]);
-                    Yt[1] = mfma32(xw1, ptile(2, ks), Yt[1]);
                 }
+                if (fold_mid) Yt[1] *= fast_exp2(ld_mid - ld_h1);   // to the second half's reference
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) Yt[1] = mfma32(xfrag(1, ks), ptile(2, ks), Yt[1]);
                 Yt[0] *= e0;
                 Yt[1] *= e1;
             } else {
@@ -538,10 +564,15 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
                 const float csi0 = sCs[wave][l32], csi1 = sCs[wave][32 + l32];
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
-                    const bf16x8 xa0 = xfrag(0, ks), xa1 = xfrag(1, ks);
+                    // one tile at a time (this rare path must not raise the
+                    // kernel's register budget)
+                    const bf16x8 xa0 = xfrag(0, ks);
                     Yt[0] = mfma32(xa0, decayed(0, 0, ks, csi0), Yt[0]);
+                    __builtin_amdgcn_sched_barrier(0);
                     Yt[1] = mfma32(xa0, decayed(1, 0, ks, csi1), Yt[1]);
-                    Yt[1] = mfma32(xa1, decayed(2, 1, ks, csi1), Yt[1]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    Yt[1] = mfma32(xfrag(1, ks), decayed(2, 1, ks, csi1), Yt[1]);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
             // Y^T to bf16, stored at the top of the next block (or after the loop)
@@ -563,7 +594,12 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
             for (int nt = 0; nt < NTL; ++nt) Sacc[nt] *= f;
         }
 #pragma unroll
-        for (int J = 0; J < 2; ++J)
+        for (int J = 0; J < 2; ++J) {
+            if (J == 1 && fold_mid) {   // the first half's update at the second half's reference
+                const float f = fast_exp2(ld_mid - ld_h1);
+#pragma unroll
+                for (int nt = 0; nt < NTL; ++nt) Sacc[nt] *= f;
+            }
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 const bf16x8 xw = xfrag(J, ks);
@@ -574,6 +610,7 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
                     Sacc[nt] = mfma32(Af, xw, Sacc[nt]);
                 }
             }
+        }
         if constexpr (FULL) {
             // Y^T through this wave's own X slice, which is dead after stage 3
 #pragma unroll

@@ -121,6 +121,38 @@ def test_strong_decay_no_nan():
     assert y_err(host_f64(Y), Yr) < 2e-2 and state_err(host_f64(S), Sr) < 2e-2
 
 
+@pytest.mark.parametrize("seg", [0, 1])
+def test_decay_regimes_per_head(seg):
+    # One head per decay regime of the 64-step blocks (log2-decay per 32-step
+    # half ~2.3, 92, 55, 138, growth, mixed per half, recipe, rare deep
+    # drops), so the output and state scales are re-based at block starts and
+    # at half-way points, and the direct form runs for some blocks.
+    sh = si.FwdShape(2, 64 * 12 + 17, 8, 64, 128, 1, 256, si.BF16)
+    d = si.make_fwd(sh, seed=11)
+    a = d["a"]
+    rng = np.random.default_rng(5)
+    a[:, :, 0] = -0.05
+    a[:, :, 1] = -2.0
+    a[:, :, 2] = -1.2
+    a[:, :, 3] = -3.0
+    a[:, :, 4] = 0.05
+    halves = rng.choice(np.array([-0.01, -0.6, -1.2, -2.5, -3.5], dtype=np.float32),
+                        size=(sh.batch, sh.seqlen // 32 + 1))
+    a[:, :, 5] = np.repeat(halves, 32, axis=1)[:, :sh.seqlen]
+    a[:, :, 7] = -0.02
+    a[:, ::50, 7] = -100.0
+    g = upload_fwd(d)
+    Y, S = ssd.chunk_scan_fwd(g["X"], g["a"], g["B"], g["C"], sh.chunk, return_final_state=True,
+                              algo=ssd.SSD_ALGO_MFMA, seg_chunks=seg)
+    torch.cuda.synchronize()
+    w = widen_fwd(d)
+    Yr, Sr = oracle.fwd(w["X"], w["a"], w["B"], w["C"], nthreads=oracle_threads())
+    ey, es = y_err(host_f64(Y), Yr), state_err(host_f64(S), Sr)
+    log("   decay regimes seg=%d err Y=%.3e S=%.3e" % (seg, ey, es))
+    assert torch.isfinite(Y.float()).all()
+    assert ey <= TOL[si.BF16] and es <= TOL[si.BF16], (ey, es)
+
+
 def test_nan_stays_in_its_slice():
     # a NaN in X[b=1, t=200, h=2] reaches only slice (1, 2).  Within that slice
     # it may also reach the steps of its own 32-step block of the chunk before
