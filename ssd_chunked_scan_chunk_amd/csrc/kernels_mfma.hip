@@ -20,28 +20,34 @@
 //
 // Decomposition on gfx950.
 //  * A workgroup is eight wavefronts, two per SIMD, over the heads of one
-//    group that share B and C.  Each wavefront owns one 32-wide head-dim tile
-//    of one head (P/32 waves per head, 256/P heads per workgroup) and carries
-//    that slice of the head's fp32 state in MFMA accumulators, so states never
-//    round-trip HBM inside a segment and the two waves of a SIMD hide each
-//    other's MFMA, LDS and exponential latencies.  When a launch would leave
-//    CUs idle the sequence is split into segments: a state-only pass (stages
-//    1, 3, 4) gives each segment's end state from zero, a scan over segments
+//    group that share B and C.  Six are state waves: each owns one 32-wide
+//    head-dim tile of one head (P/32 waves per head, 192/P heads per
+//    workgroup) and carries that slice of the head's fp32 state in MFMA
+//    accumulators, so states never round-trip HBM inside a segment.  The
+//    other two are copy waves: they issue every copy into LDS and form the
+//    shared score tiles.  A wave whose memory instruction finds the CU's
+//    queue full stalls until it drains; keeping the copies on waves with no
+//    state work lets those stalls overlap the state waves' MFMA and VALU work
+//    instead of delaying them.  When a launch would leave CUs idle the
+//    sequence is split into segments: a state-only pass (stages 1, 3, 4)
+//    gives each segment's end state from zero, a scan over segments
 //    (kernels_scan.hip) gives every segment's entering state, and the full
 //    pass starts from it.
 //  * The masked scores of a block do not depend on the head (the decay is
-//    moved onto X and the output, below), so waves 0-2 form the three causal
-//    32x32 score tiles once per workgroup and share them in LDS as bf16.
+//    moved onto X and the output, below), so the copy waves form the three
+//    causal 32x32 score tiles once per workgroup and share them in LDS as
+//    bf16.
 //  * Inputs reach LDS through asynchronous global_load_lds copies (lane L of a
 //    wave-wide copy lands at LDS base + L * size), double buffered one block
 //    ahead, so HBM traffic overlaps the MFMA work and no register holds
 //    prefetched data.  The copies are written in inline assembly: they have no
 //    register result, and keeping them out of the compiler's view stops it
 //    from inserting full vmcnt waits before every LDS access, which would
-//    serialise the prefetch.  A block's Y is stored from registers at the top
-//    of the next block, so the one vmcnt(0) wait per block never waits on
-//    fresh stores.  Two barriers per block: one publishes the block's copies
-//    (and frees the other buffer), one publishes the shared scores.
+//    serialise the prefetch.  Only the copy waves wait for copies (vmcnt(0)
+//    once per block); state waves store their Y at the end of each block and
+//    never wait on memory.  Two barriers per block: one publishes the
+//    block's copies (and frees the other buffer), one publishes the shared
+//    scores.
 //  * Every product is v_mfma_f32_32x32x16_bf16 (operand lane l holds row or
 //    column l%32 and 8 k values of group l/32; the accumulator holds column
 //    l%32, rows 8(r/4) + 4(l/32) + r%4 in register r).  Contractions use the
@@ -79,21 +85,25 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 constexpr int kXcds = 8;     // MI355X accelerator complex dies; workgroups alternate over them
 constexpr int kT = 64;       // steps per block
 constexpr int kWaves = 8;    // wavefronts per workgroup (two per SIMD)
+constexpr int kStateWaves = 6;                   // waves that carry head states
+constexpr int kAuxThreads = 64 * (kWaves - kStateWaves);   // copy and score waves
 constexpr int kThreads = 64 * kWaves;
 constexpr int kPRow = 36;    // padded row (elements) of a shared 32x32 bf16 score tile
 
 template <int P, int N>
 struct MfmaCfg {
-    static constexpr int PS = P / 32;                    // waves per head (one head-dim tile each)
-    static constexpr int HW = kWaves / PS;               // heads per workgroup
+    static constexpr int PS = P / 32;                    // state waves per head (one head-dim tile each)
+    static constexpr int HW = kStateWaves / PS;          // heads per workgroup
     static constexpr int NTL = N / 32;                   // 32-wide state-dim tiles
     static constexpr int XPR = P / 8;                    // 16-byte pieces per X row
     static constexpr int BPR = N / 8;                    // 16-byte pieces per B / C row
-    static constexpr int XOPS = HW * kT * XPR / kThreads;  // X copies per thread per block
-    static constexpr int BOPS = kT * BPR / kThreads;       // B (or C) copies per thread per block
-    static_assert(P % 32 == 0 && N % 32 == 0 && kWaves % PS == 0, "tile shape");
-    static_assert(XOPS >= 1 && BOPS >= 1, "a block must cover the workgroup");
-    static_assert(kThreads % (kT * XPR) == 0 || (kT * XPR) % kThreads == 0, "X copy shape");
+    static constexpr int XOPS = HW * kT * XPR / kAuxThreads;   // X copies per aux thread per block
+    static constexpr int BOPS = kT * BPR / kAuxThreads;        // B (or C) copies per aux thread
+    static constexpr int AOPS = (kT * HW + kAuxThreads - 1) / kAuxThreads;   // a copies (4 bytes)
+    static_assert(P % 32 == 0 && N % 32 == 0 && kStateWaves % PS == 0, "tile shape");
+    static_assert((HW * kT * XPR) % kAuxThreads == 0 && (kT * BPR) % kAuxThreads == 0, "copy shape");
+    static_assert(kAuxThreads % XPR == 0 && kAuxThreads % BPR == 0 && (kT * XPR) % kAuxThreads == 0,
+                  "a copy covers whole rows of one head");
 };
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
@@ -209,14 +219,14 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
 {
     using Cfg = MfmaCfg<P, N>;
     constexpr int HW = Cfg::HW, NTL = Cfg::NTL, XPR = Cfg::XPR, BPR = Cfg::BPR;
-    constexpr int XOPS = Cfg::XOPS, BOPS = Cfg::BOPS;
+    constexpr int XOPS = Cfg::XOPS, BOPS = Cfg::BOPS, AOPS = Cfg::AOPS;
 
     __shared__ __attribute__((aligned(16))) u16 sX[2][HW * kT * P];    // [buf][head][step][p]
     __shared__ __attribute__((aligned(16))) u16 sB[2][kT * N];         // [buf][step][n]
     __shared__ __attribute__((aligned(16))) u16 sC[FULL ? 2 : 1][FULL ? kT * N : 8];
     __shared__ __attribute__((aligned(16))) u16 sP[FULL ? 3 : 1][FULL ? 32 * kPRow : 8];  // masked scores [i][j]
-    __shared__ __attribute__((aligned(16))) float sA[2][kT * HW];      // [buf][step][head]
-    __shared__ __attribute__((aligned(16))) float sCs[kWaves][kT];     // per wave: cs * log2(e)
+    __shared__ __attribute__((aligned(16))) float sA[2][AOPS * kAuxThreads];  // [buf][step][head]
+    __shared__ __attribute__((aligned(16))) float sCs[kStateWaves][kT];       // per state wave
 
     // ---- work item: contiguous item ranges per XCD (head sets fastest) ----
     const int HPG = H / G;
@@ -232,14 +242,16 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool aux = wave >= kStateWaves;        // copy / score wave
+    const int sw = aux ? 0 : wave;               // state wave index (aux waves: unused)
     const int l32 = lane & 31, g2 = lane >> 5;
     const int trow = (lane & 15) >> 2, tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     const int hl0 = hq * HW;                     // first head of the set within the group
-    const int hw = wave % HW;                    // this wave's head within the set
+    const int hw = sw % HW;                      // this state wave's head within the set
     const int hlw = hl0 + hw;
-    const bool hvalid = hlw < HPG;
-    const int h = grp * HPG + (hvalid ? hlw : HPG - 1);  // this wave's head (clamped)
-    const int pc = (wave / HW) * 32;             // this wave's first head-dim column
+    const bool hvalid = !aux && hlw < HPG;
+    const int h = grp * HPG + (hlw < HPG ? hlw : HPG - 1);  // this wave's head (clamped)
+    const int pc = (sw / HW) * 32;               // this wave's first head-dim column
     const int64_t PN = (int64_t)P * N;
     const int64_t nblk = (L + kT - 1) / kT;
     const int64_t c_begin = seg * blocks_per_seg;
@@ -277,68 +289,75 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
         return join8(*reinterpret_cast<const u32x2*>(t + roff[nt][hf][0]),
                      *reinterpret_cast<const u32x2*>(t + roff[nt][hf][1]));
     };
-    // All copies of block c into buffer bf.  Copy k of thread tid fills LDS
-    // slot k*512 + tid (16 bytes).  A thread's row and (swizzled) piece within
-    // a copy are fixed; only a per-copy uniform row or head base changes.
-    // Rows past the end of the sequence are clamped to the last valid row
-    // (their scores are masked, their state weight is zero and their outputs
-    // are not stored).
-    constexpr unsigned XHT = kT * XPR;                   // slots per head tile
-    const unsigned utid = (unsigned)tid;
-    const unsigned xh = utid / XHT, xr = (utid / XPR) % kT;
-    const unsigned xlp = (utid % XPR) ^ (unsigned)swzbits<XPR>((int)xr);
-    constexpr unsigned BROWS = kThreads / BPR;
-    static_assert(BROWS % BPR == 0, "copy shape");
-    const unsigned br = utid / BPR, blp = (utid % BPR) ^ (unsigned)swzbits<BPR>((int)br);
-    // The copies of a block are issued in four parts spread over the previous
-    // block's work (a and the first half of X; the rest of X; B; C): issued
-    // together they fill the CU's memory queue and stall every wave until the
-    // transfer drains, while spread out they overlap the MFMA and VALU work.
-    auto dma_part = [&](int64_t c, int bf, int part) {
+
+    // ---- copies (aux waves only).  Copy k of aux thread at fills LDS slot
+    // k * kAuxThreads + at (16 bytes; 4 for a).  A thread's piece within a
+    // row is fixed, and so is the row's swizzle; per copy only a uniform row
+    // or head base changes.  Rows past the end of the sequence are clamped to
+    // the last valid row (their scores are masked, their state weight is zero
+    // and their outputs are not stored). ----
+    const unsigned at = (unsigned)(tid - kStateWaves * 64);   // aux thread (valid for aux waves)
+    const unsigned aw = (unsigned)(wave - kStateWaves);
+    constexpr unsigned XHT = kT * XPR;                          // slots per head tile
+    constexpr unsigned XRS = kAuxThreads / XPR;                 // X rows per copy
+    constexpr unsigned BRS = kAuxThreads / BPR;                 // B / C rows per copy
+    const unsigned xr0 = at / XPR, xlp = (at % XPR) ^ (unsigned)swzbits<XPR>((int)(at / XPR));
+    const unsigned br0 = at / BPR, bq = at % BPR;
+    auto copy_x = [&](int64_t c, int bf) {
         const unsigned lc = (unsigned)block_last(c);
-        const int64_t row0 = (int64_t)b * L + c * kT;
-        if (part == 0 && wave < HW) {   // a: thread -> (step, head), 64 * HW values
-            const unsigned t = utid / HW, hh = utid % HW;
-            const unsigned tr = t <= lc ? t : lc;
+        const u16* Xg = X + (((int64_t)b * L + c * kT) * H + grp * HPG) * P;
+#pragma unroll
+        for (int k = 0; k < XOPS; ++k) {
+            const unsigned s0 = (unsigned)k * kAuxThreads;      // first slot of the copy
+            const unsigned hh = s0 / XHT;                       // uniform: a copy stays in one head
+            const unsigned r = (s0 % XHT) / XPR + xr0;
+            const unsigned tr = r <= lc ? r : lc;
             const unsigned hx = hl0 + hh < (unsigned)HPG ? hl0 + hh : HPG - 1;
-            dma4(a + row0 * H + grp * HPG, (tr * (unsigned)H + hx) * 4u,
-                 lds_addr(&sA[bf][0]) + (uint32_t)(wave * 256));
-        }
-        if (part <= 1) {
-            const u16* Xg = X + (row0 * H + grp * HPG) * P;
-            const unsigned xtr = xr <= lc ? xr : lc;
-#pragma unroll
-            for (int k = 0; k < XOPS; ++k) {
-                if ((k < (XOPS + 1) / 2) != (part == 0)) continue;
-                const unsigned hh = (unsigned)(k * kThreads) / XHT + xh;
-                const unsigned hx = hl0 + hh < (unsigned)HPG ? hl0 + hh : HPG - 1;
-                dma16(Xg, ((xtr * (unsigned)H + hx) * P + xlp * 8) * 2u,
-                      lds_addr(&sX[bf][0]) + (uint32_t)((k * kThreads + wave * 64) * 16));
-            }
-        } else {
-            const u16* Tg = (part == 2 ? B : C) + (row0 * G + grp) * N;
-            const u16* tile = part == 2 ? &sB[bf][0] : &sC[FULL ? bf : 0][0];
-#pragma unroll
-            for (int k = 0; k < BOPS; ++k) {
-                const unsigned rr = k * BROWS + br;
-                const unsigned tr = rr <= lc ? rr : lc;
-                dma16(Tg, (tr * (unsigned)GN + blp * 8) * 2u,
-                      lds_addr(tile) + (uint32_t)((k * kThreads + wave * 64) * 16));
-            }
+            dma16(Xg, ((tr * (unsigned)H + hx) * P + xlp * 8) * 2u,
+                  lds_addr(&sX[bf][0]) + (uint32_t)((s0 + aw * 64) * 16));
         }
     };
-    auto dma_block = [&](int64_t c, int bf) {
-        dma_part(c, bf, 0);
-        dma_part(c, bf, 1);
-        dma_part(c, bf, 2);
-        if constexpr (FULL) dma_part(c, bf, 3);
+    auto copy_bc = [&](int64_t c, int bf, bool isB) {
+        const unsigned lc = (unsigned)block_last(c);
+        const u16* Tg = (isB ? B : C) + (((int64_t)b * L + c * kT) * G + grp) * N;
+        const u16* tile = isB ? &sB[bf][0] : &sC[FULL ? bf : 0][0];
+#pragma unroll
+        for (int k = 0; k < BOPS; ++k) {
+            const unsigned r = (unsigned)k * BRS + br0;
+            const unsigned tr = r <= lc ? r : lc;
+            const unsigned q = bq ^ (unsigned)swzbits<BPR>((int)r);
+            dma16(Tg, (tr * (unsigned)GN + q * 8) * 2u,
+                  lds_addr(tile) + (uint32_t)((k * kAuxThreads + aw * 64) * 16));
+        }
+    };
+    auto copy_a = [&](int64_t c, int bf) {   // slot s -> (step s / HW, head s % HW)
+        const unsigned lc = (unsigned)block_last(c);
+        const float* ag = a + ((int64_t)b * L + c * kT) * H + grp * HPG;
+#pragma unroll
+        for (int k = 0; k < AOPS; ++k) {
+            const unsigned s = (unsigned)k * kAuxThreads + at;
+            if ((unsigned)k * kAuxThreads + aw * 64 < (unsigned)(kT * HW)) {   // wave-uniform
+                const unsigned t = s / HW, hh = s % HW;
+                const unsigned tr = t <= lc ? t : lc;
+                const unsigned hx = hl0 + hh < (unsigned)HPG ? hl0 + hh : HPG - 1;
+                dma4(ag, (tr * (unsigned)H + hx) * 4u,
+                     lds_addr(&sA[bf][0]) + (uint32_t)((k * kAuxThreads + aw * 64) * 4));
+            }
+        }
     };
 
-    // ---- carried state: S^T tiles (rows n, columns p of this wave's tile) ----
+    // ---- carried state (state waves): S^T tiles (rows n, columns p of this wave's tile) ----
     f32x16 Sacc[NTL];
 #pragma unroll
     for (int nt = 0; nt < NTL; ++nt) Sacc[nt] = zero16();
-    if constexpr (FULL) {
+    if (aux) {
+        if (c_begin < c_end) {
+            copy_a(c_begin, 0);
+            copy_x(c_begin, 0);
+            copy_bc(c_begin, 0, true);
+            if constexpr (FULL) copy_bc(c_begin, 0, false);
+        }
+    } else if constexpr (FULL) {
         if (src.Sin) {
             const float* S0 = src.Sin + b * src.bstride + seg * src.sstride + (int64_t)h * PN;
 #pragma unroll
@@ -363,92 +382,56 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
     //   Sacc'   = Sacc + B^T X~,   ld' = ld + Lam2,
     // so stages 2 and 5 share one accumulator, the scores need only the causal
     // mask (and so are the same for every head), and one per-step factor
-    // scales the output.  Each 32-step half of the block is checked on its own:
-    // a half whose prefix sums (relative to its start) lie in [-neg, pos] keeps
-    // every weight exponent -ld - cs2_j and output exponent cs2_i + ld within
-    // +-kRange exactly when ld lies in [neg - kRange, kRange - pos] (neg and
-    // pos follow from the half's total and its sum of |a|).  When the scale
-    // reached at a half's start falls outside that interval it is re-based to
-    // the interval's centre, -Lam_h / 2: at the block start by multiplying
-    // Sacc, half-way by multiplying Sacc between the halves of stage 3 and the
-    // second row block's accumulator between the first and second column tiles
-    // of stage 2, after which the second half's X~ and output factors use its
-    // own prefix sums.  Such a scale exists when the half's spread neg + pos
-    // is at most 2 kRange (kSpan keeps a margin so the factor between the two
-    // halves' references stays below 2^127).  Only a block with a wider half
-    // takes the direct form: per-element decay of the shared scores, then
-    // Sacc' = 2^(ld + Lam2) Sacc + B^T (w o X), ld' = 0.
+    // scales the output.  Each 16-step quarter of the block (one MFMA k step)
+    // is checked on its own: a quarter whose prefix sums (relative to its
+    // start) lie in [-neg, pos] keeps every weight exponent -ld - cs2_j and
+    // output exponent cs2_i + ld within +-kRange exactly when ld lies in
+    // [neg - kRange, kRange - pos] (neg and pos follow from the quarter's
+    // total and its sum of |a|).  When the scale reached at a quarter's start
+    // falls outside that interval it is re-based to the interval's centre,
+    // -Lam_q / 2: at the block start by multiplying Sacc (and the stage-5
+    // output, which is formed before the scale is known), inside the block by
+    // multiplying Sacc between the quarters' stage-3 products and the output
+    // accumulators of the rows from that quarter on between the quarters'
+    // stage-2 products; that quarter's X~ and output factors then use its own
+    // prefix sums.  Such a scale exists when the quarter's spread neg + pos is
+    // at most 2 kRange (kSpan keeps a margin so the factor between two
+    // quarters' references stays below 2^127).  Only a block with a wider
+    // quarter takes the direct form: per-element decay of the shared scores,
+    // then Sacc' = 2^(ld + Lam2) Sacc + B^T (w o X), ld' = 0.
+    constexpr int kQ = 4;          // 16-step quarters of a block (one MFMA k step each)
     constexpr float kRange = 64.f;
     constexpr float kSpan = 2.f * kRange - 8.f;
     auto fits = [](float l, float absh, float lamh_) {
         return l >= 0.5f * (absh - lamh_) - kRange && l <= kRange - 0.5f * (absh + lamh_);
     };
     float ld = 0.f;
-    // This block's Y^T in bf16 ([row block][4-entry group]; lane = step), and
-    // the previous block's Y re-laid out through LDS so that copy k of a lane
-    // holds 16 contiguous bytes of step 16k + lane/4: a store then covers 16
-    // steps x 64 bytes instead of 64 scattered 8-byte pieces.
-    uint2 Yb[2][4];
-    u32x4 Yr[4];
+    // Y of a block goes out from registers at the block's end: Y^T is re-laid
+    // out through this wave's own X slice (dead after stage 3) so that copy k
+    // of a lane holds 16 contiguous bytes of step 16k + lane/4, and a store
+    // covers 16 steps x 64 bytes.
     const uint32_t yoff = (uint32_t)(((lane >> 2) * H + h) * P + pc + 8 * (lane & 3));
-    auto store_y = [&](int64_t c) {
-        if (!hvalid) return;
-        const int lc = block_last(c);
-        u16* yblk = Y + ((int64_t)b * L + c * kT) * H * P;
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            if (16 * k + (lane >> 2) <= lc)
-                *reinterpret_cast<u32x4*>(yblk + (yoff + (uint32_t)(16 * k * H * P))) = Yr[k];
-    };
-
-    if (c_begin < c_end) dma_block(c_begin, 0);
 
     for (int64_t c = c_begin; c < c_end; ++c) {
         const int bf = (int)((c - c_begin) & 1);
         const int last = block_last(c);
-
-        vm_wait_all();  // this wave's copies of block c (and earlier stores) are done
-        sync_lds();     // ... and every wave's; buffer bf^1 and the score tiles are free
         const bool has_next = c + 1 < c_end;
-        if (has_next) dma_part(c + 1, bf ^ 1, 0);
-        if constexpr (FULL) {
-            if (c > c_begin) store_y(c - 1);
-        }
 
-        const u16* xT = &sX[bf][hw * kT * P];
+        if (aux) vm_wait_all();   // the copies of block c are done
+        sync_lds();               // ... and visible; buffer bf^1 and the score tiles are free
+
         const u16* bT = &sB[bf][0];
-
-        // ---- stage 1: prefix sums of a (lane = step), weights (log2 units) ----
-        const float av = lane <= last ? sA[bf][lane * HW + hw] : 0.f;
-        const float cs2 = wave_scan64(av, lane) * kLog2e;
-        const float lam2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs2), 63));
-        const float lamh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs2), 31));
-        // sums of |a| over each half bound the spread of cs2 within the half
-        const float absc = wave_scan64(fabsf(av), lane) * kLog2e;
-        const float abs_h0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(absc), 31));
-        const float abs_h1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(absc), 63)) - abs_h0;
-        const float lam_h1 = lam2 - lamh;
-        lam2_total += lam2;
-        const bool fast = abs_h0 <= kSpan && abs_h1 <= kSpan;   // wave-uniform
-        if (fast && !fits(ld, abs_h0, lamh)) {               // re-base the state scale
-            const float target = -0.5f * lamh;
-            const float f = fast_exp2(ld - target);
-#pragma unroll
-            for (int nt = 0; nt < NTL; ++nt) Sacc[nt] *= f;
-            ld = target;
-        }
-        const float ld_in = ld;                               // reference of the first half
-        const float ld_mid = ld_in + lamh;                    // scale reached half-way
-        const bool fold_mid = fast && !fits(ld_mid, abs_h1, lam_h1);
-        const float ld_h1 = fold_mid ? -0.5f * lam_h1 : ld_mid;   // reference of the second half
-        // state weights 2^(wsh - cs2_j)
-        const float wsh = fast ? (lane < 32 ? -ld_in : lamh - ld_h1) : lam2;
-        ld = fast ? ld_h1 + lam_h1 : 0.f;
-        sCs[wave][lane] = cs2;
+        const u16* xT = &sX[bf][hw * kT * P];
+        u16* xTm = &sX[bf][hw * kT * P];
+        // X^T fragments of this wave's head-dim tile (lane = p, k = step in the
+        // accumulator row order); after weight_rows they are X~ = w o X.
+        auto xfrag = [&](int J, int ks) {
+            const u16* t = xT + (32 * J + 16 * ks) * P;
+            return join8(lds_tr4(t + xoff[0]), lds_tr4(t + xoff[1]));
+        };
         // The state weight of step j is applied to X in place: lane j scales row
         // j of this wave's head-dim tile (its own 32 columns, 4 pieces), so the
         // transposing reads that follow yield w o X directly.
-        u16* xTm = &sX[bf][hw * kT * P];
         auto weight_rows = [&](float wr) {
             u16* rowp = xTm + lane * P;
 #pragma unroll
@@ -463,168 +446,242 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
                 *q = o;
             }
         };
-        const float wrow = lane <= last ? fast_exp2(wsh - cs2) : 0.f;
-        if (fast) weight_rows(wrow);
-        if (has_next) dma_part(c + 1, bf ^ 1, 1);
 
-        if constexpr (FULL) {
-            // ---- shared masked scores: wave t < 3 forms tile t = (I, J) in
-            // {(0,0), (1,0), (1,1)} as S^T = B_J C_I^T, stored [i][j] in bf16 ----
-            if (wave < 3) {
-                const int I = wave > 0 ? 1 : 0, J = wave == 2 ? 1 : 0;
+        // state-wave values that live across the score barrier
+        bool fast = true;
+        bool fold[kQ] = {false, false, false, false};
+        float rq[kQ] = {0.f, 0.f, 0.f, 0.f};
+        float ld_in = 0.f, lam2 = 0.f, wrow = 0.f, pre = 1.f;
+        f32x16 Yt[2] = {zero16(), zero16()};
+
+        if (aux) {
+            // ---- copies of block c+1 (X now, the rest after the scores) ----
+            if (has_next) copy_x(c + 1, bf ^ 1);
+            if constexpr (FULL) {
+                // ---- shared masked scores: aux wave 0 forms tiles 0 and 1, aux
+                // wave 1 tile 2, tile t = (I, J) in {(0,0), (1,0), (1,1)} as
+                // S^T = B_J C_I^T, stored [i][j] in bf16 ----
                 const u16* cT = &sC[bf][0];
-                f32x16 St = zero16();
+#pragma unroll
+                for (int t = 0; t < 3; ++t) {
+                    if ((t < 2) != (aw == 0)) continue;
+                    const int I = t > 0 ? 1 : 0, J = t == 2 ? 1 : 0;
+                    f32x16 St = zero16();
+#pragma unroll
+                    for (int nt = 0; nt < NTL; ++nt)
+#pragma unroll
+                        for (int hf = 0; hf < 2; ++hf) St = mfma32(rowfrag(bT, J, nt, hf), rowfrag(cT, I, nt, hf), St);
+                    // row j of accumulator register r: 8(r/4) + 4*g2 + r%4; lane = i.
+                    // Masked entries (j > i on the diagonal) are replaced, never multiplied.
+                    const bool diag = I == J;
+                    u16* prow = &sP[t][l32 * kPRow];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int j0 = 8 * q + 4 * g2;
+                        float v[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v[e] = (!diag || j0 + e <= l32) ? St[4 * q + e] : 0.f;
+                        *reinterpret_cast<uint2*>(prow + j0) = make_uint2(pack2(v[0], v[1]), pack2(v[2], v[3]));
+                    }
+                }
+            }
+        } else {
+            // ---- stage 1: prefix sums of a (lane = step), weights (log2 units) ----
+            const float av = lane <= last ? sA[bf][lane * HW + hw] : 0.f;
+            const float cs2 = wave_scan64(av, lane) * kLog2e;
+            // sums of |a| over each quarter bound the spread of cs2 within it
+            const float absc = wave_scan64(fabsf(av), lane) * kLog2e;
+            float base[kQ + 1], lamq[kQ], absq[kQ];   // base[q]: cs2 before quarter q
+            base[0] = 0.f;
+            float abs_prev = 0.f;
+#pragma unroll
+            for (int q = 0; q < kQ; ++q) {
+                base[q + 1] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs2), 16 * q + 15));
+                const float ac = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(absc), 16 * q + 15));
+                lamq[q] = base[q + 1] - base[q];
+                absq[q] = ac - abs_prev;
+                abs_prev = ac;
+                fast = fast && absq[q] <= kSpan;                  // wave-uniform
+            }
+            lam2 = base[kQ];
+            lam2_total += lam2;
+            if (fast && !fits(ld, absq[0], lamq[0])) {           // re-base the state scale
+                const float target = -0.5f * lamq[0];
+                pre = fast_exp2(ld - target);
+                ld = target;
+            }
+            ld_in = ld;
+            // reference of each quarter; fold[q]: re-based at the start of quarter q
+            // (the accumulators then take the factor 2^(rq[q]))
+            float ldq[kQ];
+            ldq[0] = ld_in;
+#pragma unroll
+            for (int q = 1; q < kQ; ++q) {
+                const float raw = ldq[q - 1] + lamq[q - 1];
+                fold[q] = fast && !fits(raw, absq[q], lamq[q]);
+                ldq[q] = fold[q] ? -0.5f * lamq[q] : raw;
+                rq[q] = raw - ldq[q];
+            }
+            ld = fast ? ldq[kQ - 1] + lamq[kQ - 1] : 0.f;
+            // this lane's step j: quarter qj; state weight 2^(wsh - cs2_j), and
+            // (fast form) output exponent cs2_j - base + reference
+            const int qj = lane >> 4;
+            const float bj = qj == 0 ? base[0] : qj == 1 ? base[1] : qj == 2 ? base[2] : base[3];
+            const float lj = qj == 0 ? ldq[0] : qj == 1 ? ldq[1] : qj == 2 ? ldq[2] : ldq[3];
+            const float wsh = fast ? bj - lj : lam2;
+            sCs[sw][lane] = fast ? cs2 - bj + lj : cs2;
+            wrow = lane <= last ? fast_exp2(wsh - cs2) : 0.f;
+            if (fast) weight_rows(wrow);
+
+            if constexpr (FULL) {
+                // ---- stage 5 (unscaled, at the block's incoming scale): Y^T = Sacc C^T ----
+                const u16* cT = &sC[bf][0];
 #pragma unroll
                 for (int nt = 0; nt < NTL; ++nt)
 #pragma unroll
                     for (int hf = 0; hf < 2; ++hf) {
-                        St = mfma32(rowfrag(bT, J, nt, hf), rowfrag(cT, I, nt, hf), St);
+                        const bf16x8 Sf = acc_half(Sacc[nt], hf);
+#pragma unroll
+                        for (int I = 0; I < 2; ++I) Yt[I] = mfma32(Sf, rowfrag(cT, I, nt, hf), Yt[I]);
                     }
-                // row j of accumulator register r: 8(r/4) + 4*g2 + r%4; lane = i.
-                // Masked entries (j > i on the diagonal) are replaced, never multiplied.
-                const bool diag = I == J;
-                u16* prow = &sP[wave][l32 * kPRow];
+            }
+            if (pre != 1.f) {   // the block's re-based scale (fast form only)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int j0 = 8 * q + 4 * g2;
-                    float v[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = (!diag || j0 + e <= l32) ? St[4 * q + e] : 0.f;
-                    *reinterpret_cast<uint2*>(prow + j0) = make_uint2(pack2(v[0], v[1]), pack2(v[2], v[3]));
-                }
+                for (int nt = 0; nt < NTL; ++nt) Sacc[nt] *= pre;
+                Yt[0] *= pre;
+                Yt[1] *= pre;
             }
         }
 
-        // X^T fragments of this wave's head-dim tile (lane = p, k = step in the
-        // accumulator row order); after weight_rows they are X~ = w o X.
-        auto xfrag = [&](int J, int ks) {
-            const u16* t = xT + (32 * J + 16 * ks) * P;
-            return join8(lds_tr4(t + xoff[0]), lds_tr4(t + xoff[1]));
-        };
+        if constexpr (FULL) sync_lds();  // the shared score tiles are complete
 
-        if constexpr (FULL) {
-            const u16* cT = &sC[bf][0];
-            // ---- stage 5 (unscaled): Y^T = Sacc C^T for both row blocks ----
-            f32x16 Yt[2] = {zero16(), zero16()};
-#pragma unroll
-            for (int nt = 0; nt < NTL; ++nt)
-#pragma unroll
-                for (int hf = 0; hf < 2; ++hf) {
-                    const bf16x8 Sf = acc_half(Sacc[nt], hf);
-#pragma unroll
-                    for (int I = 0; I < 2; ++I) {
-                        Yt[I] = mfma32(Sf, rowfrag(cT, I, nt, hf), Yt[I]);
-                    }
-                }
-            const float e0 = fast_exp2(sCs[wave][l32] + ld_in);        // output factors
-            const float e1 = fast_exp2(sCs[wave][32 + l32] - lamh + ld_h1);
-
-            if (has_next) dma_part(c + 1, bf ^ 1, 2);
-            sync_lds();  // the shared score tiles are complete
-            if (has_next) dma_part(c + 1, bf ^ 1, 3);
-            // P tile t as the B operand of k step ks (lane = i, k = j)
-            auto ptile = [&](int t, int ks) {
-                const u16* prow = &sP[t][l32 * kPRow + 16 * ks + 4 * g2];
-                return join8(*reinterpret_cast<const u32x2*>(prow), *reinterpret_cast<const u32x2*>(prow + 8));
-            };
-            if (fast) {
-                // ---- stage 2: Y^T += X~^T P, then the per-step factor ----
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const bf16x8 xw0 = xfrag(0, ks);
-                    Yt[0] = mfma32(xw0, ptile(0, ks), Yt[0]);
-                    Yt[1] = mfma32(xw0, ptile(1, ks), Yt[1]);
-                }
-                if (fold_mid) Yt[1] *= fast_exp2(ld_mid - ld_h1);   // to the second half's reference
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) Yt[1] = mfma32(xfrag(1, ks), ptile(2, ks), Yt[1]);
-                Yt[0] *= e0;
-                Yt[1] *= e1;
-            } else {
-                Yt[0] *= e0;
-                Yt[1] *= e1;
-                // ---- stage 2, direct form: decay 2^(cs2_i - cs2_j) on the shared scores ----
-                // (masked entries stay replaced by zero: their exponent may overflow)
-                auto decayed = [&](int t, int J, int ks, float csi) {
-                    const u32x4 u = as_u32x4(ptile(t, ks));
-                    const int jl = 16 * ks + 4 * g2;              // j within the tile, element 0
-                    const f32x4 c0 = *reinterpret_cast<const f32x4*>(&sCs[wave][32 * J + jl]);
-                    const f32x4 c1 = *reinterpret_cast<const f32x4*>(&sCs[wave][32 * J + jl + 8]);
-                    const float cj[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
-                    const bool diag = t != 1;
-                    float v[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int j = jl + (e < 4 ? e : 4 + e);
-                        const float x = __uint_as_float(e & 1 ? (u[e >> 1] & 0xffff0000u) : (u[e >> 1] << 16));
-                        v[e] = (!diag || j <= l32) ? x * fast_exp2(csi - cj[e]) : 0.f;
-                    }
-                    return as_bf16x8(u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])});
+        if (aux) {
+            if (has_next) {
+                copy_a(c + 1, bf ^ 1);
+                copy_bc(c + 1, bf ^ 1, true);
+                if constexpr (FULL) copy_bc(c + 1, bf ^ 1, false);
+            }
+        } else {
+            uint2 Yb[2][4];
+            if constexpr (FULL) {
+                // output factors (the direct form scales only the state's part here)
+                const float e0 = fast_exp2(sCs[sw][l32] + (fast ? 0.f : ld_in));
+                const float e1 = fast_exp2(sCs[sw][32 + l32] + (fast ? 0.f : ld_in));
+                // P tile t as the B operand of k step ks (lane = i, k = j)
+                auto ptile = [&](int t, int ks) {
+                    const u16* prow = &sP[t][l32 * kPRow + 16 * ks + 4 * g2];
+                    return join8(*reinterpret_cast<const u32x2*>(prow), *reinterpret_cast<const u32x2*>(prow + 8));
                 };
-                const float csi0 = sCs[wave][l32], csi1 = sCs[wave][32 + l32];
+                if (fast) {
+                    // ---- stage 2: Y^T += X~^T P, then the per-step factor.  The
+                    // k steps are the quarters in order; at a re-based quarter the
+                    // rows from that quarter on move to its reference ----
+                    const bool upper = l32 >= 16;        // this lane's row is in the tile's second quarter
+                    const bf16x8 x00 = xfrag(0, 0);
+                    Yt[0] = mfma32(x00, ptile(0, 0), Yt[0]);
+                    Yt[1] = mfma32(x00, ptile(1, 0), Yt[1]);
+                    if (fold[1]) {
+                        const float f = fast_exp2(rq[1]);
+                        Yt[0] *= upper ? f : 1.f;
+                        Yt[1] *= f;
+                    }
+                    const bf16x8 x01 = xfrag(0, 1);
+                    Yt[0] = mfma32(x01, ptile(0, 1), Yt[0]);
+                    Yt[1] = mfma32(x01, ptile(1, 1), Yt[1]);
+                    if (fold[2]) Yt[1] *= fast_exp2(rq[2]);
+                    Yt[1] = mfma32(xfrag(1, 0), ptile(2, 0), Yt[1]);
+                    if (fold[3]) Yt[1] *= upper ? fast_exp2(rq[3]) : 1.f;
+                    Yt[1] = mfma32(xfrag(1, 1), ptile(2, 1), Yt[1]);
+                    Yt[0] *= e0;
+                    Yt[1] *= e1;
+                } else {
+                    Yt[0] *= e0;
+                    Yt[1] *= e1;
+                    // ---- stage 2, direct form: decay 2^(cs2_i - cs2_j) on the shared scores ----
+                    // (masked entries stay replaced by zero: their exponent may overflow)
+                    auto decayed = [&](int t, int J, int ks, float csi) {
+                        const u32x4 u = as_u32x4(ptile(t, ks));
+                        const int jl = 16 * ks + 4 * g2;              // j within the tile, element 0
+                        const f32x4 c0 = *reinterpret_cast<const f32x4*>(&sCs[sw][32 * J + jl]);
+                        const f32x4 c1 = *reinterpret_cast<const f32x4*>(&sCs[sw][32 * J + jl + 8]);
+                        const float cj[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+                        const bool diag = t != 1;
+                        float v[8];
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    // one tile at a time (this rare path must not raise the
-                    // kernel's register budget)
-                    const bf16x8 xa0 = xfrag(0, ks);
-                    Yt[0] = mfma32(xa0, decayed(0, 0, ks, csi0), Yt[0]);
-                    __builtin_amdgcn_sched_barrier(0);
-                    Yt[1] = mfma32(xa0, decayed(1, 0, ks, csi1), Yt[1]);
-                    __builtin_amdgcn_sched_barrier(0);
-                    Yt[1] = mfma32(xfrag(1, ks), decayed(2, 1, ks, csi1), Yt[1]);
-                    __builtin_amdgcn_sched_barrier(0);
+                        for (int e = 0; e < 8; ++e) {
+                            const int j = jl + (e < 4 ? e : 4 + e);
+                            const float x = __uint_as_float(e & 1 ? (u[e >> 1] & 0xffff0000u) : (u[e >> 1] << 16));
+                            v[e] = (!diag || j <= l32) ? x * fast_exp2(csi - cj[e]) : 0.f;
+                        }
+                        return as_bf16x8(u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])});
+                    };
+                    const float csi0 = sCs[sw][l32], csi1 = sCs[sw][32 + l32];
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks) {
+                        // one tile at a time (this rare path must not raise the
+                        // kernel's register budget)
+                        const bf16x8 xa0 = xfrag(0, ks);
+                        Yt[0] = mfma32(xa0, decayed(0, 0, ks, csi0), Yt[0]);
+                        __builtin_amdgcn_sched_barrier(0);
+                        Yt[1] = mfma32(xa0, decayed(1, 0, ks, csi1), Yt[1]);
+                        __builtin_amdgcn_sched_barrier(0);
+                        Yt[1] = mfma32(xfrag(1, ks), decayed(2, 1, ks, csi1), Yt[1]);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
                 }
+                // Y^T to bf16
+#pragma unroll
+                for (int I = 0; I < 2; ++I)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        Yb[I][q] = make_uint2(pack2(Yt[I][4 * q], Yt[I][4 * q + 1]), pack2(Yt[I][4 * q + 2], Yt[I][4 * q + 3]));
             }
-            // Y^T to bf16, stored at the top of the next block (or after the loop)
-#pragma unroll
-            for (int I = 0; I < 2; ++I)
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    Yb[I][q] = make_uint2(pack2(Yt[I][4 * q], Yt[I][4 * q + 1]), pack2(Yt[I][4 * q + 2], Yt[I][4 * q + 3]));
-        }
 
-        if constexpr (!FULL) {
-            if (has_next) dma_part(c + 1, bf ^ 1, 2);
-        }
-        // ---- stages 3 + 4: Sacc' = (direct form: 2^(ld + Lam2)) Sacc + B^T X~ ----
-        if (!fast) {
-            weight_rows(wrow);   // after the direct-form stage 2, which reads X unweighted
-            const float f = fast_exp2(ld_in + lam2);
-#pragma unroll
-            for (int nt = 0; nt < NTL; ++nt) Sacc[nt] *= f;
-        }
-#pragma unroll
-        for (int J = 0; J < 2; ++J) {
-            if (J == 1 && fold_mid) {   // the first half's update at the second half's reference
-                const float f = fast_exp2(ld_mid - ld_h1);
+            // ---- stages 3 + 4: Sacc' = (direct form: 2^(ld + Lam2)) Sacc + B^T X~ ----
+            if (!fast) {
+                weight_rows(wrow);   // after the direct-form stage 2, which reads X unweighted
+                const float f = fast_exp2(ld_in + lam2);
 #pragma unroll
                 for (int nt = 0; nt < NTL; ++nt) Sacc[nt] *= f;
             }
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const bf16x8 xw = xfrag(J, ks);
+            for (int J = 0; J < 2; ++J) {
 #pragma unroll
-                for (int nt = 0; nt < NTL; ++nt) {
-                    const u16* t = bT + (32 * J + 16 * ks) * N;
-                    const bf16x8 Af = join8(lds_tr4(t + toff[nt][0]), lds_tr4(t + toff[nt][1]));
-                    Sacc[nt] = mfma32(Af, xw, Sacc[nt]);
+                for (int ks = 0; ks < 2; ++ks) {
+                    if (fold[2 * J + ks]) {   // the state so far at this quarter's reference
+                        const float f = fast_exp2(rq[2 * J + ks]);
+#pragma unroll
+                        for (int nt = 0; nt < NTL; ++nt) Sacc[nt] *= f;
+                    }
+                    const bf16x8 xw = xfrag(J, ks);
+#pragma unroll
+                    for (int nt = 0; nt < NTL; ++nt) {
+                        const u16* t = bT + (32 * J + 16 * ks) * N;
+                        const bf16x8 Af = join8(lds_tr4(t + toff[nt][0]), lds_tr4(t + toff[nt][1]));
+                        Sacc[nt] = mfma32(Af, xw, Sacc[nt]);
+                    }
+                }
+            }
+            if constexpr (FULL) {
+                // Y^T through this wave's own X slice, which is dead after stage 3
+#pragma unroll
+                for (int I = 0; I < 2; ++I)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        *reinterpret_cast<uint2*>(xTm + swz<XPR>(32 * I + l32, pc + 8 * q + 4 * g2)) = Yb[I][q];
+                u32x4 Yr[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    Yr[k] = *reinterpret_cast<const u32x4*>(xTm + swz<XPR>(16 * k + (lane >> 2), pc + 8 * (lane & 3)));
+                if (hvalid) {
+                    u16* yblk = Y + ((int64_t)b * L + c * kT) * H * P;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        if (16 * k + (lane >> 2) <= last)
+                            *reinterpret_cast<u32x4*>(yblk + (yoff + (uint32_t)(16 * k * H * P))) = Yr[k];
                 }
             }
         }
-        if constexpr (FULL) {
-            // Y^T through this wave's own X slice, which is dead after stage 3
-#pragma unroll
-            for (int I = 0; I < 2; ++I)
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    *reinterpret_cast<uint2*>(xTm + swz<XPR>(32 * I + l32, pc + 8 * q + 4 * g2)) = Yb[I][q];
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                Yr[k] = *reinterpret_cast<const u32x4*>(xTm + swz<XPR>(16 * k + (lane >> 2), pc + 8 * (lane & 3)));
-        }
-    }
-    if constexpr (FULL) {
-        if (c_begin < c_end) store_y(c_end - 1);
     }
 
     // ---- epilogue: final state (full pass, last segment) or segment summary ----
@@ -655,7 +712,7 @@ bool mfma_supported(int64_t Q, int64_t P, int64_t N) {
     return (Q == 64 || Q == 128 || Q == 256) && (P == 32 || P == 64) && (N == 64 || N == 128);
 }
 
-int64_t mfma_heads_per_workgroup(int64_t P, int64_t N) { (void)N; return kWaves / (P / 32); }
+int64_t mfma_heads_per_workgroup(int64_t P, int64_t N) { (void)N; return kStateWaves / (P / 32); }
 
 #define SSD_MFMA_DISPATCH(MACRO)                     \
     if (s.P == 64 && s.N == 128) MACRO(64, 128)      \

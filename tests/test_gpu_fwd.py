@@ -123,18 +123,18 @@ def test_strong_decay_no_nan():
 
 @pytest.mark.parametrize("seg", [0, 1])
 def test_decay_regimes_per_head(seg):
-    # One head per decay regime of the 64-step blocks (log2-decay per 32-step
-    # half ~2.3, 92, 55, 138, growth, mixed per half, recipe, rare deep
+    # One head per decay regime of the 64-step blocks (log2-decay per 16-step
+    # quarter ~1.2, 69, 28, 138, growth, mixed per half, recipe, rare deep
     # drops), so the output and state scales are re-based at block starts and
-    # at half-way points, and the direct form runs for some blocks.
+    # at quarter boundaries, and the direct form runs for some blocks.
     sh = si.FwdShape(2, 64 * 12 + 17, 8, 64, 128, 1, 256, si.BF16)
     d = si.make_fwd(sh, seed=11)
     a = d["a"]
     rng = np.random.default_rng(5)
     a[:, :, 0] = -0.05
-    a[:, :, 1] = -2.0
+    a[:, :, 1] = -3.0
     a[:, :, 2] = -1.2
-    a[:, :, 3] = -3.0
+    a[:, :, 3] = -6.0
     a[:, :, 4] = 0.05
     halves = rng.choice(np.array([-0.01, -0.6, -1.2, -2.5, -3.5], dtype=np.float32),
                         size=(sh.batch, sh.seqlen // 32 + 1))
