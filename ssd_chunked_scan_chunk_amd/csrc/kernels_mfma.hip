@@ -434,16 +434,20 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
         // transposing reads that follow yield w o X directly.
         auto weight_rows = [&](float wr) {
             u16* rowp = xTm + lane * P;
+            u32x4* q[4];
+            u32x4 u[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {   // all reads first: one LDS round trip
+                q[k] = reinterpret_cast<u32x4*>(rowp + (((pc >> 3) + k) ^ swzbits<XPR>(lane)) * 8);
+                u[k] = *q[k];
+            }
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const int piece = ((pc >> 3) + k) ^ swzbits<XPR>(lane);
-                u32x4* q = reinterpret_cast<u32x4*>(rowp + piece * 8);
-                const u32x4 u = *q;
                 u32x4 o;
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    o[e] = pack2(wr * __uint_as_float(u[e] << 16), wr * __uint_as_float(u[e] & 0xffff0000u));
-                *q = o;
+                    o[e] = pack2(wr * __uint_as_float(u[k][e] << 16), wr * __uint_as_float(u[k][e] & 0xffff0000u));
+                *q[k] = o;
             }
         };
 
@@ -486,6 +490,18 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
                 }
             }
         } else {
+            if constexpr (FULL) {
+                // ---- stage 5 (unscaled, at the block's incoming scale): Y^T = Sacc C^T ----
+                const u16* cT = &sC[bf][0];
+#pragma unroll
+                for (int nt = 0; nt < NTL; ++nt)
+#pragma unroll
+                    for (int hf = 0; hf < 2; ++hf) {
+                        const bf16x8 Sf = acc_half(Sacc[nt], hf);
+#pragma unroll
+                        for (int I = 0; I < 2; ++I) Yt[I] = mfma32(Sf, rowfrag(cT, I, nt, hf), Yt[I]);
+                    }
+            }
             // ---- stage 1: prefix sums of a (lane = step), weights (log2 units) ----
             const float av = lane <= last ? sA[bf][lane * HW + hw] : 0.f;
             const float cs2 = wave_scan64(av, lane) * kLog2e;
@@ -501,15 +517,14 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
                 lamq[q] = base[q + 1] - base[q];
                 absq[q] = ac - abs_prev;
                 abs_prev = ac;
-                fast = fast && absq[q] <= kSpan;                  // wave-uniform
+                fast = fast & (absq[q] <= kSpan);                 // wave-uniform
             }
             lam2 = base[kQ];
             lam2_total += lam2;
-            if (fast && !fits(ld, absq[0], lamq[0])) {           // re-base the state scale
-                const float target = -0.5f * lamq[0];
-                pre = fast_exp2(ld - target);
-                ld = target;
-            }
+            const bool rebase = fast & !fits(ld, absq[0], lamq[0]);   // re-base the state scale
+            const float target = -0.5f * lamq[0];
+            pre = rebase ? fast_exp2(ld - target) : 1.f;
+            ld = rebase ? target : ld;
             ld_in = ld;
             // reference of each quarter; fold[q]: re-based at the start of quarter q
             // (the accumulators then take the factor 2^(rq[q]))
@@ -518,7 +533,7 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
 #pragma unroll
             for (int q = 1; q < kQ; ++q) {
                 const float raw = ldq[q - 1] + lamq[q - 1];
-                fold[q] = fast && !fits(raw, absq[q], lamq[q]);
+                fold[q] = fast & !fits(raw, absq[q], lamq[q]);
                 ldq[q] = fold[q] ? -0.5f * lamq[q] : raw;
                 rq[q] = raw - ldq[q];
             }
@@ -531,20 +546,9 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
             const float wsh = fast ? bj - lj : lam2;
             sCs[sw][lane] = fast ? cs2 - bj + lj : cs2;
             wrow = lane <= last ? fast_exp2(wsh - cs2) : 0.f;
-            if (fast) weight_rows(wrow);
-
-            if constexpr (FULL) {
-                // ---- stage 5 (unscaled, at the block's incoming scale): Y^T = Sacc C^T ----
-                const u16* cT = &sC[bf][0];
-#pragma unroll
-                for (int nt = 0; nt < NTL; ++nt)
-#pragma unroll
-                    for (int hf = 0; hf < 2; ++hf) {
-                        const bf16x8 Sf = acc_half(Sacc[nt], hf);
-#pragma unroll
-                        for (int I = 0; I < 2; ++I) Yt[I] = mfma32(Sf, rowfrag(cT, I, nt, hf), Yt[I]);
-                    }
-            }
+            // (the direct form weights X only after its stage 2; scaling by 1
+            // and rounding back leaves X unchanged)
+            weight_rows(fast ? wrow : 1.f);
             if (pre != 1.f) {   // the block's re-based scale (fast form only)
 #pragma unroll
                 for (int nt = 0; nt < NTL; ++nt) Sacc[nt] *= pre;
