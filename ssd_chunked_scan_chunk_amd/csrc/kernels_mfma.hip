@@ -50,14 +50,18 @@
 //    scores.
 //  * Every product is v_mfma_f32_32x32x16_bf16 (operand lane l holds row or
 //    column l%32 and 8 k values of group l/32; the accumulator holds column
-//    l%32, rows 8(r/4) + 4(l/32) + r%4 in register r).  Contractions use the
-//    k order {4g..4g+3, 8+4g..8+4g+3} within each 16-wide k step (g = l/32),
-//    which is exactly the row order of an accumulator's registers: the fp32
-//    state becomes the stage-5 operand in place (rounded to bf16).  Operands
-//    with the contraction along memory rows (X^T, B^T) come from
-//    ds_read_b64_tr_b16: in each 16-lane group, source lane m names row
-//    R(m/4), columns 4(m%4)..+3, and output lane i receives column i of rows
-//    R(0..3).
+//    l%32, rows 8(r/4) + 4(l/32) + r%4 in register r).  Contractions take k
+//    in natural order (group g holds k = 8g..8g+7 of each 16-wide step),
+//    except stage 5, whose k order {4g..4g+3, 8+4g..8+4g+3} is the row order
+//    of an accumulator's registers: the fp32 state becomes the stage-5
+//    operand in place (rounded to bf16), and the C rows are matched to it by
+//    a 16-byte read plus a half-swap between lanes l and l^32
+//    (v_permlane32_swap).  16-byte row reads keep every LDS read of a row
+//    tile conflict-free; 8-byte reads of 32 rows cannot be (two rows share
+//    each 16-byte bank slot).  Operands with the contraction along memory
+//    rows (X^T, B^T) come from ds_read_b64_tr_b16: in each 16-lane group,
+//    source lane m names row R(m/4), columns 4(m%4)..+3, and output lane i
+//    receives column i of rows R(0..3).
 //  * Scores are formed transposed, S^T = B C^T, so lane = step i; outputs are
 //    Y^T tiles, a lane holding 4 consecutive head-dim entries of one step.
 //  * LDS tiles are row-major with their 16-byte pieces permuted per row
@@ -88,7 +92,7 @@ constexpr int kWaves = 8;    // wavefronts per workgroup (two per SIMD)
 constexpr int kStateWaves = 6;                   // waves that carry head states
 constexpr int kAuxThreads = 64 * (kWaves - kStateWaves);   // copy and score waves
 constexpr int kThreads = 64 * kWaves;
-constexpr int kPRow = 36;    // padded row (elements) of a shared 32x32 bf16 score tile
+constexpr int kPRow = 40;    // padded row (elements) of a shared 32x32 bf16 score tile (16-byte aligned)
 
 template <int P, int N>
 struct MfmaCfg {
@@ -265,29 +269,40 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
     // Per-lane element offsets into the swizzled LDS tiles, loop invariant.
     // Tile row bases that are multiples of 16 rows (and so of the swizzle
     // period) are added per use as immediates.
-    //  roff: row reads of B / C (lane = row l32, 8 bytes at column
-    //        nt*32 + 16hf + 8sec + 4*g2);
-    //  toff: transposing reads of B (source row 4*g2 + trow + 8s, columns
+    //  roff: row reads of B / C (lane = row l32, the 16 bytes at column
+    //        nt*32 + 16hf + 8*g2);
+    //  toff: transposing reads of B (source row 8*g2 + 4s + trow, columns
     //        nt*32 + tcol);  xoff: the same of this wave's X head-dim tile.
-    uint32_t roff[NTL][2][2], toff[NTL][2], xoff[2];
+    uint32_t roff[NTL][2], toff[NTL][2], xoff[2];
 #pragma unroll
     for (int nt = 0; nt < NTL; ++nt)
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-            for (int sec = 0; sec < 2; ++sec)
-                roff[nt][hf][sec] = (uint32_t)swz<BPR>(l32, nt * 32 + 16 * hf + 8 * sec + 4 * g2);
+        for (int hf = 0; hf < 2; ++hf) roff[nt][hf] = (uint32_t)swz<BPR>(l32, nt * 32 + 16 * hf + 8 * g2);
 #pragma unroll
     for (int sh = 0; sh < 2; ++sh) {
-        const int r = 4 * g2 + trow + 8 * sh;
+        const int r = 8 * g2 + 4 * sh + trow;
 #pragma unroll
         for (int nt = 0; nt < NTL; ++nt) toff[nt][sh] = (uint32_t)swz<BPR>(r, nt * 32 + tcol);
         xoff[sh] = (uint32_t)swz<XPR>(r, pc + tcol);
     }
-    auto rowfrag = [&](const u16* tile, int I, int nt, int hf) {   // rows 32I + lane
-        const u16* t = tile + 32 * I * N;
-        return join8(*reinterpret_cast<const u32x2*>(t + roff[nt][hf][0]),
-                     *reinterpret_cast<const u32x2*>(t + roff[nt][hf][1]));
+    // Row fragment of B or C: row 32I + l32, columns nt*32 + 16hf + 8*g2 .. +7
+    // (k in natural order within the 16-wide step hf).
+    auto rowfrag = [&](const u16* tile, int I, int nt, int hf) {
+        return as_bf16x8(*reinterpret_cast<const u32x4*>(tile + 32 * I * N + roff[nt][hf]));
+    };
+    // C as the stage-5 operand in the accumulator's k order: lane (l32, g2)
+    // needs columns 16hf + 4*g2 + {0..3, 8..11}.  It reads the 16-byte piece
+    // 16hf + 8*g2 .. +7 (conflict-free) and trades halves with lane l32 of the
+    // other wave half.
+    auto cfrag = [&](const u16* tile, int I, int nt, int hf) {
+        u32x4 u = as_u32x4(rowfrag(tile, I, nt, hf));
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+            const auto r = __builtin_amdgcn_permlane32_swap(u[d], u[d + 2], false, false);
+            u[d] = r[0];
+            u[d + 2] = r[1];
+        }
+        return as_bf16x8(u);
     };
 
     // ---- copies (aux waves only).  Copy k of aux thread at fills LDS slot
@@ -423,8 +438,8 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
         const u16* bT = &sB[bf][0];
         const u16* xT = &sX[bf][hw * kT * P];
         u16* xTm = &sX[bf][hw * kT * P];
-        // X^T fragments of this wave's head-dim tile (lane = p, k = step in the
-        // accumulator row order); after weight_rows they are X~ = w o X.
+        // X^T fragments of this wave's head-dim tile (lane = p, k = step);
+        // after weight_rows they are X~ = w o X.
         auto xfrag = [&](int J, int ks) {
             const u16* t = xT + (32 * J + 16 * ks) * P;
             return join8(lds_tr4(t + xoff[0]), lds_tr4(t + xoff[1]));
@@ -499,7 +514,7 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
                     for (int hf = 0; hf < 2; ++hf) {
                         const bf16x8 Sf = acc_half(Sacc[nt], hf);
 #pragma unroll
-                        for (int I = 0; I < 2; ++I) Yt[I] = mfma32(Sf, rowfrag(cT, I, nt, hf), Yt[I]);
+                        for (int I = 0; I < 2; ++I) Yt[I] = mfma32(Sf, cfrag(cT, I, nt, hf), Yt[I]);
                     }
             }
             // ---- stage 1: prefix sums of a (lane = step), weights (log2 units) ----
@@ -573,8 +588,7 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
                 const float e1 = fast_exp2(sCs[sw][32 + l32] + (fast ? 0.f : ld_in));
                 // P tile t as the B operand of k step ks (lane = i, k = j)
                 auto ptile = [&](int t, int ks) {
-                    const u16* prow = &sP[t][l32 * kPRow + 16 * ks + 4 * g2];
-                    return join8(*reinterpret_cast<const u32x2*>(prow), *reinterpret_cast<const u32x2*>(prow + 8));
+                    return as_bf16x8(*reinterpret_cast<const u32x4*>(&sP[t][l32 * kPRow + 16 * ks + 8 * g2]));
                 };
                 if (fast) {
                     // ---- stage 2: Y^T += X~^T P, then the per-step factor.  The
@@ -605,15 +619,15 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
                     // (masked entries stay replaced by zero: their exponent may overflow)
                     auto decayed = [&](int t, int J, int ks, float csi) {
                         const u32x4 u = as_u32x4(ptile(t, ks));
-                        const int jl = 16 * ks + 4 * g2;              // j within the tile, element 0
+                        const int jl = 16 * ks + 8 * g2;              // j within the tile, element 0
                         const f32x4 c0 = *reinterpret_cast<const f32x4*>(&sCs[sw][32 * J + jl]);
-                        const f32x4 c1 = *reinterpret_cast<const f32x4*>(&sCs[sw][32 * J + jl + 8]);
+                        const f32x4 c1 = *reinterpret_cast<const f32x4*>(&sCs[sw][32 * J + jl + 4]);
                         const float cj[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
                         const bool diag = t != 1;
                         float v[8];
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
-                            const int j = jl + (e < 4 ? e : 4 + e);
+                            const int j = jl + e;
                             const float x = __uint_as_float(e & 1 ? (u[e >> 1] & 0xffff0000u) : (u[e >> 1] << 16));
                             v[e] = (!diag || j <= l32) ? x * fast_exp2(csi - cj[e]) : 0.f;
                         }
