@@ -316,9 +316,11 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
     constexpr unsigned XHT = kT * XPR;                          // slots per head tile
     constexpr unsigned XRS = kAuxThreads / XPR;                 // X rows per copy
     constexpr unsigned BRS = kAuxThreads / BPR;                 // B / C rows per copy
-    const unsigned xr0 = at / XPR, xlp = (at % XPR) ^ (unsigned)swzbits<XPR>((int)(at / XPR));
     const unsigned br0 = at / BPR, bq = at % BPR;
-    auto copy_x = [&](int64_t c, int bf) {
+    // X copies of aux wave vw's slots (either aux wave may issue them)
+    auto copy_x = [&](int64_t c, int bf, unsigned vw) {
+        const unsigned atv = vw * 64 + (unsigned)lane;
+        const unsigned xr0 = atv / XPR, xlp = (atv % XPR) ^ (unsigned)swzbits<XPR>((int)(atv / XPR));
         const unsigned lc = (unsigned)block_last(c);
         const u16* Xg = X + (((int64_t)b * L + c * kT) * H + grp * HPG) * P;
 #pragma unroll
@@ -329,7 +331,7 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
             const unsigned tr = r <= lc ? r : lc;
             const unsigned hx = hl0 + hh < (unsigned)HPG ? hl0 + hh : HPG - 1;
             dma16(Xg, ((tr * (unsigned)H + hx) * P + xlp * 8) * 2u,
-                  lds_addr(&sX[bf][0]) + (uint32_t)((s0 + aw * 64) * 16));
+                  lds_addr(&sX[bf][0]) + (uint32_t)((s0 + vw * 64) * 16));
         }
     };
     auto copy_bc = [&](int64_t c, int bf, bool isB) {
@@ -368,7 +370,7 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
     if (aux) {
         if (c_begin < c_end) {
             copy_a(c_begin, 0);
-            copy_x(c_begin, 0);
+            copy_x(c_begin, 0, aw);
             copy_bc(c_begin, 0, true);
             if constexpr (FULL) copy_bc(c_begin, 0, false);
         }
@@ -474,8 +476,12 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
         f32x16 Yt[2] = {zero16(), zero16()};
 
         if (aux) {
-            // ---- copies of block c+1 (X now, the rest after the scores) ----
-            if (has_next) copy_x(c + 1, bf ^ 1);
+            // ---- copies of block c+1: X by the aux wave with one score tile
+            // (before the scores), the rest after the scores ----
+            if (has_next && aw == 1) {
+                copy_x(c + 1, bf ^ 1, 0);
+                copy_x(c + 1, bf ^ 1, 1);
+            }
             if constexpr (FULL) {
                 // ---- shared masked scores: aux wave 0 forms tiles 0 and 1, aux
                 // wave 1 tile 2, tile t = (I, J) in {(0,0), (1,0), (1,1)} as
