@@ -48,6 +48,13 @@ def test_mfma_shapes_ragged(Q, P, N):
              tag="mfma")
 
 
+@pytest.mark.parametrize("H,P,N", [(7, 64, 128), (13, 32, 64), (5, 64, 64)])
+def test_partial_head_sets(H, P, N):
+    # heads split over several workgroups, the last one only partly filled
+    run_case(si.FwdShape(2, 2 * 256 + 70, H, P, N, 1, 256, si.BF16), seed=H, algo=ssd.SSD_ALGO_MFMA,
+             tag="heads")
+
+
 @pytest.mark.parametrize("seg", [1, 2, 3])
 def test_mfma_segmented_with_initial_state(seg):
     # segments of 1..3 chunks: state-only pass + segment scan + full pass
