@@ -62,6 +62,13 @@ def test_mfma_segmented_with_initial_state(seg):
              algo=ssd.SSD_ALGO_MFMA, seg_chunks=seg, with_s0=True, tag="seg")
 
 
+def test_segmented_many_workgroups():
+    # 16 segments x 16 batches x 16 head sets: several rounds of workgroups per
+    # launch, and a wide segment scan
+    run_case(si.FwdShape(16, 1024, 48, 64, 128, 1, 64, si.BF16), seed=5, algo=ssd.SSD_ALGO_MFMA,
+             seg_chunks=1, with_s0=True, tag="3-launch")
+
+
 def test_groups_and_valu_bf16():
     # G=2 groups (heads 0-1 read group 0, 2-3 group 1), on both paths
     sh = si.FwdShape(1, 300, 4, 64, 64, 2, 64, si.BF16)
