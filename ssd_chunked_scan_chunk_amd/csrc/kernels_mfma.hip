@@ -51,17 +51,17 @@
 //  * Every product is v_mfma_f32_32x32x16_bf16 (operand lane l holds row or
 //    column l%32 and 8 k values of group l/32; the accumulator holds column
 //    l%32, rows 8(r/4) + 4(l/32) + r%4 in register r).  Contractions take k
-//    in natural order (group g holds k = 8g..8g+7 of each 16-wide step),
-//    except stage 5, whose k order {4g..4g+3, 8+4g..8+4g+3} is the row order
-//    of an accumulator's registers: the fp32 state becomes the stage-5
-//    operand in place (rounded to bf16), and the C rows are matched to it by
-//    a 16-byte read plus a half-swap between lanes l and l^32
-//    (v_permlane32_swap).  16-byte row reads keep every LDS read of a row
+//    in natural order (group g holds k = 8g..8g+7 of each 16-wide step).
+//    The fp32 state becomes the stage-5 operand in place (rounded to bf16):
+//    the accumulator rows a lane holds in registers 8h..8h+7 are the k values
+//    8g..8g+7 of step h, and stage 3 writes the state rows in an order that
+//    makes those the consecutive n = 16h + 8g + 0..7, so the C operand is a
+//    plain 16-byte row read.  16-byte row reads keep every LDS read of a row
 //    tile conflict-free; 8-byte reads of 32 rows cannot be (two rows share
 //    each 16-byte bank slot).  Operands with the contraction along memory
 //    rows (X^T, B^T) come from ds_read_b64_tr_b16: in each 16-lane group,
-//    source lane m names row R(m/4), columns 4(m%4)..+3, and output lane i
-//    receives column i of rows R(0..3).
+//    source lane m names row R(m/4) and a 4-column quad Q(m%4), and output
+//    lanes 4j..4j+3 receive the columns of quad Q(j) of rows R(0..3).
 //  * Scores are formed transposed, S^T = B C^T, so lane = step i; outputs are
 //    Y^T tiles, a lane holding 4 consecutive head-dim entries of one step.
 //  * LDS tiles are row-major with their 16-byte pieces permuted per row
@@ -250,6 +250,13 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
     const int sw = aux ? 0 : wave;               // state wave index (aux waves: unused)
     const int l32 = lane & 31, g2 = lane >> 5;
     const int trow = (lane & 15) >> 2, tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    // B's transposing reads take the column quads of each 16 in the order
+    // 0, 2, 1, 3: the state rows then come out of stage 3 in an order in which
+    // the 8 rows that lane (l32, g2) holds in registers 8hf .. 8hf+7 of tile nt
+    // are the consecutive n = 32nt + 16hf + 8g2 + 0..7 (the stage-5 operand
+    // order of a plain 16-byte row read of C, and 32 contiguous bytes of a
+    // state row in memory).
+    const int tcolb = 16 * ((lane >> 4) & 1) + 4 * ((lane & 3) == 1 ? 2 : (lane & 3) == 2 ? 1 : (lane & 3));
     const int hl0 = hq * HW;                     // first head of the set within the group
     const int hw = sw % HW;                      // this state wave's head within the set
     const int hlw = hl0 + hw;
@@ -272,7 +279,8 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
     //  roff: row reads of B / C (lane = row l32, the 16 bytes at column
     //        nt*32 + 16hf + 8*g2);
     //  toff: transposing reads of B (source row 8*g2 + 4s + trow, columns
-    //        nt*32 + tcol);  xoff: the same of this wave's X head-dim tile.
+    //        nt*32 + tcolb);  xoff: those of this wave's X head-dim tile
+    //        (columns pc + tcol).
     uint32_t roff[NTL][2], toff[NTL][2], xoff[2];
 #pragma unroll
     for (int nt = 0; nt < NTL; ++nt)
@@ -282,27 +290,13 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
     for (int sh = 0; sh < 2; ++sh) {
         const int r = 8 * g2 + 4 * sh + trow;
 #pragma unroll
-        for (int nt = 0; nt < NTL; ++nt) toff[nt][sh] = (uint32_t)swz<BPR>(r, nt * 32 + tcol);
+        for (int nt = 0; nt < NTL; ++nt) toff[nt][sh] = (uint32_t)swz<BPR>(r, nt * 32 + tcolb);
         xoff[sh] = (uint32_t)swz<XPR>(r, pc + tcol);
     }
     // Row fragment of B or C: row 32I + l32, columns nt*32 + 16hf + 8*g2 .. +7
     // (k in natural order within the 16-wide step hf).
     auto rowfrag = [&](const u16* tile, int I, int nt, int hf) {
         return as_bf16x8(*reinterpret_cast<const u32x4*>(tile + 32 * I * N + roff[nt][hf]));
-    };
-    // C as the stage-5 operand in the accumulator's k order: lane (l32, g2)
-    // needs columns 16hf + 4*g2 + {0..3, 8..11}.  It reads the 16-byte piece
-    // 16hf + 8*g2 .. +7 (conflict-free) and trades halves with lane l32 of the
-    // other wave half.
-    auto cfrag = [&](const u16* tile, int I, int nt, int hf) {
-        u32x4 u = as_u32x4(rowfrag(tile, I, nt, hf));
-#pragma unroll
-        for (int d = 0; d < 2; ++d) {
-            const auto r = __builtin_amdgcn_permlane32_swap(u[d], u[d + 2], false, false);
-            u[d] = r[0];
-            u[d + 2] = r[1];
-        }
-        return as_bf16x8(u);
     };
 
     // ---- copies (aux waves only).  Copy k of aux thread at fills LDS slot
@@ -314,7 +308,6 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
     const unsigned at = (unsigned)(tid - kStateWaves * 64);   // aux thread (valid for aux waves)
     const unsigned aw = (unsigned)(wave - kStateWaves);
     constexpr unsigned XHT = kT * XPR;                          // slots per head tile
-    constexpr unsigned XRS = kAuxThreads / XPR;                 // X rows per copy
     constexpr unsigned BRS = kAuxThreads / BPR;                 // B / C rows per copy
     const unsigned br0 = at / BPR, bq = at % BPR;
     // X copies of aux wave vw's slots (either aux wave may issue them)
@@ -363,7 +356,9 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
         }
     };
 
-    // ---- carried state (state waves): S^T tiles (rows n, columns p of this wave's tile) ----
+    // ---- carried state (state waves): S^T tiles (rows n, columns p of this
+    // wave's tile); register r of tile nt holds n = 32nt + 16(r/8) + 8g2 + r%8
+    // of column p = pc + l32 ----
     f32x16 Sacc[NTL];
 #pragma unroll
     for (int nt = 0; nt < NTL; ++nt) Sacc[nt] = zero16();
@@ -379,10 +374,10 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
             const float* S0 = src.Sin + b * src.bstride + seg * src.sstride + (int64_t)h * PN;
 #pragma unroll
             for (int nt = 0; nt < NTL; ++nt) {
-                const float* row = S0 + (int64_t)(pc + l32) * N + nt * 32 + 4 * g2;
+                const float* row = S0 + (int64_t)(pc + l32) * N + nt * 32 + 8 * g2;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const float4 v = *reinterpret_cast<const float4*>(row + 8 * q);
+                    const float4 v = *reinterpret_cast<const float4*>(row + 16 * (q >> 1) + 4 * (q & 1));
                     Sacc[nt][4 * q + 0] = v.x;
                     Sacc[nt][4 * q + 1] = v.y;
                     Sacc[nt][4 * q + 2] = v.z;
@@ -520,7 +515,7 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
                     for (int hf = 0; hf < 2; ++hf) {
                         const bf16x8 Sf = acc_half(Sacc[nt], hf);
 #pragma unroll
-                        for (int I = 0; I < 2; ++I) Yt[I] = mfma32(Sf, cfrag(cT, I, nt, hf), Yt[I]);
+                        for (int I = 0; I < 2; ++I) Yt[I] = mfma32(Sf, rowfrag(cT, I, nt, hf), Yt[I]);
                     }
             }
             // ---- stage 1: prefix sums of a (lane = step), weights (log2 units) ----
@@ -722,10 +717,10 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
         const float f = fast_exp2(ld);
 #pragma unroll
         for (int nt = 0; nt < NTL; ++nt) {
-            float* row = Sdst + (int64_t)(pc + l32) * N + nt * 32 + 4 * g2;
+            float* row = Sdst + (int64_t)(pc + l32) * N + nt * 32 + 8 * g2;
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                *reinterpret_cast<float4*>(row + 8 * q) =
+                *reinterpret_cast<float4*>(row + 16 * (q >> 1) + 4 * (q & 1)) =
                     make_float4(f * Sacc[nt][4 * q], f * Sacc[nt][4 * q + 1], f * Sacc[nt][4 * q + 2],
                                 f * Sacc[nt][4 * q + 3]);
         }
