@@ -304,7 +304,7 @@ ssd_status ssd_chunk_scan_fwd(const ssd_fwd_desc* desc, const void* X, const flo
         return ok();
     }
     if (p.nseg == 1) {
-        ssd::StateSrc src{initial_state, s.H * PN, 0};
+        ssd::StateSrc src{initial_state, s.H * PN, nullptr, 0, 0};
         e = ssd::launch_mfma_out(s, p.seg_chunks, 1, X, a, B, C, src, Y, final_state, hs);
         if (e != hipSuccess) return hip_fail(e, "MFMA forward launch");
         return ok();
@@ -314,11 +314,12 @@ ssd_status ssd_chunk_scan_fwd(const ssd_fwd_desc* desc, const void* X, const flo
     float* lamseg = reinterpret_cast<float*>(static_cast<char*>(workspace) + ((states + 255) / 256) * 256);
     e = ssd::launch_mfma_state(s, p.seg_chunks, p.nseg - 1, p.nseg, X, a, B, Sbuf, lamseg, hs);
     if (e != hipSuccess) return hip_fail(e, "MFMA segment-state launch");
+    // segment 0 starts from initial_state itself, so slot 0 is never written
     e = ssd::launch_state_scan(s, p.nseg - 1, p.nseg, Sbuf, lamseg, s.H * p.nseg, p.nseg,
-                               initial_state, Sbuf, Sbuf + (p.nseg - 1) * s.H * PN,
+                               initial_state, Sbuf, 1, Sbuf + (p.nseg - 1) * s.H * PN,
                                p.nseg * s.H * PN, hs);
     if (e != hipSuccess) return hip_fail(e, "segment scan launch");
-    ssd::StateSrc src{Sbuf, p.nseg * s.H * PN, s.H * PN};
+    ssd::StateSrc src{initial_state, s.H * PN, Sbuf, p.nseg * s.H * PN, s.H * PN};
     e = ssd::launch_mfma_out(s, p.seg_chunks, p.nseg, X, a, B, C, src, Y, final_state, hs);
     if (e != hipSuccess) return hip_fail(e, "MFMA forward launch");
     return ok();
@@ -439,7 +440,7 @@ ssd_status ssd_state_passing(const ssd_fwd_desc* desc, const float* dstates, con
         overlap(rf, ro))
         return fail(SSD_ERR_ALIAS, "an output overlaps an input");
     hipError_t e = ssd::launch_state_scan(s, nu, nu, dstates, lam, s.H * nu, nu,
-                                          initial_state, states_in, final_state, s.H * PN,
+                                          initial_state, states_in, 0, final_state, s.H * PN,
                                           reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "state passing launch");
     return ok();
@@ -464,7 +465,7 @@ ssd_status ssd_chunk_scan(const ssd_fwd_desc* desc, const void* X, const float* 
         if (overlap(rs, rng("Y", Y, s.Bz * s.L * s.H * s.P * 2))) return fail(SSD_ERR_ALIAS, "Y overlaps states_in");
     }
     const int64_t PN = s.P * s.N;
-    ssd::StateSrc src{states_in, p.nseg * s.H * PN, s.H * PN};
+    ssd::StateSrc src{states_in, p.nseg * s.H * PN, states_in, p.nseg * s.H * PN, s.H * PN};
     hipError_t e = ssd::launch_mfma_out(s, p.seg_chunks, p.nseg, X, a, B, C, src, Y, nullptr,
                                         reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "chunk scan launch");

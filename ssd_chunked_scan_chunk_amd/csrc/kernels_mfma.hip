@@ -370,8 +370,10 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
             if constexpr (FULL) copy_bc(c_begin, 0, false);
         }
     } else if constexpr (FULL) {
-        if (src.Sin) {
-            const float* S0 = src.Sin + b * src.bstride + seg * src.sstride + (int64_t)h * PN;
+        const float* S0 = seg == 0 ? (src.first ? src.first + b * src.first_bstride : nullptr)
+                                   : (src.Sin ? src.Sin + b * src.bstride + seg * src.sstride : nullptr);
+        if (S0) {
+            S0 += (int64_t)h * PN;
 #pragma unroll
             for (int nt = 0; nt < NTL; ++nt) {
                 const float* row = S0 + (int64_t)(pc + l32) * N + nt * 32 + 8 * g2;
@@ -754,7 +756,7 @@ hipError_t launch_mfma_state(const FwdShape& s, int64_t seg_chunks, int64_t nseg
 {
     if (nseg_run <= 0) return hipSuccess;
     const dim3 grid(grid_for(s, nseg_run));
-    const StateSrc none{nullptr, 0, 0};
+    const StateSrc none{nullptr, 0, nullptr, 0, 0};
     const int64_t bps = seg_chunks * (s.Q / kT);
 #define SSD_LAUNCH_STATE(PP, NN)                                                              \
     hipLaunchKernelGGL((k_mfma_seg<PP, NN, false>), grid, dim3(kThreads), 0, st,             \

@@ -159,8 +159,8 @@ hipError_t launch_chunk_cumsum(const FwdShape& s, const float* a, float* cs, flo
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_state_scan(
     const float* D, const float* __restrict__ lam, int64_t lam_bs, int64_t lam_hs,
-    const float* __restrict__ S0, float* Sout, float* __restrict__ fin, int64_t fin_bs,
-    int64_t nu, int64_t ustride, int H, int PN)
+    const float* __restrict__ S0, float* Sout, int64_t u_write, float* __restrict__ fin,
+    int64_t fin_bs, int64_t nu, int64_t ustride, int H, int PN)
 {
     const int h = blockIdx.y, b = blockIdx.z;
     const int q = blockIdx.x * blockDim.x + threadIdx.x;  // float4 index
@@ -171,7 +171,7 @@ __global__ __launch_bounds__(256) void k_state_scan(
     for (int64_t u = 0; u < nu; ++u) {
         const int64_t off = (((int64_t)b * ustride + u) * H + h) * PN;
         const float4 d = reinterpret_cast<const float4*>(D + off)[q];
-        reinterpret_cast<float4*>(Sout + off)[q] = S;
+        if (u >= u_write) reinterpret_cast<float4*>(Sout + off)[q] = S;
         const float e = expf(lrow[u]);
         S.x = e * S.x + d.x;
         S.y = e * S.y + d.y;
@@ -184,12 +184,13 @@ __global__ __launch_bounds__(256) void k_state_scan(
 hipError_t launch_state_scan(const FwdShape& s, int64_t nu, int64_t ustride, const float* D,
                              const float* lam,
                              int64_t lam_bstride, int64_t lam_hstride, const float* S0,
-                             float* Sout, float* final_, int64_t final_bstride, hipStream_t st)
+                             float* Sout, int64_t u_write, float* final_, int64_t final_bstride,
+                             hipStream_t st)
 {
     const int PN = (int)(s.P * s.N);
     dim3 grid((unsigned)((PN / 4 + 255) / 256), (unsigned)s.H, (unsigned)s.Bz);
     hipLaunchKernelGGL(k_state_scan, grid, dim3(256), 0, st, D, lam, lam_bstride, lam_hstride,
-                       S0, Sout, final_, final_bstride, nu, ustride, (int)s.H, PN);
+                       S0, Sout, u_write, final_, final_bstride, nu, ustride, (int)s.H, PN);
     return hipGetLastError();
 }
 

@@ -11,9 +11,12 @@ struct FwdShape {
     int64_t nc;  // ceil(L / Q)
 };
 
-// Entering-state source for a segment: Sin + b*bstride + s*sstride + h*P*N,
-// or zeros when Sin is null.
+// Entering-state source for a segment: segment 0 reads first + b*first_bstride
+// + h*P*N, segment s >= 1 reads Sin + b*bstride + s*sstride + h*P*N; a null
+// pointer means zeros.
 struct StateSrc {
+    const float* first;
+    int64_t first_bstride;
     const float* Sin;
     int64_t bstride, sstride;
 };
@@ -31,12 +34,13 @@ hipError_t launch_chunk_cumsum(const FwdShape& s, const float* a, float* cs, flo
 // ---- stage 4 / segment scan: S_{u+1} = exp(lam_u) S_u + D_u ---------------------
 // D, Sout: [Bz][ustride][H][P*N] (units 0..nu-1 used);
 // lam: lam[b*lam_bstride + h*lam_hstride + u];
-// Sout[u] receives the state entering unit u; final (optional) the state after
-// the last unit at final + b*final_bstride + h*P*N.  D may equal Sout.
+// Sout[u] receives the state entering unit u for u >= u_write (units below
+// u_write are not written); final (optional) the state after the last unit at
+// final + b*final_bstride + h*P*N.  D may equal Sout.
 hipError_t launch_state_scan(const FwdShape& s, int64_t nu, int64_t ustride, const float* D,
                              const float* lam,
                              int64_t lam_bstride, int64_t lam_hstride, const float* S0,
-                             float* Sout, float* final_, int64_t final_bstride,
+                             float* Sout, int64_t u_write, float* final_, int64_t final_bstride,
                              hipStream_t st);
 
 // ---- MFMA segmented path (bf16) ----------------------------------------------------
