@@ -173,13 +173,20 @@ __device__ __forceinline__ int swz(int row, int col) {
     return row * (PR * 8) + ((((col >> 3) ^ swzbits<PR>(row)) << 3) | (col & 7));
 }
 
-// Inclusive prefix sum over the 64 lanes: shifts of 1, 2, 4, 8 within each row
-// of 16 lanes (DPP row_shr, zero shifted in), then the row totals.
-__device__ __forceinline__ float wave_scan64(float v, int lane) {
+// Inclusive prefix sum of v over the 64 lanes: shifts of 1, 2, 4, 8 within each
+// row of 16 lanes (DPP row_shr, zero shifted in), then the row totals.  The
+// same four DPP steps run on w in between (two independent chains, so each
+// fills the other's DPP wait states) and leave in lane 16r + 15 the sum of w
+// over row r.
+__device__ __forceinline__ float wave_scan64_rowsum(float v, float& w, int lane) {
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xf, 0xf, true));
+    w += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(w), 0x111, 0xf, 0xf, true));
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xf, 0xf, true));
+    w += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(w), 0x112, 0xf, 0xf, true));
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xf, 0xf, true));
+    w += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(w), 0x114, 0xf, 0xf, true));
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xf, 0xf, true));
+    w += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(w), 0x118, 0xf, 0xf, true));
     const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 15));
     const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 31));
     const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 47));
@@ -356,20 +363,71 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
         }
     };
 
-    // ---- carried state (state waves): S^T tiles (rows n, columns p of this
-    // wave's tile); register r of tile nt holds n = 32nt + 16(r/8) + 8g2 + r%8
-    // of column p = pc + l32 ----
-    f32x16 Sacc[NTL];
-#pragma unroll
-    for (int nt = 0; nt < NTL; ++nt) Sacc[nt] = zero16();
     if (aux) {
+        // ================= copy waves: copies and scores =================
+        // (copy and state waves run separate loops with the same two barriers
+        // per block, so neither keeps the other's values in registers)
         if (c_begin < c_end) {
             copy_a(c_begin, 0);
             copy_x(c_begin, 0, aw);
             copy_bc(c_begin, 0, true);
             if constexpr (FULL) copy_bc(c_begin, 0, false);
         }
-    } else if constexpr (FULL) {
+        for (int64_t c = c_begin; c < c_end; ++c) {
+            const int bf = (int)((c - c_begin) & 1);
+            const bool has_next = c + 1 < c_end;
+            vm_wait_all();   // the copies of block c are done
+            sync_lds();      // ... and visible; buffer bf^1 and the score tiles are free
+            const u16* bT = &sB[bf][0];
+            (void)bT;
+            if constexpr (FULL) {
+                // ---- shared masked scores: aux wave 0 forms tiles 0 and 1, aux
+                // wave 1 tile 2, tile t = (I, J) in {(0,0), (1,0), (1,1)} as
+                // S^T = B_J C_I^T, stored [i][j] in bf16 ----
+                const u16* cT = &sC[bf][0];
+#pragma unroll
+                for (int t = 0; t < 3; ++t) {
+                    if ((t < 2) != (aw == 0)) continue;
+                    const int I = t > 0 ? 1 : 0, J = t == 2 ? 1 : 0;
+                    f32x16 St = zero16();
+#pragma unroll
+                    for (int nt = 0; nt < NTL; ++nt)
+#pragma unroll
+                        for (int hf = 0; hf < 2; ++hf) St = mfma32(rowfrag(bT, J, nt, hf), rowfrag(cT, I, nt, hf), St);
+                    // row j of accumulator register r: 8(r/4) + 4*g2 + r%4; lane = i.
+                    // Masked entries (j > i on the diagonal) are replaced, never multiplied.
+                    const bool diag = I == J;
+                    u16* prow = &sP[t][l32 * kPRow];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int j0 = 8 * q + 4 * g2;
+                        float v[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v[e] = (!diag || j0 + e <= l32) ? St[4 * q + e] : 0.f;
+                        *reinterpret_cast<uint2*>(prow + j0) = make_uint2(pack2(v[0], v[1]), pack2(v[2], v[3]));
+                    }
+                }
+            }
+            if constexpr (FULL) sync_lds();  // the shared score tiles are complete
+            // ---- copies of block c+1 (each copy wave fills its own half of X) ----
+            if (has_next) {
+                copy_x(c + 1, bf ^ 1, aw);
+                copy_a(c + 1, bf ^ 1);
+                copy_bc(c + 1, bf ^ 1, true);
+                if constexpr (FULL) copy_bc(c + 1, bf ^ 1, false);
+            }
+        }
+        return;
+    }
+
+    // ================= state waves =================
+    // ---- carried state (state waves): S^T tiles (rows n, columns p of this
+    // wave's tile); register r of tile nt holds n = 32nt + 16(r/8) + 8g2 + r%8
+    // of column p = pc + l32 ----
+    f32x16 Sacc[NTL];
+#pragma unroll
+    for (int nt = 0; nt < NTL; ++nt) Sacc[nt] = zero16();
+    if constexpr (FULL) {
         const float* S0 = seg == 0 ? (src.first ? src.first + b * src.first_bstride : nullptr)
                                    : (src.Sin ? src.Sin + b * src.bstride + seg * src.sstride : nullptr);
         if (S0) {
@@ -420,19 +478,10 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
         return l >= 0.5f * (absh - lamh_) - kRange && l <= kRange - 0.5f * (absh + lamh_);
     };
     float ld = 0.f;
-    // Y of a block goes out from registers at the block's end: Y^T is re-laid
-    // out through this wave's own X slice (dead after stage 3) so that copy k
-    // of a lane holds 16 contiguous bytes of step 16k + lane/4, and a store
-    // covers 16 steps x 64 bytes.
-    const uint32_t yoff = (uint32_t)(((lane >> 2) * H + h) * P + pc + 8 * (lane & 3));
-
     for (int64_t c = c_begin; c < c_end; ++c) {
         const int bf = (int)((c - c_begin) & 1);
         const int last = block_last(c);
-        const bool has_next = c + 1 < c_end;
-
-        if (aux) vm_wait_all();   // the copies of block c are done
-        sync_lds();               // ... and visible; buffer bf^1 and the score tiles are free
+        sync_lds();   // the block's copies are visible
 
         const u16* bT = &sB[bf][0];
         const u16* xT = &sX[bf][hw * kT * P];
@@ -472,235 +521,197 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
         float ld_in = 0.f, lam2 = 0.f, wrow = 0.f, pre = 1.f;
         f32x16 Yt[2] = {zero16(), zero16()};
 
-        if (aux) {
-            // ---- copies of block c+1: X by the aux wave with one score tile
-            // (before the scores), the rest after the scores ----
-            if (has_next && aw == 1) {
-                copy_x(c + 1, bf ^ 1, 0);
-                copy_x(c + 1, bf ^ 1, 1);
-            }
-            if constexpr (FULL) {
-                // ---- shared masked scores: aux wave 0 forms tiles 0 and 1, aux
-                // wave 1 tile 2, tile t = (I, J) in {(0,0), (1,0), (1,1)} as
-                // S^T = B_J C_I^T, stored [i][j] in bf16 ----
-                const u16* cT = &sC[bf][0];
+        if constexpr (FULL) {
+            // ---- stage 5 (unscaled, at the block's incoming scale): Y^T = Sacc C^T ----
+            const u16* cT = &sC[bf][0];
 #pragma unroll
-                for (int t = 0; t < 3; ++t) {
-                    if ((t < 2) != (aw == 0)) continue;
-                    const int I = t > 0 ? 1 : 0, J = t == 2 ? 1 : 0;
-                    f32x16 St = zero16();
+            for (int nt = 0; nt < NTL; ++nt)
 #pragma unroll
-                    for (int nt = 0; nt < NTL; ++nt)
+                for (int hf = 0; hf < 2; ++hf) {
+                    const bf16x8 Sf = acc_half(Sacc[nt], hf);
 #pragma unroll
-                        for (int hf = 0; hf < 2; ++hf) St = mfma32(rowfrag(bT, J, nt, hf), rowfrag(cT, I, nt, hf), St);
-                    // row j of accumulator register r: 8(r/4) + 4*g2 + r%4; lane = i.
-                    // Masked entries (j > i on the diagonal) are replaced, never multiplied.
-                    const bool diag = I == J;
-                    u16* prow = &sP[t][l32 * kPRow];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int j0 = 8 * q + 4 * g2;
-                        float v[4];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) v[e] = (!diag || j0 + e <= l32) ? St[4 * q + e] : 0.f;
-                        *reinterpret_cast<uint2*>(prow + j0) = make_uint2(pack2(v[0], v[1]), pack2(v[2], v[3]));
-                    }
+                    for (int I = 0; I < 2; ++I) Yt[I] = mfma32(Sf, rowfrag(cT, I, nt, hf), Yt[I]);
                 }
-            }
-        } else {
-            if constexpr (FULL) {
-                // ---- stage 5 (unscaled, at the block's incoming scale): Y^T = Sacc C^T ----
-                const u16* cT = &sC[bf][0];
+        }
+        // ---- stage 1: prefix sums of a (lane = step), weights (log2 units) ----
+        const float av = lane <= last ? sA[bf][lane * HW + hw] : 0.f;
+        // (the sums of |a| over each quarter bound the spread of cs2 within it)
+        float absa = fabsf(av);
+        const float cs2 = wave_scan64_rowsum(av, absa, lane) * kLog2e;
+        float base[kQ + 1], lamq[kQ], absq[kQ];   // base[q]: cs2 before quarter q
+        base[0] = 0.f;
 #pragma unroll
-                for (int nt = 0; nt < NTL; ++nt)
+        for (int q = 0; q < kQ; ++q) {
+            base[q + 1] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs2), 16 * q + 15));
+            absq[q] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(absa), 16 * q + 15)) * kLog2e;
+            lamq[q] = base[q + 1] - base[q];
+            fast = fast & (absq[q] <= kSpan);                 // wave-uniform
+        }
+        lam2 = base[kQ];
+        lam2_total += lam2;
+        const bool rebase = fast & !fits(ld, absq[0], lamq[0]);   // re-base the state scale
+        const float target = -0.5f * lamq[0];
+        pre = rebase ? fast_exp2(ld - target) : 1.f;
+        ld = rebase ? target : ld;
+        ld_in = ld;
+        // reference of each quarter; fold[q]: re-based at the start of quarter q
+        // (the accumulators then take the factor 2^(rq[q]))
+        float ldq[kQ];
+        ldq[0] = ld_in;
 #pragma unroll
-                    for (int hf = 0; hf < 2; ++hf) {
-                        const bf16x8 Sf = acc_half(Sacc[nt], hf);
+        for (int q = 1; q < kQ; ++q) {
+            const float raw = ldq[q - 1] + lamq[q - 1];
+            fold[q] = fast & !fits(raw, absq[q], lamq[q]);
+            ldq[q] = fold[q] ? -0.5f * lamq[q] : raw;
+            rq[q] = raw - ldq[q];
+        }
+        ld = fast ? ldq[kQ - 1] + lamq[kQ - 1] : 0.f;
+        // this lane's step j: quarter qj; state weight 2^(wsh - cs2_j), and
+        // (fast form) output exponent cs2_j - base + reference
+        const int qj = lane >> 4;
+        const float bj = qj == 0 ? base[0] : qj == 1 ? base[1] : qj == 2 ? base[2] : base[3];
+        const float lj = qj == 0 ? ldq[0] : qj == 1 ? ldq[1] : qj == 2 ? ldq[2] : ldq[3];
+        const float wsh = fast ? bj - lj : lam2;
+        sCs[sw][lane] = fast ? cs2 - bj + lj : cs2;
+        wrow = lane <= last ? fast_exp2(wsh - cs2) : 0.f;
+        // (the direct form weights X only after its stage 2; scaling by 1
+        // and rounding back leaves X unchanged)
+        weight_rows(fast ? wrow : 1.f);
+        if (pre != 1.f) {   // the block's re-based scale (fast form only)
 #pragma unroll
-                        for (int I = 0; I < 2; ++I) Yt[I] = mfma32(Sf, rowfrag(cT, I, nt, hf), Yt[I]);
-                    }
-            }
-            // ---- stage 1: prefix sums of a (lane = step), weights (log2 units) ----
-            const float av = lane <= last ? sA[bf][lane * HW + hw] : 0.f;
-            const float cs2 = wave_scan64(av, lane) * kLog2e;
-            // sums of |a| over each quarter bound the spread of cs2 within it
-            const float absc = wave_scan64(fabsf(av), lane) * kLog2e;
-            float base[kQ + 1], lamq[kQ], absq[kQ];   // base[q]: cs2 before quarter q
-            base[0] = 0.f;
-            float abs_prev = 0.f;
-#pragma unroll
-            for (int q = 0; q < kQ; ++q) {
-                base[q + 1] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs2), 16 * q + 15));
-                const float ac = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(absc), 16 * q + 15));
-                lamq[q] = base[q + 1] - base[q];
-                absq[q] = ac - abs_prev;
-                abs_prev = ac;
-                fast = fast & (absq[q] <= kSpan);                 // wave-uniform
-            }
-            lam2 = base[kQ];
-            lam2_total += lam2;
-            const bool rebase = fast & !fits(ld, absq[0], lamq[0]);   // re-base the state scale
-            const float target = -0.5f * lamq[0];
-            pre = rebase ? fast_exp2(ld - target) : 1.f;
-            ld = rebase ? target : ld;
-            ld_in = ld;
-            // reference of each quarter; fold[q]: re-based at the start of quarter q
-            // (the accumulators then take the factor 2^(rq[q]))
-            float ldq[kQ];
-            ldq[0] = ld_in;
-#pragma unroll
-            for (int q = 1; q < kQ; ++q) {
-                const float raw = ldq[q - 1] + lamq[q - 1];
-                fold[q] = fast & !fits(raw, absq[q], lamq[q]);
-                ldq[q] = fold[q] ? -0.5f * lamq[q] : raw;
-                rq[q] = raw - ldq[q];
-            }
-            ld = fast ? ldq[kQ - 1] + lamq[kQ - 1] : 0.f;
-            // this lane's step j: quarter qj; state weight 2^(wsh - cs2_j), and
-            // (fast form) output exponent cs2_j - base + reference
-            const int qj = lane >> 4;
-            const float bj = qj == 0 ? base[0] : qj == 1 ? base[1] : qj == 2 ? base[2] : base[3];
-            const float lj = qj == 0 ? ldq[0] : qj == 1 ? ldq[1] : qj == 2 ? ldq[2] : ldq[3];
-            const float wsh = fast ? bj - lj : lam2;
-            sCs[sw][lane] = fast ? cs2 - bj + lj : cs2;
-            wrow = lane <= last ? fast_exp2(wsh - cs2) : 0.f;
-            // (the direct form weights X only after its stage 2; scaling by 1
-            // and rounding back leaves X unchanged)
-            weight_rows(fast ? wrow : 1.f);
-            if (pre != 1.f) {   // the block's re-based scale (fast form only)
-#pragma unroll
-                for (int nt = 0; nt < NTL; ++nt) Sacc[nt] *= pre;
-                Yt[0] *= pre;
-                Yt[1] *= pre;
-            }
+            for (int nt = 0; nt < NTL; ++nt) Sacc[nt] *= pre;
+            Yt[0] *= pre;
+            Yt[1] *= pre;
         }
 
         if constexpr (FULL) sync_lds();  // the shared score tiles are complete
 
-        if (aux) {
-            if (has_next) {
-                copy_a(c + 1, bf ^ 1);
-                copy_bc(c + 1, bf ^ 1, true);
-                if constexpr (FULL) copy_bc(c + 1, bf ^ 1, false);
-            }
-        } else {
-            uint2 Yb[2][4];
-            if constexpr (FULL) {
-                // output factors (the direct form scales only the state's part here)
-                const float e0 = fast_exp2(sCs[sw][l32] + (fast ? 0.f : ld_in));
-                const float e1 = fast_exp2(sCs[sw][32 + l32] + (fast ? 0.f : ld_in));
-                // P tile t as the B operand of k step ks (lane = i, k = j)
-                auto ptile = [&](int t, int ks) {
-                    return as_bf16x8(*reinterpret_cast<const u32x4*>(&sP[t][l32 * kPRow + 16 * ks + 8 * g2]));
-                };
-                if (fast) {
-                    // ---- stage 2: Y^T += X~^T P, then the per-step factor.  The
-                    // k steps are the quarters in order; at a re-based quarter the
-                    // rows from that quarter on move to its reference ----
-                    const bool upper = l32 >= 16;        // this lane's row is in the tile's second quarter
-                    const bf16x8 x00 = xfrag(0, 0);
-                    Yt[0] = mfma32(x00, ptile(0, 0), Yt[0]);
-                    Yt[1] = mfma32(x00, ptile(1, 0), Yt[1]);
-                    if (fold[1]) {
-                        const float f = fast_exp2(rq[1]);
-                        Yt[0] *= upper ? f : 1.f;
-                        Yt[1] *= f;
-                    }
-                    const bf16x8 x01 = xfrag(0, 1);
-                    Yt[0] = mfma32(x01, ptile(0, 1), Yt[0]);
-                    Yt[1] = mfma32(x01, ptile(1, 1), Yt[1]);
-                    if (fold[2]) Yt[1] *= fast_exp2(rq[2]);
-                    Yt[1] = mfma32(xfrag(1, 0), ptile(2, 0), Yt[1]);
-                    if (fold[3]) Yt[1] *= upper ? fast_exp2(rq[3]) : 1.f;
-                    Yt[1] = mfma32(xfrag(1, 1), ptile(2, 1), Yt[1]);
-                    Yt[0] *= e0;
-                    Yt[1] *= e1;
-                } else {
-                    Yt[0] *= e0;
-                    Yt[1] *= e1;
-                    // ---- stage 2, direct form: decay 2^(cs2_i - cs2_j) on the shared scores ----
-                    // (masked entries stay replaced by zero: their exponent may overflow)
-                    auto decayed = [&](int t, int J, int ks, float csi) {
-                        const u32x4 u = as_u32x4(ptile(t, ks));
-                        const int jl = 16 * ks + 8 * g2;              // j within the tile, element 0
-                        const f32x4 c0 = *reinterpret_cast<const f32x4*>(&sCs[sw][32 * J + jl]);
-                        const f32x4 c1 = *reinterpret_cast<const f32x4*>(&sCs[sw][32 * J + jl + 4]);
-                        const float cj[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
-                        const bool diag = t != 1;
-                        float v[8];
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const int j = jl + e;
-                            const float x = __uint_as_float(e & 1 ? (u[e >> 1] & 0xffff0000u) : (u[e >> 1] << 16));
-                            v[e] = (!diag || j <= l32) ? x * fast_exp2(csi - cj[e]) : 0.f;
-                        }
-                        return as_bf16x8(u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])});
-                    };
-                    const float csi0 = sCs[sw][l32], csi1 = sCs[sw][32 + l32];
-#pragma unroll
-                    for (int ks = 0; ks < 2; ++ks) {
-                        // one tile at a time (this rare path must not raise the
-                        // kernel's register budget)
-                        const bf16x8 xa0 = xfrag(0, ks);
-                        Yt[0] = mfma32(xa0, decayed(0, 0, ks, csi0), Yt[0]);
-                        __builtin_amdgcn_sched_barrier(0);
-                        Yt[1] = mfma32(xa0, decayed(1, 0, ks, csi1), Yt[1]);
-                        __builtin_amdgcn_sched_barrier(0);
-                        Yt[1] = mfma32(xfrag(1, ks), decayed(2, 1, ks, csi1), Yt[1]);
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
+        uint2 Yb[2][4];
+        bf16x8 xk[4];   // X~ fragments (J, ks) = (0,0), (0,1), (1,0), (1,1)
+        if constexpr (FULL) {
+            // output factors (the direct form scales only the state's part here)
+            const float e0 = fast_exp2(sCs[sw][l32] + (fast ? 0.f : ld_in));
+            const float e1 = fast_exp2(sCs[sw][32 + l32] + (fast ? 0.f : ld_in));
+            // P tile t as the B operand of k step ks (lane = i, k = j)
+            auto ptile = [&](int t, int ks) {
+                return as_bf16x8(*reinterpret_cast<const u32x4*>(&sP[t][l32 * kPRow + 16 * ks + 8 * g2]));
+            };
+            if (fast) {
+                // ---- stage 2: Y^T += X~^T P, then the per-step factor.  The
+                // k steps are the quarters in order; at a re-based quarter the
+                // rows from that quarter on move to its reference ----
+                const bool upper = l32 >= 16;        // this lane's row is in the tile's second quarter
+                xk[0] = xfrag(0, 0);
+                Yt[0] = mfma32(xk[0], ptile(0, 0), Yt[0]);
+                Yt[1] = mfma32(xk[0], ptile(1, 0), Yt[1]);
+                if (fold[1]) {
+                    const float f = fast_exp2(rq[1]);
+                    Yt[0] *= upper ? f : 1.f;
+                    Yt[1] *= f;
                 }
-                // Y^T to bf16
+                xk[1] = xfrag(0, 1);
+                Yt[0] = mfma32(xk[1], ptile(0, 1), Yt[0]);
+                Yt[1] = mfma32(xk[1], ptile(1, 1), Yt[1]);
+                if (fold[2]) Yt[1] *= fast_exp2(rq[2]);
+                xk[2] = xfrag(1, 0);
+                Yt[1] = mfma32(xk[2], ptile(2, 0), Yt[1]);
+                if (fold[3]) Yt[1] *= upper ? fast_exp2(rq[3]) : 1.f;
+                xk[3] = xfrag(1, 1);
+                Yt[1] = mfma32(xk[3], ptile(2, 1), Yt[1]);
+                Yt[0] *= e0;
+                Yt[1] *= e1;
+            } else {
+                Yt[0] *= e0;
+                Yt[1] *= e1;
+                // ---- stage 2, direct form: decay 2^(cs2_i - cs2_j) on the shared scores ----
+                // (masked entries stay replaced by zero: their exponent may overflow)
+                auto decayed = [&](int t, int J, int ks, float csi) {
+                    const u32x4 u = as_u32x4(ptile(t, ks));
+                    const int jl = 16 * ks + 8 * g2;              // j within the tile, element 0
+                    const f32x4 c0 = *reinterpret_cast<const f32x4*>(&sCs[sw][32 * J + jl]);
+                    const f32x4 c1 = *reinterpret_cast<const f32x4*>(&sCs[sw][32 * J + jl + 4]);
+                    const float cj[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+                    const bool diag = t != 1;
+                    float v[8];
 #pragma unroll
-                for (int I = 0; I < 2; ++I)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        Yb[I][q] = make_uint2(pack2(Yt[I][4 * q], Yt[I][4 * q + 1]), pack2(Yt[I][4 * q + 2], Yt[I][4 * q + 3]));
-            }
-
-            // ---- stages 3 + 4: Sacc' = (direct form: 2^(ld + Lam2)) Sacc + B^T X~ ----
-            if (!fast) {
-                weight_rows(wrow);   // after the direct-form stage 2, which reads X unweighted
-                const float f = fast_exp2(ld_in + lam2);
-#pragma unroll
-                for (int nt = 0; nt < NTL; ++nt) Sacc[nt] *= f;
-            }
-#pragma unroll
-            for (int J = 0; J < 2; ++J) {
+                    for (int e = 0; e < 8; ++e) {
+                        const int j = jl + e;
+                        const float x = __uint_as_float(e & 1 ? (u[e >> 1] & 0xffff0000u) : (u[e >> 1] << 16));
+                        v[e] = (!diag || j <= l32) ? x * fast_exp2(csi - cj[e]) : 0.f;
+                    }
+                    return as_bf16x8(u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])});
+                };
+                const float csi0 = sCs[sw][l32], csi1 = sCs[sw][32 + l32];
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
-                    if (fold[2 * J + ks]) {   // the state so far at this quarter's reference
-                        const float f = fast_exp2(rq[2 * J + ks]);
-#pragma unroll
-                        for (int nt = 0; nt < NTL; ++nt) Sacc[nt] *= f;
-                    }
-                    const bf16x8 xw = xfrag(J, ks);
-#pragma unroll
-                    for (int nt = 0; nt < NTL; ++nt) {
-                        const u16* t = bT + (32 * J + 16 * ks) * N;
-                        const bf16x8 Af = join8(lds_tr4(t + toff[nt][0]), lds_tr4(t + toff[nt][1]));
-                        Sacc[nt] = mfma32(Af, xw, Sacc[nt]);
-                    }
+                    // one tile at a time (this rare path must not raise the
+                    // kernel's register budget)
+                    const bf16x8 xa0 = xfrag(0, ks);
+                    Yt[0] = mfma32(xa0, decayed(0, 0, ks, csi0), Yt[0]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    Yt[1] = mfma32(xa0, decayed(1, 0, ks, csi1), Yt[1]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    Yt[1] = mfma32(xfrag(1, ks), decayed(2, 1, ks, csi1), Yt[1]);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
-            if constexpr (FULL) {
-                // Y^T through this wave's own X slice, which is dead after stage 3
+            // Y^T to bf16
 #pragma unroll
-                for (int I = 0; I < 2; ++I)
+            for (int I = 0; I < 2; ++I)
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        *reinterpret_cast<uint2*>(xTm + swz<XPR>(32 * I + l32, pc + 8 * q + 4 * g2)) = Yb[I][q];
-                u32x4 Yr[4];
+                for (int q = 0; q < 4; ++q)
+                    Yb[I][q] = make_uint2(pack2(Yt[I][4 * q], Yt[I][4 * q + 1]), pack2(Yt[I][4 * q + 2], Yt[I][4 * q + 3]));
+        }
+
+        // ---- stages 3 + 4: Sacc' = (direct form: 2^(ld + Lam2)) Sacc + B^T X~ ----
+        if (!fast) {
+            weight_rows(wrow);   // after the direct-form stage 2, which reads X unweighted
+            const float f = fast_exp2(ld_in + lam2);
+#pragma unroll
+            for (int nt = 0; nt < NTL; ++nt) Sacc[nt] *= f;
+        }
+        if (!(FULL && fast)) {   // (the fast stage 2 has left X~ in registers)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xk[i] = xfrag(i >> 1, i & 1);
+        }
+#pragma unroll
+        for (int J = 0; J < 2; ++J) {
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                if (fold[2 * J + ks]) {   // the state so far at this quarter's reference
+                    const float f = fast_exp2(rq[2 * J + ks]);
+#pragma unroll
+                    for (int nt = 0; nt < NTL; ++nt) Sacc[nt] *= f;
+                }
+                const bf16x8 xw = xk[2 * J + ks];
+#pragma unroll
+                for (int nt = 0; nt < NTL; ++nt) {
+                    const u16* t = bT + (32 * J + 16 * ks) * N;
+                    const bf16x8 Af = join8(lds_tr4(t + toff[nt][0]), lds_tr4(t + toff[nt][1]));
+                    Sacc[nt] = mfma32(Af, xw, Sacc[nt]);
+                }
+            }
+        }
+        if constexpr (FULL) {
+            // Y^T through this wave's own X slice, which is dead after stage 3,
+            // so that copy k of a lane holds 16 contiguous bytes of step
+            // 16k + lane/4 and a store covers 16 steps x 64 bytes
+#pragma unroll
+            for (int I = 0; I < 2; ++I)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<uint2*>(xTm + swz<XPR>(32 * I + l32, pc + 8 * q + 4 * g2)) = Yb[I][q];
+            u32x4 Yr[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                Yr[k] = *reinterpret_cast<const u32x4*>(xTm + swz<XPR>(16 * k + (lane >> 2), pc + 8 * (lane & 3)));
+            if (hvalid) {
+                u16* yblk = Y + ((int64_t)b * L + c * kT) * H * P;
+                const uint32_t yoff = (uint32_t)(((lane >> 2) * H + h) * P + pc + 8 * (lane & 3));
 #pragma unroll
                 for (int k = 0; k < 4; ++k)
-                    Yr[k] = *reinterpret_cast<const u32x4*>(xTm + swz<XPR>(16 * k + (lane >> 2), pc + 8 * (lane & 3)));
-                if (hvalid) {
-                    u16* yblk = Y + ((int64_t)b * L + c * kT) * H * P;
-#pragma unroll
-                    for (int k = 0; k < 4; ++k)
-                        if (16 * k + (lane >> 2) <= last)
-                            *reinterpret_cast<u32x4*>(yblk + (yoff + (uint32_t)(16 * k * H * P))) = Yr[k];
-                }
+                    if (16 * k + (lane >> 2) <= last)
+                        *reinterpret_cast<u32x4*>(yblk + (yoff + (uint32_t)(16 * k * H * P))) = Yr[k];
             }
         }
     }
