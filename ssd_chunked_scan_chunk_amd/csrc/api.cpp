@@ -58,7 +58,10 @@ constexpr int64_t kLdsPerCU = 160 * 1024;
 // used to estimate how many workgroups share a CU when planning segments.
 int64_t mfma_lds_bytes(int64_t P, int64_t N) {
     const int64_t T = 64, HW = ssd::mfma_heads_per_workgroup(P, N);
-    return 2 * (HW * T * P * 2 + 2 * T * N * 2 + T * HW * 4) + 3 * 32 * 40 * 2 + 8 * T * 4;
+    // X, B, C double buffered; a triple buffered; scans, quarter sums, score
+    // tiles and the per-wave output exponents
+    return 2 * (HW * T * P * 2 + 2 * T * N * 2) + 3 * HW * T * 4 + 2 * HW * T * 4 + 2 * HW * 16 +
+           3 * 32 * 40 * 2 + 6 * T * 4;
 }
 
 struct Plan {

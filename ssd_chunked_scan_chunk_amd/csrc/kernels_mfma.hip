@@ -103,7 +103,6 @@ struct MfmaCfg {
     static constexpr int BPR = N / 8;                    // 16-byte pieces per B / C row
     static constexpr int XOPS = HW * kT * XPR / kAuxThreads;   // X copies per aux thread per block
     static constexpr int BOPS = kT * BPR / kAuxThreads;        // B (or C) copies per aux thread
-    static constexpr int AOPS = (kT * HW + kAuxThreads - 1) / kAuxThreads;   // a copies (4 bytes)
     static_assert(P % 32 == 0 && N % 32 == 0 && kStateWaves % PS == 0, "tile shape");
     static_assert((HW * kT * XPR) % kAuxThreads == 0 && (kT * BPR) % kAuxThreads == 0, "copy shape");
     static_assert(kAuxThreads % XPR == 0 && kAuxThreads % BPR == 0 && (kT * XPR) % kAuxThreads == 0,
@@ -230,13 +229,15 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
 {
     using Cfg = MfmaCfg<P, N>;
     constexpr int HW = Cfg::HW, NTL = Cfg::NTL, XPR = Cfg::XPR, BPR = Cfg::BPR;
-    constexpr int XOPS = Cfg::XOPS, BOPS = Cfg::BOPS, AOPS = Cfg::AOPS;
+    constexpr int XOPS = Cfg::XOPS, BOPS = Cfg::BOPS;
 
     __shared__ __attribute__((aligned(16))) u16 sX[2][HW * kT * P];    // [buf][head][step][p]
     __shared__ __attribute__((aligned(16))) u16 sB[2][kT * N];         // [buf][step][n]
     __shared__ __attribute__((aligned(16))) u16 sC[FULL ? 2 : 1][FULL ? kT * N : 8];
     __shared__ __attribute__((aligned(16))) u16 sP[FULL ? 3 : 1][FULL ? 32 * kPRow : 8];  // masked scores [i][j]
-    __shared__ __attribute__((aligned(16))) float sA[2][AOPS * kAuxThreads];  // [buf][step][head]
+    __shared__ __attribute__((aligned(16))) float sA[3][HW * kT];     // [buf][head][step]
+    __shared__ __attribute__((aligned(16))) float sCs2[2][HW][kT];  // [buf][head][step] prefix sums of a, log2 units
+    __shared__ __attribute__((aligned(16))) float sAbs[2][HW][4];   // [buf][head][quarter] sums of |a|, log2 units
     __shared__ __attribute__((aligned(16))) float sCs[kStateWaves][kT];       // per state wave
 
     // ---- work item: contiguous item ranges per XCD (head sets fastest) ----
@@ -347,19 +348,17 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
                   lds_addr(tile) + (uint32_t)((k * kAuxThreads + aw * 64) * 16));
         }
     };
-    auto copy_a = [&](int64_t c, int bf) {   // slot s -> (step s / HW, head s % HW)
+    // a of the heads this copy wave scans (hh % 2 == aw), lane = step: the
+    // wave that scans a head also copies it, so its own wait suffices
+    auto copy_a = [&](int64_t c, int ia) {
         const unsigned lc = (unsigned)block_last(c);
         const float* ag = a + ((int64_t)b * L + c * kT) * H + grp * HPG;
+        const unsigned tr = (unsigned)lane <= lc ? (unsigned)lane : lc;
 #pragma unroll
-        for (int k = 0; k < AOPS; ++k) {
-            const unsigned s = (unsigned)k * kAuxThreads + at;
-            if ((unsigned)k * kAuxThreads + aw * 64 < (unsigned)(kT * HW)) {   // wave-uniform
-                const unsigned t = s / HW, hh = s % HW;
-                const unsigned tr = t <= lc ? t : lc;
-                const unsigned hx = hl0 + hh < (unsigned)HPG ? hl0 + hh : HPG - 1;
-                dma4(ag, (tr * (unsigned)H + hx) * 4u,
-                     lds_addr(&sA[bf][0]) + (uint32_t)((k * kAuxThreads + aw * 64) * 4));
-            }
+        for (int hh = 0; hh < HW; ++hh) {
+            if ((hh & 1) != (int)aw) continue;
+            const unsigned hx = hl0 + hh < (unsigned)HPG ? hl0 + hh : HPG - 1;
+            dma4(ag, (tr * (unsigned)H + hx) * 4u, lds_addr(&sA[ia][hh * kT]));
         }
     };
 
@@ -367,16 +366,38 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
         // ================= copy waves: copies and scores =================
         // (copy and state waves run separate loops with the same two barriers
         // per block, so neither keeps the other's values in registers)
+        // Stage 1's scans of block c+1 run here, after the copies of block c,
+        // while the state waves work on block c: a is copied two blocks ahead
+        // (three buffers), so a[c+1] has landed by the top of block c, and the
+        // scans publish each head's prefix sums and quarter sums of |a| for
+        // the state waves (two buffers).  Copy wave aw scans the heads hh with
+        // hh % 2 == aw.
+        auto scans = [&](int64_t cn) {
+            const int ia = (int)((cn - c_begin) % 3), io = (int)((cn - c_begin) & 1);
+            const int lastn = block_last(cn);
+#pragma unroll
+            for (int hh = 0; hh < HW; ++hh) {
+                if ((hh & 1) != (int)aw) continue;
+                const float av = lane <= lastn ? sA[ia][hh * kT + lane] : 0.f;
+                float absa = fabsf(av);
+                const float cs2 = wave_scan64_rowsum(av, absa, lane) * kLog2e;
+                sCs2[io][hh][lane] = cs2;
+                if ((lane & 15) == 15) sAbs[io][hh][lane >> 4] = absa * kLog2e;
+            }
+        };
         if (c_begin < c_end) {
             copy_a(c_begin, 0);
+            if (c_begin + 1 < c_end) copy_a(c_begin + 1, 1);
             copy_x(c_begin, 0, aw);
             copy_bc(c_begin, 0, true);
             if constexpr (FULL) copy_bc(c_begin, 0, false);
+            vm_wait_all();
+            scans(c_begin);
         }
         for (int64_t c = c_begin; c < c_end; ++c) {
             const int bf = (int)((c - c_begin) & 1);
             const bool has_next = c + 1 < c_end;
-            vm_wait_all();   // the copies of block c are done
+            vm_wait_all();   // the copies of block c (and a of block c+1) are done
             sync_lds();      // ... and visible; buffer bf^1 and the score tiles are free
             const u16* bT = &sB[bf][0];
             (void)bT;
@@ -412,9 +433,10 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
             // ---- copies of block c+1 (each copy wave fills its own half of X) ----
             if (has_next) {
                 copy_x(c + 1, bf ^ 1, aw);
-                copy_a(c + 1, bf ^ 1);
+                if (c + 2 < c_end) copy_a(c + 2, (int)((c + 2 - c_begin) % 3));
                 copy_bc(c + 1, bf ^ 1, true);
                 if constexpr (FULL) copy_bc(c + 1, bf ^ 1, false);
+                scans(c + 1);   // after the copies are on their way
             }
         }
         return;
@@ -533,17 +555,18 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
                     for (int I = 0; I < 2; ++I) Yt[I] = mfma32(Sf, rowfrag(cT, I, nt, hf), Yt[I]);
                 }
         }
-        // ---- stage 1: prefix sums of a (lane = step), weights (log2 units) ----
-        const float av = lane <= last ? sA[bf][lane * HW + hw] : 0.f;
+        // ---- stage 1: prefix sums of a (lane = step; scanned by the copy
+        // waves), decisions and weights (log2 units) ----
+        const float cs2 = sCs2[bf][hw][lane];
         // (the sums of |a| over each quarter bound the spread of cs2 within it)
-        float absa = fabsf(av);
-        const float cs2 = wave_scan64_rowsum(av, absa, lane) * kLog2e;
+        const float4 abs4 = *reinterpret_cast<const float4*>(&sAbs[bf][hw][0]);
+        const float absv[kQ] = {abs4.x, abs4.y, abs4.z, abs4.w};
         float base[kQ + 1], lamq[kQ], absq[kQ];   // base[q]: cs2 before quarter q
         base[0] = 0.f;
 #pragma unroll
         for (int q = 0; q < kQ; ++q) {
             base[q + 1] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs2), 16 * q + 15));
-            absq[q] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(absa), 16 * q + 15)) * kLog2e;
+            absq[q] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(absv[q])));
             lamq[q] = base[q + 1] - base[q];
             fast = fast & (absq[q] <= kSpan);                 // wave-uniform
         }
