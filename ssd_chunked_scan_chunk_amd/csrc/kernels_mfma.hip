@@ -215,6 +215,13 @@ __device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t ld
 }
 // no vector-memory operation of this wave outstanding
 __device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// at most K vector-memory operations of this wave outstanding (loads complete
+// in issue order, so every operation but the last K issued has completed)
+template <int K>
+__device__ __forceinline__ void vm_wait_le() {
+    static_assert(K >= 0 && K < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(K) : "memory");
+}
 // workgroup barrier ordering LDS only (no wait on HBM traffic)
 __device__ __forceinline__ void sync_lds() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -236,9 +243,11 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
     __shared__ __attribute__((aligned(16))) u16 sC[FULL ? 2 : 1][FULL ? kT * N : 8];
     __shared__ __attribute__((aligned(16))) u16 sP[FULL ? 3 : 1][FULL ? 32 * kPRow : 8];  // masked scores [i][j]
     __shared__ __attribute__((aligned(16))) float sA[3][HW * kT];     // [buf][head][step]
-    __shared__ __attribute__((aligned(16))) float sCs2[2][HW][kT];  // [buf][head][step] prefix sums of a, log2 units
-    __shared__ __attribute__((aligned(16))) float sAbs[2][HW][4];   // [buf][head][quarter] sums of |a|, log2 units
-    __shared__ __attribute__((aligned(16))) float sCs[kStateWaves][kT];       // per state wave
+    // stage 1's results per head, two buffers: output exponents, state weights
+    // per step, and the block's scale decisions
+    __shared__ __attribute__((aligned(16))) float sCs[2][HW][kT];
+    __shared__ __attribute__((aligned(16))) float sW[2][HW][kT];
+    __shared__ __attribute__((aligned(16))) float sPar[2][HW][8];
 
     // ---- work item: contiguous item ranges per XCD (head sets fastest) ----
     const int HPG = H / G;
@@ -362,37 +371,119 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
         }
     };
 
+    // The true state is 2^ld * Sacc.  In a block whose log2-decays stay within
+    // range of the state scale (the common case) the decay is never applied to
+    // the accumulators: with X~_j = 2^(-ld - cs2_j) X_j
+    //   Y_i     = 2^(cs2_i + ld) * (C_i Sacc + sum_{j<=i} (C_i . B_j) X~_j)
+    //   Sacc'   = Sacc + B^T X~,   ld' = ld + Lam2,
+    // so stages 2 and 5 share one accumulator, the scores need only the causal
+    // mask (and so are the same for every head), and one per-step factor
+    // scales the output.  Each 16-step quarter of the block (one MFMA k step)
+    // is checked on its own: a quarter whose prefix sums (relative to its
+    // start) lie in [-neg, pos] keeps every weight exponent -ld - cs2_j and
+    // output exponent cs2_i + ld within +-kRange exactly when ld lies in
+    // [neg - kRange, kRange - pos] (neg and pos follow from the quarter's
+    // total and its sum of |a|).  When the scale reached at a quarter's start
+    // falls outside that interval it is re-based to the interval's centre,
+    // -Lam_q / 2: at the block start by multiplying Sacc, inside the block by
+    // multiplying Sacc between the quarters' stage-3 products and the output
+    // accumulators of the rows from that quarter on between the quarters'
+    // stage-2 products; that quarter's X~ and output factors then use its own
+    // prefix sums.  Such a scale exists when the quarter's spread neg + pos is
+    // at most 2 kRange (kSpan keeps a margin so the factor between two
+    // quarters' references stays below 2^127).  Only a block with a wider
+    // quarter takes the direct form: per-element decay of the shared scores,
+    // then Sacc' = 2^(ld + Lam2) Sacc + B^T (w o X), ld' = 0.
+    //
+    // Stage 1 (the scans of a and these decisions) runs on the copy waves one
+    // block ahead; the state waves read the decisions, the output exponents
+    // and the weights of their head from LDS.
+    constexpr int kQ = 4;          // 16-step quarters of a block (one MFMA k step each)
+    constexpr float kRange = 64.f;
+    constexpr float kSpan = 2.f * kRange - 8.f;
+    auto fits = [](float l, float absh, float lamh_) {
+        return l >= 0.5f * (absh - lamh_) - kRange && l <= kRange - 0.5f * (absh + lamh_);
+    };
     if (aux) {
         // ================= copy waves: copies and scores =================
         // (copy and state waves run separate loops with the same two barriers
         // per block, so neither keeps the other's values in registers)
-        // Stage 1's scans of block c+1 run here, after the copies of block c,
-        // while the state waves work on block c: a is copied two blocks ahead
-        // (three buffers), so a[c+1] has landed by the top of block c, and the
-        // scans publish each head's prefix sums and quarter sums of |a| for
-        // the state waves (two buffers).  Copy wave aw scans the heads hh with
-        // hh % 2 == aw.
-        auto scans = [&](int64_t cn) {
+        // Stage 1 of block c+1 runs here, after the copies of block c, while
+        // the state waves work on block c: a is copied two blocks ahead (three
+        // buffers), so a[c+1] has landed by the top of block c.  Copy wave aw
+        // handles the heads hh with hh % 2 == aw (it copied their a itself)
+        // and tracks their scale ld across blocks.
+        float ldh[HW];
+#pragma unroll
+        for (int hh = 0; hh < HW; ++hh) ldh[hh] = 0.f;
+        auto decide = [&](int64_t cn) {
             const int ia = (int)((cn - c_begin) % 3), io = (int)((cn - c_begin) & 1);
             const int lastn = block_last(cn);
 #pragma unroll
             for (int hh = 0; hh < HW; ++hh) {
                 if ((hh & 1) != (int)aw) continue;
+                // prefix sums of a (lane = step) and the sums of |a| over each
+                // quarter, which bound the spread of cs2 within it (log2 units)
                 const float av = lane <= lastn ? sA[ia][hh * kT + lane] : 0.f;
                 float absa = fabsf(av);
                 const float cs2 = wave_scan64_rowsum(av, absa, lane) * kLog2e;
-                sCs2[io][hh][lane] = cs2;
-                if ((lane & 15) == 15) sAbs[io][hh][lane >> 4] = absa * kLog2e;
+                float base[kQ + 1], lamq[kQ], absq[kQ];   // base[q]: cs2 before quarter q
+                base[0] = 0.f;
+                bool fast = true;
+#pragma unroll
+                for (int q = 0; q < kQ; ++q) {
+                    base[q + 1] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs2), 16 * q + 15));
+                    absq[q] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(absa), 16 * q + 15)) * kLog2e;
+                    lamq[q] = base[q + 1] - base[q];
+                    fast = fast & (absq[q] <= kSpan);                 // wave-uniform
+                }
+                const float lam2 = base[kQ];
+                const float ld = ldh[hh];
+                const bool rebase = fast & !fits(ld, absq[0], lamq[0]);   // re-base the state scale
+                const float target = -0.5f * lamq[0];
+                const float pre = rebase ? fast_exp2(ld - target) : 1.f;
+                const float ld_in = rebase ? target : ld;
+                // reference of each quarter; rq[q] != 0: re-based at the start of
+                // quarter q (the accumulators then take the factor 2^(rq[q]))
+                float ldq[kQ], rq[kQ];
+                ldq[0] = ld_in;
+                rq[0] = 0.f;
+#pragma unroll
+                for (int q = 1; q < kQ; ++q) {
+                    const float raw = ldq[q - 1] + lamq[q - 1];
+                    const bool fold = fast & !fits(raw, absq[q], lamq[q]);
+                    ldq[q] = fold ? -0.5f * lamq[q] : raw;
+                    rq[q] = raw - ldq[q];
+                }
+                const float ld_out = fast ? ldq[kQ - 1] + lamq[kQ - 1] : 0.f;
+                ldh[hh] = ld_out;
+                // this lane's step j: quarter qj; state weight 2^(wsh - cs2_j), and
+                // (fast form) output exponent cs2_j - base + reference
+                const int qj = lane >> 4;
+                const float bj = qj == 0 ? base[0] : qj == 1 ? base[1] : qj == 2 ? base[2] : base[3];
+                const float lj = qj == 0 ? ldq[0] : qj == 1 ? ldq[1] : qj == 2 ? ldq[2] : ldq[3];
+                const float wsh = fast ? bj - lj : lam2;
+                sCs[io][hh][lane] = fast ? cs2 - bj + lj : cs2;
+                sW[io][hh][lane] = lane <= lastn ? fast_exp2(wsh - cs2) : 0.f;
+                if (lane == 0) {
+                    *reinterpret_cast<float4*>(&sPar[io][hh][0]) = make_float4(fast ? 1.f : 0.f, pre, ld_in, lam2);
+                    *reinterpret_cast<float4*>(&sPar[io][hh][4]) = make_float4(rq[1], rq[2], rq[3], ld_out);
+                }
             }
         };
         if (c_begin < c_end) {
+            // a of the first block first; its stage 1 runs as soon as that copy
+            // has landed, while the larger copies are still in flight (the
+            // second a copy repeats the first block's when there is no second)
             copy_a(c_begin, 0);
-            if (c_begin + 1 < c_end) copy_a(c_begin + 1, 1);
+            copy_a(c_begin + 1 < c_end ? c_begin + 1 : c_begin, 1);
             copy_x(c_begin, 0, aw);
             copy_bc(c_begin, 0, true);
             if constexpr (FULL) copy_bc(c_begin, 0, false);
-            vm_wait_all();
-            scans(c_begin);
+            constexpr int kRest = XOPS + BOPS + (FULL ? BOPS : 0);
+            if (aw == 0) vm_wait_le<(HW + 1) / 2 + kRest>();
+            else vm_wait_le<HW / 2 + kRest>();
+            decide(c_begin);
         }
         for (int64_t c = c_begin; c < c_end; ++c) {
             const int bf = (int)((c - c_begin) & 1);
@@ -436,7 +527,7 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
                 if (c + 2 < c_end) copy_a(c + 2, (int)((c + 2 - c_begin) % 3));
                 copy_bc(c + 1, bf ^ 1, true);
                 if constexpr (FULL) copy_bc(c + 1, bf ^ 1, false);
-                scans(c + 1);   // after the copies are on their way
+                decide(c + 1);   // after the copies are on their way
             }
         }
         return;
@@ -468,38 +559,8 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
             }
         }
     }
-    float lam2_total = 0.f;
-    // The true state is 2^ld * Sacc.  In a block whose log2-decays stay within
-    // range of the state scale (the common case) the decay is never applied to
-    // the accumulators: with X~_j = 2^(-ld - cs2_j) X_j
-    //   Y_i     = 2^(cs2_i + ld) * (C_i Sacc + sum_{j<=i} (C_i . B_j) X~_j)
-    //   Sacc'   = Sacc + B^T X~,   ld' = ld + Lam2,
-    // so stages 2 and 5 share one accumulator, the scores need only the causal
-    // mask (and so are the same for every head), and one per-step factor
-    // scales the output.  Each 16-step quarter of the block (one MFMA k step)
-    // is checked on its own: a quarter whose prefix sums (relative to its
-    // start) lie in [-neg, pos] keeps every weight exponent -ld - cs2_j and
-    // output exponent cs2_i + ld within +-kRange exactly when ld lies in
-    // [neg - kRange, kRange - pos] (neg and pos follow from the quarter's
-    // total and its sum of |a|).  When the scale reached at a quarter's start
-    // falls outside that interval it is re-based to the interval's centre,
-    // -Lam_q / 2: at the block start by multiplying Sacc (and the stage-5
-    // output, which is formed before the scale is known), inside the block by
-    // multiplying Sacc between the quarters' stage-3 products and the output
-    // accumulators of the rows from that quarter on between the quarters'
-    // stage-2 products; that quarter's X~ and output factors then use its own
-    // prefix sums.  Such a scale exists when the quarter's spread neg + pos is
-    // at most 2 kRange (kSpan keeps a margin so the factor between two
-    // quarters' references stays below 2^127).  Only a block with a wider
-    // quarter takes the direct form: per-element decay of the shared scores,
-    // then Sacc' = 2^(ld + Lam2) Sacc + B^T (w o X), ld' = 0.
-    constexpr int kQ = 4;          // 16-step quarters of a block (one MFMA k step each)
-    constexpr float kRange = 64.f;
-    constexpr float kSpan = 2.f * kRange - 8.f;
-    auto fits = [](float l, float absh, float lamh_) {
-        return l >= 0.5f * (absh - lamh_) - kRange && l <= kRange - 0.5f * (absh + lamh_);
-    };
-    float ld = 0.f;
+    float lam2_total = 0.f;   // the segment's log2-decay
+    float ld = 0.f;           // the scale of Sacc (log2) after the latest block
     for (int64_t c = c_begin; c < c_end; ++c) {
         const int bf = (int)((c - c_begin) & 1);
         const int last = block_last(c);
@@ -536,15 +597,27 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
             }
         };
 
-        // state-wave values that live across the score barrier
-        bool fast = true;
-        bool fold[kQ] = {false, false, false, false};
-        float rq[kQ] = {0.f, 0.f, 0.f, 0.f};
-        float ld_in = 0.f, lam2 = 0.f, wrow = 0.f, pre = 1.f;
-        f32x16 Yt[2] = {zero16(), zero16()};
+        // ---- the block's stage-1 results for this wave's head ----
+        const float4 pa = *reinterpret_cast<const float4*>(&sPar[bf][hw][0]);
+        const float4 pb = *reinterpret_cast<const float4*>(&sPar[bf][hw][4]);
+        auto uni = [](float v) { return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v))); };
+        const bool fast = uni(pa.x) != 0.f;
+        const float pre = uni(pa.y), ld_in = uni(pa.z), lam2 = uni(pa.w);
+        const float rq[kQ] = {0.f, uni(pb.x), uni(pb.y), uni(pb.z)};
+        const bool fold[kQ] = {false, rq[1] != 0.f, rq[2] != 0.f, rq[3] != 0.f};
+        ld = uni(pb.w);
+        lam2_total += lam2;
+        const float wrow = sW[bf][hw][lane];
+        if (pre != 1.f) {   // the block's re-based scale (fast form only), before stage 5
+#pragma unroll
+            for (int nt = 0; nt < NTL; ++nt) Sacc[nt] *= pre;
+        }
+        // (the direct form weights X only after its stage 2)
+        if (fast) weight_rows(wrow);
 
+        f32x16 Yt[2] = {zero16(), zero16()};
         if constexpr (FULL) {
-            // ---- stage 5 (unscaled, at the block's incoming scale): Y^T = Sacc C^T ----
+            // ---- stage 5 (at the block's re-based scale): Y^T = Sacc C^T ----
             const u16* cT = &sC[bf][0];
 #pragma unroll
             for (int nt = 0; nt < NTL; ++nt)
@@ -555,57 +628,6 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
                     for (int I = 0; I < 2; ++I) Yt[I] = mfma32(Sf, rowfrag(cT, I, nt, hf), Yt[I]);
                 }
         }
-        // ---- stage 1: prefix sums of a (lane = step; scanned by the copy
-        // waves), decisions and weights (log2 units) ----
-        const float cs2 = sCs2[bf][hw][lane];
-        // (the sums of |a| over each quarter bound the spread of cs2 within it)
-        const float4 abs4 = *reinterpret_cast<const float4*>(&sAbs[bf][hw][0]);
-        const float absv[kQ] = {abs4.x, abs4.y, abs4.z, abs4.w};
-        float base[kQ + 1], lamq[kQ], absq[kQ];   // base[q]: cs2 before quarter q
-        base[0] = 0.f;
-#pragma unroll
-        for (int q = 0; q < kQ; ++q) {
-            base[q + 1] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs2), 16 * q + 15));
-            absq[q] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(absv[q])));
-            lamq[q] = base[q + 1] - base[q];
-            fast = fast & (absq[q] <= kSpan);                 // wave-uniform
-        }
-        lam2 = base[kQ];
-        lam2_total += lam2;
-        const bool rebase = fast & !fits(ld, absq[0], lamq[0]);   // re-base the state scale
-        const float target = -0.5f * lamq[0];
-        pre = rebase ? fast_exp2(ld - target) : 1.f;
-        ld = rebase ? target : ld;
-        ld_in = ld;
-        // reference of each quarter; fold[q]: re-based at the start of quarter q
-        // (the accumulators then take the factor 2^(rq[q]))
-        float ldq[kQ];
-        ldq[0] = ld_in;
-#pragma unroll
-        for (int q = 1; q < kQ; ++q) {
-            const float raw = ldq[q - 1] + lamq[q - 1];
-            fold[q] = fast & !fits(raw, absq[q], lamq[q]);
-            ldq[q] = fold[q] ? -0.5f * lamq[q] : raw;
-            rq[q] = raw - ldq[q];
-        }
-        ld = fast ? ldq[kQ - 1] + lamq[kQ - 1] : 0.f;
-        // this lane's step j: quarter qj; state weight 2^(wsh - cs2_j), and
-        // (fast form) output exponent cs2_j - base + reference
-        const int qj = lane >> 4;
-        const float bj = qj == 0 ? base[0] : qj == 1 ? base[1] : qj == 2 ? base[2] : base[3];
-        const float lj = qj == 0 ? ldq[0] : qj == 1 ? ldq[1] : qj == 2 ? ldq[2] : ldq[3];
-        const float wsh = fast ? bj - lj : lam2;
-        sCs[sw][lane] = fast ? cs2 - bj + lj : cs2;
-        wrow = lane <= last ? fast_exp2(wsh - cs2) : 0.f;
-        // (the direct form weights X only after its stage 2; scaling by 1
-        // and rounding back leaves X unchanged)
-        weight_rows(fast ? wrow : 1.f);
-        if (pre != 1.f) {   // the block's re-based scale (fast form only)
-#pragma unroll
-            for (int nt = 0; nt < NTL; ++nt) Sacc[nt] *= pre;
-            Yt[0] *= pre;
-            Yt[1] *= pre;
-        }
 
         if constexpr (FULL) sync_lds();  // the shared score tiles are complete
 
@@ -613,8 +635,8 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
         bf16x8 xk[4];   // X~ fragments (J, ks) = (0,0), (0,1), (1,0), (1,1)
         if constexpr (FULL) {
             // output factors (the direct form scales only the state's part here)
-            const float e0 = fast_exp2(sCs[sw][l32] + (fast ? 0.f : ld_in));
-            const float e1 = fast_exp2(sCs[sw][32 + l32] + (fast ? 0.f : ld_in));
+            const float e0 = fast_exp2(sCs[bf][hw][l32] + (fast ? 0.f : ld_in));
+            const float e1 = fast_exp2(sCs[bf][hw][32 + l32] + (fast ? 0.f : ld_in));
             // P tile t as the B operand of k step ks (lane = i, k = j)
             auto ptile = [&](int t, int ks) {
                 return as_bf16x8(*reinterpret_cast<const u32x4*>(&sP[t][l32 * kPRow + 16 * ks + 8 * g2]));
@@ -651,8 +673,8 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
                 auto decayed = [&](int t, int J, int ks, float csi) {
                     const u32x4 u = as_u32x4(ptile(t, ks));
                     const int jl = 16 * ks + 8 * g2;              // j within the tile, element 0
-                    const f32x4 c0 = *reinterpret_cast<const f32x4*>(&sCs[sw][32 * J + jl]);
-                    const f32x4 c1 = *reinterpret_cast<const f32x4*>(&sCs[sw][32 * J + jl + 4]);
+                    const f32x4 c0 = *reinterpret_cast<const f32x4*>(&sCs[bf][hw][32 * J + jl]);
+                    const f32x4 c1 = *reinterpret_cast<const f32x4*>(&sCs[bf][hw][32 * J + jl + 4]);
                     const float cj[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
                     const bool diag = t != 1;
                     float v[8];
@@ -664,7 +686,7 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
                     }
                     return as_bf16x8(u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])});
                 };
-                const float csi0 = sCs[sw][l32], csi1 = sCs[sw][32 + l32];
+                const float csi0 = sCs[bf][hw][l32], csi1 = sCs[bf][hw][32 + l32];
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
                     // one tile at a time (this rare path must not raise the
