@@ -569,32 +569,20 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
         const u16* bT = &sB[bf][0];
         const u16* xT = &sX[bf][hw * kT * P];
         u16* xTm = &sX[bf][hw * kT * P];
-        // X^T fragments of this wave's head-dim tile (lane = p, k = step);
-        // after weight_rows they are X~ = w o X.
+        // X^T fragments of this wave's head-dim tile (lane = p, k = step)
         auto xfrag = [&](int J, int ks) {
             const u16* t = xT + (32 * J + 16 * ks) * P;
             return join8(lds_tr4(t + xoff[0]), lds_tr4(t + xoff[1]));
         };
-        // The state weight of step j is applied to X in place: lane j scales row
-        // j of this wave's head-dim tile (its own 32 columns, 4 pieces), so the
-        // transposing reads that follow yield w o X directly.
-        auto weight_rows = [&](float wr) {
-            u16* rowp = xTm + lane * P;
-            u32x4* q[4];
-            u32x4 u[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {   // all reads first: one LDS round trip
-                q[k] = reinterpret_cast<u32x4*>(rowp + (((pc >> 3) + k) ^ swzbits<XPR>(lane)) * 8);
-                u[k] = *q[k];
-            }
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                u32x4 o;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    o[e] = pack2(wr * __uint_as_float(u[k][e] << 16), wr * __uint_as_float(u[k][e] & 0xffff0000u));
-                *q[k] = o;
-            }
+        // ... weighted in registers, X~ = w o X: the fragment's k values are
+        // the steps 32J + 16ks + 8g2 + 0..7, whose state weights stage 1 left
+        // in LDS (X itself stays unweighted in LDS for the direct form)
+        auto xwfrag = [&](int J, int ks) {
+            const float* wp = &sW[bf][hw][32 * J + 16 * ks + 8 * g2];
+            const float4 w0 = *reinterpret_cast<const float4*>(wp);
+            const float4 w1 = *reinterpret_cast<const float4*>(wp + 4);
+            const float w8[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+            return scale8(xfrag(J, ks), w8);
         };
 
         // ---- the block's stage-1 results for this wave's head ----
@@ -607,13 +595,10 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
         const bool fold[kQ] = {false, rq[1] != 0.f, rq[2] != 0.f, rq[3] != 0.f};
         ld = uni(pb.w);
         lam2_total += lam2;
-        const float wrow = sW[bf][hw][lane];
         if (pre != 1.f) {   // the block's re-based scale (fast form only), before stage 5
 #pragma unroll
             for (int nt = 0; nt < NTL; ++nt) Sacc[nt] *= pre;
         }
-        // (the direct form weights X only after its stage 2)
-        if (fast) weight_rows(wrow);
 
         f32x16 Yt[2] = {zero16(), zero16()};
         if constexpr (FULL) {
@@ -646,7 +631,7 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
                 // k steps are the quarters in order; at a re-based quarter the
                 // rows from that quarter on move to its reference ----
                 const bool upper = l32 >= 16;        // this lane's row is in the tile's second quarter
-                xk[0] = xfrag(0, 0);
+                xk[0] = xwfrag(0, 0);
                 Yt[0] = mfma32(xk[0], ptile(0, 0), Yt[0]);
                 Yt[1] = mfma32(xk[0], ptile(1, 0), Yt[1]);
                 if (fold[1]) {
@@ -654,14 +639,14 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
                     Yt[0] *= upper ? f : 1.f;
                     Yt[1] *= f;
                 }
-                xk[1] = xfrag(0, 1);
+                xk[1] = xwfrag(0, 1);
                 Yt[0] = mfma32(xk[1], ptile(0, 1), Yt[0]);
                 Yt[1] = mfma32(xk[1], ptile(1, 1), Yt[1]);
                 if (fold[2]) Yt[1] *= fast_exp2(rq[2]);
-                xk[2] = xfrag(1, 0);
+                xk[2] = xwfrag(1, 0);
                 Yt[1] = mfma32(xk[2], ptile(2, 0), Yt[1]);
                 if (fold[3]) Yt[1] *= upper ? fast_exp2(rq[3]) : 1.f;
-                xk[3] = xfrag(1, 1);
+                xk[3] = xwfrag(1, 1);
                 Yt[1] = mfma32(xk[3], ptile(2, 1), Yt[1]);
                 Yt[0] *= e0;
                 Yt[1] *= e1;
@@ -710,14 +695,13 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
 
         // ---- stages 3 + 4: Sacc' = (direct form: 2^(ld + Lam2)) Sacc + B^T X~ ----
         if (!fast) {
-            weight_rows(wrow);   // after the direct-form stage 2, which reads X unweighted
             const float f = fast_exp2(ld_in + lam2);
 #pragma unroll
             for (int nt = 0; nt < NTL; ++nt) Sacc[nt] *= f;
         }
         if (!(FULL && fast)) {   // (the fast stage 2 has left X~ in registers)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) xk[i] = xfrag(i >> 1, i & 1);
+            for (int i = 0; i < 4; ++i) xk[i] = xwfrag(i >> 1, i & 1);
         }
 #pragma unroll
         for (int J = 0; J < 2; ++J) {
