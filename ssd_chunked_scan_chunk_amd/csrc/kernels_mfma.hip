@@ -24,11 +24,15 @@
 //    head-dim tile of one head (P/32 waves per head, 192/P heads per
 //    workgroup) and carries that slice of the head's fp32 state in MFMA
 //    accumulators, so states never round-trip HBM inside a segment.  The
-//    other two are copy waves: they issue every copy into LDS and form the
-//    shared score tiles.  A wave whose memory instruction finds the CU's
-//    queue full stalls until it drains; keeping the copies on waves with no
-//    state work lets those stalls overlap the state waves' MFMA and VALU work
-//    instead of delaying them.  When a launch would leave CUs idle the
+//    other two are copy waves: they issue every copy into LDS, form the
+//    shared score tiles and run stage 1 (the scans of a, the scale decisions
+//    and the per-step weights) one block ahead.  A wave whose memory
+//    instruction finds the CU's queue full stalls until it drains; keeping
+//    the copies on waves with no state work lets those stalls overlap the
+//    state waves' MFMA and VALU work instead of delaying them.  Copy and
+//    state waves run separate loops with the same two barriers per block, so
+//    neither keeps the other's values in registers.  When a launch would
+//    leave CUs idle the
 //    sequence is split into segments: a state-only pass (stages 1, 3, 4)
 //    gives each segment's end state from zero, a scan over segments
 //    (kernels_scan.hip) gives every segment's entering state, and the full
@@ -39,15 +43,16 @@
 //    bf16.
 //  * Inputs reach LDS through asynchronous global_load_lds copies (lane L of a
 //    wave-wide copy lands at LDS base + L * size), double buffered one block
-//    ahead, so HBM traffic overlaps the MFMA work and no register holds
+//    ahead (a: triple buffered two blocks ahead, for stage 1), so HBM traffic
+//    overlaps the MFMA work and no register holds
 //    prefetched data.  The copies are written in inline assembly: they have no
 //    register result, and keeping them out of the compiler's view stops it
 //    from inserting full vmcnt waits before every LDS access, which would
 //    serialise the prefetch.  Only the copy waves wait for copies (vmcnt(0)
 //    once per block); state waves store their Y at the end of each block and
 //    never wait on memory.  Two barriers per block: one publishes the
-//    block's copies (and frees the other buffer), one publishes the shared
-//    scores.
+//    block's copies and stage-1 results (and frees the other buffers), one
+//    publishes the shared scores.
 //  * Every product is v_mfma_f32_32x32x16_bf16 (operand lane l holds row or
 //    column l%32 and 8 k values of group l/32; the accumulator holds column
 //    l%32, rows 8(r/4) + 4(l/32) + r%4 in register r).  Contractions take k
