@@ -321,10 +321,10 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
         return as_bf16x8(*reinterpret_cast<const u32x4*>(tile + 32 * I * N + roff[nt][hf]));
     };
 
-    // ---- copies (aux waves only).  Copy k of aux thread at fills LDS slot
-    // k * kAuxThreads + at (16 bytes; 4 for a).  A thread's piece within a
-    // row is fixed, and so is the row's swizzle; per copy only a uniform row
-    // or head base changes.  Rows past the end of the sequence are clamped to
+    // ---- copies (aux waves only).  Copy k of X, B or C by aux thread at
+    // fills the 16-byte LDS slot k * kAuxThreads + at (a is copied per head,
+    // lane = step).  A thread's piece within a row is fixed, and so is the
+    // row's swizzle; per copy only a uniform row or head base changes.  Rows past the end of the sequence are clamped to
     // the last valid row (their scores are masked, their state weight is zero
     // and their outputs are not stored). ----
     const unsigned at = (unsigned)(tid - kStateWaves * 64);   // aux thread (valid for aux waves)
@@ -410,7 +410,7 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
         return l >= 0.5f * (absh - lamh_) - kRange && l <= kRange - 0.5f * (absh + lamh_);
     };
     if (aux) {
-        // ================= copy waves: copies and scores =================
+        // ================= copy waves: copies, scores and stage 1 =================
         // (copy and state waves run separate loops with the same two barriers
         // per block, so neither keeps the other's values in registers)
         // Stage 1 of block c+1 runs here, after the copies of block c, while
