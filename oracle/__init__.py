@@ -6,9 +6,10 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 
 Two independent formulations live here:
 
-* ``fwd`` / ``step`` / ``chunked_fwd``: the C oracle in ``ssd_oracle.c``
-  (sequential recurrence, one recurrent step, and the fp64 chunked four-stage
-  form with every intermediate), called through ctypes.
+* ``fwd`` / ``step`` / ``chunked_fwd`` / ``bwd``: the C oracle in
+  ``ssd_oracle.c`` (sequential recurrence, one recurrent step, the fp64
+  chunked four-stage form with every intermediate, and the gradients through
+  the recurrence's adjoint), called through ctypes.
 * ``quadratic``: numpy brute force of the dual "structured masked attention"
   form ``Y = (L o C B^T) X`` (wiki review of "Transformers are SSMs", section
   "Core concepts": SMA generalises linear attention with a data-dependent
@@ -63,7 +64,8 @@ def _load():
                                    ctypes.c_int]
         lib.oracle_step.argtypes = [ctypes.POINTER(_Dims), dp, dp, dp, dp, dp, dp]
         lib.oracle_chunked_fwd.argtypes = [ctypes.POINTER(_Dims), ctypes.c_int64] + [dp] * 13
-        for f in (lib.oracle_fwd, lib.oracle_step, lib.oracle_chunked_fwd):
+        lib.oracle_bwd.argtypes = [ctypes.POINTER(_Dims)] + [dp] * 12
+        for f in (lib.oracle_fwd, lib.oracle_step, lib.oracle_chunked_fwd, lib.oracle_bwd):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -144,6 +146,27 @@ def chunked_fwd(X, a, B, C, chunk: int, S0=None):
         _ptr(out["Ydiag"]), _ptr(out["Yoff"]), _ptr(out["Y"]), _ptr(out["S_fin"]))
     if rc:
         raise ValueError("oracle_chunked_fwd rejected its arguments (code %d)" % rc)
+    return out
+
+
+def bwd(X, a, B, C, dY, S0=None, dS_fin=None):
+    """Gradients of l = sum(dY * Y) + sum(dS_fin * S_fin) through the fp64
+    recurrence, by its adjoint (reverse-mode chain rule, see ssd_oracle.c).
+
+    Returns a dict with dX [Bz,L,H,P], da [Bz,L,H], dB / dC [Bz,L,G,N] (summed
+    over each group's heads) and dS0 [Bz,H,P,N]."""
+    X, a, B, C, dY, S0, dS_fin = map(_f64, (X, a, B, C, dY, S0, dS_fin))
+    Bz, L, H, P = X.shape
+    G, N = B.shape[2], B.shape[3]
+    out = {"dX": np.empty((Bz, L, H, P)), "da": np.empty((Bz, L, H)),
+           "dB": np.empty((Bz, L, G, N)), "dC": np.empty((Bz, L, G, N)),
+           "dS0": np.empty((Bz, H, P, N))}
+    d = _dims(X, B)
+    rc = _load().oracle_bwd(ctypes.byref(d), _ptr(X), _ptr(a), _ptr(B), _ptr(C), _ptr(S0),
+                            _ptr(dY), _ptr(dS_fin), _ptr(out["dX"]), _ptr(out["da"]),
+                            _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dS0"]))
+    if rc:
+        raise ValueError("oracle_bwd rejected its arguments (code %d)" % rc)
     return out
 
 

@@ -274,3 +274,126 @@ int oracle_chunked_fwd(const oracle_dims* d, int64_t Q, const double* X,
     free(cs);
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Gradients: the adjoint of the recurrence (reverse-mode chain rule).       */
+/* ------------------------------------------------------------------------ */
+/*
+ * For a scalar loss l with dY = dl/dY and dS_fin = dl/dS_fin (either may be
+ * all zero), the adjoint state G_t = dl/dS_t of each (b, h) slice obeys, in
+ * reverse time,
+ *
+ *   G_{L-1}  = dS_fin + dY_{L-1} (x) C_{L-1}
+ *   G_t      = dY_t (x) C_t + exp(a_{t+1}) G_{t+1}
+ *
+ * (S_t feeds Y_t directly and S_{t+1} through the decay exp(a_{t+1})), and
+ * each input's gradient is the chain rule through the one step that reads it:
+ *
+ *   dX_t[p]  = sum_n G_t[p][n] B_t[n]              (S_t = ... + X_t (x) B_t)
+ *   dB_t[n] += sum_p G_t[p][n] X_t[p]              (summed over the group's heads)
+ *   dC_t[n] += sum_p dY_t[p] S_t[p][n]             (Y_t = S_t C_t; group sum)
+ *   da_t     = exp(a_t) sum_{p,n} G_t[p][n] S_{t-1}[p][n]
+ *   dS0      = exp(a_0) G_0
+ *
+ * The reverse sweep needs the forward states S_t.  They are recomputed one
+ * segment of K steps at a time from checkpoints stored every K steps by a
+ * forward sweep, so memory stays at (L/K + K) states per slice; the arithmetic
+ * is exactly the forward recurrence's, so the recomputed states are the
+ * forward's bit for bit.
+ *
+ * Layouts as above; dX like X, da like a, dB/dC like B/C, dS0 like S0.
+ * S0, dS_fin and dS0 may be NULL (zero initial state / no final-state
+ * gradient / not wanted).
+ */
+int oracle_bwd(const oracle_dims* d, const double* X, const double* a, const double* B,
+               const double* C, const double* S0, const double* dY, const double* dS_fin,
+               double* dX, double* da, double* dB, double* dC, double* dS0)
+{
+    if (!d || !X || !a || !B || !C || !dY || !dX || !da || !dB || !dC) return 1;
+    if (d->ngroups <= 0 || d->nheads % d->ngroups != 0) return 2;
+    const int64_t Bz = d->batch, L = d->seqlen, H = d->nheads, P = d->headdim;
+    const int64_t N = d->dstate, G = d->ngroups, PN = P * N;
+    const int64_t K = 64;                         /* steps per recomputed segment */
+    const int64_t nck = (L + K - 1) / K;
+    double* ck = (double*)malloc(sizeof(double) * (size_t)((nck > 0 ? nck : 1) * PN));
+    double* seg = (double*)malloc(sizeof(double) * (size_t)(K * PN));
+    double* S = (double*)malloc(sizeof(double) * (size_t)PN);
+    double* Gs = (double*)malloc(sizeof(double) * (size_t)PN);
+    if (!ck || !seg || !S || !Gs) {
+        free(ck); free(seg); free(S); free(Gs);
+        return 3;
+    }
+    memset(dB, 0, sizeof(double) * (size_t)(Bz * L * G * N));
+    memset(dC, 0, sizeof(double) * (size_t)(Bz * L * G * N));
+#define X_AT(t, p) X[((b * L + (t)) * H + h) * P + (p)]
+#define DX_AT(t, p) dX[((b * L + (t)) * H + h) * P + (p)]
+#define DY_AT(t, p) dY[((b * L + (t)) * H + h) * P + (p)]
+#define A_AT(t) a[(b * L + (t)) * H + h]
+#define B_AT(t, n) B[((b * L + (t)) * G + g) * N + (n)]
+#define C_AT(t, n) C[((b * L + (t)) * G + g) * N + (n)]
+    for (int64_t b = 0; b < Bz; ++b)
+        for (int64_t h = 0; h < H; ++h) {
+            const int64_t g = h * G / H;
+            /* forward sweep: ck[m] = the state entering step m*K */
+            for (int64_t k = 0; k < PN; ++k) S[k] = S0 ? S0[(b * H + h) * PN + k] : 0.0;
+            for (int64_t t = 0; t < L; ++t) {
+                if (t % K == 0) memcpy(ck + (t / K) * PN, S, sizeof(double) * (size_t)PN);
+                const double e = exp(A_AT(t));
+                for (int64_t p = 0; p < P; ++p)
+                    for (int64_t n = 0; n < N; ++n)
+                        S[p * N + n] = e * S[p * N + n] + X_AT(t, p) * B_AT(t, n);
+            }
+            /* reverse sweep */
+            for (int64_t k = 0; k < PN; ++k) Gs[k] = dS_fin ? dS_fin[(b * H + h) * PN + k] : 0.0;
+            for (int64_t m = nck - 1; m >= 0; --m) {
+                const int64_t t0 = m * K, t1 = (t0 + K < L) ? t0 + K : L;
+                /* recompute the segment's post-update states */
+                memcpy(S, ck + m * PN, sizeof(double) * (size_t)PN);
+                for (int64_t t = t0; t < t1; ++t) {
+                    const double e = exp(A_AT(t));
+                    for (int64_t p = 0; p < P; ++p)
+                        for (int64_t n = 0; n < N; ++n)
+                            S[p * N + n] = e * S[p * N + n] + X_AT(t, p) * B_AT(t, n);
+                    memcpy(seg + (t - t0) * PN, S, sizeof(double) * (size_t)PN);
+                }
+                for (int64_t t = t1 - 1; t >= t0; --t) {
+                    const double* St = seg + (t - t0) * PN;
+                    const double* Sprev = (t > t0) ? seg + (t - t0 - 1) * PN : ck + m * PN;
+                    /* G_t = dY_t (x) C_t + (decayed later contributions, already in Gs) */
+                    for (int64_t p = 0; p < P; ++p)
+                        for (int64_t n = 0; n < N; ++n) Gs[p * N + n] += DY_AT(t, p) * C_AT(t, n);
+                    for (int64_t n = 0; n < N; ++n) {
+                        double sc = 0.0, sb = 0.0;
+                        for (int64_t p = 0; p < P; ++p) {
+                            sc += DY_AT(t, p) * St[p * N + n];
+                            sb += Gs[p * N + n] * X_AT(t, p);
+                        }
+                        dC[((b * L + t) * G + g) * N + n] += sc;
+                        dB[((b * L + t) * G + g) * N + n] += sb;
+                    }
+                    for (int64_t p = 0; p < P; ++p) {
+                        double s = 0.0;
+                        for (int64_t n = 0; n < N; ++n) s += Gs[p * N + n] * B_AT(t, n);
+                        DX_AT(t, p) = s;
+                    }
+                    const double e = exp(A_AT(t));
+                    double s = 0.0;
+                    for (int64_t k = 0; k < PN; ++k) s += Gs[k] * Sprev[k];
+                    da[(b * L + t) * H + h] = e * s;
+                    for (int64_t k = 0; k < PN; ++k) Gs[k] *= e;   /* now dl/dS_{t-1} */
+                }
+            }
+            if (dS0) memcpy(dS0 + (b * H + h) * PN, Gs, sizeof(double) * (size_t)PN);
+        }
+#undef X_AT
+#undef DX_AT
+#undef DY_AT
+#undef A_AT
+#undef B_AT
+#undef C_AT
+    free(ck);
+    free(seg);
+    free(S);
+    free(Gs);
+    return 0;
+}

@@ -256,3 +256,112 @@ def test_input_recipes_ranges():
     # same seed, same draws
     d3 = si.make_fwd(si.FwdShape(2, 300, 8, 4, 4, 1, 64, "bf16"))
     np.testing.assert_array_equal(d2["X"], d3["X"])
+
+
+# ---- gradients: the adjoint of the recurrence ---------------------------------
+
+def _loss(X, a, B, C, S0, dY, dS):
+    Y, S = oracle.fwd(X, a, B, C, S0=S0)
+    return float(np.sum(dY * Y) + np.sum(dS * S))
+
+
+@pytest.mark.parametrize("G", [1, 2])
+def test_gradients_match_central_differences(G):
+    # every gradient against central differences of the forward oracle on a
+    # tiny case with an initial state and a final-state gradient; catches a
+    # dropped adjoint term, a decay applied at the wrong step, a missing
+    # group sum for dB/dC or a transposed contraction
+    rng = np.random.default_rng(40 + G)
+    Bz, L, H, P, N = 1, 9, 2, 3, 4
+    X, a, B, C = rand_case(rng, Bz, L, H, P, N, G)
+    S0 = rng.standard_normal((Bz, H, P, N))
+    dY = rng.standard_normal((Bz, L, H, P))
+    dS = rng.standard_normal((Bz, H, P, N))
+    gr = oracle.bwd(X, a, B, C, dY, S0=S0, dS_fin=dS)
+    args = {"X": X, "a": a, "B": B, "C": C, "S0": S0}
+    eps = 1e-6
+    for name, arr in args.items():
+        num = np.empty_like(arr)
+        for idx in np.ndindex(arr.shape):
+            keep = arr[idx]
+            arr[idx] = keep + eps
+            lp = _loss(args["X"], args["a"], args["B"], args["C"], args["S0"], dY, dS)
+            arr[idx] = keep - eps
+            lm = _loss(args["X"], args["a"], args["B"], args["C"], args["S0"], dY, dS)
+            arr[idx] = keep
+            num[idx] = (lp - lm) / (2 * eps)
+        got = gr["d" + name]
+        scale = np.max(np.abs(num))
+        assert np.max(np.abs(got - num)) <= 1e-7 * scale, name
+
+
+def test_dX_is_the_transposed_quadratic_form():
+    # dX = M^T dY with M = Lmask o (C B^T) per slice (the brute-force dual
+    # form, built independently of the recurrence); zero initial state and no
+    # final-state gradient
+    rng = np.random.default_rng(7)
+    X, a, B, C = rand_case(rng, Bz=2, L=23, H=4, P=3, N=5, G=2)
+    dY = rng.standard_normal(X.shape)
+    gr = oracle.bwd(X, a, B, C, dY)
+    Bz, L, H, P = X.shape
+    G = B.shape[2]
+    for b in range(Bz):
+        for h in range(H):
+            g = h * G // H
+            M = oracle.decay_mask(a[b, :, h]) * (C[b, :, g, :] @ B[b, :, g, :].T)
+            np.testing.assert_allclose(gr["dX"][b, :, h, :], M.T @ dY[b, :, h, :], rtol=0, atol=1e-11)
+
+
+def test_da_equals_reverse_cumsum_identity():
+    # da_t = sum_{k>=t} (dY_k . Y_k - X_k . dX_k) + <dS_fin, S_fin>: the loss
+    # depends on a only through the prefix sums cs_k, with dl/dcs_k = row sum
+    # minus column sum of the weighted mask; an independent formula for da
+    rng = np.random.default_rng(8)
+    X, a, B, C = rand_case(rng, Bz=2, L=31, H=3, P=4, N=3, G=1)
+    S0 = rng.standard_normal((2, 3, 4, 3))
+    dY = rng.standard_normal(X.shape)
+    dS = rng.standard_normal(S0.shape)
+    Y, S = oracle.fwd(X, a, B, C, S0=S0)
+    gr = oracle.bwd(X, a, B, C, dY, S0=S0, dS_fin=dS)
+    term = np.sum(dY * Y, axis=3) - np.sum(X * gr["dX"], axis=3)          # [Bz, L, H]
+    rev = np.flip(np.cumsum(np.flip(term, axis=1), axis=1), axis=1)
+    expect = rev + np.sum(dS * S, axis=(2, 3))[:, None, :]
+    np.testing.assert_allclose(gr["da"], expect, rtol=0, atol=1e-10 * np.max(np.abs(expect)))
+
+
+def test_zero_decay_gradients_are_linear_attention_gradients():
+    # a = 0: Y = tril(C B^T) X per slice, so dC_t = sum_{s<=t} (dY_t . X_s) B_s
+    # and dB_s = sum_{t>=s} (dY_t . X_s) C_t, summed over the group's heads
+    rng = np.random.default_rng(9)
+    X, _, B, C = rand_case(rng, Bz=1, L=17, H=4, P=3, N=5, G=2)
+    a = np.zeros(X.shape[:3])
+    dY = rng.standard_normal(X.shape)
+    gr = oracle.bwd(X, a, B, C, dY)
+    Bz, L, H, P = X.shape
+    G = B.shape[2]
+    dB = np.zeros(B.shape)
+    dC = np.zeros(C.shape)
+    for h in range(H):
+        g = h * G // H
+        W = np.tril(dY[0, :, h, :] @ X[0, :, h, :].T)      # W[t, s] = dY_t . X_s, s <= t
+        dC[0, :, g, :] += W @ B[0, :, g, :]
+        dB[0, :, g, :] += W.T @ C[0, :, g, :]
+    np.testing.assert_allclose(gr["dC"], dC, rtol=0, atol=1e-11)
+    np.testing.assert_allclose(gr["dB"], dB, rtol=0, atol=1e-11)
+
+
+def test_gradients_across_recompute_segments():
+    # a sequence longer than the oracle's 64-step recompute segment, checked
+    # through the transposed quadratic form (dX) and the initial-state
+    # response (dS0 = sum_t exp(cs_t) dY_t (x) C_t with zero dS_fin)
+    rng = np.random.default_rng(10)
+    X, a, B, C = rand_case(rng, Bz=1, L=150, H=2, P=2, N=3, G=1, a_scale=0.05)
+    S0 = rng.standard_normal((1, 2, 2, 3))
+    dY = rng.standard_normal(X.shape)
+    gr = oracle.bwd(X, a, B, C, dY, S0=S0)
+    for h in range(2):
+        M = oracle.decay_mask(a[0, :, h]) * (C[0, :, 0, :] @ B[0, :, 0, :].T)
+        np.testing.assert_allclose(gr["dX"][0, :, h, :], M.T @ dY[0, :, h, :], rtol=0, atol=1e-10)
+        cs = np.cumsum(a[0, :, h])
+        dS0 = np.einsum("t,tp,tn->pn", np.exp(cs), dY[0, :, h, :], C[0, :, 0, :])
+        np.testing.assert_allclose(gr["dS0"][0, h], dS0, rtol=0, atol=1e-10)
