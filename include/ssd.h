@@ -119,6 +119,36 @@ ssd_status ssd_chunk_scan_fwd(const ssd_fwd_desc* desc, const void* X, const flo
 ssd_status ssd_step(const ssd_step_desc* desc, float* state, const void* x, const float* a,
                     const void* B, const void* C, void* y, void* stream);
 
+/* ---- Backward (gradients of the full forward) ----
+ *
+ * For a scalar loss l with upstream gradients dY = dl/dY and (optional)
+ * dfinal_state = dl/dS_fin, the adjoint of the recurrence above --
+ * G_t = dl/dS_t = dY_t C_t^T + exp(a_{t+1}) G_{t+1}, G_{L-1} also receiving
+ * dS_fin -- gives
+ *     dX_t = G_t B_t,   dB_t = sum_{h in group} G_t^T X_t,
+ *     dC_t = sum_{h in group} S_t^T dY_t,   da_t = exp(a_t) <G_t, S_{t-1}>,
+ *     dinitial_state = exp(a_0) G_0
+ * (the reverse-mode derivative of the 1-semiseparable product that the
+ * CiteArk page of "Transformers are SSMs", section "AI research summary",
+ * names; the page's mention of training optimisations is what it serves).
+ * bf16 inputs only, chunk in {64,128,256}, headdim in {32,64}, dstate in
+ * {64,128}; desc->algo must be AUTO or MFMA and seg_chunks is ignored.
+ * Reads X, a, B, C, initial_state (NULL = zero) and dY, dfinal_state (NULL =
+ * zero); writes dX, dB, dC (bf16, rounded once from fp32 sums), da (fp32)
+ * and, if dinitial_state != NULL, that gradient (fp32).  No output may
+ * overlap an input, another output or the workspace.  The workspace holds
+ * the per-chunk forward states and the adjoint's per-chunk states plus
+ * time-reversed copies of the operands (about
+ * 2 * batch * nchunks * nheads * headdim * dstate * 4 bytes plus a few
+ * sequence-sized bf16 arrays); its size comes from ssd_bwd_workspace_bytes
+ * and its contents on entry are ignored.  Errors as for ssd_chunk_scan_fwd. */
+ssd_status ssd_bwd_workspace_bytes(const ssd_fwd_desc* desc, size_t* bytes);
+ssd_status ssd_chunk_scan_bwd(const ssd_fwd_desc* desc, const void* X, const float* a,
+                              const void* B, const void* C, const float* initial_state,
+                              const void* dY, const float* dfinal_state, void* dX, float* da,
+                              void* dB, void* dC, float* dinitial_state, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
 /* ---- Stage entry points (the same kernels' building blocks, exposed so
  * each stage can be checked and timed on its own).  bf16 MFMA path only,
  * except ssd_chunk_cumsum which takes any dtype descriptor.  Stages 3-5 work

@@ -21,7 +21,7 @@ from . import _lib
 from ._lib import (SSD_ALGO_AUTO, SSD_ALGO_MFMA, SSD_ALGO_VALU, SSD_BF16, SSD_F32,
                    SSDError)
 
-__all__ = ["chunk_scan_fwd", "step", "chunk_cumsum", "chunk_state", "state_passing",
+__all__ = ["chunk_scan_fwd", "chunk_scan_bwd", "bwd_workspace_bytes", "step", "chunk_cumsum", "chunk_state", "state_passing",
            "chunk_scan", "fwd_plan", "workspace_bytes", "SSDError", "SSD_ALGO_AUTO",
            "SSD_ALGO_MFMA", "SSD_ALGO_VALU", "library_path"]
 
@@ -98,6 +98,41 @@ def chunk_scan_fwd(X, a, B, C, chunk, initial_state=None, return_final_state=Fal
         ctypes.byref(d), _ptr(X), _ptr(a), _ptr(B), _ptr(C), _ptr(initial_state), _ptr(Y),
         _ptr(final_state), _ptr(workspace), wsz, _stream(dev)))
     return Y, final_state
+
+
+def bwd_workspace_bytes(X, B, chunk) -> int:
+    d = _desc(X, B, chunk, SSD_ALGO_AUTO, 0)
+    n = ctypes.c_size_t()
+    _lib.check(_L().ssd_bwd_workspace_bytes(ctypes.byref(d), ctypes.byref(n)))
+    return n.value
+
+
+def chunk_scan_bwd(X, a, B, C, dY, chunk, initial_state=None, dfinal_state=None,
+                   return_dinitial_state=False, workspace=None):
+    """Gradients of the full forward for upstream dY (and dfinal_state).
+
+    Returns a dict with dX, dB, dC (X's dtype), da (float32) and dinitial_state
+    (float32, or None unless requested)."""
+    d = _desc(X, B, chunk, SSD_ALGO_AUTO, 0)
+    dev = X.device
+    dX = torch.empty_like(X)
+    dB = torch.empty_like(B)
+    dC = torch.empty_like(C)
+    da = torch.empty_like(a)
+    dS0 = None
+    if return_dinitial_state:
+        dS0 = torch.empty((X.shape[0], X.shape[2], X.shape[3], B.shape[3]), dtype=torch.float32,
+                          device=dev)
+    nws = ctypes.c_size_t()
+    _lib.check(_L().ssd_bwd_workspace_bytes(ctypes.byref(d), ctypes.byref(nws)))
+    if workspace is None and nws.value > 0:
+        workspace = torch.empty(nws.value, dtype=torch.uint8, device=dev)
+    wsz = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _lib.check(_L().ssd_chunk_scan_bwd(
+        ctypes.byref(d), _ptr(X), _ptr(a), _ptr(B), _ptr(C), _ptr(initial_state), _ptr(dY),
+        _ptr(dfinal_state), _ptr(dX), _ptr(da), _ptr(dB), _ptr(dC), _ptr(dS0), _ptr(workspace),
+        wsz, _stream(dev)))
+    return {"dX": dX, "da": da, "dB": dB, "dC": dC, "dinitial_state": dS0}
 
 
 def step(state, x, a, B, C, y=None):

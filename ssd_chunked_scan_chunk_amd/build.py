@@ -16,7 +16,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libssd.so")
-SOURCES = ["api.cpp", "kernels_scan.hip", "kernels_mfma.hip", "kernels_step.hip"]
+SOURCES = ["api.cpp", "kernels_scan.hip", "kernels_mfma.hip", "kernels_step.hip",
+           "kernels_bwd.hip"]
 
 
 def hipcc() -> str:
@@ -52,7 +53,7 @@ def build(verbose: bool = False) -> str:
                 print("\n".join(msgs), file=sys.stderr)
         return obj
 
-    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+    with ThreadPoolExecutor(max_workers=min(5, len(SOURCES))) as ex:
         objs = list(ex.map(compile_one, SOURCES))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs

@@ -220,6 +220,133 @@ ssd_status check_fwd_io(const Plan& p, const void* X, const float* a, const void
     return SSD_OK;
 }
 
+// Enqueue the planned forward; every argument has been validated.
+ssd_status run_fwd(const Plan& p, const void* X, const float* a, const void* B, const void* C,
+                   const float* initial_state, void* Y, float* final_state, void* workspace,
+                   hipStream_t hs) {
+    const ssd::FwdShape& s = p.s;
+    const int64_t PN = s.P * s.N;
+    hipError_t e = hipSuccess;
+    if (s.Bz == 0) return ok();
+    if (s.L == 0) {
+        if (final_state) {
+            e = initial_state ? ssd::launch_copy_f32(final_state, initial_state, s.Bz * s.H * PN, hs)
+                              : ssd::launch_fill_zero(final_state, s.Bz * s.H * PN, hs);
+            if (e != hipSuccess) return hip_fail(e, "empty-sequence final state");
+        }
+        return ok();
+    }
+    if (p.algo == SSD_ALGO_VALU) {
+        e = ssd::launch_valu_fwd(s, p.bf16, X, a, B, C, initial_state, Y, final_state, hs);
+        if (e != hipSuccess) return hip_fail(e, "VALU forward launch");
+        return ok();
+    }
+    if (p.nseg == 1) {
+        ssd::StateSrc src{initial_state, s.H * PN, nullptr, 0, 0};
+        e = ssd::launch_mfma_out(s, p.seg_chunks, 1, X, a, B, C, src, Y, final_state, hs);
+        if (e != hipSuccess) return hip_fail(e, "MFMA forward launch");
+        return ok();
+    }
+    float* Sbuf = static_cast<float*>(workspace);
+    const size_t states = (size_t)s.Bz * p.nseg * s.H * PN * sizeof(float);
+    float* lamseg = reinterpret_cast<float*>(static_cast<char*>(workspace) + ((states + 255) / 256) * 256);
+    e = ssd::launch_mfma_state(s, p.seg_chunks, p.nseg - 1, p.nseg, X, a, B, Sbuf, lamseg, hs);
+    if (e != hipSuccess) return hip_fail(e, "MFMA segment-state launch");
+    // segment 0 starts from initial_state itself, so slot 0 is never written
+    e = ssd::launch_state_scan(s, p.nseg - 1, p.nseg, Sbuf, lamseg, s.H * p.nseg, p.nseg,
+                               initial_state, Sbuf, 1, Sbuf + (p.nseg - 1) * s.H * PN,
+                               p.nseg * s.H * PN, hs);
+    if (e != hipSuccess) return hip_fail(e, "segment scan launch");
+    ssd::StateSrc src{initial_state, s.H * PN, Sbuf, p.nseg * s.H * PN, s.H * PN};
+    e = ssd::launch_mfma_out(s, p.seg_chunks, p.nseg, X, a, B, C, src, Y, final_state, hs);
+    if (e != hipSuccess) return hip_fail(e, "MFMA forward launch");
+    return ok();
+}
+
+
+// ---- backward plan ------------------------------------------------------------
+// Workspace regions of the backward, in order.
+enum BwdBuf {
+    W_SFW, W_LAMFW,       // forward chunk-entering states and chunk log-decays
+    W_SREV, W_LAMREV,     // the same for the time-reversed adjoint problem
+    W_DYR, W_CR, W_BR, W_AR, W_DXR,   // reversed dY, C, B, shifted a; reversed dX
+    W_BEXP, W_AEXP, W_S0T, W_DCH,     // dC pass: B per head, a per sub-head, S0^T, output
+    W_CREXP, W_XR, W_AREXP, W_DSFT, W_DBH,   // dB pass (reversed)
+    W_INNER,              // workspace of the dC / dB passes
+    kBwdBufs
+};
+
+struct BwdPlan {
+    ssd::FwdShape s;   // the layer
+    ssd::FwdShape sr;  // the reversed problem: seqlen padded to whole chunks
+    int64_t ns;        // the dB / dC passes split the state dimension into ns head-dims of 64
+    Plan pc, pb;       // plans of the dC and dB passes
+    size_t off[kBwdBufs + 1];
+};
+
+ssd_status make_bwd_plan(const ssd_fwd_desc* d, BwdPlan* bp) {
+    ssd_status st = check_desc(d, true);
+    if (st != SSD_OK) return st;
+    if (d->dtype != SSD_BF16)
+        return fail(SSD_ERR_UNSUPPORTED, "the backward is compiled for bf16 inputs only");
+    if (d->algo == SSD_ALGO_VALU)
+        return fail(SSD_ERR_UNSUPPORTED, "the backward has no VALU variant");
+    const ssd::FwdShape s = shape_of(d);
+    if (!ssd::mfma_supported(s.Q, s.P, s.N) || !ssd::bwd_da_supported(s.Q, s.P, s.N))
+        return fail(SSD_ERR_UNSUPPORTED,
+                    "no backward kernels for chunk=%lld headdim=%lld dstate=%lld "
+                    "(chunk in {64,128,256}, headdim in {32,64}, dstate in {64,128})",
+                    (long long)s.Q, (long long)s.P, (long long)s.N);
+    if ((s.Bz * s.nc * s.H + 8) * 256 >= ((int64_t)1 << 32) || s.nc > 0x7fffffff)
+        return fail(SSD_ERR_UNSUPPORTED, "batch*chunks*heads too large for one launch");
+    bp->s = s;
+    bp->sr = s;
+    bp->sr.L = s.nc * s.Q;
+    bp->ns = s.N / 64;
+    // dC: the forward-time product with x in the role of B, dy in that of C and
+    // B (split into 64-wide pieces, one per sub-head) in that of X; dB: the same
+    // on reversed time with dy as B, x as C and C as X
+    ssd_fwd_desc dc{s.Bz, s.L, s.H * bp->ns, s.N / bp->ns, s.P, s.H, s.Q, SSD_BF16,
+                    SSD_ALGO_AUTO, 0};
+    ssd_fwd_desc db = dc;
+    db.seqlen = bp->sr.L;
+    st = make_plan(&dc, &bp->pc);
+    if (st != SSD_OK) return st;
+    st = make_plan(&db, &bp->pb);
+    if (st != SSD_OK) return st;
+    const int64_t Bz = s.Bz, L = s.L, Lp = bp->sr.L, H = s.H, G = s.G, P = s.P, N = s.N;
+    const int64_t nc = s.nc, PN = P * N, ns = bp->ns;
+    int64_t bytes[kBwdBufs] = {};
+    if (Bz > 0 && L > 0) {
+        bytes[W_SFW] = Bz * nc * H * PN * 4;
+        bytes[W_LAMFW] = Bz * H * nc * 4;
+        bytes[W_SREV] = bytes[W_SFW];
+        bytes[W_LAMREV] = bytes[W_LAMFW];
+        bytes[W_DYR] = Bz * Lp * H * P * 2;
+        bytes[W_CR] = Bz * Lp * G * N * 2;
+        bytes[W_BR] = bytes[W_CR];
+        bytes[W_AR] = Bz * Lp * H * 4;
+        bytes[W_DXR] = bytes[W_DYR];
+        bytes[W_BEXP] = Bz * L * H * N * 2;
+        bytes[W_AEXP] = Bz * L * H * ns * 4;
+        bytes[W_S0T] = Bz * H * PN * 4;
+        bytes[W_DCH] = bytes[W_BEXP];
+        bytes[W_CREXP] = Bz * Lp * H * N * 2;
+        bytes[W_XR] = bytes[W_DYR];
+        bytes[W_AREXP] = Bz * Lp * H * ns * 4;
+        bytes[W_DSFT] = bytes[W_S0T];
+        bytes[W_DBH] = bytes[W_CREXP];
+        bytes[W_INNER] = (int64_t)(bp->pc.ws > bp->pb.ws ? bp->pc.ws : bp->pb.ws);
+    }
+    size_t o = 0;
+    for (int i = 0; i < kBwdBufs; ++i) {
+        bp->off[i] = o;
+        o += (size_t)(((bytes[i] + 255) / 256) * 256);
+    }
+    bp->off[kBwdBufs] = o;
+    return SSD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -288,44 +415,8 @@ ssd_status ssd_chunk_scan_fwd(const ssd_fwd_desc* desc, const void* X, const flo
         for (const Range& o : others)
             if (overlap(w, o)) return fail(SSD_ERR_ALIAS, "workspace overlaps %s", o.name);
     }
-    const ssd::FwdShape& s = p.s;
-    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-    const int64_t PN = s.P * s.N;
-    hipError_t e = hipSuccess;
-    if (s.Bz == 0) return ok();
-    if (s.L == 0) {
-        if (final_state) {
-            e = initial_state ? ssd::launch_copy_f32(final_state, initial_state, s.Bz * s.H * PN, hs)
-                              : ssd::launch_fill_zero(final_state, s.Bz * s.H * PN, hs);
-            if (e != hipSuccess) return hip_fail(e, "empty-sequence final state");
-        }
-        return ok();
-    }
-    if (p.algo == SSD_ALGO_VALU) {
-        e = ssd::launch_valu_fwd(s, p.bf16, X, a, B, C, initial_state, Y, final_state, hs);
-        if (e != hipSuccess) return hip_fail(e, "VALU forward launch");
-        return ok();
-    }
-    if (p.nseg == 1) {
-        ssd::StateSrc src{initial_state, s.H * PN, nullptr, 0, 0};
-        e = ssd::launch_mfma_out(s, p.seg_chunks, 1, X, a, B, C, src, Y, final_state, hs);
-        if (e != hipSuccess) return hip_fail(e, "MFMA forward launch");
-        return ok();
-    }
-    float* Sbuf = static_cast<float*>(workspace);
-    const size_t states = (size_t)s.Bz * p.nseg * s.H * PN * sizeof(float);
-    float* lamseg = reinterpret_cast<float*>(static_cast<char*>(workspace) + ((states + 255) / 256) * 256);
-    e = ssd::launch_mfma_state(s, p.seg_chunks, p.nseg - 1, p.nseg, X, a, B, Sbuf, lamseg, hs);
-    if (e != hipSuccess) return hip_fail(e, "MFMA segment-state launch");
-    // segment 0 starts from initial_state itself, so slot 0 is never written
-    e = ssd::launch_state_scan(s, p.nseg - 1, p.nseg, Sbuf, lamseg, s.H * p.nseg, p.nseg,
-                               initial_state, Sbuf, 1, Sbuf + (p.nseg - 1) * s.H * PN,
-                               p.nseg * s.H * PN, hs);
-    if (e != hipSuccess) return hip_fail(e, "segment scan launch");
-    ssd::StateSrc src{initial_state, s.H * PN, Sbuf, p.nseg * s.H * PN, s.H * PN};
-    e = ssd::launch_mfma_out(s, p.seg_chunks, p.nseg, X, a, B, C, src, Y, final_state, hs);
-    if (e != hipSuccess) return hip_fail(e, "MFMA forward launch");
-    return ok();
+    return run_fwd(p, X, a, B, C, initial_state, Y, final_state, workspace,
+                   reinterpret_cast<hipStream_t>(stream));
 }
 
 ssd_status ssd_step(const ssd_step_desc* d, float* state, const void* x, const float* a,
@@ -472,6 +563,124 @@ ssd_status ssd_chunk_scan(const ssd_fwd_desc* desc, const void* X, const float* 
     hipError_t e = ssd::launch_mfma_out(s, p.seg_chunks, p.nseg, X, a, B, C, src, Y, nullptr,
                                         reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "chunk scan launch");
+    return ok();
+}
+
+
+ssd_status ssd_bwd_workspace_bytes(const ssd_fwd_desc* desc, size_t* bytes) {
+    if (!bytes) return fail(SSD_ERR_NULL, "bytes is NULL");
+    BwdPlan bp;
+    ssd_status st = make_bwd_plan(desc, &bp);
+    if (st != SSD_OK) return st;
+    *bytes = bp.off[kBwdBufs];
+    return ok();
+}
+
+ssd_status ssd_chunk_scan_bwd(const ssd_fwd_desc* desc, const void* X, const float* a,
+                              const void* B, const void* C, const float* initial_state,
+                              const void* dY, const float* dfinal_state, void* dX, float* da,
+                              void* dB, void* dC, float* dinitial_state, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    BwdPlan bp;
+    ssd_status st = make_bwd_plan(desc, &bp);
+    if (st != SSD_OK) return st;
+    const ssd::FwdShape& s = bp.s;
+    const int64_t Bz = s.Bz, L = s.L, Lp = bp.sr.L, H = s.H, G = s.G, P = s.P, N = s.N;
+    const int64_t nc = s.nc, PN = P * N, ns = bp.ns;
+    const size_t need = bp.off[kBwdBufs];
+    if (Bz == 0) return ok();
+    if (L > 0 && (!X || !a || !B || !C || !dY || !dX || !da || !dB || !dC))
+        return fail(SSD_ERR_NULL, "X, a, B, C, dY, dX, da, dB and dC are required");
+    const void* v16[] = {X, B, C, dY, dX, dB, dC, initial_state, dfinal_state, dinitial_state, workspace};
+    const char* n16[] = {"X", "B", "C", "dY", "dX", "dB", "dC", "initial_state", "dfinal_state",
+                         "dinitial_state", "workspace"};
+    for (int i = 0; i < 11; ++i)
+        if (v16[i] && !aligned(v16[i], 16)) return fail(SSD_ERR_ALIGN, "%s is not 16-byte aligned", n16[i]);
+    if ((a && !aligned(a, 4)) || (da && !aligned(da, 4))) return fail(SSD_ERR_ALIGN, "a / da misaligned");
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(SSD_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need, workspace_bytes,
+                    workspace ? "" : ", NULL");
+    const int64_t nX = Bz * L * H * P * 2, nBC = Bz * L * G * N * 2, nA = Bz * L * H * 4, nS = Bz * H * PN * 4;
+    const Range ins[] = {rng("X", X, nX), rng("a", a, nA), rng("B", B, nBC), rng("C", C, nBC),
+                         rng("initial_state", initial_state, initial_state ? nS : 0),
+                         rng("dY", dY, nX), rng("dfinal_state", dfinal_state, dfinal_state ? nS : 0)};
+    const Range outs[] = {rng("dX", dX, nX), rng("da", da, nA), rng("dB", dB, nBC), rng("dC", dC, nBC),
+                          rng("dinitial_state", dinitial_state, dinitial_state ? nS : 0),
+                          rng("workspace", workspace, need > 0 ? (int64_t)need : 0)};
+    for (int i = 0; i < 6; ++i) {
+        for (const Range& r : ins)
+            if (overlap(outs[i], r)) return fail(SSD_ERR_ALIAS, "%s overlaps input %s", outs[i].name, r.name);
+        for (int j = i + 1; j < 6; ++j)
+            if (overlap(outs[i], outs[j])) return fail(SSD_ERR_ALIAS, "%s overlaps %s", outs[i].name, outs[j].name);
+    }
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    if (L == 0) {   // S_fin = S0: the adjoint passes straight through
+        if (dinitial_state) {
+            e = dfinal_state ? ssd::launch_copy_f32(dinitial_state, dfinal_state, Bz * H * PN, hs)
+                             : ssd::launch_fill_zero(dinitial_state, Bz * H * PN, hs);
+            if (e != hipSuccess) return hip_fail(e, "empty-sequence state gradient");
+        }
+        return ok();
+    }
+    char* ws = static_cast<char*>(workspace);
+    auto F = [&](int i) { return reinterpret_cast<float*>(ws + bp.off[i]); };
+    auto V = [&](int i) { return static_cast<void*>(ws + bp.off[i]); };
+#define SSD_TRY(expr, what)                                  \
+    do {                                                     \
+        e = (expr);                                          \
+        if (e != hipSuccess) return hip_fail(e, what);       \
+    } while (0)
+    // 1. the state entering every forward chunk
+    SSD_TRY(ssd::launch_mfma_state(s, 1, nc - 1, nc, X, a, B, F(W_SFW), F(W_LAMFW), hs), "bwd: chunk states");
+    SSD_TRY(ssd::launch_state_scan(s, nc - 1, nc, F(W_SFW), F(W_LAMFW), H * nc, nc, initial_state,
+                                   F(W_SFW), 0, F(W_SFW) + (nc - 1) * H * PN, nc * H * PN, hs),
+            "bwd: state scan");
+    // 2. the adjoint recurrence runs backwards in time: reverse the sequence
+    // (padded at its start to whole chunks, so that reversed chunks coincide
+    // with forward ones), with the decay of reversed step t' = a at forward
+    // step Lp - t' (zero where that is past the end)
+    SSD_TRY(ssd::launch_remap_rows(V(W_DYR), dY, Bz, Lp, L, Lp - 1, -1, H * P * 2, hs), "bwd: reverse dY");
+    SSD_TRY(ssd::launch_remap_rows(V(W_CR), C, Bz, Lp, L, Lp - 1, -1, G * N * 2, hs), "bwd: reverse C");
+    SSD_TRY(ssd::launch_remap_rows(V(W_BR), B, Bz, Lp, L, Lp - 1, -1, G * N * 2, hs), "bwd: reverse B");
+    SSD_TRY(ssd::launch_remap_a(F(W_AR), a, Bz, Lp, L, Lp, -1, H, 1, hs), "bwd: reverse a");
+    // 3. dX = G B, with G the state of the reversed problem (dy as X, C as B,
+    // B as C, dS_fin as its initial state); its final state is G_0
+    SSD_TRY(ssd::launch_mfma_state(bp.sr, 1, nc - 1, nc, V(W_DYR), F(W_AR), V(W_CR), F(W_SREV),
+                                   F(W_LAMREV), hs), "bwd: adjoint chunk states");
+    SSD_TRY(ssd::launch_state_scan(bp.sr, nc - 1, nc, F(W_SREV), F(W_LAMREV), H * nc, nc, dfinal_state,
+                                   F(W_SREV), 0, F(W_SREV) + (nc - 1) * H * PN, nc * H * PN, hs),
+            "bwd: adjoint state scan");
+    {
+        ssd::StateSrc src{dfinal_state, H * PN, F(W_SREV), nc * H * PN, H * PN};
+        SSD_TRY(ssd::launch_mfma_out(bp.sr, 1, nc, V(W_DYR), F(W_AR), V(W_CR), V(W_BR), src, V(W_DXR),
+                                     dinitial_state, hs), "bwd: dX pass");
+    }
+    SSD_TRY(ssd::launch_remap_rows(dX, V(W_DXR), Bz, L, Lp, Lp - 1, -1, H * P * 2, hs), "bwd: dX order");
+    if (dinitial_state)
+        SSD_TRY(ssd::launch_scale_state_by_a0(dinitial_state, a, Bz, L, H, PN, hs), "bwd: dS0");
+    // 4. da from the chunk-local four-term form
+    SSD_TRY(ssd::launch_bwd_da(s, X, dY, a, B, C, F(W_SFW), F(W_SREV), da, hs), "bwd: da");
+    // 5. dC = S^T dy: forward-time product, state dimensions exchanged
+    SSD_TRY(ssd::launch_bcast_heads(V(W_BEXP), B, Bz, L, L, 0, 1, H, G, N, hs), "bwd: B per head");
+    SSD_TRY(ssd::launch_remap_a(F(W_AEXP), a, Bz, L, L, 0, 1, H, ns, hs), "bwd: a per sub-head");
+    if (initial_state)
+        SSD_TRY(ssd::launch_state_transpose(F(W_S0T), initial_state, Bz * H, P, N, hs), "bwd: S0^T");
+    st = run_fwd(bp.pc, V(W_BEXP), F(W_AEXP), X, dY, initial_state ? F(W_S0T) : nullptr, V(W_DCH),
+                 nullptr, V(W_INNER), hs);
+    if (st != SSD_OK) return st;
+    SSD_TRY(ssd::launch_group_sum(dC, V(W_DCH), Bz, L, L, 0, 1, H, G, N, hs), "bwd: dC group sum");
+    // 6. dB = G^T x: reversed-time product, state dimensions exchanged
+    SSD_TRY(ssd::launch_bcast_heads(V(W_CREXP), C, Bz, Lp, L, Lp - 1, -1, H, G, N, hs), "bwd: C per head");
+    SSD_TRY(ssd::launch_remap_rows(V(W_XR), X, Bz, Lp, L, Lp - 1, -1, H * P * 2, hs), "bwd: reverse X");
+    SSD_TRY(ssd::launch_remap_a(F(W_AREXP), a, Bz, Lp, L, Lp, -1, H, ns, hs), "bwd: reverse a per sub-head");
+    if (dfinal_state)
+        SSD_TRY(ssd::launch_state_transpose(F(W_DSFT), dfinal_state, Bz * H, P, N, hs), "bwd: dS_fin^T");
+    st = run_fwd(bp.pb, V(W_CREXP), F(W_AREXP), V(W_DYR), V(W_XR), dfinal_state ? F(W_DSFT) : nullptr,
+                 V(W_DBH), nullptr, V(W_INNER), hs);
+    if (st != SSD_OK) return st;
+    SSD_TRY(ssd::launch_group_sum(dB, V(W_DBH), Bz, L, Lp, Lp - 1, -1, H, G, N, hs), "bwd: dB group sum");
+#undef SSD_TRY
     return ok();
 }
 

@@ -1,0 +1,494 @@
+// kernels_bwd.hip -- the gfx950 kernels of the SSD layer's backward pass.
+//
+// Gradients of l(Y, S_fin) through S_t = exp(a_t) S_{t-1} + x_t B_t^T,
+// y_t = S_t C_t (the recurrence the chunked algorithm computes, wiki review
+// of "Transformers are SSMs", section "Core concepts").  With the adjoint
+// state G_t = dl/dS_t (G_t = dy_t C_t^T + exp(a_{t+1}) G_{t+1}, G_{L-1}
+// also receiving dS_fin):
+//   dx_t = G_t B_t,  dB_t = G_t^T x_t,  dC_t = S_t^T dy_t  (summed over the
+//   heads of a group),  da_t = exp(a_t) <G_t, S_{t-1}>,  dS0 = exp(a_0) G_0.
+// The first three are again semiseparable products, so the host runs them
+// through the forward MFMA kernel on rearranged operands (time reversal for
+// the sums over later steps, the state's two dimensions exchanged for dB and
+// dC).  This file holds the operand rearrangements and the da kernel.
+//
+// da is formed chunk by chunk from four pieces that involve no cancellation
+// between large sums (the identity da_t = sum_{k>=t}(dy_k.y_k - x_k.dx_k) +
+// <dS_fin, S_fin> is exact but cancels catastrophically in fp32 once y and dx
+// carry bf16-level error).  For t in a chunk with local prefix sums cs,
+// total Lam, entering state S_in and R = exp(a_next) G_next, the adjoint
+// entering from the right:
+//   da_t = sum_{i>=t>j} exp(cs_i - cs_j)(dy_i.x_j)(C_i.B_j)     (masked Q x Q)
+//        + sum_{i>=t} exp(cs_i) dy_i . (S_in C_i)
+//        + sum_{j<t}  exp(Lam - cs_j) x_j . (R B_j)
+//        + exp(Lam) <R, S_in>.
+#include "ssd_device.hpp"
+#include "ssd_launch.hpp"
+
+namespace ssd {
+
+typedef float f32x16_b __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_b __attribute__((ext_vector_type(4)));
+
+static int64_t grid_cap(int64_t n, int64_t per) {
+    const int64_t g = (n + per - 1) / per;
+    return g < 1 ? 1 : (g > 8192 ? 8192 : g);
+}
+
+// ---------------------------------------------------------------------------
+// Operand rearrangements.  Time maps: output step t reads source step
+// s = off + dir * t, and positions with s outside [0, Lin) are zero.
+// ---------------------------------------------------------------------------
+
+// rows of W8 16-byte pieces: out[b][t][:] = in[b][s][:]
+__global__ void k_remap_rows(uint4* __restrict__ out, const uint4* __restrict__ in, int64_t Bz,
+                             int64_t Lout, int64_t Lin, int64_t off, int64_t dir, int64_t W8)
+{
+    const int64_t total = Bz * Lout * W8;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t row = idx / W8, k = idx - row * W8;
+        const int64_t b = row / Lout, t = row - b * Lout;
+        const int64_t s = off + dir * t;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (s >= 0 && s < Lin) v = in[(b * Lin + s) * W8 + k];
+        out[idx] = v;
+    }
+}
+
+// B or C of the head's group, per head: out[b][t][h][:] = in[b][s][h / (H/G)][:]
+// (rows of N8 16-byte pieces)
+__global__ void k_bcast_heads(uint4* __restrict__ out, const uint4* __restrict__ in, int64_t Bz,
+                              int64_t Lout, int64_t Lin, int64_t off, int64_t dir, int H, int G,
+                              int64_t N8)
+{
+    const int64_t W8 = (int64_t)H * N8;
+    const int64_t total = Bz * Lout * W8;
+    const int hpg = H / G;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t row = idx / W8, r = idx - row * W8;
+        const int64_t h = r / N8, k = r - h * N8;
+        const int64_t b = row / Lout, t = row - b * Lout;
+        const int64_t s = off + dir * t;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (s >= 0 && s < Lin) v = in[((b * Lin + s) * G + h / hpg) * N8 + k];
+        out[idx] = v;
+    }
+}
+
+// log-decays per (sub)head: out[b][t][h * ns + k] = a[b][s][h]
+__global__ void k_remap_a(float* __restrict__ out, const float* __restrict__ a, int64_t Bz,
+                          int64_t Lout, int64_t Lin, int64_t off, int64_t dir, int H, int ns)
+{
+    const int64_t W = (int64_t)H * ns;
+    const int64_t total = Bz * Lout * W;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t row = idx / W, r = idx - row * W;
+        const int64_t b = row / Lout, t = row - b * Lout;
+        const int64_t s = off + dir * t;
+        out[idx] = (s >= 0 && s < Lin) ? a[(b * Lin + s) * H + r / ns] : 0.f;
+    }
+}
+
+// per-(b, h) transpose of a P x N state: out[bh][n][p] = in[bh][p][n]
+__global__ void k_state_transpose(float* __restrict__ out, const float* __restrict__ in,
+                                  int64_t BH, int P, int N)
+{
+    const int64_t PN = (int64_t)P * N, total = BH * PN;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t bh = idx / PN, r = idx - bh * PN;
+        const int n = (int)(r / P), p = (int)(r - (int64_t)n * P);
+        out[idx] = in[bh * PN + (int64_t)p * N + n];
+    }
+}
+
+// sum over each group's heads (fp32), rounded once:
+// out[b][t][g][n] = sum_{h in g} in[b][s][h][n]
+__global__ void k_group_sum(u16* __restrict__ out, const u16* __restrict__ in, int64_t Bz,
+                            int64_t Lout, int64_t Lin, int64_t off, int64_t dir, int H, int G,
+                            int N)
+{
+    const int64_t W = (int64_t)G * N;
+    const int64_t total = Bz * Lout * W;
+    const int hpg = H / G;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t row = idx / W, r = idx - row * W;
+        const int64_t g = r / N, n = r - g * N;
+        const int64_t b = row / Lout, t = row - b * Lout;
+        const int64_t s = off + dir * t;
+        float acc = 0.f;
+        if (s >= 0 && s < Lin) {
+            const u16* src = in + ((b * Lin + s) * H + g * hpg) * N + n;
+            for (int k = 0; k < hpg; ++k) acc += bf_bits_to_f32(src[(int64_t)k * N]);
+        }
+        out[idx] = f32_to_bf_bits(acc);
+    }
+}
+
+// st[b][h][:] *= exp(a[b][0][h])
+__global__ void k_scale_state_by_a0(float* __restrict__ st, const float* __restrict__ a,
+                                    int64_t Bz, int64_t L, int H, int64_t PN)
+{
+    const int64_t total = Bz * H * PN;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t bh = idx / PN;
+        const int64_t b = bh / H, h = bh - b * H;
+        st[idx] *= expf(a[b * L * H + h]);
+    }
+}
+
+hipError_t launch_remap_rows(void* out, const void* in, int64_t Bz, int64_t Lout, int64_t Lin,
+                             int64_t off, int64_t dir, int64_t row_bytes, hipStream_t st)
+{
+    const int64_t W8 = row_bytes / 16, n = Bz * Lout * W8;
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_remap_rows, dim3((unsigned)grid_cap(n, 256)), dim3(256), 0, st,
+                       (uint4*)out, (const uint4*)in, Bz, Lout, Lin, off, dir, W8);
+    return hipGetLastError();
+}
+
+hipError_t launch_bcast_heads(void* out, const void* in, int64_t Bz, int64_t Lout, int64_t Lin,
+                              int64_t off, int64_t dir, int64_t H, int64_t G, int64_t N,
+                              hipStream_t st)
+{
+    const int64_t N8 = N * 2 / 16, n = Bz * Lout * H * N8;
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_bcast_heads, dim3((unsigned)grid_cap(n, 256)), dim3(256), 0, st,
+                       (uint4*)out, (const uint4*)in, Bz, Lout, Lin, off, dir, (int)H, (int)G, N8);
+    return hipGetLastError();
+}
+
+hipError_t launch_remap_a(float* out, const float* a, int64_t Bz, int64_t Lout, int64_t Lin,
+                          int64_t off, int64_t dir, int64_t H, int64_t ns, hipStream_t st)
+{
+    const int64_t n = Bz * Lout * H * ns;
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_remap_a, dim3((unsigned)grid_cap(n, 256)), dim3(256), 0, st, out, a, Bz,
+                       Lout, Lin, off, dir, (int)H, (int)ns);
+    return hipGetLastError();
+}
+
+hipError_t launch_state_transpose(float* out, const float* in, int64_t BH, int64_t P, int64_t N,
+                                  hipStream_t st)
+{
+    const int64_t n = BH * P * N;
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_state_transpose, dim3((unsigned)grid_cap(n, 256)), dim3(256), 0, st, out,
+                       in, BH, (int)P, (int)N);
+    return hipGetLastError();
+}
+
+hipError_t launch_group_sum(void* out, const void* in, int64_t Bz, int64_t Lout, int64_t Lin,
+                            int64_t off, int64_t dir, int64_t H, int64_t G, int64_t N,
+                            hipStream_t st)
+{
+    const int64_t n = Bz * Lout * G * N;
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_group_sum, dim3((unsigned)grid_cap(n, 256)), dim3(256), 0, st, (u16*)out,
+                       (const u16*)in, Bz, Lout, Lin, off, dir, (int)H, (int)G, (int)N);
+    return hipGetLastError();
+}
+
+hipError_t launch_scale_state_by_a0(float* state, const float* a, int64_t Bz, int64_t L,
+                                    int64_t H, int64_t PN, hipStream_t st)
+{
+    const int64_t n = Bz * H * PN;
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_scale_state_by_a0, dim3((unsigned)grid_cap(n, 256)), dim3(256), 0, st,
+                       state, a, Bz, L, (int)H, PN);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// da.  One workgroup (4 wavefronts) per (chunk, head, batch).  The masked
+// Q x Q term is taken in 32 x 32 tiles (I, J), J <= I, of
+//   M_ij = exp(cs_i - cs_j) (dy_i . x_j)(C_i . B_j)   (i > j; 0 otherwise)
+// whose two dot-product matrices come from MFMA on the bf16 inputs
+// themselves (exact products, fp32 sums).  For t in tile T the wanted sum
+// over {i >= t, j < t} splits into: the diagonal tile's own part; the row
+// sums of M left of tile T (rows i >= t of tile T); the column sums of M
+// below tile T (columns j < t of tile T); and the tiles strictly below and
+// left of the diagonal tile (a constant per T).  Wave w owns row tiles w and
+// 7 - w (balanced work for 8 tiles).
+//
+// MFMA 32x32x16 operand/accumulator layout (lane l, l32 = l % 32, g2 = l / 32):
+// operand fragments hold row l32, k = 8 g2 .. 8 g2 + 7 of a row-major
+// (row, k) tile; accumulator register r holds row 8(r/4) + 4 g2 + r%4 of the
+// first operand and column l32 of the second.
+// ---------------------------------------------------------------------------
+constexpr int kDaThreads = 256;
+constexpr int kDaMaxQ = 256;
+
+__device__ __forceinline__ f32x16_b mfma32b(const bf16x8& a, const bf16x8& b, const f32x16_b& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16_b zero16b() {
+    f32x16_b z;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) z[r] = 0.f;
+    return z;
+}
+__device__ __forceinline__ uint32_t pack2b(float lo, float hi) {
+    return (uint32_t)f32_to_bf_bits(lo) | ((uint32_t)f32_to_bf_bits(hi) << 16);
+}
+// LDS writes and reads of this wavefront's other lanes complete and ordered
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ int acc_row(int r, int g2) { return 8 * (r >> 2) + 4 * g2 + (r & 3); }
+
+// per-row sum (over the 32 columns) of an accumulator tile via wave scratch
+// [32][33]; the sum of row `lane` is returned in lanes 0..31
+__device__ __forceinline__ float tile_rowsum(const f32x16_b& v, float* scr, int lane) {
+    const int l32 = lane & 31, g2 = lane >> 5;
+    wave_lds_sync();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) scr[acc_row(r, g2) * 33 + l32] = v[r];
+    wave_lds_sync();
+    float s = 0.f;
+    if (lane < 32)
+        for (int j = 0; j < 32; ++j) s += scr[lane * 33 + j];
+    wave_lds_sync();
+    return s;
+}
+
+// sum over the workgroup (all threads call; two barriers)
+__device__ __forceinline__ float block_sum(float v, float* sred) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) sred[wave] = v;
+    __syncthreads();
+    float t = 0.f;
+    for (int w = 0; w < kDaThreads / 64; ++w) t += sred[w];
+    __syncthreads();
+    return t;
+}
+
+template <int P, int N>
+__global__ __launch_bounds__(kDaThreads) void k_bwd_da(
+    const u16* __restrict__ X, const u16* __restrict__ dY, const float* __restrict__ a,
+    const u16* __restrict__ Bm, const u16* __restrict__ Cm, const float* __restrict__ Sin,
+    const float* __restrict__ Srev, float* __restrict__ da, int64_t L, int H, int G, int Q,
+    int64_t nc)
+{
+    constexpr int XS = P + 8, BS = N + 8;   // padded LDS rows (elements): 16-byte row reads spread over banks
+    constexpr int PN = P * N;
+    __shared__ __attribute__((aligned(16))) u16 sX[kDaMaxQ * XS];
+    __shared__ __attribute__((aligned(16))) u16 sB[kDaMaxQ * BS];
+    __shared__ float sCs[kDaMaxQ], sRS[kDaMaxQ], sDg[kDaMaxQ], sT2[kDaMaxQ], sT3[kDaMaxQ];
+    __shared__ float sCS[kDaThreads / 64][kDaMaxQ];
+    __shared__ float sF[8][8];
+    __shared__ float sScr[kDaThreads / 64][32 * 33];
+    __shared__ float sRed[8];
+
+    const int64_t c = blockIdx.x;
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int g = h / (H / G);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, g2 = lane >> 5;
+    const int64_t t0 = c * Q;
+    const int Lc = (int)((L - t0 < Q) ? (L - t0) : Q);
+    const int nI = Q / 32;
+
+    // ---- segment sums of the chunk (zero past a ragged end) ----
+    const float av = tid < Lc ? a[((int64_t)b * L + t0 + tid) * H + h] : 0.f;
+    const float cs = block_inclusive_scan(av, sRed, (Q + 63) / 64);
+    if (tid < Q) {
+        sCs[tid] = cs;
+        sRS[tid] = 0.f; sDg[tid] = 0.f; sT2[tid] = 0.f; sT3[tid] = 0.f;
+    }
+    for (int k = tid; k < (kDaThreads / 64) * kDaMaxQ; k += kDaThreads) (&sCS[0][0])[k] = 0.f;
+    if (tid < 64) (&sF[0][0])[tid] = 0.f;
+
+    // ---- X and B rows of the chunk into LDS (rows past the end are zero) ----
+    for (int k = tid; k < Q * (P / 8); k += kDaThreads) {
+        const int i = k / (P / 8), q = k - i * (P / 8);
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (i < Lc) v = *reinterpret_cast<const uint4*>(X + (((int64_t)b * L + t0 + i) * H + h) * P + 8 * q);
+        *reinterpret_cast<uint4*>(sX + i * XS + 8 * q) = v;
+    }
+    for (int k = tid; k < Q * (N / 8); k += kDaThreads) {
+        const int i = k / (N / 8), q = k - i * (N / 8);
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (i < Lc) v = *reinterpret_cast<const uint4*>(Bm + (((int64_t)b * L + t0 + i) * G + g) * N + 8 * q);
+        *reinterpret_cast<uint4*>(sB + i * BS + 8 * q) = v;
+    }
+
+    // ---- entering state, and the adjoint entering from the right:
+    // R = exp(a at the next chunk's first step) G there; dS_fin for the last chunk ----
+    const float* Sc = Sin + (((int64_t)b * nc + c) * H + h) * PN;
+    const float* Rc = Srev + (((int64_t)b * nc + (nc - 1 - c)) * H + h) * PN;
+    const float fR = c < nc - 1 ? expf(a[((int64_t)b * L + (c + 1) * Q) * H + h]) : 1.f;
+    float dot = 0.f;
+    for (int k = tid; k < PN; k += kDaThreads) dot += Sc[k] * Rc[k];
+    dot = block_sum(dot, sRed);   // (its barriers also publish the LDS fills above)
+    const float Lam = sCs[Lc - 1];
+    const float t4 = fR * expf(Lam) * dot;
+
+    float* scr = &sScr[wave][0];
+    auto xfrag = [&](int J, int ks) {   // rows j of X (k = p)
+        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4_b*>(sX + (32 * J + l32) * XS + 16 * ks + 8 * g2));
+    };
+    auto bfrag = [&](int J, int ks) {   // rows j of B (k = n)
+        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4_b*>(sB + (32 * J + l32) * BS + 16 * ks + 8 * g2));
+    };
+    // rows p of a fp32 state (k = n), rounded to bf16
+    auto sfrag = [&](const float* S, int pt, int ks) {
+        const float* q = S + (int64_t)(32 * pt + l32) * N + 16 * ks + 8 * g2;
+        const float4 v0 = *reinterpret_cast<const float4*>(q);
+        const float4 v1 = *reinterpret_cast<const float4*>(q + 4);
+        return __builtin_bit_cast(bf16x8, u32x4_b{pack2b(v0.x, v0.y), pack2b(v0.z, v0.w),
+                                                  pack2b(v1.x, v1.y), pack2b(v1.z, v1.w)});
+    };
+
+    for (int pass = 0; pass < 2; ++pass) {
+        const int I = pass == 0 ? wave : 7 - wave;
+        if (I >= nI || (pass == 1 && I == wave) || 32 * I >= Lc) continue;
+        // row-side operands from HBM: dy and C rows i = 32I + l32 (zero past the end)
+        const int irow = 32 * I + l32;
+        const bool iok = irow < Lc;
+        const int64_t tr = (int64_t)b * L + t0 + irow;
+        bf16x8 dyf[P / 16], cf[N / 16];
+#pragma unroll
+        for (int ks = 0; ks < P / 16; ++ks) {
+            u32x4_b v = {0u, 0u, 0u, 0u};
+            if (iok) v = *reinterpret_cast<const u32x4_b*>(dY + (tr * H + h) * P + 16 * ks + 8 * g2);
+            dyf[ks] = __builtin_bit_cast(bf16x8, v);
+        }
+#pragma unroll
+        for (int ks = 0; ks < N / 16; ++ks) {
+            u32x4_b v = {0u, 0u, 0u, 0u};
+            if (iok) v = *reinterpret_cast<const u32x4_b*>(Cm + (tr * G + g) * N + 16 * ks + 8 * g2);
+            cf[ks] = __builtin_bit_cast(bf16x8, v);
+        }
+        float csI[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) csI[r] = sCs[32 * I + acc_row(r, g2)];
+
+        f32x16_b Mrow = zero16b();
+        for (int J = 0; J <= I; ++J) {
+            f32x16_b DX = zero16b(), CB = zero16b();
+#pragma unroll
+            for (int ks = 0; ks < P / 16; ++ks) DX = mfma32b(dyf[ks], xfrag(J, ks), DX);
+#pragma unroll
+            for (int ks = 0; ks < N / 16; ++ks) CB = mfma32b(cf[ks], bfrag(J, ks), CB);
+            const float csj = sCs[32 * J + l32];
+            f32x16_b M;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const bool keep = J < I || acc_row(r, g2) > l32;
+                M[r] = keep ? fast_exp2((csI[r] - csj) * kLog2e) * DX[r] * CB[r] : 0.f;
+            }
+            if (J < I) {
+                Mrow += M;
+                float cv = 0.f;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) cv += M[r];
+                cv += __shfl_xor(cv, 32, 64);             // column 32J + l32 over the tile's 32 rows
+                if (lane < 32) sCS[wave][32 * J + l32] += cv;
+                float tv = lane < 32 ? cv : 0.f;
+#pragma unroll
+                for (int d = 16; d >= 1; d >>= 1) tv += __shfl_xor(tv, d, 64);
+                if (lane == 0) sF[I][J] = tv;
+            } else {
+                // diagonal tile: sum over {i >= t > j} inside the tile, t = lane
+                wave_lds_sync();
+#pragma unroll
+                for (int r = 0; r < 16; ++r) scr[acc_row(r, g2) * 33 + l32] = M[r];
+                wave_lds_sync();
+                if (lane < 32) {
+                    float s = 0.f;
+                    for (int i = lane; i < 32; ++i)
+                        for (int j = 0; j < lane; ++j) s += scr[i * 33 + j];
+                    sDg[32 * I + lane] = s;
+                }
+                wave_lds_sync();
+            }
+        }
+        // row sums of M left of this tile
+        {
+            const float s = tile_rowsum(Mrow, scr, lane);
+            if (lane < 32) sRS[32 * I + lane] = s;
+        }
+        // state part of the output, dotted with dy: exp(cs_i) dy_i . (S_in C_i)
+        {
+            f32x16_b acc = zero16b();
+#pragma unroll
+            for (int pt = 0; pt < P / 32; ++pt) {
+                f32x16_b U = zero16b();
+#pragma unroll
+                for (int ks = 0; ks < N / 16; ++ks) U = mfma32b(cf[ks], sfrag(Sc, pt, ks), U);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int i = 32 * I + acc_row(r, g2);
+                    const float dyv = i < Lc ? bf_bits_to_f32(dY[(((int64_t)b * L + t0 + i) * H + h) * P + 32 * pt + l32]) : 0.f;
+                    acc[r] += U[r] * dyv;
+                }
+            }
+            const float s = tile_rowsum(acc, scr, lane);
+            if (lane < 32) sT2[32 * I + lane] = expf(sCs[32 * I + lane]) * s;
+        }
+        // adjoint from the right dotted with x: exp(Lam - cs_j) x_j . (R B_j), j in this tile
+        {
+            f32x16_b acc = zero16b();
+#pragma unroll
+            for (int pt = 0; pt < P / 32; ++pt) {
+                f32x16_b V = zero16b();
+#pragma unroll
+                for (int ks = 0; ks < N / 16; ++ks) V = mfma32b(bfrag(I, ks), sfrag(Rc, pt, ks), V);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int j = 32 * I + acc_row(r, g2);
+                    acc[r] += V[r] * bf_bits_to_f32(sX[j * XS + 32 * pt + l32]);
+                }
+            }
+            const float s = tile_rowsum(acc, scr, lane);
+            if (lane < 32) sT3[32 * I + lane] = fR * expf(Lam - sCs[32 * I + lane]) * s;
+        }
+    }
+    __syncthreads();
+
+    // ---- assemble da_t ----
+    if (tid < Lc) {
+        const int t = tid, T = t >> 5;
+        float d = sDg[t];
+        for (int i = t; i < 32 * T + 32; ++i) d += sRS[i];
+        for (int j = 32 * T; j < t; ++j)
+            for (int w = 0; w < kDaThreads / 64; ++w) d += sCS[w][j];
+        for (int I = T + 1; I < nI; ++I)
+            for (int J = 0; J < T; ++J) d += sF[I][J];
+        float s2 = 0.f, s3 = 0.f;
+        for (int i = t; i < Q; ++i) s2 += sT2[i];
+        for (int j = 0; j < t; ++j) s3 += sT3[j];
+        da[((int64_t)b * L + t0 + t) * H + h] = d + s2 + s3 + t4;
+    }
+}
+
+bool bwd_da_supported(int64_t Q, int64_t P, int64_t N) {
+    return (Q == 64 || Q == 128 || Q == 256) && (P == 32 || P == 64) && (N == 64 || N == 128);
+}
+
+hipError_t launch_bwd_da(const FwdShape& s, const void* X, const void* dY, const float* a,
+                         const void* B, const void* C, const float* Sin, const float* Srev,
+                         float* da, hipStream_t st)
+{
+    if (s.Bz == 0 || s.L == 0) return hipSuccess;
+    const dim3 grid((unsigned)s.nc, (unsigned)s.H, (unsigned)s.Bz);
+#define SSD_LAUNCH_DA(PP, NN)                                                                    \
+    hipLaunchKernelGGL((k_bwd_da<PP, NN>), grid, dim3(kDaThreads), 0, st, (const u16*)X,          \
+                       (const u16*)dY, a, (const u16*)B, (const u16*)C, Sin, Srev, da, s.L,      \
+                       (int)s.H, (int)s.G, (int)s.Q, s.nc);
+    if (s.P == 64 && s.N == 128) SSD_LAUNCH_DA(64, 128)
+    else if (s.P == 64 && s.N == 64) SSD_LAUNCH_DA(64, 64)
+    else if (s.P == 32 && s.N == 128) SSD_LAUNCH_DA(32, 128)
+    else if (s.P == 32 && s.N == 64) SSD_LAUNCH_DA(32, 64)
+    else return hipErrorInvalidValue;
+#undef SSD_LAUNCH_DA
+    return hipGetLastError();
+}
+
+}  // namespace ssd

@@ -65,6 +65,37 @@ hipError_t launch_step(int64_t Bz, int64_t H, int64_t P, int64_t N, int64_t G, b
                        float* state, const void* x, const float* a, const void* B,
                        const void* C, void* y, hipStream_t st);
 
+// ---- backward: operand rearrangements and da ------------------------------------
+// Time maps: output step t of Lout reads source step s = off + dir * t of Lin;
+// steps with s outside [0, Lin) are zero.
+// rows of row_bytes (a multiple of 16): out[b][t][:] = in[b][s][:]
+hipError_t launch_remap_rows(void* out, const void* in, int64_t Bz, int64_t Lout, int64_t Lin,
+                             int64_t off, int64_t dir, int64_t row_bytes, hipStream_t st);
+// bf16 B or C per head: out[b][t][h][:] = in[b][s][h / (H/G)][:] (N a multiple of 8)
+hipError_t launch_bcast_heads(void* out, const void* in, int64_t Bz, int64_t Lout, int64_t Lin,
+                              int64_t off, int64_t dir, int64_t H, int64_t G, int64_t N,
+                              hipStream_t st);
+// out[b][t][h * ns + k] = a[b][s][h]
+hipError_t launch_remap_a(float* out, const float* a, int64_t Bz, int64_t Lout, int64_t Lin,
+                          int64_t off, int64_t dir, int64_t H, int64_t ns, hipStream_t st);
+// out[bh][n][p] = in[bh][p][n]
+hipError_t launch_state_transpose(float* out, const float* in, int64_t BH, int64_t P, int64_t N,
+                                  hipStream_t st);
+// bf16 out[b][t][g][n] = sum over the group's heads of bf16 in[b][s][h][n] (fp32 sum)
+hipError_t launch_group_sum(void* out, const void* in, int64_t Bz, int64_t Lout, int64_t Lin,
+                            int64_t off, int64_t dir, int64_t H, int64_t G, int64_t N,
+                            hipStream_t st);
+// state[b][h][:] *= exp(a[b][0][h])
+hipError_t launch_scale_state_by_a0(float* state, const float* a, int64_t Bz, int64_t L,
+                                    int64_t H, int64_t PN, hipStream_t st);
+// da from the chunk-entering states Sin [Bz][nc][H][P][N] of the forward and
+// the entering states Srev [Bz][nc][H][P][N] of the time-reversed adjoint
+// problem (slot k: the adjoint at the first step of forward chunk nc - k).
+bool bwd_da_supported(int64_t Q, int64_t P, int64_t N);
+hipError_t launch_bwd_da(const FwdShape& s, const void* X, const void* dY, const float* a,
+                         const void* B, const void* C, const float* Sin, const float* Srev,
+                         float* da, hipStream_t st);
+
 // zero-fill (used for empty sequences: final state = 0)
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t st);

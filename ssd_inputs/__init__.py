@@ -148,6 +148,17 @@ def make_fwd(shape: FwdShape, seed: int = 0, with_initial_state: bool = False):
     return out
 
 
+def make_upstream_grads(shape: FwdShape, seed: int = 0):
+    """Upstream gradients for a backward test: dY ~ N(0, 1) in the shape's
+    dtype (like Y) and dS_fin ~ N(0, 0.1^2) float32 [Bz,H,P,N], drawn in that
+    order from their own stream (seed offset so they differ from the inputs)."""
+    rng = np.random.default_rng(seed + 0x5EED)
+    Bz, L, H, P = shape.batch, shape.seqlen, shape.nheads, shape.headdim
+    dY = _store(rng.standard_normal((Bz, L, H, P), dtype=np.float32), shape.dtype)
+    dSf = (0.1 * rng.standard_normal((Bz, H, P, shape.dstate), dtype=np.float32)).astype(np.float32)
+    return {"dY": dY, "dS_fin": dSf}
+
+
 def make_decode(shape: StepShape, seed: int = 0, steps: Optional[int] = None):
     """Draw a decode run: state cache [Bz,H,P,N] f32 and per-step inputs
     x [T,Bz,H,P], a [T,Bz,H], B/C [T,Bz,G,N]."""

@@ -135,3 +135,39 @@ def test_stage_validation(lib):
     assert lib.ssd_chunk_cumsum(ctypes.byref(desc(chunk=512)), FAKE, FAKE2, FAKE2, None) == _lib.SSD_ERR_UNSUPPORTED
     assert lib.ssd_chunk_cumsum(ctypes.byref(desc()), None, FAKE2, FAKE2, None) == _lib.SSD_ERR_NULL
     assert lib.ssd_state_passing(ctypes.byref(desc()), FAKE, FAKE, None, None, None, None) == _lib.SSD_ERR_NULL
+
+
+def bwd(lib, d, X=FAKE, a=FAKE, B=FAKE, C=FAKE, S0=None, dY=FAKE, dSf=None, dX=FAKE2, da=None,
+        dB=None, dC=None, dS0=None, ws=None, wsz=0):
+    da = da if da is not None else ctypes.c_void_p((1 << 30) + (1 << 26))
+    dB = dB if dB is not None else ctypes.c_void_p((1 << 30) + (2 << 26))
+    dC = dC if dC is not None else ctypes.c_void_p((1 << 30) + (3 << 26))
+    return lib.ssd_chunk_scan_bwd(ctypes.byref(d), X, a, B, C, S0, dY, dSf, dX, da, dB, dC, dS0,
+                                  ws, wsz, None)
+
+
+def test_bwd_validation(lib):
+    n = ctypes.c_size_t()
+    d = desc()
+    assert lib.ssd_bwd_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == 0
+    # per-chunk forward and adjoint states at least
+    assert n.value >= 2 * 2 * 2 * 4 * 64 * 128 * 4
+    # fp32, VALU-only, uncompiled shapes and chunks are rejected on the host
+    for kw in (dict(dtype=_lib.SSD_F32), dict(algo=_lib.SSD_ALGO_VALU), dict(headdim=48),
+               dict(chunk=32), dict(dstate=32)):
+        assert lib.ssd_bwd_workspace_bytes(ctypes.byref(desc(**kw)), ctypes.byref(n)) == _lib.SSD_ERR_UNSUPPORTED
+        assert bwd(lib, desc(**kw)) == _lib.SSD_ERR_UNSUPPORTED
+    assert bwd(lib, desc(nheads=6, ngroups=4)) == _lib.SSD_ERR_SHAPE
+    assert bwd(lib, d, dY=None) == _lib.SSD_ERR_NULL
+    assert bwd(lib, d, dX=ctypes.c_void_p((1 << 30) + 8)) == _lib.SSD_ERR_ALIGN
+    # a workspace is required, and outputs may not overlap inputs, each other or it
+    assert bwd(lib, d) == _lib.SSD_ERR_WORKSPACE
+    ws = ctypes.c_void_p(1 << 36)
+    assert bwd(lib, d, ws=ws, wsz=n.value - 1) == _lib.SSD_ERR_WORKSPACE
+    lib.ssd_bwd_workspace_bytes(ctypes.byref(d), ctypes.byref(n))
+    assert bwd(lib, d, dX=FAKE, ws=ws, wsz=n.value) == _lib.SSD_ERR_ALIAS
+    assert bwd(lib, d, dB=FAKE2, ws=ws, wsz=n.value) == _lib.SSD_ERR_ALIAS
+    assert bwd(lib, d, dC=ws, ws=ws, wsz=n.value) == _lib.SSD_ERR_ALIAS
+    # an empty batch is a no-op that needs nothing
+    assert lib.ssd_bwd_workspace_bytes(ctypes.byref(desc(batch=0)), ctypes.byref(n)) == 0 and n.value == 0
+    assert bwd(lib, desc(batch=0), X=None, dY=None) == 0

@@ -1,0 +1,99 @@
+"""GPU parity of the backward against the fp64 adjoint of the recurrence.
+
+Every case runs ssd_chunk_scan_bwd through the C ABI and compares dX, da, dB,
+dC and the initial-state gradient with oracle.bwd on the same seeded inputs
+and upstream gradients, in the slice-normwise relative error (2e-2 for bf16
+inputs with fp32 accumulation; the outputs dX, dB, dC are bf16)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ssd_chunked_scan_chunk_amd as ssd
+import ssd_inputs as si
+from gpu_util import dev_tensor, host_f64, log, upload_fwd, widen_fwd
+from parity import TOL, slice_rel_err, state_err, y_err
+
+pytestmark = pytest.mark.gpu
+
+
+def bwd_case(shape, seed=0, with_s0=True, with_dsf=True, want_ds0=True, tag=""):
+    log("bwd case %s %s s0=%s dsf=%s" % (tag, shape, with_s0, with_dsf))
+    d = si.make_fwd(shape, seed=seed, with_initial_state=with_s0)
+    u = si.make_upstream_grads(shape, seed=seed)
+    g = upload_fwd(d)
+    dY = dev_tensor(u["dY"], shape.dtype)
+    dSf = dev_tensor(u["dS_fin"], si.F32) if with_dsf else None
+    out = ssd.chunk_scan_bwd(g["X"], g["a"], g["B"], g["C"], dY, shape.chunk,
+                             initial_state=g.get("S0"), dfinal_state=dSf,
+                             return_dinitial_state=want_ds0)
+    torch.cuda.synchronize()
+    w = widen_fwd(d)
+    ref = oracle.bwd(w["X"], w["a"], w["B"], w["C"], si.widen(u["dY"], shape.dtype),
+                     S0=w.get("S0"), dS_fin=u["dS_fin"].astype(np.float64) if with_dsf else None)
+    errs = {"dX": y_err(host_f64(out["dX"]), ref["dX"]),
+            "da": slice_rel_err(host_f64(out["da"]), ref["da"], (0, 2)),
+            "dB": slice_rel_err(host_f64(out["dB"]), ref["dB"], (0, 2)),
+            "dC": slice_rel_err(host_f64(out["dC"]), ref["dC"], (0, 2))}
+    if want_ds0:
+        errs["dS0"] = state_err(host_f64(out["dinitial_state"]), ref["dS0"])
+    log("   " + " ".join("%s=%.3e" % kv for kv in errs.items()))
+    tol = TOL[shape.dtype]
+    assert all(v <= tol for v in errs.values()), errs
+    return out
+
+
+@pytest.mark.parametrize("Q,P,N,H,G", [(256, 64, 128, 4, 1), (128, 64, 64, 4, 2), (64, 64, 128, 6, 3),
+                                       (128, 32, 64, 3, 1), (64, 32, 128, 2, 2)])
+def test_bwd_shapes_ragged(Q, P, N, H, G):
+    # several chunks plus a ragged tail, grouped B/C, initial state and dS_fin
+    bwd_case(si.FwdShape(2, 3 * Q + 37, H, P, N, G, Q, si.BF16), seed=Q + P + N + G, tag="shapes")
+
+
+def test_bwd_without_states():
+    # no initial state and no final-state gradient; L a whole number of chunks
+    bwd_case(si.FwdShape(2, 512, 4, 64, 128, 1, 128, si.BF16), seed=5, with_s0=False,
+             with_dsf=False, tag="no-states")
+
+
+def test_bwd_single_short_chunk():
+    bwd_case(si.FwdShape(3, 45, 2, 64, 64, 1, 256, si.BF16), seed=6, tag="short")
+
+
+def test_bwd_weak_decay_long():
+    # the 130M value recipe (slow decays: the states carry far) over 8 chunks
+    bwd_case(si.FwdShape(1, 2048, 4, 64, 128, 1, 256, si.BF16, dt_recipe="mamba2_dt"), seed=7,
+             tag="weak-decay")
+
+
+def test_bwd_empty_sequence():
+    sh = si.FwdShape(2, 0, 4, 64, 128, 1, 256, si.BF16)
+    X = torch.empty((2, 0, 4, 64), dtype=torch.bfloat16, device="cuda")
+    B = torch.empty((2, 0, 1, 128), dtype=torch.bfloat16, device="cuda")
+    a = torch.empty((2, 0, 4), dtype=torch.float32, device="cuda")
+    dSf = torch.randn((2, 4, 64, 128), device="cuda")
+    out = ssd.chunk_scan_bwd(X, a, B, B.clone(), X.clone(), sh.chunk, dfinal_state=dSf,
+                             return_dinitial_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out["dinitial_state"], dSf)
+
+
+def test_bwd_deterministic():
+    sh = si.FwdShape(2, 600, 4, 64, 128, 1, 256, si.BF16)
+    d = si.make_fwd(sh, seed=8, with_initial_state=True)
+    u = si.make_upstream_grads(sh, seed=8)
+    g = upload_fwd(d)
+    dY = dev_tensor(u["dY"], sh.dtype)
+    dSf = dev_tensor(u["dS_fin"], si.F32)
+    r1 = ssd.chunk_scan_bwd(g["X"], g["a"], g["B"], g["C"], dY, 256, g["S0"], dSf, True)
+    r2 = ssd.chunk_scan_bwd(g["X"], g["a"], g["B"], g["C"], dY, 256, g["S0"], dSf, True)
+    torch.cuda.synchronize()
+    for k in r1:
+        assert torch.equal(r1[k], r2[k]), k
+
+
+def test_bwd_m2_130m_shape():
+    # the Mamba-2 130M layer shape at batch 2 (the oracle's adjoint at full batch takes longer)
+    sh = si.FWD_CONFIGS["m2_130m"]
+    bwd_case(si.FwdShape(2, sh.seqlen, sh.nheads, sh.headdim, sh.dstate, sh.ngroups, sh.chunk,
+                         sh.dtype, dt_recipe=sh.dt_recipe), seed=9, tag="m2-130m")

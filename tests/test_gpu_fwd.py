@@ -69,6 +69,16 @@ def test_segmented_many_workgroups():
              seg_chunks=1, with_s0=True, tag="3-launch")
 
 
+@pytest.mark.parametrize("H,P,N,G,Q,seg", [(8, 64, 128, 2, 128, 2), (12, 32, 128, 3, 64, 3),
+                                             (7, 32, 64, 1, 256, 1)])
+def test_segmented_groups_and_narrow_heads(H, P, N, G, Q, seg):
+    # segmented plans with several B/C groups and with 32-wide heads (six heads
+    # per workgroup, split between the copy waves' stage-1 work), ragged tail
+    # and an initial state
+    run_case(si.FwdShape(2, 4 * Q + 37, H, P, N, G, Q, si.BF16), seed=H + G, algo=ssd.SSD_ALGO_MFMA,
+             seg_chunks=seg, with_s0=True, tag="seg-groups")
+
+
 def test_groups_and_valu_bf16():
     # G=2 groups (heads 0-1 read group 0, 2-3 group 1), on both paths
     sh = si.FwdShape(1, 300, 4, 64, 64, 2, 64, si.BF16)
