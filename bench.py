@@ -19,8 +19,8 @@ Prints ONE JSON line.  Besides the contract fields it carries:
                 against the bf16 dense peak;
   cpu_baseline  the fp64 CPU oracle on the same workload (host cores);
   secondary     the other workloads of the metric: the 2.7B-shaped layer,
-                the state-64 sweep at seqlen 32K, and the decode step's
-                HBM bandwidth.
+                the state-64 sweep at seqlen 32K, the decode step's HBM
+                bandwidth, and the backward of the 130M-shaped layer.
 """
 import argparse
 import json
@@ -189,6 +189,55 @@ def bench_decode(steps, warmup):
     return t, nbytes
 
 
+def bwd_algo_flops_per_token(sh, block=KERNEL_BLOCK):
+    """MFMA flops per token of the backward as the library evaluates it: the
+    time-reversed forward for dX (same flops as the forward), the dC and dB
+    passes (the forward with headdim and state exchanged, the state split into
+    64-wide sub-heads), the per-chunk states of the forward and of the reversed
+    problem, and the da kernel (per chunk Q: the lower triangle of 32x32 tiles
+    of dY X^T and C B^T per head, plus C S_in^T and B R^T)."""
+    import dataclasses
+    P, N, H, Q = sh.headdim, sh.dstate, sh.nheads, sh.chunk
+    ns = N // 64
+    swapped = dataclasses.replace(sh, nheads=H * ns, headdim=N // ns, dstate=P, ngroups=H)
+    nI = Q // 32
+    da = H * ((nI * (nI + 1) // 2) * 32 * 32 * 2 * (P + N) + 2 * 2 * Q * P * N) / Q
+    states = 2 * 2 * N * P * H   # chunk states of the forward and of the reversed problem
+    return fwd_algo_flops_per_token(sh, block) + 2 * fwd_algo_flops_per_token(swapped, block) + da + states
+
+
+def bench_backward(sh, steps, warmup, nbatch, seed0=100):
+    """Time `steps` backward calls (all of dX, da, dB, dC, dS0) cycling over
+    `nbatch` seeded batches with their upstream gradients."""
+    import torch
+    import ssd_chunked_scan_chunk_amd as ssd
+    import ssd_inputs as si
+    batches = []
+    for i in range(nbatch):
+        g = upload(si.make_fwd(sh, seed=seed0 + i, with_initial_state=True))
+        d = si.make_fwd(sh, seed=seed0 + i, with_initial_state=True)
+        g["S0"] = torch.from_numpy(d["S0"]).cuda()
+        u = si.make_upstream_grads(sh, seed=seed0 + i)
+        g["dY"] = torch.from_numpy(np.ascontiguousarray(u["dY"], dtype=np.uint16)).view(torch.bfloat16).cuda()
+        g["dSf"] = torch.from_numpy(u["dS_fin"]).cuda()
+        batches.append(g)
+    g0 = batches[0]
+    ws = torch.empty(max(1, ssd.bwd_workspace_bytes(g0["X"], g0["B"], sh.chunk)), dtype=torch.uint8,
+                     device="cuda")
+
+    def step(i):
+        g = batches[i % nbatch]
+        ssd.chunk_scan_bwd(g["X"], g["a"], g["B"], g["C"], g["dY"], sh.chunk, initial_state=g["S0"],
+                           dfinal_state=g["dSf"], return_dinitial_state=True, workspace=ws)
+
+    for i in range(warmup):
+        step(i)
+    t = time_events(step, steps) / steps
+    del batches, ws
+    torch.cuda.empty_cache()
+    return t
+
+
 def cpu_baseline(sh):
     """The fp64 oracle (never tuned) on the same workload, on the host cores."""
     import oracle
@@ -218,6 +267,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--bwd-only", action="store_true",
+                    help="only time the backward of the 130M-shaped layer (for profiling)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 512 MiB (counter calibration)")
     args = ap.parse_args()
@@ -243,6 +294,12 @@ def main():
 
     sh = si.FWD_CONFIGS["m2_130m"]
     tokens = sh.batch * sh.seqlen
+    if args.bwd_only:
+        tb = bench_backward(sh, args.steps, args.warmup, 2)
+        fl = tokens * bwd_algo_flops_per_token(sh)
+        print(json.dumps({"backward_m2_130m": {"ms_per_step": tb * 1e3, "tokens_per_s": tokens / tb,
+                                               "mfma_frac": fl / tb / 1e12 / BF16_PEAK_TFLOPS}}))
+        return
     per_batch = tokens * fwd_algo_bytes_per_token(sh)
     nbatch = max(2, int(np.ceil(2 * 256e6 / per_batch)))   # > 2x the Infinity Cache
     t_step, t_kernel, plan, passes = bench_forward(sh, args.steps, args.warmup, nbatch)
@@ -292,6 +349,13 @@ def main():
         sec["decode_step"] = {"workload": "batch 256, 80 heads, headdim 64, dstate 128, fp32 state in place",
                               "us_per_step": td * 1e6, "GB_per_s": nbytes / td / 1e9,
                               "hbm_frac": nbytes / td / 1e9 / HBM_PEAK_GBS, "tokens_per_s": 256 / td}
+        tb = bench_backward(sh, max(10, args.steps // 2), 3, 2)
+        fl = tokens * bwd_algo_flops_per_token(sh)
+        sec["backward_m2_130m"] = {
+            "workload": "gradients dX, da, dB, dC, d(initial state) of the 130M-shaped layer "
+                        "for upstream dY and d(final state)",
+            "ms_per_step": tb * 1e3, "tokens_per_s": tokens / tb, "bwd_over_fwd": tb / t_step,
+            "mfma_frac": fl / tb / 1e12 / BF16_PEAK_TFLOPS, "algo_flops_per_step": fl}
         out["secondary"] = sec
 
     if not args.no_cpu:

@@ -22,6 +22,8 @@
 //        + sum_{i>=t} exp(cs_i) dy_i . (S_in C_i)
 //        + sum_{j<t}  exp(Lam - cs_j) x_j . (R B_j)
 //        + exp(Lam) <R, S_in>.
+#include <type_traits>
+
 #include "ssd_device.hpp"
 #include "ssd_launch.hpp"
 
@@ -214,12 +216,19 @@ hipError_t launch_scale_state_by_a0(float* state, const float* a, int64_t Bz, in
 // sums of M left of tile T (rows i >= t of tile T); the column sums of M
 // below tile T (columns j < t of tile T); and the tiles strictly below and
 // left of the diagonal tile (a constant per T).  Wave w owns row tiles w and
-// 7 - w (balanced work for 8 tiles).
+// 7 - w (balanced work for 8 tiles).  The state terms are formed transposed
+// (state rows p as the first operand) so that their sums over p stay inside
+// a lane.
 //
 // MFMA 32x32x16 operand/accumulator layout (lane l, l32 = l % 32, g2 = l / 32):
 // operand fragments hold row l32, k = 8 g2 .. 8 g2 + 7 of a row-major
 // (row, k) tile; accumulator register r holds row 8(r/4) + 4 g2 + r%4 of the
 // first operand and column l32 of the second.
+//
+// LDS tiles are row-major bf16 with PR 16-byte pieces per row, piece q of row
+// r stored at q ^ f(r), f(r) = (r / (16 / PR)) mod PR: the 16 rows that a
+// half-wave reads at one logical piece fall on 16 distinct 16-byte slots of
+// the 256-byte bank window.
 // ---------------------------------------------------------------------------
 constexpr int kDaThreads = 256;
 constexpr int kDaMaxQ = 256;
@@ -236,23 +245,17 @@ __device__ __forceinline__ f32x16_b zero16b() {
 __device__ __forceinline__ uint32_t pack2b(float lo, float hi) {
     return (uint32_t)f32_to_bf_bits(lo) | ((uint32_t)f32_to_bf_bits(hi) << 16);
 }
+__device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 // LDS writes and reads of this wavefront's other lanes complete and ordered
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ int acc_row(int r, int g2) { return 8 * (r >> 2) + 4 * g2 + (r & 3); }
 
-// per-row sum (over the 32 columns) of an accumulator tile via wave scratch
-// [32][33]; the sum of row `lane` is returned in lanes 0..31
-__device__ __forceinline__ float tile_rowsum(const f32x16_b& v, float* scr, int lane) {
-    const int l32 = lane & 31, g2 = lane >> 5;
-    wave_lds_sync();
-#pragma unroll
-    for (int r = 0; r < 16; ++r) scr[acc_row(r, g2) * 33 + l32] = v[r];
-    wave_lds_sync();
-    float s = 0.f;
-    if (lane < 32)
-        for (int j = 0; j < 32; ++j) s += scr[lane * 33 + j];
-    wave_lds_sync();
-    return s;
+// element offset of (row, col) in a swizzled tile with PR pieces per row
+template <int PR>
+__device__ __forceinline__ int dswz(int row, int col) {
+    const int f = (row / (16 / PR)) & (PR - 1);
+    return row * PR * 8 + ((((col >> 3) ^ f)) << 3) + (col & 7);
 }
 
 // sum over the workgroup (all threads call; two barriers)
@@ -263,6 +266,7 @@ __device__ __forceinline__ float block_sum(float v, float* sred) {
     if ((threadIdx.x & 63) == 0) sred[wave] = v;
     __syncthreads();
     float t = 0.f;
+#pragma unroll
     for (int w = 0; w < kDaThreads / 64; ++w) t += sred[w];
     __syncthreads();
     return t;
@@ -275,10 +279,12 @@ __global__ __launch_bounds__(kDaThreads) void k_bwd_da(
     const float* __restrict__ Srev, float* __restrict__ da, int64_t L, int H, int G, int Q,
     int64_t nc)
 {
-    constexpr int XS = P + 8, BS = N + 8;   // padded LDS rows (elements): 16-byte row reads spread over banks
+    constexpr int XPR = P / 8, BPR = N / 8;   // 16-byte pieces per row
     constexpr int PN = P * N;
-    __shared__ __attribute__((aligned(16))) u16 sX[kDaMaxQ * XS];
-    __shared__ __attribute__((aligned(16))) u16 sB[kDaMaxQ * BS];
+    __shared__ __attribute__((aligned(16))) u16 sX[kDaMaxQ * P];
+    __shared__ __attribute__((aligned(16))) u16 sB[kDaMaxQ * N];
+    __shared__ __attribute__((aligned(16))) u16 sS[P * N];   // entering state, bf16
+    __shared__ __attribute__((aligned(16))) u16 sR[P * N];   // adjoint from the right, bf16
     __shared__ float sCs[kDaMaxQ], sRS[kDaMaxQ], sDg[kDaMaxQ], sT2[kDaMaxQ], sT3[kDaMaxQ];
     __shared__ float sCS[kDaThreads / 64][kDaMaxQ];
     __shared__ float sF[8][8];
@@ -305,45 +311,50 @@ __global__ __launch_bounds__(kDaThreads) void k_bwd_da(
     if (tid < 64) (&sF[0][0])[tid] = 0.f;
 
     // ---- X and B rows of the chunk into LDS (rows past the end are zero) ----
-    for (int k = tid; k < Q * (P / 8); k += kDaThreads) {
-        const int i = k / (P / 8), q = k - i * (P / 8);
+    for (int k = tid; k < Q * XPR; k += kDaThreads) {
+        const int i = k / XPR, q = k - i * XPR;
         uint4 v = make_uint4(0u, 0u, 0u, 0u);
         if (i < Lc) v = *reinterpret_cast<const uint4*>(X + (((int64_t)b * L + t0 + i) * H + h) * P + 8 * q);
-        *reinterpret_cast<uint4*>(sX + i * XS + 8 * q) = v;
+        *reinterpret_cast<uint4*>(sX + dswz<XPR>(i, 8 * q)) = v;
     }
-    for (int k = tid; k < Q * (N / 8); k += kDaThreads) {
-        const int i = k / (N / 8), q = k - i * (N / 8);
+    for (int k = tid; k < Q * BPR; k += kDaThreads) {
+        const int i = k / BPR, q = k - i * BPR;
         uint4 v = make_uint4(0u, 0u, 0u, 0u);
         if (i < Lc) v = *reinterpret_cast<const uint4*>(Bm + (((int64_t)b * L + t0 + i) * G + g) * N + 8 * q);
-        *reinterpret_cast<uint4*>(sB + i * BS + 8 * q) = v;
+        *reinterpret_cast<uint4*>(sB + dswz<BPR>(i, 8 * q)) = v;
     }
 
-    // ---- entering state, and the adjoint entering from the right:
-    // R = exp(a at the next chunk's first step) G there; dS_fin for the last chunk ----
+    // ---- entering state S_in and the adjoint entering from the right,
+    // R = exp(a at the next chunk's first step) G there (dS_fin for the last
+    // chunk), rounded to bf16 for the MFMA; their fp32 inner product on the way ----
     const float* Sc = Sin + (((int64_t)b * nc + c) * H + h) * PN;
     const float* Rc = Srev + (((int64_t)b * nc + (nc - 1 - c)) * H + h) * PN;
     const float fR = c < nc - 1 ? expf(a[((int64_t)b * L + (c + 1) * Q) * H + h]) : 1.f;
     float dot = 0.f;
-    for (int k = tid; k < PN; k += kDaThreads) dot += Sc[k] * Rc[k];
+    for (int k = tid; k < PN / 8; k += kDaThreads) {
+        const int p = k / BPR, q = k - p * BPR;
+        const float4 s0 = reinterpret_cast<const float4*>(Sc)[2 * k];
+        const float4 s1 = reinterpret_cast<const float4*>(Sc)[2 * k + 1];
+        const float4 r0 = reinterpret_cast<const float4*>(Rc)[2 * k];
+        const float4 r1 = reinterpret_cast<const float4*>(Rc)[2 * k + 1];
+        dot += s0.x * r0.x + s0.y * r0.y + s0.z * r0.z + s0.w * r0.w +
+               s1.x * r1.x + s1.y * r1.y + s1.z * r1.z + s1.w * r1.w;
+        *reinterpret_cast<uint4*>(sS + dswz<BPR>(p, 8 * q)) =
+            make_uint4(pack2b(s0.x, s0.y), pack2b(s0.z, s0.w), pack2b(s1.x, s1.y), pack2b(s1.z, s1.w));
+        *reinterpret_cast<uint4*>(sR + dswz<BPR>(p, 8 * q)) =
+            make_uint4(pack2b(r0.x, r0.y), pack2b(r0.z, r0.w), pack2b(r1.x, r1.y), pack2b(r1.z, r1.w));
+    }
     dot = block_sum(dot, sRed);   // (its barriers also publish the LDS fills above)
     const float Lam = sCs[Lc - 1];
     const float t4 = fR * expf(Lam) * dot;
 
     float* scr = &sScr[wave][0];
-    auto xfrag = [&](int J, int ks) {   // rows j of X (k = p)
-        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4_b*>(sX + (32 * J + l32) * XS + 16 * ks + 8 * g2));
+    auto frag = [&](const u16* tile, auto pr, int row, int ks) {   // row `row`, k = 16ks + 8g2 .. +7
+        constexpr int PR = decltype(pr)::value;
+        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4_b*>(tile + dswz<PR>(row, 16 * ks + 8 * g2)));
     };
-    auto bfrag = [&](int J, int ks) {   // rows j of B (k = n)
-        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4_b*>(sB + (32 * J + l32) * BS + 16 * ks + 8 * g2));
-    };
-    // rows p of a fp32 state (k = n), rounded to bf16
-    auto sfrag = [&](const float* S, int pt, int ks) {
-        const float* q = S + (int64_t)(32 * pt + l32) * N + 16 * ks + 8 * g2;
-        const float4 v0 = *reinterpret_cast<const float4*>(q);
-        const float4 v1 = *reinterpret_cast<const float4*>(q + 4);
-        return __builtin_bit_cast(bf16x8, u32x4_b{pack2b(v0.x, v0.y), pack2b(v0.z, v0.w),
-                                                  pack2b(v1.x, v1.y), pack2b(v1.z, v1.w)});
-    };
+    using XP = std::integral_constant<int, XPR>;
+    using BP = std::integral_constant<int, BPR>;
 
     for (int pass = 0; pass < 2; ++pass) {
         const int I = pass == 0 ? wave : 7 - wave;
@@ -352,12 +363,13 @@ __global__ __launch_bounds__(kDaThreads) void k_bwd_da(
         const int irow = 32 * I + l32;
         const bool iok = irow < Lc;
         const int64_t tr = (int64_t)b * L + t0 + irow;
-        bf16x8 dyf[P / 16], cf[N / 16];
+        u32x4_b dyu[P / 16];
+        bf16x8 cf[N / 16];
 #pragma unroll
         for (int ks = 0; ks < P / 16; ++ks) {
             u32x4_b v = {0u, 0u, 0u, 0u};
             if (iok) v = *reinterpret_cast<const u32x4_b*>(dY + (tr * H + h) * P + 16 * ks + 8 * g2);
-            dyf[ks] = __builtin_bit_cast(bf16x8, v);
+            dyu[ks] = v;
         }
 #pragma unroll
         for (int ks = 0; ks < N / 16; ++ks) {
@@ -373,9 +385,10 @@ __global__ __launch_bounds__(kDaThreads) void k_bwd_da(
         for (int J = 0; J <= I; ++J) {
             f32x16_b DX = zero16b(), CB = zero16b();
 #pragma unroll
-            for (int ks = 0; ks < P / 16; ++ks) DX = mfma32b(dyf[ks], xfrag(J, ks), DX);
+            for (int ks = 0; ks < P / 16; ++ks)
+                DX = mfma32b(__builtin_bit_cast(bf16x8, dyu[ks]), frag(sX, XP{}, 32 * J + l32, ks), DX);
 #pragma unroll
-            for (int ks = 0; ks < N / 16; ++ks) CB = mfma32b(cf[ks], bfrag(J, ks), CB);
+            for (int ks = 0; ks < N / 16; ++ks) CB = mfma32b(cf[ks], frag(sB, BP{}, 32 * J + l32, ks), CB);
             const float csj = sCs[32 * J + l32];
             f32x16_b M;
 #pragma unroll
@@ -395,15 +408,27 @@ __global__ __launch_bounds__(kDaThreads) void k_bwd_da(
                 for (int d = 16; d >= 1; d >>= 1) tv += __shfl_xor(tv, d, 64);
                 if (lane == 0) sF[I][J] = tv;
             } else {
-                // diagonal tile: sum over {i >= t > j} inside the tile, t = lane
+                // diagonal tile: sum over {i >= t > j} inside the tile.  Lane i
+                // turns its row into exclusive prefix sums over j, then lane t
+                // sums column t of those over i >= t.
                 wave_lds_sync();
 #pragma unroll
                 for (int r = 0; r < 16; ++r) scr[acc_row(r, g2) * 33 + l32] = M[r];
                 wave_lds_sync();
                 if (lane < 32) {
+                    float run = 0.f;
+#pragma unroll
+                    for (int j = 0; j < 32; ++j) {
+                        const float v = scr[lane * 33 + j];
+                        scr[lane * 33 + j] = run;
+                        run += v;
+                    }
+                }
+                wave_lds_sync();
+                if (lane < 32) {
                     float s = 0.f;
-                    for (int i = lane; i < 32; ++i)
-                        for (int j = 0; j < lane; ++j) s += scr[i * 33 + j];
+#pragma unroll
+                    for (int i = 0; i < 32; ++i) s += i >= lane ? scr[i * 33 + lane] : 0.f;
                     sDg[32 * I + lane] = s;
                 }
                 wave_lds_sync();
@@ -411,61 +436,111 @@ __global__ __launch_bounds__(kDaThreads) void k_bwd_da(
         }
         // row sums of M left of this tile
         {
-            const float s = tile_rowsum(Mrow, scr, lane);
-            if (lane < 32) sRS[32 * I + lane] = s;
+            wave_lds_sync();
+#pragma unroll
+            for (int r = 0; r < 16; ++r) scr[acc_row(r, g2) * 33 + l32] = Mrow[r];
+            wave_lds_sync();
+            if (lane < 32) {
+                float s = 0.f;
+#pragma unroll
+                for (int j = 0; j < 32; ++j) s += scr[lane * 33 + j];
+                sRS[32 * I + lane] = s;
+            }
+            wave_lds_sync();
         }
-        // state part of the output, dotted with dy: exp(cs_i) dy_i . (S_in C_i)
+        // state part of the output dotted with dy: exp(cs_i) dy_i . (S_in C_i),
+        // from (S_in C^T) with rows p, column i = l32.  Register r of 16-wide
+        // p-tile q = r/4 holds p = 8q + 4g2 + r%4 (+32pt); this lane's dy row
+        // holds p = 16ks + 8g2 + 0..7, the partner lane (l ^ 32) the other half
         {
-            f32x16_b acc = zero16b();
+            float acc = 0.f;
 #pragma unroll
             for (int pt = 0; pt < P / 32; ++pt) {
                 f32x16_b U = zero16b();
 #pragma unroll
-                for (int ks = 0; ks < N / 16; ++ks) U = mfma32b(cf[ks], sfrag(Sc, pt, ks), U);
+                for (int ks = 0; ks < N / 16; ++ks) U = mfma32b(frag(sS, BP{}, 32 * pt + l32, ks), cf[ks], U);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int i = 32 * I + acc_row(r, g2);
-                    const float dyv = i < Lc ? bf_bits_to_f32(dY[(((int64_t)b * L + t0 + i) * H + h) * P + 32 * pt + l32]) : 0.f;
-                    acc[r] += U[r] * dyv;
+                for (int hq = 0; hq < 2; ++hq) {
+                    const int ks = 2 * pt + hq;
+                    const u32x4_b own = dyu[ks];
+                    const uint32_t s0 = g2 == 0 ? own[2] : own[0], s1 = g2 == 0 ? own[3] : own[1];
+                    const uint32_t r0 = (uint32_t)__shfl_xor((int)s0, 32, 64);
+                    const uint32_t r1 = (uint32_t)__shfl_xor((int)s1, 32, 64);
+#pragma unroll
+                    for (int qq = 0; qq < 2; ++qq) {
+                        const int q = 2 * hq + qq;   // 8-wide p group inside the 32-wide tile
+                        const bool mine = qq == g2;
+                        const uint32_t d0 = mine ? (g2 == 0 ? own[0] : own[2]) : r0;
+                        const uint32_t d1 = mine ? (g2 == 0 ? own[1] : own[3]) : r1;
+                        acc += U[4 * q + 0] * bf_lo(d0) + U[4 * q + 1] * bf_hi(d0) +
+                               U[4 * q + 2] * bf_lo(d1) + U[4 * q + 3] * bf_hi(d1);
+                    }
                 }
             }
-            const float s = tile_rowsum(acc, scr, lane);
-            if (lane < 32) sT2[32 * I + lane] = expf(sCs[32 * I + lane]) * s;
+            acc += __shfl_xor(acc, 32, 64);
+            if (lane < 32 && irow < Lc) sT2[irow] = expf(sCs[irow]) * acc;
         }
-        // adjoint from the right dotted with x: exp(Lam - cs_j) x_j . (R B_j), j in this tile
+        // adjoint from the right dotted with x: exp(Lam - cs_j) x_j . (R B_j),
+        // from (R B^T) with rows p, column j = l32 of this tile
         {
-            f32x16_b acc = zero16b();
+            float acc = 0.f;
+            const int jrow = irow;
 #pragma unroll
             for (int pt = 0; pt < P / 32; ++pt) {
                 f32x16_b V = zero16b();
 #pragma unroll
-                for (int ks = 0; ks < N / 16; ++ks) V = mfma32b(bfrag(I, ks), sfrag(Rc, pt, ks), V);
+                for (int ks = 0; ks < N / 16; ++ks)
+                    V = mfma32b(frag(sR, BP{}, 32 * pt + l32, ks), frag(sB, BP{}, jrow, ks), V);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int j = 32 * I + acc_row(r, g2);
-                    acc[r] += V[r] * bf_bits_to_f32(sX[j * XS + 32 * pt + l32]);
+                for (int q = 0; q < 4; ++q) {
+                    const uint2 xv = *reinterpret_cast<const uint2*>(sX + dswz<XPR>(jrow, 32 * pt + 8 * q + 4 * g2));
+                    acc += V[4 * q + 0] * bf_lo(xv.x) + V[4 * q + 1] * bf_hi(xv.x) +
+                           V[4 * q + 2] * bf_lo(xv.y) + V[4 * q + 3] * bf_hi(xv.y);
                 }
             }
-            const float s = tile_rowsum(acc, scr, lane);
-            if (lane < 32) sT3[32 * I + lane] = fR * expf(Lam - sCs[32 * I + lane]) * s;
+            acc += __shfl_xor(acc, 32, 64);
+            if (lane < 32 && jrow < Lc) sT3[jrow] = fR * expf(Lam - sCs[jrow]) * acc;
         }
     }
     __syncthreads();
 
-    // ---- assemble da_t ----
-    if (tid < Lc) {
-        const int t = tid, T = t >> 5;
-        float d = sDg[t];
-        for (int i = t; i < 32 * T + 32; ++i) d += sRS[i];
-        for (int j = 32 * T; j < t; ++j)
-            for (int w = 0; w < kDaThreads / 64; ++w) d += sCS[w][j];
-        for (int I = T + 1; I < nI; ++I)
-            for (int J = 0; J < T; ++J) d += sF[I][J];
-        float s2 = 0.f, s3 = 0.f;
-        for (int i = t; i < Q; ++i) s2 += sT2[i];
-        for (int j = 0; j < t; ++j) s3 += sT3[j];
-        da[((int64_t)b * L + t0 + t) * H + h] = d + s2 + s3 + t4;
+    // ---- assemble da_t (thread t): segmented scans inside 32-step tiles,
+    // workgroup scans over the chunk ----
+    const int t = tid, T = t >> 5;
+    const bool tin = t < Q;
+    // column sums below tile T, exclusive prefix over j < t inside the tile
+    float csv = 0.f;
+    if (tin) {
+#pragma unroll
+        for (int w = 0; w < kDaThreads / 64; ++w) csv += sCS[w][t];
     }
+    float cpre = csv;
+#pragma unroll
+    for (int d = 1; d < 32; d <<= 1) {
+        const float u = __shfl_up(cpre, d, 32);
+        if (l32 >= d) cpre += u;
+    }
+    cpre -= csv;
+    // row sums left of tile T, suffix over i >= t inside the tile
+    float rsuf = tin ? sRS[t] : 0.f;
+#pragma unroll
+    for (int d = 1; d < 32; d <<= 1) {
+        const float u = __shfl_down(rsuf, d, 32);
+        if (l32 + d < 32) rsuf += u;
+    }
+    // tiles below and left of the diagonal tile T
+    float kT = 0.f;
+    if (tin)
+        for (int I = T + 1; I < nI; ++I)
+            for (int J = 0; J < T; ++J) kT += sF[I][J];
+    // sum of the state terms over i >= t (scan of the reversed order) and of
+    // the right-adjoint terms over j < t (scan of the shifted order)
+    const float t2suf = block_inclusive_scan(tin ? sT2[Q - 1 - t] : 0.f, sRed, (Q + 63) / 64);
+    const float t3pre = block_inclusive_scan((tin && t > 0) ? sT3[t - 1] : 0.f, sRed, (Q + 63) / 64);
+    if (tin) sT2[Q - 1 - t] = t2suf;   // (every read of sT2 above precedes the scan's barriers)
+    __syncthreads();
+    if (t < Lc)
+        da[((int64_t)b * L + t0 + t) * H + h] = sDg[t] + rsuf + cpre + kT + sT2[t] + t3pre + t4;
 }
 
 bool bwd_da_supported(int64_t Q, int64_t P, int64_t N) {
