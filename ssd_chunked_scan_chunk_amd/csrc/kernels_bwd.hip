@@ -107,27 +107,40 @@ __global__ void k_state_transpose(float* __restrict__ out, const float* __restri
     }
 }
 
-// sum over each group's heads (fp32), rounded once:
+// sum over each group's heads (fp32), rounded once, 8 elements per thread:
 // out[b][t][g][n] = sum_{h in g} in[b][s][h][n]
-__global__ void k_group_sum(u16* __restrict__ out, const u16* __restrict__ in, int64_t Bz,
+__global__ void k_group_sum(uint4* __restrict__ out, const uint4* __restrict__ in, int64_t Bz,
                             int64_t Lout, int64_t Lin, int64_t off, int64_t dir, int H, int G,
-                            int N)
+                            int N8)
 {
-    const int64_t W = (int64_t)G * N;
+    const int64_t W = (int64_t)G * N8;
     const int64_t total = Bz * Lout * W;
     const int hpg = H / G;
     for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
          idx += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t row = idx / W, r = idx - row * W;
-        const int64_t g = r / N, n = r - g * N;
+        const int64_t row = idx / W;
+        const int r = (int)(idx - row * W);
+        const int gi = r / N8, k = r - gi * N8;
         const int64_t b = row / Lout, t = row - b * Lout;
         const int64_t s = off + dir * t;
-        float acc = 0.f;
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         if (s >= 0 && s < Lin) {
-            const u16* src = in + ((b * Lin + s) * H + g * hpg) * N + n;
-            for (int k = 0; k < hpg; ++k) acc += bf_bits_to_f32(src[(int64_t)k * N]);
+            const uint4* src = in + ((b * Lin + s) * H + (int64_t)gi * hpg) * N8 + k;
+            for (int j = 0; j < hpg; ++j) {
+                const uint4 v = src[(int64_t)j * N8];
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    acc[2 * e] += __uint_as_float(w[e] << 16);
+                    acc[2 * e + 1] += __uint_as_float(w[e] & 0xffff0000u);
+                }
+            }
         }
-        out[idx] = f32_to_bf_bits(acc);
+        uint32_t o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            o[e] = (uint32_t)f32_to_bf_bits(acc[2 * e]) | ((uint32_t)f32_to_bf_bits(acc[2 * e + 1]) << 16);
+        out[idx] = make_uint4(o[0], o[1], o[2], o[3]);
     }
 }
 
@@ -139,8 +152,8 @@ __global__ void k_scale_state_by_a0(float* __restrict__ st, const float* __restr
     for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
          idx += (int64_t)gridDim.x * blockDim.x) {
         const int64_t bh = idx / PN;
-        const int64_t b = bh / H, h = bh - b * H;
-        st[idx] *= expf(a[b * L * H + h]);
+        const int b = (int)(bh / H), h = (int)(bh - (int64_t)b * H);
+        st[idx] *= expf(a[(int64_t)b * L * H + h]);
     }
 }
 
@@ -189,10 +202,10 @@ hipError_t launch_group_sum(void* out, const void* in, int64_t Bz, int64_t Lout,
                             int64_t off, int64_t dir, int64_t H, int64_t G, int64_t N,
                             hipStream_t st)
 {
-    const int64_t n = Bz * Lout * G * N;
+    const int64_t n = Bz * Lout * G * (N / 8);
     if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_group_sum, dim3((unsigned)grid_cap(n, 256)), dim3(256), 0, st, (u16*)out,
-                       (const u16*)in, Bz, Lout, Lin, off, dir, (int)H, (int)G, (int)N);
+    hipLaunchKernelGGL(k_group_sum, dim3((unsigned)grid_cap(n, 256)), dim3(256), 0, st, (uint4*)out,
+                       (const uint4*)in, Bz, Lout, Lin, off, dir, (int)H, (int)G, (int)(N / 8));
     return hipGetLastError();
 }
 
