@@ -299,6 +299,10 @@ ssd_status make_bwd_plan(const ssd_fwd_desc* d, BwdPlan* bp) {
                     (long long)s.Q, (long long)s.P, (long long)s.N);
     if ((s.Bz * s.nc * s.H + 8) * 256 >= ((int64_t)1 << 32) || s.nc > 0x7fffffff)
         return fail(SSD_ERR_UNSUPPORTED, "batch*chunks*heads too large for one launch");
+    // the copy kernels launch (row blocks of up to 256 threads) x steps blocks
+    const int64_t row_items = s.H * (s.N > s.P ? s.N : s.P) / 8;
+    if (s.nc * s.Q * (((row_items + 255) / 256) * 256) >= ((int64_t)1 << 31))
+        return fail(SSD_ERR_UNSUPPORTED, "seqlen*nheads too large for the backward's copy kernels");
     bp->s = s;
     bp->sr = s;
     bp->sr.L = s.nc * s.Q;

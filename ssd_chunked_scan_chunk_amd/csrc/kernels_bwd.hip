@@ -42,56 +42,47 @@ static int64_t grid_cap(int64_t n, int64_t per) {
 // s = off + dir * t, and positions with s outside [0, Lin) are zero.
 // ---------------------------------------------------------------------------
 
+// The copies below run on a (row blocks x steps, batch) grid: block x covers
+// piece block x % nbx of output step x / nbx, blockIdx.y is the batch, so no
+// per-element division is needed.
+
 // rows of W8 16-byte pieces: out[b][t][:] = in[b][s][:]
-__global__ void k_remap_rows(uint4* __restrict__ out, const uint4* __restrict__ in, int64_t Bz,
-                             int64_t Lout, int64_t Lin, int64_t off, int64_t dir, int64_t W8)
+__global__ void k_remap_rows(uint4* __restrict__ out, const uint4* __restrict__ in, int64_t Lout,
+                             int64_t Lin, int64_t off, int64_t dir, int W8, int nbx)
 {
-    const int64_t total = Bz * Lout * W8;
-    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
-         idx += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t row = idx / W8, k = idx - row * W8;
-        const int64_t b = row / Lout, t = row - b * Lout;
-        const int64_t s = off + dir * t;
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (s >= 0 && s < Lin) v = in[(b * Lin + s) * W8 + k];
-        out[idx] = v;
-    }
+    const int64_t t = blockIdx.x / nbx, b = blockIdx.y;
+    const int k = (int)(blockIdx.x - t * nbx) * blockDim.x + threadIdx.x;
+    if (k >= W8) return;
+    const int64_t s = off + dir * t;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (s >= 0 && s < Lin) v = in[(b * Lin + s) * W8 + k];
+    out[(b * Lout + t) * W8 + k] = v;
 }
 
 // B or C of the head's group, per head: out[b][t][h][:] = in[b][s][h / (H/G)][:]
 // (rows of N8 16-byte pieces)
-__global__ void k_bcast_heads(uint4* __restrict__ out, const uint4* __restrict__ in, int64_t Bz,
-                              int64_t Lout, int64_t Lin, int64_t off, int64_t dir, int H, int G,
-                              int64_t N8)
+__global__ void k_bcast_heads(uint4* __restrict__ out, const uint4* __restrict__ in, int64_t Lout,
+                              int64_t Lin, int64_t off, int64_t dir, int H, int G, int N8, int nbx)
 {
-    const int64_t W8 = (int64_t)H * N8;
-    const int64_t total = Bz * Lout * W8;
-    const int hpg = H / G;
-    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
-         idx += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t row = idx / W8, r = idx - row * W8;
-        const int64_t h = r / N8, k = r - h * N8;
-        const int64_t b = row / Lout, t = row - b * Lout;
-        const int64_t s = off + dir * t;
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (s >= 0 && s < Lin) v = in[((b * Lin + s) * G + h / hpg) * N8 + k];
-        out[idx] = v;
-    }
+    const int64_t t = blockIdx.x / nbx, b = blockIdx.y;
+    const int k = (int)(blockIdx.x - t * nbx) * blockDim.x + threadIdx.x;
+    if (k >= H * N8) return;
+    const int h = k / N8, q = k - h * N8;
+    const int64_t s = off + dir * t;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (s >= 0 && s < Lin) v = in[((b * Lin + s) * G + h / (H / G)) * N8 + q];
+    out[(b * Lout + t) * H * N8 + k] = v;
 }
 
 // log-decays per (sub)head: out[b][t][h * ns + k] = a[b][s][h]
-__global__ void k_remap_a(float* __restrict__ out, const float* __restrict__ a, int64_t Bz,
-                          int64_t Lout, int64_t Lin, int64_t off, int64_t dir, int H, int ns)
+__global__ void k_remap_a(float* __restrict__ out, const float* __restrict__ a, int64_t Lout,
+                          int64_t Lin, int64_t off, int64_t dir, int H, int ns, int nbx)
 {
-    const int64_t W = (int64_t)H * ns;
-    const int64_t total = Bz * Lout * W;
-    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
-         idx += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t row = idx / W, r = idx - row * W;
-        const int64_t b = row / Lout, t = row - b * Lout;
-        const int64_t s = off + dir * t;
-        out[idx] = (s >= 0 && s < Lin) ? a[(b * Lin + s) * H + r / ns] : 0.f;
-    }
+    const int64_t t = blockIdx.x / nbx, b = blockIdx.y;
+    const int k = (int)(blockIdx.x - t * nbx) * blockDim.x + threadIdx.x;
+    if (k >= H * ns) return;
+    const int64_t s = off + dir * t;
+    out[(b * Lout + t) * H * ns + k] = (s >= 0 && s < Lin) ? a[(b * Lin + s) * H + k / ns] : 0.f;
 }
 
 // per-(b, h) transpose of a P x N state: out[bh][n][p] = in[bh][p][n]
@@ -109,39 +100,33 @@ __global__ void k_state_transpose(float* __restrict__ out, const float* __restri
 
 // sum over each group's heads (fp32), rounded once, 8 elements per thread:
 // out[b][t][g][n] = sum_{h in g} in[b][s][h][n]
-__global__ void k_group_sum(uint4* __restrict__ out, const uint4* __restrict__ in, int64_t Bz,
-                            int64_t Lout, int64_t Lin, int64_t off, int64_t dir, int H, int G,
-                            int N8)
+__global__ void k_group_sum(uint4* __restrict__ out, const uint4* __restrict__ in, int64_t Lout,
+                            int64_t Lin, int64_t off, int64_t dir, int H, int G, int N8, int nbx)
 {
-    const int64_t W = (int64_t)G * N8;
-    const int64_t total = Bz * Lout * W;
+    const int64_t t = blockIdx.x / nbx, b = blockIdx.y;
+    const int k = (int)(blockIdx.x - t * nbx) * blockDim.x + threadIdx.x;
+    if (k >= G * N8) return;
+    const int gi = k / N8, q = k - gi * N8;
     const int hpg = H / G;
-    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
-         idx += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t row = idx / W;
-        const int r = (int)(idx - row * W);
-        const int gi = r / N8, k = r - gi * N8;
-        const int64_t b = row / Lout, t = row - b * Lout;
-        const int64_t s = off + dir * t;
-        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (s >= 0 && s < Lin) {
-            const uint4* src = in + ((b * Lin + s) * H + (int64_t)gi * hpg) * N8 + k;
-            for (int j = 0; j < hpg; ++j) {
-                const uint4 v = src[(int64_t)j * N8];
-                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    const int64_t s = off + dir * t;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (s >= 0 && s < Lin) {
+        const uint4* src = in + ((b * Lin + s) * H + (int64_t)gi * hpg) * N8 + q;
+        for (int j = 0; j < hpg; ++j) {
+            const uint4 v = src[(int64_t)j * N8];
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    acc[2 * e] += __uint_as_float(w[e] << 16);
-                    acc[2 * e + 1] += __uint_as_float(w[e] & 0xffff0000u);
-                }
+            for (int e = 0; e < 4; ++e) {
+                acc[2 * e] += __uint_as_float(w[e] << 16);
+                acc[2 * e + 1] += __uint_as_float(w[e] & 0xffff0000u);
             }
         }
-        uint32_t o[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            o[e] = (uint32_t)f32_to_bf_bits(acc[2 * e]) | ((uint32_t)f32_to_bf_bits(acc[2 * e + 1]) << 16);
-        out[idx] = make_uint4(o[0], o[1], o[2], o[3]);
     }
+    uint32_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        o[e] = (uint32_t)f32_to_bf_bits(acc[2 * e]) | ((uint32_t)f32_to_bf_bits(acc[2 * e + 1]) << 16);
+    out[(b * Lout + t) * G * N8 + k] = make_uint4(o[0], o[1], o[2], o[3]);
 }
 
 // st[b][h][:] *= exp(a[b][0][h])
@@ -157,13 +142,23 @@ __global__ void k_scale_state_by_a0(float* __restrict__ st, const float* __restr
     }
 }
 
+// threads per block of a copy row: a multiple of 64 covering `w` items (at most 256)
+static unsigned row_threads(int64_t w) {
+    const int64_t t = ((w + 63) / 64) * 64;
+    return (unsigned)(t < 256 ? t : 256);
+}
+static int row_blocks(int64_t w) { return (int)((w + row_threads(w) - 1) / row_threads(w)); }
+static dim3 row_grid(int64_t w, int64_t Lout, int64_t Bz) {
+    return dim3((unsigned)(row_blocks(w) * Lout), (unsigned)Bz);
+}
+
 hipError_t launch_remap_rows(void* out, const void* in, int64_t Bz, int64_t Lout, int64_t Lin,
                              int64_t off, int64_t dir, int64_t row_bytes, hipStream_t st)
 {
-    const int64_t W8 = row_bytes / 16, n = Bz * Lout * W8;
-    if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_remap_rows, dim3((unsigned)grid_cap(n, 256)), dim3(256), 0, st,
-                       (uint4*)out, (const uint4*)in, Bz, Lout, Lin, off, dir, W8);
+    const int64_t W8 = row_bytes / 16;
+    if (Bz * Lout * W8 <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_remap_rows, row_grid(W8, Lout, Bz), dim3(row_threads(W8)), 0, st,
+                       (uint4*)out, (const uint4*)in, Lout, Lin, off, dir, (int)W8, row_blocks(W8));
     return hipGetLastError();
 }
 
@@ -171,20 +166,20 @@ hipError_t launch_bcast_heads(void* out, const void* in, int64_t Bz, int64_t Lou
                               int64_t off, int64_t dir, int64_t H, int64_t G, int64_t N,
                               hipStream_t st)
 {
-    const int64_t N8 = N * 2 / 16, n = Bz * Lout * H * N8;
-    if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_bcast_heads, dim3((unsigned)grid_cap(n, 256)), dim3(256), 0, st,
-                       (uint4*)out, (const uint4*)in, Bz, Lout, Lin, off, dir, (int)H, (int)G, N8);
+    const int64_t N8 = N * 2 / 16;
+    if (Bz * Lout * H * N8 <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_bcast_heads, row_grid(H * N8, Lout, Bz), dim3(row_threads(H * N8)), 0, st,
+                       (uint4*)out, (const uint4*)in, Lout, Lin, off, dir, (int)H, (int)G, (int)N8,
+                       row_blocks(H * N8));
     return hipGetLastError();
 }
 
 hipError_t launch_remap_a(float* out, const float* a, int64_t Bz, int64_t Lout, int64_t Lin,
                           int64_t off, int64_t dir, int64_t H, int64_t ns, hipStream_t st)
 {
-    const int64_t n = Bz * Lout * H * ns;
-    if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_remap_a, dim3((unsigned)grid_cap(n, 256)), dim3(256), 0, st, out, a, Bz,
-                       Lout, Lin, off, dir, (int)H, (int)ns);
+    if (Bz * Lout * H * ns <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_remap_a, row_grid(H * ns, Lout, Bz), dim3(row_threads(H * ns)), 0, st, out, a,
+                       Lout, Lin, off, dir, (int)H, (int)ns, row_blocks(H * ns));
     return hipGetLastError();
 }
 
@@ -202,10 +197,11 @@ hipError_t launch_group_sum(void* out, const void* in, int64_t Bz, int64_t Lout,
                             int64_t off, int64_t dir, int64_t H, int64_t G, int64_t N,
                             hipStream_t st)
 {
-    const int64_t n = Bz * Lout * G * (N / 8);
-    if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_group_sum, dim3((unsigned)grid_cap(n, 256)), dim3(256), 0, st, (uint4*)out,
-                       (const uint4*)in, Bz, Lout, Lin, off, dir, (int)H, (int)G, (int)(N / 8));
+    const int64_t w = G * (N / 8);
+    if (Bz * Lout * w <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_group_sum, row_grid(w, Lout, Bz), dim3(row_threads(w)), 0, st, (uint4*)out,
+                       (const uint4*)in, Lout, Lin, off, dir, (int)H, (int)G, (int)(N / 8),
+                       row_blocks(w));
     return hipGetLastError();
 }
 
@@ -264,6 +260,17 @@ __device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ int acc_row(int r, int g2) { return 8 * (r >> 2) + 4 * g2 + (r & 3); }
 
+// sum of v over lanes 0..31: inclusive sums within rows of 16 lanes (DPP
+// row_shr 1, 2, 4, 8 with zeros shifted in), then lanes 15 and 31
+__device__ __forceinline__ float sum_lanes32(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xf, 0xf, true));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xf, 0xf, true));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xf, 0xf, true));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xf, 0xf, true));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 15)) +
+           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 31));
+}
+
 // element offset of (row, col) in a swizzled tile with PR pieces per row
 template <int PR>
 __device__ __forceinline__ int dswz(int row, int col) {
@@ -286,7 +293,7 @@ __device__ __forceinline__ float block_sum(float v, float* sred) {
 }
 
 template <int P, int N>
-__global__ __launch_bounds__(kDaThreads) void k_bwd_da(
+__global__ __launch_bounds__(kDaThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_bwd_da(
     const u16* __restrict__ X, const u16* __restrict__ dY, const float* __restrict__ a,
     const u16* __restrict__ Bm, const u16* __restrict__ Cm, const float* __restrict__ Sin,
     const float* __restrict__ Srev, float* __restrict__ da, int64_t L, int H, int G, int Q,
@@ -323,19 +330,31 @@ __global__ __launch_bounds__(kDaThreads) void k_bwd_da(
     for (int k = tid; k < (kDaThreads / 64) * kDaMaxQ; k += kDaThreads) (&sCS[0][0])[k] = 0.f;
     if (tid < 64) (&sF[0][0])[tid] = 0.f;
 
-    // ---- X and B rows of the chunk into LDS (rows past the end are zero) ----
-    for (int k = tid; k < Q * XPR; k += kDaThreads) {
-        const int i = k / XPR, q = k - i * XPR;
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (i < Lc) v = *reinterpret_cast<const uint4*>(X + (((int64_t)b * L + t0 + i) * H + h) * P + 8 * q);
-        *reinterpret_cast<uint4*>(sX + dswz<XPR>(i, 8 * q)) = v;
-    }
-    for (int k = tid; k < Q * BPR; k += kDaThreads) {
-        const int i = k / BPR, q = k - i * BPR;
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (i < Lc) v = *reinterpret_cast<const uint4*>(Bm + (((int64_t)b * L + t0 + i) * G + g) * N + 8 * q);
-        *reinterpret_cast<uint4*>(sB + dswz<BPR>(i, 8 * q)) = v;
-    }
+    // ---- X and B rows of the chunk into LDS (rows past the end are zero).
+    // Each thread issues kStage loads before its first LDS store, so the
+    // staging waits on HBM once per batch rather than once per piece ----
+    constexpr int kStage = 8;
+    auto stage_rows = [&](u16* tile, const u16* src, int64_t row_stride, auto pr) {
+        constexpr int PR = decltype(pr)::value;
+        for (int k0 = tid; k0 < Q * PR; k0 += kDaThreads * kStage) {
+            uint4 v[kStage];
+#pragma unroll
+            for (int u = 0; u < kStage; ++u) {
+                const int k = k0 + u * kDaThreads;
+                const int i = k / PR, q = k - i * PR;
+                v[u] = make_uint4(0u, 0u, 0u, 0u);
+                if (k < Q * PR && i < Lc) v[u] = *reinterpret_cast<const uint4*>(src + (int64_t)i * row_stride + 8 * q);
+            }
+#pragma unroll
+            for (int u = 0; u < kStage; ++u) {
+                const int k = k0 + u * kDaThreads;
+                const int i = k / PR, q = k - i * PR;
+                if (k < Q * PR) *reinterpret_cast<uint4*>(tile + dswz<PR>(i, 8 * q)) = v[u];
+            }
+        }
+    };
+    stage_rows(sX, X + (((int64_t)b * L + t0) * H + h) * P, (int64_t)H * P, std::integral_constant<int, XPR>{});
+    stage_rows(sB, Bm + (((int64_t)b * L + t0) * G + g) * N, (int64_t)G * N, std::integral_constant<int, BPR>{});
 
     // ---- entering state S_in and the adjoint entering from the right,
     // R = exp(a at the next chunk's first step) G there (dS_fin for the last
@@ -344,18 +363,29 @@ __global__ __launch_bounds__(kDaThreads) void k_bwd_da(
     const float* Rc = Srev + (((int64_t)b * nc + (nc - 1 - c)) * H + h) * PN;
     const float fR = c < nc - 1 ? expf(a[((int64_t)b * L + (c + 1) * Q) * H + h]) : 1.f;
     float dot = 0.f;
-    for (int k = tid; k < PN / 8; k += kDaThreads) {
-        const int p = k / BPR, q = k - p * BPR;
-        const float4 s0 = reinterpret_cast<const float4*>(Sc)[2 * k];
-        const float4 s1 = reinterpret_cast<const float4*>(Sc)[2 * k + 1];
-        const float4 r0 = reinterpret_cast<const float4*>(Rc)[2 * k];
-        const float4 r1 = reinterpret_cast<const float4*>(Rc)[2 * k + 1];
-        dot += s0.x * r0.x + s0.y * r0.y + s0.z * r0.z + s0.w * r0.w +
-               s1.x * r1.x + s1.y * r1.y + s1.z * r1.z + s1.w * r1.w;
-        *reinterpret_cast<uint4*>(sS + dswz<BPR>(p, 8 * q)) =
-            make_uint4(pack2b(s0.x, s0.y), pack2b(s0.z, s0.w), pack2b(s1.x, s1.y), pack2b(s1.z, s1.w));
-        *reinterpret_cast<uint4*>(sR + dswz<BPR>(p, 8 * q)) =
-            make_uint4(pack2b(r0.x, r0.y), pack2b(r0.z, r0.w), pack2b(r1.x, r1.y), pack2b(r1.z, r1.w));
+    for (int k0 = tid; k0 < PN / 8; k0 += kDaThreads * 2) {
+        float4 sv[2][2], rv[2][2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int k = k0 + u * kDaThreads < PN / 8 ? k0 + u * kDaThreads : k0;
+            sv[u][0] = reinterpret_cast<const float4*>(Sc)[2 * k];
+            sv[u][1] = reinterpret_cast<const float4*>(Sc)[2 * k + 1];
+            rv[u][0] = reinterpret_cast<const float4*>(Rc)[2 * k];
+            rv[u][1] = reinterpret_cast<const float4*>(Rc)[2 * k + 1];
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int k = k0 + u * kDaThreads;
+            if (k >= PN / 8) break;
+            const int p = k / BPR, q = k - p * BPR;
+            const float4 s0 = sv[u][0], s1 = sv[u][1], r0 = rv[u][0], r1 = rv[u][1];
+            dot += s0.x * r0.x + s0.y * r0.y + s0.z * r0.z + s0.w * r0.w +
+                   s1.x * r1.x + s1.y * r1.y + s1.z * r1.z + s1.w * r1.w;
+            *reinterpret_cast<uint4*>(sS + dswz<BPR>(p, 8 * q)) =
+                make_uint4(pack2b(s0.x, s0.y), pack2b(s0.z, s0.w), pack2b(s1.x, s1.y), pack2b(s1.z, s1.w));
+            *reinterpret_cast<uint4*>(sR + dswz<BPR>(p, 8 * q)) =
+                make_uint4(pack2b(r0.x, r0.y), pack2b(r0.z, r0.w), pack2b(r1.x, r1.y), pack2b(r1.z, r1.w));
+        }
     }
     dot = block_sum(dot, sRed);   // (its barriers also publish the LDS fills above)
     const float Lam = sCs[Lc - 1];
@@ -396,12 +426,18 @@ __global__ __launch_bounds__(kDaThreads) void k_bwd_da(
 
         f32x16_b Mrow = zero16b();
         for (int J = 0; J <= I; ++J) {
+            // the column tile's operand fragments, all read before the first MFMA
+            bf16x8 xb[P / 16], bb[N / 16];
+#pragma unroll
+            for (int ks = 0; ks < P / 16; ++ks) xb[ks] = frag(sX, XP{}, 32 * J + l32, ks);
+#pragma unroll
+            for (int ks = 0; ks < N / 16; ++ks) bb[ks] = frag(sB, BP{}, 32 * J + l32, ks);
+            __builtin_amdgcn_sched_barrier(0);   // (keep the reads ahead of the MFMA chain)
             f32x16_b DX = zero16b(), CB = zero16b();
 #pragma unroll
-            for (int ks = 0; ks < P / 16; ++ks)
-                DX = mfma32b(__builtin_bit_cast(bf16x8, dyu[ks]), frag(sX, XP{}, 32 * J + l32, ks), DX);
+            for (int ks = 0; ks < P / 16; ++ks) DX = mfma32b(__builtin_bit_cast(bf16x8, dyu[ks]), xb[ks], DX);
 #pragma unroll
-            for (int ks = 0; ks < N / 16; ++ks) CB = mfma32b(cf[ks], frag(sB, BP{}, 32 * J + l32, ks), CB);
+            for (int ks = 0; ks < N / 16; ++ks) CB = mfma32b(cf[ks], bb[ks], CB);
             const float csj = sCs[32 * J + l32];
             f32x16_b M;
 #pragma unroll
@@ -415,10 +451,8 @@ __global__ __launch_bounds__(kDaThreads) void k_bwd_da(
 #pragma unroll
                 for (int r = 0; r < 16; ++r) cv += M[r];
                 cv += __shfl_xor(cv, 32, 64);             // column 32J + l32 over the tile's 32 rows
-                if (lane < 32) sCS[wave][32 * J + l32] += cv;
-                float tv = lane < 32 ? cv : 0.f;
-#pragma unroll
-                for (int d = 16; d >= 1; d >>= 1) tv += __shfl_xor(tv, d, 64);
+                if (lane < 32) atomicAdd(&sCS[wave][32 * J + l32], cv);   // (one writer per address)
+                const float tv = sum_lanes32(cv);
                 if (lane == 0) sF[I][J] = tv;
             } else {
                 // diagonal tile: sum over {i >= t > j} inside the tile.  Lane i
