@@ -280,7 +280,8 @@ struct BwdPlan {
     ssd::FwdShape s;   // the layer
     ssd::FwdShape sr;  // the reversed problem: seqlen padded to whole chunks
     int64_t ns;        // the dB / dC passes split the state dimension into ns head-dims of 64
-    Plan pc, pb;       // plans of the dC and dB passes
+    bool xg;           // headdim 64: dB / dC read B, C, a and the chunk states in place
+    Plan pc, pb;       // plans of the dC and dB passes (otherwise)
     size_t off[kBwdBufs + 1];
 };
 
@@ -307,6 +308,7 @@ ssd_status make_bwd_plan(const ssd_fwd_desc* d, BwdPlan* bp) {
     bp->sr = s;
     bp->sr.L = s.nc * s.Q;
     bp->ns = s.N / 64;
+    bp->xg = s.P == 64;
     // dC: the forward-time product with x in the role of B, dy in that of C and
     // B (split into 64-wide pieces, one per sub-head) in that of X; dB: the same
     // on reversed time with dy as B, x as C and C as X
@@ -331,16 +333,18 @@ ssd_status make_bwd_plan(const ssd_fwd_desc* d, BwdPlan* bp) {
         bytes[W_BR] = bytes[W_CR];
         bytes[W_AR] = Bz * Lp * H * 4;
         bytes[W_DXR] = bytes[W_DYR];
-        bytes[W_BEXP] = Bz * L * H * N * 2;
-        bytes[W_AEXP] = Bz * L * H * ns * 4;
-        bytes[W_S0T] = Bz * H * PN * 4;
-        bytes[W_DCH] = bytes[W_BEXP];
-        bytes[W_CREXP] = Bz * Lp * H * N * 2;
+        bytes[W_DCH] = Bz * L * H * N * 2;
         bytes[W_XR] = bytes[W_DYR];
-        bytes[W_AREXP] = Bz * Lp * H * ns * 4;
-        bytes[W_DSFT] = bytes[W_S0T];
-        bytes[W_DBH] = bytes[W_CREXP];
-        bytes[W_INNER] = (int64_t)(bp->pc.ws > bp->pb.ws ? bp->pc.ws : bp->pb.ws);
+        bytes[W_DBH] = Bz * Lp * H * N * 2;
+        if (!bp->xg) {
+            bytes[W_BEXP] = Bz * L * H * N * 2;
+            bytes[W_AEXP] = Bz * L * H * ns * 4;
+            bytes[W_S0T] = Bz * H * PN * 4;
+            bytes[W_CREXP] = Bz * Lp * H * N * 2;
+            bytes[W_AREXP] = Bz * Lp * H * ns * 4;
+            bytes[W_DSFT] = bytes[W_S0T];
+            bytes[W_INNER] = (int64_t)(bp->pc.ws > bp->pb.ws ? bp->pc.ws : bp->pb.ws);
+        }
     }
     size_t o = 0;
     for (int i = 0; i < kBwdBufs; ++i) {
@@ -665,6 +669,26 @@ ssd_status ssd_chunk_scan_bwd(const ssd_fwd_desc* desc, const void* X, const flo
         SSD_TRY(ssd::launch_scale_state_by_a0(dinitial_state, a, Bz, L, H, PN, hs), "bwd: dS0");
     // 4. da from the chunk-local four-term form
     SSD_TRY(ssd::launch_bwd_da(s, X, dY, a, B, C, F(W_SFW), F(W_SREV), da, hs), "bwd: da");
+    if (bp.xg) {
+        // 5-6. dC = S^T dy and dB = G^T x: the products with the state's two
+        // dimensions exchanged (headdim 64 over the state's 64-wide column
+        // pieces, state = the layer's headdim), entering each chunk from the
+        // transposed chunk states already at hand: S for dC (forward time),
+        // the adjoint for dB (reversed time)
+        ssd::FwdShape sc = s;
+        sc.H = H * ns; sc.P = 64; sc.N = P; sc.G = H;
+        ssd::StateSrc srcc{initial_state, H * PN, F(W_SFW), nc * H * PN, H * PN};
+        SSD_TRY(ssd::launch_mfma_out_xg(sc, G, B, a, X, dY, srcc, V(W_DCH), hs), "bwd: dC pass");
+        SSD_TRY(ssd::launch_group_sum(dC, V(W_DCH), Bz, L, L, 0, 1, H, G, N, hs), "bwd: dC group sum");
+        ssd::FwdShape sb = sc;
+        sb.L = Lp;
+        SSD_TRY(ssd::launch_remap_rows(V(W_XR), X, Bz, Lp, L, Lp - 1, -1, H * P * 2, hs), "bwd: reverse X");
+        ssd::StateSrc srcb{dfinal_state, H * PN, F(W_SREV), nc * H * PN, H * PN};
+        SSD_TRY(ssd::launch_mfma_out_xg(sb, G, V(W_CR), F(W_AR), V(W_DYR), V(W_XR), srcb, V(W_DBH), hs),
+                "bwd: dB pass");
+        SSD_TRY(ssd::launch_group_sum(dB, V(W_DBH), Bz, L, Lp, Lp - 1, -1, H, G, N, hs), "bwd: dB group sum");
+        return ok();
+    }
     // 5. dC = S^T dy: forward-time product, state dimensions exchanged
     SSD_TRY(ssd::launch_bcast_heads(V(W_BEXP), B, Bz, L, L, 0, 1, H, G, N, hs), "bwd: B per head");
     SSD_TRY(ssd::launch_remap_a(F(W_AEXP), a, Bz, L, L, 0, 1, H, ns, hs), "bwd: a per sub-head");

@@ -232,12 +232,18 @@ __device__ __forceinline__ void sync_lds() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int P, int N, bool FULL>
+// XG (the backward's exchanged-dimension products): X is a B or C array of
+// x_groups groups whose rows hold the HPG heads of a group side by side (head
+// hl of group grp reads columns hl*P .. of group grp / (G / x_groups)); every
+// head of a group reads the a of head grp of an [L][G] array; and the entering
+// states are read transposed, head hl of group grp taking columns hl*P .. of
+// the [N][HPG*P] state of head grp.
+template <int P, int N, bool FULL, bool XG = false>
 __global__ __launch_bounds__(kThreads) void k_mfma_seg(
     const u16* __restrict__ X, const float* __restrict__ a, const u16* __restrict__ B,
     const u16* __restrict__ C, StateSrc src, u16* __restrict__ Y, float* __restrict__ S_fin,
     float* __restrict__ Sseg, float* __restrict__ lamseg, int64_t nseg_total, int64_t L,
-    int H, int G, int64_t blocks_per_seg, int nseg_grid, int Bz)
+    int H, int G, int64_t blocks_per_seg, int nseg_grid, int Bz, int x_groups)
 {
     using Cfg = MfmaCfg<P, N>;
     constexpr int HW = Cfg::HW, NTL = Cfg::NTL, XPR = Cfg::XPR, BPR = Cfg::BPR;
@@ -337,7 +343,9 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
         const unsigned atv = vw * 64 + (unsigned)lane;
         const unsigned xr0 = atv / XPR, xlp = (atv % XPR) ^ (unsigned)swzbits<XPR>((int)(atv / XPR));
         const unsigned lc = (unsigned)block_last(c);
-        const u16* Xg = X + (((int64_t)b * L + c * kT) * H + grp * HPG) * P;
+        const u16* Xg;
+        if constexpr (XG) Xg = X + (((int64_t)b * L + c * kT) * x_groups + grp / (G / x_groups)) * (HPG * P);
+        else Xg = X + (((int64_t)b * L + c * kT) * H + grp * HPG) * P;
 #pragma unroll
         for (int k = 0; k < XOPS; ++k) {
             const unsigned s0 = (unsigned)k * kAuxThreads;      // first slot of the copy
@@ -345,8 +353,12 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
             const unsigned r = (s0 % XHT) / XPR + xr0;
             const unsigned tr = r <= lc ? r : lc;
             const unsigned hx = hl0 + hh < (unsigned)HPG ? hl0 + hh : HPG - 1;
-            dma16(Xg, ((tr * (unsigned)H + hx) * P + xlp * 8) * 2u,
-                  lds_addr(&sX[bf][0]) + (uint32_t)((s0 + vw * 64) * 16));
+            if constexpr (XG)
+                dma16(Xg, (tr * (unsigned)(x_groups * HPG * P) + hx * P + xlp * 8) * 2u,
+                      lds_addr(&sX[bf][0]) + (uint32_t)((s0 + vw * 64) * 16));
+            else
+                dma16(Xg, ((tr * (unsigned)H + hx) * P + xlp * 8) * 2u,
+                      lds_addr(&sX[bf][0]) + (uint32_t)((s0 + vw * 64) * 16));
         }
     };
     auto copy_bc = [&](int64_t c, int bf, bool isB) {
@@ -366,13 +378,16 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
     // wave that scans a head also copies it, so its own wait suffices
     auto copy_a = [&](int64_t c, int ia) {
         const unsigned lc = (unsigned)block_last(c);
-        const float* ag = a + ((int64_t)b * L + c * kT) * H + grp * HPG;
+        const float* ag;
+        if constexpr (XG) ag = a + ((int64_t)b * L + c * kT) * G + grp;
+        else ag = a + ((int64_t)b * L + c * kT) * H + grp * HPG;
         const unsigned tr = (unsigned)lane <= lc ? (unsigned)lane : lc;
 #pragma unroll
         for (int hh = 0; hh < HW; ++hh) {
             if ((hh & 1) != (int)aw) continue;
             const unsigned hx = hl0 + hh < (unsigned)HPG ? hl0 + hh : HPG - 1;
-            dma4(ag, (tr * (unsigned)H + hx) * 4u, lds_addr(&sA[ia][hh * kT]));
+            if constexpr (XG) dma4(ag, tr * (unsigned)G * 4u, lds_addr(&sA[ia][hh * kT]));
+            else dma4(ag, (tr * (unsigned)H + hx) * 4u, lds_addr(&sA[ia][hh * kT]));
         }
     };
 
@@ -548,7 +563,16 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
     if constexpr (FULL) {
         const float* S0 = seg == 0 ? (src.first ? src.first + b * src.first_bstride : nullptr)
                                    : (src.Sin ? src.Sin + b * src.bstride + seg * src.sstride : nullptr);
-        if (S0) {
+        if (XG && S0) {
+            // transposed: Sacc(p, n) = S[grp][n][hl*P + p] of an [N][HPG*P] state
+            const int hlc = hlw < HPG ? hlw : HPG - 1;
+            const float* St = S0 + (int64_t)grp * HPG * PN + hlc * P + pc + l32;
+#pragma unroll
+            for (int nt = 0; nt < NTL; ++nt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    Sacc[nt][r] = St[(int64_t)(nt * 32 + 16 * (r >> 3) + 8 * g2 + (r & 7)) * (HPG * P)];
+        } else if (S0) {
             S0 += (int64_t)h * PN;
 #pragma unroll
             for (int nt = 0; nt < NTL; ++nt) {
@@ -807,7 +831,7 @@ hipError_t launch_mfma_state(const FwdShape& s, int64_t seg_chunks, int64_t nseg
     hipLaunchKernelGGL((k_mfma_seg<PP, NN, false>), grid, dim3(kThreads), 0, st,             \
                        (const u16*)X, a, (const u16*)B, (const u16*)nullptr, none,          \
                        (u16*)nullptr, (float*)nullptr, Sseg, lamseg, nseg_total, s.L,       \
-                       (int)s.H, (int)s.G, bps, (int)nseg_run, (int)s.Bz);
+                       (int)s.H, (int)s.G, bps, (int)nseg_run, (int)s.Bz, 0);
     SSD_MFMA_DISPATCH(SSD_LAUNCH_STATE)
 #undef SSD_LAUNCH_STATE
     return hipGetLastError();
@@ -823,9 +847,22 @@ hipError_t launch_mfma_out(const FwdShape& s, int64_t seg_chunks, int64_t nseg,
     hipLaunchKernelGGL((k_mfma_seg<PP, NN, true>), grid, dim3(kThreads), 0, st,              \
                        (const u16*)X, a, (const u16*)B, (const u16*)C, src, (u16*)Y, S_fin, \
                        (float*)nullptr, (float*)nullptr, (int64_t)0, s.L, (int)s.H,          \
-                       (int)s.G, bps, (int)nseg, (int)s.Bz);
+                       (int)s.G, bps, (int)nseg, (int)s.Bz, 0);
     SSD_MFMA_DISPATCH(SSD_LAUNCH_OUT)
 #undef SSD_LAUNCH_OUT
+    return hipGetLastError();
+}
+
+hipError_t launch_mfma_out_xg(const FwdShape& s, int64_t x_groups, const void* X, const float* a,
+                              const void* B, const void* C, StateSrc src, void* Y, hipStream_t st)
+{
+    if (!(s.P == 64 && s.N == 64) || x_groups < 1 || s.G % x_groups != 0) return hipErrorInvalidValue;
+    const dim3 grid(grid_for(s, s.nc));
+    const int64_t bps = s.Q / kT;
+    hipLaunchKernelGGL((k_mfma_seg<64, 64, true, true>), grid, dim3(kThreads), 0, st,
+                       (const u16*)X, a, (const u16*)B, (const u16*)C, src, (u16*)Y, (float*)nullptr,
+                       (float*)nullptr, (float*)nullptr, (int64_t)0, s.L, (int)s.H, (int)s.G, bps,
+                       (int)s.nc, (int)s.Bz, (int)x_groups);
     return hipGetLastError();
 }
 

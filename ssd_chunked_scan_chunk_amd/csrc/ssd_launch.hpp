@@ -60,6 +60,14 @@ hipError_t launch_mfma_out(const FwdShape& s, int64_t seg_chunks, int64_t nseg,
                            const void* X, const float* a, const void* B, const void* C,
                            StateSrc src, void* Y, float* S_fin, hipStream_t st);
 
+// The backward's exchanged-dimension products (headdim 64, state 64, one chunk
+// per segment): X [Bz][L][x_groups][(H/G)*64] bf16 shared by the H/G heads of
+// a group (head hl reads columns hl*64 ..), a [Bz][L][G] (one decay per group),
+// and the entering state of segment s read transposed from the [64][(H/G)*64]
+// state of group grp in src (segment 0 from src.first, s >= 1 from src.Sin).
+hipError_t launch_mfma_out_xg(const FwdShape& s, int64_t x_groups, const void* X, const float* a,
+                              const void* B, const void* C, StateSrc src, void* Y, hipStream_t st);
+
 // ---- decode step ---------------------------------------------------------------------
 hipError_t launch_step(int64_t Bz, int64_t H, int64_t P, int64_t N, int64_t G, bool bf16,
                        float* state, const void* x, const float* a, const void* B,
