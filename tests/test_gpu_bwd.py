@@ -97,3 +97,18 @@ def test_bwd_m2_130m_shape():
     sh = si.FWD_CONFIGS["m2_130m"]
     bwd_case(si.FwdShape(2, sh.seqlen, sh.nheads, sh.headdim, sh.dstate, sh.ngroups, sh.chunk,
                          sh.dtype, dt_recipe=sh.dt_recipe), seed=9, tag="m2-130m")
+
+
+def test_bwd_m2_2p7b_row():
+    # one batch row of the Mamba-2 2.7B layer shape (80 heads sharing one
+    # group, 16 chunks), all gradients against the full oracle adjoint
+    sh = si.FWD_CONFIGS["m2_2p7b"]
+    bwd_case(si.FwdShape(1, sh.seqlen, sh.nheads, sh.headdim, sh.dstate, sh.ngroups, sh.chunk,
+                         sh.dtype), seed=11, tag="m2-2p7b-row")
+
+
+def test_bwd_long_many_chunks():
+    # 64 chunks of 64 steps with a ragged tail: the reversed sequence's padding,
+    # the chunk-state scans over many units and the per-chunk adjoint slots
+    bwd_case(si.FwdShape(1, 64 * 64 - 21, 3, 64, 64, 1, 64, si.BF16, dt_recipe="mamba2_dt"),
+             seed=12, tag="many-chunks")
