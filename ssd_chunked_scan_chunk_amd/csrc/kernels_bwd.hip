@@ -224,10 +224,13 @@ hipError_t launch_scale_state_by_a0(float* state, const float* a, int64_t Bz, in
 // over {i >= t, j < t} splits into: the diagonal tile's own part; the row
 // sums of M left of tile T (rows i >= t of tile T); the column sums of M
 // below tile T (columns j < t of tile T); and the tiles strictly below and
-// left of the diagonal tile (a constant per T).  Wave w owns row tiles w and
-// 7 - w (balanced work for 8 tiles).  The state terms are formed transposed
-// (state rows p as the first operand) so that their sums over p stay inside
-// a lane.
+// left of the diagonal tile (a constant per T).  Eight wavefronts, two per
+// SIMD so that one's MFMA, LDS and exp latencies hide behind the other's
+// work: waves w and w + 4 share row tiles w and 7 - w (balanced for 8
+// tiles), taking the column tiles J of even and of odd index respectively.
+// The state terms are formed transposed (state rows p as the first operand)
+// so that their sums over p stay inside a lane; the even waves take the
+// entering-state term, the odd ones the right-adjoint term.
 //
 // MFMA 32x32x16 operand/accumulator layout (lane l, l32 = l % 32, g2 = l / 32):
 // operand fragments hold row l32, k = 8 g2 .. 8 g2 + 7 of a row-major
@@ -239,7 +242,8 @@ hipError_t launch_scale_state_by_a0(float* state, const float* a, int64_t Bz, in
 // half-wave reads at one logical piece fall on 16 distinct 16-byte slots of
 // the 256-byte bank window.
 // ---------------------------------------------------------------------------
-constexpr int kDaThreads = 256;
+constexpr int kDaThreads = 512;   // eight wavefronts
+constexpr int kDaWaves = kDaThreads / 64;
 constexpr int kDaMaxQ = 256;
 
 __device__ __forceinline__ f32x16_b mfma32b(const bf16x8& a, const bf16x8& b, const f32x16_b& c) {
@@ -293,7 +297,7 @@ __device__ __forceinline__ float block_sum(float v, float* sred) {
 }
 
 template <int P, int N>
-__global__ __launch_bounds__(kDaThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_bwd_da(
+__global__ __launch_bounds__(kDaThreads) void k_bwd_da(
     const u16* __restrict__ X, const u16* __restrict__ dY, const float* __restrict__ a,
     const u16* __restrict__ Bm, const u16* __restrict__ Cm, const float* __restrict__ Sin,
     const float* __restrict__ Srev, float* __restrict__ da, int64_t L, int H, int G, int Q,
@@ -301,33 +305,40 @@ __global__ __launch_bounds__(kDaThreads) __attribute__((amdgpu_waves_per_eu(1, 1
 {
     constexpr int XPR = P / 8, BPR = N / 8;   // 16-byte pieces per row
     constexpr int PN = P * N;
+    constexpr int kScr = 32 * 33;             // floats of one wave's scratch tile
+    constexpr int kUnion = kDaWaves * kScr * 4 > 2 * PN * 2 ? kDaWaves * kScr * 4 : 2 * PN * 2;
     __shared__ __attribute__((aligned(16))) u16 sX[kDaMaxQ * P];
     __shared__ __attribute__((aligned(16))) u16 sB[kDaMaxQ * N];
-    __shared__ __attribute__((aligned(16))) u16 sS[P * N];   // entering state, bf16
-    __shared__ __attribute__((aligned(16))) u16 sR[P * N];   // adjoint from the right, bf16
-    __shared__ float sCs[kDaMaxQ], sRS[kDaMaxQ], sDg[kDaMaxQ], sT2[kDaMaxQ], sT3[kDaMaxQ];
-    __shared__ float sCS[kDaThreads / 64][kDaMaxQ];
+    // the masked-term phase uses this as per-wave scratch tiles, the state
+    // phase as the bf16 entering state and right adjoint
+    __shared__ __attribute__((aligned(16))) unsigned char sU[kUnion];
+    __shared__ float sCs[kDaMaxQ], sDg[kDaMaxQ], sT2[kDaMaxQ], sT3[kDaMaxQ];
+    __shared__ float sRS[2][kDaMaxQ];          // row sums left of the diagonal, per column parity
+    __shared__ float sCS[kDaWaves][kDaMaxQ];   // column sums below the diagonal, per wave
     __shared__ float sF[8][8];
-    __shared__ float sScr[kDaThreads / 64][32 * 33];
-    __shared__ float sRed[8];
+    __shared__ float sRed[kDaWaves];
 
     const int64_t c = blockIdx.x;
     const int h = blockIdx.y, b = blockIdx.z;
     const int g = h / (H / G);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int par = wave >> 2, wq = wave & 3;
     const int l32 = lane & 31, g2 = lane >> 5;
     const int64_t t0 = c * Q;
     const int Lc = (int)((L - t0 < Q) ? (L - t0) : Q);
     const int nI = Q / 32;
+    float* scr = reinterpret_cast<float*>(sU) + wave * kScr;
+    u16* sS = reinterpret_cast<u16*>(sU);
+    u16* sR = sS + PN;
 
     // ---- segment sums of the chunk (zero past a ragged end) ----
     const float av = tid < Lc ? a[((int64_t)b * L + t0 + tid) * H + h] : 0.f;
     const float cs = block_inclusive_scan(av, sRed, (Q + 63) / 64);
     if (tid < Q) {
         sCs[tid] = cs;
-        sRS[tid] = 0.f; sDg[tid] = 0.f; sT2[tid] = 0.f; sT3[tid] = 0.f;
+        sRS[0][tid] = 0.f; sRS[1][tid] = 0.f; sDg[tid] = 0.f; sT2[tid] = 0.f; sT3[tid] = 0.f;
     }
-    for (int k = tid; k < (kDaThreads / 64) * kDaMaxQ; k += kDaThreads) (&sCS[0][0])[k] = 0.f;
+    for (int k = tid; k < kDaWaves * kDaMaxQ; k += kDaThreads) (&sCS[0][0])[k] = 0.f;
     if (tid < 64) (&sF[0][0])[tid] = 0.f;
 
     // ---- X and B rows of the chunk into LDS (rows past the end are zero).
@@ -355,6 +366,115 @@ __global__ __launch_bounds__(kDaThreads) __attribute__((amdgpu_waves_per_eu(1, 1
     };
     stage_rows(sX, X + (((int64_t)b * L + t0) * H + h) * P, (int64_t)H * P, std::integral_constant<int, XPR>{});
     stage_rows(sB, Bm + (((int64_t)b * L + t0) * G + g) * N, (int64_t)G * N, std::integral_constant<int, BPR>{});
+    __syncthreads();
+
+    auto frag = [&](const u16* tile, auto pr, int row, int ks) {   // row `row`, k = 16ks + 8g2 .. +7
+        constexpr int PR = decltype(pr)::value;
+        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4_b*>(tile + dswz<PR>(row, 16 * ks + 8 * g2)));
+    };
+    using XP = std::integral_constant<int, XPR>;
+    using BP = std::integral_constant<int, BPR>;
+    // row-side operands from HBM: dy and C rows i = 32I + l32 (zero past the end)
+    auto load_rows = [&](int I, u32x4_b (&dyu)[P / 16], bf16x8 (&cf)[N / 16]) {
+        const int irow = 32 * I + l32;
+        const bool iok = irow < Lc;
+        const int64_t tr = (int64_t)b * L + t0 + irow;
+#pragma unroll
+        for (int ks = 0; ks < P / 16; ++ks) {
+            u32x4_b v = {0u, 0u, 0u, 0u};
+            if (iok) v = *reinterpret_cast<const u32x4_b*>(dY + (tr * H + h) * P + 16 * ks + 8 * g2);
+            dyu[ks] = v;
+        }
+#pragma unroll
+        for (int ks = 0; ks < N / 16; ++ks) {
+            u32x4_b v = {0u, 0u, 0u, 0u};
+            if (iok) v = *reinterpret_cast<const u32x4_b*>(Cm + (tr * G + g) * N + 16 * ks + 8 * g2);
+            cf[ks] = __builtin_bit_cast(bf16x8, v);
+        }
+    };
+
+    // ================= the masked term =================
+    for (int pass = 0; pass < 2; ++pass) {
+        const int I = pass == 0 ? wq : 7 - wq;   // (never the same tile twice: wq <= 3)
+        if (I >= nI || 32 * I >= Lc) continue;
+        u32x4_b dyu[P / 16];
+        bf16x8 cf[N / 16];
+        load_rows(I, dyu, cf);
+        float csI[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) csI[r] = sCs[32 * I + acc_row(r, g2)] * kLog2e;
+
+        f32x16_b Mrow = zero16b();
+        for (int J = par; J <= I; J += 2) {
+            // the column tile's operand fragments, all read before the first MFMA
+            bf16x8 xb[P / 16], bb[N / 16];
+#pragma unroll
+            for (int ks = 0; ks < P / 16; ++ks) xb[ks] = frag(sX, XP{}, 32 * J + l32, ks);
+#pragma unroll
+            for (int ks = 0; ks < N / 16; ++ks) bb[ks] = frag(sB, BP{}, 32 * J + l32, ks);
+            __builtin_amdgcn_sched_barrier(0);   // (keep the reads ahead of the MFMA chain)
+            f32x16_b DX = zero16b(), CB = zero16b();
+#pragma unroll
+            for (int ks = 0; ks < P / 16; ++ks) DX = mfma32b(__builtin_bit_cast(bf16x8, dyu[ks]), xb[ks], DX);
+#pragma unroll
+            for (int ks = 0; ks < N / 16; ++ks) CB = mfma32b(cf[ks], bb[ks], CB);
+            const float csj = sCs[32 * J + l32] * kLog2e;
+            f32x16_b M;
+            if (J < I) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) M[r] = fast_exp2(csI[r] - csj) * DX[r] * CB[r];
+                Mrow += M;
+                float cv = 0.f;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) cv += M[r];
+                cv += __shfl_xor(cv, 32, 64);             // column 32J + l32 over the tile's 32 rows
+                if (lane < 32) atomicAdd(&sCS[wave][32 * J + l32], cv);   // (one writer per address)
+                const float tv = sum_lanes32(cv);
+                if (lane == 0) sF[I][J] = tv;
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    M[r] = acc_row(r, g2) > l32 ? fast_exp2(csI[r] - csj) * DX[r] * CB[r] : 0.f;
+                // diagonal tile: sum over {i >= t > j} inside the tile.  Lane i
+                // turns its row into exclusive prefix sums over j, then lane t
+                // sums column t of those over i >= t.
+                wave_lds_sync();
+#pragma unroll
+                for (int r = 0; r < 16; ++r) scr[acc_row(r, g2) * 33 + l32] = M[r];
+                wave_lds_sync();
+                if (lane < 32) {
+                    float run = 0.f;
+#pragma unroll
+                    for (int j = 0; j < 32; ++j) {
+                        const float v = scr[lane * 33 + j];
+                        scr[lane * 33 + j] = run;
+                        run += v;
+                    }
+                }
+                wave_lds_sync();
+                if (lane < 32) {
+                    float s = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 32; ++i) s += i >= lane ? scr[i * 33 + lane] : 0.f;
+                    sDg[32 * I + lane] = s;
+                }
+                wave_lds_sync();
+            }
+        }
+        // this wave's share (its column parity) of the row sums left of the tile
+        wave_lds_sync();
+#pragma unroll
+        for (int r = 0; r < 16; ++r) scr[acc_row(r, g2) * 33 + l32] = Mrow[r];
+        wave_lds_sync();
+        if (lane < 32) {
+            float s = 0.f;
+#pragma unroll
+            for (int j = 0; j < 32; ++j) s += scr[lane * 33 + j];
+            sRS[par][32 * I + lane] = s;
+        }
+        wave_lds_sync();
+    }
+    __syncthreads();   // the scratch tiles are free
 
     // ---- entering state S_in and the adjoint entering from the right,
     // R = exp(a at the next chunk's first step) G there (dS_fin for the last
@@ -387,119 +507,23 @@ __global__ __launch_bounds__(kDaThreads) __attribute__((amdgpu_waves_per_eu(1, 1
                 make_uint4(pack2b(r0.x, r0.y), pack2b(r0.z, r0.w), pack2b(r1.x, r1.y), pack2b(r1.z, r1.w));
         }
     }
-    dot = block_sum(dot, sRed);   // (its barriers also publish the LDS fills above)
+    dot = block_sum(dot, sRed);   // (its barriers also publish the states above)
     const float Lam = sCs[Lc - 1];
     const float t4 = fR * expf(Lam) * dot;
 
-    float* scr = &sScr[wave][0];
-    auto frag = [&](const u16* tile, auto pr, int row, int ks) {   // row `row`, k = 16ks + 8g2 .. +7
-        constexpr int PR = decltype(pr)::value;
-        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4_b*>(tile + dswz<PR>(row, 16 * ks + 8 * g2)));
-    };
-    using XP = std::integral_constant<int, XPR>;
-    using BP = std::integral_constant<int, BPR>;
-
+    // ================= the state terms =================
     for (int pass = 0; pass < 2; ++pass) {
-        const int I = pass == 0 ? wave : 7 - wave;
-        if (I >= nI || (pass == 1 && I == wave) || 32 * I >= Lc) continue;
-        // row-side operands from HBM: dy and C rows i = 32I + l32 (zero past the end)
+        const int I = pass == 0 ? wq : 7 - wq;
+        if (I >= nI || 32 * I >= Lc) continue;
         const int irow = 32 * I + l32;
-        const bool iok = irow < Lc;
-        const int64_t tr = (int64_t)b * L + t0 + irow;
-        u32x4_b dyu[P / 16];
-        bf16x8 cf[N / 16];
-#pragma unroll
-        for (int ks = 0; ks < P / 16; ++ks) {
-            u32x4_b v = {0u, 0u, 0u, 0u};
-            if (iok) v = *reinterpret_cast<const u32x4_b*>(dY + (tr * H + h) * P + 16 * ks + 8 * g2);
-            dyu[ks] = v;
-        }
-#pragma unroll
-        for (int ks = 0; ks < N / 16; ++ks) {
-            u32x4_b v = {0u, 0u, 0u, 0u};
-            if (iok) v = *reinterpret_cast<const u32x4_b*>(Cm + (tr * G + g) * N + 16 * ks + 8 * g2);
-            cf[ks] = __builtin_bit_cast(bf16x8, v);
-        }
-        float csI[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) csI[r] = sCs[32 * I + acc_row(r, g2)];
-
-        f32x16_b Mrow = zero16b();
-        for (int J = 0; J <= I; ++J) {
-            // the column tile's operand fragments, all read before the first MFMA
-            bf16x8 xb[P / 16], bb[N / 16];
-#pragma unroll
-            for (int ks = 0; ks < P / 16; ++ks) xb[ks] = frag(sX, XP{}, 32 * J + l32, ks);
-#pragma unroll
-            for (int ks = 0; ks < N / 16; ++ks) bb[ks] = frag(sB, BP{}, 32 * J + l32, ks);
-            __builtin_amdgcn_sched_barrier(0);   // (keep the reads ahead of the MFMA chain)
-            f32x16_b DX = zero16b(), CB = zero16b();
-#pragma unroll
-            for (int ks = 0; ks < P / 16; ++ks) DX = mfma32b(__builtin_bit_cast(bf16x8, dyu[ks]), xb[ks], DX);
-#pragma unroll
-            for (int ks = 0; ks < N / 16; ++ks) CB = mfma32b(cf[ks], bb[ks], CB);
-            const float csj = sCs[32 * J + l32];
-            f32x16_b M;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const bool keep = J < I || acc_row(r, g2) > l32;
-                M[r] = keep ? fast_exp2((csI[r] - csj) * kLog2e) * DX[r] * CB[r] : 0.f;
-            }
-            if (J < I) {
-                Mrow += M;
-                float cv = 0.f;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) cv += M[r];
-                cv += __shfl_xor(cv, 32, 64);             // column 32J + l32 over the tile's 32 rows
-                if (lane < 32) atomicAdd(&sCS[wave][32 * J + l32], cv);   // (one writer per address)
-                const float tv = sum_lanes32(cv);
-                if (lane == 0) sF[I][J] = tv;
-            } else {
-                // diagonal tile: sum over {i >= t > j} inside the tile.  Lane i
-                // turns its row into exclusive prefix sums over j, then lane t
-                // sums column t of those over i >= t.
-                wave_lds_sync();
-#pragma unroll
-                for (int r = 0; r < 16; ++r) scr[acc_row(r, g2) * 33 + l32] = M[r];
-                wave_lds_sync();
-                if (lane < 32) {
-                    float run = 0.f;
-#pragma unroll
-                    for (int j = 0; j < 32; ++j) {
-                        const float v = scr[lane * 33 + j];
-                        scr[lane * 33 + j] = run;
-                        run += v;
-                    }
-                }
-                wave_lds_sync();
-                if (lane < 32) {
-                    float s = 0.f;
-#pragma unroll
-                    for (int i = 0; i < 32; ++i) s += i >= lane ? scr[i * 33 + lane] : 0.f;
-                    sDg[32 * I + lane] = s;
-                }
-                wave_lds_sync();
-            }
-        }
-        // row sums of M left of this tile
-        {
-            wave_lds_sync();
-#pragma unroll
-            for (int r = 0; r < 16; ++r) scr[acc_row(r, g2) * 33 + l32] = Mrow[r];
-            wave_lds_sync();
-            if (lane < 32) {
-                float s = 0.f;
-#pragma unroll
-                for (int j = 0; j < 32; ++j) s += scr[lane * 33 + j];
-                sRS[32 * I + lane] = s;
-            }
-            wave_lds_sync();
-        }
-        // state part of the output dotted with dy: exp(cs_i) dy_i . (S_in C_i),
-        // from (S_in C^T) with rows p, column i = l32.  Register r of 16-wide
-        // p-tile q = r/4 holds p = 8q + 4g2 + r%4 (+32pt); this lane's dy row
-        // holds p = 16ks + 8g2 + 0..7, the partner lane (l ^ 32) the other half
-        {
+        if (par == 0) {
+            // state part of the output dotted with dy: exp(cs_i) dy_i . (S_in C_i),
+            // from (S_in C^T) with rows p, column i = l32.  Register r of 16-wide
+            // p-tile q = r/4 holds p = 8q + 4g2 + r%4 (+32pt); this lane's dy row
+            // holds p = 16ks + 8g2 + 0..7, the partner lane (l ^ 32) the other half
+            u32x4_b dyu[P / 16];
+            bf16x8 cf[N / 16];
+            load_rows(I, dyu, cf);
             float acc = 0.f;
 #pragma unroll
             for (int pt = 0; pt < P / 32; ++pt) {
@@ -526,27 +550,25 @@ __global__ __launch_bounds__(kDaThreads) __attribute__((amdgpu_waves_per_eu(1, 1
             }
             acc += __shfl_xor(acc, 32, 64);
             if (lane < 32 && irow < Lc) sT2[irow] = expf(sCs[irow]) * acc;
-        }
-        // adjoint from the right dotted with x: exp(Lam - cs_j) x_j . (R B_j),
-        // from (R B^T) with rows p, column j = l32 of this tile
-        {
+        } else {
+            // adjoint from the right dotted with x: exp(Lam - cs_j) x_j . (R B_j),
+            // from (R B^T) with rows p, column j = l32 of this tile
             float acc = 0.f;
-            const int jrow = irow;
 #pragma unroll
             for (int pt = 0; pt < P / 32; ++pt) {
                 f32x16_b V = zero16b();
 #pragma unroll
                 for (int ks = 0; ks < N / 16; ++ks)
-                    V = mfma32b(frag(sR, BP{}, 32 * pt + l32, ks), frag(sB, BP{}, jrow, ks), V);
+                    V = mfma32b(frag(sR, BP{}, 32 * pt + l32, ks), frag(sB, BP{}, irow, ks), V);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const uint2 xv = *reinterpret_cast<const uint2*>(sX + dswz<XPR>(jrow, 32 * pt + 8 * q + 4 * g2));
+                    const uint2 xv = *reinterpret_cast<const uint2*>(sX + dswz<XPR>(irow, 32 * pt + 8 * q + 4 * g2));
                     acc += V[4 * q + 0] * bf_lo(xv.x) + V[4 * q + 1] * bf_hi(xv.x) +
                            V[4 * q + 2] * bf_lo(xv.y) + V[4 * q + 3] * bf_hi(xv.y);
                 }
             }
             acc += __shfl_xor(acc, 32, 64);
-            if (lane < 32 && jrow < Lc) sT3[jrow] = fR * expf(Lam - sCs[jrow]) * acc;
+            if (lane < 32 && irow < Lc) sT3[irow] = fR * expf(Lam - sCs[irow]) * acc;
         }
     }
     __syncthreads();
@@ -559,7 +581,7 @@ __global__ __launch_bounds__(kDaThreads) __attribute__((amdgpu_waves_per_eu(1, 1
     float csv = 0.f;
     if (tin) {
 #pragma unroll
-        for (int w = 0; w < kDaThreads / 64; ++w) csv += sCS[w][t];
+        for (int w = 0; w < kDaWaves; ++w) csv += sCS[w][t];
     }
     float cpre = csv;
 #pragma unroll
@@ -569,7 +591,7 @@ __global__ __launch_bounds__(kDaThreads) __attribute__((amdgpu_waves_per_eu(1, 1
     }
     cpre -= csv;
     // row sums left of tile T, suffix over i >= t inside the tile
-    float rsuf = tin ? sRS[t] : 0.f;
+    float rsuf = tin ? sRS[0][t] + sRS[1][t] : 0.f;
 #pragma unroll
     for (int d = 1; d < 32; d <<= 1) {
         const float u = __shfl_down(rsuf, d, 32);
