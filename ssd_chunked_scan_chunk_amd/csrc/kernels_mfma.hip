@@ -99,16 +99,16 @@ constexpr int kAuxThreads = 64 * (kWaves - kStateWaves);   // copy and score wav
 constexpr int kThreads = 64 * kWaves;
 constexpr int kPRow = 40;    // padded row (elements) of a shared 32x32 bf16 score tile (16-byte aligned)
 
-template <int P, int N>
+template <int P, int N, int SW = kStateWaves>
 struct MfmaCfg {
     static constexpr int PS = P / 32;                    // state waves per head (one head-dim tile each)
-    static constexpr int HW = kStateWaves / PS;          // heads per workgroup
+    static constexpr int HW = SW / PS;                   // heads per workgroup
     static constexpr int NTL = N / 32;                   // 32-wide state-dim tiles
     static constexpr int XPR = P / 8;                    // 16-byte pieces per X row
     static constexpr int BPR = N / 8;                    // 16-byte pieces per B / C row
     static constexpr int XOPS = HW * kT * XPR / kAuxThreads;   // X copies per aux thread per block
     static constexpr int BOPS = kT * BPR / kAuxThreads;        // B (or C) copies per aux thread
-    static_assert(P % 32 == 0 && N % 32 == 0 && kStateWaves % PS == 0, "tile shape");
+    static_assert(P % 32 == 0 && N % 32 == 0 && SW % PS == 0, "tile shape");
     static_assert((HW * kT * XPR) % kAuxThreads == 0 && (kT * BPR) % kAuxThreads == 0, "copy shape");
     static_assert(kAuxThreads % XPR == 0 && kAuxThreads % BPR == 0 && (kT * XPR) % kAuxThreads == 0,
                   "a copy covers whole rows of one head");
@@ -237,15 +237,16 @@ __device__ __forceinline__ void sync_lds() {
 // hl of group grp reads columns hl*P .. of group grp / (G / x_groups)); every
 // head of a group reads the a of head grp of an [L][G] array; and the entering
 // states are read transposed, head hl of group grp taking columns hl*P .. of
-// the [N][HPG*P] state of head grp.
-template <int P, int N, bool FULL, bool XG = false>
-__global__ __launch_bounds__(kThreads) void k_mfma_seg(
+// the [N][HPG*P] state of head grp.  SW is the number of state waves (the
+// workgroup has SW + 2 wavefronts).
+template <int P, int N, bool FULL, bool XG = false, int SW = kStateWaves>
+__global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(SW == kStateWaves ? 2 : 3))) void k_mfma_seg(
     const u16* __restrict__ X, const float* __restrict__ a, const u16* __restrict__ B,
     const u16* __restrict__ C, StateSrc src, u16* __restrict__ Y, float* __restrict__ S_fin,
     float* __restrict__ Sseg, float* __restrict__ lamseg, int64_t nseg_total, int64_t L,
     int H, int G, int64_t blocks_per_seg, int nseg_grid, int Bz, int x_groups)
 {
-    using Cfg = MfmaCfg<P, N>;
+    using Cfg = MfmaCfg<P, N, SW>;
     constexpr int HW = Cfg::HW, NTL = Cfg::NTL, XPR = Cfg::XPR, BPR = Cfg::BPR;
     constexpr int XOPS = Cfg::XOPS, BOPS = Cfg::BOPS;
 
@@ -274,7 +275,7 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const bool aux = wave >= kStateWaves;        // copy / score wave
+    const bool aux = wave >= SW;                 // copy / score wave
     const int sw = aux ? 0 : wave;               // state wave index (aux waves: unused)
     const int l32 = lane & 31, g2 = lane >> 5;
     const int trow = (lane & 15) >> 2, tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
@@ -333,8 +334,8 @@ __global__ __launch_bounds__(kThreads) void k_mfma_seg(
     // row's swizzle; per copy only a uniform row or head base changes.  Rows past the end of the sequence are clamped to
     // the last valid row (their scores are masked, their state weight is zero
     // and their outputs are not stored). ----
-    const unsigned at = (unsigned)(tid - kStateWaves * 64);   // aux thread (valid for aux waves)
-    const unsigned aw = (unsigned)(wave - kStateWaves);
+    const unsigned at = (unsigned)(tid - SW * 64);           // aux thread (valid for aux waves)
+    const unsigned aw = (unsigned)(wave - SW);
     constexpr unsigned XHT = kT * XPR;                          // slots per head tile
     constexpr unsigned BRS = kAuxThreads / BPR;                 // B / C rows per copy
     const unsigned br0 = at / BPR, bq = at % BPR;
@@ -857,9 +858,13 @@ hipError_t launch_mfma_out_xg(const FwdShape& s, int64_t x_groups, const void* X
                               const void* B, const void* C, StateSrc src, void* Y, hipStream_t st)
 {
     if (!(s.P == 64 && s.N == 64) || x_groups < 1 || s.G % x_groups != 0) return hipErrorInvalidValue;
-    const dim3 grid(grid_for(s, s.nc));
+    // four state waves: two sub-heads of 64 per workgroup (a group has H/G of them)
+    constexpr int kSW = 4;
+    const int64_t hq = (s.H / s.G + kSW / 2 - 1) / (kSW / 2);
+    const int64_t items = s.Bz * s.nc * s.G * hq;
+    const dim3 grid((unsigned)(((items + kXcds - 1) / kXcds) * kXcds));
     const int64_t bps = s.Q / kT;
-    hipLaunchKernelGGL((k_mfma_seg<64, 64, true, true>), grid, dim3(kThreads), 0, st,
+    hipLaunchKernelGGL((k_mfma_seg<64, 64, true, true, kSW>), grid, dim3(64 * (kSW + 2)), 0, st,
                        (const u16*)X, a, (const u16*)B, (const u16*)C, src, (u16*)Y, (float*)nullptr,
                        (float*)nullptr, (float*)nullptr, (int64_t)0, s.L, (int)s.H, (int)s.G, bps,
                        (int)s.nc, (int)s.Bz, (int)x_groups);
