@@ -233,9 +233,39 @@ def bench_backward(sh, steps, warmup, nbatch, seed0=100):
     for i in range(warmup):
         step(i)
     t = time_events(step, steps) / steps
-    del batches, ws
+
+    # the dominant kernel (da) alone through its stage entry point, fed chunk
+    # states of the right shape (their values do not change the work)
+    nc = (sh.seqlen + sh.chunk - 1) // sh.chunk
+    st_shape = (sh.batch, nc, sh.nheads, sh.headdim, sh.dstate)
+    Sin = 0.1 * torch.randn(st_shape, device="cuda")
+    Adj = 0.1 * torch.randn(st_shape, device="cuda")
+    da = torch.empty_like(g0["a"])
+
+    def da_step(i):
+        g = batches[i % nbatch]
+        ssd.bwd_da(g["X"], g["a"], g["B"], g["C"], g["dY"], sh.chunk, Sin, Adj, da=da)
+
+    for i in range(warmup):
+        da_step(i)
+    t_da = time_events(da_step, steps) / steps
+    del batches, ws, Sin, Adj, da
     torch.cuda.empty_cache()
-    return t
+    return t, t_da
+
+
+def bwd_da_work(sh):
+    """(MFMA flops, algorithmic HBM bytes) of one da-kernel launch: per chunk
+    and head the lower-triangle 32x32 tiles of dY X^T (K = P) and C B^T (K = N)
+    plus C S_in^T and B R^T; X, dY, B, C, a and the two fp32 chunk-state
+    arrays in, da out."""
+    P, N, H, G, Q = sh.headdim, sh.dstate, sh.nheads, sh.ngroups, sh.chunk
+    nc = (sh.seqlen + Q - 1) // Q
+    nI = Q // 32
+    flops = sh.batch * nc * H * ((nI * (nI + 1) // 2) * 32 * 32 * 2 * (P + N) + 2 * 2 * Q * P * N)
+    tok = sh.batch * sh.seqlen
+    nbytes = tok * (2 * H * P * 2 + 2 * G * N * 2 + 2 * H * 4) + 2 * sh.batch * nc * H * P * N * 4
+    return flops, nbytes
 
 
 def cpu_baseline(sh):
@@ -295,10 +325,14 @@ def main():
     sh = si.FWD_CONFIGS["m2_130m"]
     tokens = sh.batch * sh.seqlen
     if args.bwd_only:
-        tb = bench_backward(sh, args.steps, args.warmup, 2)
+        tb, tda = bench_backward(sh, args.steps, args.warmup, 2)
         fl = tokens * bwd_algo_flops_per_token(sh)
+        dfl, dby = bwd_da_work(sh)
         print(json.dumps({"backward_m2_130m": {"ms_per_step": tb * 1e3, "tokens_per_s": tokens / tb,
-                                               "mfma_frac": fl / tb / 1e12 / BF16_PEAK_TFLOPS}}))
+                                               "mfma_frac": fl / tb / 1e12 / BF16_PEAK_TFLOPS,
+                                               "da_kernel_us": tda * 1e6,
+                                               "da_mfma_frac": dfl / tda / 1e12 / BF16_PEAK_TFLOPS,
+                                               "da_hbm_frac": dby / tda / 1e9 / HBM_PEAK_GBS}}))
         return
     per_batch = tokens * fwd_algo_bytes_per_token(sh)
     nbatch = max(2, int(np.ceil(2 * 256e6 / per_batch)))   # > 2x the Infinity Cache
@@ -349,13 +383,21 @@ def main():
         sec["decode_step"] = {"workload": "batch 256, 80 heads, headdim 64, dstate 128, fp32 state in place",
                               "us_per_step": td * 1e6, "GB_per_s": nbytes / td / 1e9,
                               "hbm_frac": nbytes / td / 1e9 / HBM_PEAK_GBS, "tokens_per_s": 256 / td}
-        tb = bench_backward(sh, max(10, args.steps // 2), 3, 2)
+        tb, tda = bench_backward(sh, max(10, args.steps // 2), 3, 2)
         fl = tokens * bwd_algo_flops_per_token(sh)
+        dfl, dby = bwd_da_work(sh)
         sec["backward_m2_130m"] = {
             "workload": "gradients dX, da, dB, dC, d(initial state) of the 130M-shaped layer "
                         "for upstream dY and d(final state)",
             "ms_per_step": tb * 1e3, "tokens_per_s": tokens / tb, "bwd_over_fwd": tb / t_step,
-            "mfma_frac": fl / tb / 1e12 / BF16_PEAK_TFLOPS, "algo_flops_per_step": fl}
+            "mfma_frac": fl / tb / 1e12 / BF16_PEAK_TFLOPS, "algo_flops_per_step": fl,
+            # its dominant kernel, timed alone with HIP events
+            "dominant_kernel": {"kernel": "k_bwd_da", "us": tda * 1e6,
+                                "mfma": {"achieved": dfl / tda / 1e12, "peak": BF16_PEAK_TFLOPS,
+                                         "unit": "TFLOP/s", "frac": dfl / tda / 1e12 / BF16_PEAK_TFLOPS},
+                                "hbm": {"achieved": dby / tda / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                        "frac": dby / tda / 1e9 / HBM_PEAK_GBS},
+                                "algo_flops_per_launch": dfl, "algo_bytes_per_launch": dby}}
         out["secondary"] = sec
 
     if not args.no_cpu:

@@ -149,6 +149,23 @@ ssd_status ssd_chunk_scan_bwd(const ssd_fwd_desc* desc, const void* X, const flo
                               void* dB, void* dC, float* dinitial_state, void* workspace,
                               size_t workspace_bytes, void* stream);
 
+/* The backward's da stage on its own (the dominant kernel of the backward):
+ * for each chunk c, with the state entering it states_in[b][c][h] and the
+ * adjoint adjoint_in[b][c][h] = dl/dS_t at the first step t of chunk c + 1
+ * (dfinal_state, or 0, for the last chunk), both fp32
+ * [batch][nchunks][nheads][headdim][dstate], and R = exp(a_t) adjoint_in
+ * (R = adjoint_in for the last chunk):
+ *   da_t = sum_{i>=t>j} exp(cs_i - cs_j)(dY_i.X_j)(C_i.B_j)
+ *        + sum_{i>=t} exp(cs_i) dY_i.(S_in C_i) + sum_{j<t} exp(Lam - cs_j) X_j.(R B_j)
+ *        + exp(Lam) <R, S_in>
+ * over the chunk's steps (cs the chunk's prefix sums of a, Lam its total).
+ * This equals da of ssd_chunk_scan_bwd when the states are the true ones.
+ * Shapes and supported sizes as for ssd_chunk_scan_bwd; da must not overlap
+ * an input. */
+ssd_status ssd_bwd_da(const ssd_fwd_desc* desc, const void* X, const float* a, const void* B,
+                      const void* C, const void* dY, const float* states_in,
+                      const float* adjoint_in, float* da, void* stream);
+
 /* ---- Stage entry points (the same kernels' building blocks, exposed so
  * each stage can be checked and timed on its own).  bf16 MFMA path only,
  * except ssd_chunk_cumsum which takes any dtype descriptor.  Stages 3-5 work

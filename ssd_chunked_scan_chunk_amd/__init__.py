@@ -21,7 +21,7 @@ from . import _lib
 from ._lib import (SSD_ALGO_AUTO, SSD_ALGO_MFMA, SSD_ALGO_VALU, SSD_BF16, SSD_F32,
                    SSDError)
 
-__all__ = ["chunk_scan_fwd", "chunk_scan_bwd", "bwd_workspace_bytes", "step", "chunk_cumsum", "chunk_state", "state_passing",
+__all__ = ["chunk_scan_fwd", "chunk_scan_bwd", "bwd_workspace_bytes", "bwd_da", "step", "chunk_cumsum", "chunk_state", "state_passing",
            "chunk_scan", "fwd_plan", "workspace_bytes", "SSDError", "SSD_ALGO_AUTO",
            "SSD_ALGO_MFMA", "SSD_ALGO_VALU", "library_path"]
 
@@ -133,6 +133,18 @@ def chunk_scan_bwd(X, a, B, C, dY, chunk, initial_state=None, dfinal_state=None,
         _ptr(dfinal_state), _ptr(dX), _ptr(da), _ptr(dB), _ptr(dC), _ptr(dS0), _ptr(workspace),
         wsz, _stream(dev)))
     return {"dX": dX, "da": da, "dB": dB, "dC": dC, "dinitial_state": dS0}
+
+
+def bwd_da(X, a, B, C, dY, chunk, states_in, adjoint_in, da=None):
+    """The backward's da stage alone, from the states entering each chunk and
+    the adjoint dl/dS at the first step of each next chunk (dS_fin for the
+    last), both [Bz, nchunks, H, P, N] float32."""
+    d = _desc(X, B, chunk, SSD_ALGO_AUTO, 0)
+    if da is None:
+        da = torch.empty_like(a)
+    _lib.check(_L().ssd_bwd_da(ctypes.byref(d), _ptr(X), _ptr(a), _ptr(B), _ptr(C), _ptr(dY),
+                               _ptr(states_in), _ptr(adjoint_in), _ptr(da), _stream(X.device)))
+    return da
 
 
 def step(state, x, a, B, C, y=None):

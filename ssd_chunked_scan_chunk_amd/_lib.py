@@ -28,7 +28,7 @@ EXPORTS = (
     "ssd_fwd_workspace_bytes", "ssd_fwd_plan", "ssd_chunk_scan_fwd", "ssd_step",
     "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan",
     "ssd_status_str", "ssd_last_error", "ssd_version", "ssd_bwd_workspace_bytes",
-    "ssd_chunk_scan_bwd",
+    "ssd_chunk_scan_bwd", "ssd_bwd_da",
 )
 
 
@@ -77,9 +77,10 @@ def load(path: str = LIB_PATH):
     lib.ssd_chunk_scan.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp]
     lib.ssd_bwd_workspace_bytes.argtypes = [pd, ctypes.POINTER(sz)]
     lib.ssd_chunk_scan_bwd.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.ssd_bwd_da.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     for f in ("ssd_fwd_workspace_bytes", "ssd_fwd_plan", "ssd_chunk_scan_fwd", "ssd_step",
               "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan",
-              "ssd_bwd_workspace_bytes", "ssd_chunk_scan_bwd"):
+              "ssd_bwd_workspace_bytes", "ssd_chunk_scan_bwd", "ssd_bwd_da"):
         getattr(lib, f).restype = ctypes.c_int
     lib.ssd_status_str.argtypes = [ctypes.c_int]
     lib.ssd_status_str.restype = ctypes.c_char_p

@@ -668,7 +668,7 @@ ssd_status ssd_chunk_scan_bwd(const ssd_fwd_desc* desc, const void* X, const flo
     if (dinitial_state)
         SSD_TRY(ssd::launch_scale_state_by_a0(dinitial_state, a, Bz, L, H, PN, hs), "bwd: dS0");
     // 4. da from the chunk-local four-term form
-    SSD_TRY(ssd::launch_bwd_da(s, X, dY, a, B, C, F(W_SFW), F(W_SREV), da, hs), "bwd: da");
+    SSD_TRY(ssd::launch_bwd_da(s, X, dY, a, B, C, F(W_SFW), F(W_SREV), true, da, hs), "bwd: da");
     if (bp.xg) {
         // 5-6. dC = S^T dy and dB = G^T x: the products with the state's two
         // dimensions exchanged (headdim 64 over the state's 64-wide column
@@ -709,6 +709,34 @@ ssd_status ssd_chunk_scan_bwd(const ssd_fwd_desc* desc, const void* X, const flo
     if (st != SSD_OK) return st;
     SSD_TRY(ssd::launch_group_sum(dB, V(W_DBH), Bz, L, Lp, Lp - 1, -1, H, G, N, hs), "bwd: dB group sum");
 #undef SSD_TRY
+    return ok();
+}
+
+ssd_status ssd_bwd_da(const ssd_fwd_desc* desc, const void* X, const float* a, const void* B,
+                      const void* C, const void* dY, const float* states_in,
+                      const float* adjoint_in, float* da, void* stream) {
+    BwdPlan bp;
+    ssd_status st = make_bwd_plan(desc, &bp);
+    if (st != SSD_OK) return st;
+    const ssd::FwdShape& s = bp.s;
+    if (s.Bz == 0 || s.L == 0) return ok();
+    if (!X || !a || !B || !C || !dY || !states_in || !adjoint_in || !da)
+        return fail(SSD_ERR_NULL, "X, a, B, C, dY, states_in, adjoint_in and da are required");
+    const void* v16[] = {X, B, C, dY, states_in, adjoint_in};
+    for (const void* q : v16)
+        if (!aligned(q, 16)) return fail(SSD_ERR_ALIGN, "X, B, C, dY and the state arrays must be 16-byte aligned");
+    if (!aligned(a, 4) || !aligned(da, 4)) return fail(SSD_ERR_ALIGN, "a / da misaligned");
+    const int64_t nX = s.Bz * s.L * s.H * s.P * 2, nBC = s.Bz * s.L * s.G * s.N * 2;
+    const int64_t nSt = s.Bz * s.nc * s.H * s.P * s.N * 4, nA = s.Bz * s.L * s.H * 4;
+    const Range ins[] = {rng("X", X, nX), rng("a", a, nA), rng("B", B, nBC), rng("C", C, nBC),
+                         rng("dY", dY, nX), rng("states_in", states_in, nSt),
+                         rng("adjoint_in", adjoint_in, nSt)};
+    const Range o = rng("da", da, nA);
+    for (const Range& r : ins)
+        if (overlap(o, r)) return fail(SSD_ERR_ALIAS, "da overlaps %s", r.name);
+    hipError_t e = ssd::launch_bwd_da(s, X, dY, a, B, C, states_in, adjoint_in, false, da,
+                                      reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "da launch");
     return ok();
 }
 

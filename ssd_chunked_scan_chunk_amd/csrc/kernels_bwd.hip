@@ -301,7 +301,7 @@ __global__ __launch_bounds__(kDaThreads) void k_bwd_da(
     const u16* __restrict__ X, const u16* __restrict__ dY, const float* __restrict__ a,
     const u16* __restrict__ Bm, const u16* __restrict__ Cm, const float* __restrict__ Sin,
     const float* __restrict__ Srev, float* __restrict__ da, int64_t L, int H, int G, int Q,
-    int64_t nc)
+    int64_t nc, int adj_reversed)
 {
     constexpr int XPR = P / 8, BPR = N / 8;   // 16-byte pieces per row
     constexpr int PN = P * N;
@@ -480,7 +480,7 @@ __global__ __launch_bounds__(kDaThreads) void k_bwd_da(
     // R = exp(a at the next chunk's first step) G there (dS_fin for the last
     // chunk), rounded to bf16 for the MFMA; their fp32 inner product on the way ----
     const float* Sc = Sin + (((int64_t)b * nc + c) * H + h) * PN;
-    const float* Rc = Srev + (((int64_t)b * nc + (nc - 1 - c)) * H + h) * PN;
+    const float* Rc = Srev + (((int64_t)b * nc + (adj_reversed ? nc - 1 - c : c)) * H + h) * PN;
     const float fR = c < nc - 1 ? expf(a[((int64_t)b * L + (c + 1) * Q) * H + h]) : 1.f;
     float dot = 0.f;
     for (int k0 = tid; k0 < PN / 8; k0 += kDaThreads * 2) {
@@ -618,14 +618,14 @@ bool bwd_da_supported(int64_t Q, int64_t P, int64_t N) {
 
 hipError_t launch_bwd_da(const FwdShape& s, const void* X, const void* dY, const float* a,
                          const void* B, const void* C, const float* Sin, const float* Srev,
-                         float* da, hipStream_t st)
+                         bool adj_reversed, float* da, hipStream_t st)
 {
     if (s.Bz == 0 || s.L == 0) return hipSuccess;
     const dim3 grid((unsigned)s.nc, (unsigned)s.H, (unsigned)s.Bz);
 #define SSD_LAUNCH_DA(PP, NN)                                                                    \
     hipLaunchKernelGGL((k_bwd_da<PP, NN>), grid, dim3(kDaThreads), 0, st, (const u16*)X,          \
                        (const u16*)dY, a, (const u16*)B, (const u16*)C, Sin, Srev, da, s.L,      \
-                       (int)s.H, (int)s.G, (int)s.Q, s.nc);
+                       (int)s.H, (int)s.G, (int)s.Q, s.nc, adj_reversed ? 1 : 0);
     if (s.P == 64 && s.N == 128) SSD_LAUNCH_DA(64, 128)
     else if (s.P == 64 && s.N == 64) SSD_LAUNCH_DA(64, 64)
     else if (s.P == 32 && s.N == 128) SSD_LAUNCH_DA(32, 128)

@@ -97,12 +97,13 @@ hipError_t launch_group_sum(void* out, const void* in, int64_t Bz, int64_t Lout,
 hipError_t launch_scale_state_by_a0(float* state, const float* a, int64_t Bz, int64_t L,
                                     int64_t H, int64_t PN, hipStream_t st);
 // da from the chunk-entering states Sin [Bz][nc][H][P][N] of the forward and
-// the entering states Srev [Bz][nc][H][P][N] of the time-reversed adjoint
-// problem (slot k: the adjoint at the first step of forward chunk nc - k).
+// the right adjoints Srev [Bz][nc][H][P][N]: the adjoint at the first step of
+// chunk c + 1 (dS_fin for the last chunk) in slot c, or in slot nc - 1 - c
+// when adj_reversed (the order of the time-reversed problem's chunk states).
 bool bwd_da_supported(int64_t Q, int64_t P, int64_t N);
 hipError_t launch_bwd_da(const FwdShape& s, const void* X, const void* dY, const float* a,
                          const void* B, const void* C, const float* Sin, const float* Srev,
-                         float* da, hipStream_t st);
+                         bool adj_reversed, float* da, hipStream_t st);
 
 // zero-fill (used for empty sequences: final state = 0)
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);

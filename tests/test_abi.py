@@ -171,3 +171,16 @@ def test_bwd_validation(lib):
     # an empty batch is a no-op that needs nothing
     assert lib.ssd_bwd_workspace_bytes(ctypes.byref(desc(batch=0)), ctypes.byref(n)) == 0 and n.value == 0
     assert bwd(lib, desc(batch=0), X=None, dY=None) == 0
+
+
+def test_bwd_da_stage_validation(lib):
+    call = lambda d, *p: lib.ssd_bwd_da(ctypes.byref(d), *p, None)
+    F = [ctypes.c_void_p(1 << k) for k in (20, 24, 26, 28, 30, 32, 34)]
+    out = ctypes.c_void_p(1 << 36)
+    assert call(desc(dtype=_lib.SSD_F32), *F, out) == _lib.SSD_ERR_UNSUPPORTED
+    assert call(desc(chunk=32), *F, out) == _lib.SSD_ERR_UNSUPPORTED
+    assert call(desc(), None, *F[1:], out) == _lib.SSD_ERR_NULL
+    assert call(desc(), *F, None) == _lib.SSD_ERR_NULL
+    assert call(desc(), *F[:5], ctypes.c_void_p((1 << 32) + 8), F[6], out) == _lib.SSD_ERR_ALIGN
+    assert call(desc(), *F, F[6]) == _lib.SSD_ERR_ALIAS
+    assert call(desc(batch=0), None, None, None, None, None, None, None, None) == 0

@@ -112,3 +112,52 @@ def test_bwd_long_many_chunks():
     # the chunk-state scans over many units and the per-chunk adjoint slots
     bwd_case(si.FwdShape(1, 64 * 64 - 21, 3, 64, 64, 1, 64, si.BF16, dt_recipe="mamba2_dt"),
              seed=12, tag="many-chunks")
+
+
+def _chunk_states_and_adjoints(w, dY, dSf, Q):
+    """fp64 states entering each chunk and the adjoint dl/dS at the first step
+    of each next chunk (dS_fin for the last), by the recurrence and its adjoint
+    written out step by step (small shapes only)."""
+    X, a, B, C, S0 = w["X"], w["a"], w["B"], w["C"], w.get("S0")
+    Bz, L, H, P = X.shape
+    G, N = B.shape[2], B.shape[3]
+    nc = (L + Q - 1) // Q
+    Sin = np.zeros((Bz, nc, H, P, N))
+    Adj = np.zeros((Bz, nc, H, P, N))
+    for b in range(Bz):
+        for h in range(H):
+            g = h * G // H
+            s = S0[b, h].copy() if S0 is not None else np.zeros((P, N))
+            for t in range(L):
+                if t % Q == 0:
+                    Sin[b, t // Q, h] = s
+                s = np.exp(a[b, t, h]) * s + np.outer(X[b, t, h], B[b, t, g])
+            gst = dSf[b, h].copy()
+            for t in range(L - 1, -1, -1):
+                gst = np.outer(dY[b, t, h], C[b, t, g]) + (np.exp(a[b, t + 1, h]) * gst if t + 1 < L else gst)
+                if t % Q == 0 and t > 0:
+                    Adj[b, t // Q - 1, h] = gst
+            Adj[b, nc - 1, h] = dSf[b, h]
+    return Sin, Adj
+
+
+@pytest.mark.parametrize("Q,P,N", [(64, 64, 128), (128, 32, 64)])
+def test_bwd_da_stage(Q, P, N):
+    # the da kernel on its own, fed exact chunk states, against the oracle's da
+    sh = si.FwdShape(2, 2 * Q + 29, 3, P, N, 1, Q, si.BF16)
+    log("da stage %s" % (sh,))
+    d = si.make_fwd(sh, seed=21, with_initial_state=True)
+    u = si.make_upstream_grads(sh, seed=21)
+    w = widen_fwd(d)
+    dY = si.widen(u["dY"], sh.dtype)
+    dSf = u["dS_fin"].astype(np.float64)
+    Sin, Adj = _chunk_states_and_adjoints(w, dY, dSf, Q)
+    g = upload_fwd(d)
+    da = ssd.bwd_da(g["X"], g["a"], g["B"], g["C"], dev_tensor(u["dY"], sh.dtype), Q,
+                    torch.from_numpy(Sin.astype(np.float32)).cuda(),
+                    torch.from_numpy(Adj.astype(np.float32)).cuda())
+    torch.cuda.synchronize()
+    ref = oracle.bwd(w["X"], w["a"], w["B"], w["C"], dY, S0=w["S0"], dS_fin=dSf)
+    e = slice_rel_err(host_f64(da), ref["da"], (0, 2))
+    log("   err da=%.3e" % e)
+    assert e <= TOL[sh.dtype], e
