@@ -316,10 +316,12 @@ ssd_status make_bwd_plan(const ssd_fwd_desc* d, BwdPlan* bp) {
                     SSD_ALGO_AUTO, 0};
     ssd_fwd_desc db = dc;
     db.seqlen = bp->sr.L;
-    st = make_plan(&dc, &bp->pc);
-    if (st != SSD_OK) return st;
-    st = make_plan(&db, &bp->pb);
-    if (st != SSD_OK) return st;
+    if (!bp->xg) {   // (the in-place exchanged-dimension passes need no plan of their own)
+        st = make_plan(&dc, &bp->pc);
+        if (st != SSD_OK) return st;
+        st = make_plan(&db, &bp->pb);
+        if (st != SSD_OK) return st;
+    }
     const int64_t Bz = s.Bz, L = s.L, Lp = bp->sr.L, H = s.H, G = s.G, P = s.P, N = s.N;
     const int64_t nc = s.nc, PN = P * N, ns = bp->ns;
     int64_t bytes[kBwdBufs] = {};
