@@ -297,6 +297,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only time the decode step (batch 256, 80 heads; for profiling)")
     ap.add_argument("--bwd-only", action="store_true",
                     help="only time the backward of the 130M-shaped layer (for profiling)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -324,6 +326,12 @@ def main():
 
     sh = si.FWD_CONFIGS["m2_130m"]
     tokens = sh.batch * sh.seqlen
+    if args.decode_only:
+        td, nbytes = bench_decode(args.steps, args.warmup)
+        print(json.dumps({"decode_step": {"us_per_step": td * 1e6, "GB_per_s": nbytes / td / 1e9,
+                                          "hbm_frac": nbytes / td / 1e9 / HBM_PEAK_GBS,
+                                          "bytes_per_step": nbytes}}))
+        return
     if args.bwd_only:
         tb, tda = bench_backward(sh, args.steps, args.warmup, 2)
         fl = tokens * bwd_algo_flops_per_token(sh)
