@@ -159,6 +159,24 @@ def make_upstream_grads(shape: FwdShape, seed: int = 0):
     return {"dY": dY, "dS_fin": dSf}
 
 
+def make_integer_grads_case(shape: FwdShape, seed: int = 0):
+    """Decay-free integer inputs for exactness checks: a = 0, X, B, C, dY with
+    entries in {-1, 0, 1} (exact in bf16), S0 and dS_fin with integer entries
+    in [-2, 2].  Every product and partial sum the layer and its gradients form
+    is then a small integer."""
+    rng = np.random.default_rng(seed)
+    Bz, L, H, P = shape.batch, shape.seqlen, shape.nheads, shape.headdim
+    G, N = shape.ngroups, shape.dstate
+    tern = lambda *sz: rng.integers(-1, 2, size=sz).astype(np.float32)
+    out = {"X": _store(tern(Bz, L, H, P), shape.dtype), "a": np.zeros((Bz, L, H), np.float32),
+           "B": _store(tern(Bz, L, G, N), shape.dtype), "C": _store(tern(Bz, L, G, N), shape.dtype),
+           "shape": shape}
+    out["S0"] = rng.integers(-2, 3, size=(Bz, H, P, N)).astype(np.float32)
+    out["dY"] = _store(tern(Bz, L, H, P), shape.dtype)
+    out["dS_fin"] = rng.integers(-2, 3, size=(Bz, H, P, N)).astype(np.float32)
+    return out
+
+
 def make_decode(shape: StepShape, seed: int = 0, steps: Optional[int] = None):
     """Draw a decode run: state cache [Bz,H,P,N] f32 and per-step inputs
     x [T,Bz,H,P], a [T,Bz,H], B/C [T,Bz,G,N]."""

@@ -161,3 +161,55 @@ def test_bwd_da_stage(Q, P, N):
     e = slice_rel_err(host_f64(da), ref["da"], (0, 2))
     log("   err da=%.3e" % e)
     assert e <= TOL[sh.dtype], e
+
+
+def _integer_case(sh, seed):
+    d = si.make_integer_grads_case(sh, seed=seed)
+    w = widen_fwd(d)
+    dY = si.widen(d["dY"], sh.dtype)
+    dSf = d["dS_fin"].astype(np.float64)
+    ref = oracle.bwd(w["X"], w["a"], w["B"], w["C"], dY, S0=w["S0"], dS_fin=dSf)
+    return d, w, dY, dSf, ref
+
+
+@pytest.mark.parametrize("Q,P,N", [(64, 64, 128), (128, 32, 64)])
+def test_bwd_da_stage_exact(Q, P, N):
+    # zero decay and entries in {-1, 0, 1}: every product and sum in the da
+    # kernel is an exact small integer (the states stay below 256 in magnitude,
+    # so their bf16 operands are exact too), so da must equal the oracle's
+    # exactly -- a check of every mask, tile and index of the kernel
+    sh = si.FwdShape(2, 2 * Q + 29, 3, P, N, 1, Q, si.BF16)
+    log("exact da stage %s" % (sh,))
+    d, w, dY, dSf, ref = _integer_case(sh, 31)
+    Sin, Adj = _chunk_states_and_adjoints(w, dY, dSf, Q)
+    assert np.abs(Sin).max() < 256 and np.abs(Adj).max() < 256
+    g = upload_fwd(d)
+    da = ssd.bwd_da(g["X"], g["a"], g["B"], g["C"], dev_tensor(d["dY"], sh.dtype), Q,
+                    torch.from_numpy(Sin.astype(np.float32)).cuda(),
+                    torch.from_numpy(Adj.astype(np.float32)).cuda())
+    torch.cuda.synchronize()
+    got = host_f64(da)
+    log("   max |da| %.0f, max abs error %.3g" % (np.abs(ref["da"]).max(), np.abs(got - ref["da"]).max()))
+    assert np.array_equal(got, ref["da"])
+
+
+def test_bwd_exact_decay_free():
+    # the whole backward on the same kind of inputs: da is exact (its states
+    # come from the chunk-state passes, exact on integers), the bf16 outputs
+    # are within the bf16 tolerance
+    sh = si.FwdShape(2, 3 * 64 + 17, 4, 64, 128, 2, 64, si.BF16)
+    log("exact backward %s" % (sh,))
+    d, w, dY, dSf, ref = _integer_case(sh, 32)
+    g = upload_fwd(d)
+    out = ssd.chunk_scan_bwd(g["X"], g["a"], g["B"], g["C"], dev_tensor(d["dY"], sh.dtype), sh.chunk,
+                             initial_state=g["S0"], dfinal_state=dev_tensor(d["dS_fin"], si.F32),
+                             return_dinitial_state=True)
+    torch.cuda.synchronize()
+    got = host_f64(out["da"])
+    log("   max |da| %.0f, max abs error %.3g" % (np.abs(ref["da"]).max(), np.abs(got - ref["da"]).max()))
+    assert np.array_equal(got, ref["da"])
+    for k, k2 in (("dX", "dX"), ("dB", "dB"), ("dC", "dC")):
+        e = slice_rel_err(host_f64(out[k]), ref[k2], (0, 2))
+        log("   %s err %.3e" % (k, e))
+        assert e <= TOL[sh.dtype], (k, e)
+    assert state_err(host_f64(out["dinitial_state"]), ref["dS0"]) <= TOL[sh.dtype]

@@ -99,3 +99,27 @@ def test_step_deterministic_and_resumable():
         y3 = ssd.step(st, g1["x"][t], g1["a"][t], g1["B"][t], g1["C"][t])
     torch.cuda.synchronize()
     assert torch.equal(st, g1["state"]) and torch.equal(y3, y1)
+
+
+def test_decode_exact_decay_free():
+    # a = 0 and ternary x, B, C with an integer state: every step's update is an
+    # exact small-integer fp32 sum, so the state is exact and y is the exact
+    # value rounded once to bf16
+    import ssd_inputs as si
+    rng = np.random.default_rng(51)
+    Bz, H, P, N, G, T = 3, 4, 64, 128, 2, 20
+    tern = lambda *sz: rng.integers(-1, 2, size=sz).astype(np.float32)
+    st = rng.integers(-3, 4, size=(Bz, H, P, N)).astype(np.float32)
+    state = torch.from_numpy(st).cuda()
+    ref = st.astype(np.float64)
+    for t in range(T):
+        x, B, C = tern(Bz, H, P), tern(Bz, G, N), tern(Bz, G, N)
+        a = np.zeros((Bz, H), np.float32)
+        bf = lambda v: torch.from_numpy(si.f32_to_bf16_bits(v)).view(torch.bfloat16).cuda()
+        y = ssd.step(state, bf(x), torch.from_numpy(a).cuda(), bf(B), bf(C))
+        ref, yr = oracle.step(ref, x.astype(np.float64), a.astype(np.float64), B.astype(np.float64),
+                              C.astype(np.float64))
+        torch.cuda.synchronize()
+        yr_bf16 = si.widen(si.f32_to_bf16_bits(yr.astype(np.float32)), si.BF16)
+        assert np.array_equal(y.float().cpu().numpy().astype(np.float64), yr_bf16), t
+    assert np.array_equal(state.cpu().numpy().astype(np.float64), ref)

@@ -204,3 +204,27 @@ def test_deterministic():
     Y2, S2 = ssd.chunk_scan_fwd(g["X"], g["a"], g["B"], g["C"], 256, return_final_state=True, seg_chunks=2)
     torch.cuda.synchronize()
     assert torch.equal(Y1, Y2) and torch.equal(S1, S2)
+
+
+@pytest.mark.parametrize("Q,P,N,G,seg", [(256, 64, 128, 1, 1), (128, 64, 64, 2, 0), (64, 32, 128, 1, 2),
+                                         (128, 32, 64, 3, 1)])
+def test_fwd_exact_decay_free(Q, P, N, G, seg):
+    # zero decay and entries in {-1, 0, 1}: the scores, the states (below 256
+    # here) and every fp32 sum are exact small integers, so Y must equal the
+    # exact result rounded once to bf16 and the final state must be exact --
+    # a check of every mask, tile, scale and index of the MFMA path
+    H = 6 if G == 3 else 4
+    sh = si.FwdShape(2, 3 * Q + 37, H, P, N, G, Q, si.BF16)
+    log("exact fwd %s seg=%d" % (sh, seg))
+    d = si.make_integer_grads_case(sh, seed=41 + Q + P)
+    g = upload_fwd(d)
+    Y, S = ssd.chunk_scan_fwd(g["X"], g["a"], g["B"], g["C"], Q, initial_state=g["S0"],
+                              return_final_state=True, algo=ssd.SSD_ALGO_MFMA, seg_chunks=seg)
+    torch.cuda.synchronize()
+    w = widen_fwd(d)
+    Yr, Sr = oracle.fwd(w["X"], w["a"], w["B"], w["C"], S0=w["S0"])
+    assert np.abs(Sr).max() < 256
+    Yr_bf16 = si.widen(si.f32_to_bf16_bits(Yr.astype(np.float32)), si.BF16)
+    log("   max |Y| %.0f, max |S| %.0f" % (np.abs(Yr).max(), np.abs(Sr).max()))
+    assert np.array_equal(host_f64(Y), Yr_bf16)
+    assert np.array_equal(host_f64(S), Sr)
