@@ -213,3 +213,12 @@ def test_bwd_exact_decay_free():
         log("   %s err %.3e" % (k, e))
         assert e <= TOL[sh.dtype], (k, e)
     assert state_err(host_f64(out["dinitial_state"]), ref["dS0"]) <= TOL[sh.dtype]
+
+
+@pytest.mark.parametrize("with_s0,with_dsf", [(True, False), (False, True)])
+def test_bwd_one_group_per_head(with_s0, with_dsf):
+    # G = H: each head reads its own B and C (the exchanged-dimension passes
+    # then read B / C per head); initial state and final-state gradient each
+    # present without the other
+    bwd_case(si.FwdShape(2, 2 * 128 + 45, 4, 64, 128, 4, 128, si.BF16), seed=13 + with_s0,
+             with_s0=with_s0, with_dsf=with_dsf, tag="G=H")
