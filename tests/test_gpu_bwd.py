@@ -193,26 +193,34 @@ def test_bwd_da_stage_exact(Q, P, N):
     assert np.array_equal(got, ref["da"])
 
 
-def test_bwd_exact_decay_free():
-    # the whole backward on the same kind of inputs: da is exact (its states
-    # come from the chunk-state passes, exact on integers), the bf16 outputs
-    # are within the bf16 tolerance
-    sh = si.FwdShape(2, 3 * 64 + 17, 4, 64, 128, 2, 64, si.BF16)
+@pytest.mark.parametrize("G", [2, 4])
+def test_bwd_exact_decay_free(G):
+    # the whole backward on the same kind of inputs.  Its states and adjoints
+    # stay below 256, so every bf16 operand inside is exact and every sum an
+    # exact integer: da and the initial-state gradient must be exact, dX the
+    # exact value rounded once to bf16; with one head per group (G = H) so must
+    # dB and dC (otherwise they are rounded per head before the group sum)
+    sh = si.FwdShape(2, 3 * 64 + 17, 4, 64, 128, G, 64, si.BF16)
     log("exact backward %s" % (sh,))
-    d, w, dY, dSf, ref = _integer_case(sh, 32)
+    d, w, dY, dSf, ref = _integer_case(sh, 33)
     g = upload_fwd(d)
     out = ssd.chunk_scan_bwd(g["X"], g["a"], g["B"], g["C"], dev_tensor(d["dY"], sh.dtype), sh.chunk,
                              initial_state=g["S0"], dfinal_state=dev_tensor(d["dS_fin"], si.F32),
                              return_dinitial_state=True)
     torch.cuda.synchronize()
-    got = host_f64(out["da"])
-    log("   max |da| %.0f, max abs error %.3g" % (np.abs(ref["da"]).max(), np.abs(got - ref["da"]).max()))
-    assert np.array_equal(got, ref["da"])
-    for k, k2 in (("dX", "dX"), ("dB", "dB"), ("dC", "dC")):
-        e = slice_rel_err(host_f64(out[k]), ref[k2], (0, 2))
-        log("   %s err %.3e" % (k, e))
-        assert e <= TOL[sh.dtype], (k, e)
-    assert state_err(host_f64(out["dinitial_state"]), ref["dS0"]) <= TOL[sh.dtype]
+    bf = lambda v: si.widen(si.f32_to_bf16_bits(v.astype(np.float32)), si.BF16)
+    log("   max |da| %.0f, max |dX| %.0f" % (np.abs(ref["da"]).max(), np.abs(ref["dX"]).max()))
+    assert np.array_equal(host_f64(out["da"]), ref["da"])
+    assert np.array_equal(host_f64(out["dinitial_state"]), ref["dS0"])
+    assert np.array_equal(host_f64(out["dX"]), bf(ref["dX"]))
+    for k in ("dB", "dC"):
+        got = host_f64(out[k])
+        if G == sh.nheads:
+            assert np.array_equal(got, bf(ref[k])), k
+        else:
+            e = slice_rel_err(got, ref[k], (0, 2))
+            log("   %s err %.3e" % (k, e))
+            assert e <= TOL[sh.dtype], (k, e)
 
 
 @pytest.mark.parametrize("with_s0,with_dsf", [(True, False), (False, True)])
