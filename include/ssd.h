@@ -131,10 +131,13 @@ ssd_status ssd_step(const ssd_step_desc* desc, float* state, const void* x, cons
  * (the reverse-mode derivative of the 1-semiseparable product that the
  * CiteArk page of "Transformers are SSMs", section "AI research summary",
  * names; the page's mention of training optimisations is what it serves).
- * bf16 inputs only, chunk in {64,128,256}, headdim in {32,64}, dstate in
- * {64,128}; desc->algo must be AUTO or MFMA and seg_chunks is ignored.
+ * bf16 inputs: chunk in {64,128,256}, headdim in {32,64}, dstate in {64,128}
+ * (MFMA kernels; desc->algo AUTO or MFMA).  fp32 inputs: every shape the fp32
+ * forward takes with nheads*headdim, ngroups*dstate and dstate multiples of
+ * 4 (VALU kernels in fp32; desc->algo AUTO or VALU).  seg_chunks is ignored.
  * Reads X, a, B, C, initial_state (NULL = zero) and dY, dfinal_state (NULL =
- * zero); writes dX, dB, dC (bf16, rounded once from fp32 sums), da (fp32)
+ * zero); writes dX, dB, dC (in the inputs' dtype; bf16 rounded once from fp32
+ * sums, except that dB and dC sum their per-head bf16 contributions), da (fp32)
  * and, if dinitial_state != NULL, that gradient (fp32).  No output may
  * overlap an input, another output or the workspace.  The workspace holds
  * the per-chunk forward states and the adjoint's per-chunk states plus

@@ -280,7 +280,9 @@ struct BwdPlan {
     ssd::FwdShape s;   // the layer
     ssd::FwdShape sr;  // the reversed problem: seqlen padded to whole chunks
     int64_t ns;        // the dB / dC passes split the state dimension into ns head-dims of 64
-    bool xg;           // headdim 64: dB / dC read B, C, a and the chunk states in place
+    bool xg;           // bf16, headdim 64: dB / dC read B, C, a and the chunk states in place
+    bool f32;          // fp32 inputs: VALU kernels throughout
+    int64_t es;        // element bytes of X, B, C and the gradients
     Plan pc, pb;       // plans of the dC and dB passes (otherwise)
     size_t off[kBwdBufs + 1];
 };
@@ -288,31 +290,42 @@ struct BwdPlan {
 ssd_status make_bwd_plan(const ssd_fwd_desc* d, BwdPlan* bp) {
     ssd_status st = check_desc(d, true);
     if (st != SSD_OK) return st;
-    if (d->dtype != SSD_BF16)
-        return fail(SSD_ERR_UNSUPPORTED, "the backward is compiled for bf16 inputs only");
-    if (d->algo == SSD_ALGO_VALU)
-        return fail(SSD_ERR_UNSUPPORTED, "the backward has no VALU variant");
     const ssd::FwdShape s = shape_of(d);
-    if (!ssd::mfma_supported(s.Q, s.P, s.N) || !ssd::bwd_da_supported(s.Q, s.P, s.N))
-        return fail(SSD_ERR_UNSUPPORTED,
-                    "no backward kernels for chunk=%lld headdim=%lld dstate=%lld "
-                    "(chunk in {64,128,256}, headdim in {32,64}, dstate in {64,128})",
-                    (long long)s.Q, (long long)s.P, (long long)s.N);
+    bp->f32 = d->dtype == SSD_F32;
+    bp->es = bp->f32 ? 4 : 2;
+    if (bp->f32) {
+        // fp32: the VALU forward for every pass and the VALU da
+        if (!ssd::valu_fwd_supported(s) || (s.H * s.P) % 4 != 0 || (s.G * s.N) % 4 != 0 || s.N % 4 != 0)
+            return fail(SSD_ERR_UNSUPPORTED,
+                        "no fp32 backward for chunk=%lld headdim=%lld dstate=%lld (chunk <= 256, "
+                        "headdim*dstate <= 16384, nheads*headdim, ngroups*dstate and dstate multiples of 4)",
+                        (long long)s.Q, (long long)s.P, (long long)s.N);
+        if (d->algo == SSD_ALGO_MFMA)
+            return fail(SSD_ERR_UNSUPPORTED, "the MFMA backward needs bf16 inputs");
+    } else {
+        if (d->algo == SSD_ALGO_VALU)
+            return fail(SSD_ERR_UNSUPPORTED, "the bf16 backward has no VALU variant");
+        if (!ssd::mfma_supported(s.Q, s.P, s.N) || !ssd::bwd_da_supported(s.Q, s.P, s.N))
+            return fail(SSD_ERR_UNSUPPORTED,
+                        "no backward kernels for chunk=%lld headdim=%lld dstate=%lld "
+                        "(chunk in {64,128,256}, headdim in {32,64}, dstate in {64,128})",
+                        (long long)s.Q, (long long)s.P, (long long)s.N);
+    }
     if ((s.Bz * s.nc * s.H + 8) * 256 >= ((int64_t)1 << 32) || s.nc > 0x7fffffff)
         return fail(SSD_ERR_UNSUPPORTED, "batch*chunks*heads too large for one launch");
     // the copy kernels launch (row blocks of up to 256 threads) x steps blocks
-    const int64_t row_items = s.H * (s.N > s.P ? s.N : s.P) / 8;
+    const int64_t row_items = s.H * (s.N > s.P ? s.N : s.P) * bp->es / 16;
     if (s.nc * s.Q * (((row_items + 255) / 256) * 256) >= ((int64_t)1 << 31))
         return fail(SSD_ERR_UNSUPPORTED, "seqlen*nheads too large for the backward's copy kernels");
     bp->s = s;
     bp->sr = s;
     bp->sr.L = s.nc * s.Q;
-    bp->ns = s.N / 64;
-    bp->xg = s.P == 64;
+    bp->ns = bp->f32 ? 1 : s.N / 64;
+    bp->xg = !bp->f32 && s.P == 64;
     // dC: the forward-time product with x in the role of B, dy in that of C and
     // B (split into 64-wide pieces, one per sub-head) in that of X; dB: the same
     // on reversed time with dy as B, x as C and C as X
-    ssd_fwd_desc dc{s.Bz, s.L, s.H * bp->ns, s.N / bp->ns, s.P, s.H, s.Q, SSD_BF16,
+    ssd_fwd_desc dc{s.Bz, s.L, s.H * bp->ns, s.N / bp->ns, s.P, s.H, s.Q, d->dtype,
                     SSD_ALGO_AUTO, 0};
     ssd_fwd_desc db = dc;
     db.seqlen = bp->sr.L;
@@ -323,26 +336,26 @@ ssd_status make_bwd_plan(const ssd_fwd_desc* d, BwdPlan* bp) {
         if (st != SSD_OK) return st;
     }
     const int64_t Bz = s.Bz, L = s.L, Lp = bp->sr.L, H = s.H, G = s.G, P = s.P, N = s.N;
-    const int64_t nc = s.nc, PN = P * N, ns = bp->ns;
+    const int64_t nc = s.nc, PN = P * N, ns = bp->ns, es = bp->es;
     int64_t bytes[kBwdBufs] = {};
     if (Bz > 0 && L > 0) {
         bytes[W_SFW] = Bz * nc * H * PN * 4;
         bytes[W_LAMFW] = Bz * H * nc * 4;
         bytes[W_SREV] = bytes[W_SFW];
         bytes[W_LAMREV] = bytes[W_LAMFW];
-        bytes[W_DYR] = Bz * Lp * H * P * 2;
-        bytes[W_CR] = Bz * Lp * G * N * 2;
+        bytes[W_DYR] = Bz * Lp * H * P * es;
+        bytes[W_CR] = Bz * Lp * G * N * es;
         bytes[W_BR] = bytes[W_CR];
         bytes[W_AR] = Bz * Lp * H * 4;
         bytes[W_DXR] = bytes[W_DYR];
-        bytes[W_DCH] = Bz * L * H * N * 2;
+        bytes[W_DCH] = Bz * L * H * N * es;
         bytes[W_XR] = bytes[W_DYR];
-        bytes[W_DBH] = Bz * Lp * H * N * 2;
+        bytes[W_DBH] = Bz * Lp * H * N * es;
         if (!bp->xg) {
-            bytes[W_BEXP] = Bz * L * H * N * 2;
+            bytes[W_BEXP] = Bz * L * H * N * es;
             bytes[W_AEXP] = Bz * L * H * ns * 4;
             bytes[W_S0T] = Bz * H * PN * 4;
-            bytes[W_CREXP] = Bz * Lp * H * N * 2;
+            bytes[W_CREXP] = Bz * Lp * H * N * es;
             bytes[W_AREXP] = Bz * Lp * H * ns * 4;
             bytes[W_DSFT] = bytes[W_S0T];
             bytes[W_INNER] = (int64_t)(bp->pc.ws > bp->pb.ws ? bp->pc.ws : bp->pb.ws);
@@ -596,7 +609,7 @@ ssd_status ssd_chunk_scan_bwd(const ssd_fwd_desc* desc, const void* X, const flo
     if (st != SSD_OK) return st;
     const ssd::FwdShape& s = bp.s;
     const int64_t Bz = s.Bz, L = s.L, Lp = bp.sr.L, H = s.H, G = s.G, P = s.P, N = s.N;
-    const int64_t nc = s.nc, PN = P * N, ns = bp.ns;
+    const int64_t nc = s.nc, PN = P * N, ns = bp.ns, es = bp.es;
     const size_t need = bp.off[kBwdBufs];
     if (Bz == 0) return ok();
     if (L > 0 && (!X || !a || !B || !C || !dY || !dX || !da || !dB || !dC))
@@ -610,7 +623,7 @@ ssd_status ssd_chunk_scan_bwd(const ssd_fwd_desc* desc, const void* X, const flo
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(SSD_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need, workspace_bytes,
                     workspace ? "" : ", NULL");
-    const int64_t nX = Bz * L * H * P * 2, nBC = Bz * L * G * N * 2, nA = Bz * L * H * 4, nS = Bz * H * PN * 4;
+    const int64_t nX = Bz * L * H * P * es, nBC = Bz * L * G * N * es, nA = Bz * L * H * 4, nS = Bz * H * PN * 4;
     const Range ins[] = {rng("X", X, nX), rng("a", a, nA), rng("B", B, nBC), rng("C", C, nBC),
                          rng("initial_state", initial_state, initial_state ? nS : 0),
                          rng("dY", dY, nX), rng("dfinal_state", dfinal_state, dfinal_state ? nS : 0)};
@@ -641,6 +654,24 @@ ssd_status ssd_chunk_scan_bwd(const ssd_fwd_desc* desc, const void* X, const flo
         e = (expr);                                          \
         if (e != hipSuccess) return hip_fail(e, what);       \
     } while (0)
+    if (bp.f32) {
+        // fp32: the VALU forward gives the chunk states (and, on the reversed
+        // problem, dX, G_0 and the adjoint's chunk states in one pass); the
+        // rest follows the bf16 path's plan with VALU kernels
+        SSD_TRY(ssd::launch_valu_fwd(s, false, X, a, B, C, initial_state, nullptr, nullptr, hs, F(W_SFW)),
+                "bwd: chunk states");
+        SSD_TRY(ssd::launch_remap_rows(V(W_DYR), dY, Bz, Lp, L, Lp - 1, -1, H * P * es, hs), "bwd: reverse dY");
+        SSD_TRY(ssd::launch_remap_rows(V(W_CR), C, Bz, Lp, L, Lp - 1, -1, G * N * es, hs), "bwd: reverse C");
+        SSD_TRY(ssd::launch_remap_rows(V(W_BR), B, Bz, Lp, L, Lp - 1, -1, G * N * es, hs), "bwd: reverse B");
+        SSD_TRY(ssd::launch_remap_a(F(W_AR), a, Bz, Lp, L, Lp, -1, H, 1, hs), "bwd: reverse a");
+        SSD_TRY(ssd::launch_valu_fwd(bp.sr, false, V(W_DYR), F(W_AR), V(W_CR), V(W_BR), dfinal_state,
+                                     V(W_DXR), dinitial_state, hs, F(W_SREV)), "bwd: dX pass");
+        SSD_TRY(ssd::launch_remap_rows(dX, V(W_DXR), Bz, L, Lp, Lp - 1, -1, H * P * es, hs), "bwd: dX order");
+        if (dinitial_state)
+            SSD_TRY(ssd::launch_scale_state_by_a0(dinitial_state, a, Bz, L, H, PN, hs), "bwd: dS0");
+        SSD_TRY(ssd::launch_bwd_da_valu(s, (const float*)X, (const float*)dY, a, (const float*)B,
+                                        (const float*)C, F(W_SFW), F(W_SREV), da, hs), "bwd: da");
+    } else {
     // 1. the state entering every forward chunk
     SSD_TRY(ssd::launch_mfma_state(s, 1, nc - 1, nc, X, a, B, F(W_SFW), F(W_LAMFW), hs), "bwd: chunk states");
     SSD_TRY(ssd::launch_state_scan(s, nc - 1, nc, F(W_SFW), F(W_LAMFW), H * nc, nc, initial_state,
@@ -650,9 +681,9 @@ ssd_status ssd_chunk_scan_bwd(const ssd_fwd_desc* desc, const void* X, const flo
     // (padded at its start to whole chunks, so that reversed chunks coincide
     // with forward ones), with the decay of reversed step t' = a at forward
     // step Lp - t' (zero where that is past the end)
-    SSD_TRY(ssd::launch_remap_rows(V(W_DYR), dY, Bz, Lp, L, Lp - 1, -1, H * P * 2, hs), "bwd: reverse dY");
-    SSD_TRY(ssd::launch_remap_rows(V(W_CR), C, Bz, Lp, L, Lp - 1, -1, G * N * 2, hs), "bwd: reverse C");
-    SSD_TRY(ssd::launch_remap_rows(V(W_BR), B, Bz, Lp, L, Lp - 1, -1, G * N * 2, hs), "bwd: reverse B");
+    SSD_TRY(ssd::launch_remap_rows(V(W_DYR), dY, Bz, Lp, L, Lp - 1, -1, H * P * es, hs), "bwd: reverse dY");
+    SSD_TRY(ssd::launch_remap_rows(V(W_CR), C, Bz, Lp, L, Lp - 1, -1, G * N * es, hs), "bwd: reverse C");
+    SSD_TRY(ssd::launch_remap_rows(V(W_BR), B, Bz, Lp, L, Lp - 1, -1, G * N * es, hs), "bwd: reverse B");
     SSD_TRY(ssd::launch_remap_a(F(W_AR), a, Bz, Lp, L, Lp, -1, H, 1, hs), "bwd: reverse a");
     // 3. dX = G B, with G the state of the reversed problem (dy as X, C as B,
     // B as C, dS_fin as its initial state); its final state is G_0
@@ -666,11 +697,12 @@ ssd_status ssd_chunk_scan_bwd(const ssd_fwd_desc* desc, const void* X, const flo
         SSD_TRY(ssd::launch_mfma_out(bp.sr, 1, nc, V(W_DYR), F(W_AR), V(W_CR), V(W_BR), src, V(W_DXR),
                                      dinitial_state, hs), "bwd: dX pass");
     }
-    SSD_TRY(ssd::launch_remap_rows(dX, V(W_DXR), Bz, L, Lp, Lp - 1, -1, H * P * 2, hs), "bwd: dX order");
+    SSD_TRY(ssd::launch_remap_rows(dX, V(W_DXR), Bz, L, Lp, Lp - 1, -1, H * P * es, hs), "bwd: dX order");
     if (dinitial_state)
         SSD_TRY(ssd::launch_scale_state_by_a0(dinitial_state, a, Bz, L, H, PN, hs), "bwd: dS0");
     // 4. da from the chunk-local four-term form
     SSD_TRY(ssd::launch_bwd_da(s, X, dY, a, B, C, F(W_SFW), F(W_SREV), true, da, hs), "bwd: da");
+    }
     if (bp.xg) {
         // 5-6. dC = S^T dy and dB = G^T x: the products with the state's two
         // dimensions exchanged (headdim 64 over the state's 64-wide column
@@ -681,35 +713,35 @@ ssd_status ssd_chunk_scan_bwd(const ssd_fwd_desc* desc, const void* X, const flo
         sc.H = H * ns; sc.P = 64; sc.N = P; sc.G = H;
         ssd::StateSrc srcc{initial_state, H * PN, F(W_SFW), nc * H * PN, H * PN};
         SSD_TRY(ssd::launch_mfma_out_xg(sc, G, B, a, X, dY, srcc, V(W_DCH), hs), "bwd: dC pass");
-        SSD_TRY(ssd::launch_group_sum(dC, V(W_DCH), Bz, L, L, 0, 1, H, G, N, hs), "bwd: dC group sum");
+        SSD_TRY(ssd::launch_group_sum(dC, V(W_DCH), Bz, L, L, 0, 1, H, G, N, true, hs), "bwd: dC group sum");
         ssd::FwdShape sb = sc;
         sb.L = Lp;
-        SSD_TRY(ssd::launch_remap_rows(V(W_XR), X, Bz, Lp, L, Lp - 1, -1, H * P * 2, hs), "bwd: reverse X");
+        SSD_TRY(ssd::launch_remap_rows(V(W_XR), X, Bz, Lp, L, Lp - 1, -1, H * P * es, hs), "bwd: reverse X");
         ssd::StateSrc srcb{dfinal_state, H * PN, F(W_SREV), nc * H * PN, H * PN};
         SSD_TRY(ssd::launch_mfma_out_xg(sb, G, V(W_CR), F(W_AR), V(W_DYR), V(W_XR), srcb, V(W_DBH), hs),
                 "bwd: dB pass");
-        SSD_TRY(ssd::launch_group_sum(dB, V(W_DBH), Bz, L, Lp, Lp - 1, -1, H, G, N, hs), "bwd: dB group sum");
+        SSD_TRY(ssd::launch_group_sum(dB, V(W_DBH), Bz, L, Lp, Lp - 1, -1, H, G, N, true, hs), "bwd: dB group sum");
         return ok();
     }
     // 5. dC = S^T dy: forward-time product, state dimensions exchanged
-    SSD_TRY(ssd::launch_bcast_heads(V(W_BEXP), B, Bz, L, L, 0, 1, H, G, N, hs), "bwd: B per head");
+    SSD_TRY(ssd::launch_bcast_heads(V(W_BEXP), B, Bz, L, L, 0, 1, H, G, N * es, hs), "bwd: B per head");
     SSD_TRY(ssd::launch_remap_a(F(W_AEXP), a, Bz, L, L, 0, 1, H, ns, hs), "bwd: a per sub-head");
     if (initial_state)
         SSD_TRY(ssd::launch_state_transpose(F(W_S0T), initial_state, Bz * H, P, N, hs), "bwd: S0^T");
     st = run_fwd(bp.pc, V(W_BEXP), F(W_AEXP), X, dY, initial_state ? F(W_S0T) : nullptr, V(W_DCH),
                  nullptr, V(W_INNER), hs);
     if (st != SSD_OK) return st;
-    SSD_TRY(ssd::launch_group_sum(dC, V(W_DCH), Bz, L, L, 0, 1, H, G, N, hs), "bwd: dC group sum");
+    SSD_TRY(ssd::launch_group_sum(dC, V(W_DCH), Bz, L, L, 0, 1, H, G, N, !bp.f32, hs), "bwd: dC group sum");
     // 6. dB = G^T x: reversed-time product, state dimensions exchanged
-    SSD_TRY(ssd::launch_bcast_heads(V(W_CREXP), C, Bz, Lp, L, Lp - 1, -1, H, G, N, hs), "bwd: C per head");
-    SSD_TRY(ssd::launch_remap_rows(V(W_XR), X, Bz, Lp, L, Lp - 1, -1, H * P * 2, hs), "bwd: reverse X");
+    SSD_TRY(ssd::launch_bcast_heads(V(W_CREXP), C, Bz, Lp, L, Lp - 1, -1, H, G, N * es, hs), "bwd: C per head");
+    SSD_TRY(ssd::launch_remap_rows(V(W_XR), X, Bz, Lp, L, Lp - 1, -1, H * P * es, hs), "bwd: reverse X");
     SSD_TRY(ssd::launch_remap_a(F(W_AREXP), a, Bz, Lp, L, Lp, -1, H, ns, hs), "bwd: reverse a per sub-head");
     if (dfinal_state)
         SSD_TRY(ssd::launch_state_transpose(F(W_DSFT), dfinal_state, Bz * H, P, N, hs), "bwd: dS_fin^T");
     st = run_fwd(bp.pb, V(W_CREXP), F(W_AREXP), V(W_DYR), V(W_XR), dfinal_state ? F(W_DSFT) : nullptr,
                  V(W_DBH), nullptr, V(W_INNER), hs);
     if (st != SSD_OK) return st;
-    SSD_TRY(ssd::launch_group_sum(dB, V(W_DBH), Bz, L, Lp, Lp - 1, -1, H, G, N, hs), "bwd: dB group sum");
+    SSD_TRY(ssd::launch_group_sum(dB, V(W_DBH), Bz, L, Lp, Lp - 1, -1, H, G, N, !bp.f32, hs), "bwd: dB group sum");
 #undef SSD_TRY
     return ok();
 }
@@ -720,6 +752,7 @@ ssd_status ssd_bwd_da(const ssd_fwd_desc* desc, const void* X, const float* a, c
     BwdPlan bp;
     ssd_status st = make_bwd_plan(desc, &bp);
     if (st != SSD_OK) return st;
+    if (bp.f32) return fail(SSD_ERR_UNSUPPORTED, "the da stage entry point runs the bf16 MFMA kernel");
     const ssd::FwdShape& s = bp.s;
     if (s.Bz == 0 || s.L == 0) return ok();
     if (!X || !a || !B || !C || !dY || !states_in || !adjoint_in || !da)

@@ -98,35 +98,47 @@ __global__ void k_state_transpose(float* __restrict__ out, const float* __restri
     }
 }
 
-// sum over each group's heads (fp32), rounded once, 8 elements per thread:
-// out[b][t][g][n] = sum_{h in g} in[b][s][h][n]
+// sum over each group's heads in fp32 (bf16 rounded once), one 16-byte
+// piece per thread: out[b][t][g][n] = sum_{h in g} in[b][s][h][n]
+template <typename T>
 __global__ void k_group_sum(uint4* __restrict__ out, const uint4* __restrict__ in, int64_t Lout,
-                            int64_t Lin, int64_t off, int64_t dir, int H, int G, int N8, int nbx)
+                            int64_t Lin, int64_t off, int64_t dir, int H, int G, int N16, int nbx)
 {
+    constexpr int E = 16 / sizeof(T);   // elements per piece
     const int64_t t = blockIdx.x / nbx, b = blockIdx.y;
     const int k = (int)(blockIdx.x - t * nbx) * blockDim.x + threadIdx.x;
-    if (k >= G * N8) return;
-    const int gi = k / N8, q = k - gi * N8;
+    if (k >= G * N16) return;
+    const int gi = k / N16, q = k - gi * N16;
     const int hpg = H / G;
     const int64_t s = off + dir * t;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = 0.f;
     if (s >= 0 && s < Lin) {
-        const uint4* src = in + ((b * Lin + s) * H + (int64_t)gi * hpg) * N8 + q;
+        const uint4* src = in + ((b * Lin + s) * H + (int64_t)gi * hpg) * N16 + q;
         for (int j = 0; j < hpg; ++j) {
-            const uint4 v = src[(int64_t)j * N8];
+            const uint4 v = src[(int64_t)j * N16];
             const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                acc[2 * e] += __uint_as_float(w[e] << 16);
-                acc[2 * e + 1] += __uint_as_float(w[e] & 0xffff0000u);
+                if constexpr (E == 8) {
+                    acc[2 * e] += __uint_as_float(w[e] << 16);
+                    acc[2 * e + 1] += __uint_as_float(w[e] & 0xffff0000u);
+                } else {
+                    acc[e] += __uint_as_float(w[e]);
+                }
             }
         }
     }
     uint32_t o[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-        o[e] = (uint32_t)f32_to_bf_bits(acc[2 * e]) | ((uint32_t)f32_to_bf_bits(acc[2 * e + 1]) << 16);
-    out[(b * Lout + t) * G * N8 + k] = make_uint4(o[0], o[1], o[2], o[3]);
+    for (int e = 0; e < 4; ++e) {
+        if constexpr (E == 8)
+            o[e] = (uint32_t)f32_to_bf_bits(acc[2 * e]) | ((uint32_t)f32_to_bf_bits(acc[2 * e + 1]) << 16);
+        else
+            o[e] = __float_as_uint(acc[e]);
+    }
+    out[(b * Lout + t) * G * N16 + k] = make_uint4(o[0], o[1], o[2], o[3]);
 }
 
 // st[b][h][:] *= exp(a[b][0][h])
@@ -163,10 +175,10 @@ hipError_t launch_remap_rows(void* out, const void* in, int64_t Bz, int64_t Lout
 }
 
 hipError_t launch_bcast_heads(void* out, const void* in, int64_t Bz, int64_t Lout, int64_t Lin,
-                              int64_t off, int64_t dir, int64_t H, int64_t G, int64_t N,
+                              int64_t off, int64_t dir, int64_t H, int64_t G, int64_t row_bytes,
                               hipStream_t st)
 {
-    const int64_t N8 = N * 2 / 16;
+    const int64_t N8 = row_bytes / 16;
     if (Bz * Lout * H * N8 <= 0) return hipSuccess;
     hipLaunchKernelGGL(k_bcast_heads, row_grid(H * N8, Lout, Bz), dim3(row_threads(H * N8)), 0, st,
                        (uint4*)out, (const uint4*)in, Lout, Lin, off, dir, (int)H, (int)G, (int)N8,
@@ -194,14 +206,18 @@ hipError_t launch_state_transpose(float* out, const float* in, int64_t BH, int64
 }
 
 hipError_t launch_group_sum(void* out, const void* in, int64_t Bz, int64_t Lout, int64_t Lin,
-                            int64_t off, int64_t dir, int64_t H, int64_t G, int64_t N,
+                            int64_t off, int64_t dir, int64_t H, int64_t G, int64_t N, bool bf16,
                             hipStream_t st)
 {
-    const int64_t w = G * (N / 8);
+    const int64_t N16 = N * (bf16 ? 2 : 4) / 16, w = G * N16;
     if (Bz * Lout * w <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_group_sum, row_grid(w, Lout, Bz), dim3(row_threads(w)), 0, st, (uint4*)out,
-                       (const uint4*)in, Lout, Lin, off, dir, (int)H, (int)G, (int)(N / 8),
-                       row_blocks(w));
+    if (bf16)
+        hipLaunchKernelGGL(k_group_sum<u16>, row_grid(w, Lout, Bz), dim3(row_threads(w)), 0, st, (uint4*)out,
+                           (const uint4*)in, Lout, Lin, off, dir, (int)H, (int)G, (int)N16, row_blocks(w));
+    else
+        hipLaunchKernelGGL(k_group_sum<float>, row_grid(w, Lout, Bz), dim3(row_threads(w)), 0, st,
+                           (uint4*)out, (const uint4*)in, Lout, Lin, off, dir, (int)H, (int)G, (int)N16,
+                           row_blocks(w));
     return hipGetLastError();
 }
 
@@ -610,6 +626,129 @@ __global__ __launch_bounds__(kDaThreads) void k_bwd_da(
     __syncthreads();
     if (t < Lc)
         da[((int64_t)b * L + t0 + t) * H + h] = sDg[t] + rsuf + cpre + kT + sT2[t] + t3pre + t4;
+}
+
+// ---------------------------------------------------------------------------
+// da on VALUs in fp32 (fp32 inputs): the same four-term decomposition, the
+// masked term from the row prefix sums T_i(t) = sum_{j < min(t, i)} M_ij of
+// 64-row blocks held in LDS, summed per t over i >= t in a fixed order.  One
+// workgroup per (chunk, head, batch); a plain, slow path for the fp32 layer.
+// ---------------------------------------------------------------------------
+constexpr int kDaValuRows = 64;
+
+__global__ __launch_bounds__(256) void k_bwd_da_valu(
+    const float* __restrict__ X, const float* __restrict__ dY, const float* __restrict__ a,
+    const float* __restrict__ Bm, const float* __restrict__ Cm, const float* __restrict__ Sin,
+    const float* __restrict__ Srev, float* __restrict__ da, int64_t L, int H, int G, int P, int N,
+    int Q, int64_t nc)
+{
+    extern __shared__ float sm[];
+    float* sCs = sm;                        // [Q] prefix sums of a in the chunk
+    float* sT = sCs + Q;                    // [kDaValuRows][Q] row prefix sums of a row block
+    float* sD = sT + kDaValuRows * Q;       // [Q] masked term
+    float* sT2 = sD + Q;                    // [Q] entering-state term per step
+    float* sT3 = sT2 + Q;                   // [Q] right-adjoint term per step
+    float* sRed = sT3 + Q;                  // [4]
+    const int64_t c = blockIdx.x;
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int g = h / (H / G);
+    const int tid = threadIdx.x;
+    const int64_t t0 = c * Q;
+    const int Lc = (int)((L - t0 < Q) ? (L - t0) : Q);
+    const int64_t PN = (int64_t)P * N;
+    auto xrow = [&](int i) { return X + (((int64_t)b * L + t0 + i) * H + h) * P; };
+    auto dyrow = [&](int i) { return dY + (((int64_t)b * L + t0 + i) * H + h) * P; };
+    auto brow = [&](int i) { return Bm + (((int64_t)b * L + t0 + i) * G + g) * N; };
+    auto crow = [&](int i) { return Cm + (((int64_t)b * L + t0 + i) * G + g) * N; };
+
+    const float av = tid < Lc ? a[((int64_t)b * L + t0 + tid) * H + h] : 0.f;
+    const float cs = block_inclusive_scan(av, sRed, (Q + 63) / 64);
+    if (tid < Q) { sCs[tid] = cs; sD[tid] = 0.f; }
+    __syncthreads();
+    const float Lam = sCs[Lc - 1];
+
+    // masked term: sum over {i >= t > j} of exp(cs_i - cs_j)(dy_i.x_j)(C_i.B_j).
+    // Row i first holds M_ij for j < i, its decay exp(a_{j+1} + ... + a_i)
+    // accumulated term by term from the diagonal down (no difference of two
+    // prefix sums), then the row is turned into its exclusive prefix sums.
+    for (int i0 = 0; i0 < Lc; i0 += kDaValuRows) {
+        const int i = i0 + tid;
+        if (tid < kDaValuRows && i < Lc) {
+            float* row = sT + tid * Q;
+            float seg = 0.f;
+            for (int j = i - 1; j >= 0; --j) {
+                seg += a[((int64_t)b * L + t0 + j + 1) * H + h];
+                float dx = 0.f, cb = 0.f;
+                for (int p = 0; p < P; ++p) dx += dyrow(i)[p] * xrow(j)[p];
+                for (int n = 0; n < N; ++n) cb += crow(i)[n] * brow(j)[n];
+                row[j] = expf(seg) * dx * cb;
+            }
+            float run = 0.f;
+            for (int t = 0; t < Q; ++t) {
+                const float m = t < i ? row[t] : 0.f;
+                row[t] = run;
+                run += m;
+            }
+        }
+        __syncthreads();
+        if (tid < Lc) {
+            float acc = 0.f;
+            for (int k = 0; k < kDaValuRows && i0 + k < Lc; ++k)
+                if (i0 + k >= tid) acc += sT[k * Q + tid];
+            sD[tid] += acc;
+        }
+        __syncthreads();
+    }
+
+    // the entering state S_in and the adjoint from the right R = exp(a_next) G_next
+    // (slot nc - 1 - c of the reversed problem's chunk states; dS_fin last)
+    const float* Sc = Sin + (((int64_t)b * nc + c) * H + h) * PN;
+    const float* Rc = Srev + (((int64_t)b * nc + (nc - 1 - c)) * H + h) * PN;
+    const float fR = c < nc - 1 ? expf(a[((int64_t)b * L + (c + 1) * Q) * H + h]) : 1.f;
+    if (tid < Lc) {
+        const int i = tid;
+        float t2 = 0.f, t3 = 0.f;
+        for (int p = 0; p < P; ++p) {
+            float sc = 0.f, rb = 0.f;
+            for (int n = 0; n < N; ++n) {
+                sc += Sc[(int64_t)p * N + n] * crow(i)[n];
+                rb += Rc[(int64_t)p * N + n] * brow(i)[n];
+            }
+            t2 += dyrow(i)[p] * sc;
+            t3 += xrow(i)[p] * rb;
+        }
+        sT2[i] = expf(sCs[i]) * t2;
+        sT3[i] = fR * expf(Lam - sCs[i]) * t3;
+    }
+    float dot = 0.f;
+    for (int64_t k = tid; k < PN; k += 256) dot += Sc[k] * Rc[k];
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) dot += __shfl_xor(dot, d, 64);
+    __syncthreads();
+    if ((tid & 63) == 0) sRed[tid >> 6] = dot;
+    __syncthreads();
+    const float t4 = fR * expf(Lam) * (sRed[0] + sRed[1] + sRed[2] + sRed[3]);
+    if (tid < Lc) {
+        float v = sD[tid] + t4;
+        for (int i = tid; i < Lc; ++i) v += sT2[i];
+        for (int j = 0; j < tid; ++j) v += sT3[j];
+        da[((int64_t)b * L + t0 + tid) * H + h] = v;
+    }
+}
+
+hipError_t launch_bwd_da_valu(const FwdShape& s, const float* X, const float* dY, const float* a,
+                              const float* B, const float* C, const float* Sin, const float* Srev,
+                              float* da, hipStream_t st)
+{
+    if (s.Bz == 0 || s.L == 0) return hipSuccess;
+    const size_t lds = (size_t)((kDaValuRows + 4) * s.Q + 4) * sizeof(float);
+    hipError_t e = hipFuncSetAttribute((const void*)k_bwd_da_valu, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_bwd_da_valu, dim3((unsigned)s.nc, (unsigned)s.H, (unsigned)s.Bz), dim3(256), lds, st,
+                       X, dY, a, B, C, Sin, Srev, da, s.L, (int)s.H, (int)s.G, (int)s.P, (int)s.N, (int)s.Q,
+                       s.nc);
+    return hipGetLastError();
 }
 
 bool bwd_da_supported(int64_t Q, int64_t P, int64_t N) {

@@ -25,11 +25,14 @@ namespace ssd {
 // ---------------------------------------------------------------------------
 constexpr int kValuThreads = 256;
 
+// Y may be null (only the states are wanted); S_chunks (optional) receives
+// the state entering every chunk, [Bz][nc][H][P*N].
 template <typename T>
 __global__ __launch_bounds__(kValuThreads) void k_valu_fwd(
     const T* __restrict__ X, const float* __restrict__ a, const T* __restrict__ B,
     const T* __restrict__ C, const float* __restrict__ S0, T* __restrict__ Y,
-    float* __restrict__ S_fin, int64_t L, int H, int P, int N, int G, int Q)
+    float* __restrict__ S_fin, float* __restrict__ S_chunks, int64_t L, int H, int P, int N,
+    int G, int Q)
 {
     extern __shared__ float smem[];
     float* sA = smem;           // [Q] a of the chunk
@@ -55,9 +58,12 @@ __global__ __launch_bounds__(kValuThreads) void k_valu_fwd(
         const float cs = block_inclusive_scan(av, sTot, (Q + 63) / 64);
         if (tid < Q) sCs[tid] = cs;
         __syncthreads();
+        if (S_chunks)
+            for (int k = tid; k < PN; k += kValuThreads)
+                S_chunks[(((int64_t)b * nc + c) * H + h) * PN + k] = sS[k];
 
         // outputs of the chunk: intra-chunk masked product + carried state
-        for (int idx = tid; idx < Lc * P; idx += kValuThreads) {
+        for (int idx = tid; Y && idx < Lc * P; idx += kValuThreads) {
             const int i = idx / P, p = idx - i * P;
             const T* Ci = C + (((int64_t)b * L + t0 + i) * G + g) * N;
             float acc = 0.f, seg = 0.f;
@@ -98,7 +104,7 @@ bool valu_fwd_supported(const FwdShape& s) {
 
 hipError_t launch_valu_fwd(const FwdShape& s, bool bf16, const void* X, const float* a,
                            const void* B, const void* C, const float* S0, void* Y,
-                           float* S_fin, hipStream_t st)
+                           float* S_fin, hipStream_t st, float* S_chunks)
 {
     const size_t lds = (size_t)(2 * s.Q + s.P * s.N + 4) * sizeof(float);
     dim3 grid((unsigned)s.H, (unsigned)s.Bz);
@@ -107,15 +113,15 @@ hipError_t launch_valu_fwd(const FwdShape& s, bool bf16, const void* X, const fl
         hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(k, grid, dim3(kValuThreads), lds, st, (const u16*)X, a, (const u16*)B,
-                           (const u16*)C, S0, (u16*)Y, S_fin, s.L, (int)s.H, (int)s.P, (int)s.N,
-                           (int)s.G, (int)s.Q);
+                           (const u16*)C, S0, (u16*)Y, S_fin, S_chunks, s.L, (int)s.H, (int)s.P,
+                           (int)s.N, (int)s.G, (int)s.Q);
     } else {
         auto k = k_valu_fwd<float>;
         hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(k, grid, dim3(kValuThreads), lds, st, (const float*)X, a, (const float*)B,
-                           (const float*)C, S0, (float*)Y, S_fin, s.L, (int)s.H, (int)s.P, (int)s.N,
-                           (int)s.G, (int)s.Q);
+                           (const float*)C, S0, (float*)Y, S_fin, S_chunks, s.L, (int)s.H,
+                           (int)s.P, (int)s.N, (int)s.G, (int)s.Q);
     }
     return hipGetLastError();
 }

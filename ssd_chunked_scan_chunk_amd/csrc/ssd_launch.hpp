@@ -22,9 +22,11 @@ struct StateSrc {
 };
 
 // ---- VALU path (any dtype; fp32 arithmetic, exact segment sums) -------------
+// Y may be null; S_chunks (optional) receives the state entering every chunk
+// [Bz][nc][H][P][N].
 hipError_t launch_valu_fwd(const FwdShape& s, bool bf16, const void* X, const float* a,
                            const void* B, const void* C, const float* S0, void* Y,
-                           float* S_fin, hipStream_t st);
+                           float* S_fin, hipStream_t st, float* S_chunks = nullptr);
 bool valu_fwd_supported(const FwdShape& s);
 
 // ---- stage 1: in-chunk prefix sums ---------------------------------------------
@@ -79,9 +81,10 @@ hipError_t launch_step(int64_t Bz, int64_t H, int64_t P, int64_t N, int64_t G, b
 // rows of row_bytes (a multiple of 16): out[b][t][:] = in[b][s][:]
 hipError_t launch_remap_rows(void* out, const void* in, int64_t Bz, int64_t Lout, int64_t Lin,
                              int64_t off, int64_t dir, int64_t row_bytes, hipStream_t st);
-// bf16 B or C per head: out[b][t][h][:] = in[b][s][h / (H/G)][:] (N a multiple of 8)
+// B or C per head: out[b][t][h][:] = in[b][s][h / (H/G)][:] (rows of row_bytes, a
+// multiple of 16)
 hipError_t launch_bcast_heads(void* out, const void* in, int64_t Bz, int64_t Lout, int64_t Lin,
-                              int64_t off, int64_t dir, int64_t H, int64_t G, int64_t N,
+                              int64_t off, int64_t dir, int64_t H, int64_t G, int64_t row_bytes,
                               hipStream_t st);
 // out[b][t][h * ns + k] = a[b][s][h]
 hipError_t launch_remap_a(float* out, const float* a, int64_t Bz, int64_t Lout, int64_t Lin,
@@ -89,9 +92,10 @@ hipError_t launch_remap_a(float* out, const float* a, int64_t Bz, int64_t Lout, 
 // out[bh][n][p] = in[bh][p][n]
 hipError_t launch_state_transpose(float* out, const float* in, int64_t BH, int64_t P, int64_t N,
                                   hipStream_t st);
-// bf16 out[b][t][g][n] = sum over the group's heads of bf16 in[b][s][h][n] (fp32 sum)
+// out[b][t][g][n] = sum over the group's heads of in[b][s][h][n] (fp32 sum; bf16 or
+// fp32 elements, N * element size a multiple of 16 bytes)
 hipError_t launch_group_sum(void* out, const void* in, int64_t Bz, int64_t Lout, int64_t Lin,
-                            int64_t off, int64_t dir, int64_t H, int64_t G, int64_t N,
+                            int64_t off, int64_t dir, int64_t H, int64_t G, int64_t N, bool bf16,
                             hipStream_t st);
 // state[b][h][:] *= exp(a[b][0][h])
 hipError_t launch_scale_state_by_a0(float* state, const float* a, int64_t Bz, int64_t L,
@@ -101,6 +105,10 @@ hipError_t launch_scale_state_by_a0(float* state, const float* a, int64_t Bz, in
 // chunk c + 1 (dS_fin for the last chunk) in slot c, or in slot nc - 1 - c
 // when adj_reversed (the order of the time-reversed problem's chunk states).
 bool bwd_da_supported(int64_t Q, int64_t P, int64_t N);
+// the fp32 VALU da (fp32 inputs), Srev in the reversed problem's slot order
+hipError_t launch_bwd_da_valu(const FwdShape& s, const float* X, const float* dY, const float* a,
+                              const float* B, const float* C, const float* Sin, const float* Srev,
+                              float* da, hipStream_t st);
 hipError_t launch_bwd_da(const FwdShape& s, const void* X, const void* dY, const float* a,
                          const void* B, const void* C, const float* Sin, const float* Srev,
                          bool adj_reversed, float* da, hipStream_t st);

@@ -152,9 +152,13 @@ def test_bwd_validation(lib):
     assert lib.ssd_bwd_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == 0
     # per-chunk forward and adjoint states at least
     assert n.value >= 2 * 2 * 2 * 4 * 64 * 128 * 4
-    # fp32, VALU-only, uncompiled shapes and chunks are rejected on the host
-    for kw in (dict(dtype=_lib.SSD_F32), dict(algo=_lib.SSD_ALGO_VALU), dict(headdim=48),
-               dict(chunk=32), dict(dstate=32)):
+    # the MFMA path forced on fp32, the VALU path forced on bf16, shapes without
+    # kernels are rejected on the host; fp32 itself is planned (VALU kernels)
+    nf = ctypes.c_size_t()
+    assert lib.ssd_bwd_workspace_bytes(ctypes.byref(desc(dtype=_lib.SSD_F32)), ctypes.byref(nf)) == 0
+    for kw in (dict(dtype=_lib.SSD_F32, algo=_lib.SSD_ALGO_MFMA), dict(algo=_lib.SSD_ALGO_VALU),
+               dict(headdim=48), dict(chunk=32), dict(dstate=32), dict(dtype=_lib.SSD_F32, chunk=512),
+               dict(dtype=_lib.SSD_F32, headdim=3, nheads=3)):
         assert lib.ssd_bwd_workspace_bytes(ctypes.byref(desc(**kw)), ctypes.byref(n)) == _lib.SSD_ERR_UNSUPPORTED
         assert bwd(lib, desc(**kw)) == _lib.SSD_ERR_UNSUPPORTED
     assert bwd(lib, desc(nheads=6, ngroups=4)) == _lib.SSD_ERR_SHAPE
@@ -163,6 +167,7 @@ def test_bwd_validation(lib):
     # a workspace is required, and outputs may not overlap inputs, each other or it
     assert bwd(lib, d) == _lib.SSD_ERR_WORKSPACE
     ws = ctypes.c_void_p(1 << 36)
+    assert lib.ssd_bwd_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == 0
     assert bwd(lib, d, ws=ws, wsz=n.value - 1) == _lib.SSD_ERR_WORKSPACE
     lib.ssd_bwd_workspace_bytes(ctypes.byref(d), ctypes.byref(n))
     assert bwd(lib, d, dX=FAKE, ws=ws, wsz=n.value) == _lib.SSD_ERR_ALIAS

@@ -230,3 +230,12 @@ def test_bwd_one_group_per_head(with_s0, with_dsf):
     # present without the other
     bwd_case(si.FwdShape(2, 2 * 128 + 45, 4, 64, 128, 4, 128, si.BF16), seed=13 + with_s0,
              with_s0=with_s0, with_dsf=with_dsf, tag="G=H")
+
+
+@pytest.mark.parametrize("shape", [si.FWD_CONFIGS["tiny_f32"],
+                                   si.FwdShape(2, 3 * 64 + 37, 4, 32, 32, 2, 64, si.F32),
+                                   si.FwdShape(1, 2 * 128 + 5, 2, 16, 64, 1, 128, si.F32)],
+                         ids=["tiny_f32", "ragged_G2", "Q128"])
+def test_bwd_f32(shape):
+    # the fp32 backward (VALU kernels throughout) at the fp32 tolerance
+    bwd_case(shape, seed=61, tag="f32")
