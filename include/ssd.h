@@ -143,7 +143,7 @@ ssd_status ssd_step(const ssd_step_desc* desc, float* state, const void* x, cons
  * the per-chunk forward states and the adjoint's per-chunk states plus
  * time-reversed copies of the operands (about
  * 2 * batch * nchunks * nheads * headdim * dstate * 4 bytes plus a few
- * sequence-sized bf16 arrays); its size comes from ssd_bwd_workspace_bytes
+ * sequence-sized arrays in the inputs' dtype); its size comes from ssd_bwd_workspace_bytes
  * and its contents on entry are ignored.  Errors as for ssd_chunk_scan_fwd. */
 ssd_status ssd_bwd_workspace_bytes(const ssd_fwd_desc* desc, size_t* bytes);
 ssd_status ssd_chunk_scan_bwd(const ssd_fwd_desc* desc, const void* X, const float* a,
