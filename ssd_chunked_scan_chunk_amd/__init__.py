@@ -1,4 +1,5 @@
-"""MI355X (gfx950) SSD layer: chunked forward and recurrent decode step.
+"""MI355X (gfx950) SSD layer: chunked forward, its backward, and the recurrent
+decode step.
 
 A thin torch binding over libssd.so's C ABI (include/ssd.h).  This module
 only marshals arguments -- checks devices/dtypes/contiguity, allocates
