@@ -239,3 +239,11 @@ def test_bwd_one_group_per_head(with_s0, with_dsf):
 def test_bwd_f32(shape):
     # the fp32 backward (VALU kernels throughout) at the fp32 tolerance
     bwd_case(shape, seed=61, tag="f32")
+
+
+@pytest.mark.parametrize("L,dtype", [(1, si.BF16), (1, si.F32), (65, si.BF16), (65, si.F32)])
+def test_bwd_one_step_tails(L, dtype):
+    # a single step, and a last chunk of one step: the reversed sequence is
+    # then almost all padding
+    P, N = (64, 64) if dtype == si.BF16 else (16, 32)
+    bwd_case(si.FwdShape(2, L, 3, P, N, 1, 64, dtype), seed=70 + L, tag="tail")
