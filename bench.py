@@ -284,10 +284,24 @@ def cpu_baseline(sh):
         if dt * threads >= 10.0 or dt >= 30.0:
             break
     tokens = sh.batch * sh.seqlen * reps
+    # one thread on one batch row (a bounded sample of the same work)
+    t1 = time.perf_counter()
+    oracle.fwd(w["X"][:1], a[:1], w["B"][:1], w["C"][:1], nthreads=1)
+    dt1 = time.perf_counter() - t1
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": "the full %dx%d-token batch (%d heads), %d times, through the sequential "
                       "fp64 recurrence with (batch, head) slices spread over %d threads; %.2f s wall"
-                      % (sh.batch, sh.seqlen, sh.nheads, reps, threads, dt)}
+                      % (sh.batch, sh.seqlen, sh.nheads, reps, threads, dt),
+            "single_thread_value": sh.seqlen / dt1, "single_thread_sample": "one batch row, one thread",
+            "cpu_model": model}
 
 
 def main():
