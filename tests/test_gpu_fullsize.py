@@ -60,3 +60,10 @@ def test_sweep_n64_512k_sampled():
     # the longest N=64 sweep point: batch 1, seqlen 524288, 32 heads, P=N=64
     sh = si.sweep_shape(524288)
     check_sampled(sh, 0, {0: [0, 17, 31]})
+
+
+@pytest.mark.parametrize("L", [32768, 131072])
+def test_sweep_n64_long_sampled(L):
+    # the remaining N=64 sweep points (their segment plans differ from the
+    # shorter ones checked in full): first, a middle and the last head
+    check_sampled(si.sweep_shape(L), 0, {0: [0, 15, 31]})
