@@ -247,3 +247,26 @@ def test_bwd_one_step_tails(L, dtype):
     # then almost all padding
     P, N = (64, 64) if dtype == si.BF16 else (16, 32)
     bwd_case(si.FwdShape(2, L, 3, P, N, 1, 64, dtype), seed=70 + L, tag="tail")
+
+
+@pytest.mark.parametrize("dtype", [si.BF16, si.F32])
+def test_bwd_workspace_contents_ignored(dtype):
+    # a workspace full of NaN bytes gives bit-for-bit the gradients of a zeroed
+    # one: no pass reads a workspace region it has not written
+    P, N = (64, 128) if dtype == si.BF16 else (16, 32)
+    sh = si.FwdShape(2, 2 * 64 + 19, 3, P, N, 1, 64, dtype)
+    d = si.make_fwd(sh, seed=81, with_initial_state=True)
+    u = si.make_upstream_grads(sh, seed=81)
+    g = upload_fwd(d)
+    dY = dev_tensor(u["dY"], dtype)
+    dSf = dev_tensor(u["dS_fin"], si.F32)
+    n = ssd.bwd_workspace_bytes(g["X"], g["B"], sh.chunk)
+    outs = []
+    for fill in (0, 0xFF):
+        ws = torch.full((n,), fill, dtype=torch.uint8, device="cuda")
+        outs.append(ssd.chunk_scan_bwd(g["X"], g["a"], g["B"], g["C"], dY, sh.chunk, g["S0"], dSf, True,
+                                       workspace=ws))
+    torch.cuda.synchronize()
+    for k in outs[0]:
+        assert torch.equal(outs[0][k], outs[1][k]), k
+        assert torch.isfinite(outs[1][k].float()).all(), k

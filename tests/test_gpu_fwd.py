@@ -228,3 +228,21 @@ def test_fwd_exact_decay_free(Q, P, N, G, seg):
     log("   max |Y| %.0f, max |S| %.0f" % (np.abs(Yr).max(), np.abs(Sr).max()))
     assert np.array_equal(host_f64(Y), Yr_bf16)
     assert np.array_equal(host_f64(S), Sr)
+
+
+def test_fwd_workspace_contents_ignored():
+    # segmented plan (its workspace holds segment states; slot 0 is neither
+    # written nor read): a workspace of NaN bytes gives the same Y and state
+    sh = si.FwdShape(2, 4 * 256 + 37, 6, 64, 128, 1, 256, si.BF16)
+    d = si.make_fwd(sh, seed=91, with_initial_state=True)
+    g = upload_fwd(d)
+    n = ssd.workspace_bytes(g["X"], g["B"], sh.chunk, seg_chunks=1)
+    assert n > 0
+    outs = []
+    for fill in (0, 0xFF):
+        ws = torch.full((n,), fill, dtype=torch.uint8, device="cuda")
+        outs.append(ssd.chunk_scan_fwd(g["X"], g["a"], g["B"], g["C"], sh.chunk, initial_state=g["S0"],
+                                       return_final_state=True, seg_chunks=1, workspace=ws))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    assert torch.isfinite(outs[1][0].float()).all()
