@@ -275,6 +275,12 @@ __device__ __forceinline__ uint32_t pack2b(float lo, float hi) {
     return (uint32_t)f32_to_bf_bits(lo) | ((uint32_t)f32_to_bf_bits(hi) << 16);
 }
 __device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+// two floats as bf16 high parts (hi) and the bf16 roundings of their remainders (lo)
+__device__ __forceinline__ void split2(float x, float y, uint32_t& hi, uint32_t& lo) {
+    const u16 hx = f32_to_bf_bits(x), hy = f32_to_bf_bits(y);
+    hi = (uint32_t)hx | ((uint32_t)hy << 16);
+    lo = pack2b(x - bf_bits_to_f32(hx), y - bf_bits_to_f32(hy));
+}
 __device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 // LDS writes and reads of this wavefront's other lanes complete and ordered
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
@@ -322,12 +328,12 @@ __global__ __launch_bounds__(kDaThreads) void k_bwd_da(
     constexpr int XPR = P / 8, BPR = N / 8;   // 16-byte pieces per row
     constexpr int PN = P * N;
     constexpr int kScr = 32 * 33;             // floats of one wave's scratch tile
-    constexpr int kUnion = kDaWaves * kScr * 4 > 2 * PN * 2 ? kDaWaves * kScr * 4 : 2 * PN * 2;
+    static_assert(4 * P <= kDaMaxQ, "the split states fit where B was");
     __shared__ __attribute__((aligned(16))) u16 sX[kDaMaxQ * P];
+    // B rows in the masked-term phase; the entering state and the right
+    // adjoint, each split into bf16 high and low parts, in the state phase
     __shared__ __attribute__((aligned(16))) u16 sB[kDaMaxQ * N];
-    // the masked-term phase uses this as per-wave scratch tiles, the state
-    // phase as the bf16 entering state and right adjoint
-    __shared__ __attribute__((aligned(16))) unsigned char sU[kUnion];
+    __shared__ __attribute__((aligned(16))) float sU[kDaWaves * kScr];   // per-wave scratch tiles
     __shared__ float sCs[kDaMaxQ], sDg[kDaMaxQ], sT2[kDaMaxQ], sT3[kDaMaxQ];
     __shared__ float sRS[2][kDaMaxQ];          // row sums left of the diagonal, per column parity
     __shared__ float sCS[kDaWaves][kDaMaxQ];   // column sums below the diagonal, per wave
@@ -343,9 +349,11 @@ __global__ __launch_bounds__(kDaThreads) void k_bwd_da(
     const int64_t t0 = c * Q;
     const int Lc = (int)((L - t0 < Q) ? (L - t0) : Q);
     const int nI = Q / 32;
-    float* scr = reinterpret_cast<float*>(sU) + wave * kScr;
-    u16* sS = reinterpret_cast<u16*>(sU);
-    u16* sR = sS + PN;
+    float* scr = sU + wave * kScr;
+    u16* sSh = sB;            // (state phase only)
+    u16* sSl = sB + PN;
+    u16* sRh = sB + 2 * PN;
+    u16* sRl = sB + 3 * PN;
 
     // ---- segment sums of the chunk (zero past a ragged end) ----
     const float av = tid < Lc ? a[((int64_t)b * L + t0 + tid) * H + h] : 0.f;
@@ -490,11 +498,14 @@ __global__ __launch_bounds__(kDaThreads) void k_bwd_da(
         }
         wave_lds_sync();
     }
-    __syncthreads();   // the scratch tiles are free
+    __syncthreads();   // B's LDS tile is free
 
     // ---- entering state S_in and the adjoint entering from the right,
     // R = exp(a at the next chunk's first step) G there (dS_fin for the last
-    // chunk), rounded to bf16 for the MFMA; their fp32 inner product on the way ----
+    // chunk), each split into bf16 high and low parts (v = hi + lo to about
+    // 2^-17) so that the state terms keep fp32-level accuracy (they can cancel
+    // against the fp32 term exp(Lam) <R, S_in>); their fp32 inner product on
+    // the way ----
     const float* Sc = Sin + (((int64_t)b * nc + c) * H + h) * PN;
     const float* Rc = Srev + (((int64_t)b * nc + (adj_reversed ? nc - 1 - c : c)) * H + h) * PN;
     const float fR = c < nc - 1 ? expf(a[((int64_t)b * L + (c + 1) * Q) * H + h]) : 1.f;
@@ -517,10 +528,19 @@ __global__ __launch_bounds__(kDaThreads) void k_bwd_da(
             const float4 s0 = sv[u][0], s1 = sv[u][1], r0 = rv[u][0], r1 = rv[u][1];
             dot += s0.x * r0.x + s0.y * r0.y + s0.z * r0.z + s0.w * r0.w +
                    s1.x * r1.x + s1.y * r1.y + s1.z * r1.z + s1.w * r1.w;
-            *reinterpret_cast<uint4*>(sS + dswz<BPR>(p, 8 * q)) =
-                make_uint4(pack2b(s0.x, s0.y), pack2b(s0.z, s0.w), pack2b(s1.x, s1.y), pack2b(s1.z, s1.w));
-            *reinterpret_cast<uint4*>(sR + dswz<BPR>(p, 8 * q)) =
-                make_uint4(pack2b(r0.x, r0.y), pack2b(r0.z, r0.w), pack2b(r1.x, r1.y), pack2b(r1.z, r1.w));
+            const float sv8[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+            const float rv8[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+            uint32_t shi[4], slo[4], rhi[4], rlo[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                split2(sv8[2 * e], sv8[2 * e + 1], shi[e], slo[e]);
+                split2(rv8[2 * e], rv8[2 * e + 1], rhi[e], rlo[e]);
+            }
+            const int o = dswz<BPR>(p, 8 * q);
+            *reinterpret_cast<uint4*>(sSh + o) = make_uint4(shi[0], shi[1], shi[2], shi[3]);
+            *reinterpret_cast<uint4*>(sSl + o) = make_uint4(slo[0], slo[1], slo[2], slo[3]);
+            *reinterpret_cast<uint4*>(sRh + o) = make_uint4(rhi[0], rhi[1], rhi[2], rhi[3]);
+            *reinterpret_cast<uint4*>(sRl + o) = make_uint4(rlo[0], rlo[1], rlo[2], rlo[3]);
         }
     }
     dot = block_sum(dot, sRed);   // (its barriers also publish the states above)
@@ -545,7 +565,10 @@ __global__ __launch_bounds__(kDaThreads) void k_bwd_da(
             for (int pt = 0; pt < P / 32; ++pt) {
                 f32x16_b U = zero16b();
 #pragma unroll
-                for (int ks = 0; ks < N / 16; ++ks) U = mfma32b(frag(sS, BP{}, 32 * pt + l32, ks), cf[ks], U);
+                for (int ks = 0; ks < N / 16; ++ks) {
+                    U = mfma32b(frag(sSh, BP{}, 32 * pt + l32, ks), cf[ks], U);
+                    U = mfma32b(frag(sSl, BP{}, 32 * pt + l32, ks), cf[ks], U);
+                }
 #pragma unroll
                 for (int hq = 0; hq < 2; ++hq) {
                     const int ks = 2 * pt + hq;
@@ -568,14 +591,28 @@ __global__ __launch_bounds__(kDaThreads) void k_bwd_da(
             if (lane < 32 && irow < Lc) sT2[irow] = expf(sCs[irow]) * acc;
         } else {
             // adjoint from the right dotted with x: exp(Lam - cs_j) x_j . (R B_j),
-            // from (R B^T) with rows p, column j = l32 of this tile
+            // from (R B^T) with rows p, column j = l32 of this tile (B rows
+            // from HBM / L2 now that B's LDS tile holds the states)
+            bf16x8 bq[N / 16];
+            {
+                const bool jok = irow < Lc;
+                const u16* brow = Bm + (((int64_t)b * L + t0 + irow) * G + g) * N + 8 * g2;
+#pragma unroll
+                for (int ks = 0; ks < N / 16; ++ks) {
+                    u32x4_b v = {0u, 0u, 0u, 0u};
+                    if (jok) v = *reinterpret_cast<const u32x4_b*>(brow + 16 * ks);
+                    bq[ks] = __builtin_bit_cast(bf16x8, v);
+                }
+            }
             float acc = 0.f;
 #pragma unroll
             for (int pt = 0; pt < P / 32; ++pt) {
                 f32x16_b V = zero16b();
 #pragma unroll
-                for (int ks = 0; ks < N / 16; ++ks)
-                    V = mfma32b(frag(sR, BP{}, 32 * pt + l32, ks), frag(sB, BP{}, irow, ks), V);
+                for (int ks = 0; ks < N / 16; ++ks) {
+                    V = mfma32b(frag(sRh, BP{}, 32 * pt + l32, ks), bq[ks], V);
+                    V = mfma32b(frag(sRl, BP{}, 32 * pt + l32, ks), bq[ks], V);
+                }
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const uint2 xv = *reinterpret_cast<const uint2*>(sX + dswz<XPR>(irow, 32 * pt + 8 * q + 4 * g2));
