@@ -133,11 +133,11 @@ ssd_status ssd_step(const ssd_step_desc* desc, float* state, const void* x, cons
  * names; the page's mention of training optimisations is what it serves).
  * bf16 inputs: chunk in {64,128,256}, headdim in {32,64}, dstate in {64,128}
  * (MFMA kernels; desc->algo AUTO or MFMA).  fp32 inputs: every shape the fp32
- * forward takes with nheads*headdim, ngroups*dstate and dstate multiples of
- * 4 (VALU kernels in fp32; desc->algo AUTO or VALU).  seg_chunks is ignored.
+ * forward takes with nheads*headdim a multiple of 4 and dstate a multiple of
+ * 8 (VALU kernels in fp32; desc->algo AUTO or VALU).  seg_chunks is ignored.
  * Reads X, a, B, C, initial_state (NULL = zero) and dY, dfinal_state (NULL =
  * zero); writes dX, dB, dC (in the inputs' dtype; bf16 rounded once from fp32
- * sums, except that dB and dC sum their per-head bf16 contributions), da (fp32)
+ * sums, dB and dC after summing the heads' fp32 contributions), da (fp32)
  * and, if dinitial_state != NULL, that gradient (fp32).  No output may
  * overlap an input, another output or the workspace.  The workspace holds
  * the per-chunk forward states and the adjoint's per-chunk states plus

@@ -223,7 +223,7 @@ ssd_status check_fwd_io(const Plan& p, const void* X, const float* a, const void
 // Enqueue the planned forward; every argument has been validated.
 ssd_status run_fwd(const Plan& p, const void* X, const float* a, const void* B, const void* C,
                    const float* initial_state, void* Y, float* final_state, void* workspace,
-                   hipStream_t hs) {
+                   hipStream_t hs, bool y_f32 = false) {
     const ssd::FwdShape& s = p.s;
     const int64_t PN = s.P * s.N;
     hipError_t e = hipSuccess;
@@ -236,8 +236,10 @@ ssd_status run_fwd(const Plan& p, const void* X, const float* a, const void* B, 
         }
         return ok();
     }
+    if (y_f32 && p.algo != SSD_ALGO_VALU)
+        return fail(SSD_ERR_UNSUPPORTED, "fp32 output from bf16 inputs needs the VALU kernel");
     if (p.algo == SSD_ALGO_VALU) {
-        e = ssd::launch_valu_fwd(s, p.bf16, X, a, B, C, initial_state, Y, final_state, hs);
+        e = ssd::launch_valu_fwd(s, p.bf16, X, a, B, C, initial_state, Y, final_state, hs, nullptr, y_f32);
         if (e != hipSuccess) return hip_fail(e, "VALU forward launch");
         return ok();
     }
@@ -295,10 +297,10 @@ ssd_status make_bwd_plan(const ssd_fwd_desc* d, BwdPlan* bp) {
     bp->es = bp->f32 ? 4 : 2;
     if (bp->f32) {
         // fp32: the VALU forward for every pass and the VALU da
-        if (!ssd::valu_fwd_supported(s) || (s.H * s.P) % 4 != 0 || (s.G * s.N) % 4 != 0 || s.N % 4 != 0)
+        if (!ssd::valu_fwd_supported(s) || (s.H * s.P) % 4 != 0 || s.N % 8 != 0)
             return fail(SSD_ERR_UNSUPPORTED,
                         "no fp32 backward for chunk=%lld headdim=%lld dstate=%lld (chunk <= 256, "
-                        "headdim*dstate <= 16384, nheads*headdim, ngroups*dstate and dstate multiples of 4)",
+                        "headdim*dstate <= 16384, nheads*headdim a multiple of 4, dstate of 8)",
                         (long long)s.Q, (long long)s.P, (long long)s.N);
         if (d->algo == SSD_ALGO_MFMA)
             return fail(SSD_ERR_UNSUPPORTED, "the MFMA backward needs bf16 inputs");
@@ -348,9 +350,12 @@ ssd_status make_bwd_plan(const ssd_fwd_desc* d, BwdPlan* bp) {
         bytes[W_BR] = bytes[W_CR];
         bytes[W_AR] = Bz * Lp * H * 4;
         bytes[W_DXR] = bytes[W_DYR];
-        bytes[W_DCH] = Bz * L * H * N * es;
+        // per-head dC / dB contributions in fp32, summed over the group's heads
+        // before the one rounding
+        const int64_t eh = 4;
+        bytes[W_DCH] = Bz * L * H * N * eh;
         bytes[W_XR] = bytes[W_DYR];
-        bytes[W_DBH] = Bz * Lp * H * N * es;
+        bytes[W_DBH] = Bz * Lp * H * N * eh;
         if (!bp->xg) {
             bytes[W_BEXP] = Bz * L * H * N * es;
             bytes[W_AEXP] = Bz * L * H * ns * 4;
@@ -713,14 +718,14 @@ ssd_status ssd_chunk_scan_bwd(const ssd_fwd_desc* desc, const void* X, const flo
         sc.H = H * ns; sc.P = 64; sc.N = P; sc.G = H;
         ssd::StateSrc srcc{initial_state, H * PN, F(W_SFW), nc * H * PN, H * PN};
         SSD_TRY(ssd::launch_mfma_out_xg(sc, G, B, a, X, dY, srcc, V(W_DCH), hs), "bwd: dC pass");
-        SSD_TRY(ssd::launch_group_sum(dC, V(W_DCH), Bz, L, L, 0, 1, H, G, N, true, hs), "bwd: dC group sum");
+        SSD_TRY(ssd::launch_group_sum(dC, V(W_DCH), Bz, L, L, 0, 1, H, G, N, false, true, hs), "bwd: dC group sum");
         ssd::FwdShape sb = sc;
         sb.L = Lp;
         SSD_TRY(ssd::launch_remap_rows(V(W_XR), X, Bz, Lp, L, Lp - 1, -1, H * P * es, hs), "bwd: reverse X");
         ssd::StateSrc srcb{dfinal_state, H * PN, F(W_SREV), nc * H * PN, H * PN};
         SSD_TRY(ssd::launch_mfma_out_xg(sb, G, V(W_CR), F(W_AR), V(W_DYR), V(W_XR), srcb, V(W_DBH), hs),
                 "bwd: dB pass");
-        SSD_TRY(ssd::launch_group_sum(dB, V(W_DBH), Bz, L, Lp, Lp - 1, -1, H, G, N, true, hs), "bwd: dB group sum");
+        SSD_TRY(ssd::launch_group_sum(dB, V(W_DBH), Bz, L, Lp, Lp - 1, -1, H, G, N, false, true, hs), "bwd: dB group sum");
         return ok();
     }
     // 5. dC = S^T dy: forward-time product, state dimensions exchanged
@@ -729,9 +734,9 @@ ssd_status ssd_chunk_scan_bwd(const ssd_fwd_desc* desc, const void* X, const flo
     if (initial_state)
         SSD_TRY(ssd::launch_state_transpose(F(W_S0T), initial_state, Bz * H, P, N, hs), "bwd: S0^T");
     st = run_fwd(bp.pc, V(W_BEXP), F(W_AEXP), X, dY, initial_state ? F(W_S0T) : nullptr, V(W_DCH),
-                 nullptr, V(W_INNER), hs);
+                 nullptr, V(W_INNER), hs, true);
     if (st != SSD_OK) return st;
-    SSD_TRY(ssd::launch_group_sum(dC, V(W_DCH), Bz, L, L, 0, 1, H, G, N, !bp.f32, hs), "bwd: dC group sum");
+    SSD_TRY(ssd::launch_group_sum(dC, V(W_DCH), Bz, L, L, 0, 1, H, G, N, false, !bp.f32, hs), "bwd: dC group sum");
     // 6. dB = G^T x: reversed-time product, state dimensions exchanged
     SSD_TRY(ssd::launch_bcast_heads(V(W_CREXP), C, Bz, Lp, L, Lp - 1, -1, H, G, N * es, hs), "bwd: C per head");
     SSD_TRY(ssd::launch_remap_rows(V(W_XR), X, Bz, Lp, L, Lp - 1, -1, H * P * es, hs), "bwd: reverse X");
@@ -739,9 +744,9 @@ ssd_status ssd_chunk_scan_bwd(const ssd_fwd_desc* desc, const void* X, const flo
     if (dfinal_state)
         SSD_TRY(ssd::launch_state_transpose(F(W_DSFT), dfinal_state, Bz * H, P, N, hs), "bwd: dS_fin^T");
     st = run_fwd(bp.pb, V(W_CREXP), F(W_AREXP), V(W_DYR), V(W_XR), dfinal_state ? F(W_DSFT) : nullptr,
-                 V(W_DBH), nullptr, V(W_INNER), hs);
+                 V(W_DBH), nullptr, V(W_INNER), hs, true);
     if (st != SSD_OK) return st;
-    SSD_TRY(ssd::launch_group_sum(dB, V(W_DBH), Bz, L, Lp, Lp - 1, -1, H, G, N, !bp.f32, hs), "bwd: dB group sum");
+    SSD_TRY(ssd::launch_group_sum(dB, V(W_DBH), Bz, L, Lp, Lp - 1, -1, H, G, N, false, !bp.f32, hs), "bwd: dB group sum");
 #undef SSD_TRY
     return ok();
 }

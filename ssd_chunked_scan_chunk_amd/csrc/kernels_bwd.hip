@@ -98,47 +98,52 @@ __global__ void k_state_transpose(float* __restrict__ out, const float* __restri
     }
 }
 
-// sum over each group's heads in fp32 (bf16 rounded once), one 16-byte
-// piece per thread: out[b][t][g][n] = sum_{h in g} in[b][s][h][n]
-template <typename T>
-__global__ void k_group_sum(uint4* __restrict__ out, const uint4* __restrict__ in, int64_t Lout,
-                            int64_t Lin, int64_t off, int64_t dir, int H, int G, int N16, int nbx)
+// sum over each group's heads in fp32, rounded once to the output type; a
+// thread covers 8 elements (two 16-byte input pieces for fp32 input):
+// out[b][t][g][n] = sum_{h in g} in[b][s][h][n]
+template <typename TI, typename TO>
+__global__ void k_group_sum(TO* __restrict__ out, const TI* __restrict__ in, int64_t Lout,
+                            int64_t Lin, int64_t off, int64_t dir, int H, int G, int N8, int nbx)
 {
-    constexpr int E = 16 / sizeof(T);   // elements per piece
     const int64_t t = blockIdx.x / nbx, b = blockIdx.y;
     const int k = (int)(blockIdx.x - t * nbx) * blockDim.x + threadIdx.x;
-    if (k >= G * N16) return;
-    const int gi = k / N16, q = k - gi * N16;
+    if (k >= G * N8) return;
+    const int gi = k / N8, q = k - gi * N8;
     const int hpg = H / G;
+    const int N = 8 * N8;
     const int64_t s = off + dir * t;
-    float acc[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = 0.f;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (s >= 0 && s < Lin) {
-        const uint4* src = in + ((b * Lin + s) * H + (int64_t)gi * hpg) * N16 + q;
+        const TI* src = in + ((b * Lin + s) * H + (int64_t)gi * hpg) * N + 8 * q;
         for (int j = 0; j < hpg; ++j) {
-            const uint4 v = src[(int64_t)j * N16];
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            const TI* p = src + (int64_t)j * N;
+            if constexpr (sizeof(TI) == 2) {
+                const uint4 v = *reinterpret_cast<const uint4*>(p);
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                if constexpr (E == 8) {
+                for (int e = 0; e < 4; ++e) {
                     acc[2 * e] += __uint_as_float(w[e] << 16);
                     acc[2 * e + 1] += __uint_as_float(w[e] & 0xffff0000u);
-                } else {
-                    acc[e] += __uint_as_float(w[e]);
                 }
+            } else {
+                const float4 v0 = *reinterpret_cast<const float4*>(p);
+                const float4 v1 = *reinterpret_cast<const float4*>(p + 4);
+                acc[0] += v0.x; acc[1] += v0.y; acc[2] += v0.z; acc[3] += v0.w;
+                acc[4] += v1.x; acc[5] += v1.y; acc[6] += v1.z; acc[7] += v1.w;
             }
         }
     }
-    uint32_t o[4];
+    TO* dst = out + ((b * Lout + t) * G + gi) * N + 8 * q;
+    if constexpr (sizeof(TO) == 2) {
+        uint32_t o[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        if constexpr (E == 8)
+        for (int e = 0; e < 4; ++e)
             o[e] = (uint32_t)f32_to_bf_bits(acc[2 * e]) | ((uint32_t)f32_to_bf_bits(acc[2 * e + 1]) << 16);
-        else
-            o[e] = __float_as_uint(acc[e]);
+        *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+    } else {
+        *reinterpret_cast<float4*>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        *reinterpret_cast<float4*>(dst + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
     }
-    out[(b * Lout + t) * G * N16 + k] = make_uint4(o[0], o[1], o[2], o[3]);
 }
 
 // st[b][h][:] *= exp(a[b][0][h])
@@ -206,18 +211,21 @@ hipError_t launch_state_transpose(float* out, const float* in, int64_t BH, int64
 }
 
 hipError_t launch_group_sum(void* out, const void* in, int64_t Bz, int64_t Lout, int64_t Lin,
-                            int64_t off, int64_t dir, int64_t H, int64_t G, int64_t N, bool bf16,
-                            hipStream_t st)
+                            int64_t off, int64_t dir, int64_t H, int64_t G, int64_t N, bool in_bf16,
+                            bool out_bf16, hipStream_t st)
 {
-    const int64_t N16 = N * (bf16 ? 2 : 4) / 16, w = G * N16;
+    const int64_t N8 = N / 8, w = G * N8;
     if (Bz * Lout * w <= 0) return hipSuccess;
-    if (bf16)
-        hipLaunchKernelGGL(k_group_sum<u16>, row_grid(w, Lout, Bz), dim3(row_threads(w)), 0, st, (uint4*)out,
-                           (const uint4*)in, Lout, Lin, off, dir, (int)H, (int)G, (int)N16, row_blocks(w));
-    else
-        hipLaunchKernelGGL(k_group_sum<float>, row_grid(w, Lout, Bz), dim3(row_threads(w)), 0, st,
-                           (uint4*)out, (const uint4*)in, Lout, Lin, off, dir, (int)H, (int)G, (int)N16,
-                           row_blocks(w));
+    const dim3 grid = row_grid(w, Lout, Bz), block(row_threads(w));
+    const int nbx = row_blocks(w);
+#define SSD_GS(TI, TO)                                                                            \
+    hipLaunchKernelGGL((k_group_sum<TI, TO>), grid, block, 0, st, (TO*)out, (const TI*)in, Lout, Lin, \
+                       off, dir, (int)H, (int)G, (int)N8, nbx)
+    if (in_bf16 && out_bf16) SSD_GS(u16, u16);
+    else if (!in_bf16 && out_bf16) SSD_GS(float, u16);
+    else if (!in_bf16 && !out_bf16) SSD_GS(float, float);
+    else return hipErrorInvalidValue;
+#undef SSD_GS
     return hipGetLastError();
 }
 

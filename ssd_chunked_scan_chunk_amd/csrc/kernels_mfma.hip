@@ -237,8 +237,8 @@ __device__ __forceinline__ void sync_lds() {
 // hl of group grp reads columns hl*P .. of group grp / (G / x_groups)); every
 // head of a group reads the a of head grp of an [L][G] array; and the entering
 // states are read transposed, head hl of group grp taking columns hl*P .. of
-// the [N][HPG*P] state of head grp.  SW is the number of state waves (the
-// workgroup has SW + 2 wavefronts).
+// the [N][HPG*P] state of head grp; Y is written in fp32.  SW is the number
+// of state waves (the workgroup has SW + 2 wavefronts).
 template <int P, int N, bool FULL, bool XG = false, int SW = kStateWaves>
 __global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(SW == kStateWaves ? 2 : 3))) void k_mfma_seg(
     const u16* __restrict__ X, const float* __restrict__ a, const u16* __restrict__ B,
@@ -715,12 +715,28 @@ __global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(S
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
-            // Y^T to bf16
+            if constexpr (XG) {
+                // fp32 out, straight from the accumulators (lane = step, four
+                // consecutive head-dim entries per register quad): the
+                // backward sums these over a group's heads before rounding
+                if (hvalid) {
+                    float* yrow = reinterpret_cast<float*>(Y) + (((int64_t)b * L + c * kT) * H + h) * P + pc + 4 * g2;
 #pragma unroll
-            for (int I = 0; I < 2; ++I)
+                    for (int I = 0; I < 2; ++I)
+                        if (32 * I + l32 <= last)
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    Yb[I][q] = make_uint2(pack2(Yt[I][4 * q], Yt[I][4 * q + 1]), pack2(Yt[I][4 * q + 2], Yt[I][4 * q + 3]));
+                            for (int q = 0; q < 4; ++q)
+                                *reinterpret_cast<float4*>(yrow + (int64_t)(32 * I + l32) * H * P + 8 * q) =
+                                    make_float4(Yt[I][4 * q], Yt[I][4 * q + 1], Yt[I][4 * q + 2], Yt[I][4 * q + 3]);
+                }
+            } else {
+                // Y^T to bf16
+#pragma unroll
+                for (int I = 0; I < 2; ++I)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        Yb[I][q] = make_uint2(pack2(Yt[I][4 * q], Yt[I][4 * q + 1]), pack2(Yt[I][4 * q + 2], Yt[I][4 * q + 3]));
+            }
         }
 
         // ---- stages 3 + 4: Sacc' = (direct form: 2^(ld + Lam2)) Sacc + B^T X~ ----
@@ -751,7 +767,7 @@ __global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(S
                 }
             }
         }
-        if constexpr (FULL) {
+        if constexpr (FULL && !XG) {
             // Y^T through this wave's own X slice, which is dead after stage 3,
             // so that copy k of a lane holds 16 contiguous bytes of step
             // 16k + lane/4 and a store covers 16 steps x 64 bytes

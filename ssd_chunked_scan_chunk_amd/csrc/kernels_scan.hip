@@ -25,12 +25,12 @@ namespace ssd {
 // ---------------------------------------------------------------------------
 constexpr int kValuThreads = 256;
 
-// Y may be null (only the states are wanted); S_chunks (optional) receives
-// the state entering every chunk, [Bz][nc][H][P*N].
-template <typename T>
+// Y (of type TY) may be null (only the states are wanted); S_chunks
+// (optional) receives the state entering every chunk, [Bz][nc][H][P*N].
+template <typename T, typename TY = T>
 __global__ __launch_bounds__(kValuThreads) void k_valu_fwd(
     const T* __restrict__ X, const float* __restrict__ a, const T* __restrict__ B,
-    const T* __restrict__ C, const float* __restrict__ S0, T* __restrict__ Y,
+    const T* __restrict__ C, const float* __restrict__ S0, TY* __restrict__ Y,
     float* __restrict__ S_fin, float* __restrict__ S_chunks, int64_t L, int H, int P, int N,
     int G, int Q)
 {
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(kValuThreads) void k_valu_fwd(
             }
             float off = 0.f;
             for (int n = 0; n < N; ++n) off += Elem<T>::load(Ci + n) * sS[p * N + n];
-            Elem<T>::store(Y + (((int64_t)b * L + t0 + i) * H + h) * P + p, acc + expf(sCs[i]) * off);
+            Elem<TY>::store(Y + (((int64_t)b * L + t0 + i) * H + h) * P + p, acc + expf(sCs[i]) * off);
         }
         __syncthreads();
         // chunk state and the hand-off across the chunk boundary
@@ -104,11 +104,18 @@ bool valu_fwd_supported(const FwdShape& s) {
 
 hipError_t launch_valu_fwd(const FwdShape& s, bool bf16, const void* X, const float* a,
                            const void* B, const void* C, const float* S0, void* Y,
-                           float* S_fin, hipStream_t st, float* S_chunks)
+                           float* S_fin, hipStream_t st, float* S_chunks, bool y_f32)
 {
     const size_t lds = (size_t)(2 * s.Q + s.P * s.N + 4) * sizeof(float);
     dim3 grid((unsigned)s.H, (unsigned)s.Bz);
-    if (bf16) {
+    if (bf16 && y_f32) {
+        auto k = k_valu_fwd<u16, float>;
+        hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(k, grid, dim3(kValuThreads), lds, st, (const u16*)X, a, (const u16*)B,
+                           (const u16*)C, S0, (float*)Y, S_fin, S_chunks, s.L, (int)s.H, (int)s.P,
+                           (int)s.N, (int)s.G, (int)s.Q);
+    } else if (bf16) {
         auto k = k_valu_fwd<u16>;
         hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;

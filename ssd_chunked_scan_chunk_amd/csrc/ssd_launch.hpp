@@ -23,10 +23,11 @@ struct StateSrc {
 
 // ---- VALU path (any dtype; fp32 arithmetic, exact segment sums) -------------
 // Y may be null; S_chunks (optional) receives the state entering every chunk
-// [Bz][nc][H][P][N].
+// [Bz][nc][H][P][N]; y_f32 writes Y in fp32 for bf16 inputs.
 hipError_t launch_valu_fwd(const FwdShape& s, bool bf16, const void* X, const float* a,
                            const void* B, const void* C, const float* S0, void* Y,
-                           float* S_fin, hipStream_t st, float* S_chunks = nullptr);
+                           float* S_fin, hipStream_t st, float* S_chunks = nullptr,
+                           bool y_f32 = false);
 bool valu_fwd_supported(const FwdShape& s);
 
 // ---- stage 1: in-chunk prefix sums ---------------------------------------------
@@ -67,6 +68,7 @@ hipError_t launch_mfma_out(const FwdShape& s, int64_t seg_chunks, int64_t nseg,
 // a group (head hl reads columns hl*64 ..), a [Bz][L][G] (one decay per group),
 // and the entering state of segment s read transposed from the [64][(H/G)*64]
 // state of group grp in src (segment 0 from src.first, s >= 1 from src.Sin).
+// Y is fp32 [Bz][L][H][64].
 hipError_t launch_mfma_out_xg(const FwdShape& s, int64_t x_groups, const void* X, const float* a,
                               const void* B, const void* C, StateSrc src, void* Y, hipStream_t st);
 
@@ -92,11 +94,12 @@ hipError_t launch_remap_a(float* out, const float* a, int64_t Bz, int64_t Lout, 
 // out[bh][n][p] = in[bh][p][n]
 hipError_t launch_state_transpose(float* out, const float* in, int64_t BH, int64_t P, int64_t N,
                                   hipStream_t st);
-// out[b][t][g][n] = sum over the group's heads of in[b][s][h][n] (fp32 sum; bf16 or
-// fp32 elements, N * element size a multiple of 16 bytes)
+// out[b][t][g][n] = sum over the group's heads of in[b][s][h][n] (fp32 sum, rounded
+// once to out's type): in_bf16 / out_bf16 choose bf16 or fp32 elements (N times the
+// element size a multiple of 16 bytes)
 hipError_t launch_group_sum(void* out, const void* in, int64_t Bz, int64_t Lout, int64_t Lin,
-                            int64_t off, int64_t dir, int64_t H, int64_t G, int64_t N, bool bf16,
-                            hipStream_t st);
+                            int64_t off, int64_t dir, int64_t H, int64_t G, int64_t N, bool in_bf16,
+                            bool out_bf16, hipStream_t st);
 // state[b][h][:] *= exp(a[b][0][h])
 hipError_t launch_scale_state_by_a0(float* state, const float* a, int64_t Bz, int64_t L,
                                     int64_t H, int64_t PN, hipStream_t st);
