@@ -61,3 +61,35 @@ def test_random_shape_fwd_bwd(shape, with_s0, with_dsf, seed):
             "dS0": state_err(host_f64(gr["dinitial_state"]), ref["dS0"])}
     log("   " + " ".join("%s=%.2e" % kv for kv in errs.items()))
     assert all(v <= tol for v in errs.values()), errs
+
+
+def _f32_shapes(n=8, seed=4242):
+    rng = np.random.default_rng(seed)
+    out = []
+    for k in range(n):
+        G = int(rng.choice([1, 2]))
+        H = G * int(rng.integers(1, 4))
+        P = int(rng.choice([8, 16, 32]))
+        N = int(rng.choice([16, 32, 64]))
+        Q = int(rng.choice([32, 64, 128]))
+        L = int(rng.integers(1, 3 * Q))
+        Bz = int(rng.integers(1, 3))
+        out.append((si.FwdShape(Bz, L, H, P, N, G, Q, si.F32), bool(rng.integers(0, 2)),
+                    bool(rng.integers(0, 2)), 900 + k))
+    return out
+
+
+@pytest.mark.parametrize("shape,with_s0,with_dsf,seed", _f32_shapes(),
+                         ids=lambda v: str(v) if not isinstance(v, si.FwdShape) else
+                         "B%dL%dH%dP%dN%dG%dQ%d" % (v.batch, v.seqlen, v.nheads, v.headdim, v.dstate,
+                                                    v.ngroups, v.chunk))
+def test_random_shape_fwd_bwd_f32(shape, with_s0, with_dsf, seed):
+    # the same on fp32 inputs (VALU kernels) at the fp32 tolerance
+    test_random_shape_fwd_bwd(shape, with_s0, with_dsf, seed)
+
+
+def test_one_step_group_cancellation():
+    # regression: one step, four heads per group -- the group sums of dB and dC
+    # are a sum over heads of x.dy that can nearly cancel, so the heads'
+    # contributions must be summed before rounding to bf16
+    test_random_shape_fwd_bwd(si.FwdShape(2, 1, 12, 64, 128, 3, 256, si.BF16), True, False, 120)
