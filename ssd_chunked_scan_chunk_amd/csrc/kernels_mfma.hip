@@ -147,6 +147,17 @@ __device__ __forceinline__ bf16x8 acc_half(const f32x16& v, int h) {
     return as_bf16x8(u32x4{pack2(v[8 * h + 0], v[8 * h + 1]), pack2(v[8 * h + 2], v[8 * h + 3]),
                            pack2(v[8 * h + 4], v[8 * h + 5]), pack2(v[8 * h + 6], v[8 * h + 7])});
 }
+// the remainders v - hi of the eight values acc_half(v, h) rounded, themselves
+// rounded to bf16: hi + lo carries v to about 16 significant bits
+__device__ __forceinline__ bf16x8 acc_half_lo(const f32x16& v, int h, const bf16x8& hi) {
+    const u32x4 u = as_u32x4(hi);
+    u32x4 o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        o[k] = pack2(v[8 * h + 2 * k] - __uint_as_float(u[k] << 16),
+                     v[8 * h + 2 * k + 1] - __uint_as_float(u[k] & 0xffff0000u));
+    return as_bf16x8(o);
+}
 // bf16x8 scaled elementwise in fp32 and rounded back
 __device__ __forceinline__ bf16x8 scale8(bf16x8 v, const float (&s)[8]) {
     const u32x4 u = as_u32x4(v);
@@ -237,8 +248,14 @@ __device__ __forceinline__ void sync_lds() {
 // hl of group grp reads columns hl*P .. of group grp / (G / x_groups)); every
 // head of a group reads the a of head grp of an [L][G] array; and the entering
 // states are read transposed, head hl of group grp taking columns hl*P .. of
-// the [N][HPG*P] state of head grp; Y is written in fp32.  SW is the number
-// of state waves (the workgroup has SW + 2 wavefronts).
+// the [N][HPG*P] state of head grp; Y is written in fp32.  These outputs are
+// summed over the original group's heads afterwards, and those sums can
+// cancel (at a single step, dB and dC are a sum over heads of x.dy times one
+// row), so the output path keeps about 16 bits: every block takes the direct
+// form, the copy waves store the decayed masked scores (the same for all the
+// workgroup's heads, which share one decay) as bf16 high and low parts, and
+// stage 5 multiplies the state's high and low parts.  SW is the number of
+// state waves (the workgroup has SW + 2 wavefronts).
 template <int P, int N, bool FULL, bool XG = false, int SW = kStateWaves>
 __global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(SW == kStateWaves ? 2 : 3))) void k_mfma_seg(
     const u16* __restrict__ X, const float* __restrict__ a, const u16* __restrict__ B,
@@ -253,7 +270,9 @@ __global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(S
     __shared__ __attribute__((aligned(16))) u16 sX[2][HW * kT * P];    // [buf][head][step][p]
     __shared__ __attribute__((aligned(16))) u16 sB[2][kT * N];         // [buf][step][n]
     __shared__ __attribute__((aligned(16))) u16 sC[FULL ? 2 : 1][FULL ? kT * N : 8];
-    __shared__ __attribute__((aligned(16))) u16 sP[FULL ? 3 : 1][FULL ? 32 * kPRow : 8];  // masked scores [i][j]
+    // masked scores [i][j]; XG: decayed, high part then low part, unpadded
+    // rows with the 16-byte pieces XOR-swizzled by (i / 4) % 4
+    __shared__ __attribute__((aligned(16))) u16 sP[FULL ? 3 : 1][FULL ? (XG ? 2 * 32 * 32 : 32 * kPRow) : 8];
     __shared__ __attribute__((aligned(16))) float sA[3][HW * kT];     // [buf][head][step]
     // stage 1's results per head, two buffers: output exponents, state weights
     // per step, and the block's scale decisions
@@ -450,7 +469,7 @@ __global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(S
                 const float cs2 = wave_scan64_rowsum(av, absa, lane) * kLog2e;
                 float base[kQ + 1], lamq[kQ], absq[kQ];   // base[q]: cs2 before quarter q
                 base[0] = 0.f;
-                bool fast = true;
+                bool fast = !XG;
 #pragma unroll
                 for (int q = 0; q < kQ; ++q) {
                     base[q + 1] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs2), 16 * q + 15));
@@ -530,6 +549,28 @@ __global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(S
                     // row j of accumulator register r: 8(r/4) + 4*g2 + r%4; lane = i.
                     // Masked entries (j > i on the diagonal) are replaced, never multiplied.
                     const bool diag = I == J;
+                    if constexpr (XG) {
+                        // decayed by 2^(cs2_i - cs2_j) (the direct form's exponents,
+                        // shared by every head here), split into high and low parts
+                        const float csi = sCs[bf][0][32 * I + l32];
+                        u16* prow = &sP[t][l32 * 32];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int j0 = 8 * q + 4 * g2;
+                            const float4 cj = *reinterpret_cast<const float4*>(&sCs[bf][0][32 * J + j0]);
+                            const float cjv[4] = {cj.x, cj.y, cj.z, cj.w};
+                            float v[4];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                v[e] = (!diag || j0 + e <= l32) ? St[4 * q + e] * fast_exp2(csi - cjv[e]) : 0.f;
+                            const uint32_t h01 = pack2(v[0], v[1]), h23 = pack2(v[2], v[3]);
+                            const uint32_t l01 = pack2(v[0] - __uint_as_float(h01 << 16), v[1] - __uint_as_float(h01 & 0xffff0000u));
+                            const uint32_t l23 = pack2(v[2] - __uint_as_float(h23 << 16), v[3] - __uint_as_float(h23 & 0xffff0000u));
+                            const int off = 8 * (q ^ ((l32 >> 2) & 3)) + 4 * g2;
+                            *reinterpret_cast<uint2*>(prow + off) = make_uint2(h01, h23);
+                            *reinterpret_cast<uint2*>(prow + 32 * 32 + off) = make_uint2(l01, l23);
+                        }
+                    } else {
                     u16* prow = &sP[t][l32 * kPRow];
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
@@ -538,6 +579,7 @@ __global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(S
 #pragma unroll
                         for (int e = 0; e < 4; ++e) v[e] = (!diag || j0 + e <= l32) ? St[4 * q + e] : 0.f;
                         *reinterpret_cast<uint2*>(prow + j0) = make_uint2(pack2(v[0], v[1]), pack2(v[2], v[3]));
+                    }
                     }
                 }
             }
@@ -619,7 +661,7 @@ __global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(S
         const float4 pa = *reinterpret_cast<const float4*>(&sPar[bf][hw][0]);
         const float4 pb = *reinterpret_cast<const float4*>(&sPar[bf][hw][4]);
         auto uni = [](float v) { return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v))); };
-        const bool fast = uni(pa.x) != 0.f;
+        const bool fast = !XG && uni(pa.x) != 0.f;   // (XG: always the direct form)
         const float pre = uni(pa.y), ld_in = uni(pa.z), lam2 = uni(pa.w);
         const float rq[kQ] = {0.f, uni(pb.x), uni(pb.y), uni(pb.z)};
         const bool fold[kQ] = {false, rq[1] != 0.f, rq[2] != 0.f, rq[3] != 0.f};
@@ -641,6 +683,11 @@ __global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(S
                     const bf16x8 Sf = acc_half(Sacc[nt], hf);
 #pragma unroll
                     for (int I = 0; I < 2; ++I) Yt[I] = mfma32(Sf, rowfrag(cT, I, nt, hf), Yt[I]);
+                    if constexpr (XG) {   // the state's low part
+                        const bf16x8 Sl = acc_half_lo(Sacc[nt], hf, Sf);
+#pragma unroll
+                        for (int I = 0; I < 2; ++I) Yt[I] = mfma32(Sl, rowfrag(cT, I, nt, hf), Yt[I]);
+                    }
                 }
         }
 
@@ -701,6 +748,24 @@ __global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(S
                     }
                     return as_bf16x8(u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])});
                 };
+                if constexpr (XG) {
+                    // the copy waves' decayed scores, high and low parts, on unweighted X
+                    auto pt = [&](int t, int ks, int part) {
+                        return as_bf16x8(*reinterpret_cast<const u32x4*>(
+                            &sP[t][part * 32 * 32 + l32 * 32 + 8 * ((2 * ks + g2) ^ ((l32 >> 2) & 3))]));
+                    };
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks) {
+                        const bf16x8 xa0 = xfrag(0, ks);
+                        const bf16x8 xa1 = xfrag(1, ks);
+#pragma unroll
+                        for (int part = 0; part < 2; ++part) {
+                            Yt[0] = mfma32(xa0, pt(0, ks, part), Yt[0]);
+                            Yt[1] = mfma32(xa0, pt(1, ks, part), Yt[1]);
+                            Yt[1] = mfma32(xa1, pt(2, ks, part), Yt[1]);
+                        }
+                    }
+                } else {
                 const float csi0 = sCs[bf][hw][l32], csi1 = sCs[bf][hw][32 + l32];
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
@@ -713,6 +778,7 @@ __global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(S
                     __builtin_amdgcn_sched_barrier(0);
                     Yt[1] = mfma32(xfrag(1, ks), decayed(2, 1, ks, csi1), Yt[1]);
                     __builtin_amdgcn_sched_barrier(0);
+                }
                 }
             }
             if constexpr (XG) {

@@ -88,8 +88,15 @@ def test_random_shape_fwd_bwd_f32(shape, with_s0, with_dsf, seed):
     test_random_shape_fwd_bwd(shape, with_s0, with_dsf, seed)
 
 
-def test_one_step_group_cancellation():
-    # regression: one step, four heads per group -- the group sums of dB and dC
-    # are a sum over heads of x.dy that can nearly cancel, so the heads'
-    # contributions must be summed before rounding to bf16
-    test_random_shape_fwd_bwd(si.FwdShape(2, 1, 12, 64, 128, 3, 256, si.BF16), True, False, 120)
+@pytest.mark.parametrize("shape,with_s0,with_dsf,seed", [
+    (si.FwdShape(2, 1, 12, 64, 128, 3, 256, si.BF16), True, False, 120),
+    (si.FwdShape(3, 1, 9, 64, 64, 3, 256, si.BF16), True, False, 132),
+    (si.FwdShape(2, 1, 2, 64, 128, 1, 256, si.BF16), True, True, 156),
+], ids=["G3x4", "G3x3", "G1x2_dsf"])
+def test_one_step_group_cancellation(shape, with_s0, with_dsf, seed):
+    # regression: at one step the group sums of dB and dC are a sum over heads
+    # of x.dy times one row, which can nearly cancel (x.dy of -2.01, -7.61 and
+    # 10.15 in one of these groups): the heads' contributions are summed in
+    # fp32 before rounding, and each head's own score and state terms must keep
+    # more than bf16's 8 bits, or their rounding dominates the cancelled sum
+    test_random_shape_fwd_bwd(shape, with_s0, with_dsf, seed)
