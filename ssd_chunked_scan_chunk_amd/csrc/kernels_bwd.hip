@@ -44,7 +44,9 @@ static int64_t grid_cap(int64_t n, int64_t per) {
 
 // The copies below run on a (row blocks x steps, batch) grid: block x covers
 // piece block x % nbx of output step x / nbx, blockIdx.y is the batch, so no
-// per-element division is needed.
+// per-element division is needed.  The group sum, whose output rows can be
+// as short as 16 pieces, instead takes a flat range of a batch's rows (one
+// division per thread, against dozens of loads).
 
 // rows of W8 16-byte pieces: out[b][t][:] = in[b][s][:]
 __global__ void k_remap_rows(uint4* __restrict__ out, const uint4* __restrict__ in, int64_t Lout,
@@ -100,14 +102,19 @@ __global__ void k_state_transpose(float* __restrict__ out, const float* __restri
 
 // sum over each group's heads in fp32, rounded once to the output type; a
 // thread covers 8 elements (two 16-byte input pieces for fp32 input):
-// out[b][t][g][n] = sum_{h in g} in[b][s][h][n]
+// out[b][t][g][n] = sum_{h in g} in[b][s][h][n]: thread (t, g, 8-column piece)
+// of a flat range over a batch's rows (several short rows share a workgroup),
+// the heads summed in order, four loads in flight
 template <typename TI, typename TO>
-__global__ void k_group_sum(TO* __restrict__ out, const TI* __restrict__ in, int64_t Lout,
-                            int64_t Lin, int64_t off, int64_t dir, int H, int G, int N8, int nbx)
+__global__ __launch_bounds__(256) void k_group_sum(TO* __restrict__ out, const TI* __restrict__ in,
+                                                   int64_t Lout, int64_t Lin, int64_t off, int64_t dir,
+                                                   int H, int G, int N8)
 {
-    const int64_t t = blockIdx.x / nbx, b = blockIdx.y;
-    const int k = (int)(blockIdx.x - t * nbx) * blockDim.x + threadIdx.x;
-    if (k >= G * N8) return;
+    const int64_t w = (int64_t)G * N8;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= Lout * w) return;
+    const int64_t t = idx / w, b = blockIdx.y;
+    const int k = (int)(idx - t * w);
     const int gi = k / N8, q = k - gi * N8;
     const int hpg = H / G;
     const int N = 8 * N8;
@@ -115,6 +122,7 @@ __global__ void k_group_sum(TO* __restrict__ out, const TI* __restrict__ in, int
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (s >= 0 && s < Lin) {
         const TI* src = in + ((b * Lin + s) * H + (int64_t)gi * hpg) * N + 8 * q;
+#pragma unroll 4
         for (int j = 0; j < hpg; ++j) {
             const TI* p = src + (int64_t)j * N;
             if constexpr (sizeof(TI) == 2) {
@@ -216,11 +224,10 @@ hipError_t launch_group_sum(void* out, const void* in, int64_t Bz, int64_t Lout,
 {
     const int64_t N8 = N / 8, w = G * N8;
     if (Bz * Lout * w <= 0) return hipSuccess;
-    const dim3 grid = row_grid(w, Lout, Bz), block(row_threads(w));
-    const int nbx = row_blocks(w);
+    const dim3 grid((unsigned)((Lout * w + 255) / 256), (unsigned)Bz), block(256);
 #define SSD_GS(TI, TO)                                                                            \
     hipLaunchKernelGGL((k_group_sum<TI, TO>), grid, block, 0, st, (TO*)out, (const TI*)in, Lout, Lin, \
-                       off, dir, (int)H, (int)G, (int)N8, nbx)
+                       off, dir, (int)H, (int)G, (int)N8)
     if (in_bf16 && out_bf16) SSD_GS(u16, u16);
     else if (!in_bf16 && out_bf16) SSD_GS(float, u16);
     else if (!in_bf16 && !out_bf16) SSD_GS(float, float);
