@@ -3,6 +3,8 @@ path) against the fp64 oracle: a spread of batch sizes, sequence lengths
 (ragged, shorter than a chunk, a single step), head counts not divisible by
 the heads per workgroup, group counts, head dims, state sizes and chunks, with
 and without the initial state and the final-state gradient."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -61,6 +63,19 @@ def test_random_shape_fwd_bwd(shape, with_s0, with_dsf, seed):
             "dS0": state_err(host_f64(gr["dinitial_state"]), ref["dS0"])}
     log("   " + " ".join("%s=%.2e" % kv for kv in errs.items()))
     assert all(v <= tol for v in errs.values()), errs
+
+
+def _weak_decay_shapes(n=8, seed=99):
+    # the same spread with Mamba-2's dt recipe: weak decay, long memory, large states
+    return [(dataclasses.replace(sh, dt_recipe="mamba2_dt"), s0, dsf, sd) for (sh, s0, dsf, sd) in _shapes(n, seed)]
+
+
+@pytest.mark.parametrize("shape,with_s0,with_dsf,seed", _weak_decay_shapes(),
+                         ids=lambda v: str(v) if not isinstance(v, si.FwdShape) else
+                         "B%dL%dH%dP%dN%dG%dQ%d" % (v.batch, v.seqlen, v.nheads, v.headdim, v.dstate,
+                                                    v.ngroups, v.chunk))
+def test_random_shape_fwd_bwd_weak_decay(shape, with_s0, with_dsf, seed):
+    test_random_shape_fwd_bwd(shape, with_s0, with_dsf, seed)
 
 
 def _f32_shapes(n=8, seed=4242):
