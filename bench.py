@@ -1,26 +1,33 @@
 #!/usr/bin/env python3
 """Benchmark of the MI355X SSD layer (chunked forward + recurrent decode).
 
-One step = one full forward (all four stages) of the Mamba-2 130M-shaped SSD
-layer -- batch 4, seqlen 2048, 24 heads, headdim 64, state 128, 1 group,
-chunk 256, bf16 X/B/C with fp32 a -- over one batch of seeded synthetic
-inputs already resident in HBM.  Several distinct input batches are cycled so
-that the working set of the timed loop (> 256 MB) does not sit in the 256 MB
+One step = one full forward (all four stages) of the Mamba-2 2.7B-shaped SSD
+layer -- batch 8, seqlen 4096, 80 heads, headdim 64, state 128, 1 group,
+chunk 256, bf16 X/B/C with fp32 a, returning the final state -- over one
+batch of seeded synthetic inputs already resident in HBM.  Distinct input
+batches are cycled so that the timed loop's working set exceeds the 256 MB
 Infinity Cache.
 
 Prints ONE JSON line.  Besides the contract fields it carries:
-  roofline      the dominant kernel (the MFMA full pass) against the HBM peak,
-                from algorithmic bytes and that kernel's own launch duration,
-                measured with HIP events on the launch stream (the pass is
-                launched alone through the stage entry point, in the same
-                segment configuration the step uses);
-  passes        the step's three launches timed one by one the same way;
-  mfma          MFMA flops of the step (the 64-step blocking the kernels run)
-                against the bf16 dense peak;
+  roofline      the dominant kernel (the MFMA full pass) against the HBM peak:
+                algorithmic bytes per launch over that kernel's own average
+                launch duration, measured with HIP events on the launch
+                stream (the pass alone through its stage entry point when the
+                step has several launches, the step itself when it is that
+                one launch); `traffic` is the counter-measured HBM bytes of a
+                launch from the committed rocprofv3 summary when that was
+                taken on the current kernel source;
+  mfma          MFMA flops of the step against the bf16 dense peak, counted
+                at the caller's chunk (the survey's algorithmic count:
+                causal halves of the chunk's C B^T and masked product, chunk
+                state and state-to-output) and at the 64-step blocks the
+                kernels execute;
+  passes        the step's launches timed one by one the same way;
   cpu_baseline  the fp64 CPU oracle on the same workload (host cores);
-  secondary     the other workloads of the metric: the 2.7B-shaped layer,
-                the state-64 sweep at seqlen 32K, the decode step's HBM
-                bandwidth, and the backward of the 130M-shaped layer.
+  secondary     the rest of the metric's workloads: the 130M-shaped layer,
+                the state-64 seqlen sweep at all six lengths (512 .. 512K),
+                the decode step's HBM bandwidth, and the backward of the
+                130M-shaped layer.
 """
 import argparse
 import json
@@ -43,28 +50,36 @@ def fwd_algo_bytes_per_token(sh):
     return sh.nheads * sh.headdim * 2 * es + 2 * sh.ngroups * sh.dstate * es + 4 * sh.nheads
 
 
+def fwd_algo_bytes(sh):
+    """Minimum HBM bytes of one forward: every token's bytes, plus the final
+    state (fp32) when the workload returns it."""
+    fin = sh.batch * sh.nheads * sh.headdim * sh.dstate * 4 if sh.final_state else 0
+    return sh.batch * sh.seqlen * fwd_algo_bytes_per_token(sh) + fin
+
+
 KERNEL_BLOCK = 64   # the fused kernels' block length (the output does not depend on it)
 
 
 def fwd_algo_flops_per_token(sh, block=KERNEL_BLOCK):
     """MFMA flops per token of the blocked form with blocks of `block` steps:
     causal half of C B^T once per group, causal half of (L o S) X per head,
-    block state and state-to-output per head."""
+    block state and state-to-output per head.  With block = the caller's
+    chunk this is the survey's algorithmic count."""
     Q, N, P, H, G = block, sh.dstate, sh.headdim, sh.nheads, sh.ngroups
     return (Q + 1) * (N * G + P * H) + 4 * N * P * H
 
 
-def stored_traffic():
-    """HBM bytes per launch of the full-pass kernel from the committed
-    rocprofv3 FETCH_SIZE/WRITE_SIZE summary (calibrated on a plain copy), or
-    None when that summary was taken on a different kernel source."""
+def stored_traffic(profile):
+    """HBM bytes per launch of the full-pass kernel from a committed rocprofv3
+    FETCH_SIZE/WRITE_SIZE summary (calibrated on a plain copy), or None when
+    that summary was taken on a different kernel source."""
     import hashlib
     src = os.path.join(ROOT, "ssd_chunked_scan_chunk_amd", "csrc", "kernels_mfma.hip")
-    prof = os.path.join(ROOT, "profiles", "k_mfma_seg_full_m2_130m_hbm_traffic.md")
+    prof = os.path.join(ROOT, "profiles", profile)
     try:
         sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
         fields = dict(l.split(":", 1) for l in open(prof) if l.startswith(("traffic_bytes", "kernel_source")))
-    except OSError:
+    except (OSError, ValueError):
         return None
     if fields.get("kernel_source_sha256_16", "").strip() != sha:
         return None
@@ -99,7 +114,8 @@ def time_events(fn, steps):
 
 def bench_forward(sh, steps, warmup, nbatch, seed0=0):
     """Time `steps` forwards cycling over `nbatch` seeded batches.
-    Returns (seconds per step, seconds per launch of the full-pass kernel, plan)."""
+    Returns (seconds per step, seconds per launch of the full-pass kernel,
+    plan, per-pass milliseconds)."""
     import torch
     import ssd_chunked_scan_chunk_amd as ssd
     import ssd_inputs as si
@@ -120,13 +136,18 @@ def bench_forward(sh, steps, warmup, nbatch, seed0=0):
         step(i)
     t_step = time_events(step, steps) / steps
 
-    # the step's launches one by one, in the configuration the step uses: the
-    # state-only pass over the segments, the segment scan, and the full pass
-    # (the dominant kernel) fed entering states (their values do not change
-    # the work)
+    # The step's launches one by one, in the configuration the step uses.
+    # With one segment the step is the full pass itself (one launch).  With
+    # several: the state-only pass over the segments, the segment scan, and
+    # the full pass (the dominant kernel) fed entering states (their values
+    # do not change the work).
     algo, seg_chunks, nseg = plan
     passes = {}
-    if algo == ssd.SSD_ALGO_MFMA:
+    t_kernel = None
+    if algo == ssd.SSD_ALGO_MFMA and nseg == 1:
+        t_kernel = t_step
+        passes["full_pass_ms"] = t_step * 1e3
+    elif algo == ssd.SSD_ALGO_MFMA:
         Bz, H, P, N = sh.batch, sh.nheads, sh.headdim, sh.dstate
         Sin = torch.zeros((Bz, nseg, H, P, N), dtype=torch.float32, device="cuda")
 
@@ -137,29 +158,50 @@ def bench_forward(sh, steps, warmup, nbatch, seed0=0):
 
         for i in range(warmup):
             full(i)
-        passes["full_pass_ms"] = time_events(full, steps) / steps * 1e3
-        if nseg > 1:
-            dS = torch.empty((Bz, nseg, H, P, N), dtype=torch.float32, device="cuda")
-            lam_u = torch.zeros((Bz, H, nseg), dtype=torch.float32, device="cuda")
+        t_kernel = time_events(full, steps) / steps
+        passes["full_pass_ms"] = t_kernel * 1e3
+        dS = torch.empty((Bz, nseg, H, P, N), dtype=torch.float32, device="cuda")
+        lam_u = torch.zeros((Bz, H, nseg), dtype=torch.float32, device="cuda")
 
-            def state(i):
-                g = batches[i % nbatch]
-                ssd.chunk_state(g["X"], g["a"], g["B"], sh.chunk, seg_chunks=seg_chunks, out=dS)
+        def state(i):
+            g = batches[i % nbatch]
+            ssd.chunk_state(g["X"], g["a"], g["B"], sh.chunk, seg_chunks=seg_chunks, out=dS)
 
-            def scan(i):
-                ssd.state_passing(dS, lam_u, sh.chunk, sh.seqlen, out=Sin, return_final_state=False,
-                                  seg_chunks=seg_chunks)
+        def scan(i):
+            ssd.state_passing(dS, lam_u, sh.chunk, sh.seqlen, out=Sin, return_final_state=False,
+                              seg_chunks=seg_chunks)
 
-            for fn, key in ((state, "state_pass_ms"), (scan, "segment_scan_ms")):
-                for i in range(warmup):
-                    fn(i)
-                passes[key] = time_events(fn, steps) / steps * 1e3
-            del dS, lam_u
-        del Sin
-    t_kernel = passes.get("full_pass_ms", 0.0) / 1e3 or None
+        for fn, key in ((state, "state_pass_ms"), (scan, "segment_scan_ms")):
+            for i in range(warmup):
+                fn(i)
+            passes[key] = time_events(fn, steps) / steps * 1e3
+        del dS, lam_u, Sin
     del batches, Ys
     torch.cuda.empty_cache()
     return t_step, t_kernel, plan, passes
+
+
+def n_batches(sh):
+    """Distinct input batches to cycle: more than 2x the Infinity Cache."""
+    return max(1, int(np.ceil(2 * 256e6 / fwd_algo_bytes(sh))))
+
+
+def measure_forward(sh, steps, warmup):
+    """One forward workload: step time, tokens/s, plan, passes, and the
+    HBM / MFMA fractions of the step and of its full pass."""
+    t_step, t_kernel, plan, passes = bench_forward(sh, steps, warmup, n_batches(sh))
+    tok = sh.batch * sh.seqlen
+    nbytes = fwd_algo_bytes(sh)
+    fq = tok * fwd_algo_flops_per_token(sh, sh.chunk)
+    f64 = tok * fwd_algo_flops_per_token(sh)
+    return {"tokens_per_s": tok / t_step, "ms_per_step": t_step * 1e3,
+            "plan": {"algo": plan[0], "seg_chunks": plan[1], "nseg": plan[2]},
+            "hbm_frac": nbytes / t_step / 1e9 / HBM_PEAK_GBS,
+            "full_pass_hbm_frac": nbytes / t_kernel / 1e9 / HBM_PEAK_GBS if t_kernel else None,
+            "mfma_frac": fq / t_step / 1e12 / BF16_PEAK_TFLOPS,
+            "mfma_frac_blocks64": f64 / t_step / 1e12 / BF16_PEAK_TFLOPS,
+            "algo_bytes": nbytes, "algo_flops": fq, "algo_flops_blocks64": f64,
+            "passes": passes, "_t_kernel": t_kernel, "_t_step": t_step}
 
 
 def bench_decode(steps, warmup):
@@ -269,24 +311,30 @@ def bwd_da_work(sh):
 
 
 def cpu_baseline(sh):
-    """The fp64 oracle (never tuned) on the same workload, on the host cores."""
+    """The fp64 oracle (never tuned) on a bounded sample of the same workload,
+    on the host cores: the first batch rows of the seeded batch, all heads,
+    full length (heads and batch rows are independent, so this is the same
+    per-token work), repeated until about 10 CPU-seconds are timed."""
     import oracle
     import ssd_inputs as si
     d = si.make_fwd(sh, seed=0)
-    w = {k: si.widen(d[k], sh.dtype) for k in ("X", "B", "C")}
-    a = d["a"].astype(np.float64)
-    threads = os.cpu_count() or 1
+    rows = max(1, min(sh.batch, 2))
+    w = {k: si.widen(d[k][:rows], sh.dtype) for k in ("X", "B", "C")}
+    a = d["a"][:rows].astype(np.float64)
+    del d
+    threads = min(16, os.cpu_count() or 1)
     reps, t0 = 0, time.perf_counter()
-    while True:   # repeat the batch until ~10 CPU-seconds of work are timed
+    while True:
         oracle.fwd(w["X"], a, w["B"], w["C"], nthreads=threads)
         reps += 1
         dt = time.perf_counter() - t0
         if dt * threads >= 10.0 or dt >= 30.0:
             break
-    tokens = sh.batch * sh.seqlen * reps
-    # one thread on one batch row (a bounded sample of the same work)
+    tokens = rows * sh.seqlen * reps
+    # one thread on one batch row and a quarter of the heads
+    hq = max(1, sh.nheads // 4)
     t1 = time.perf_counter()
-    oracle.fwd(w["X"][:1], a[:1], w["B"][:1], w["C"][:1], nthreads=1)
+    oracle.fwd(w["X"][:1, :, :hq], a[:1, :, :hq], w["B"][:1], w["C"][:1], nthreads=1)
     dt1 = time.perf_counter() - t1
     model = ""
     try:
@@ -297,20 +345,25 @@ def cpu_baseline(sh):
     except OSError:
         pass
     return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "the full %dx%d-token batch (%d heads), %d times, through the sequential "
-                      "fp64 recurrence with (batch, head) slices spread over %d threads; %.2f s wall"
-                      % (sh.batch, sh.seqlen, sh.nheads, reps, threads, dt),
-            "single_thread_value": sh.seqlen / dt1, "single_thread_sample": "one batch row, one thread",
+            "sample": "%d of the %d batch rows (%d heads, %d steps each), %d time(s), through the "
+                      "sequential fp64 recurrence with (batch, head) slices spread over %d threads; "
+                      "%.2f s wall" % (rows, sh.batch, sh.nheads, sh.seqlen, reps, threads, dt),
+            "single_thread_value": sh.seqlen * hq / sh.nheads / dt1,
+            "single_thread_sample": "one batch row, %d of %d heads, one thread (tokens/s scaled to all "
+                                    "heads)" % (hq, sh.nheads),
             "cpu_model": model}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--workload", default="m2_2p7b",
+                    help="forward workload of the headline: m2_2p7b (default), m2_130m, or "
+                         "sweep<seqlen> (for profiling one workload alone)")
     ap.add_argument("--decode-only", action="store_true",
                     help="only time the decode step (batch 256, 80 heads; for profiling)")
     ap.add_argument("--bwd-only", action="store_true",
@@ -338,80 +391,93 @@ def main():
     import ssd_inputs as si
     import ssd_chunked_scan_chunk_amd as ssd  # noqa: F401  (fails loudly if libssd.so is missing)
 
-    sh = si.FWD_CONFIGS["m2_130m"]
-    tokens = sh.batch * sh.seqlen
     if args.decode_only:
         td, nbytes = bench_decode(args.steps, args.warmup)
         print(json.dumps({"decode_step": {"us_per_step": td * 1e6, "GB_per_s": nbytes / td / 1e9,
                                           "hbm_frac": nbytes / td / 1e9 / HBM_PEAK_GBS,
                                           "bytes_per_step": nbytes}}))
         return
+    s130 = si.FWD_CONFIGS["m2_130m"]
     if args.bwd_only:
-        tb, tda = bench_backward(sh, args.steps, args.warmup, 2)
-        fl = tokens * bwd_algo_flops_per_token(sh)
-        dfl, dby = bwd_da_work(sh)
+        tokens = s130.batch * s130.seqlen
+        tb, tda = bench_backward(s130, args.steps, args.warmup, 2)
+        fl = tokens * bwd_algo_flops_per_token(s130)
+        dfl, dby = bwd_da_work(s130)
         print(json.dumps({"backward_m2_130m": {"ms_per_step": tb * 1e3, "tokens_per_s": tokens / tb,
                                                "mfma_frac": fl / tb / 1e12 / BF16_PEAK_TFLOPS,
                                                "da_kernel_us": tda * 1e6,
                                                "da_mfma_frac": dfl / tda / 1e12 / BF16_PEAK_TFLOPS,
                                                "da_hbm_frac": dby / tda / 1e9 / HBM_PEAK_GBS}}))
         return
-    per_batch = tokens * fwd_algo_bytes_per_token(sh)
-    nbatch = max(2, int(np.ceil(2 * 256e6 / per_batch)))   # > 2x the Infinity Cache
-    t_step, t_kernel, plan, passes = bench_forward(sh, args.steps, args.warmup, nbatch)
 
-    algo_bytes = tokens * fwd_algo_bytes_per_token(sh)
-    algo_flops = tokens * fwd_algo_flops_per_token(sh)
+    wl = args.workload
+    sh = si.sweep_shape(int(wl[5:])) if wl.startswith("sweep") else si.FWD_CONFIGS[wl]
+    m = measure_forward(sh, args.steps, args.warmup)
+    t_kernel = m.pop("_t_kernel")
+    m.pop("_t_step")
+    tokens = sh.batch * sh.seqlen
+    algo_bytes = m["algo_bytes"]
     achieved = algo_bytes / t_kernel / 1e9 if t_kernel else None
+    names = {"m2_2p7b": "m2_2p7b SSD layer fwd + final state: batch 8, seqlen 4096, 80 heads, headdim 64, "
+                        "dstate 128, 1 group, chunk 256",
+             "m2_130m": "m2_130m SSD layer fwd: batch 4, seqlen 2048, 24 heads, headdim 64, dstate 128, "
+                        "1 group, chunk 256"}
+    workload = names.get(wl, "state-64 sweep fwd: batch 1, seqlen %d, 32 heads, headdim 64, dstate 64, "
+                             "1 group, chunk 256" % sh.seqlen)
+    profile = {"m2_2p7b": "k_mfma_seg_full_m2_2p7b_hbm_traffic.md",
+               "m2_130m": "k_mfma_seg_full_m2_130m_hbm_traffic.md"}.get(wl, "")
     out = {
         "metric": "SSD fwd tokens/s + MFMA% of bf16 peak at N=64/128; decode GB/s % of HBM peak",
-        "value": tokens / t_step,
+        "value": m["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": t_step * 1e3,
+        "ms_per_step": m["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) X/B/C, a = dt*A with Mamba-2 dt recipe; %d batches cycled)" % nbatch,
-        "config": {"workload": "m2_130m SSD layer fwd: batch 4, seqlen 2048, 24 heads, headdim 64, "
-                               "dstate 128, 1 group, chunk 256",
-                   "plan": {"algo": plan[0], "seg_chunks": plan[1], "nseg": plan[2]}},
+        "data": "synthetic (seeded N(0,1) X/B/C, a = dt*A per the workload's dt recipe; %d batch(es) cycled)"
+                % n_batches(sh),
+        "config": {"workload": workload, "plan": m["plan"]},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": (achieved / HBM_PEAK_GBS) if achieved else None, "traffic": stored_traffic(),
+                     "frac": (achieved / HBM_PEAK_GBS) if achieved else None,
+                     "traffic": stored_traffic(profile) if profile else None,
                      "kernel": "k_mfma_seg full pass", "kernel_ms": t_kernel * 1e3 if t_kernel else None,
                      "algo_bytes_per_launch": algo_bytes},
-        "passes": passes,
-        "mfma": {"achieved": algo_flops / t_step / 1e12, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                 "frac": algo_flops / t_step / 1e12 / BF16_PEAK_TFLOPS,
-                 "algo_flops_per_step": algo_flops},
+        "passes": m["passes"],
+        "mfma": {"achieved": m["algo_flops"] / (m["ms_per_step"] * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
+                 "unit": "TFLOP/s", "frac": m["mfma_frac"],
+                 "flops_per_step": m["algo_flops"], "count": "algorithmic, at the caller's chunk",
+                 "frac_blocks64": m["mfma_frac_blocks64"], "flops_per_step_blocks64": m["algo_flops_blocks64"]},
+        "hbm_frac_step": m["hbm_frac"],
     }
 
     if not args.no_secondary:
         sec = {}
-        for name, shp in (("m2_2p7b", si.FWD_CONFIGS["m2_2p7b"]), ("sweep_n64_L32768", si.sweep_shape(32768))):
-            tok = shp.batch * shp.seqlen
-            nb = max(1, int(np.ceil(2 * 256e6 / (tok * fwd_algo_bytes_per_token(shp)))))
-            ts, tk, pl, ps = bench_forward(shp, max(5, args.steps // 5), 2, nb)
-            fl = tok * fwd_algo_flops_per_token(shp)
-            sec[name] = {"tokens_per_s": tok / ts, "ms_per_step": ts * 1e3,
-                         "hbm_frac": tok * fwd_algo_bytes_per_token(shp) / ts / 1e9 / HBM_PEAK_GBS,
-                         "mfma_frac": fl / ts / 1e12 / BF16_PEAK_TFLOPS, "plan": list(pl),
-                         "full_pass_hbm_frac": (tok * fwd_algo_bytes_per_token(shp) / tk / 1e9 / HBM_PEAK_GBS
-                                                if tk else None), "passes": ps}
+        if wl != "m2_130m":
+            r = measure_forward(s130, args.steps, args.warmup)
+            r.pop("_t_kernel"), r.pop("_t_step")
+            sec["m2_130m"] = r
+        for L in si.SWEEP_SEQLENS:
+            shp = si.sweep_shape(L)
+            r = measure_forward(shp, max(5, args.steps // (1 + L // 65536)), 2)
+            r.pop("_t_kernel"), r.pop("_t_step")
+            sec["sweep_n64_L%d" % L] = r
         td, nbytes = bench_decode(max(20, args.steps), 5)
         sec["decode_step"] = {"workload": "batch 256, 80 heads, headdim 64, dstate 128, fp32 state in place",
                               "us_per_step": td * 1e6, "GB_per_s": nbytes / td / 1e9,
                               "hbm_frac": nbytes / td / 1e9 / HBM_PEAK_GBS, "tokens_per_s": 256 / td}
-        tb, tda = bench_backward(sh, max(10, args.steps // 2), 3, 2)
-        fl = tokens * bwd_algo_flops_per_token(sh)
-        dfl, dby = bwd_da_work(sh)
+        tokens130 = s130.batch * s130.seqlen
+        tb, tda = bench_backward(s130, max(10, args.steps // 2), 3, 2)
+        fl = tokens130 * bwd_algo_flops_per_token(s130)
+        dfl, dby = bwd_da_work(s130)
+        fwd130 = sec["m2_130m"]["ms_per_step"] if "m2_130m" in sec else m["ms_per_step"]
         sec["backward_m2_130m"] = {
             "workload": "gradients dX, da, dB, dC, d(initial state) of the 130M-shaped layer "
                         "for upstream dY and d(final state)",
-            "ms_per_step": tb * 1e3, "tokens_per_s": tokens / tb, "bwd_over_fwd": tb / t_step,
+            "ms_per_step": tb * 1e3, "tokens_per_s": tokens130 / tb, "bwd_over_fwd": tb * 1e3 / fwd130,
             "mfma_frac": fl / tb / 1e12 / BF16_PEAK_TFLOPS, "algo_flops_per_step": fl,
             # its dominant kernel, timed alone with HIP events
             "dominant_kernel": {"kernel": "k_bwd_da", "us": tda * 1e6,

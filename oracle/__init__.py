@@ -32,7 +32,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ssd_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# SSD_ORACLE_LIB names another build of ssd_oracle.c (a sanitizer build)
+_LIB_PATH = os.environ.get("SSD_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 
@@ -55,8 +56,8 @@ class _Dims(ctypes.Structure):
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH) or (
-                os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
+        if not os.environ.get("SSD_ORACLE_LIB") and (not os.path.exists(_LIB_PATH) or (
+                os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC))):
             build()
         lib = ctypes.CDLL(_LIB_PATH)
         dp = ctypes.POINTER(ctypes.c_double)

@@ -11,7 +11,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libssd.so")
+# SSD_LIB names another build of the same C ABI (the tests use it to run the
+# host-side validation under the sanitizers)
+LIB_PATH = os.environ.get("SSD_LIB") or os.path.join(HERE, "libssd.so")
 
 SSD_OK, SSD_ERR_NULL, SSD_ERR_SHAPE, SSD_ERR_DTYPE, SSD_ERR_ALIGN = 0, 1, 2, 3, 4
 SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_HIP, SSD_ERR_ALIAS = 5, 6, 7, 8

@@ -51,6 +51,7 @@ bool overlap(const Range& a, const Range& b) {
 
 constexpr int64_t kNumCU = 256;          // MI355X compute units
 constexpr int64_t kLdsPerCU = 160 * 1024;
+constexpr int64_t kMfmaThreads = 512;    // the largest workgroup of the MFMA kernels
 
 // LDS of the MFMA kernel's full pass for (P, N): double-buffered 64-step
 // blocks of X for the workgroup's heads, B and C, the shared score tiles and
@@ -184,8 +185,9 @@ ssd_status make_plan(const ssd_fwd_desc* d, Plan* p) {
         p->seg_chunks = k;
         p->nseg = (s.nc + k - 1) / k;
         if (p->nseg > 65535) return fail(SSD_ERR_UNSUPPORTED, "too many segments (%lld)", (long long)p->nseg);
-        // one-dimensional grid of (batch, segment, head set) workgroups of 256 threads
-        if ((s.Bz * p->nseg * s.H + 8) * 256 >= ((int64_t)1 << 32))
+        // one-dimensional grid of at most batch*segments*heads workgroups (plus
+        // padding to the XCD count) of kMfmaThreads threads each
+        if ((s.Bz * p->nseg * s.H + 8) * kMfmaThreads >= ((int64_t)1 << 32))
             return fail(SSD_ERR_UNSUPPORTED, "batch*segments*heads (%lld) too large for one launch",
                         (long long)(s.Bz * p->nseg * s.H));
         if (p->nseg > 1) {
@@ -313,7 +315,10 @@ ssd_status make_bwd_plan(const ssd_fwd_desc* d, BwdPlan* bp) {
                         "(chunk in {64,128,256}, headdim in {32,64}, dstate in {64,128})",
                         (long long)s.Q, (long long)s.P, (long long)s.N);
     }
-    if ((s.Bz * s.nc * s.H + 8) * 256 >= ((int64_t)1 << 32) || s.nc > 0x7fffffff)
+    // the chunk-state and dX passes launch up to batch*chunks*heads workgroups,
+    // the exchanged-dimension passes up to batch*chunks*(heads+groups), each of
+    // at most kMfmaThreads threads
+    if ((s.Bz * s.nc * (s.H + s.G) + 8) * kMfmaThreads >= ((int64_t)1 << 32) || s.nc > 0x7fffffff)
         return fail(SSD_ERR_UNSUPPORTED, "batch*chunks*heads too large for one launch");
     // the copy kernels launch (row blocks of up to 256 threads) x steps blocks
     const int64_t row_items = s.H * (s.N > s.P ? s.N : s.P) * bp->es / 16;

@@ -803,10 +803,6 @@ hipError_t launch_bwd_da_valu(const FwdShape& s, const float* X, const float* dY
     return hipGetLastError();
 }
 
-bool bwd_da_supported(int64_t Q, int64_t P, int64_t N) {
-    return (Q == 64 || Q == 128 || Q == 256) && (P == 32 || P == 64) && (N == 64 || N == 128);
-}
-
 hipError_t launch_bwd_da(const FwdShape& s, const void* X, const void* dY, const float* a,
                          const void* B, const void* C, const float* Sin, const float* Srev,
                          bool adj_reversed, float* da, hipStream_t st)

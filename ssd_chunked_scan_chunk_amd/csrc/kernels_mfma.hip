@@ -94,7 +94,7 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 constexpr int kXcds = 8;     // MI355X accelerator complex dies; workgroups alternate over them
 constexpr int kT = 64;       // steps per block
 constexpr int kWaves = 8;    // wavefronts per workgroup (two per SIMD)
-constexpr int kStateWaves = 6;                   // waves that carry head states
+constexpr int kStateWaves = kMfmaStateWaves;     // waves that carry head states
 constexpr int kAuxThreads = 64 * (kWaves - kStateWaves);   // copy and score waves
 constexpr int kThreads = 64 * kWaves;
 constexpr int kPRow = 40;    // padded row (elements) of a shared 32x32 bf16 score tile (16-byte aligned)
@@ -880,12 +880,6 @@ __global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(S
         }
     }
 }
-
-bool mfma_supported(int64_t Q, int64_t P, int64_t N) {
-    return (Q == 64 || Q == 128 || Q == 256) && (P == 32 || P == 64) && (N == 64 || N == 128);
-}
-
-int64_t mfma_heads_per_workgroup(int64_t P, int64_t N) { (void)N; return kStateWaves / (P / 32); }
 
 #define SSD_MFMA_DISPATCH(MACRO)                     \
     if (s.P == 64 && s.N == 128) MACRO(64, 128)      \

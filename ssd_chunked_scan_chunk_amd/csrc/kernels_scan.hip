@@ -40,7 +40,7 @@ __global__ __launch_bounds__(kValuThreads) void k_valu_fwd(
     float* sS = sCs + Q;        // [P*N] carried state
     float* sTot = sS + P * N;   // [4] scan scratch
 
-    const int h = blockIdx.x, b = blockIdx.y, g = h * G / H;
+    const int h = blockIdx.x, b = blockIdx.y, g = h / (H / G);
     const int tid = threadIdx.x;
     const int PN = P * N;
     const int64_t bh = (int64_t)b * H + h;
@@ -96,10 +96,6 @@ __global__ __launch_bounds__(kValuThreads) void k_valu_fwd(
     __syncthreads();
     if (S_fin)
         for (int k = tid; k < PN; k += kValuThreads) S_fin[bh * PN + k] = sS[k];
-}
-
-bool valu_fwd_supported(const FwdShape& s) {
-    return s.Q >= 1 && s.Q <= 256 && s.P * s.N <= 16384;
 }
 
 hipError_t launch_valu_fwd(const FwdShape& s, bool bf16, const void* X, const float* a,

@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256) void k_step(float* __restrict__ state, const T
     constexpr int RPP = 256 / LPR;       // rows per pass of the workgroup
     constexpr int P = RPP * ROWS;
     const int bh = blockIdx.x;
-    const int b = bh / H, h = bh - b * H, g = h * G / H;
+    const int b = bh / H, h = bh - b * H, g = h / (H / G);
     const int tid = threadIdx.x;
     const int nq = tid % LPR, r0 = tid / LPR;
 
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256) void k_step_any(float* __restrict__ state, con
     const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (row >= rows) return;
     const int64_t bh = row / P;
-    const int b = (int)(bh / H), h = (int)(bh - (int64_t)b * H), g = h * G / H;
+    const int b = (int)(bh / H), h = (int)(bh - (int64_t)b * H), g = h / (H / G);
     using Acc = typename AccOf<T>::type;
     const Acc e = AccOf<T>::exp(a[bh]);
     const Acc xp = Elem<T>::load(x + row);

@@ -1,0 +1,26 @@
+// shapes.cpp -- host-side description of the compiled kernel set: which
+// shapes each kernel family takes and how the forward MFMA kernel groups
+// heads into workgroups.  Host code only (no kernels), so the C ABI's
+// planning can also be built and checked without a GPU toolchain.
+#include "ssd_launch.hpp"
+
+namespace ssd {
+
+bool mfma_supported(int64_t Q, int64_t P, int64_t N) {
+    return (Q == 64 || Q == 128 || Q == 256) && (P == 32 || P == 64) && (N == 64 || N == 128);
+}
+
+int64_t mfma_heads_per_workgroup(int64_t P, int64_t N) {
+    (void)N;
+    return kMfmaStateWaves / (P / 32);
+}
+
+bool valu_fwd_supported(const FwdShape& s) {
+    return s.Q >= 1 && s.Q <= 256 && s.P * s.N <= 16384;
+}
+
+bool bwd_da_supported(int64_t Q, int64_t P, int64_t N) {
+    return (Q == 64 || Q == 128 || Q == 256) && (P == 32 || P == 64) && (N == 64 || N == 128);
+}
+
+}  // namespace ssd

@@ -1,4 +1,4 @@
-// ssd_device.cuh -- device-side building blocks shared by the gfx950 kernels:
+// ssd_device.hpp -- device-side building blocks shared by the gfx950 kernels:
 // bf16 storage conversion, wavefront/workgroup fp32 prefix sums and the MFMA
 // fragment types.  gfx950 only (wave64, v_mfma_f32_16x16x32_bf16).
 #pragma once

@@ -6,6 +6,10 @@
 
 namespace ssd {
 
+// State wavefronts of the forward MFMA kernel's workgroup (each carries one
+// 32-wide head-dim slice of one head's state).
+constexpr int kMfmaStateWaves = 6;
+
 struct FwdShape {
     int64_t Bz, L, H, P, N, G, Q;
     int64_t nc;  // ceil(L / Q)
@@ -48,7 +52,7 @@ hipError_t launch_state_scan(const FwdShape& s, int64_t nu, int64_t ustride, con
 
 // ---- MFMA segmented path (bf16) ----------------------------------------------------
 bool mfma_supported(int64_t Q, int64_t P, int64_t N);
-// heads sharing B and C in one MFMA workgroup (four wavefronts)
+// heads sharing B and C in one MFMA workgroup (kMfmaStateWaves / (P / 32))
 int64_t mfma_heads_per_workgroup(int64_t P, int64_t N);
 // Pass A: for segments [0, nseg_run) of seg_chunks chunks each, the state at
 // the end of the segment starting from zero -> Sseg [Bz][nseg_total][H][P][N]

@@ -84,14 +84,14 @@ class FwdShape:
     chunk: int
     dtype: str
     dt_recipe: str = "standard"
-    final_state: bool = True
+    final_state: bool = True     # whether the workload returns the final state
 
 
 FWD_CONFIGS = {
     # tiny fp32 case that the oracle finishes instantly
     "tiny_f32": FwdShape(1, 256, 2, 16, 16, 1, 64, F32),
     # Mamba-2 130M-shaped layer
-    "m2_130m": FwdShape(4, 2048, 24, 64, 128, 1, 256, BF16, dt_recipe="mamba2_dt"),
+    "m2_130m": FwdShape(4, 2048, 24, 64, 128, 1, 256, BF16, dt_recipe="mamba2_dt", final_state=False),
     # Mamba-2 2.7B-shaped layer, returns the final state
     "m2_2p7b": FwdShape(8, 4096, 80, 64, 128, 1, 256, BF16),
 }
@@ -100,7 +100,7 @@ SWEEP_SEQLENS = (512, 2048, 8192, 32768, 131072, 524288)
 
 
 def sweep_shape(seqlen: int) -> FwdShape:
-    return FwdShape(1, seqlen, 32, 64, 64, 1, 256, BF16)
+    return FwdShape(1, seqlen, 32, 64, 64, 1, 256, BF16, final_state=False)
 
 
 @dataclasses.dataclass(frozen=True)

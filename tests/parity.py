@@ -29,6 +29,40 @@ def slice_rel_err(got, ref, slice_axes):
     return float((num / den).max())
 
 
+def elementwise_diag(got, ref, slice_axes, floor=1e-3):
+    """Diagnostic: max |got - ref| / |ref| over the entries whose |ref| is at
+    least ``floor`` times their slice's largest |ref| (elementwise relative
+    error is unbounded near zero, so it is logged, not bounded)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    other = tuple(i for i in range(ref.ndim) if i not in slice_axes)
+    smax = np.abs(ref).max(axis=other, keepdims=True)
+    keep = np.abs(ref) >= floor * smax
+    if not keep.any():
+        return 0.0
+    return float((np.abs(got - ref)[keep] / np.abs(ref)[keep]).max())
+
+
+def chunk_rel_err(got, ref, chunk):
+    """Y [Bz, L, H, P]: max over (batch, head, chunk of ``chunk`` steps) of
+    max|got - ref| / max|ref| inside that chunk -- the slice-normwise error
+    with each chunk normalised by its own magnitude (a tighter check than one
+    normalisation over a whole long sequence)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    Bz, L, H, P = ref.shape
+    nc = (L + chunk - 1) // chunk
+    pad = nc * chunk - L
+    if pad:
+        z = np.zeros((Bz, pad, H, P))
+        got, ref = np.concatenate([got, z], 1), np.concatenate([ref, z], 1)
+    d = np.abs(got - ref).reshape(Bz, nc, chunk, H, P).max(axis=(2, 4))
+    m = np.abs(ref).reshape(Bz, nc, chunk, H, P).max(axis=(2, 4))
+    if np.isnan(got).any():
+        return float("inf")
+    return float((d / np.where(m == 0, 1.0, m)).max())
+
+
 def y_err(got, ref):
     """Y is [Bz, L, H, P]: slices are (batch, head)."""
     return slice_rel_err(got, ref, (0, 2))

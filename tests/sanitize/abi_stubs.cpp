@@ -1,0 +1,43 @@
+// abi_stubs.cpp -- kernel launchers for a host-only build of the C ABI
+// (api.cpp + shapes.cpp) under AddressSanitizer / UndefinedBehaviorSanitizer.
+// That build exercises argument validation and planning on the CPU; every
+// call it is given fails validation or is host-only, so none of these should
+// run.  If one does, it reports hipErrorNotSupported instead of launching.
+#include "ssd_launch.hpp"
+
+extern "C" const char* hipGetErrorString(hipError_t) { return "stub launcher (host-only build)"; }
+
+namespace ssd {
+#define SSD_STUB return hipErrorNotSupported
+hipError_t launch_valu_fwd(const FwdShape&, bool, const void*, const float*, const void*, const void*,
+                           const float*, void*, float*, hipStream_t, float*, bool) { SSD_STUB; }
+hipError_t launch_chunk_cumsum(const FwdShape&, const float*, float*, float*, hipStream_t) { SSD_STUB; }
+hipError_t launch_state_scan(const FwdShape&, int64_t, int64_t, const float*, const float*, int64_t,
+                             int64_t, const float*, float*, int64_t, float*, int64_t, hipStream_t) { SSD_STUB; }
+hipError_t launch_mfma_state(const FwdShape&, int64_t, int64_t, int64_t, const void*, const float*,
+                             const void*, float*, float*, hipStream_t) { SSD_STUB; }
+hipError_t launch_mfma_out(const FwdShape&, int64_t, int64_t, const void*, const float*, const void*,
+                           const void*, StateSrc, void*, float*, hipStream_t) { SSD_STUB; }
+hipError_t launch_mfma_out_xg(const FwdShape&, int64_t, const void*, const float*, const void*,
+                              const void*, StateSrc, void*, hipStream_t) { SSD_STUB; }
+hipError_t launch_step(int64_t, int64_t, int64_t, int64_t, int64_t, bool, float*, const void*,
+                       const float*, const void*, const void*, void*, hipStream_t) { SSD_STUB; }
+hipError_t launch_remap_rows(void*, const void*, int64_t, int64_t, int64_t, int64_t, int64_t, int64_t,
+                             hipStream_t) { SSD_STUB; }
+hipError_t launch_bcast_heads(void*, const void*, int64_t, int64_t, int64_t, int64_t, int64_t, int64_t,
+                              int64_t, int64_t, hipStream_t) { SSD_STUB; }
+hipError_t launch_remap_a(float*, const float*, int64_t, int64_t, int64_t, int64_t, int64_t, int64_t,
+                          int64_t, hipStream_t) { SSD_STUB; }
+hipError_t launch_state_transpose(float*, const float*, int64_t, int64_t, int64_t, hipStream_t) { SSD_STUB; }
+hipError_t launch_group_sum(void*, const void*, int64_t, int64_t, int64_t, int64_t, int64_t, int64_t,
+                            int64_t, int64_t, bool, bool, hipStream_t) { SSD_STUB; }
+hipError_t launch_scale_state_by_a0(float*, const float*, int64_t, int64_t, int64_t, int64_t,
+                                    hipStream_t) { SSD_STUB; }
+hipError_t launch_bwd_da_valu(const FwdShape&, const float*, const float*, const float*, const float*,
+                              const float*, const float*, const float*, float*, hipStream_t) { SSD_STUB; }
+hipError_t launch_bwd_da(const FwdShape&, const void*, const void*, const float*, const void*,
+                         const void*, const float*, const float*, bool, float*, hipStream_t) { SSD_STUB; }
+hipError_t launch_fill_zero(float*, int64_t, hipStream_t) { SSD_STUB; }
+hipError_t launch_copy_f32(float*, const float*, int64_t, hipStream_t) { SSD_STUB; }
+#undef SSD_STUB
+}  // namespace ssd

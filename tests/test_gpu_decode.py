@@ -123,3 +123,33 @@ def test_decode_exact_decay_free():
         yr_bf16 = si.widen(si.f32_to_bf16_bits(yr.astype(np.float32)), si.BF16)
         assert np.array_equal(y.float().cpu().numpy().astype(np.float64), yr_bf16), t
     assert np.array_equal(state.cpu().numpy().astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("dtype,seg", [(si.BF16, 0), (si.BF16, 1), (si.F32, 0)])
+def test_prefill_then_decode_handoff(dtype, seg):
+    # constant-memory inference: a chunked forward over the first L1 steps
+    # (ragged last chunk; seg=1 forces one chunk per segment, so the final
+    # state comes out of the segmented plan) hands its final state to ssd_step,
+    # which continues in place for L2 steps; outputs and the state after L1+L2
+    # steps must match the oracle run over the whole sequence
+    Bz, H, P, N, G, Q, L1, L2 = 3, 8, 64, 128, 2, 256, 700, 40
+    log("prefill->decode %s seg=%d" % (dtype, seg))
+    sh = si.FwdShape(Bz, L1 + L2, H, P, N, G, Q, dtype)
+    d = si.make_fwd(sh, seed=23)
+    g = upload_fwd(d)
+    Yp, state = ssd.chunk_scan_fwd(g["X"][:, :L1].contiguous(), g["a"][:, :L1].contiguous(),
+                                   g["B"][:, :L1].contiguous(), g["C"][:, :L1].contiguous(), Q,
+                                   return_final_state=True, seg_chunks=seg)
+    ys = []
+    for t in range(L1, L1 + L2):
+        ys.append(ssd.step(state, g["X"][:, t].contiguous(), g["a"][:, t].contiguous(),
+                           g["B"][:, t].contiguous(), g["C"][:, t].contiguous()))
+    Yd = torch.stack(ys, dim=1)
+    torch.cuda.synchronize()
+    w = widen_fwd(d)
+    Yr, Sr = oracle.fwd(w["X"], w["a"], w["B"], w["C"])
+    tol = 1e-5 if dtype == si.F32 else 2e-2
+    ep, ed = y_err(host_f64(Yp), Yr[:, :L1]), y_err(host_f64(Yd), Yr[:, L1:])
+    es = slice_rel_err(host_f64(state), Sr, (0, 1))
+    log("   err prefill Y=%.3e decode y=%.3e state=%.3e" % (ep, ed, es))
+    assert ep < tol and ed < tol and es < tol, (ep, ed, es)
