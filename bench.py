@@ -70,20 +70,27 @@ def fwd_algo_flops_per_token(sh, block=KERNEL_BLOCK):
 
 
 def stored_traffic(profile):
-    """HBM bytes per launch of the full-pass kernel from a committed rocprofv3
+    """HBM bytes per launch of the fused-pass kernel from a committed rocprofv3
     FETCH_SIZE/WRITE_SIZE summary (calibrated on a plain copy), or None when
     that summary was taken on a different kernel source."""
-    import hashlib
-    src = os.path.join(ROOT, "ssd_chunked_scan_chunk_amd", "csrc", "kernels_mfma.hip")
     prof = os.path.join(ROOT, "profiles", profile)
     try:
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        sha = fused_kernel_sha()
         fields = dict(l.split(":", 1) for l in open(prof) if l.startswith(("traffic_bytes", "kernel_source")))
     except (OSError, ValueError):
         return None
     if fields.get("kernel_source_sha256_16", "").strip() != sha:
         return None
     return int(fields["traffic_bytes_per_launch"])
+
+
+def fused_kernel_sha():
+    """First 16 hex digits of the SHA-256 of the fused-pass kernel's sources."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("kernels_fwd.hip", "mfma_util.hpp"):
+        h.update(open(os.path.join(ROOT, "ssd_chunked_scan_chunk_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def upload(d):
@@ -123,7 +130,7 @@ def bench_forward(sh, steps, warmup, nbatch, seed0=0):
     Ys = [torch.empty_like(b["X"]) for b in batches]
     fin = torch.empty((sh.batch, sh.nheads, sh.headdim, sh.dstate), dtype=torch.float32, device="cuda")
     X0 = batches[0]["X"]
-    plan = ssd.fwd_plan(X0, batches[0]["B"], sh.chunk)
+    plan = ssd.fwd_plan(X0, batches[0]["B"], sh.chunk, with_units=True)
     nws = ssd.workspace_bytes(X0, batches[0]["B"], sh.chunk)
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
 
@@ -141,7 +148,7 @@ def bench_forward(sh, steps, warmup, nbatch, seed0=0):
     # several: the state-only pass over the segments, the segment scan, and
     # the full pass (the dominant kernel) fed entering states (their values
     # do not change the work).
-    algo, seg_chunks, nseg = plan
+    algo, seg_chunks, nseg, units = plan
     passes = {}
     t_kernel = None
     if algo == ssd.SSD_ALGO_MFMA and nseg == 1:
@@ -154,7 +161,7 @@ def bench_forward(sh, steps, warmup, nbatch, seed0=0):
         def full(i):
             g = batches[i % nbatch]
             ssd.chunk_scan(g["X"], g["a"], g["B"], g["C"], sh.chunk, states_in=Sin,
-                           seg_chunks=seg_chunks, Y=Ys[i % nbatch])
+                           seg_chunks=seg_chunks, Y=Ys[i % nbatch], wg_units=units)
 
         for i in range(warmup):
             full(i)
@@ -195,7 +202,7 @@ def measure_forward(sh, steps, warmup):
     fq = tok * fwd_algo_flops_per_token(sh, sh.chunk)
     f64 = tok * fwd_algo_flops_per_token(sh)
     return {"tokens_per_s": tok / t_step, "ms_per_step": t_step * 1e3,
-            "plan": {"algo": plan[0], "seg_chunks": plan[1], "nseg": plan[2]},
+            "plan": {"algo": plan[0], "seg_chunks": plan[1], "nseg": plan[2], "wg_units": plan[3]},
             "hbm_frac": nbytes / t_step / 1e9 / HBM_PEAK_GBS,
             "full_pass_hbm_frac": nbytes / t_kernel / 1e9 / HBM_PEAK_GBS if t_kernel else None,
             "mfma_frac": fq / t_step / 1e12 / BF16_PEAK_TFLOPS,
@@ -424,8 +431,8 @@ def main():
                         "1 group, chunk 256"}
     workload = names.get(wl, "state-64 sweep fwd: batch 1, seqlen %d, 32 heads, headdim 64, dstate 64, "
                              "1 group, chunk 256" % sh.seqlen)
-    profile = {"m2_2p7b": "k_mfma_seg_full_m2_2p7b_hbm_traffic.md",
-               "m2_130m": "k_mfma_seg_full_m2_130m_hbm_traffic.md"}.get(wl, "")
+    profile = {"m2_2p7b": "k_fwd_m2_2p7b_hbm_traffic.md",
+               "m2_130m": "k_fwd_m2_130m_hbm_traffic.md"}.get(wl, "")
     out = {
         "metric": "SSD fwd tokens/s + MFMA% of bf16 peak at N=64/128; decode GB/s % of HBM peak",
         "value": m["tokens_per_s"],
@@ -444,7 +451,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": (achieved / HBM_PEAK_GBS) if achieved else None,
                      "traffic": stored_traffic(profile) if profile else None,
-                     "kernel": "k_mfma_seg full pass", "kernel_ms": t_kernel * 1e3 if t_kernel else None,
+                     "kernel": "k_fwd (fused pass)", "kernel_ms": t_kernel * 1e3 if t_kernel else None,
                      "algo_bytes_per_launch": algo_bytes},
         "passes": m["passes"],
         "mfma": {"achieved": m["algo_flops"] / (m["ms_per_step"] * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,

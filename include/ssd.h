@@ -74,12 +74,17 @@ typedef enum ssd_algo {
  * form and everything across blocks through the carried state.  The result
  * does not depend on chunk beyond rounding.  seg_chunks (MFMA path) is the
  * number of consecutive chunks one workgroup walks while carrying the state
- * in registers; 0 lets the library choose from the shape. */
+ * in registers; 0 lets the library choose from the shape.  wg_units (MFMA
+ * path) is the number of 32-wide head-dim slices of heads (units) one
+ * workgroup of the fused forward pass carries, 4, 5 or 6; 0 lets the library
+ * choose.  Neither changes the result beyond rounding order. */
 typedef struct ssd_fwd_desc {
     int64_t batch, seqlen, nheads, headdim, dstate, ngroups, chunk;
     int32_t dtype;      /* ssd_dtype */
     int32_t algo;       /* ssd_algo  */
     int64_t seg_chunks; /* 0 = automatic */
+    int32_t wg_units;   /* 0 = automatic, else 4, 5 or 6 */
+    int32_t reserved;   /* must be 0 */
 } ssd_fwd_desc;
 
 typedef struct ssd_step_desc {
@@ -93,10 +98,11 @@ typedef struct ssd_step_desc {
 ssd_status ssd_fwd_workspace_bytes(const ssd_fwd_desc* desc, size_t* bytes);
 
 /* The chunk/segment plan the library uses for *desc: *algo receives the
- * ssd_algo that runs, *seg_chunks the chunks per segment (MFMA path) and
- * *nseg the number of segments.  Host only. */
+ * ssd_algo that runs, *seg_chunks the chunks per segment (MFMA path), *nseg
+ * the number of segments and *wg_units the units per workgroup of the fused
+ * pass (MFMA path; 0 otherwise).  Any output pointer may be NULL.  Host only. */
 ssd_status ssd_fwd_plan(const ssd_fwd_desc* desc, int32_t* algo, int64_t* seg_chunks,
-                        int64_t* nseg);
+                        int64_t* nseg, int32_t* wg_units);
 
 /* Full forward: the four stages (segment sums, intra-chunk masked product,
  * chunk states with the inter-chunk state scan, state-to-output) over the

@@ -116,38 +116,43 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _desc(X, B, chunk, algo, seg_chunks):
+def _desc(X, B, chunk, algo, seg_chunks, wg_units=0):
     Bz, L, H, P = X.shape
     G, N = B.shape[2], B.shape[3]
-    return _lib.fwd_desc(Bz, L, H, P, N, G, int(chunk), _dtype_code(X), int(algo), int(seg_chunks))
+    return _lib.fwd_desc(Bz, L, H, P, N, G, int(chunk), _dtype_code(X), int(algo), int(seg_chunks),
+                         int(wg_units))
 
 
-def fwd_plan(X, B, chunk, algo=SSD_ALGO_AUTO, seg_chunks=0):
-    """(algo, seg_chunks, nseg) the library would use for these shapes."""
-    d = _desc(X, B, chunk, algo, seg_chunks)
+def fwd_plan(X, B, chunk, algo=SSD_ALGO_AUTO, seg_chunks=0, wg_units=0, with_units=False):
+    """(algo, seg_chunks, nseg) the library would use for these shapes, plus
+    the fused pass's units per workgroup when ``with_units``."""
+    d = _desc(X, B, chunk, algo, seg_chunks, wg_units)
     a = ctypes.c_int32()
     k = ctypes.c_int64()
     n = ctypes.c_int64()
-    _lib.check(_L().ssd_fwd_plan(ctypes.byref(d), ctypes.byref(a), ctypes.byref(k), ctypes.byref(n)))
-    return a.value, k.value, n.value
+    u = ctypes.c_int32()
+    _lib.check(_L().ssd_fwd_plan(ctypes.byref(d), ctypes.byref(a), ctypes.byref(k), ctypes.byref(n),
+                                 ctypes.byref(u)))
+    return (a.value, k.value, n.value, u.value) if with_units else (a.value, k.value, n.value)
 
 
-def workspace_bytes(X, B, chunk, algo=SSD_ALGO_AUTO, seg_chunks=0) -> int:
-    d = _desc(X, B, chunk, algo, seg_chunks)
+def workspace_bytes(X, B, chunk, algo=SSD_ALGO_AUTO, seg_chunks=0, wg_units=0) -> int:
+    d = _desc(X, B, chunk, algo, seg_chunks, wg_units)
     n = ctypes.c_size_t()
     _lib.check(_L().ssd_fwd_workspace_bytes(ctypes.byref(d), ctypes.byref(n)))
     return n.value
 
 
 def chunk_scan_fwd(X, a, B, C, chunk, initial_state=None, return_final_state=False,
-                   algo=SSD_ALGO_AUTO, seg_chunks=0, Y=None, final_state=None, workspace=None):
+                   algo=SSD_ALGO_AUTO, seg_chunks=0, Y=None, final_state=None, workspace=None,
+                   wg_units=0):
     """Full SSD forward.  Returns (Y, final_state or None)."""
     Bz, L, H, P, G, N = _check_fwd_inputs(X, a, B, C)
     dev = X.device
     _check("initial_state", initial_state, (Bz, H, P, N), torch.float32, dev)
     _check("Y", Y, X.shape, X.dtype, dev)
     _check("final_state", final_state, (Bz, H, P, N), torch.float32, dev)
-    d = _desc(X, B, chunk, algo, seg_chunks)
+    d = _desc(X, B, chunk, algo, seg_chunks, wg_units)
     if Y is None:
         Y = torch.empty_like(X)
     if final_state is None and return_final_state:
@@ -320,14 +325,14 @@ def state_passing(dstates, lam, chunk, seqlen, initial_state=None, return_final_
     return out, fin
 
 
-def chunk_scan(X, a, B, C, chunk, states_in=None, seg_chunks=1, Y=None):
+def chunk_scan(X, a, B, C, chunk, states_in=None, seg_chunks=1, Y=None, wg_units=0):
     """Stages 2 + 5: Y from the inputs and the states entering each unit of
     `seg_chunks` chunks ([Bz,U,H,P,N]; None = zero)."""
     Bz, L, H, P, G, N = _check_fwd_inputs(X, a, B, C)
     U = _units(L, chunk, seg_chunks)
     _check("states_in", states_in, (Bz, U, H, P, N), torch.float32, X.device)
     _check("Y", Y, X.shape, X.dtype, X.device)
-    d = _desc(X, B, chunk, SSD_ALGO_MFMA, max(1, int(seg_chunks)))
+    d = _desc(X, B, chunk, SSD_ALGO_MFMA, max(1, int(seg_chunks)), wg_units)
     if Y is None:
         Y = torch.empty_like(X)
     _lib.check(_L().ssd_chunk_scan(ctypes.byref(d), _ptr(X), _ptr(a), _ptr(B), _ptr(C),

@@ -39,7 +39,8 @@ class FwdDesc(ctypes.Structure):
                 ("nheads", ctypes.c_int64), ("headdim", ctypes.c_int64),
                 ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
                 ("chunk", ctypes.c_int64), ("dtype", ctypes.c_int32),
-                ("algo", ctypes.c_int32), ("seg_chunks", ctypes.c_int64)]
+                ("algo", ctypes.c_int32), ("seg_chunks", ctypes.c_int64),
+                ("wg_units", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class StepDesc(ctypes.Structure):
@@ -70,7 +71,8 @@ def load(path: str = LIB_PATH):
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     pd = ctypes.POINTER(FwdDesc)
     lib.ssd_fwd_workspace_bytes.argtypes = [pd, ctypes.POINTER(sz)]
-    lib.ssd_fwd_plan.argtypes = [pd, ctypes.POINTER(i32), ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    lib.ssd_fwd_plan.argtypes = [pd, ctypes.POINTER(i32), ctypes.POINTER(i64), ctypes.POINTER(i64),
+                                 ctypes.POINTER(i32)]
     lib.ssd_chunk_scan_fwd.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ssd_step.argtypes = [ctypes.POINTER(StepDesc), vp, vp, vp, vp, vp, vp, vp]
     lib.ssd_chunk_cumsum.argtypes = [pd, vp, vp, vp, vp]
@@ -80,7 +82,8 @@ def load(path: str = LIB_PATH):
     lib.ssd_bwd_workspace_bytes.argtypes = [pd, ctypes.POINTER(sz)]
     lib.ssd_chunk_scan_bwd.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ssd_bwd_da.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp]
-    for f in ("ssd_fwd_workspace_bytes", "ssd_fwd_plan", "ssd_chunk_scan_fwd", "ssd_step",
+    for f in ("ssd_fwd_workspace_bytes", "ssd_fwd_plan", "ssd_chunk_scan_fwd",
+              "ssd_step",
               "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan",
               "ssd_bwd_workspace_bytes", "ssd_chunk_scan_bwd", "ssd_bwd_da"):
         getattr(lib, f).restype = ctypes.c_int
@@ -100,6 +103,6 @@ def check(status: int):
 
 
 def fwd_desc(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype,
-             algo=SSD_ALGO_AUTO, seg_chunks=0) -> FwdDesc:
+             algo=SSD_ALGO_AUTO, seg_chunks=0, wg_units=0) -> FwdDesc:
     return FwdDesc(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype, algo,
-                   seg_chunks)
+                   seg_chunks, wg_units, 0)

@@ -68,6 +68,7 @@ int64_t mfma_lds_bytes(int64_t P, int64_t N) {
 struct Plan {
     int32_t algo;
     int64_t seg_chunks, nseg;
+    int sw;          // units per workgroup of the fused pass (MFMA path)
     size_t ws;
     ssd::FwdShape s;
     bool bf16;
@@ -91,6 +92,9 @@ ssd_status check_desc(const ssd_fwd_desc* d, bool need_chunk_le_256) {
         return fail(SSD_ERR_DTYPE, "dtype %d is not SSD_F32 or SSD_BF16", (int)d->dtype);
     if (d->algo < SSD_ALGO_AUTO || d->algo > SSD_ALGO_MFMA)
         return fail(SSD_ERR_UNSUPPORTED, "unknown algo %d", (int)d->algo);
+    if (d->wg_units != 0 && (d->wg_units < 4 || d->wg_units > 6))
+        return fail(SSD_ERR_UNSUPPORTED, "wg_units must be 0 (automatic), 4, 5 or 6 (got %d)", (int)d->wg_units);
+    if (d->reserved != 0) return fail(SSD_ERR_SHAPE, "reserved must be 0");
     if (need_chunk_le_256 && d->chunk > 256)
         return fail(SSD_ERR_UNSUPPORTED, "chunk %lld > 256", (long long)d->chunk);
     // grid limits (dims are launched as unsigned grid sizes) and 32-bit in-slice indexing
@@ -110,47 +114,84 @@ ssd::FwdShape shape_of(const ssd_fwd_desc* d) {
     return s;
 }
 
-// Segment plan of the MFMA path.  A workgroup (the heads of one group that
-// share it) walks k consecutive chunks; nseg = ceil(nc / k) segments per
-// (b, head set).  Estimated time in microseconds, from measurements of the
-// kernels on MI355X: a full-pass block of 64 steps takes about kBlockUs on
-// one CU, a state-only block about kStateFrac of that, and more than one
-// segment adds the state round trips through HBM (written by the state
-// pass, read and written by the segment scan, read by the full pass) and
-// two launches.  For each segment count only the most balanced k is tried;
-// the cheapest wins, ties going to fewer segments.
-int64_t auto_seg_chunks(const ssd::FwdShape& s) {
-    constexpr double kBlockUs = 6.5, kStateFrac = 0.45, kStateBytesPerUs = 4.0e6, kLaunchUs = 4.0;
-    const int64_t per_cu = kLdsPerCU / mfma_lds_bytes(s.P, s.N);
-    const int64_t slots = kNumCU * (per_cu > 0 ? per_cu : 1);
-    const int64_t hw = ssd::mfma_heads_per_workgroup(s.P, s.N);
-    const int64_t wg = s.Bz * s.G * ((s.H / s.G + hw - 1) / hw);  // workgroups per segment
-    const double blocks_per_chunk = (double)((s.Q + 63) / 64);
-    const double state_bytes = 4.0 * (double)(s.Bz * s.H * s.P * s.N) * 4.0;  // per segment boundary
-    const int64_t max_seg = s.nc < 65535 ? s.nc : 65535;
-    double best = 1e300;
-    int64_t best_k = s.nc;
-    int64_t prev_k = -1;
-    for (int64_t want = 1; want <= max_seg; ++want) {
-        const int64_t k = (s.nc + want - 1) / want;   // longest segment
-        if (k == prev_k) continue;
-        prev_k = k;
-        const int64_t nseg = (s.nc + k - 1) / k;
-        const double blocks = (double)k * blocks_per_chunk;
-        double cost = (double)((wg * nseg + slots - 1) / slots) * blocks * kBlockUs;
-        if (nseg > 1) {
-            cost += (double)((wg * (nseg - 1) + slots - 1) / slots) * blocks * kBlockUs * kStateFrac;
-            cost += (double)nseg * state_bytes / kStateBytesPerUs + 2.0 * kLaunchUs;
-        }
-        if (cost < best - 1e-9) {
-            best = cost;
-            best_k = k;
-        }
+// Plan of the MFMA path: the segment length k (chunks one workgroup walks
+// while carrying the state in registers) and the fused pass's units per
+// workgroup sw.  The estimate (microseconds) is a model fitted to timings of
+// 120 plans over eight shapes on MI355X (within about 10% of each):
+//  - fused pass: one workgroup per CU, so ceil(workgroups / 256) rounds of
+//    k * Q / 64 blocks each; a block takes kFusedUs[N][sw] when few
+//    workgroups run, plus kOccUs[N] * sw / 5 scaled by the fraction of the
+//    CUs in use (HBM and L2 contention);
+//  - more than one segment adds the state-only pass (rounds of its
+//    workgroups, kStateUs[N] per block), the segment scan's sequential
+//    latency per segment, the states' HBM round trip (written by the state
+//    pass, read and written by the scan, read by the fused pass) and the two
+//    extra launches.
+// For each segment count only the most balanced k is tried; the cheapest
+// (k, sw) wins, ties going to fewer segments and fewer units.
+double plan_cost_us(const ssd::FwdShape& s, int64_t k, int sw) {
+    constexpr double kFusedUs[2][3] = {{1.83, 1.89, 2.19}, {1.70, 2.34, 2.33}};   // [N > 64][sw - 4]
+    constexpr double kOccUs[2] = {0.35, 1.28}, kStateUs[2] = {1.45, 1.29};
+    constexpr double kLaunchUs = 3.9, kSegExtraUs = 8.2, kSegLatencyUs = 0.39, kUsPerStateMB = 0.133;
+    const int wide = s.N > 64 ? 1 : 0;
+    const int64_t nseg = (s.nc + k - 1) / k;
+    const double blocks = (double)k * (double)((s.Q + 63) / 64);
+    const int64_t upg = (s.H / s.G) * (s.P / 32);
+    const int64_t wg_full = s.Bz * s.G * ((upg + sw - 1) / sw) * nseg;
+    const double busy = (double)(wg_full < kNumCU ? wg_full : kNumCU) / (double)kNumCU;
+    double cost = kLaunchUs + (double)((wg_full + kNumCU - 1) / kNumCU) * blocks *
+                                  (kFusedUs[wide][sw - 4] + kOccUs[wide] * busy * sw / 5.0);
+    if (nseg > 1) {
+        const int64_t hw = ssd::mfma_heads_per_workgroup(s.P, s.N);
+        const int64_t per_cu = kLdsPerCU / mfma_lds_bytes(s.P, s.N);
+        const int64_t slots = kNumCU * (per_cu > 0 ? per_cu : 1);
+        const int64_t wg_state = s.Bz * s.G * ((s.H / s.G + hw - 1) / hw) * (nseg - 1);
+        const double state_mb = 4.0 * (double)(s.Bz * s.H * s.P * s.N) * 4.0 * 1e-6;
+        cost += (double)((wg_state + slots - 1) / slots) * blocks * kStateUs[wide];
+        cost += kSegExtraUs + kSegLatencyUs * (double)nseg + kUsPerStateMB * state_mb * (double)nseg;
     }
-    return best_k;
+    return cost;
 }
 
-ssd_status make_plan(const ssd_fwd_desc* d, Plan* p) {
+// Workspace of the segmented plan: the fp32 states of segments 1 .. nseg-1
+// (slot 0 is never used) and the segments' log-decays, each region rounded
+// up to 256 bytes; none for a single segment.
+size_t fwd_ws_bytes(const ssd::FwdShape& s, int64_t nseg) {
+    if (nseg <= 1) return 0;
+    const size_t states = (size_t)s.Bz * nseg * s.H * s.P * s.N * sizeof(float);
+    const size_t lams = (size_t)s.Bz * s.H * nseg * sizeof(float);
+    return ((states + 255) / 256) * 256 + ((lams + 255) / 256) * 256;
+}
+
+// Cheapest plan whose workspace fits ws_cap (a single segment always does).
+void auto_plan(const ssd::FwdShape& s, int64_t k_fixed, int sw_fixed, size_t ws_cap, int64_t* k_out,
+               int* sw_out) {
+    const int64_t max_seg = s.nc < 65535 ? s.nc : 65535;
+    double best = 1e300;
+    int64_t best_k = k_fixed > 0 ? k_fixed : s.nc;
+    int best_sw = sw_fixed > 0 ? sw_fixed : 4;
+    for (int sw = 4; sw <= 6; ++sw) {
+        if ((sw_fixed > 0 && sw != sw_fixed) || !ssd::fwd_units_supported(s.P, sw)) continue;
+        int64_t prev_k = -1;
+        for (int64_t want = 1; want <= max_seg; ++want) {
+            const int64_t k = k_fixed > 0 ? k_fixed : (s.nc + want - 1) / want;   // longest segment
+            if (k == prev_k) continue;
+            prev_k = k;
+            if (k_fixed <= 0 && fwd_ws_bytes(s, (s.nc + k - 1) / k) > ws_cap) continue;
+            const double cost = plan_cost_us(s, k, sw);
+            if (cost < best - 1e-9) {
+                best = cost;
+                best_k = k;
+                best_sw = sw;
+            }
+            if (k_fixed > 0) break;
+        }
+    }
+    *k_out = best_k;
+    *sw_out = best_sw;
+}
+
+ssd_status make_plan(const ssd_fwd_desc* d, Plan* p, size_t ws_cap = SIZE_MAX) {
     ssd_status st = check_desc(d, false);
     if (st != SSD_OK) return st;
     p->s = shape_of(d);
@@ -178,10 +219,17 @@ ssd_status make_plan(const ssd_fwd_desc* d, Plan* p) {
     }
     p->seg_chunks = 0;
     p->nseg = 1;
+    p->sw = 0;
     p->ws = 0;
     if (p->algo == SSD_ALGO_MFMA && s.nc > 0 && s.Bz > 0) {
-        int64_t k = d->seg_chunks > 0 ? d->seg_chunks : auto_seg_chunks(s);
+        if (d->wg_units != 0 && !ssd::fwd_units_supported(s.P, d->wg_units))
+            return fail(SSD_ERR_UNSUPPORTED, "wg_units %d is not compiled for headdim %lld", (int)d->wg_units,
+                        (long long)s.P);
+        int64_t k = 0;
+        int sw = 0;
+        auto_plan(s, d->seg_chunks, d->wg_units, ws_cap, &k, &sw);
         if (k > s.nc) k = s.nc;
+        p->sw = sw;
         p->seg_chunks = k;
         p->nseg = (s.nc + k - 1) / k;
         if (p->nseg > 65535) return fail(SSD_ERR_UNSUPPORTED, "too many segments (%lld)", (long long)p->nseg);
@@ -190,11 +238,12 @@ ssd_status make_plan(const ssd_fwd_desc* d, Plan* p) {
         if ((s.Bz * p->nseg * s.H + 8) * kMfmaThreads >= ((int64_t)1 << 32))
             return fail(SSD_ERR_UNSUPPORTED, "batch*segments*heads (%lld) too large for one launch",
                         (long long)(s.Bz * p->nseg * s.H));
-        if (p->nseg > 1) {
-            const size_t states = (size_t)s.Bz * p->nseg * s.H * s.P * s.N * sizeof(float);
-            const size_t lams = (size_t)s.Bz * s.H * p->nseg * sizeof(float);
-            p->ws = ((states + 255) / 256) * 256 + ((lams + 255) / 256) * 256;
-        }
+        p->ws = fwd_ws_bytes(s, p->nseg);
+        if (p->ws > ws_cap)
+            return fail(SSD_ERR_WORKSPACE,
+                        "the requested plan (%lld chunks per segment, %lld segments) needs %zu bytes of "
+                        "workspace; the fixed workspace holds %zu",
+                        (long long)p->seg_chunks, (long long)p->nseg, p->ws, ws_cap);
     }
     return SSD_OK;
 }
@@ -247,7 +296,7 @@ ssd_status run_fwd(const Plan& p, const void* X, const float* a, const void* B, 
     }
     if (p.nseg == 1) {
         ssd::StateSrc src{initial_state, s.H * PN, nullptr, 0, 0};
-        e = ssd::launch_mfma_out(s, p.seg_chunks, 1, X, a, B, C, src, Y, final_state, hs);
+        e = ssd::launch_fwd(s, p.sw, p.seg_chunks, 1, X, a, B, C, src, Y, final_state, hs);
         if (e != hipSuccess) return hip_fail(e, "MFMA forward launch");
         return ok();
     }
@@ -262,7 +311,7 @@ ssd_status run_fwd(const Plan& p, const void* X, const float* a, const void* B, 
                                p.nseg * s.H * PN, hs);
     if (e != hipSuccess) return hip_fail(e, "segment scan launch");
     ssd::StateSrc src{initial_state, s.H * PN, Sbuf, p.nseg * s.H * PN, s.H * PN};
-    e = ssd::launch_mfma_out(s, p.seg_chunks, p.nseg, X, a, B, C, src, Y, final_state, hs);
+    e = ssd::launch_fwd(s, p.sw, p.seg_chunks, p.nseg, X, a, B, C, src, Y, final_state, hs);
     if (e != hipSuccess) return hip_fail(e, "MFMA forward launch");
     return ok();
 }
@@ -412,13 +461,15 @@ ssd_status ssd_fwd_workspace_bytes(const ssd_fwd_desc* desc, size_t* bytes) {
     return ok();
 }
 
-ssd_status ssd_fwd_plan(const ssd_fwd_desc* desc, int32_t* algo, int64_t* seg_chunks, int64_t* nseg) {
+ssd_status ssd_fwd_plan(const ssd_fwd_desc* desc, int32_t* algo, int64_t* seg_chunks, int64_t* nseg,
+                        int32_t* wg_units) {
     Plan p;
     ssd_status st = make_plan(desc, &p);
     if (st != SSD_OK) return st;
     if (algo) *algo = p.algo;
     if (seg_chunks) *seg_chunks = p.seg_chunks;
     if (nseg) *nseg = p.nseg;
+    if (wg_units) *wg_units = p.sw;
     return ok();
 }
 
@@ -593,8 +644,8 @@ ssd_status ssd_chunk_scan(const ssd_fwd_desc* desc, const void* X, const float* 
     }
     const int64_t PN = s.P * s.N;
     ssd::StateSrc src{states_in, p.nseg * s.H * PN, states_in, p.nseg * s.H * PN, s.H * PN};
-    hipError_t e = ssd::launch_mfma_out(s, p.seg_chunks, p.nseg, X, a, B, C, src, Y, nullptr,
-                                        reinterpret_cast<hipStream_t>(stream));
+    hipError_t e = ssd::launch_fwd(s, p.sw, p.seg_chunks, p.nseg, X, a, B, C, src, Y, nullptr,
+                                   reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "chunk scan launch");
     return ok();
 }

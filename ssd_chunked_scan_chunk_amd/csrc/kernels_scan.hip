@@ -22,8 +22,13 @@ namespace ssd {
 // chunk-state decays exp(a_{j+1} + ... + a_{end}) are accumulated term by term
 // from the diagonal outwards, so no decay is ever formed as a difference of
 // two large prefix sums (fp32 cancellation would cost ~1e-5 relative).
+// The chunk's masked, decayed scores exp(a_{j+1} + ... + a_i) (C_i . B_j) are
+// formed once per (i, j), kValuRows rows at a time into LDS (thread j owns
+// column j and carries its segment sum down the rows), and then shared by
+// every head-dim entry p of those rows.
 // ---------------------------------------------------------------------------
 constexpr int kValuThreads = 256;
+constexpr int kValuRows = 16;
 
 // Y (of type TY) may be null (only the states are wanted); S_chunks
 // (optional) receives the state entering every chunk, [Bz][nc][H][P*N].
@@ -39,6 +44,7 @@ __global__ __launch_bounds__(kValuThreads) void k_valu_fwd(
     float* sCs = sA + Q;        // [Q] inclusive prefix sums
     float* sS = sCs + Q;        // [P*N] carried state
     float* sTot = sS + P * N;   // [4] scan scratch
+    float* sM = sTot + 4;       // [kValuRows][Q] decayed scores of a row block
 
     const int h = blockIdx.x, b = blockIdx.y, g = h / (H / G);
     const int tid = threadIdx.x;
@@ -62,21 +68,39 @@ __global__ __launch_bounds__(kValuThreads) void k_valu_fwd(
             for (int k = tid; k < PN; k += kValuThreads)
                 S_chunks[(((int64_t)b * nc + c) * H + h) * PN + k] = sS[k];
 
-        // outputs of the chunk: intra-chunk masked product + carried state
-        for (int idx = tid; Y && idx < Lc * P; idx += kValuThreads) {
-            const int i = idx / P, p = idx - i * P;
-            const T* Ci = C + (((int64_t)b * L + t0 + i) * G + g) * N;
-            float acc = 0.f, seg = 0.f;
-            for (int j = i; j >= 0; --j) {
-                if (j < i) seg += sA[j + 1];
+        // outputs of the chunk: intra-chunk masked product + carried state,
+        // a block of kValuRows rows at a time
+        float seg = 0.f;   // thread j: a_{j+1} + ... + a_i for the latest row i
+        for (int i0 = 0; Y && i0 < Lc; i0 += kValuRows) {
+            const int nr = Lc - i0 < kValuRows ? Lc - i0 : kValuRows;
+            if (tid < Lc) {
+                const int j = tid;
                 const T* Bj = B + (((int64_t)b * L + t0 + j) * G + g) * N;
-                float cb = 0.f;
-                for (int n = 0; n < N; ++n) cb += Elem<T>::load(Ci + n) * Elem<T>::load(Bj + n);
-                acc += expf(seg) * cb * Elem<T>::load(X + (((int64_t)b * L + t0 + j) * H + h) * P + p);
+                for (int r = 0; r < nr; ++r) {
+                    const int i = i0 + r;
+                    float m = 0.f;
+                    if (j <= i) {
+                        if (j < i) seg += sA[i];
+                        const T* Ci = C + (((int64_t)b * L + t0 + i) * G + g) * N;
+                        float cb = 0.f;
+                        for (int n = 0; n < N; ++n) cb += Elem<T>::load(Ci + n) * Elem<T>::load(Bj + n);
+                        m = expf(seg) * cb;
+                    }
+                    sM[r * Q + j] = m;
+                }
             }
-            float off = 0.f;
-            for (int n = 0; n < N; ++n) off += Elem<T>::load(Ci + n) * sS[p * N + n];
-            Elem<TY>::store(Y + (((int64_t)b * L + t0 + i) * H + h) * P + p, acc + expf(sCs[i]) * off);
+            __syncthreads();
+            for (int idx = tid; idx < nr * P; idx += kValuThreads) {
+                const int r = idx / P, p = idx - r * P, i = i0 + r;
+                const T* Ci = C + (((int64_t)b * L + t0 + i) * G + g) * N;
+                float acc = 0.f;
+                for (int j = i; j >= 0; --j)
+                    acc += sM[r * Q + j] * Elem<T>::load(X + (((int64_t)b * L + t0 + j) * H + h) * P + p);
+                float off = 0.f;
+                for (int n = 0; n < N; ++n) off += Elem<T>::load(Ci + n) * sS[p * N + n];
+                Elem<TY>::store(Y + (((int64_t)b * L + t0 + i) * H + h) * P + p, acc + expf(sCs[i]) * off);
+            }
+            __syncthreads();
         }
         __syncthreads();
         // chunk state and the hand-off across the chunk boundary
@@ -102,7 +126,7 @@ hipError_t launch_valu_fwd(const FwdShape& s, bool bf16, const void* X, const fl
                            const void* B, const void* C, const float* S0, void* Y,
                            float* S_fin, hipStream_t st, float* S_chunks, bool y_f32)
 {
-    const size_t lds = (size_t)(2 * s.Q + s.P * s.N + 4) * sizeof(float);
+    const size_t lds = (size_t)(2 * s.Q + s.P * s.N + 4 + kValuRows * s.Q) * sizeof(float);
     dim3 grid((unsigned)s.H, (unsigned)s.Bz);
     if (bf16 && y_f32) {
         auto k = k_valu_fwd<u16, float>;

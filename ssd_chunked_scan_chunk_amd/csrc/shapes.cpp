@@ -15,6 +15,13 @@ int64_t mfma_heads_per_workgroup(int64_t P, int64_t N) {
     return kMfmaStateWaves / (P / 32);
 }
 
+// The fused pass's units per workgroup: 4, 5 or 6 for headdim 64; 4 or 5
+// for headdim 32 (six single-unit heads would need more LDS for their
+// per-head stage-1 results than a CU has).
+bool fwd_units_supported(int64_t P, int sw) {
+    return sw == 4 || sw == 5 || (sw == 6 && P == 64);
+}
+
 bool valu_fwd_supported(const FwdShape& s) {
     return s.Q >= 1 && s.Q <= 256 && s.P * s.N <= 16384;
 }

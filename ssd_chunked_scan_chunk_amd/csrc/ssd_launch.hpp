@@ -67,6 +67,15 @@ hipError_t launch_mfma_out(const FwdShape& s, int64_t seg_chunks, int64_t nseg,
                            const void* X, const float* a, const void* B, const void* C,
                            StateSrc src, void* Y, float* S_fin, hipStream_t st);
 
+// The fused forward pass (kernels_fwd.hip): sw (4, 5 or 6) units -- 32-wide
+// head-dim slices of heads -- per workgroup, for every segment starting from
+// its entering state; writes Y and (last segment) the final state.
+hipError_t launch_fwd(const FwdShape& s, int sw, int64_t seg_chunks, int64_t nseg, const void* X,
+                      const float* a, const void* B, const void* C, StateSrc src, void* Y,
+                      float* S_fin, hipStream_t st);
+int64_t fwd_workgroups(const FwdShape& s, int64_t nseg, int sw);
+bool fwd_units_supported(int64_t P, int sw);
+
 // The backward's exchanged-dimension products (headdim 64, state 64, one chunk
 // per segment): X [Bz][L][x_groups][(H/G)*64] bf16 shared by the H/G heads of
 // a group (head hl reads columns hl*64 ..), a [Bz][L][G] (one decay per group),

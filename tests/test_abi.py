@@ -88,10 +88,11 @@ def test_fwd_rejects_nulls_alignment_alias_workspace(lib):
     assert fwd(lib, desc(headdim=48, algo=_lib.SSD_ALGO_MFMA)) == _lib.SSD_ERR_UNSUPPORTED
 
 
-def plan(lib, d):
-    a, k, n = ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int64()
-    assert lib.ssd_fwd_plan(ctypes.byref(d), ctypes.byref(a), ctypes.byref(k), ctypes.byref(n)) == 0
-    return a.value, k.value, n.value
+def plan(lib, d, units=False):
+    a, k, n, u = ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32()
+    assert lib.ssd_fwd_plan(ctypes.byref(d), ctypes.byref(a), ctypes.byref(k), ctypes.byref(n),
+                            ctypes.byref(u)) == 0
+    return (a.value, k.value, n.value, u.value) if units else (a.value, k.value, n.value)
 
 
 def test_plans(lib):
@@ -106,6 +107,14 @@ def test_plans(lib):
     assert a == _lib.SSD_ALGO_MFMA and n > 1 and k * n >= 2048
     a, k, n = plan(lib, desc(seg_chunks=3, seqlen=256 * 10))
     assert (k, n) == (3, 4)
+    # the 2.7B-shaped layer: 8 x 80 x 2 = 1280 units in 256 workgroups of five, one segment
+    assert plan(lib, desc(batch=8, seqlen=4096, nheads=80), units=True) == (_lib.SSD_ALGO_MFMA, 16, 1, 5)
+    # a forced split is honoured; others are rejected on the host
+    assert plan(lib, desc(wg_units=4), units=True)[3] == 4
+    assert plan(lib, desc(wg_units=6, seg_chunks=1), units=True)[1:] == (1, 2, 6)
+    for bad in (1, 3, 7):
+        assert fwd(lib, desc(wg_units=bad)) == _lib.SSD_ERR_UNSUPPORTED
+    assert plan(lib, desc(dtype=_lib.SSD_F32), units=True)[3] == 0
     # workspace is zero for a single segment
     n0 = ctypes.c_size_t(123)
     assert lib.ssd_fwd_workspace_bytes(ctypes.byref(desc(batch=64, seqlen=4096, nheads=80)), ctypes.byref(n0)) == 0

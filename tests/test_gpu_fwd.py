@@ -177,6 +177,30 @@ def test_decay_regimes_per_head(seg):
     assert ey <= TOL[si.BF16] and es <= TOL[si.BF16], (ey, es)
 
 
+def test_deep_rebase_keeps_the_state():
+    # Per 64-step block of head 0, log2-decays per 16-step quarter of 100, 45,
+    # then 15 near-free steps and one step of 178, then a mild quarter.  The
+    # second quarter leaves the state's scale at its floor (2^-95 of the
+    # output scale) and the third re-bases it by about 184 octaves: a factor
+    # of 2^-184 would round to zero in fp32, yet the state still carries most
+    # of the outputs of that quarter's first 15 steps.
+    sh = si.FwdShape(1, 64 * 4 + 9, 2, 64, 128, 1, 256, si.BF16)
+    d = si.make_fwd(sh, seed=13)
+    ln2 = np.log(2.0)
+    blk = np.concatenate([np.full(16, -100.0 / 16), np.full(16, -45.0 / 16),
+                          np.full(15, -0.01), [-178.0 + 0.15], np.full(16, -0.3)]) * ln2
+    d["a"][0, :, 0] = np.tile(blk, 5)[:sh.seqlen].astype(np.float32)
+    g = upload_fwd(d)
+    Y, S = ssd.chunk_scan_fwd(g["X"], g["a"], g["B"], g["C"], sh.chunk, return_final_state=True,
+                              algo=ssd.SSD_ALGO_MFMA)
+    torch.cuda.synchronize()
+    w = widen_fwd(d)
+    Yr, Sr = oracle.fwd(w["X"], w["a"], w["B"], w["C"], nthreads=oracle_threads())
+    ey, es = y_err(host_f64(Y), Yr), state_err(host_f64(S), Sr)
+    log("   deep re-base err Y=%.3e S=%.3e" % (ey, es))
+    assert ey <= TOL[si.BF16] and es <= TOL[si.BF16], (ey, es)
+
+
 def test_nan_stays_in_its_slice():
     # a NaN in X[b=1, t=200, h=2] reaches only slice (1, 2).  Within that slice
     # it may also reach the steps of its own 32-step block of the chunk before
