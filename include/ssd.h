@@ -116,6 +116,23 @@ ssd_status ssd_chunk_scan_fwd(const ssd_fwd_desc* desc, const void* X, const flo
                               void* Y, float* final_state, void* workspace,
                               size_t workspace_bytes, void* stream);
 
+/* ssd_chunk_scan_fwd for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same computation and arguments without the workspace.
+ * The segmented plan's workspace is a device array inside the library, one
+ * per GPU, of SSD_NOALLOC_SCRATCH_BYTES (held until the process ends).  The
+ * automatic plan is restricted to plans whose workspace fits it (a single
+ * segment needs none, so every shape the forward takes has one; for shapes
+ * whose unrestricted plan needs more, the plan and so the rounding may differ
+ * from ssd_chunk_scan_fwd's).  A plan fixed by desc->seg_chunks that needs
+ * more is rejected with SSD_ERR_WORKSPACE.  Calls no allocating routine.
+ * Calls that overlap in time on one GPU share that array and race: order
+ * them on one stream (or synchronise between them). */
+#define SSD_NOALLOC_SCRATCH_BYTES (64u << 20)
+ssd_status ssd_chunk_scan_fwd_noalloc(const ssd_fwd_desc* desc, const void* X, const float* a,
+                                      const void* B, const void* C, const float* initial_state,
+                                      void* Y, float* final_state, void* stream);
+
 /* Single-token recurrent decode step for every (b, h) (constant-memory
  * inference): state <- exp(a) * state + x (x) B, then y = state C.
  * state [batch][nheads][headdim][dstate] float32 is updated in place;

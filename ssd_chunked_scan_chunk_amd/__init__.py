@@ -23,7 +23,7 @@ from . import _lib
 from ._lib import (SSD_ALGO_AUTO, SSD_ALGO_MFMA, SSD_ALGO_VALU, SSD_BF16, SSD_F32,
                    SSDError)
 
-__all__ = ["chunk_scan_fwd", "chunk_scan_bwd", "bwd_workspace_bytes", "bwd_da", "step", "chunk_cumsum", "chunk_state", "state_passing",
+__all__ = ["chunk_scan_fwd", "chunk_scan_fwd_noalloc", "chunk_scan_bwd", "bwd_workspace_bytes", "bwd_da", "step", "chunk_cumsum", "chunk_state", "state_passing",
            "chunk_scan", "fwd_plan", "workspace_bytes", "SSDError", "SSD_ALGO_AUTO",
            "SSD_ALGO_MFMA", "SSD_ALGO_VALU", "library_path"]
 
@@ -167,6 +167,26 @@ def chunk_scan_fwd(X, a, B, C, chunk, initial_state=None, return_final_state=Fal
     _lib.check(_L().ssd_chunk_scan_fwd(
         ctypes.byref(d), _ptr(X), _ptr(a), _ptr(B), _ptr(C), _ptr(initial_state), _ptr(Y),
         _ptr(final_state), _ptr(workspace), wsz, _stream(dev)))
+    return Y, final_state
+
+
+def chunk_scan_fwd_noalloc(X, a, B, C, chunk, initial_state=None, Y=None, final_state=None,
+                           algo=SSD_ALGO_AUTO, seg_chunks=0, wg_units=0):
+    """The forward through the C ABI's allocation-free entry point: the
+    library's own per-GPU device array holds the segment states, so the call
+    allocates nothing when Y (and final_state, if wanted) are passed in.
+    Returns (Y, final_state or None)."""
+    Bz, L, H, P, G, N = _check_fwd_inputs(X, a, B, C)
+    dev = X.device
+    _check("initial_state", initial_state, (Bz, H, P, N), torch.float32, dev)
+    _check("Y", Y, X.shape, X.dtype, dev)
+    _check("final_state", final_state, (Bz, H, P, N), torch.float32, dev)
+    d = _desc(X, B, chunk, algo, seg_chunks, wg_units)
+    if Y is None:
+        Y = torch.empty_like(X)
+    _lib.check(_L().ssd_chunk_scan_fwd_noalloc(
+        ctypes.byref(d), _ptr(X), _ptr(a), _ptr(B), _ptr(C), _ptr(initial_state), _ptr(Y),
+        _ptr(final_state), _stream(dev)))
     return Y, final_state
 
 

@@ -30,8 +30,9 @@ EXPORTS = (
     "ssd_fwd_workspace_bytes", "ssd_fwd_plan", "ssd_chunk_scan_fwd", "ssd_step",
     "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan",
     "ssd_status_str", "ssd_last_error", "ssd_version", "ssd_bwd_workspace_bytes",
-    "ssd_chunk_scan_bwd", "ssd_bwd_da",
+    "ssd_chunk_scan_bwd", "ssd_bwd_da", "ssd_chunk_scan_fwd_noalloc",
 )
+SSD_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class FwdDesc(ctypes.Structure):
@@ -74,6 +75,7 @@ def load(path: str = LIB_PATH):
     lib.ssd_fwd_plan.argtypes = [pd, ctypes.POINTER(i32), ctypes.POINTER(i64), ctypes.POINTER(i64),
                                  ctypes.POINTER(i32)]
     lib.ssd_chunk_scan_fwd.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.ssd_chunk_scan_fwd_noalloc.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.ssd_step.argtypes = [ctypes.POINTER(StepDesc), vp, vp, vp, vp, vp, vp, vp]
     lib.ssd_chunk_cumsum.argtypes = [pd, vp, vp, vp, vp]
     lib.ssd_chunk_state.argtypes = [pd, vp, vp, vp, vp, vp]
@@ -82,7 +84,7 @@ def load(path: str = LIB_PATH):
     lib.ssd_bwd_workspace_bytes.argtypes = [pd, ctypes.POINTER(sz)]
     lib.ssd_chunk_scan_bwd.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ssd_bwd_da.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp]
-    for f in ("ssd_fwd_workspace_bytes", "ssd_fwd_plan", "ssd_chunk_scan_fwd",
+    for f in ("ssd_fwd_workspace_bytes", "ssd_fwd_plan", "ssd_chunk_scan_fwd", "ssd_chunk_scan_fwd_noalloc",
               "ssd_step",
               "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan",
               "ssd_bwd_workspace_bytes", "ssd_chunk_scan_bwd", "ssd_bwd_da"):

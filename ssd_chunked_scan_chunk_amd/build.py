@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libssd.so")
 SOURCES = ["api.cpp", "shapes.cpp", "kernels_scan.hip", "kernels_mfma.hip", "kernels_fwd.hip", "kernels_step.hip",
-           "kernels_bwd.hip"]
+           "kernels_bwd.hip", "noalloc.hip"]
 
 
 def hipcc() -> str:

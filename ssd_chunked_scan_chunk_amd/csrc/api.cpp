@@ -431,6 +431,27 @@ ssd_status make_bwd_plan(const ssd_fwd_desc* d, BwdPlan* bp) {
 
 }  // namespace
 
+namespace ssd {
+
+ssd_status fwd_with_fixed_workspace(const ssd_fwd_desc* desc, const void* X, const float* a,
+                                    const void* B, const void* C, const float* initial_state,
+                                    void* Y, float* final_state, size_t ws_cap,
+                                    hipError_t (*get_ws)(void**), void* stream) {
+    Plan p;
+    ssd_status st = make_plan(desc, &p, ws_cap);
+    if (st != SSD_OK) return st;
+    st = check_fwd_io(p, X, a, B, C, initial_state, Y, final_state);
+    if (st != SSD_OK) return st;
+    void* ws = nullptr;
+    if (p.ws > 0) {
+        const hipError_t e = get_ws(&ws);
+        if (e != hipSuccess) return hip_fail(e, "fixed workspace address");
+    }
+    return run_fwd(p, X, a, B, C, initial_state, Y, final_state, ws, reinterpret_cast<hipStream_t>(stream));
+}
+
+}  // namespace ssd
+
 extern "C" {
 
 const char* ssd_status_str(ssd_status s) {

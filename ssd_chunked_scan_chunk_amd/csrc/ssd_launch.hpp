@@ -129,6 +129,17 @@ hipError_t launch_bwd_da(const FwdShape& s, const void* X, const void* dY, const
                          const void* B, const void* C, const float* Sin, const float* Srev,
                          bool adj_reversed, float* da, hipStream_t st);
 
+// The forward of the C ABI with a fixed workspace region of ws_cap bytes
+// (api.cpp): plans within the cap, validates every argument on the host, then
+// asks get_ws for the region's device address and enqueues.
+}  // namespace ssd
+#include "ssd.h"
+namespace ssd {
+ssd_status fwd_with_fixed_workspace(const ssd_fwd_desc* desc, const void* X, const float* a,
+                                    const void* B, const void* C, const float* initial_state,
+                                    void* Y, float* final_state, size_t ws_cap,
+                                    hipError_t (*get_ws)(void**), void* stream);
+
 // zero-fill (used for empty sequences: final state = 0)
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t st);

@@ -7,6 +7,20 @@
 
 extern "C" const char* hipGetErrorString(hipError_t) { return "stub launcher (host-only build)"; }
 
+// the allocation-free forward over a host stand-in for its device array
+// (the launch stubs never touch it)
+static hipError_t fake_scratch(void** p) {
+    static unsigned char region[256];
+    *p = region;
+    return hipSuccess;
+}
+extern "C" ssd_status ssd_chunk_scan_fwd_noalloc(const ssd_fwd_desc* desc, const void* X, const float* a,
+                                                 const void* B, const void* C, const float* initial_state,
+                                                 void* Y, float* final_state, void* stream) {
+    return ssd::fwd_with_fixed_workspace(desc, X, a, B, C, initial_state, Y, final_state,
+                                         SSD_NOALLOC_SCRATCH_BYTES, fake_scratch, stream);
+}
+
 namespace ssd {
 #define SSD_STUB return hipErrorNotSupported
 hipError_t launch_valu_fwd(const FwdShape&, bool, const void*, const float*, const void*, const void*,
