@@ -233,9 +233,33 @@ def bench_decode(steps, warmup):
     t = time_events(step, steps) / steps
     Bz, H, P, N, G = sh.batch, sh.nheads, sh.headdim, sh.dstate, sh.ngroups
     nbytes = 2 * Bz * H * P * N * 4 + 2 * Bz * H * P * 2 + 2 * Bz * G * N * 2 + Bz * H * 4
+    # The practical ceiling: the library's plain in-place read-modify-write of
+    # the same state array (scale 1, so the state keeps its values), for each
+    # of its launch shapes.
+    ceiling = {}
+    for per_thread in (1, 2, 4, 8):
+        for nt in (False, True):
+            def fn(i, v=per_thread, n=nt):
+                ssd.stream_rmw(state, 1.0, v, n)
+            for i in range(warmup):
+                fn(i)
+            tr = time_events(fn, steps) / steps
+            ceiling["v%d%s" % (per_thread, "_nt" if nt else "")] = 2 * state.numel() * 4 / tr / 1e9
     del state, x, B, C, a, y
     torch.cuda.empty_cache()
-    return t, nbytes
+    return t, nbytes, ceiling
+
+
+def decode_record(td, nbytes, ceiling):
+    best = max(ceiling.values())
+    return {"workload": "batch 256, 80 heads, headdim 64, dstate 128, fp32 state in place",
+            "us_per_step": td * 1e6, "GB_per_s": nbytes / td / 1e9,
+            "hbm_frac": nbytes / td / 1e9 / HBM_PEAK_GBS, "tokens_per_s": 256 / td,
+            "bytes_per_step": nbytes,
+            "stream_ceiling": {"GB_per_s": best, "hbm_frac": best / HBM_PEAK_GBS,
+                               "decode_frac_of_ceiling": nbytes / td / 1e9 / best,
+                               "kernel": "ssd_stream_rmw: in-place fp32 x *= 1 over the same state array",
+                               "by_launch_shape_GB_per_s": ceiling}}
 
 
 def bwd_algo_flops_per_token(sh, block=KERNEL_BLOCK):
@@ -399,10 +423,8 @@ def main():
     import ssd_chunked_scan_chunk_amd as ssd  # noqa: F401  (fails loudly if libssd.so is missing)
 
     if args.decode_only:
-        td, nbytes = bench_decode(args.steps, args.warmup)
-        print(json.dumps({"decode_step": {"us_per_step": td * 1e6, "GB_per_s": nbytes / td / 1e9,
-                                          "hbm_frac": nbytes / td / 1e9 / HBM_PEAK_GBS,
-                                          "bytes_per_step": nbytes}}))
+        td, nbytes, ceil = bench_decode(args.steps, args.warmup)
+        print(json.dumps({"decode_step": decode_record(td, nbytes, ceil)}))
         return
     s130 = si.FWD_CONFIGS["m2_130m"]
     if args.bwd_only:
@@ -472,10 +494,8 @@ def main():
             r = measure_forward(shp, max(5, args.steps // (1 + L // 65536)), 2)
             r.pop("_t_kernel"), r.pop("_t_step")
             sec["sweep_n64_L%d" % L] = r
-        td, nbytes = bench_decode(max(20, args.steps), 5)
-        sec["decode_step"] = {"workload": "batch 256, 80 heads, headdim 64, dstate 128, fp32 state in place",
-                              "us_per_step": td * 1e6, "GB_per_s": nbytes / td / 1e9,
-                              "hbm_frac": nbytes / td / 1e9 / HBM_PEAK_GBS, "tokens_per_s": 256 / td}
+        td, nbytes, ceil = bench_decode(max(20, args.steps), 5)
+        sec["decode_step"] = decode_record(td, nbytes, ceil)
         tokens130 = s130.batch * s130.seqlen
         tb, tda = bench_backward(s130, max(10, args.steps // 2), 3, 2)
         fl = tokens130 * bwd_algo_flops_per_token(s130)

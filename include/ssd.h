@@ -142,6 +142,16 @@ ssd_status ssd_chunk_scan_fwd_noalloc(const ssd_fwd_desc* desc, const void* X, c
 ssd_status ssd_step(const ssd_step_desc* desc, float* state, const void* x, const float* a,
                     const void* B, const void* C, void* y, void* stream);
 
+/* The HBM ceiling ssd_step is measured against: data[i] *= scale in place
+ * for i < n (n a multiple of 4; data fp32, 16-byte aligned, on the device),
+ * the same read-modify-write stream as the decode step's state with no other
+ * traffic.  per_thread in {1, 2, 4, 8} float4 per thread; nontemporal 1 uses
+ * the nontemporal load/store hints of the decode kernel, 0 plain accesses.
+ * Errors: SSD_ERR_SHAPE / SSD_ERR_UNSUPPORTED / SSD_ERR_NULL / SSD_ERR_ALIGN
+ * before anything is enqueued, SSD_ERR_HIP if the launch fails. */
+ssd_status ssd_stream_rmw(float* data, int64_t n, float scale, int32_t per_thread, int32_t nontemporal,
+                          void* stream);
+
 /* ---- Backward (gradients of the full forward) ----
  *
  * For a scalar loss l with upstream gradients dY = dl/dY and (optional)

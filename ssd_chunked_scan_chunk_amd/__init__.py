@@ -23,7 +23,7 @@ from . import _lib
 from ._lib import (SSD_ALGO_AUTO, SSD_ALGO_MFMA, SSD_ALGO_VALU, SSD_BF16, SSD_F32,
                    SSDError)
 
-__all__ = ["chunk_scan_fwd", "chunk_scan_fwd_noalloc", "chunk_scan_bwd", "bwd_workspace_bytes", "bwd_da", "step", "chunk_cumsum", "chunk_state", "state_passing",
+__all__ = ["chunk_scan_fwd", "chunk_scan_fwd_noalloc", "chunk_scan_bwd", "bwd_workspace_bytes", "bwd_da", "step", "stream_rmw", "chunk_cumsum", "chunk_state", "state_passing",
            "chunk_scan", "fwd_plan", "workspace_bytes", "SSDError", "SSD_ALGO_AUTO",
            "SSD_ALGO_MFMA", "SSD_ALGO_VALU", "library_path"]
 
@@ -281,6 +281,19 @@ def step(state, x, a, B, C, y=None):
     _lib.check(_L().ssd_step(ctypes.byref(d), _ptr(state), _ptr(x), _ptr(a), _ptr(B), _ptr(C),
                              _ptr(y), _stream(state.device)))
     return y
+
+
+def stream_rmw(t, scale, per_thread=8, nontemporal=True):
+    """In-place ``t *= scale`` over a contiguous fp32 device tensor through the
+    library's streaming kernel: the HBM ceiling the decode step is measured
+    against.  Returns t."""
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or not t.is_contiguous():
+        raise ValueError("t must be a contiguous float32 tensor")
+    if t.numel() % 4 != 0:
+        raise ValueError("t.numel() must be a multiple of 4")
+    _lib.check(_L().ssd_stream_rmw(_ptr(t), t.numel(), float(scale), int(per_thread), int(bool(nontemporal)),
+                                   _stream(t.device)))
+    return t
 
 
 # ---- stage entry points ------------------------------------------------------

@@ -537,6 +537,10 @@ ssd_status ssd_step(const ssd_step_desc* d, float* state, const void* x, const f
     if (d->reserved != 0) return fail(SSD_ERR_SHAPE, "reserved must be 0");
     if (d->batch * d->nheads > ((int64_t)1 << 31) - 1 || d->headdim * d->dstate > (1 << 24))
         return fail(SSD_ERR_UNSUPPORTED, "sizes beyond the supported range");
+    // every launch shape of the step kernels is at most one thread per 4 state
+    // elements (at least one per row), and a launch holds < 2^32 threads
+    if (d->batch * d->nheads * d->headdim * (d->dstate >= 4 ? d->dstate / 4 : 1) >= ((int64_t)1 << 32))
+        return fail(SSD_ERR_UNSUPPORTED, "batch*nheads*headdim*dstate too large for one launch");
     if (d->batch == 0) return ok();
     if (!state || !x || !a || !B || !C || !y) return fail(SSD_ERR_NULL, "state, x, a, B, C and y are required");
     const int64_t es = d->dtype == SSD_BF16 ? 2 : 4;
@@ -558,6 +562,22 @@ ssd_status ssd_step(const ssd_step_desc* d, float* state, const void* x, const f
                                     d->dtype == SSD_BF16, state, x, a, B, C, y,
                                     reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "decode step launch");
+    return ok();
+}
+
+ssd_status ssd_stream_rmw(float* data, int64_t n, float scale, int32_t per_thread, int32_t nontemporal,
+                          void* stream) {
+    if (n < 0 || n % 4 != 0) return fail(SSD_ERR_SHAPE, "n (%lld) must be a non-negative multiple of 4", (long long)n);
+    if (per_thread != 1 && per_thread != 2 && per_thread != 4 && per_thread != 8)
+        return fail(SSD_ERR_UNSUPPORTED, "per_thread must be 1, 2, 4 or 8");
+    if (nontemporal != 0 && nontemporal != 1) return fail(SSD_ERR_SHAPE, "nontemporal must be 0 or 1");
+    if (n / 4 > ((int64_t)1 << 31) * 256) return fail(SSD_ERR_UNSUPPORTED, "n beyond the supported range");
+    if (n == 0) return ok();
+    if (!data) return fail(SSD_ERR_NULL, "data is NULL");
+    if (!aligned(data, 16)) return fail(SSD_ERR_ALIGN, "data must be 16-byte aligned");
+    const hipError_t e = ssd::launch_stream_rmw(data, n / 4, scale, per_thread, nontemporal != 0,
+                                                reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "stream launch");
     return ok();
 }
 

@@ -487,7 +487,19 @@ __global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(2
     }
 
     float ld = 0.f;   // the scale of Sacc (log2) after the latest block
+    // The state lives in one fixed register range across the loop: without
+    // the pin the compiler kept the loop-carried state in one range and the
+    // fast form's products in another, copying 64 registers out and back in
+    // every block.
+    auto pin_state = [&]() {
+        if constexpr (NTL == 4)
+            asm volatile("" : "+{v[2:17]}"(Sacc[0]), "+{v[18:33]}"(Sacc[1]), "+{v[34:49]}"(Sacc[2]),
+                              "+{v[50:65]}"(Sacc[3]));
+        else
+            asm volatile("" : "+{v[2:17]}"(Sacc[0]), "+{v[18:33]}"(Sacc[1]));
+    };
     for (int64_t c = c_begin; c < c_end; ++c) {
+        pin_state();
         const int bs = (int)((c - c_begin) & 1);          // B, C, scores, stage-1 buffers
         const int xs = (int)((c - c_begin) % NXB);        // X buffer
         const int last = block_last(c);
@@ -555,6 +567,30 @@ __global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(2
                 for (int q = 0; q < 4; ++q)
                     Yb[I][q] = make_uint2(pack2(Yt[I][4 * q], Yt[I][4 * q + 1]),
                                           pack2(Yt[I][4 * q + 2], Yt[I][4 * q + 3]));
+        };
+        // ---- Y^T through this unit's own X tile (dead after stage 3), so that
+        // copy k of a lane holds 16 contiguous bytes of step 16k + lane/4 and a
+        // store covers 16 steps x 64 bytes.  Called at the end of each form,
+        // so that nothing after the branch needs registers while the state is
+        // live (a shared tail made the compiler move the state out and back) ----
+        auto store_y = [&]() {
+#pragma unroll
+            for (int I = 0; I < 2; ++I)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<uint2*>(xTm + swz<XPU>(32 * I + l32, 8 * q + 4 * g2)) = Yb[I][q];
+            u32x4 Yr[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                Yr[k] = *reinterpret_cast<const u32x4*>(xTm + swz<XPU>(16 * k + (lane >> 2), 8 * (lane & 3)));
+            if (uvalid) {
+                u16* yblk = Y + ((int64_t)b * L + c * kT) * H * P;
+                const uint32_t yoff = (uint32_t)(((lane >> 2) * H + h) * P + pc + 8 * (lane & 3));
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    if (16 * k + (lane >> 2) <= last)
+                        *reinterpret_cast<u32x4*>(yblk + (yoff + (uint32_t)(16 * k * H * P))) = Yr[k];
+            }
         };
         if (fast) {
             // ================= fast form, software-pipelined =================
@@ -645,6 +681,8 @@ __global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(2
             Yt[0] *= fast_exp2(csr[0]);
             Yt[1] *= fast_exp2(csr[1]);
             pack_y();
+            store_y();
+            pin_state();
         } else {
             // ================= direct form (rare), plain order =================
             // A quarter's log2-decay spread too wide for any power-of-two
@@ -711,26 +749,8 @@ __global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(2
 #pragma unroll
                 for (int nt = 0; nt < NTL; ++nt) Sacc[nt] = mfma32(bq[nt], xw, Sacc[nt]);
             }
-        }
-        // ---- Y^T through this unit's own X tile (dead after stage 3), so that
-        // copy k of a lane holds 16 contiguous bytes of step 16k + lane/4 and a
-        // store covers 16 steps x 64 bytes ----
-#pragma unroll
-        for (int I = 0; I < 2; ++I)
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                *reinterpret_cast<uint2*>(xTm + swz<XPU>(32 * I + l32, 8 * q + 4 * g2)) = Yb[I][q];
-        u32x4 Yr[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            Yr[k] = *reinterpret_cast<const u32x4*>(xTm + swz<XPU>(16 * k + (lane >> 2), 8 * (lane & 3)));
-        if (uvalid) {
-            u16* yblk = Y + ((int64_t)b * L + c * kT) * H * P;
-            const uint32_t yoff = (uint32_t)(((lane >> 2) * H + h) * P + pc + 8 * (lane & 3));
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                if (16 * k + (lane >> 2) <= last)
-                    *reinterpret_cast<u32x4*>(yblk + (yoff + (uint32_t)(16 * k * H * P))) = Yr[k];
+            store_y();
+            pin_state();
         }
     }
 

@@ -13,6 +13,10 @@
 #include "ssd_device.hpp"
 #include "ssd_launch.hpp"
 
+#ifndef SSD_STEP_ROWS
+#define SSD_STEP_ROWS 2
+#endif
+
 namespace ssd {
 
 template <typename T> __device__ __forceinline__ float4 load4(const T* p);
@@ -35,20 +39,24 @@ template <> struct AccOf<u16> {
     __device__ __forceinline__ static float exp(float a) { return expf(a); }
 };
 
-// Fast path: N/4 lanes per state row (N in {16, 32, 64, 128, 256}), P a
-// multiple of 256 / (N/4); ROWS = rows handled per thread.
+// Fast path: N/4 lanes per state row (N in {16, 32, 64, 128, 256}); a
+// workgroup covers ROWS * 256 / (N/4) consecutive rows of one (b, h), so that
+// SPLIT = P / that workgroups share a (b, h) and each thread streams only ROWS
+// float4 of the state (fewer per thread keep more of them in flight across
+// the chip: the in-place stream of the same array reaches its best rate at
+// one float4 per thread).
 template <typename T, int N, int ROWS>
 __global__ __launch_bounds__(256) void k_step(float* __restrict__ state, const T* __restrict__ x,
                                               const float* __restrict__ a, const T* __restrict__ B,
-                                              const T* __restrict__ C, T* __restrict__ y, int H, int G)
+                                              const T* __restrict__ C, T* __restrict__ y, int H, int G,
+                                              int P, int split)
 {
     constexpr int LPR = N / 4;           // lanes per row
     constexpr int RPP = 256 / LPR;       // rows per pass of the workgroup
-    constexpr int P = RPP * ROWS;
-    const int bh = blockIdx.x;
+    const int bh = blockIdx.x / split, part = blockIdx.x - bh * split;
     const int b = bh / H, h = bh - b * H, g = h / (H / G);
     const int tid = threadIdx.x;
-    const int nq = tid % LPR, r0 = tid / LPR;
+    const int nq = tid % LPR, r0 = part * (RPP * ROWS) + tid / LPR;
 
     float* Sb = state + (int64_t)bh * P * N;
     f32x4 s[ROWS];
@@ -112,18 +120,62 @@ __global__ __launch_bounds__(256) void k_step_any(float* __restrict__ state, con
     Elem<T>::store(y + row, (float)acc);
 }
 
+// The practical HBM ceiling of the decode step: the same in-place fp32
+// read-modify-write (every element multiplied by s), with no other traffic.
+// V float4 per thread, all loads issued before any store; NT selects the
+// nontemporal hints the decode kernel uses.
+template <int V, bool NT>
+__global__ __launch_bounds__(256) void k_stream_rmw(float* __restrict__ data, int64_t n4, float s)
+{
+    f32x4* p = reinterpret_cast<f32x4*>(data);
+    const int64_t base = (int64_t)blockIdx.x * (256 * V) + threadIdx.x;
+    f32x4 v[V];
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+        const int64_t i = base + (int64_t)k * 256;
+        if (i < n4) v[k] = NT ? __builtin_nontemporal_load(p + i) : p[i];
+    }
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+        const int64_t i = base + (int64_t)k * 256;
+        if (i < n4) {
+            const f32x4 w = v[k] * s;
+            if (NT) __builtin_nontemporal_store(w, p + i);
+            else p[i] = w;
+        }
+    }
+}
+
+hipError_t launch_stream_rmw(float* data, int64_t n4, float s, int per_thread, bool nontemporal,
+                             hipStream_t st)
+{
+    const int64_t per_block = 256 * (int64_t)per_thread;
+    const dim3 grid((unsigned)((n4 + per_block - 1) / per_block)), blk(256);
+#define SSD_RMW(VV)                                                                          \
+    if (per_thread == VV) {                                                                  \
+        if (nontemporal) hipLaunchKernelGGL((k_stream_rmw<VV, true>), grid, blk, 0, st, data, n4, s); \
+        else hipLaunchKernelGGL((k_stream_rmw<VV, false>), grid, blk, 0, st, data, n4, s);  \
+        return hipGetLastError();                                                            \
+    }
+    SSD_RMW(1) SSD_RMW(2) SSD_RMW(4) SSD_RMW(8)
+#undef SSD_RMW
+    return hipErrorInvalidValue;
+}
+
 template <typename T>
 static hipError_t launch_step_t(int64_t Bz, int64_t H, int64_t P, int64_t N, int64_t G,
                                 float* state, const T* x, const float* a, const T* B,
                                 const T* C, T* y, hipStream_t st)
 {
-    const dim3 grid((unsigned)(Bz * H)), blk(256);
-#define SSD_STEP_CASE(NN, PP)                                                              \
-    if (N == NN && P == PP) {                                                              \
-        constexpr int rows = PP / (256 / (NN / 4));                                        \
-        hipLaunchKernelGGL((k_step<T, NN, rows>), grid, blk, 0, st, state, x, a, B, C, y,  \
-                           (int)H, (int)G);                                                \
-        return hipGetLastError();                                                          \
+    const dim3 blk(256);
+    // SSD_STEP_ROWS float4 per thread where the rows allow it
+#define SSD_STEP_CASE(NN, PP)                                                                 \
+    if (N == NN && P == PP) {                                                                 \
+        constexpr int rpp = 256 / (NN / 4), rows = SSD_STEP_ROWS < PP / rpp ? SSD_STEP_ROWS : PP / rpp; \
+        constexpr int split = PP / (rpp * rows);                                              \
+        hipLaunchKernelGGL((k_step<T, NN, rows>), dim3((unsigned)(Bz * H * split)), blk, 0, st, state, x, \
+                           a, B, C, y, (int)H, (int)G, (int)PP, split);                       \
+        return hipGetLastError();                                                             \
     }
     SSD_STEP_CASE(128, 64)
     SSD_STEP_CASE(64, 64)

@@ -140,6 +140,10 @@ ssd_status fwd_with_fixed_workspace(const ssd_fwd_desc* desc, const void* X, con
                                     void* Y, float* final_state, size_t ws_cap,
                                     hipError_t (*get_ws)(void**), void* stream);
 
+// in-place data[i] *= s over n4 float4 (the decode step's HBM ceiling)
+hipError_t launch_stream_rmw(float* data, int64_t n4, float s, int per_thread, bool nontemporal,
+                             hipStream_t st);
+
 // zero-fill (used for empty sequences: final state = 0)
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t st);

@@ -39,6 +39,7 @@ hipError_t launch_mfma_out_xg(const FwdShape&, int64_t, const void*, const float
                               const void*, StateSrc, void*, hipStream_t) { SSD_STUB; }
 hipError_t launch_step(int64_t, int64_t, int64_t, int64_t, int64_t, bool, float*, const void*,
                        const float*, const void*, const void*, void*, hipStream_t) { SSD_STUB; }
+hipError_t launch_stream_rmw(float*, int64_t, float, int, bool, hipStream_t) { SSD_STUB; }
 hipError_t launch_remap_rows(void*, const void*, int64_t, int64_t, int64_t, int64_t, int64_t, int64_t,
                              hipStream_t) { SSD_STUB; }
 hipError_t launch_bcast_heads(void*, const void*, int64_t, int64_t, int64_t, int64_t, int64_t, int64_t,

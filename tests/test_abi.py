@@ -131,9 +131,25 @@ def test_step_validation(lib):
     assert call(st(nheads=6, ngroups=4), *F) == _lib.SSD_ERR_SHAPE
     assert call(st(dtype=9), *F) == _lib.SSD_ERR_DTYPE
     assert call(st(reserved=1), *F) == _lib.SSD_ERR_SHAPE
+    # 2^20 (b, h) slices of 64 x 128: 2^31 threads of 4 state elements is fine,
+    # 2^22 slices would need 2^33 threads in one launch
+    assert call(st(batch=1 << 14, nheads=64), None, *F[1:]) == _lib.SSD_ERR_NULL
+    assert call(st(batch=1 << 16, nheads=64), *F) == _lib.SSD_ERR_UNSUPPORTED
     assert call(st(), None, *F[1:]) == _lib.SSD_ERR_NULL
     assert call(st(), ctypes.c_void_p((1 << 20) + 4), *F[1:]) == _lib.SSD_ERR_ALIGN
     assert call(st(), F[0], F[1], F[2], F[3], F[4], F[0]) == _lib.SSD_ERR_ALIAS
+
+
+def test_stream_rmw_validation(lib):
+    call = lambda *a: lib.ssd_stream_rmw(*a, None)
+    p = ctypes.c_void_p(1 << 20)
+    assert call(p, 6, 1.0, 8, 1) == _lib.SSD_ERR_SHAPE            # n not a multiple of 4
+    assert call(p, -4, 1.0, 8, 1) == _lib.SSD_ERR_SHAPE
+    assert call(p, 64, 1.0, 3, 1) == _lib.SSD_ERR_UNSUPPORTED     # per_thread not in {1,2,4,8}
+    assert call(p, 64, 1.0, 8, 2) == _lib.SSD_ERR_SHAPE           # nontemporal not 0/1
+    assert call(None, 64, 1.0, 8, 1) == _lib.SSD_ERR_NULL
+    assert call(ctypes.c_void_p((1 << 20) + 4), 64, 1.0, 8, 1) == _lib.SSD_ERR_ALIGN
+    assert call(None, 0, 1.0, 8, 1) == _lib.SSD_OK                # empty: nothing to do
 
 
 def test_stage_validation(lib):

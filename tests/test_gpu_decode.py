@@ -153,3 +153,19 @@ def test_prefill_then_decode_handoff(dtype, seg):
     es = slice_rel_err(host_f64(state), Sr, (0, 1))
     log("   err prefill Y=%.3e decode y=%.3e state=%.3e" % (ep, ed, es))
     assert ep < tol and ed < tol and es < tol, (ep, ed, es)
+
+
+@pytest.mark.parametrize("n,per_thread,nt", [(4, 8, True), (4 * 1000 + 4, 1, False), (1 << 20, 8, True),
+                                             (1 << 20, 2, False), (3 * 256 * 4 * 4 + 12, 4, True)])
+def test_stream_rmw_exact(n, per_thread, nt):
+    # the ceiling kernel multiplies every element exactly once (ragged tails
+    # included) and touches nothing past n
+    g = torch.Generator().manual_seed(n)
+    base = torch.randn(n + 64, generator=g, dtype=torch.float32)
+    t = base.cuda()
+    ssd.stream_rmw(t[:n], 0.75, per_thread, nt)
+    torch.cuda.synchronize()
+    got = t.cpu()
+    assert torch.equal(got[:n], base[:n] * 0.75)
+    assert torch.equal(got[n:], base[n:])
+
