@@ -117,7 +117,7 @@ ssd::FwdShape shape_of(const ssd_fwd_desc* d) {
 // Plan of the MFMA path: the segment length k (chunks one workgroup walks
 // while carrying the state in registers) and the fused pass's units per
 // workgroup sw.  The estimate (microseconds) is a model fitted to timings of
-// 120 plans over eight shapes on MI355X (within about 10% of each):
+// 162 plans over eight shapes on MI355X (most within 10%; boxes differ by up to 10%):
 //  - fused pass: one workgroup per CU, so ceil(workgroups / 256) rounds of
 //    k * Q / 64 blocks each; a block takes kFusedUs[N][sw] when few
 //    workgroups run, plus kOccUs[N] * sw / 5 scaled by the fraction of the
@@ -130,9 +130,9 @@ ssd::FwdShape shape_of(const ssd_fwd_desc* d) {
 // For each segment count only the most balanced k is tried; the cheapest
 // (k, sw) wins, ties going to fewer segments and fewer units.
 double plan_cost_us(const ssd::FwdShape& s, int64_t k, int sw) {
-    constexpr double kFusedUs[2][3] = {{1.83, 1.89, 2.19}, {1.70, 2.34, 2.33}};   // [N > 64][sw - 4]
-    constexpr double kOccUs[2] = {0.35, 1.28}, kStateUs[2] = {1.45, 1.29};
-    constexpr double kLaunchUs = 3.9, kSegExtraUs = 8.2, kSegLatencyUs = 0.39, kUsPerStateMB = 0.133;
+    constexpr double kFusedUs[2][3] = {{1.79, 1.81, 2.17}, {1.51, 2.49, 2.30}};   // [N > 64][sw - 4]
+    constexpr double kOccUs[2] = {0.49, 1.36}, kStateUs[2] = {1.44, 1.27};
+    constexpr double kLaunchUs = 4.3, kSegExtraUs = 8.2, kSegLatencyUs = 0.34, kUsPerStateMB = 0.1375;
     const int wide = s.N > 64 ? 1 : 0;
     const int64_t nseg = (s.nc + k - 1) / k;
     const double blocks = (double)k * (double)((s.Q + 63) / 64);
