@@ -8,8 +8,14 @@ batch of seeded synthetic inputs already resident in HBM.  Distinct input
 batches are cycled so that the timed loop's working set exceeds the 256 MB
 Infinity Cache.
 
+Before each timed leg's W warm-up steps the GPU runs CLOCK_SETTLE_MS of
+the library's streaming kernel on a scratch array (clock_settle_ms in the
+line): after the host-side input generation its clocks need ~25 ms of
+sustained work to come back up, which would otherwise land in the K timed
+steps.
+
 Prints ONE JSON line.  Besides the contract fields it carries:
-  roofline      the dominant kernel (the MFMA full pass) against the HBM peak:
+  roofline      the dominant kernel (the fused pass) against the HBM peak:
                 algorithmic bytes per launch over that kernel's own average
                 launch duration, measured with HIP events on the launch
                 stream (the pass alone through its stage entry point when the
@@ -26,7 +32,8 @@ Prints ONE JSON line.  Besides the contract fields it carries:
   cpu_baseline  the fp64 CPU oracle on the same workload (host cores);
   secondary     the rest of the metric's workloads: the 130M-shaped layer,
                 the state-64 seqlen sweep at all six lengths (512 .. 512K),
-                the decode step's HBM bandwidth, and the backward of the
+                the decode step's HBM bandwidth (and the in-place stream
+                ceiling of the same state array), and the backward of the
                 130M-shaped layer.
 """
 import argparse
@@ -106,6 +113,52 @@ def upload(d):
     return out
 
 
+CLOCK_SETTLE_MS = 100.0
+_settle_buf = None
+
+
+def settle_clocks(ms=CLOCK_SETTLE_MS):
+    """Keep the GPU busy for `ms` milliseconds with the library's streaming
+    kernel on a 256 MB scratch array (not a step of any workload).  After the
+    seconds of host-side input generation the GPU's clocks take ~25 ms of
+    sustained work to come back up: the 2.7B-shaped forward reads 0.27-0.29 ms
+    in its first 20 steps after a 5-step warm-up and 0.226 ms from ~100 steps
+    on.  Every timed leg calls this right before its warm-up steps, so the K
+    timed steps measure the kernels at their running clocks."""
+    import torch
+    import ssd_chunked_scan_chunk_amd as ssd
+    global _settle_buf
+    if _settle_buf is None:
+        _settle_buf = torch.zeros(64 << 20, dtype=torch.float32, device="cuda")
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    done = 0.0
+    while done < ms:
+        e0.record()
+        for _ in range(20):
+            ssd.stream_rmw(_settle_buf, 1.0, 1, True)
+        e1.record()
+        e1.synchronize()
+        done += e0.elapsed_time(e1)
+
+
+def warm(fn, min_steps, min_ms=30.0):
+    """Untimed calls of fn: at least min_steps, and at least min_ms of GPU
+    time (the secondary legs, whose steps range from 20 us to 2 ms)."""
+    import torch
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    done, i = 0.0, 0
+    while i < min_steps or done < min_ms:
+        e0.record()
+        for _ in range(max(1, min_steps)):
+            fn(i)
+            i += 1
+        e1.record()
+        e1.synchronize()
+        done += e0.elapsed_time(e1)
+
+
 def time_events(fn, steps):
     import torch
     e0 = torch.cuda.Event(enable_timing=True)
@@ -119,7 +172,7 @@ def time_events(fn, steps):
     return e0.elapsed_time(e1) / 1e3  # seconds
 
 
-def bench_forward(sh, steps, warmup, nbatch, seed0=0):
+def bench_forward(sh, steps, warmup, nbatch, seed0=0, warm_ms=0.0):
     """Time `steps` forwards cycling over `nbatch` seeded batches.
     Returns (seconds per step, seconds per launch of the full-pass kernel,
     plan, per-pass milliseconds)."""
@@ -139,8 +192,8 @@ def bench_forward(sh, steps, warmup, nbatch, seed0=0):
         ssd.chunk_scan_fwd(g["X"], g["a"], g["B"], g["C"], sh.chunk, Y=Ys[i % nbatch],
                            final_state=fin if sh.final_state else None, workspace=ws)
 
-    for i in range(warmup):
-        step(i)
+    settle_clocks()
+    warm(step, warmup, warm_ms)
     t_step = time_events(step, steps) / steps
 
     # The step's launches one by one, in the configuration the step uses.
@@ -193,10 +246,10 @@ def n_batches(sh):
     return max(1, int(np.ceil(2 * 256e6 / fwd_algo_bytes(sh))))
 
 
-def measure_forward(sh, steps, warmup):
+def measure_forward(sh, steps, warmup, warm_ms=0.0):
     """One forward workload: step time, tokens/s, plan, passes, and the
     HBM / MFMA fractions of the step and of its full pass."""
-    t_step, t_kernel, plan, passes = bench_forward(sh, steps, warmup, n_batches(sh))
+    t_step, t_kernel, plan, passes = bench_forward(sh, steps, warmup, n_batches(sh), warm_ms=warm_ms)
     tok = sh.batch * sh.seqlen
     nbytes = fwd_algo_bytes(sh)
     fq = tok * fwd_algo_flops_per_token(sh, sh.chunk)
@@ -228,15 +281,14 @@ def bench_decode(steps, warmup):
         t = i % T
         ssd.step(state, x[t], a[t], B[t], C[t], y=y)
 
-    for i in range(warmup):
-        step(i)
-    t = time_events(step, steps) / steps
     Bz, H, P, N, G = sh.batch, sh.nheads, sh.headdim, sh.dstate, sh.ngroups
     nbytes = 2 * Bz * H * P * N * 4 + 2 * Bz * H * P * 2 + 2 * Bz * G * N * 2 + Bz * H * 4
-    # The practical ceiling: the library's plain in-place read-modify-write of
-    # the same state array (scale 1, so the state keeps its values), for each
-    # of its launch shapes.
+    # The practical ceiling first (it also brings the GPU out of the idle
+    # spell of the input generation): the library's plain in-place
+    # read-modify-write of the same state array (scale 1, so the state keeps
+    # its values), for each of its launch shapes.
     ceiling = {}
+    settle_clocks()
     for per_thread in (1, 2, 4, 8):
         for nt in (False, True):
             def fn(i, v=per_thread, n=nt):
@@ -245,17 +297,25 @@ def bench_decode(steps, warmup):
                 fn(i)
             tr = time_events(fn, steps) / steps
             ceiling["v%d%s" % (per_thread, "_nt" if nt else "")] = 2 * state.numel() * 4 / tr / 1e9
+    # then the decode steps: a longer warm-up, and the timed steps in chunks
+    # of 20 (their spread shows whether clocks were still settling)
+    for i in range(max(warmup, 50)):
+        step(i)
+    chunks = [time_events(step, 20) / 20 for _ in range(max(1, steps // 20))]
+    t = float(np.median(chunks))
     del state, x, B, C, a, y
     torch.cuda.empty_cache()
+    ceiling["_chunks_us"] = [round(c * 1e6, 1) for c in chunks]
     return t, nbytes, ceiling
 
 
 def decode_record(td, nbytes, ceiling):
+    chunks = ceiling.pop("_chunks_us")
     best = max(ceiling.values())
     return {"workload": "batch 256, 80 heads, headdim 64, dstate 128, fp32 state in place",
             "us_per_step": td * 1e6, "GB_per_s": nbytes / td / 1e9,
             "hbm_frac": nbytes / td / 1e9 / HBM_PEAK_GBS, "tokens_per_s": 256 / td,
-            "bytes_per_step": nbytes,
+            "bytes_per_step": nbytes, "us_per_step_by_20_step_chunk": chunks,
             "stream_ceiling": {"GB_per_s": best, "hbm_frac": best / HBM_PEAK_GBS,
                                "decode_frac_of_ceiling": nbytes / td / 1e9 / best,
                                "kernel": "ssd_stream_rmw: in-place fp32 x *= 1 over the same state array",
@@ -303,8 +363,8 @@ def bench_backward(sh, steps, warmup, nbatch, seed0=100):
         ssd.chunk_scan_bwd(g["X"], g["a"], g["B"], g["C"], g["dY"], sh.chunk, initial_state=g["S0"],
                            dfinal_state=g["dSf"], return_dinitial_state=True, workspace=ws)
 
-    for i in range(warmup):
-        step(i)
+    settle_clocks()
+    warm(step, warmup, 30.0)
     t = time_events(step, steps) / steps
 
     # the dominant kernel (da) alone through its stage entry point, fed chunk
@@ -388,8 +448,9 @@ def cpu_baseline(sh):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=100,
+                    help="untimed steps before the timed ones; the default covers the ~25 ms the GPU clocks take to come up under this workload")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--workload", default="m2_2p7b",
@@ -462,6 +523,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_settle_ms": CLOCK_SETTLE_MS,
         "ms_per_step": m["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
@@ -486,15 +548,15 @@ def main():
     if not args.no_secondary:
         sec = {}
         if wl != "m2_130m":
-            r = measure_forward(s130, args.steps, args.warmup)
+            r = measure_forward(s130, args.steps, args.warmup, warm_ms=30.0)
             r.pop("_t_kernel"), r.pop("_t_step")
             sec["m2_130m"] = r
         for L in si.SWEEP_SEQLENS:
             shp = si.sweep_shape(L)
-            r = measure_forward(shp, max(5, args.steps // (1 + L // 65536)), 2)
+            r = measure_forward(shp, max(5, args.steps // (1 + L // 65536)), 2, warm_ms=30.0)
             r.pop("_t_kernel"), r.pop("_t_step")
             sec["sweep_n64_L%d" % L] = r
-        td, nbytes, ceil = bench_decode(max(20, args.steps), 5)
+        td, nbytes, ceil = bench_decode(max(100, args.steps), 5)
         sec["decode_step"] = decode_record(td, nbytes, ceil)
         tokens130 = s130.batch * s130.seqlen
         tb, tda = bench_backward(s130, max(10, args.steps // 2), 3, 2)
