@@ -30,7 +30,8 @@ Prints ONE JSON line.  Besides the contract fields it carries:
                 kernels execute;
   passes        the step's launches timed one by one the same way;
   cpu_baseline  the fp64 CPU oracle on the same workload (host cores);
-  secondary     the rest of the metric's workloads: the 130M-shaped layer,
+  secondary     the rest of the metric's workloads: the 130M-shaped layer
+                (bf16, and fp32 through the VALU kernel),
                 the state-64 seqlen sweep at all six lengths (512 .. 512K),
                 the decode step's HBM bandwidth (and the in-place stream
                 ceiling of the same state array), and the backward of the
@@ -49,6 +50,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector
 
 
 def fwd_algo_bytes_per_token(sh):
@@ -556,6 +558,20 @@ def main():
             r = measure_forward(shp, max(5, args.steps // (1 + L // 65536)), 2, warm_ms=30.0)
             r.pop("_t_kernel"), r.pop("_t_step")
             sec["sweep_n64_L%d" % L] = r
+        # the fp32 path (the VALU kernel, exact segment sums, fp32 throughout)
+        # on the 130M-shaped layer
+        import dataclasses
+        s130f = dataclasses.replace(s130, dtype=si.F32)
+        r = measure_forward(s130f, max(5, args.steps // 5), 2, warm_ms=30.0)
+        sec["m2_130m_fp32"] = {
+            "workload": "the 130M-shaped layer with fp32 X, B, C (VALU kernel)",
+            "ms_per_step": r["ms_per_step"], "tokens_per_s": r["tokens_per_s"], "plan": r["plan"],
+            "hbm_frac": r["hbm_frac"], "algo_bytes": r["algo_bytes"],
+            "valu_fp32": {"flops_per_step": r["algo_flops"],
+                          "achieved": r["algo_flops"] / (r["ms_per_step"] * 1e-3) / 1e12,
+                          "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                          "frac": r["algo_flops"] / (r["ms_per_step"] * 1e-3) / 1e12 / FP32_VALU_PEAK_TFLOPS,
+                          "count": "the chunked form's flops at the caller's chunk"}}
         td, nbytes, ceil = bench_decode(max(100, args.steps), 5)
         sec["decode_step"] = decode_record(td, nbytes, ceil)
         tokens130 = s130.batch * s130.seqlen

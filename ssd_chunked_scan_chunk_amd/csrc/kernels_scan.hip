@@ -122,12 +122,236 @@ __global__ __launch_bounds__(kValuThreads) void k_valu_fwd(
         for (int k = tid; k < PN; k += kValuThreads) S_fin[bh * PN + k] = sS[k];
 }
 
+// ---------------------------------------------------------------------------
+// VALU forward, staged variant for the shapes whose chunk fits in LDS (N <= 128,
+// Q <= 256, P*N a multiple of 256 with each thread's 32 or fewer state entries
+// in one row).  Same per-(b, h) walk and the same fp32 products, but every
+// operand of an inner loop comes from LDS or registers: the chunk's X in LDS,
+// thread j's B row in registers for the scores, C rows per row block and B
+// rows per 64-step block in LDS.  Decays come from fp64 prefix sums of a:
+// exp(cs_i - cs_j) with the difference taken in fp64 has no cancellation
+// (the fp32 sums above were built term by term for the same reason), and each
+// step's state weight exp(cs_end - cs_j) is formed once per step instead of
+// once per state entry.
+// ---------------------------------------------------------------------------
+constexpr int kValuNMax = 128, kValuNRMax = 32, kValuJB = 64;
+
+__device__ __forceinline__ double block_scan_f64(double v, double* s_tot) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const double u = __shfl_up(v, d, 64);
+        if (lane >= d) v += u;
+    }
+    if (lane == 63) s_tot[wave] = v;
+    lds_barrier();
+    double add = 0.0;
+    for (int w = 0; w < wave; ++w) add += s_tot[w];
+    lds_barrier();
+    return v + add;
+}
+
+static size_t valu_fast_lds(const FwdShape& s) {
+    const size_t work = (size_t)kValuRows * s.Q + (size_t)kValuRows * s.N;
+    const size_t bblk = (size_t)kValuJB * s.N;
+    return ((size_t)s.Q * s.P + (size_t)s.P * s.N + (work > bblk ? work : bblk) + s.Q) * sizeof(float) +
+           ((size_t)s.Q + 4) * sizeof(double);
+}
+
+static bool valu_fast_ok(const FwdShape& s) {
+    // (Q and N multiples of 4 keep every 16-byte LDS read aligned)
+    if (s.N > kValuNMax || s.Q > kValuThreads || (s.P * s.N) % kValuThreads != 0 || s.Q % 4 != 0 ||
+        s.N % 4 != 0)
+        return false;
+    const int64_t nr = s.P * s.N / kValuThreads;
+    return nr <= kValuNRMax && s.N % nr == 0 && valu_fast_lds(s) <= 160 * 1024;
+}
+
+template <typename T, typename TY = T>
+__global__ __launch_bounds__(kValuThreads) void k_valu_fwd_staged(
+    const T* __restrict__ X, const float* __restrict__ a, const T* __restrict__ B,
+    const T* __restrict__ C, const float* __restrict__ S0, TY* __restrict__ Y,
+    float* __restrict__ S_fin, float* __restrict__ S_chunks, int64_t L, int H, int P, int N,
+    int G, int Q)
+{
+    extern __shared__ double smem64[];
+    double* sCs = smem64;                 // [Q] fp64 inclusive prefix sums of a
+    double* sTot = sCs + Q;               // [4] scan scratch
+    float* sX = reinterpret_cast<float*>(sTot + 4);   // [Q][P] the chunk's X
+    float* sS = sX + Q * P;               // [P][N] carried state
+    float* sW = sS + P * N;               // [Q] state weights of the chunk's steps
+    float* sWork = sW + Q;                // scores [kValuRows][Q] + C rows [kValuRows][N], or B rows [kValuJB][N]
+    float* sM = sWork;
+    float* sC = sWork + kValuRows * Q;
+
+    const int h = blockIdx.x, b = blockIdx.y, g = h / (H / G);
+    const int tid = threadIdx.x;
+    const int PN = P * N;
+    const int NR = PN / kValuThreads;     // state entries per thread, one row
+    const int sp = tid * NR / N, sn0 = (tid * NR) % N;
+    const int64_t bh = (int64_t)b * H + h;
+    auto xrow = [&](int64_t t) { return X + (((int64_t)b * L + t) * H + h) * P; };
+    auto brow = [&](int64_t t) { return B + (((int64_t)b * L + t) * G + g) * N; };
+    auto crow = [&](int64_t t) { return C + (((int64_t)b * L + t) * G + g) * N; };
+
+    for (int k = tid; k < PN; k += kValuThreads) sS[k] = S0 ? S0[bh * PN + k] : 0.f;
+
+    const int64_t nc = (L + Q - 1) / Q;
+    for (int64_t c = 0; c < nc; ++c) {
+        const int64_t t0 = c * Q;
+        const int Lc = (int)((L - t0 < Q) ? (L - t0) : Q);
+        __syncthreads();
+        const double av = tid < Lc ? (double)a[((int64_t)b * L + t0 + tid) * H + h] : 0.0;
+        const double cs = block_scan_f64(av, sTot);
+        if (tid < Q) sCs[tid] = cs;
+        for (int k = tid; k < Q * P; k += kValuThreads) {
+            const int i = k / P;
+            sX[k] = i < Lc ? Elem<T>::load(xrow(t0 + i) + (k - i * P)) : 0.f;
+        }
+        if (S_chunks)
+            for (int k = tid; k < PN; k += kValuThreads)
+                S_chunks[(((int64_t)b * nc + c) * H + h) * PN + k] = sS[k];
+        __syncthreads();
+
+        // ---- outputs: masked decayed scores per row block, then Y rows ----
+        if (Y) {
+            float bj[kValuNMax];
+#pragma unroll
+            for (int n = 0; n < kValuNMax; ++n)
+                bj[n] = (tid < Lc && n < N) ? Elem<T>::load(brow(t0 + tid) + n) : 0.f;
+            for (int i0 = 0; i0 < Lc; i0 += kValuRows) {
+                const int nr = Lc - i0 < kValuRows ? Lc - i0 : kValuRows;
+                for (int k = tid; k < nr * N; k += kValuThreads) {
+                    const int r = k / N;
+                    sC[k] = Elem<T>::load(crow(t0 + i0 + r) + (k - r * N));
+                }
+                __syncthreads();
+                if (tid < Lc) {
+                    for (int r = 0; r < nr; ++r) {
+                        const int i = i0 + r;
+                        float m = 0.f;
+                        if (tid <= i) {
+                            // four partial sums over n = 4k + e (16-byte reads of C)
+                            float cb4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                            for (int n = 0; n < kValuNMax; n += 4)
+                                if (n < N) {
+                                    const float4 cv = *reinterpret_cast<const float4*>(&sC[r * N + n]);
+                                    cb4[0] += cv.x * bj[n];
+                                    cb4[1] += cv.y * bj[n + 1];
+                                    cb4[2] += cv.z * bj[n + 2];
+                                    cb4[3] += cv.w * bj[n + 3];
+                                }
+                            m = expf((float)(sCs[i] - sCs[tid])) * ((cb4[0] + cb4[1]) + (cb4[2] + cb4[3]));
+                        }
+                        sM[r * Q + tid] = m;
+                    }
+                }
+                __syncthreads();
+                for (int idx = tid; idx < nr * P; idx += kValuThreads) {
+                    const int r = idx / P, p = idx - r * P, i = i0 + r;
+                    // four partial sums each (j = 4k + e; n = 4k + e with 16-byte reads)
+                    float acc4[4] = {0.f, 0.f, 0.f, 0.f};
+                    int j = 0;
+                    for (; j + 3 <= i; j += 4) {
+                        const float4 mv = *reinterpret_cast<const float4*>(&sM[r * Q + j]);
+                        acc4[0] += mv.x * sX[j * P + p];
+                        acc4[1] += mv.y * sX[(j + 1) * P + p];
+                        acc4[2] += mv.z * sX[(j + 2) * P + p];
+                        acc4[3] += mv.w * sX[(j + 3) * P + p];
+                    }
+                    for (; j <= i; ++j) acc4[0] += sM[r * Q + j] * sX[j * P + p];
+                    const float acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+                    float off4[4] = {0.f, 0.f, 0.f, 0.f};
+                    for (int n = 0; n < N; n += 4) {
+                        const float4 cv = *reinterpret_cast<const float4*>(&sC[r * N + n]);
+                        const float4 sv = *reinterpret_cast<const float4*>(&sS[p * N + n]);
+                        off4[0] += cv.x * sv.x;
+                        off4[1] += cv.y * sv.y;
+                        off4[2] += cv.z * sv.z;
+                        off4[3] += cv.w * sv.w;
+                    }
+                    const float off = (off4[0] + off4[1]) + (off4[2] + off4[3]);
+                    Elem<TY>::store(Y + (((int64_t)b * L + t0 + i) * H + h) * P + p,
+                                    acc + expf((float)sCs[i]) * off);
+                }
+                __syncthreads();
+            }
+        }
+
+        // ---- chunk state: dS[p][n] = sum_j w_j X[j][p] B[j][n], B rows staged
+        // kValuJB at a time; S <- exp(cs_end) S + dS ----
+        if (tid < Q) sW[tid] = tid < Lc ? expf((float)(sCs[Lc - 1] - sCs[tid])) : 0.f;
+        float ds[kValuNRMax];
+#pragma unroll
+        for (int e = 0; e < kValuNRMax; ++e) ds[e] = 0.f;
+        for (int j0 = 0; j0 < Lc; j0 += kValuJB) {
+            const int nj = Lc - j0 < kValuJB ? Lc - j0 : kValuJB;
+            __syncthreads();
+            for (int k = tid; k < nj * N; k += kValuThreads) {
+                const int r = k / N;
+                sWork[k] = Elem<T>::load(brow(t0 + j0 + r) + (k - r * N));
+            }
+            __syncthreads();
+            if (NR % 4 == 0) {   // 16-byte reads of the B rows
+                for (int jj = 0; jj < nj; ++jj) {
+                    const float xw = sW[j0 + jj] * sX[(j0 + jj) * P + sp];
+                    const float* brw = sWork + jj * N + sn0;
+#pragma unroll
+                    for (int e = 0; e < kValuNRMax; e += 4)
+                        if (e < NR) {
+                            const float4 bv = *reinterpret_cast<const float4*>(brw + e);
+                            ds[e] += xw * bv.x;
+                            ds[e + 1] += xw * bv.y;
+                            ds[e + 2] += xw * bv.z;
+                            ds[e + 3] += xw * bv.w;
+                        }
+                }
+            } else {
+                for (int jj = 0; jj < nj; ++jj) {
+                    const float xw = sW[j0 + jj] * sX[(j0 + jj) * P + sp];
+                    const float* brw = sWork + jj * N + sn0;
+#pragma unroll
+                    for (int e = 0; e < kValuNRMax; ++e)
+                        if (e < NR) ds[e] += xw * brw[e];
+                }
+            }
+        }
+        __syncthreads();
+        const float decay = expf((float)sCs[Lc - 1]);
+#pragma unroll
+        for (int e = 0; e < kValuNRMax; ++e)
+            if (e < NR) sS[sp * N + sn0 + e] = decay * sS[sp * N + sn0 + e] + ds[e];
+    }
+    __syncthreads();
+    if (S_fin)
+        for (int k = tid; k < PN; k += kValuThreads) S_fin[bh * PN + k] = sS[k];
+}
+
 hipError_t launch_valu_fwd(const FwdShape& s, bool bf16, const void* X, const float* a,
                            const void* B, const void* C, const float* S0, void* Y,
                            float* S_fin, hipStream_t st, float* S_chunks, bool y_f32)
 {
-    const size_t lds = (size_t)(2 * s.Q + s.P * s.N + 4 + kValuRows * s.Q) * sizeof(float);
     dim3 grid((unsigned)s.H, (unsigned)s.Bz);
+    if (valu_fast_ok(s)) {
+        const size_t lds = valu_fast_lds(s);
+#define SSD_VALU_STAGED(TT, TYY)                                                                       \
+    do {                                                                                               \
+        auto k = k_valu_fwd_staged<TT, TYY>;                                                           \
+        hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, \
+                                           (int)lds);                                                  \
+        if (e != hipSuccess) return e;                                                                 \
+        hipLaunchKernelGGL(k, grid, dim3(kValuThreads), lds, st, (const TT*)X, a, (const TT*)B,        \
+                           (const TT*)C, S0, (TYY*)Y, S_fin, S_chunks, s.L, (int)s.H, (int)s.P,        \
+                           (int)s.N, (int)s.G, (int)s.Q);                                              \
+    } while (0)
+        if (bf16 && y_f32) SSD_VALU_STAGED(u16, float);
+        else if (bf16) SSD_VALU_STAGED(u16, u16);
+        else SSD_VALU_STAGED(float, float);
+#undef SSD_VALU_STAGED
+        return hipGetLastError();
+    }
+    const size_t lds = (size_t)(2 * s.Q + s.P * s.N + 4 + kValuRows * s.Q) * sizeof(float);
     if (bf16 && y_f32) {
         auto k = k_valu_fwd<u16, float>;
         hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
