@@ -117,7 +117,7 @@ ssd::FwdShape shape_of(const ssd_fwd_desc* d) {
 // Plan of the MFMA path: the segment length k (chunks one workgroup walks
 // while carrying the state in registers) and the fused pass's units per
 // workgroup sw.  The estimate (microseconds) is a model fitted to timings of
-// 162 plans over eight shapes on MI355X (most within 10%; boxes differ by up to 10%):
+// 49 plans over eight shapes on MI355X at running clocks (most within 7%):
 //  - fused pass: one workgroup per CU, so ceil(workgroups / 256) rounds of
 //    k * Q / 64 blocks each; a block takes kFusedUs[N][sw] when few
 //    workgroups run, plus kOccUs[N] * sw / 5 scaled by the fraction of the
@@ -128,11 +128,15 @@ ssd::FwdShape shape_of(const ssd_fwd_desc* d) {
 //    pass, read and written by the scan, read by the fused pass) and the two
 //    extra launches.
 // For each segment count only the most balanced k is tried; the cheapest
-// (k, sw) wins, ties going to fewer segments and fewer units.
+// (k, sw) wins, ties going to fewer segments and fewer units.  Segments are
+// at most kMaxSegSteps long when that leaves them few enough: longer ones
+// measured slower than the model predicts (the 512K-step sweep point: 90-chunk
+// segments 1.63 ms against 1.51 ms at 45 chunks).
+constexpr int64_t kMaxSegSteps = 16384;
 double plan_cost_us(const ssd::FwdShape& s, int64_t k, int sw) {
-    constexpr double kFusedUs[2][3] = {{1.79, 1.81, 2.17}, {1.51, 2.49, 2.30}};   // [N > 64][sw - 4]
-    constexpr double kOccUs[2] = {0.49, 1.36}, kStateUs[2] = {1.44, 1.27};
-    constexpr double kLaunchUs = 4.3, kSegExtraUs = 8.2, kSegLatencyUs = 0.34, kUsPerStateMB = 0.1375;
+    constexpr double kFusedUs[2][3] = {{1.88, 1.94, 2.25}, {1.97, 2.70, 2.83}};   // [N > 64][sw - 4]
+    constexpr double kOccUs[2] = {0.48, 0.55}, kStateUs[2] = {1.22, 1.30};
+    constexpr double kLaunchUs = 6.1, kSegExtraUs = 8.2, kSegLatencyUs = 0.25, kUsPerStateMB = 0.1166;
     const int wide = s.N > 64 ? 1 : 0;
     const int64_t nseg = (s.nc + k - 1) / k;
     const double blocks = (double)k * (double)((s.Q + 63) / 64);
@@ -177,6 +181,8 @@ void auto_plan(const ssd::FwdShape& s, int64_t k_fixed, int sw_fixed, size_t ws_
             const int64_t k = k_fixed > 0 ? k_fixed : (s.nc + want - 1) / want;   // longest segment
             if (k == prev_k) continue;
             prev_k = k;
+            if (k_fixed <= 0 && k * s.Q > kMaxSegSteps && (s.nc + kMaxSegSteps / s.Q - 1) / (kMaxSegSteps / s.Q) <= max_seg)
+                continue;
             if (k_fixed <= 0 && fwd_ws_bytes(s, (s.nc + k - 1) / k) > ws_cap) continue;
             const double cost = plan_cost_us(s, k, sw);
             if (cost < best - 1e-9) {

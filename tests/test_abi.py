@@ -107,10 +107,10 @@ def test_plans(lib):
     assert a == _lib.SSD_ALGO_MFMA and n > 1 and k * n >= 2048
     a, k, n = plan(lib, desc(seg_chunks=3, seqlen=256 * 10))
     assert (k, n) == (3, 4)
-    # the 2.7B-shaped layer: 8 x 80 x 2 = 1280 units, one segment, in 214
-    # workgroups of six (measured faster than 256 of five, whose fifth unit
-    # shares a SIMD)
-    assert plan(lib, desc(batch=8, seqlen=4096, nheads=80), units=True) == (_lib.SSD_ALGO_MFMA, 16, 1, 6)
+    # the 2.7B-shaped layer: 8 x 80 x 2 = 1280 units in 256 workgroups of five, one segment
+    assert plan(lib, desc(batch=8, seqlen=4096, nheads=80), units=True) == (_lib.SSD_ALGO_MFMA, 16, 1, 5)
+    # long sequences: segments of at most 16K steps
+    assert plan(lib, desc(batch=1, seqlen=524288, nheads=32, dstate=64))[1] * 256 <= 16384
     # a forced split is honoured; others are rejected on the host
     assert plan(lib, desc(wg_units=4), units=True)[3] == 4
     assert plan(lib, desc(wg_units=6, seg_chunks=1), units=True)[1:] == (1, 2, 6)
