@@ -147,8 +147,9 @@ ssd_status ssd_step(const ssd_step_desc* desc, float* state, const void* x, cons
  * the same read-modify-write stream as the decode step's state with no other
  * traffic.  per_thread in {1, 2, 4, 8} float4 per thread; nontemporal 1 uses
  * the nontemporal load/store hints of the decode kernel, 0 plain accesses.
- * Errors: SSD_ERR_SHAPE / SSD_ERR_UNSUPPORTED / SSD_ERR_NULL / SSD_ERR_ALIGN
- * before anything is enqueued, SSD_ERR_HIP if the launch fails. */
+ * n / 4 must be below 2^32.  Errors: SSD_ERR_SHAPE / SSD_ERR_UNSUPPORTED /
+ * SSD_ERR_NULL / SSD_ERR_ALIGN before anything is enqueued, SSD_ERR_HIP if
+ * the launch fails. */
 ssd_status ssd_stream_rmw(float* data, int64_t n, float scale, int32_t per_thread, int32_t nontemporal,
                           void* stream);
 

@@ -577,7 +577,8 @@ ssd_status ssd_stream_rmw(float* data, int64_t n, float scale, int32_t per_threa
     if (per_thread != 1 && per_thread != 2 && per_thread != 4 && per_thread != 8)
         return fail(SSD_ERR_UNSUPPORTED, "per_thread must be 1, 2, 4 or 8");
     if (nontemporal != 0 && nontemporal != 1) return fail(SSD_ERR_SHAPE, "nontemporal must be 0 or 1");
-    if (n / 4 > ((int64_t)1 << 31) * 256) return fail(SSD_ERR_UNSUPPORTED, "n beyond the supported range");
+    // one thread per float4 at most, and a launch holds < 2^32 threads
+    if (n / 4 >= ((int64_t)1 << 32)) return fail(SSD_ERR_UNSUPPORTED, "n beyond the supported range");
     if (n == 0) return ok();
     if (!data) return fail(SSD_ERR_NULL, "data is NULL");
     if (!aligned(data, 16)) return fail(SSD_ERR_ALIGN, "data must be 16-byte aligned");

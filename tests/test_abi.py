@@ -152,6 +152,7 @@ def test_stream_rmw_validation(lib):
     assert call(None, 64, 1.0, 8, 1) == _lib.SSD_ERR_NULL
     assert call(ctypes.c_void_p((1 << 20) + 4), 64, 1.0, 8, 1) == _lib.SSD_ERR_ALIGN
     assert call(None, 0, 1.0, 8, 1) == _lib.SSD_OK                # empty: nothing to do
+    assert call(p, 4 << 32, 1.0, 1, 1) == _lib.SSD_ERR_UNSUPPORTED  # 2^32 float4: too many threads
 
 
 def test_stage_validation(lib):
