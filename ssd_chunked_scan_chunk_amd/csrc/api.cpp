@@ -802,9 +802,13 @@ ssd_status ssd_chunk_scan_bwd(const ssd_fwd_desc* desc, const void* X, const flo
                                    F(W_SREV), 0, F(W_SREV) + (nc - 1) * H * PN, nc * H * PN, hs),
             "bwd: adjoint state scan");
     {
+        // the fused forward pass on the reversed problem, one chunk per segment
         ssd::StateSrc src{dfinal_state, H * PN, F(W_SREV), nc * H * PN, H * PN};
-        SSD_TRY(ssd::launch_mfma_out(bp.sr, 1, nc, V(W_DYR), F(W_AR), V(W_CR), V(W_BR), src, V(W_DXR),
-                                     dinitial_state, hs), "bwd: dX pass");
+        int64_t k1 = 1;
+        int sw1 = 4;
+        auto_plan(bp.sr, 1, 0, SIZE_MAX, &k1, &sw1);
+        SSD_TRY(ssd::launch_fwd(bp.sr, sw1, 1, nc, V(W_DYR), F(W_AR), V(W_CR), V(W_BR), src, V(W_DXR),
+                                dinitial_state, hs), "bwd: dX pass");
     }
     SSD_TRY(ssd::launch_remap_rows(dX, V(W_DXR), Bz, L, Lp, Lp - 1, -1, H * P * es, hs), "bwd: dX order");
     if (dinitial_state)
