@@ -146,6 +146,9 @@ __global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(2
 
     if (wave == SW) {
         // ======== X wave: copies of X and a two blocks ahead, stage 1 one block ahead ========
+        // (issue priority over the state wave sharing its SIMD: its copies and
+        // stage 1 gate the next block)
+        __builtin_amdgcn_s_setprio(2);
         // Copy k of unit j fills the 16-byte LDS slots 64k + lane of the unit's
         // tile: row (64k + lane) / 4, stored piece lane % 4, which holds the
         // row's logical piece (lane % 4) ^ swzbits<4>(row).
@@ -320,6 +323,7 @@ __global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(2
     }
 
     if (wave == SW + 1) {
+        __builtin_amdgcn_s_setprio(2);
         // ======== score wave: B and C of the next block, and its scores ========
         // Copy k of sub-tile nt fills the 16-byte slots 64k + lane: row
         // 16k + lane/4, stored piece lane % 4, which holds logical piece
