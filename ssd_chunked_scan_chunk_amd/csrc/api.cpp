@@ -825,14 +825,14 @@ ssd_status ssd_chunk_scan_bwd(const ssd_fwd_desc* desc, const void* X, const flo
         ssd::FwdShape sc = s;
         sc.H = H * ns; sc.P = 64; sc.N = P; sc.G = H;
         ssd::StateSrc srcc{initial_state, H * PN, F(W_SFW), nc * H * PN, H * PN};
-        SSD_TRY(ssd::launch_mfma_out_xg(sc, G, B, a, X, dY, srcc, V(W_DCH), hs), "bwd: dC pass");
-        SSD_TRY(ssd::launch_group_sum(dC, V(W_DCH), Bz, L, L, 0, 1, H, G, N, false, true, hs), "bwd: dC group sum");
-        ssd::FwdShape sb = sc;
-        sb.L = Lp;
-        SSD_TRY(ssd::launch_remap_rows(V(W_XR), X, Bz, Lp, L, Lp - 1, -1, H * P * es, hs), "bwd: reverse X");
         ssd::StateSrc srcb{dfinal_state, H * PN, F(W_SREV), nc * H * PN, H * PN};
-        SSD_TRY(ssd::launch_mfma_out_xg(sb, G, V(W_CR), F(W_AR), V(W_DYR), V(W_XR), srcb, V(W_DBH), hs),
-                "bwd: dB pass");
+        SSD_TRY(ssd::launch_remap_rows(V(W_XR), X, Bz, Lp, L, Lp - 1, -1, H * P * es, hs), "bwd: reverse X");
+        // dC on forward time (B as X, x as B, dy as C); dB on reversed time
+        // (C as X, dy as B, x as C): one launch
+        const ssd::XgPass pc{B, a, X, dY, srcc, F(W_DCH), L};
+        const ssd::XgPass pb{V(W_CR), F(W_AR), V(W_DYR), V(W_XR), srcb, F(W_DBH), Lp};
+        SSD_TRY(ssd::launch_mfma_out_xg_pair(sc, G, pc, pb, hs), "bwd: dC and dB passes");
+        SSD_TRY(ssd::launch_group_sum(dC, V(W_DCH), Bz, L, L, 0, 1, H, G, N, false, true, hs), "bwd: dC group sum");
         SSD_TRY(ssd::launch_group_sum(dB, V(W_DBH), Bz, L, Lp, Lp - 1, -1, H, G, N, false, true, hs), "bwd: dB group sum");
         return ok();
     }

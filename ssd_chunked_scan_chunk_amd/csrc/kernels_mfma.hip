@@ -119,12 +119,15 @@ struct MfmaCfg {
 // workgroup's heads, which share one decay) as bf16 high and low parts, and
 // stage 5 multiplies the state's high and low parts.  SW is the number of
 // state waves (the workgroup has SW + 2 wavefronts).
-template <int P, int N, bool FULL, bool XG = false, int SW = kStateWaves>
-__global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(SW == kStateWaves ? 2 : 3))) void k_mfma_seg(
+// The body of one workgroup; wg is its index among the nwg workgroups of
+// its launch (or of its half of a paired launch).
+template <int P, int N, bool FULL, bool XG, int SW>
+__device__ __forceinline__ void mfma_seg_body(
     const u16* __restrict__ X, const float* __restrict__ a, const u16* __restrict__ B,
     const u16* __restrict__ C, StateSrc src, u16* __restrict__ Y, float* __restrict__ S_fin,
     float* __restrict__ Sseg, float* __restrict__ lamseg, int64_t nseg_total, int64_t L,
-    int H, int G, int64_t blocks_per_seg, int nseg_grid, int Bz, int x_groups)
+    int H, int G, int64_t blocks_per_seg, int nseg_grid, int Bz, int x_groups, unsigned wg,
+    unsigned nwg)
 {
     using Cfg = MfmaCfg<P, N, SW>;
     constexpr int HW = Cfg::HW, NTL = Cfg::NTL, XPR = Cfg::XPR, BPR = Cfg::BPR;
@@ -147,8 +150,8 @@ __global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(S
     const int HPG = H / G;
     const int HQ = (HPG + HW - 1) / HW;
     const int64_t items = (int64_t)Bz * nseg_grid * G * HQ;
-    const int64_t per_xcd = gridDim.x / kXcds;
-    const int64_t item = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+    const int64_t per_xcd = nwg / kXcds;
+    const int64_t item = (int64_t)(wg % kXcds) * per_xcd + wg / kXcds;
     if (item >= items) return;
     const int hq = (int)(item % HQ);
     const int grp = (int)((item / HQ) % G);
@@ -744,6 +747,36 @@ __global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(S
     }
 }
 
+template <int P, int N, bool FULL, bool XG = false, int SW = kStateWaves>
+__global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(SW == kStateWaves ? 2 : 3))) void k_mfma_seg(
+    const u16* __restrict__ X, const float* __restrict__ a, const u16* __restrict__ B,
+    const u16* __restrict__ C, StateSrc src, u16* __restrict__ Y, float* __restrict__ S_fin,
+    float* __restrict__ Sseg, float* __restrict__ lamseg, int64_t nseg_total, int64_t L,
+    int H, int G, int64_t blocks_per_seg, int nseg_grid, int Bz, int x_groups)
+{
+    mfma_seg_body<P, N, FULL, XG, SW>(X, a, B, C, src, Y, S_fin, Sseg, lamseg, nseg_total, L, H, G,
+                                      blocks_per_seg, nseg_grid, Bz, x_groups, blockIdx.x, gridDim.x);
+}
+
+// Two exchanged-dimension products in one launch (the backward's dC and dB
+// passes): workgroups [0, grid0) run the first, the rest the second.  Both
+// share every size but the sequence length; grid0 is a multiple of the XCD
+// count, so a workgroup's XCD is the same in either numbering.
+template <int SW>
+__global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(3))) void k_mfma_xg_pair(
+    XgPass p0, XgPass p1, unsigned grid0, int H, int G, int64_t blocks_per_seg, int nseg_grid, int Bz,
+    int x_groups)
+{
+    const bool second = blockIdx.x >= grid0;
+    const XgPass& p = second ? p1 : p0;
+    const unsigned wg = second ? blockIdx.x - grid0 : blockIdx.x;
+    const unsigned nwg = second ? gridDim.x - grid0 : grid0;
+    mfma_seg_body<64, 64, true, true, SW>(static_cast<const u16*>(p.X), p.a, static_cast<const u16*>(p.B),
+                                          static_cast<const u16*>(p.C), p.src, reinterpret_cast<u16*>(p.Y),
+                                          nullptr, nullptr, nullptr, 0, p.L, H, G, blocks_per_seg, nseg_grid,
+                                          Bz, x_groups, wg, nwg);
+}
+
 #define SSD_MFMA_DISPATCH(MACRO)                     \
     if (s.P == 64 && s.N == 128) MACRO(64, 128)      \
     else if (s.P == 64 && s.N == 64) MACRO(64, 64)   \
@@ -777,36 +810,19 @@ hipError_t launch_mfma_state(const FwdShape& s, int64_t seg_chunks, int64_t nseg
     return hipGetLastError();
 }
 
-hipError_t launch_mfma_out(const FwdShape& s, int64_t seg_chunks, int64_t nseg,
-                           const void* X, const float* a, const void* B, const void* C,
-                           StateSrc src, void* Y, float* S_fin, hipStream_t st)
-{
-    const dim3 grid(grid_for(s, nseg));
-    const int64_t bps = seg_chunks * (s.Q / kT);
-#define SSD_LAUNCH_OUT(PP, NN)                                                                \
-    hipLaunchKernelGGL((k_mfma_seg<PP, NN, true>), grid, dim3(kThreads), 0, st,              \
-                       (const u16*)X, a, (const u16*)B, (const u16*)C, src, (u16*)Y, S_fin, \
-                       (float*)nullptr, (float*)nullptr, (int64_t)0, s.L, (int)s.H,          \
-                       (int)s.G, bps, (int)nseg, (int)s.Bz, 0);
-    SSD_MFMA_DISPATCH(SSD_LAUNCH_OUT)
-#undef SSD_LAUNCH_OUT
-    return hipGetLastError();
-}
-
-hipError_t launch_mfma_out_xg(const FwdShape& s, int64_t x_groups, const void* X, const float* a,
-                              const void* B, const void* C, StateSrc src, void* Y, hipStream_t st)
+hipError_t launch_mfma_out_xg_pair(const FwdShape& s, int64_t x_groups, const XgPass& p0, const XgPass& p1,
+                                   hipStream_t st)
 {
     if (!(s.P == 64 && s.N == 64) || x_groups < 1 || s.G % x_groups != 0) return hipErrorInvalidValue;
+    if ((p0.L + s.Q - 1) / s.Q != s.nc || (p1.L + s.Q - 1) / s.Q != s.nc) return hipErrorInvalidValue;
     // four state waves: two sub-heads of 64 per workgroup (a group has H/G of them)
     constexpr int kSW = 4;
     const int64_t hq = (s.H / s.G + kSW / 2 - 1) / (kSW / 2);
     const int64_t items = s.Bz * s.nc * s.G * hq;
-    const dim3 grid((unsigned)(((items + kXcds - 1) / kXcds) * kXcds));
+    const unsigned grid0 = (unsigned)(((items + kXcds - 1) / kXcds) * kXcds);
     const int64_t bps = s.Q / kT;
-    hipLaunchKernelGGL((k_mfma_seg<64, 64, true, true, kSW>), grid, dim3(64 * (kSW + 2)), 0, st,
-                       (const u16*)X, a, (const u16*)B, (const u16*)C, src, (u16*)Y, (float*)nullptr,
-                       (float*)nullptr, (float*)nullptr, (int64_t)0, s.L, (int)s.H, (int)s.G, bps,
-                       (int)s.nc, (int)s.Bz, (int)x_groups);
+    hipLaunchKernelGGL((k_mfma_xg_pair<kSW>), dim3(2 * grid0), dim3(64 * (kSW + 2)), 0, st, p0, p1, grid0,
+                       (int)s.H, (int)s.G, bps, (int)s.nc, (int)s.Bz, (int)x_groups);
     return hipGetLastError();
 }
 

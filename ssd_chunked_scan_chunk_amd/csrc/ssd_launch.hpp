@@ -61,12 +61,6 @@ int64_t mfma_heads_per_workgroup(int64_t P, int64_t N);
 hipError_t launch_mfma_state(const FwdShape& s, int64_t seg_chunks, int64_t nseg_run,
                              int64_t nseg_total, const void* X, const float* a,
                              const void* B, float* Sseg, float* lamseg, hipStream_t st);
-// Pass C: for every segment, starting from its entering state, write Y and
-// (last segment) the final state.
-hipError_t launch_mfma_out(const FwdShape& s, int64_t seg_chunks, int64_t nseg,
-                           const void* X, const float* a, const void* B, const void* C,
-                           StateSrc src, void* Y, float* S_fin, hipStream_t st);
-
 // The fused forward pass (kernels_fwd.hip): sw (4, 5 or 6) units -- 32-wide
 // head-dim slices of heads -- per workgroup, for every segment starting from
 // its entering state; writes Y and (last segment) the final state.
@@ -77,13 +71,23 @@ int64_t fwd_workgroups(const FwdShape& s, int64_t nseg, int sw);
 bool fwd_units_supported(int64_t P, int sw);
 
 // The backward's exchanged-dimension products (headdim 64, state 64, one chunk
-// per segment): X [Bz][L][x_groups][(H/G)*64] bf16 shared by the H/G heads of
-// a group (head hl reads columns hl*64 ..), a [Bz][L][G] (one decay per group),
-// and the entering state of segment s read transposed from the [64][(H/G)*64]
-// state of group grp in src (segment 0 from src.first, s >= 1 from src.Sin).
-// Y is fp32 [Bz][L][H][64].
-hipError_t launch_mfma_out_xg(const FwdShape& s, int64_t x_groups, const void* X, const float* a,
-                              const void* B, const void* C, StateSrc src, void* Y, hipStream_t st);
+// per segment), two in one launch that share every size in s but the sequence
+// length (p0.L, p1.L; each must have s.nc chunks): X [Bz][L][x_groups][(H/G)*64]
+// bf16 shared by the H/G heads of a group (head hl reads columns hl*64 ..), a
+// [Bz][L][G] (one decay per group), and the entering state of segment s read
+// transposed from the [64][(H/G)*64] state of group grp in src (segment 0 from
+// src.first, s >= 1 from src.Sin).  Y is fp32 [Bz][L][H][64].
+struct XgPass {
+    const void* X;
+    const float* a;
+    const void* B;
+    const void* C;
+    StateSrc src;
+    float* Y;
+    int64_t L;
+};
+hipError_t launch_mfma_out_xg_pair(const FwdShape& s, int64_t x_groups, const XgPass& p0, const XgPass& p1,
+                                   hipStream_t st);
 
 // ---- decode step ---------------------------------------------------------------------
 hipError_t launch_step(int64_t Bz, int64_t H, int64_t P, int64_t N, int64_t G, bool bf16,
