@@ -596,166 +596,144 @@ __global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(2
                         *reinterpret_cast<u32x4*>(yblk + (yoff + (uint32_t)(16 * k * H * P))) = Yr[k];
             }
         };
-        if (fast) {
-            // ================= fast form, software-pipelined =================
-            // Operand reads are issued a group ahead of the MFMAs that consume
-            // them, with scheduling fences so that the compiler keeps them
-            // there: one state tile of C ahead in stage 5, stage 2's operands
-            // during stage 5's last tiles, one quarter of B^T ahead in stage 3.
-            u32x4 cf[2][2][2];          // C fragments, two state tiles
-            load_c(0, cf[0]);
-            if (fold[0]) {              // the block's re-based scale, before stage 5
+        // ================= one instruction stream for both forms =================
+        // Operand reads are issued a group ahead of the MFMAs that consume
+        // them, with scheduling fences so that the compiler keeps them there:
+        // one state tile of C ahead in stage 5, stage 2's operands during
+        // stage 5's last tiles, one quarter of B^T ahead in stage 3.  A block
+        // in the direct form (a quarter's log2-decay spread too wide for any
+        // power-of-two scale) runs the same products on other operands and
+        // scales: stage 5's output and the state are scaled after stage 5
+        // (Sacc' = 2^(ld + Lam2) Sacc + B^T (w o X)), and stage 2 multiplies
+        // the unweighted X by the per-element decayed scores.  Keeping one
+        // stream (the form only picks operands and in-place scalings) keeps
+        // the state in one register range; two separate forms made the
+        // compiler move all 64 state registers out and back every block.
+        u32x4 cf[2][2][2];          // C fragments, two state tiles
+        load_c(0, cf[0]);
+        if (fold[0]) {              // the block's re-based scale, before stage 5 (fast form)
 #pragma unroll
-                for (int nt = 0; nt < NTL; ++nt) scale_pow2(Sacc[nt], rq[0]);
+            for (int nt = 0; nt < NTL; ++nt) scale_pow2(Sacc[nt], rq[0]);
+        }
+        i16x4 xr[4][2];             // X^T fragments (J, ks) = (0,0), (0,1), (1,0), (1,1)
+        float4 wv[4][2];            // their steps' state weights
+        u32x4 pt[6];                // score tiles as stage 2's B operands
+        float csr[2];               // output exponents of rows l32 and 32 + l32
+        bf16x8 xk[4];               // X~ fragments
+        // ---- stage 5: Y^T = Sacc C^T ----
+#pragma unroll
+        for (int nt = 0; nt < NTL; ++nt) {
+            if (nt + 1 < NTL) load_c(nt + 1, cf[(nt + 1) & 1]);
+            if (nt == NTL - 2 || NTL == 1) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) load_x(i, xr[i]);
+                load_w(0, wv[0]);
+                load_w(1, wv[1]);
             }
-            i16x4 xr[4][2];             // X^T fragments (J, ks) = (0,0), (0,1), (1,0), (1,1)
-            float4 wv[4][2];            // their steps' state weights
-            u32x4 pt[6];                // score tiles as stage 2's B operands
-            float csr[2];               // output exponents of rows l32 and 32 + l32
-            bf16x8 xk[4];               // X~ fragments
-            // ---- stage 5: Y^T = Sacc C^T ----
-#pragma unroll
-            for (int nt = 0; nt < NTL; ++nt) {
-                if (nt + 1 < NTL) load_c(nt + 1, cf[(nt + 1) & 1]);
-                if (nt == NTL - 2 || NTL == 1) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) load_x(i, xr[i]);
-                    load_w(0, wv[0]);
-                    load_w(1, wv[1]);
-                }
-                if (nt == NTL - 1) {
-                    load_w(2, wv[2]);
-                    load_w(3, wv[3]);
-                    pt[0] = load_p(0);
-                    pt[1] = load_p(1);
-                    csr[0] = sCs[bs][hw][l32];
-                    csr[1] = sCs[bs][hw][32 + l32];
-                }
-                fence();
-#pragma unroll
-                for (int hf = 0; hf < 2; ++hf) {
-                    const bf16x8 Sf = acc_half(Sacc[nt], hf);
-#pragma unroll
-                    for (int I = 0; I < 2; ++I) Yt[I] = mfma32(Sf, as_bf16x8(cf[nt & 1][hf][I]), Yt[I]);
-                }
-                if (nt == NTL - 1) {
-                    xk[0] = weigh(xr[0], wv[0]);
-                    xk[1] = weigh(xr[1], wv[1]);
-                }
-                fence();
+            if (nt == NTL - 1) {
+                load_w(2, wv[2]);
+                load_w(3, wv[3]);
+                pt[0] = load_p(0);
+                pt[1] = load_p(1);
+                csr[0] = sCs[bs][hw][l32];
+                csr[1] = sCs[bs][hw][32 + l32];
             }
+            fence();
 #pragma unroll
-            for (int i = 2; i < 6; ++i) pt[i] = load_p(i);
-            xk[2] = weigh(xr[2], wv[2]);
-            xk[3] = weigh(xr[3], wv[3]);
-            bf16x8 bt[2][NTL];          // B^T fragments, two quarters
-            load_bt(0, bt[0]);
-            // ---- stages 2, 3 and 4, quarter by quarter, interleaved (the two
-            // stages are independent: stage 3 updates the state, stage 2 the
-            // output).  Stage 3: Sacc' = Sacc + B^T X~, with the state moved to
-            // a re-based quarter's reference before its products.  Stage 2:
-            // Y^T += X~^T P; at a re-based quarter the rows from that quarter
-            // on move to its reference after the products before it. ----
-            const bool upper = l32 >= 16;
+            for (int hf = 0; hf < 2; ++hf) {
+                const bf16x8 Sf = acc_half(Sacc[nt], hf);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                if (q + 1 < 4) load_bt(q + 1, bt[(q + 1) & 1]);
-                fence();
-                if (q > 0 && fold[q]) {
-#pragma unroll
-                    for (int nt = 0; nt < NTL; ++nt) scale_pow2(Sacc[nt], rq[q]);
-                }
-#pragma unroll
-                for (int nt = 0; nt < NTL; ++nt)
-                    Sacc[nt] = mfma32(bt[q & 1][nt], xk[q], Sacc[nt]);
-                if (q < 2) {
-                    Yt[0] = mfma32(xk[q], as_bf16x8(pt[2 * q]), Yt[0]);
-                    Yt[1] = mfma32(xk[q], as_bf16x8(pt[2 * q + 1]), Yt[1]);
-                } else {
-                    Yt[1] = mfma32(xk[q], as_bf16x8(pt[2 + q]), Yt[1]);
-                }
-                if (q == 0 && fold[1]) {
-                    scale_pow2(Yt[0], upper ? rq[1] : 0);
-                    scale_pow2(Yt[1], rq[1]);
-                }
-                if (q == 1 && fold[2]) scale_pow2(Yt[1], rq[2]);
-                if (q == 2 && fold[3]) scale_pow2(Yt[1], upper ? rq[3] : 0);
-                fence();
+                for (int I = 0; I < 2; ++I) Yt[I] = mfma32(Sf, as_bf16x8(cf[nt & 1][hf][I]), Yt[I]);
             }
-            Yt[0] *= fast_exp2(csr[0]);
-            Yt[1] *= fast_exp2(csr[1]);
-            pack_y();
-            store_y();
-            pin_state();
-        } else {
-            // ================= direct form (rare), plain order =================
-            // A quarter's log2-decay spread too wide for any power-of-two
-            // scale: per-element decay of the shared scores, then
-            // Sacc' = 2^(ld + Lam2) Sacc + B^T (w o X).
-#pragma unroll
-            for (int nt = 0; nt < NTL; ++nt) {
-                u32x4 cf[2][2];
-                load_c(nt, cf);
-#pragma unroll
-                for (int hf = 0; hf < 2; ++hf) {
-                    const bf16x8 Sf = acc_half(Sacc[nt], hf);
-#pragma unroll
-                    for (int I = 0; I < 2; ++I) Yt[I] = mfma32(Sf, as_bf16x8(cf[hf][I]), Yt[I]);
-                }
+            if (nt == NTL - 1) {
+                xk[0] = weigh(xr[0], wv[0]);
+                xk[1] = weigh(xr[1], wv[1]);
             }
-            const float csi0 = sCs[bs][hw][l32], csi1 = sCs[bs][hw][32 + l32];
-            Yt[0] *= fast_exp2(csi0 + ld_in);
-            Yt[1] *= fast_exp2(csi1 + ld_in);
-            // decay 2^(cs2_i - cs2_j) on the shared scores (masked entries
-            // stay zero: their exponent may overflow)
-            auto decayed = [&](int t, int J, int ks, float csi) {
-                const u32x4 uu = load_p(t == 2 ? 4 + ks : 2 * ks + t);
-                const int jl = 16 * ks + 8 * g2;
-                const f32x4 c0 = *reinterpret_cast<const f32x4*>(&sCs[bs][hw][32 * J + jl]);
-                const f32x4 c1 = *reinterpret_cast<const f32x4*>(&sCs[bs][hw][32 * J + jl + 4]);
+            fence();
+        }
+#pragma unroll
+        for (int i = 2; i < 6; ++i) pt[i] = load_p(i);
+        xk[2] = weigh(xr[2], wv[2]);
+        xk[3] = weigh(xr[3], wv[3]);
+        bf16x8 bt[2][NTL];          // B^T fragments, two quarters
+        load_bt(0, bt[0]);
+        if (!fast) {
+            // direct form: stage 5's output at the block's entering scale,
+            // the state moved to the block's end, and the scores decayed per
+            // element by 2^(cs2_i - cs2_j) (masked entries stay zero: their
+            // exponent may overflow).  Score tile i is (t, ks) = (0,0) (1,0)
+            // (0,1) (1,1) (2,0) (2,1); tile t covers rows 32 (t > 0) .. and
+            // columns 32 (t == 2) ..
+            Yt[0] *= fast_exp2(csr[0] + ld_in);
+            Yt[1] *= fast_exp2(csr[1] + ld_in);
+            const float f = fast_exp2(ld_in + lam2);
+#pragma unroll
+            for (int nt = 0; nt < NTL; ++nt) Sacc[nt] *= f;
+#pragma unroll
+            for (int i = 0; i < 6; ++i) {
+                const int t = i < 4 ? (i & 1) : 2, ks = i < 4 ? (i >> 1) : (i & 1);
+                const float csi = t == 0 ? csr[0] : csr[1];
+                const int jl = 32 * (t == 2) + 16 * ks + 8 * g2;
+                const f32x4 c0 = *reinterpret_cast<const f32x4*>(&sCs[bs][hw][jl]);
+                const f32x4 c1 = *reinterpret_cast<const f32x4*>(&sCs[bs][hw][jl + 4]);
                 const float cj[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
                 const bool diag = t != 1;
                 float v[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const int j = jl + e;
-                    const float x = __uint_as_float(e & 1 ? (uu[e >> 1] & 0xffff0000u) : (uu[e >> 1] << 16));
+                    const int j = 16 * ks + 8 * g2 + e;
+                    const float x = __uint_as_float(e & 1 ? (pt[i][e >> 1] & 0xffff0000u) : (pt[i][e >> 1] << 16));
                     v[e] = (!diag || j <= l32) ? x * fast_exp2(csi - cj[e]) : 0.f;
                 }
-                return as_bf16x8(u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])});
-            };
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                i16x4 x0[2], x1[2];
-                load_x(ks, x0);
-                load_x(2 + ks, x1);
-                const bf16x8 xa0 = join8(x0[0], x0[1]);
-                Yt[0] = mfma32(xa0, decayed(0, 0, ks, csi0), Yt[0]);
-                fence();
-                Yt[1] = mfma32(xa0, decayed(1, 0, ks, csi1), Yt[1]);
-                fence();
-                Yt[1] = mfma32(join8(x1[0], x1[1]), decayed(2, 1, ks, csi1), Yt[1]);
-                fence();
+                pt[i] = u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])};
             }
-            pack_y();
-            const float f = fast_exp2(ld_in + lam2);
-#pragma unroll
-            for (int nt = 0; nt < NTL; ++nt) Sacc[nt] *= f;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                i16x4 x[2];
-                float4 w[2];
-                load_x(q, x);
-                load_w(q, w);
-                const bf16x8 xw = weigh(x, w);
-                bf16x8 bq[NTL];
-                load_bt(q, bq);
-#pragma unroll
-                for (int nt = 0; nt < NTL; ++nt) Sacc[nt] = mfma32(bq[nt], xw, Sacc[nt]);
-            }
-            store_y();
-            pin_state();
         }
+        // ---- stages 2, 3 and 4, quarter by quarter, interleaved (the two
+        // stages are independent: stage 3 updates the state, stage 2 the
+        // output).  Stage 3: Sacc' = Sacc + B^T X~, with the state moved to
+        // a re-based quarter's reference before its products.  Stage 2:
+        // Y^T += X~^T P (direct form: X^T P~); at a re-based quarter the rows
+        // from that quarter on move to its reference after the products
+        // before it. ----
+        const bool upper = l32 >= 16;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (q + 1 < 4) load_bt(q + 1, bt[(q + 1) & 1]);
+            fence();
+            if (q > 0 && fold[q]) {
+#pragma unroll
+                for (int nt = 0; nt < NTL; ++nt) scale_pow2(Sacc[nt], rq[q]);
+            }
+#pragma unroll
+            for (int nt = 0; nt < NTL; ++nt)
+                Sacc[nt] = mfma32(bt[q & 1][nt], xk[q], Sacc[nt]);
+            bf16x8 xa = xk[q];      // stage 2's X operand (direct form: X itself, read again)
+            if (!fast) {
+                i16x4 xu[2];
+                load_x(q, xu);
+                xa = join8(xu[0], xu[1]);
+            }
+            if (q < 2) {
+                Yt[0] = mfma32(xa, as_bf16x8(pt[2 * q]), Yt[0]);
+                Yt[1] = mfma32(xa, as_bf16x8(pt[2 * q + 1]), Yt[1]);
+            } else {
+                Yt[1] = mfma32(xa, as_bf16x8(pt[2 + q]), Yt[1]);
+            }
+            if (q == 0 && fold[1]) {
+                scale_pow2(Yt[0], upper ? rq[1] : 0);
+                scale_pow2(Yt[1], rq[1]);
+            }
+            if (q == 1 && fold[2]) scale_pow2(Yt[1], rq[2]);
+            if (q == 2 && fold[3]) scale_pow2(Yt[1], upper ? rq[3] : 0);
+            fence();
+        }
+        if (fast) {
+            Yt[0] *= fast_exp2(csr[0]);
+            Yt[1] *= fast_exp2(csr[1]);
+        }
+        pack_y();
+        store_y();
+        pin_state();
     }
 
     // ---- epilogue: final state (last segment) ----
