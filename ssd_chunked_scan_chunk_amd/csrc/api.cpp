@@ -763,6 +763,14 @@ ssd_status ssd_chunk_scan_bwd(const ssd_fwd_desc* desc, const void* X, const flo
         e = (expr);                                          \
         if (e != hipSuccess) return hip_fail(e, what);       \
     } while (0)
+    // The bf16 plan reads the time-reversed problem in place when the sequence
+    // is whole chunks (no padding) and the exchanged-dimension products run on
+    // the MFMA kernel; otherwise its operands are copied out reversed.
+    const bool rin = !bp.f32 && bp.xg && Lp == L && L % 64 == 0;
+    const void* dYr = rin ? dY : V(W_DYR);
+    const void* Cr = rin ? C : V(W_CR);
+    const void* Br = rin ? B : V(W_BR);
+    const float* ar = rin ? a : F(W_AR);
     if (bp.f32) {
         // fp32: the VALU forward gives the chunk states (and, on the reversed
         // problem, dX, G_0 and the adjoint's chunk states in one pass); the
@@ -786,18 +794,22 @@ ssd_status ssd_chunk_scan_bwd(const ssd_fwd_desc* desc, const void* X, const flo
     SSD_TRY(ssd::launch_state_scan(s, nc - 1, nc, F(W_SFW), F(W_LAMFW), H * nc, nc, initial_state,
                                    F(W_SFW), 0, F(W_SFW) + (nc - 1) * H * PN, nc * H * PN, hs),
             "bwd: state scan");
-    // 2. the adjoint recurrence runs backwards in time: reverse the sequence
+    // 2. the adjoint recurrence runs backwards in time: the reversed sequence
     // (padded at its start to whole chunks, so that reversed chunks coincide
     // with forward ones), with the decay of reversed step t' = a at forward
-    // step Lp - t' (zero where that is past the end)
-    SSD_TRY(ssd::launch_remap_rows(V(W_DYR), dY, Bz, Lp, L, Lp - 1, -1, H * P * es, hs), "bwd: reverse dY");
-    SSD_TRY(ssd::launch_remap_rows(V(W_CR), C, Bz, Lp, L, Lp - 1, -1, G * N * es, hs), "bwd: reverse C");
-    SSD_TRY(ssd::launch_remap_rows(V(W_BR), B, Bz, Lp, L, Lp - 1, -1, G * N * es, hs), "bwd: reverse B");
-    SSD_TRY(ssd::launch_remap_a(F(W_AR), a, Bz, Lp, L, Lp, -1, H, 1, hs), "bwd: reverse a");
+    // step Lp - t' (zero where that is past the end).  A sequence of whole
+    // chunks needs no padding, and the kernels read (and write) the reversed
+    // problem in place; otherwise it is copied out reversed.
+    if (!rin) {
+        SSD_TRY(ssd::launch_remap_rows(V(W_DYR), dY, Bz, Lp, L, Lp - 1, -1, H * P * es, hs), "bwd: reverse dY");
+        SSD_TRY(ssd::launch_remap_rows(V(W_CR), C, Bz, Lp, L, Lp - 1, -1, G * N * es, hs), "bwd: reverse C");
+        SSD_TRY(ssd::launch_remap_rows(V(W_BR), B, Bz, Lp, L, Lp - 1, -1, G * N * es, hs), "bwd: reverse B");
+        SSD_TRY(ssd::launch_remap_a(F(W_AR), a, Bz, Lp, L, Lp, -1, H, 1, hs), "bwd: reverse a");
+    }
     // 3. dX = G B, with G the state of the reversed problem (dy as X, C as B,
     // B as C, dS_fin as its initial state); its final state is G_0
-    SSD_TRY(ssd::launch_mfma_state(bp.sr, 1, nc - 1, nc, V(W_DYR), F(W_AR), V(W_CR), F(W_SREV),
-                                   F(W_LAMREV), hs), "bwd: adjoint chunk states");
+    SSD_TRY(ssd::launch_mfma_state(bp.sr, 1, nc - 1, nc, dYr, ar, Cr, F(W_SREV), F(W_LAMREV), hs, rin),
+            "bwd: adjoint chunk states");
     SSD_TRY(ssd::launch_state_scan(bp.sr, nc - 1, nc, F(W_SREV), F(W_LAMREV), H * nc, nc, dfinal_state,
                                    F(W_SREV), 0, F(W_SREV) + (nc - 1) * H * PN, nc * H * PN, hs),
             "bwd: adjoint state scan");
@@ -807,10 +819,11 @@ ssd_status ssd_chunk_scan_bwd(const ssd_fwd_desc* desc, const void* X, const flo
         int64_t k1 = 1;
         int sw1 = 4;
         auto_plan(bp.sr, 1, 0, SIZE_MAX, &k1, &sw1);
-        SSD_TRY(ssd::launch_fwd(bp.sr, sw1, 1, nc, V(W_DYR), F(W_AR), V(W_CR), V(W_BR), src, V(W_DXR),
-                                dinitial_state, hs), "bwd: dX pass");
+        SSD_TRY(ssd::launch_fwd(bp.sr, sw1, 1, nc, dYr, ar, Cr, Br, src, rin ? dX : V(W_DXR), dinitial_state,
+                                hs, rin), "bwd: dX pass");
     }
-    SSD_TRY(ssd::launch_remap_rows(dX, V(W_DXR), Bz, L, Lp, Lp - 1, -1, H * P * es, hs), "bwd: dX order");
+    if (!rin)
+        SSD_TRY(ssd::launch_remap_rows(dX, V(W_DXR), Bz, L, Lp, Lp - 1, -1, H * P * es, hs), "bwd: dX order");
     if (dinitial_state)
         SSD_TRY(ssd::launch_scale_state_by_a0(dinitial_state, a, Bz, L, H, PN, hs), "bwd: dS0");
     // 4. da from the chunk-local four-term form
@@ -826,14 +839,20 @@ ssd_status ssd_chunk_scan_bwd(const ssd_fwd_desc* desc, const void* X, const flo
         sc.H = H * ns; sc.P = 64; sc.N = P; sc.G = H;
         ssd::StateSrc srcc{initial_state, H * PN, F(W_SFW), nc * H * PN, H * PN};
         ssd::StateSrc srcb{dfinal_state, H * PN, F(W_SREV), nc * H * PN, H * PN};
-        SSD_TRY(ssd::launch_remap_rows(V(W_XR), X, Bz, Lp, L, Lp - 1, -1, H * P * es, hs), "bwd: reverse X");
+        if (!rin)
+            SSD_TRY(ssd::launch_remap_rows(V(W_XR), X, Bz, Lp, L, Lp - 1, -1, H * P * es, hs), "bwd: reverse X");
         // dC on forward time (B as X, x as B, dy as C); dB on reversed time
-        // (C as X, dy as B, x as C): one launch
-        const ssd::XgPass pc{B, a, X, dY, srcc, F(W_DCH), L};
-        const ssd::XgPass pb{V(W_CR), F(W_AR), V(W_DYR), V(W_XR), srcb, F(W_DBH), Lp};
+        // (C as X, dy as B, x as C): one launch.  Read in place, the reversed
+        // problem also writes its per-head dB in forward order.
+        const ssd::XgPass pc{B, a, X, dY, srcc, F(W_DCH), L, 0};
+        const ssd::XgPass pb{Cr, ar, dYr, rin ? X : V(W_XR), srcb, F(W_DBH), Lp, rin ? 1 : 0};
         SSD_TRY(ssd::launch_mfma_out_xg_pair(sc, G, pc, pb, hs), "bwd: dC and dB passes");
         SSD_TRY(ssd::launch_group_sum(dC, V(W_DCH), Bz, L, L, 0, 1, H, G, N, false, true, hs), "bwd: dC group sum");
-        SSD_TRY(ssd::launch_group_sum(dB, V(W_DBH), Bz, L, Lp, Lp - 1, -1, H, G, N, false, true, hs), "bwd: dB group sum");
+        if (rin)
+            SSD_TRY(ssd::launch_group_sum(dB, V(W_DBH), Bz, L, L, 0, 1, H, G, N, false, true, hs), "bwd: dB group sum");
+        else
+            SSD_TRY(ssd::launch_group_sum(dB, V(W_DBH), Bz, L, Lp, Lp - 1, -1, H, G, N, false, true, hs),
+                    "bwd: dB group sum");
         return ok();
     }
     // 5. dC = S^T dy: forward-time product, state dimensions exchanged

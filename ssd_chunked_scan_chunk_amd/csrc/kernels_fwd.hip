@@ -67,7 +67,7 @@ struct FwdCfg {
     static_assert(P % 32 == 0 && N % 32 == 0 && SW >= 2 && NW <= 8, "shape");
 };
 
-template <int P, int N, int SW>
+template <int P, int N, int SW, bool REV = false>
 __global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(2))) void k_fwd(
     const u16* __restrict__ X, const float* __restrict__ a, const u16* __restrict__ B,
     const u16* __restrict__ C, StateSrc src, u16* __restrict__ Y, float* __restrict__ S_fin,
@@ -121,6 +121,15 @@ __global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(2
         const int64_t last = L - 1 - c * kT;
         return (int)(last < kT - 1 ? last : kT - 1);
     };
+    // Time order of the sequence arrays.  REV: step t of the problem is step
+    // L - 1 - t of X, B, C and Y, and its decay is a at step L - t (none at
+    // t = 0), the time-reversed problem of the backward read in place (L a
+    // multiple of the block: block c is the memory block L/kT - 1 - c, rows
+    // reversed).  row_base: first memory row of block c; row_loc: memory row
+    // of the block's step r relative to it.
+    constexpr bool rev = REV;
+    auto row_base = [&](int64_t c) -> int64_t { return rev ? L - kT * (c + 1) : c * kT; };
+    auto row_loc = [&](unsigned r) -> unsigned { return rev ? (unsigned)(kT - 1) - r : r; };
 
     // Decay scales (as in the segmented kernel).  The true state is 2^ld *
     // Sacc.  In a block whose log2-decays stay within range of the state
@@ -154,7 +163,7 @@ __global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(2
         // row's logical piece (lane % 4) ^ swzbits<4>(row).
         auto copy_x = [&](int64_t c, int xs) {
             const unsigned lc = (unsigned)block_last(c);
-            const u16* Xg = X + ((int64_t)b * L + c * kT) * H * P;
+            const u16* Xg = X + ((int64_t)b * L + row_base(c)) * H * P;
 #pragma unroll
             for (int k = 0; k < XOPS; ++k) {
                 const int j = k / (kT * XPU / 64);             // unit (uniform)
@@ -164,7 +173,7 @@ __global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(2
                 const unsigned r = (unsigned)(kk * 64 + lane) / XPU;
                 const unsigned q = ((unsigned)lane % XPU) ^ (unsigned)swzbits<XPU>((int)r);
                 const unsigned tr = r <= lc ? r : lc;
-                dma16(Xg, ((tr * (unsigned)H + (unsigned)hj) * P + pj + q * 8) * 2u,
+                dma16(Xg, ((row_loc(tr) * (unsigned)H + (unsigned)hj) * P + pj + q * 8) * 2u,
                       lds_addr(&sX[xs][j][0]) + (uint32_t)(kk * 64 * 16));
             }
         };
@@ -172,12 +181,16 @@ __global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(2
         // that the wait counts below are constants
         auto copy_a = [&](int64_t c, int as) {
             const unsigned lc = (unsigned)block_last(c);
-            const float* ag = a + ((int64_t)b * L + c * kT) * H + grp * HPG;
-            const unsigned tr = (unsigned)lane <= lc ? (unsigned)lane : lc;
+            const float* ag = a + ((int64_t)b * L + row_base(c)) * H + grp * HPG;
+            // rev: the decay of step t is a at memory step L - t, one row past
+            // step t's own; for t = 0 (c = 0, lane 0) that is past the end, so
+            // the lane reads a row inside and stage 1 takes zero instead
+            const unsigned tr0 = (unsigned)lane <= lc ? (unsigned)lane : lc;
+            const unsigned tr = !rev ? tr0 : (c == 0 && tr0 == 0) ? (unsigned)(kT - 1) : (unsigned)kT - tr0;
 #pragma unroll
             for (int hh = 0; hh < HWX; ++hh) {
                 const unsigned hx = (unsigned)(hl0 + (hh < nh ? hh : nh - 1));
-                dma4(ag, (tr * (unsigned)H + hx) * 4u, lds_addr(&sA[as][hh][0]));
+                dma4(ag, (tr * (unsigned)H + hx) * 4u, lds_addr(&sA[as][hh][0]));   // (row tr already in memory order)
             }
         };
         // Stage 1, vectorised over heads: one 16-lane row per head, lane li of
@@ -214,7 +227,8 @@ __global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(2
                 const int hh = 4 * ps + rw < HWX ? 4 * ps + rw : HWX - 1;   // head slot of this row
                 const bool row_ok = 4 * ps + rw < HWX;
                 const float4 a4 = *reinterpret_cast<const float4*>(&sA[io][hh][4 * li]);
-                const float av[4] = {4 * li + 0 <= lastn ? a4.x : 0.f, 4 * li + 1 <= lastn ? a4.y : 0.f,
+                const bool first = rev && cn == 0 && li == 0;   // reversed step 0 has no decay
+                const float av[4] = {4 * li + 0 <= lastn && !first ? a4.x : 0.f, 4 * li + 1 <= lastn ? a4.y : 0.f,
                                      4 * li + 2 <= lastn ? a4.z : 0.f, 4 * li + 3 <= lastn ? a4.w : 0.f};
                 // in-lane prefix sums, then the row scan of the lanes' totals
                 float pin[4];
@@ -331,14 +345,14 @@ __global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(2
         const unsigned qb = ((unsigned)lane & 3u) ^ (((unsigned)lane >> 4) & 3u);
         auto copy_bc = [&](int64_t c, int bs) {
             const unsigned lc = (unsigned)block_last(c);
-            const int64_t row0 = (((int64_t)b * L + c * kT) * G + grp) * N;
+            const int64_t row0 = (((int64_t)b * L + row_base(c)) * G + grp) * N;
 #pragma unroll
             for (int k = 0; k < kT * XPU / 64; ++k) {
                 const unsigned r = 16u * (unsigned)k + (unsigned)lane / 4u;
                 const unsigned tr = r <= lc ? r : lc;
 #pragma unroll
                 for (int nt = 0; nt < NTL; ++nt) {
-                    const uint32_t go = (tr * (unsigned)(G * N) + (unsigned)(nt * 32) + qb * 8u) * 2u;
+                    const uint32_t go = (row_loc(tr) * (unsigned)(G * N) + (unsigned)(nt * 32) + qb * 8u) * 2u;
                     dma16(B + row0, go, lds_addr(&sB[bs][nt * SUB]) + (uint32_t)(k * 64 * 16));
                     dma16(C + row0, go, lds_addr(&sC[bs][nt * SUB]) + (uint32_t)(k * 64 * 16));
                 }
@@ -351,7 +365,7 @@ __global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(2
         constexpr int kTouch = 2 * kT * N * 2 / 128 / 64;   // touch copies per block
         auto touch_bc = [&](int64_t c) {
             const unsigned lc = (unsigned)block_last(c);
-            const int64_t row0 = (((int64_t)b * L + c * kT) * G + grp) * N;
+            const int64_t row0 = (((int64_t)b * L + row_base(c)) * G + grp) * N;
 #pragma unroll
             for (int k = 0; k < kTouch; ++k) {
                 const unsigned li = (unsigned)(k * 64 + lane);     // line index over B then C
@@ -359,7 +373,7 @@ __global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(2
                 const unsigned ln = li % (unsigned)(kT * N * 2 / 128);
                 const unsigned r = ln / (unsigned)(N * 2 / 128), piece = ln % (unsigned)(N * 2 / 128);
                 const unsigned tr = r <= lc ? r : lc;
-                dma4(half ? C + row0 : B + row0, (tr * (unsigned)(G * N) + piece * 64u) * 2u,
+                dma4(half ? C + row0 : B + row0, (row_loc(tr) * (unsigned)(G * N) + piece * 64u) * 2u,
                      lds_addr(&sTouch[0]));
             }
         };
@@ -588,12 +602,13 @@ __global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(2
             for (int k = 0; k < 4; ++k)
                 Yr[k] = *reinterpret_cast<const u32x4*>(xTm + swz<XPU>(16 * k + (lane >> 2), 8 * (lane & 3)));
             if (uvalid) {
-                u16* yblk = Y + ((int64_t)b * L + c * kT) * H * P;
-                const uint32_t yoff = (uint32_t)(((lane >> 2) * H + h) * P + pc + 8 * (lane & 3));
+                u16* yblk = Y + ((int64_t)b * L + row_base(c)) * H * P;
+                const int yoff = (int)((row_loc((unsigned)(lane >> 2)) * H + h) * P + pc + 8 * (lane & 3));
+                const int ystep = rev ? -16 * H * P : 16 * H * P;   // step 16k + lane/4 of the block
 #pragma unroll
                 for (int k = 0; k < 4; ++k)
                     if (16 * k + (lane >> 2) <= last)
-                        *reinterpret_cast<u32x4*>(yblk + (yoff + (uint32_t)(16 * k * H * P))) = Yr[k];
+                        *reinterpret_cast<u32x4*>(yblk + (yoff + k * ystep)) = Yr[k];
             }
         };
         // ================= one instruction stream for both forms =================
@@ -763,25 +778,39 @@ int64_t fwd_workgroups(const FwdShape& s, int64_t nseg, int sw) {
 
 hipError_t launch_fwd(const FwdShape& s, int sw, int64_t seg_chunks, int64_t nseg, const void* X,
                       const float* a, const void* B, const void* C, StateSrc src, void* Y,
-                      float* S_fin, hipStream_t st)
+                      float* S_fin, hipStream_t st, bool rev)
 {
+    if (rev && s.L % kT != 0) return hipErrorInvalidValue;
     const dim3 grid((unsigned)fwd_workgroups(s, nseg, sw));
     const int64_t bps = seg_chunks * (s.Q / kT);
-#define SSD_LAUNCH_FWD(PP, NN, SWW)                                                             \
-    hipLaunchKernelGGL((k_fwd<PP, NN, SWW>), grid, dim3(64 * (SWW + 2)), 0, st, (const u16*)X,   \
+#define SSD_LAUNCH_FWD(PP, NN, SWW, RR)                                                         \
+    hipLaunchKernelGGL((k_fwd<PP, NN, SWW, RR>), grid, dim3(64 * (SWW + 2)), 0, st, (const u16*)X, \
                        a, (const u16*)B, (const u16*)C, src, (u16*)Y, S_fin, s.L, (int)s.H,    \
                        (int)s.G, bps, (int)nseg, (int)s.Bz)
 #define SSD_FWD_SW(PP, NN)                                 \
-    if (sw == 4) SSD_LAUNCH_FWD(PP, NN, 4);                \
-    else if (sw == 5) SSD_LAUNCH_FWD(PP, NN, 5);           \
-    else if (sw == 6 && PP == 64) SSD_LAUNCH_FWD(64, NN, 6); \
+    if (sw == 4) SSD_LAUNCH_FWD(PP, NN, 4, false);         \
+    else if (sw == 5) SSD_LAUNCH_FWD(PP, NN, 5, false);    \
+    else if (sw == 6 && PP == 64) SSD_LAUNCH_FWD(64, NN, 6, false); \
+    else return hipErrorInvalidValue;
+#define SSD_FWD_SW_REV(NN)                                 \
+    if (sw == 4) SSD_LAUNCH_FWD(64, NN, 4, true);          \
+    else if (sw == 5) SSD_LAUNCH_FWD(64, NN, 5, true);     \
+    else if (sw == 6) SSD_LAUNCH_FWD(64, NN, 6, true);     \
     else return hipErrorInvalidValue;
     if (!fwd_units_supported(s.P, sw)) return hipErrorInvalidValue;
+    // the time-reversed instantiations exist for headdim 64 (the backward's dX pass)
+    if (rev) {
+        if (s.P == 64 && s.N == 128) { SSD_FWD_SW_REV(128) }
+        else if (s.P == 64 && s.N == 64) { SSD_FWD_SW_REV(64) }
+        else return hipErrorInvalidValue;
+        return hipGetLastError();
+    }
     if (s.P == 64 && s.N == 128) { SSD_FWD_SW(64, 128) }
     else if (s.P == 64 && s.N == 64) { SSD_FWD_SW(64, 64) }
     else if (s.P == 32 && s.N == 128) { SSD_FWD_SW(32, 128) }
     else if (s.P == 32 && s.N == 64) { SSD_FWD_SW(32, 64) }
     else return hipErrorInvalidValue;
+#undef SSD_FWD_SW_REV
 #undef SSD_FWD_SW
 #undef SSD_LAUNCH_FWD
     return hipGetLastError();

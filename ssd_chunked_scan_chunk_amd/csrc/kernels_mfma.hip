@@ -127,7 +127,7 @@ __device__ __forceinline__ void mfma_seg_body(
     const u16* __restrict__ C, StateSrc src, u16* __restrict__ Y, float* __restrict__ S_fin,
     float* __restrict__ Sseg, float* __restrict__ lamseg, int64_t nseg_total, int64_t L,
     int H, int G, int64_t blocks_per_seg, int nseg_grid, int Bz, int x_groups, unsigned wg,
-    unsigned nwg)
+    unsigned nwg, int rev)
 {
     using Cfg = MfmaCfg<P, N, SW>;
     constexpr int HW = Cfg::HW, NTL = Cfg::NTL, XPR = Cfg::XPR, BPR = Cfg::BPR;
@@ -187,6 +187,14 @@ __device__ __forceinline__ void mfma_seg_body(
         const int64_t last = L - 1 - c * kT;
         return (int)(last < kT - 1 ? last : kT - 1);
     };
+    // Time order of the sequence arrays.  rev: step t of the problem is step
+    // L - 1 - t of X, B, C and Y, and its decay is a at step L - t (none at
+    // t = 0), the time-reversed problem of the backward read in place (L a
+    // multiple of the block: block c is the memory block L/kT - 1 - c, rows
+    // reversed).  row_base: first memory row of block c; row_loc: memory row
+    // of the block's step r relative to it.
+    auto row_base = [&](int64_t c) -> int64_t { return rev ? L - kT * (c + 1) : c * kT; };
+    auto row_loc = [&](unsigned r) -> unsigned { return rev ? (unsigned)(kT - 1) - r : r; };
     // Per-lane element offsets into the swizzled LDS tiles, loop invariant.
     // Tile row bases that are multiples of 16 rows (and so of the swizzle
     // period) are added per use as immediates.
@@ -230,14 +238,14 @@ __device__ __forceinline__ void mfma_seg_body(
         const unsigned xr0 = atv / XPR, xlp = (atv % XPR) ^ (unsigned)swzbits<XPR>((int)(atv / XPR));
         const unsigned lc = (unsigned)block_last(c);
         const u16* Xg;
-        if constexpr (XG) Xg = X + (((int64_t)b * L + c * kT) * x_groups + grp / (G / x_groups)) * (HPG * P);
-        else Xg = X + (((int64_t)b * L + c * kT) * H + grp * HPG) * P;
+        if constexpr (XG) Xg = X + (((int64_t)b * L + row_base(c)) * x_groups + grp / (G / x_groups)) * (HPG * P);
+        else Xg = X + (((int64_t)b * L + row_base(c)) * H + grp * HPG) * P;
 #pragma unroll
         for (int k = 0; k < XOPS; ++k) {
             const unsigned s0 = (unsigned)k * kAuxThreads;      // first slot of the copy
             const unsigned hh = s0 / XHT;                       // uniform: a copy stays in one head
             const unsigned r = (s0 % XHT) / XPR + xr0;
-            const unsigned tr = r <= lc ? r : lc;
+            const unsigned tr = row_loc(r <= lc ? r : lc);
             const unsigned hx = hl0 + hh < (unsigned)HPG ? hl0 + hh : HPG - 1;
             if constexpr (XG)
                 dma16(Xg, (tr * (unsigned)(x_groups * HPG * P) + hx * P + xlp * 8) * 2u,
@@ -249,12 +257,12 @@ __device__ __forceinline__ void mfma_seg_body(
     };
     auto copy_bc = [&](int64_t c, int bf, bool isB) {
         const unsigned lc = (unsigned)block_last(c);
-        const u16* Tg = (isB ? B : C) + (((int64_t)b * L + c * kT) * G + grp) * N;
+        const u16* Tg = (isB ? B : C) + (((int64_t)b * L + row_base(c)) * G + grp) * N;
         const u16* tile = isB ? &sB[bf][0] : &sC[FULL ? bf : 0][0];
 #pragma unroll
         for (int k = 0; k < BOPS; ++k) {
             const unsigned r = (unsigned)k * BRS + br0;
-            const unsigned tr = r <= lc ? r : lc;
+            const unsigned tr = row_loc(r <= lc ? r : lc);
             const unsigned q = bq ^ (unsigned)swzbits<BPR>((int)r);
             dma16(Tg, (tr * (unsigned)GN + q * 8) * 2u,
                   lds_addr(tile) + (uint32_t)((k * kAuxThreads + aw * 64) * 16));
@@ -265,9 +273,13 @@ __device__ __forceinline__ void mfma_seg_body(
     auto copy_a = [&](int64_t c, int ia) {
         const unsigned lc = (unsigned)block_last(c);
         const float* ag;
-        if constexpr (XG) ag = a + ((int64_t)b * L + c * kT) * G + grp;
-        else ag = a + ((int64_t)b * L + c * kT) * H + grp * HPG;
-        const unsigned tr = (unsigned)lane <= lc ? (unsigned)lane : lc;
+        if constexpr (XG) ag = a + ((int64_t)b * L + row_base(c)) * G + grp;
+        else ag = a + ((int64_t)b * L + row_base(c)) * H + grp * HPG;
+        // rev: the decay of step t is a at memory step L - t, one row past
+        // step t's own; for t = 0 (c = 0, lane 0) that is past the end, so
+        // the lane reads a row inside and stage 1 takes zero instead
+        const unsigned tr0 = (unsigned)lane <= lc ? (unsigned)lane : lc;
+        const unsigned tr = !rev ? tr0 : (c == 0 && tr0 == 0) ? (unsigned)(kT - 1) : (unsigned)kT - tr0;
 #pragma unroll
         for (int hh = 0; hh < HW; ++hh) {
             if ((hh & 1) != (int)aw) continue;
@@ -330,7 +342,8 @@ __device__ __forceinline__ void mfma_seg_body(
                 if ((hh & 1) != (int)aw) continue;
                 // prefix sums of a (lane = step) and the sums of |a| over each
                 // quarter, which bound the spread of cs2 within it (log2 units)
-                const float av = lane <= lastn ? sA[ia][hh * kT + lane] : 0.f;
+                const bool first = rev && cn == 0 && lane == 0;   // reversed step 0 has no decay
+                const float av = lane <= lastn && !first ? sA[ia][hh * kT + lane] : 0.f;
                 float absa = fabsf(av);
                 const float cs2 = wave_scan64_rowsum(av, absa, lane) * kLog2e;
                 float base[kQ + 1], lamq[kQ], absq[kQ];   // base[q]: cs2 before quarter q
@@ -652,13 +665,13 @@ __device__ __forceinline__ void mfma_seg_body(
                 // consecutive head-dim entries per register quad): the
                 // backward sums these over a group's heads before rounding
                 if (hvalid) {
-                    float* yrow = reinterpret_cast<float*>(Y) + (((int64_t)b * L + c * kT) * H + h) * P + pc + 4 * g2;
+                    float* yrow = reinterpret_cast<float*>(Y) + (((int64_t)b * L + row_base(c)) * H + h) * P + pc + 4 * g2;
 #pragma unroll
                     for (int I = 0; I < 2; ++I)
                         if (32 * I + l32 <= last)
 #pragma unroll
                             for (int q = 0; q < 4; ++q)
-                                *reinterpret_cast<float4*>(yrow + (int64_t)(32 * I + l32) * H * P + 8 * q) =
+                                *reinterpret_cast<float4*>(yrow + (int64_t)row_loc((unsigned)(32 * I + l32)) * H * P + 8 * q) =
                                     make_float4(Yt[I][4 * q], Yt[I][4 * q + 1], Yt[I][4 * q + 2], Yt[I][4 * q + 3]);
                 }
             } else {
@@ -752,10 +765,10 @@ __global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(S
     const u16* __restrict__ X, const float* __restrict__ a, const u16* __restrict__ B,
     const u16* __restrict__ C, StateSrc src, u16* __restrict__ Y, float* __restrict__ S_fin,
     float* __restrict__ Sseg, float* __restrict__ lamseg, int64_t nseg_total, int64_t L,
-    int H, int G, int64_t blocks_per_seg, int nseg_grid, int Bz, int x_groups)
+    int H, int G, int64_t blocks_per_seg, int nseg_grid, int Bz, int x_groups, int rev)
 {
     mfma_seg_body<P, N, FULL, XG, SW>(X, a, B, C, src, Y, S_fin, Sseg, lamseg, nseg_total, L, H, G,
-                                      blocks_per_seg, nseg_grid, Bz, x_groups, blockIdx.x, gridDim.x);
+                                      blocks_per_seg, nseg_grid, Bz, x_groups, blockIdx.x, gridDim.x, rev);
 }
 
 // Two exchanged-dimension products in one launch (the backward's dC and dB
@@ -774,7 +787,7 @@ __global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(3
     mfma_seg_body<64, 64, true, true, SW>(static_cast<const u16*>(p.X), p.a, static_cast<const u16*>(p.B),
                                           static_cast<const u16*>(p.C), p.src, reinterpret_cast<u16*>(p.Y),
                                           nullptr, nullptr, nullptr, 0, p.L, H, G, blocks_per_seg, nseg_grid,
-                                          Bz, x_groups, wg, nwg);
+                                          Bz, x_groups, wg, nwg, p.rev);
 }
 
 #define SSD_MFMA_DISPATCH(MACRO)                     \
@@ -794,9 +807,10 @@ static unsigned grid_for(const FwdShape& s, int64_t nseg) {
 
 hipError_t launch_mfma_state(const FwdShape& s, int64_t seg_chunks, int64_t nseg_run,
                              int64_t nseg_total, const void* X, const float* a,
-                             const void* B, float* Sseg, float* lamseg, hipStream_t st)
+                             const void* B, float* Sseg, float* lamseg, hipStream_t st, bool rev)
 {
     if (nseg_run <= 0) return hipSuccess;
+    if (rev && s.L % kT != 0) return hipErrorInvalidValue;
     const dim3 grid(grid_for(s, nseg_run));
     const StateSrc none{nullptr, 0, nullptr, 0, 0};
     const int64_t bps = seg_chunks * (s.Q / kT);
@@ -804,7 +818,7 @@ hipError_t launch_mfma_state(const FwdShape& s, int64_t seg_chunks, int64_t nseg
     hipLaunchKernelGGL((k_mfma_seg<PP, NN, false>), grid, dim3(kThreads), 0, st,             \
                        (const u16*)X, a, (const u16*)B, (const u16*)nullptr, none,          \
                        (u16*)nullptr, (float*)nullptr, Sseg, lamseg, nseg_total, s.L,       \
-                       (int)s.H, (int)s.G, bps, (int)nseg_run, (int)s.Bz, 0);
+                       (int)s.H, (int)s.G, bps, (int)nseg_run, (int)s.Bz, 0, rev ? 1 : 0);
     SSD_MFMA_DISPATCH(SSD_LAUNCH_STATE)
 #undef SSD_LAUNCH_STATE
     return hipGetLastError();
@@ -815,6 +829,7 @@ hipError_t launch_mfma_out_xg_pair(const FwdShape& s, int64_t x_groups, const Xg
 {
     if (!(s.P == 64 && s.N == 64) || x_groups < 1 || s.G % x_groups != 0) return hipErrorInvalidValue;
     if ((p0.L + s.Q - 1) / s.Q != s.nc || (p1.L + s.Q - 1) / s.Q != s.nc) return hipErrorInvalidValue;
+    if ((p0.rev && p0.L % kT != 0) || (p1.rev && p1.L % kT != 0)) return hipErrorInvalidValue;
     // four state waves: two sub-heads of 64 per workgroup (a group has H/G of them)
     constexpr int kSW = 4;
     const int64_t hq = (s.H / s.G + kSW / 2 - 1) / (kSW / 2);

@@ -57,22 +57,29 @@ int64_t mfma_heads_per_workgroup(int64_t P, int64_t N);
 // Pass A: for segments [0, nseg_run) of seg_chunks chunks each, the state at
 // the end of the segment starting from zero -> Sseg [Bz][nseg_total][H][P][N]
 // (slot s), and the segment's total log-decay -> lamseg [Bz][H][nseg_total]
-// (lamseg may be null).
+// (lamseg may be null).  rev: the time-reversed problem read in place, as
+// for launch_fwd.
 hipError_t launch_mfma_state(const FwdShape& s, int64_t seg_chunks, int64_t nseg_run,
                              int64_t nseg_total, const void* X, const float* a,
-                             const void* B, float* Sseg, float* lamseg, hipStream_t st);
+                             const void* B, float* Sseg, float* lamseg, hipStream_t st,
+                             bool rev = false);
 // The fused forward pass (kernels_fwd.hip): sw (4, 5 or 6) units -- 32-wide
 // head-dim slices of heads -- per workgroup, for every segment starting from
-// its entering state; writes Y and (last segment) the final state.
+// its entering state; writes Y and (last segment) the final state.  rev
+// (s.L a multiple of 64, headdim 64): the time-reversed problem read and written in
+// place -- step t is step s.L - 1 - t of X, B, C and Y, with the decay a at
+// step s.L - t (none for t = 0).
 hipError_t launch_fwd(const FwdShape& s, int sw, int64_t seg_chunks, int64_t nseg, const void* X,
                       const float* a, const void* B, const void* C, StateSrc src, void* Y,
-                      float* S_fin, hipStream_t st);
+                      float* S_fin, hipStream_t st, bool rev = false);
 int64_t fwd_workgroups(const FwdShape& s, int64_t nseg, int sw);
 bool fwd_units_supported(int64_t P, int sw);
 
 // The backward's exchanged-dimension products (headdim 64, state 64, one chunk
 // per segment), two in one launch that share every size in s but the sequence
-// length (p0.L, p1.L; each must have s.nc chunks): X [Bz][L][x_groups][(H/G)*64]
+// length (p0.L, p1.L; each must have s.nc chunks) and the time order (rev: the
+// time-reversed problem read and written in place, as for launch_fwd; L a
+// multiple of 64): X [Bz][L][x_groups][(H/G)*64]
 // bf16 shared by the H/G heads of a group (head hl reads columns hl*64 ..), a
 // [Bz][L][G] (one decay per group), and the entering state of segment s read
 // transposed from the [64][(H/G)*64] state of group grp in src (segment 0 from
@@ -85,6 +92,7 @@ struct XgPass {
     StateSrc src;
     float* Y;
     int64_t L;
+    int rev;
 };
 hipError_t launch_mfma_out_xg_pair(const FwdShape& s, int64_t x_groups, const XgPass& p0, const XgPass& p1,
                                    hipStream_t st);

@@ -50,6 +50,15 @@ def test_bwd_shapes_ragged(Q, P, N, H, G):
     bwd_case(si.FwdShape(2, 3 * Q + 37, H, P, N, G, Q, si.BF16), seed=Q + P + N + G, tag="shapes")
 
 
+@pytest.mark.parametrize("Q,P,N,H,G", [(256, 64, 128, 4, 1), (128, 64, 64, 4, 2), (64, 64, 128, 6, 3),
+                                       (128, 32, 64, 3, 1)])
+def test_bwd_shapes_whole_chunks(Q, P, N, H, G):
+    # a whole number of chunks: the reversed problem needs no padding and the
+    # headdim-64 plans read (and write) it in place, with the reversed step 0
+    # taking no decay; headdim 32 still copies it out
+    bwd_case(si.FwdShape(2, 3 * Q, H, P, N, G, Q, si.BF16), seed=Q + P + N + G + 1, tag="whole-chunks")
+
+
 def test_bwd_without_states():
     # no initial state and no final-state gradient; L a whole number of chunks
     bwd_case(si.FwdShape(2, 512, 4, 64, 128, 1, 128, si.BF16), seed=5, with_s0=False,
