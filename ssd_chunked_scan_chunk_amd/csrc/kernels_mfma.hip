@@ -129,6 +129,7 @@ __device__ __forceinline__ void mfma_seg_body(
     int H, int G, int64_t blocks_per_seg, int nseg_grid, int Bz, int x_groups, unsigned wg,
     unsigned nwg, int rev)
 {
+    static_assert(!FULL || XG, "the output pass runs only as the backward's exchanged-dimension products");
     using Cfg = MfmaCfg<P, N, SW>;
     constexpr int HW = Cfg::HW, NTL = Cfg::NTL, XPR = Cfg::XPR, BPR = Cfg::BPR;
     constexpr int XOPS = Cfg::XOPS, BOPS = Cfg::BOPS;
@@ -136,9 +137,9 @@ __device__ __forceinline__ void mfma_seg_body(
     __shared__ __attribute__((aligned(16))) u16 sX[2][HW * kT * P];    // [buf][head][step][p]
     __shared__ __attribute__((aligned(16))) u16 sB[2][kT * N];         // [buf][step][n]
     __shared__ __attribute__((aligned(16))) u16 sC[FULL ? 2 : 1][FULL ? kT * N : 8];
-    // masked scores [i][j]; XG: decayed, high part then low part, unpadded
-    // rows with the 16-byte pieces XOR-swizzled by (i / 4) % 4
-    __shared__ __attribute__((aligned(16))) u16 sP[FULL ? 3 : 1][FULL ? (XG ? 2 * 32 * 32 : 32 * kPRow) : 8];
+    // output pass: the decayed masked scores [i][j], high part then low part,
+    // unpadded rows with the 16-byte pieces XOR-swizzled by (i / 4) % 4
+    __shared__ __attribute__((aligned(16))) u16 sP[FULL ? 3 : 1][FULL ? 2 * 32 * 32 : 8];
     __shared__ __attribute__((aligned(16))) float sA[3][HW * kT];     // [buf][head][step]
     // stage 1's results per head, two buffers: output exponents, state weights
     // per step, and the block's scale decisions
@@ -427,38 +428,26 @@ __device__ __forceinline__ void mfma_seg_body(
                         for (int hf = 0; hf < 2; ++hf) St = mfma32(rowfrag(bT, J, nt, hf), rowfrag(cT, I, nt, hf), St);
                     // row j of accumulator register r: 8(r/4) + 4*g2 + r%4; lane = i.
                     // Masked entries (j > i on the diagonal) are replaced, never multiplied.
+                    // decayed by 2^(cs2_i - cs2_j) (the direct form's exponents,
+                    // shared by every head here), split into high and low parts
                     const bool diag = I == J;
-                    if constexpr (XG) {
-                        // decayed by 2^(cs2_i - cs2_j) (the direct form's exponents,
-                        // shared by every head here), split into high and low parts
-                        const float csi = sCs[bf][0][32 * I + l32];
-                        u16* prow = &sP[t][l32 * 32];
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const int j0 = 8 * q + 4 * g2;
-                            const float4 cj = *reinterpret_cast<const float4*>(&sCs[bf][0][32 * J + j0]);
-                            const float cjv[4] = {cj.x, cj.y, cj.z, cj.w};
-                            float v[4];
-#pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                v[e] = (!diag || j0 + e <= l32) ? St[4 * q + e] * fast_exp2(csi - cjv[e]) : 0.f;
-                            const uint32_t h01 = pack2(v[0], v[1]), h23 = pack2(v[2], v[3]);
-                            const uint32_t l01 = pack2(v[0] - __uint_as_float(h01 << 16), v[1] - __uint_as_float(h01 & 0xffff0000u));
-                            const uint32_t l23 = pack2(v[2] - __uint_as_float(h23 << 16), v[3] - __uint_as_float(h23 & 0xffff0000u));
-                            const int off = 8 * (q ^ ((l32 >> 2) & 3)) + 4 * g2;
-                            *reinterpret_cast<uint2*>(prow + off) = make_uint2(h01, h23);
-                            *reinterpret_cast<uint2*>(prow + 32 * 32 + off) = make_uint2(l01, l23);
-                        }
-                    } else {
-                    u16* prow = &sP[t][l32 * kPRow];
+                    const float csi = sCs[bf][0][32 * I + l32];
+                    u16* prow = &sP[t][l32 * 32];
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const int j0 = 8 * q + 4 * g2;
+                        const float4 cj = *reinterpret_cast<const float4*>(&sCs[bf][0][32 * J + j0]);
+                        const float cjv[4] = {cj.x, cj.y, cj.z, cj.w};
                         float v[4];
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) v[e] = (!diag || j0 + e <= l32) ? St[4 * q + e] : 0.f;
-                        *reinterpret_cast<uint2*>(prow + j0) = make_uint2(pack2(v[0], v[1]), pack2(v[2], v[3]));
-                    }
+                        for (int e = 0; e < 4; ++e)
+                            v[e] = (!diag || j0 + e <= l32) ? St[4 * q + e] * fast_exp2(csi - cjv[e]) : 0.f;
+                        const uint32_t h01 = pack2(v[0], v[1]), h23 = pack2(v[2], v[3]);
+                        const uint32_t l01 = pack2(v[0] - __uint_as_float(h01 << 16), v[1] - __uint_as_float(h01 & 0xffff0000u));
+                        const uint32_t l23 = pack2(v[2] - __uint_as_float(h23 << 16), v[3] - __uint_as_float(h23 & 0xffff0000u));
+                        const int off = 8 * (q ^ ((l32 >> 2) & 3)) + 4 * g2;
+                        *reinterpret_cast<uint2*>(prow + off) = make_uint2(h01, h23);
+                        *reinterpret_cast<uint2*>(prow + 32 * 32 + off) = make_uint2(l01, l23);
                     }
                 }
             }
@@ -485,7 +474,7 @@ __device__ __forceinline__ void mfma_seg_body(
     if constexpr (FULL) {
         const float* S0 = seg == 0 ? (src.first ? src.first + b * src.first_bstride : nullptr)
                                    : (src.Sin ? src.Sin + b * src.bstride + seg * src.sstride : nullptr);
-        if (XG && S0) {
+        if (S0) {
             // transposed: Sacc(p, n) = S[grp][n][hl*P + p] of an [N][HPG*P] state
             const int hlc = hlw < HPG ? hlw : HPG - 1;
             const float* St = S0 + (int64_t)grp * HPG * PN + hlc * P + pc + l32;
@@ -494,20 +483,6 @@ __device__ __forceinline__ void mfma_seg_body(
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     Sacc[nt][r] = St[(int64_t)(nt * 32 + 16 * (r >> 3) + 8 * g2 + (r & 7)) * (HPG * P)];
-        } else if (S0) {
-            S0 += (int64_t)h * PN;
-#pragma unroll
-            for (int nt = 0; nt < NTL; ++nt) {
-                const float* row = S0 + (int64_t)(pc + l32) * N + nt * 32 + 8 * g2;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float4 v = *reinterpret_cast<const float4*>(row + 16 * (q >> 1) + 4 * (q & 1));
-                    Sacc[nt][4 * q + 0] = v.x;
-                    Sacc[nt][4 * q + 1] = v.y;
-                    Sacc[nt][4 * q + 2] = v.z;
-                    Sacc[nt][4 * q + 3] = v.w;
-                }
-            }
         }
     }
     float lam2_total = 0.f;   // the segment's log2-decay
@@ -519,7 +494,6 @@ __device__ __forceinline__ void mfma_seg_body(
 
         const u16* bT = &sB[bf][0];
         const u16* xT = &sX[bf][hw * kT * P];
-        u16* xTm = &sX[bf][hw * kT * P];
         // X^T fragments of this wave's head-dim tile (lane = p, k = step)
         auto xfrag = [&](int J, int ks) {
             const u16* t = xT + (32 * J + 16 * ks) * P;
@@ -572,115 +546,40 @@ __device__ __forceinline__ void mfma_seg_body(
 
         if constexpr (FULL) sync_lds();  // the shared score tiles are complete
 
-        uint2 Yb[2][4];
         bf16x8 xk[4];   // X~ fragments (J, ks) = (0,0), (0,1), (1,0), (1,1)
         if constexpr (FULL) {
-            // output factors (the direct form scales only the state's part here)
-            const float e0 = fast_exp2(sCs[bf][hw][l32] + (fast ? 0.f : ld_in));
-            const float e1 = fast_exp2(sCs[bf][hw][32 + l32] + (fast ? 0.f : ld_in));
-            // P tile t as the B operand of k step ks (lane = i, k = j)
-            auto ptile = [&](int t, int ks) {
-                return as_bf16x8(*reinterpret_cast<const u32x4*>(&sP[t][l32 * kPRow + 16 * ks + 8 * g2]));
+            // stage 5's part at the block's entering scale, then stage 2 in the
+            // direct form: the copy waves' decayed scores, high and low parts,
+            // on unweighted X
+            Yt[0] *= fast_exp2(sCs[bf][hw][l32] + ld_in);
+            Yt[1] *= fast_exp2(sCs[bf][hw][32 + l32] + ld_in);
+            auto pt = [&](int t, int ks, int part) {
+                return as_bf16x8(*reinterpret_cast<const u32x4*>(
+                    &sP[t][part * 32 * 32 + l32 * 32 + 8 * ((2 * ks + g2) ^ ((l32 >> 2) & 3))]));
             };
-            if (fast) {
-                // ---- stage 2: Y^T += X~^T P, then the per-step factor.  The
-                // k steps are the quarters in order; at a re-based quarter the
-                // rows from that quarter on move to its reference ----
-                const bool upper = l32 >= 16;        // this lane's row is in the tile's second quarter
-                xk[0] = xwfrag(0, 0);
-                Yt[0] = mfma32(xk[0], ptile(0, 0), Yt[0]);
-                Yt[1] = mfma32(xk[0], ptile(1, 0), Yt[1]);
-                if (fold[1]) {
-                    const float f = fast_exp2(rq[1]);
-                    Yt[0] *= upper ? f : 1.f;
-                    Yt[1] *= f;
-                }
-                xk[1] = xwfrag(0, 1);
-                Yt[0] = mfma32(xk[1], ptile(0, 1), Yt[0]);
-                Yt[1] = mfma32(xk[1], ptile(1, 1), Yt[1]);
-                if (fold[2]) Yt[1] *= fast_exp2(rq[2]);
-                xk[2] = xwfrag(1, 0);
-                Yt[1] = mfma32(xk[2], ptile(2, 0), Yt[1]);
-                if (fold[3]) Yt[1] *= upper ? fast_exp2(rq[3]) : 1.f;
-                xk[3] = xwfrag(1, 1);
-                Yt[1] = mfma32(xk[3], ptile(2, 1), Yt[1]);
-                Yt[0] *= e0;
-                Yt[1] *= e1;
-            } else {
-                Yt[0] *= e0;
-                Yt[1] *= e1;
-                // ---- stage 2, direct form: decay 2^(cs2_i - cs2_j) on the shared scores ----
-                // (masked entries stay replaced by zero: their exponent may overflow)
-                auto decayed = [&](int t, int J, int ks, float csi) {
-                    const u32x4 u = as_u32x4(ptile(t, ks));
-                    const int jl = 16 * ks + 8 * g2;              // j within the tile, element 0
-                    const f32x4 c0 = *reinterpret_cast<const f32x4*>(&sCs[bf][hw][32 * J + jl]);
-                    const f32x4 c1 = *reinterpret_cast<const f32x4*>(&sCs[bf][hw][32 * J + jl + 4]);
-                    const float cj[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
-                    const bool diag = t != 1;
-                    float v[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int j = jl + e;
-                        const float x = __uint_as_float(e & 1 ? (u[e >> 1] & 0xffff0000u) : (u[e >> 1] << 16));
-                        v[e] = (!diag || j <= l32) ? x * fast_exp2(csi - cj[e]) : 0.f;
-                    }
-                    return as_bf16x8(u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])});
-                };
-                if constexpr (XG) {
-                    // the copy waves' decayed scores, high and low parts, on unweighted X
-                    auto pt = [&](int t, int ks, int part) {
-                        return as_bf16x8(*reinterpret_cast<const u32x4*>(
-                            &sP[t][part * 32 * 32 + l32 * 32 + 8 * ((2 * ks + g2) ^ ((l32 >> 2) & 3))]));
-                    };
+            for (int ks = 0; ks < 2; ++ks) {
+                const bf16x8 xa0 = xfrag(0, ks);
+                const bf16x8 xa1 = xfrag(1, ks);
 #pragma unroll
-                    for (int ks = 0; ks < 2; ++ks) {
-                        const bf16x8 xa0 = xfrag(0, ks);
-                        const bf16x8 xa1 = xfrag(1, ks);
-#pragma unroll
-                        for (int part = 0; part < 2; ++part) {
-                            Yt[0] = mfma32(xa0, pt(0, ks, part), Yt[0]);
-                            Yt[1] = mfma32(xa0, pt(1, ks, part), Yt[1]);
-                            Yt[1] = mfma32(xa1, pt(2, ks, part), Yt[1]);
-                        }
-                    }
-                } else {
-                const float csi0 = sCs[bf][hw][l32], csi1 = sCs[bf][hw][32 + l32];
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    // one tile at a time (this rare path must not raise the
-                    // kernel's register budget)
-                    const bf16x8 xa0 = xfrag(0, ks);
-                    Yt[0] = mfma32(xa0, decayed(0, 0, ks, csi0), Yt[0]);
-                    __builtin_amdgcn_sched_barrier(0);
-                    Yt[1] = mfma32(xa0, decayed(1, 0, ks, csi1), Yt[1]);
-                    __builtin_amdgcn_sched_barrier(0);
-                    Yt[1] = mfma32(xfrag(1, ks), decayed(2, 1, ks, csi1), Yt[1]);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
+                for (int part = 0; part < 2; ++part) {
+                    Yt[0] = mfma32(xa0, pt(0, ks, part), Yt[0]);
+                    Yt[1] = mfma32(xa0, pt(1, ks, part), Yt[1]);
+                    Yt[1] = mfma32(xa1, pt(2, ks, part), Yt[1]);
                 }
             }
-            if constexpr (XG) {
-                // fp32 out, straight from the accumulators (lane = step, four
-                // consecutive head-dim entries per register quad): the
-                // backward sums these over a group's heads before rounding
-                if (hvalid) {
-                    float* yrow = reinterpret_cast<float*>(Y) + (((int64_t)b * L + row_base(c)) * H + h) * P + pc + 4 * g2;
-#pragma unroll
-                    for (int I = 0; I < 2; ++I)
-                        if (32 * I + l32 <= last)
-#pragma unroll
-                            for (int q = 0; q < 4; ++q)
-                                *reinterpret_cast<float4*>(yrow + (int64_t)row_loc((unsigned)(32 * I + l32)) * H * P + 8 * q) =
-                                    make_float4(Yt[I][4 * q], Yt[I][4 * q + 1], Yt[I][4 * q + 2], Yt[I][4 * q + 3]);
-                }
-            } else {
-                // Y^T to bf16
+            // fp32 out, straight from the accumulators (lane = step, four
+            // consecutive head-dim entries per register quad): the backward
+            // sums these over a group's heads before rounding
+            if (hvalid) {
+                float* yrow = reinterpret_cast<float*>(Y) + (((int64_t)b * L + row_base(c)) * H + h) * P + pc + 4 * g2;
 #pragma unroll
                 for (int I = 0; I < 2; ++I)
+                    if (32 * I + l32 <= last)
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        Yb[I][q] = make_uint2(pack2(Yt[I][4 * q], Yt[I][4 * q + 1]), pack2(Yt[I][4 * q + 2], Yt[I][4 * q + 3]));
+                        for (int q = 0; q < 4; ++q)
+                            *reinterpret_cast<float4*>(yrow + (int64_t)row_loc((unsigned)(32 * I + l32)) * H * P + 8 * q) =
+                                make_float4(Yt[I][4 * q], Yt[I][4 * q + 1], Yt[I][4 * q + 2], Yt[I][4 * q + 3]);
             }
         }
 
@@ -690,10 +589,8 @@ __device__ __forceinline__ void mfma_seg_body(
 #pragma unroll
             for (int nt = 0; nt < NTL; ++nt) Sacc[nt] *= f;
         }
-        if (!(FULL && fast)) {   // (the fast stage 2 has left X~ in registers)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) xk[i] = xwfrag(i >> 1, i & 1);
-        }
+        for (int i = 0; i < 4; ++i) xk[i] = xwfrag(i >> 1, i & 1);
 #pragma unroll
         for (int J = 0; J < 2; ++J) {
 #pragma unroll
@@ -710,28 +607,6 @@ __device__ __forceinline__ void mfma_seg_body(
                     const bf16x8 Af = join8(lds_tr4(t + toff[nt][0]), lds_tr4(t + toff[nt][1]));
                     Sacc[nt] = mfma32(Af, xw, Sacc[nt]);
                 }
-            }
-        }
-        if constexpr (FULL && !XG) {
-            // Y^T through this wave's own X slice, which is dead after stage 3,
-            // so that copy k of a lane holds 16 contiguous bytes of step
-            // 16k + lane/4 and a store covers 16 steps x 64 bytes
-#pragma unroll
-            for (int I = 0; I < 2; ++I)
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    *reinterpret_cast<uint2*>(xTm + swz<XPR>(32 * I + l32, pc + 8 * q + 4 * g2)) = Yb[I][q];
-            u32x4 Yr[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                Yr[k] = *reinterpret_cast<const u32x4*>(xTm + swz<XPR>(16 * k + (lane >> 2), pc + 8 * (lane & 3)));
-            if (hvalid) {
-                u16* yblk = Y + ((int64_t)b * L + c * kT) * H * P;
-                const uint32_t yoff = (uint32_t)(((lane >> 2) * H + h) * P + pc + 8 * (lane & 3));
-#pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    if (16 * k + (lane >> 2) <= last)
-                        *reinterpret_cast<u32x4*>(yblk + (yoff + (uint32_t)(16 * k * H * P))) = Yr[k];
             }
         }
     }
