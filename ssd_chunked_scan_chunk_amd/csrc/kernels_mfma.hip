@@ -1,4 +1,8 @@
-// kernels_mfma.hip -- bf16 MFMA kernels of the SSD layer for gfx950.
+// kernels_mfma.hip -- bf16 MFMA kernels of the SSD layer for gfx950: the
+// state-only pass of the segmented forward plan (stages 1, 3, 4) and the
+// backward's exchanged-dimension products (the output pass, in the direct
+// form).  The forward's full pass is the fused kernel of kernels_fwd.hip; the
+// design below is shared by both files.
 //
 // The layer's sequence map is the 1-semiseparable matrix M = Lmask o (C B^T)
 // applied to X (wiki review of "Transformers are SSMs", section "Core
@@ -36,7 +40,7 @@
 //    sequence is split into segments: a state-only pass (stages 1, 3, 4)
 //    gives each segment's end state from zero, a scan over segments
 //    (kernels_scan.hip) gives every segment's entering state, and the full
-//    pass starts from it.
+//    pass (kernels_fwd.hip) starts from it.
 //  * The masked scores of a block do not depend on the head (the decay is
 //    moved onto X and the output, below), so the copy waves form the three
 //    causal 32x32 score tiles once per workgroup and share them in LDS as
@@ -49,8 +53,8 @@
 //    register result, and keeping them out of the compiler's view stops it
 //    from inserting full vmcnt waits before every LDS access, which would
 //    serialise the prefetch.  Only the copy waves wait for copies (vmcnt(0)
-//    once per block); state waves store their Y at the end of each block and
-//    never wait on memory.  Two barriers per block: one publishes the
+//    once per block); state waves store their outputs at the end of each
+//    block and never wait on memory.  Two barriers per block: one publishes the
 //    block's copies and stage-1 results (and frees the other buffers), one
 //    publishes the shared scores.
 //  * Every product is v_mfma_f32_32x32x16_bf16 (operand lane l holds row or
