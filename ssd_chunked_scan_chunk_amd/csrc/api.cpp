@@ -819,13 +819,12 @@ ssd_status ssd_chunk_scan_bwd(const ssd_fwd_desc* desc, const void* X, const flo
         int64_t k1 = 1;
         int sw1 = 4;
         auto_plan(bp.sr, 1, 0, SIZE_MAX, &k1, &sw1);
+        // its final state G_0 times e^{a_0} is d(initial state)
         SSD_TRY(ssd::launch_fwd(bp.sr, sw1, 1, nc, dYr, ar, Cr, Br, src, rin ? dX : V(W_DXR), dinitial_state,
-                                hs, rin), "bwd: dX pass");
+                                hs, rin, a, L * H), "bwd: dX pass");
     }
     if (!rin)
         SSD_TRY(ssd::launch_remap_rows(dX, V(W_DXR), Bz, L, Lp, Lp - 1, -1, H * P * es, hs), "bwd: dX order");
-    if (dinitial_state)
-        SSD_TRY(ssd::launch_scale_state_by_a0(dinitial_state, a, Bz, L, H, PN, hs), "bwd: dS0");
     // 4. da from the chunk-local four-term form
     SSD_TRY(ssd::launch_bwd_da(s, X, dY, a, B, C, F(W_SFW), F(W_SREV), true, da, hs), "bwd: da");
     }

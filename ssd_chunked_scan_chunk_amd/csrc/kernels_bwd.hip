@@ -101,56 +101,50 @@ __global__ void k_state_transpose(float* __restrict__ out, const float* __restri
 }
 
 // sum over each group's heads in fp32, rounded once to the output type; a
-// thread covers 8 elements (two 16-byte input pieces for fp32 input):
-// out[b][t][g][n] = sum_{h in g} in[b][s][h][n]: thread (t, g, 8-column piece)
-// of a flat range over a batch's rows (several short rows share a workgroup),
-// the heads summed in order, four loads in flight
+// thread covers 4 consecutive elements (one 16-byte input piece for fp32
+// input), so that the lanes of a wave read whole rows of consecutive pieces:
+// out[b][t][g][n] = sum_{h in g} in[b][s][h][n]: thread (t, g, 4-column
+// piece) of a flat range over a batch's rows, the heads summed in order,
+// eight loads in flight
 template <typename TI, typename TO>
 __global__ __launch_bounds__(256) void k_group_sum(TO* __restrict__ out, const TI* __restrict__ in,
                                                    int64_t Lout, int64_t Lin, int64_t off, int64_t dir,
-                                                   int H, int G, int N8)
+                                                   int H, int G, int N4)
 {
-    const int64_t w = (int64_t)G * N8;
+    const int64_t w = (int64_t)G * N4;
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= Lout * w) return;
     const int64_t t = idx / w, b = blockIdx.y;
     const int k = (int)(idx - t * w);
-    const int gi = k / N8, q = k - gi * N8;
+    const int gi = k / N4, q = k - gi * N4;
     const int hpg = H / G;
-    const int N = 8 * N8;
+    const int N = 4 * N4;
     const int64_t s = off + dir * t;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
     if (s >= 0 && s < Lin) {
-        const TI* src = in + ((b * Lin + s) * H + (int64_t)gi * hpg) * N + 8 * q;
-#pragma unroll 4
+        const TI* src = in + ((b * Lin + s) * H + (int64_t)gi * hpg) * N + 4 * q;
+#pragma unroll 8
         for (int j = 0; j < hpg; ++j) {
             const TI* p = src + (int64_t)j * N;
             if constexpr (sizeof(TI) == 2) {
-                const uint4 v = *reinterpret_cast<const uint4*>(p);
-                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    acc[2 * e] += __uint_as_float(w[e] << 16);
-                    acc[2 * e + 1] += __uint_as_float(w[e] & 0xffff0000u);
-                }
+                const uint2 v = *reinterpret_cast<const uint2*>(p);
+                acc[0] += __uint_as_float(v.x << 16);
+                acc[1] += __uint_as_float(v.x & 0xffff0000u);
+                acc[2] += __uint_as_float(v.y << 16);
+                acc[3] += __uint_as_float(v.y & 0xffff0000u);
             } else {
-                const float4 v0 = *reinterpret_cast<const float4*>(p);
-                const float4 v1 = *reinterpret_cast<const float4*>(p + 4);
-                acc[0] += v0.x; acc[1] += v0.y; acc[2] += v0.z; acc[3] += v0.w;
-                acc[4] += v1.x; acc[5] += v1.y; acc[6] += v1.z; acc[7] += v1.w;
+                const float4 v = *reinterpret_cast<const float4*>(p);
+                acc[0] += v.x; acc[1] += v.y; acc[2] += v.z; acc[3] += v.w;
             }
         }
     }
-    TO* dst = out + ((b * Lout + t) * G + gi) * N + 8 * q;
+    TO* dst = out + ((b * Lout + t) * G + gi) * N + 4 * q;
     if constexpr (sizeof(TO) == 2) {
-        uint32_t o[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            o[e] = (uint32_t)f32_to_bf_bits(acc[2 * e]) | ((uint32_t)f32_to_bf_bits(acc[2 * e + 1]) << 16);
-        *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+        *reinterpret_cast<uint2*>(dst) =
+            make_uint2((uint32_t)f32_to_bf_bits(acc[0]) | ((uint32_t)f32_to_bf_bits(acc[1]) << 16),
+                       (uint32_t)f32_to_bf_bits(acc[2]) | ((uint32_t)f32_to_bf_bits(acc[3]) << 16));
     } else {
         *reinterpret_cast<float4*>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-        *reinterpret_cast<float4*>(dst + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
     }
 }
 
@@ -222,12 +216,12 @@ hipError_t launch_group_sum(void* out, const void* in, int64_t Bz, int64_t Lout,
                             int64_t off, int64_t dir, int64_t H, int64_t G, int64_t N, bool in_bf16,
                             bool out_bf16, hipStream_t st)
 {
-    const int64_t N8 = N / 8, w = G * N8;
+    const int64_t N4 = N / 4, w = G * N4;
     if (Bz * Lout * w <= 0) return hipSuccess;
     const dim3 grid((unsigned)((Lout * w + 255) / 256), (unsigned)Bz), block(256);
 #define SSD_GS(TI, TO)                                                                            \
     hipLaunchKernelGGL((k_group_sum<TI, TO>), grid, block, 0, st, (TO*)out, (const TI*)in, Lout, Lin, \
-                       off, dir, (int)H, (int)G, (int)N8)
+                       off, dir, (int)H, (int)G, (int)N4)
     if (in_bf16 && out_bf16) SSD_GS(u16, u16);
     else if (!in_bf16 && out_bf16) SSD_GS(float, u16);
     else if (!in_bf16 && !out_bf16) SSD_GS(float, float);

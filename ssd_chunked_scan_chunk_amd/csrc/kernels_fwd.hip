@@ -71,7 +71,8 @@ template <int P, int N, int SW, bool REV = false>
 __global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(2))) void k_fwd(
     const u16* __restrict__ X, const float* __restrict__ a, const u16* __restrict__ B,
     const u16* __restrict__ C, StateSrc src, u16* __restrict__ Y, float* __restrict__ S_fin,
-    int64_t L, int H, int G, int64_t blocks_per_seg, int nseg_grid, int Bz)
+    const float* __restrict__ fin_a, int64_t fin_a_bstride, int64_t L, int H, int G,
+    int64_t blocks_per_seg, int nseg_grid, int Bz)
 {
     using Cfg = FwdCfg<P, N, SW>;
     constexpr int PS = Cfg::PS, NTL = Cfg::NTL, XPU = Cfg::XPU, HWX = Cfg::HWX;
@@ -755,14 +756,15 @@ __global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(2
     if (!uvalid || !S_fin || seg != nseg_grid - 1) return;
     float* Sdst = S_fin + ((int64_t)b * H + h) * PN;
     const float f = fast_exp2(ld);
+    const float e = fin_a ? expf(fin_a[b * fin_a_bstride + h]) : 1.f;   // the state, then this factor
 #pragma unroll
     for (int nt = 0; nt < NTL; ++nt) {
         float* row = Sdst + (int64_t)(pc + l32) * N + nt * 32 + 8 * g2;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
             *reinterpret_cast<float4*>(row + 16 * (q >> 1) + 4 * (q & 1)) =
-                make_float4(f * Sacc[nt][4 * q], f * Sacc[nt][4 * q + 1], f * Sacc[nt][4 * q + 2],
-                            f * Sacc[nt][4 * q + 3]);
+                make_float4(e * (f * Sacc[nt][4 * q]), e * (f * Sacc[nt][4 * q + 1]),
+                            e * (f * Sacc[nt][4 * q + 2]), e * (f * Sacc[nt][4 * q + 3]));
     }
 }
 
@@ -778,14 +780,15 @@ int64_t fwd_workgroups(const FwdShape& s, int64_t nseg, int sw) {
 
 hipError_t launch_fwd(const FwdShape& s, int sw, int64_t seg_chunks, int64_t nseg, const void* X,
                       const float* a, const void* B, const void* C, StateSrc src, void* Y,
-                      float* S_fin, hipStream_t st, bool rev)
+                      float* S_fin, hipStream_t st, bool rev, const float* fin_a, int64_t fin_a_bstride)
 {
     if (rev && s.L % kT != 0) return hipErrorInvalidValue;
     const dim3 grid((unsigned)fwd_workgroups(s, nseg, sw));
     const int64_t bps = seg_chunks * (s.Q / kT);
 #define SSD_LAUNCH_FWD(PP, NN, SWW, RR)                                                         \
     hipLaunchKernelGGL((k_fwd<PP, NN, SWW, RR>), grid, dim3(64 * (SWW + 2)), 0, st, (const u16*)X, \
-                       a, (const u16*)B, (const u16*)C, src, (u16*)Y, S_fin, s.L, (int)s.H,    \
+                       a, (const u16*)B, (const u16*)C, src, (u16*)Y, S_fin, fin_a, fin_a_bstride, \
+                       s.L, (int)s.H,                                                          \
                        (int)s.G, bps, (int)nseg, (int)s.Bz)
 #define SSD_FWD_SW(PP, NN)                                 \
     if (sw == 4) SSD_LAUNCH_FWD(PP, NN, 4, false);         \

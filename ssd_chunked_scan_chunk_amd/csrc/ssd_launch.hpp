@@ -69,9 +69,12 @@ hipError_t launch_mfma_state(const FwdShape& s, int64_t seg_chunks, int64_t nseg
 // (s.L a multiple of 64, headdim 64): the time-reversed problem read and written in
 // place -- step t is step s.L - 1 - t of X, B, C and Y, with the decay a at
 // step s.L - t (none for t = 0).
+// fin_a (optional): the final state is also multiplied by exp(fin_a[b *
+// fin_a_bstride + h]) (the backward's d(initial state) = e^{a_0} G_0)
 hipError_t launch_fwd(const FwdShape& s, int sw, int64_t seg_chunks, int64_t nseg, const void* X,
                       const float* a, const void* B, const void* C, StateSrc src, void* Y,
-                      float* S_fin, hipStream_t st, bool rev = false);
+                      float* S_fin, hipStream_t st, bool rev = false, const float* fin_a = nullptr,
+                      int64_t fin_a_bstride = 0);
 int64_t fwd_workgroups(const FwdShape& s, int64_t nseg, int sw);
 bool fwd_units_supported(int64_t P, int sw);
 

@@ -31,7 +31,8 @@ hipError_t launch_state_scan(const FwdShape&, int64_t, int64_t, const float*, co
 hipError_t launch_mfma_state(const FwdShape&, int64_t, int64_t, int64_t, const void*, const float*,
                              const void*, float*, float*, hipStream_t, bool) { SSD_STUB; }
 hipError_t launch_fwd(const FwdShape&, int, int64_t, int64_t, const void*, const float*, const void*,
-                      const void*, StateSrc, void*, float*, hipStream_t, bool) { SSD_STUB; }
+                      const void*, StateSrc, void*, float*, hipStream_t, bool, const float*,
+                      int64_t) { SSD_STUB; }
 int64_t fwd_workgroups(const FwdShape&, int64_t, int) { return 0; }
 hipError_t launch_mfma_out_xg_pair(const FwdShape&, int64_t, const XgPass&, const XgPass&, hipStream_t) { SSD_STUB; }
 hipError_t launch_step(int64_t, int64_t, int64_t, int64_t, int64_t, bool, float*, const void*,
