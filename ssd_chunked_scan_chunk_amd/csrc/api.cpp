@@ -789,30 +789,39 @@ ssd_status ssd_chunk_scan_bwd(const ssd_fwd_desc* desc, const void* X, const flo
         SSD_TRY(ssd::launch_bwd_da_valu(s, (const float*)X, (const float*)dY, a, (const float*)B,
                                         (const float*)C, F(W_SFW), F(W_SREV), da, hs), "bwd: da");
     } else {
-    // 1. the state entering every forward chunk
-    SSD_TRY(ssd::launch_mfma_state(s, 1, nc - 1, nc, X, a, B, F(W_SFW), F(W_LAMFW), hs), "bwd: chunk states");
-    SSD_TRY(ssd::launch_state_scan(s, nc - 1, nc, F(W_SFW), F(W_LAMFW), H * nc, nc, initial_state,
-                                   F(W_SFW), 0, F(W_SFW) + (nc - 1) * H * PN, nc * H * PN, hs),
-            "bwd: state scan");
-    // 2. the adjoint recurrence runs backwards in time: the reversed sequence
+    // 1. the state entering every forward chunk, and 2. the adjoint's: the
+    // adjoint recurrence runs backwards in time, on the reversed sequence
     // (padded at its start to whole chunks, so that reversed chunks coincide
     // with forward ones), with the decay of reversed step t' = a at forward
-    // step Lp - t' (zero where that is past the end).  A sequence of whole
-    // chunks needs no padding, and the kernels read (and write) the reversed
-    // problem in place; otherwise it is copied out reversed.
-    if (!rin) {
+    // step Lp - t' (zero where that is past the end).  Its chunk states give
+    // dX = G B, G being the state of the reversed problem (dy as X, C as B,
+    // B as C, dS_fin as its initial state); its final state is G_0.  A
+    // sequence of whole chunks needs no padding, and the kernels read (and
+    // write) the reversed problem in place, both state passes in one launch;
+    // otherwise it is copied out reversed.
+    if (rin) {
+        const ssd::StatePass pf{X, a, B, F(W_SFW), F(W_LAMFW), 0};
+        const ssd::StatePass pr{dYr, ar, Cr, F(W_SREV), F(W_LAMREV), 1};
+        SSD_TRY(ssd::launch_mfma_state_pair(s, 1, nc - 1, nc, pf, pr, hs), "bwd: chunk states");
+    } else {
+        SSD_TRY(ssd::launch_mfma_state(s, 1, nc - 1, nc, X, a, B, F(W_SFW), F(W_LAMFW), hs), "bwd: chunk states");
         SSD_TRY(ssd::launch_remap_rows(V(W_DYR), dY, Bz, Lp, L, Lp - 1, -1, H * P * es, hs), "bwd: reverse dY");
         SSD_TRY(ssd::launch_remap_rows(V(W_CR), C, Bz, Lp, L, Lp - 1, -1, G * N * es, hs), "bwd: reverse C");
         SSD_TRY(ssd::launch_remap_rows(V(W_BR), B, Bz, Lp, L, Lp - 1, -1, G * N * es, hs), "bwd: reverse B");
         SSD_TRY(ssd::launch_remap_a(F(W_AR), a, Bz, Lp, L, Lp, -1, H, 1, hs), "bwd: reverse a");
+        SSD_TRY(ssd::launch_mfma_state(bp.sr, 1, nc - 1, nc, dYr, ar, Cr, F(W_SREV), F(W_LAMREV), hs, false),
+                "bwd: adjoint chunk states");
     }
-    // 3. dX = G B, with G the state of the reversed problem (dy as X, C as B,
-    // B as C, dS_fin as its initial state); its final state is G_0
-    SSD_TRY(ssd::launch_mfma_state(bp.sr, 1, nc - 1, nc, dYr, ar, Cr, F(W_SREV), F(W_LAMREV), hs, rin),
-            "bwd: adjoint chunk states");
-    SSD_TRY(ssd::launch_state_scan(bp.sr, nc - 1, nc, F(W_SREV), F(W_LAMREV), H * nc, nc, dfinal_state,
-                                   F(W_SREV), 0, F(W_SREV) + (nc - 1) * H * PN, nc * H * PN, hs),
-            "bwd: adjoint state scan");
+    {
+        // both chunk-state scans (forward time from S0, reversed time from
+        // dS_fin) in one launch; each writes its last chunk's entering state
+        // into the last slot
+        const ssd::ScanJob jf{F(W_SFW), F(W_LAMFW), H * nc, nc, initial_state, F(W_SFW), 0,
+                              F(W_SFW) + (nc - 1) * H * PN, nc * H * PN};
+        const ssd::ScanJob jr{F(W_SREV), F(W_LAMREV), H * nc, nc, dfinal_state, F(W_SREV), 0,
+                              F(W_SREV) + (nc - 1) * H * PN, nc * H * PN};
+        SSD_TRY(ssd::launch_state_scan_pair(s, nc - 1, nc, jf, jr, hs), "bwd: state scans");
+    }
     {
         // the fused forward pass on the reversed problem, one chunk per segment
         ssd::StateSrc src{dfinal_state, H * PN, F(W_SREV), nc * H * PN, H * PN};
@@ -846,12 +855,11 @@ ssd_status ssd_chunk_scan_bwd(const ssd_fwd_desc* desc, const void* X, const flo
         const ssd::XgPass pc{B, a, X, dY, srcc, F(W_DCH), L, 0};
         const ssd::XgPass pb{Cr, ar, dYr, rin ? X : V(W_XR), srcb, F(W_DBH), Lp, rin ? 1 : 0};
         SSD_TRY(ssd::launch_mfma_out_xg_pair(sc, G, pc, pb, hs), "bwd: dC and dB passes");
-        SSD_TRY(ssd::launch_group_sum(dC, V(W_DCH), Bz, L, L, 0, 1, H, G, N, false, true, hs), "bwd: dC group sum");
-        if (rin)
-            SSD_TRY(ssd::launch_group_sum(dB, V(W_DBH), Bz, L, L, 0, 1, H, G, N, false, true, hs), "bwd: dB group sum");
-        else
-            SSD_TRY(ssd::launch_group_sum(dB, V(W_DBH), Bz, L, Lp, Lp - 1, -1, H, G, N, false, true, hs),
-                    "bwd: dB group sum");
+        // both group sums in one launch (dB's per-head rows are in reversed
+        // order when they were computed on a reversed copy)
+        const ssd::GsJob gc{dC, V(W_DCH), L, 0, 1};
+        const ssd::GsJob gb = rin ? ssd::GsJob{dB, V(W_DBH), L, 0, 1} : ssd::GsJob{dB, V(W_DBH), Lp, Lp - 1, -1};
+        SSD_TRY(ssd::launch_group_sum_pair(gc, gb, Bz, L, H, G, N, false, true, hs), "bwd: dC and dB group sums");
         return ok();
     }
     // 5. dC = S^T dy: forward-time product, state dimensions exchanged

@@ -107,25 +107,28 @@ __global__ void k_state_transpose(float* __restrict__ out, const float* __restri
 // piece) of a flat range over a batch's rows, the heads summed in order,
 // eight loads in flight
 template <typename TI, typename TO>
-__global__ __launch_bounds__(256) void k_group_sum(TO* __restrict__ out, const TI* __restrict__ in,
-                                                   int64_t Lout, int64_t Lin, int64_t off, int64_t dir,
-                                                   int H, int G, int N4)
+__global__ __launch_bounds__(256) void k_group_sum(GsJob j0, GsJob j1, int Bz, int64_t Lout, int H, int G,
+                                                   int N4)
 {
+    // blockIdx.y < Bz: job j0 for batch blockIdx.y; otherwise job j1 (a paired launch)
+    const bool second = (int)blockIdx.y >= Bz;
+    const GsJob j = second ? j1 : j0;
     const int64_t w = (int64_t)G * N4;
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= Lout * w) return;
-    const int64_t t = idx / w, b = blockIdx.y;
+    const int64_t t = idx / w, b = second ? (int64_t)blockIdx.y - Bz : (int64_t)blockIdx.y;
     const int k = (int)(idx - t * w);
     const int gi = k / N4, q = k - gi * N4;
     const int hpg = H / G;
     const int N = 4 * N4;
-    const int64_t s = off + dir * t;
+    const int64_t s = j.off + j.dir * t;
+    const TI* __restrict__ in = static_cast<const TI*>(j.in);
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    if (s >= 0 && s < Lin) {
-        const TI* src = in + ((b * Lin + s) * H + (int64_t)gi * hpg) * N + 4 * q;
+    if (s >= 0 && s < j.Lin) {
+        const TI* src = in + ((b * j.Lin + s) * H + (int64_t)gi * hpg) * N + 4 * q;
 #pragma unroll 8
-        for (int j = 0; j < hpg; ++j) {
-            const TI* p = src + (int64_t)j * N;
+        for (int jj = 0; jj < hpg; ++jj) {
+            const TI* p = src + (int64_t)jj * N;
             if constexpr (sizeof(TI) == 2) {
                 const uint2 v = *reinterpret_cast<const uint2*>(p);
                 acc[0] += __uint_as_float(v.x << 16);
@@ -138,7 +141,7 @@ __global__ __launch_bounds__(256) void k_group_sum(TO* __restrict__ out, const T
             }
         }
     }
-    TO* dst = out + ((b * Lout + t) * G + gi) * N + 4 * q;
+    TO* dst = static_cast<TO*>(j.out) + ((b * Lout + t) * G + gi) * N + 4 * q;
     if constexpr (sizeof(TO) == 2) {
         *reinterpret_cast<uint2*>(dst) =
             make_uint2((uint32_t)f32_to_bf_bits(acc[0]) | ((uint32_t)f32_to_bf_bits(acc[1]) << 16),
@@ -212,22 +215,39 @@ hipError_t launch_state_transpose(float* out, const float* in, int64_t BH, int64
     return hipGetLastError();
 }
 
-hipError_t launch_group_sum(void* out, const void* in, int64_t Bz, int64_t Lout, int64_t Lin,
-                            int64_t off, int64_t dir, int64_t H, int64_t G, int64_t N, bool in_bf16,
-                            bool out_bf16, hipStream_t st)
+static hipError_t launch_gs_jobs(const GsJob& j0, const GsJob& j1, int njobs, int64_t Bz, int64_t Lout,
+                                 int64_t H, int64_t G, int64_t N, bool in_bf16, bool out_bf16, hipStream_t st)
 {
     const int64_t N4 = N / 4, w = G * N4;
     if (Bz * Lout * w <= 0) return hipSuccess;
-    const dim3 grid((unsigned)((Lout * w + 255) / 256), (unsigned)Bz), block(256);
-#define SSD_GS(TI, TO)                                                                            \
-    hipLaunchKernelGGL((k_group_sum<TI, TO>), grid, block, 0, st, (TO*)out, (const TI*)in, Lout, Lin, \
-                       off, dir, (int)H, (int)G, (int)N4)
+    const dim3 grid((unsigned)((Lout * w + 255) / 256), (unsigned)(njobs * Bz)), block(256);
+#define SSD_GS(TI, TO)                                                                         \
+    hipLaunchKernelGGL((k_group_sum<TI, TO>), grid, block, 0, st, j0, j1, (int)Bz, Lout, (int)H, \
+                       (int)G, (int)N4)
     if (in_bf16 && out_bf16) SSD_GS(u16, u16);
     else if (!in_bf16 && out_bf16) SSD_GS(float, u16);
     else if (!in_bf16 && !out_bf16) SSD_GS(float, float);
     else return hipErrorInvalidValue;
 #undef SSD_GS
     return hipGetLastError();
+}
+
+hipError_t launch_group_sum(void* out, const void* in, int64_t Bz, int64_t Lout, int64_t Lin,
+                            int64_t off, int64_t dir, int64_t H, int64_t G, int64_t N, bool in_bf16,
+                            bool out_bf16, hipStream_t st)
+{
+    const GsJob j{out, in, Lin, off, dir};
+    return launch_gs_jobs(j, j, 1, Bz, Lout, H, G, N, in_bf16, out_bf16, st);
+}
+
+hipError_t launch_group_sum_pair(const GsJob& j0, const GsJob& j1, int64_t Bz, int64_t Lout, int64_t H,
+                                 int64_t G, int64_t N, bool in_bf16, bool out_bf16, hipStream_t st)
+{
+    if (2 * Bz > 65535) {   // keep grid.y within the 16-bit range: two launches
+        const hipError_t e = launch_gs_jobs(j0, j0, 1, Bz, Lout, H, G, N, in_bf16, out_bf16, st);
+        return e != hipSuccess ? e : launch_gs_jobs(j1, j1, 1, Bz, Lout, H, G, N, in_bf16, out_bf16, st);
+    }
+    return launch_gs_jobs(j0, j1, 2, Bz, Lout, H, G, N, in_bf16, out_bf16, st);
 }
 
 hipError_t launch_scale_state_by_a0(float* state, const float* a, int64_t Bz, int64_t L,

@@ -669,6 +669,24 @@ __global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(3
                                           Bz, x_groups, wg, nwg, p.rev);
 }
 
+// Two state-only passes in one launch (the backward's forward-time and
+// reversed-time chunk states): workgroups [0, grid0) run the first, the rest
+// the second.  Both share every size; grid0 is a multiple of the XCD count.
+template <int P, int N>
+__global__ __launch_bounds__(64 * (kStateWaves + 2)) __attribute__((amdgpu_waves_per_eu(2))) void k_mfma_state_pair(
+    StatePass p0, StatePass p1, unsigned grid0, int64_t nseg_total, int64_t L, int H, int G,
+    int64_t blocks_per_seg, int nseg_grid, int Bz)
+{
+    const bool second = blockIdx.x >= grid0;
+    const StatePass& p = second ? p1 : p0;
+    const unsigned wg = second ? blockIdx.x - grid0 : blockIdx.x;
+    const unsigned nwg = second ? gridDim.x - grid0 : grid0;
+    const StateSrc none{nullptr, 0, nullptr, 0, 0};
+    mfma_seg_body<P, N, false, false, kStateWaves>(static_cast<const u16*>(p.X), p.a, static_cast<const u16*>(p.B),
+                                                   nullptr, none, nullptr, nullptr, p.Sseg, p.lamseg, nseg_total, L,
+                                                   H, G, blocks_per_seg, nseg_grid, Bz, 0, wg, nwg, p.rev);
+}
+
 #define SSD_MFMA_DISPATCH(MACRO)                     \
     if (s.P == 64 && s.N == 128) MACRO(64, 128)      \
     else if (s.P == 64 && s.N == 64) MACRO(64, 64)   \
@@ -700,6 +718,21 @@ hipError_t launch_mfma_state(const FwdShape& s, int64_t seg_chunks, int64_t nseg
                        (int)s.H, (int)s.G, bps, (int)nseg_run, (int)s.Bz, 0, rev ? 1 : 0);
     SSD_MFMA_DISPATCH(SSD_LAUNCH_STATE)
 #undef SSD_LAUNCH_STATE
+    return hipGetLastError();
+}
+
+hipError_t launch_mfma_state_pair(const FwdShape& s, int64_t seg_chunks, int64_t nseg_run, int64_t nseg_total,
+                                  const StatePass& p0, const StatePass& p1, hipStream_t st)
+{
+    if (nseg_run <= 0) return hipSuccess;
+    if ((p0.rev || p1.rev) && s.L % kT != 0) return hipErrorInvalidValue;
+    const unsigned grid0 = grid_for(s, nseg_run);
+    const int64_t bps = seg_chunks * (s.Q / kT);
+#define SSD_LAUNCH_STATE_PAIR(PP, NN)                                                         \
+    hipLaunchKernelGGL((k_mfma_state_pair<PP, NN>), dim3(2 * grid0), dim3(kThreads), 0, st, p0, p1, \
+                       grid0, nseg_total, s.L, (int)s.H, (int)s.G, bps, (int)nseg_run, (int)s.Bz);
+    SSD_MFMA_DISPATCH(SSD_LAUNCH_STATE_PAIR)
+#undef SSD_LAUNCH_STATE_PAIR
     return hipGetLastError();
 }
 

@@ -412,30 +412,60 @@ hipError_t launch_chunk_cumsum(const FwdShape& s, const float* a, float* cs, flo
 // ---------------------------------------------------------------------------
 // Stage 4: sequential over units (chunks or segments), parallel over
 // (b, h, 4-float groups of the state).  Each thread streams its float4 of
-// every unit: read D_u, write the entering state, fold.
+// every unit: read D_u, write the entering state, fold.  The reads of a window
+// of kScanWin units are issued before any of its stores, so one memory round
+// trip covers the window (the entering states may overwrite D in place: a
+// thread writes only locations it has already read).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_state_scan(
-    const float* D, const float* __restrict__ lam, int64_t lam_bs, int64_t lam_hs,
-    const float* __restrict__ S0, float* Sout, int64_t u_write, float* __restrict__ fin,
-    int64_t fin_bs, int64_t nu, int64_t ustride, int H, int PN)
+constexpr int kScanWin = 8;
+
+__global__ __launch_bounds__(256) void k_state_scan(ScanJob j0, ScanJob j1, int Bz, int64_t nu,
+                                                    int64_t ustride, int H, int PN)
 {
-    const int h = blockIdx.y, b = blockIdx.z;
+    // blockIdx.z < Bz: job j0 for batch blockIdx.z; otherwise job j1 (a paired launch)
+    const bool second = (int)blockIdx.z >= Bz;
+    const ScanJob j = second ? j1 : j0;
+    const int h = blockIdx.y, b = second ? (int)blockIdx.z - Bz : (int)blockIdx.z;
     const int q = blockIdx.x * blockDim.x + threadIdx.x;  // float4 index
     if (q * 4 >= PN) return;
     const int64_t bh = (int64_t)b * H + h;
-    float4 S = S0 ? reinterpret_cast<const float4*>(S0 + bh * PN)[q] : make_float4(0.f, 0.f, 0.f, 0.f);
-    const float* lrow = lam + b * lam_bs + h * lam_hs;
-    for (int64_t u = 0; u < nu; ++u) {
-        const int64_t off = (((int64_t)b * ustride + u) * H + h) * PN;
-        const float4 d = reinterpret_cast<const float4*>(D + off)[q];
-        if (u >= u_write) reinterpret_cast<float4*>(Sout + off)[q] = S;
-        const float e = expf(lrow[u]);
-        S.x = e * S.x + d.x;
-        S.y = e * S.y + d.y;
-        S.z = e * S.z + d.z;
-        S.w = e * S.w + d.w;
+    float4 S = j.S0 ? reinterpret_cast<const float4*>(j.S0 + bh * PN)[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float* lrow = j.lam + b * j.lam_bs + h * j.lam_hs;
+    const int64_t ustep = (int64_t)H * PN;                       // floats between units
+    const int64_t base = ((int64_t)b * ustride * H + h) * PN;    // unit 0 of (b, h)
+    for (int64_t u0 = 0; u0 < nu; u0 += kScanWin) {
+        float4 d[kScanWin];
+        float l[kScanWin];
+#pragma unroll
+        for (int k = 0; k < kScanWin; ++k) {
+            if (u0 + k < nu) {
+                d[k] = reinterpret_cast<const float4*>(j.D + base + (u0 + k) * ustep)[q];
+                l[k] = lrow[u0 + k];
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kScanWin; ++k) {
+            const int64_t u = u0 + k;
+            if (u < nu) {
+                if (u >= j.u_write) reinterpret_cast<float4*>(j.Sout + base + u * ustep)[q] = S;
+                const float e = expf(l[k]);
+                S.x = e * S.x + d[k].x;
+                S.y = e * S.y + d[k].y;
+                S.z = e * S.z + d[k].z;
+                S.w = e * S.w + d[k].w;
+            }
+        }
     }
-    if (fin) reinterpret_cast<float4*>(fin + b * fin_bs + (int64_t)h * PN)[q] = S;
+    if (j.fin) reinterpret_cast<float4*>(j.fin + b * j.fin_bs + (int64_t)h * PN)[q] = S;
+}
+
+static hipError_t launch_scan_jobs(const FwdShape& s, int64_t nu, int64_t ustride, const ScanJob& j0,
+                                   const ScanJob& j1, int njobs, hipStream_t st)
+{
+    const int PN = (int)(s.P * s.N);
+    dim3 grid((unsigned)((PN / 4 + 255) / 256), (unsigned)s.H, (unsigned)(njobs * s.Bz));
+    hipLaunchKernelGGL(k_state_scan, grid, dim3(256), 0, st, j0, j1, (int)s.Bz, nu, ustride, (int)s.H, PN);
+    return hipGetLastError();
 }
 
 hipError_t launch_state_scan(const FwdShape& s, int64_t nu, int64_t ustride, const float* D,
@@ -444,11 +474,18 @@ hipError_t launch_state_scan(const FwdShape& s, int64_t nu, int64_t ustride, con
                              float* Sout, int64_t u_write, float* final_, int64_t final_bstride,
                              hipStream_t st)
 {
-    const int PN = (int)(s.P * s.N);
-    dim3 grid((unsigned)((PN / 4 + 255) / 256), (unsigned)s.H, (unsigned)s.Bz);
-    hipLaunchKernelGGL(k_state_scan, grid, dim3(256), 0, st, D, lam, lam_bstride, lam_hstride,
-                       S0, Sout, u_write, final_, final_bstride, nu, ustride, (int)s.H, PN);
-    return hipGetLastError();
+    const ScanJob j{D, lam, lam_bstride, lam_hstride, S0, Sout, u_write, final_, final_bstride};
+    return launch_scan_jobs(s, nu, ustride, j, j, 1, st);
+}
+
+hipError_t launch_state_scan_pair(const FwdShape& s, int64_t nu, int64_t ustride, const ScanJob& j0,
+                                  const ScanJob& j1, hipStream_t st)
+{
+    if (2 * s.Bz > 65535) {   // keep grid.z within the 16-bit range: two launches
+        const hipError_t e = launch_scan_jobs(s, nu, ustride, j0, j0, 1, st);
+        return e != hipSuccess ? e : launch_scan_jobs(s, nu, ustride, j1, j1, 1, st);
+    }
+    return launch_scan_jobs(s, nu, ustride, j0, j1, 2, st);
 }
 
 __global__ void k_fill_zero(float* p, int64_t n) {

@@ -49,6 +49,20 @@ hipError_t launch_state_scan(const FwdShape& s, int64_t nu, int64_t ustride, con
                              int64_t lam_bstride, int64_t lam_hstride, const float* S0,
                              float* Sout, int64_t u_write, float* final_, int64_t final_bstride,
                              hipStream_t st);
+// One scan of two independent state sequences of the same shape in one
+// launch (the backward's forward-time and reversed-time chunk states).
+struct ScanJob {
+    const float* D;
+    const float* lam;
+    int64_t lam_bs, lam_hs;
+    const float* S0;
+    float* Sout;
+    int64_t u_write;
+    float* fin;
+    int64_t fin_bs;
+};
+hipError_t launch_state_scan_pair(const FwdShape& s, int64_t nu, int64_t ustride, const ScanJob& j0,
+                                  const ScanJob& j1, hipStream_t st);
 
 // ---- MFMA segmented path (bf16) ----------------------------------------------------
 bool mfma_supported(int64_t Q, int64_t P, int64_t N);
@@ -63,6 +77,19 @@ hipError_t launch_mfma_state(const FwdShape& s, int64_t seg_chunks, int64_t nseg
                              int64_t nseg_total, const void* X, const float* a,
                              const void* B, float* Sseg, float* lamseg, hipStream_t st,
                              bool rev = false);
+// Two state-only passes of the same shape in one launch (the backward's
+// forward-time and reversed-time chunk states); each names its X, a and B
+// arrays, its outputs and whether it reads the time-reversed problem in place.
+struct StatePass {
+    const void* X;
+    const float* a;
+    const void* B;
+    float* Sseg;
+    float* lamseg;
+    int rev;
+};
+hipError_t launch_mfma_state_pair(const FwdShape& s, int64_t seg_chunks, int64_t nseg_run, int64_t nseg_total,
+                                  const StatePass& p0, const StatePass& p1, hipStream_t st);
 // The fused forward pass (kernels_fwd.hip): sw (4, 5 or 6) units -- 32-wide
 // head-dim slices of heads -- per workgroup, for every segment starting from
 // its entering state; writes Y and (last segment) the final state.  rev
@@ -128,6 +155,16 @@ hipError_t launch_state_transpose(float* out, const float* in, int64_t BH, int64
 hipError_t launch_group_sum(void* out, const void* in, int64_t Bz, int64_t Lout, int64_t Lin,
                             int64_t off, int64_t dir, int64_t H, int64_t G, int64_t N, bool in_bf16,
                             bool out_bf16, hipStream_t st);
+// Two group sums of the same output shape in one launch (the backward's dB
+// and dC): each job names its output, its input, the input's length and its
+// row map (input row off + dir * t for output row t).
+struct GsJob {
+    void* out;
+    const void* in;
+    int64_t Lin, off, dir;
+};
+hipError_t launch_group_sum_pair(const GsJob& j0, const GsJob& j1, int64_t Bz, int64_t Lout, int64_t H,
+                                 int64_t G, int64_t N, bool in_bf16, bool out_bf16, hipStream_t st);
 // state[b][h][:] *= exp(a[b][0][h])
 hipError_t launch_scale_state_by_a0(float* state, const float* a, int64_t Bz, int64_t L,
                                     int64_t H, int64_t PN, hipStream_t st);

@@ -28,8 +28,12 @@ hipError_t launch_valu_fwd(const FwdShape&, bool, const void*, const float*, con
 hipError_t launch_chunk_cumsum(const FwdShape&, const float*, float*, float*, hipStream_t) { SSD_STUB; }
 hipError_t launch_state_scan(const FwdShape&, int64_t, int64_t, const float*, const float*, int64_t,
                              int64_t, const float*, float*, int64_t, float*, int64_t, hipStream_t) { SSD_STUB; }
+hipError_t launch_state_scan_pair(const FwdShape&, int64_t, int64_t, const ScanJob&, const ScanJob&,
+                                  hipStream_t) { SSD_STUB; }
 hipError_t launch_mfma_state(const FwdShape&, int64_t, int64_t, int64_t, const void*, const float*,
                              const void*, float*, float*, hipStream_t, bool) { SSD_STUB; }
+hipError_t launch_mfma_state_pair(const FwdShape&, int64_t, int64_t, int64_t, const StatePass&,
+                                  const StatePass&, hipStream_t) { SSD_STUB; }
 hipError_t launch_fwd(const FwdShape&, int, int64_t, int64_t, const void*, const float*, const void*,
                       const void*, StateSrc, void*, float*, hipStream_t, bool, const float*,
                       int64_t) { SSD_STUB; }
@@ -47,6 +51,8 @@ hipError_t launch_remap_a(float*, const float*, int64_t, int64_t, int64_t, int64
 hipError_t launch_state_transpose(float*, const float*, int64_t, int64_t, int64_t, hipStream_t) { SSD_STUB; }
 hipError_t launch_group_sum(void*, const void*, int64_t, int64_t, int64_t, int64_t, int64_t, int64_t,
                             int64_t, int64_t, bool, bool, hipStream_t) { SSD_STUB; }
+hipError_t launch_group_sum_pair(const GsJob&, const GsJob&, int64_t, int64_t, int64_t, int64_t, int64_t, bool,
+                                 bool, hipStream_t) { SSD_STUB; }
 hipError_t launch_scale_state_by_a0(float*, const float*, int64_t, int64_t, int64_t, int64_t,
                                     hipStream_t) { SSD_STUB; }
 hipError_t launch_bwd_da_valu(const FwdShape&, const float*, const float*, const float*, const float*,
