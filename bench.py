@@ -162,15 +162,27 @@ def warm(fn, min_steps, min_ms=30.0):
 
 
 def time_events(fn, steps):
+    """Seconds for `steps` calls of fn, between HIP events on the current
+    stream.  One untimed call is queued ahead of the first event, so that a
+    host-side pause at the first launch after the synchronisation lands
+    outside the timed region; the garbage collector is held off meanwhile
+    (not run first: a collection idles the GPU long enough for its clocks to
+    drop before the timed calls)."""
+    import gc
     import torch
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for i in range(steps):
-        fn(i)
-    e1.record()
-    torch.cuda.synchronize()
+    gc.disable()
+    try:
+        torch.cuda.synchronize()
+        fn(steps)
+        e0.record()
+        for i in range(steps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+    finally:
+        gc.enable()
     return e0.elapsed_time(e1) / 1e3  # seconds
 
 
@@ -329,14 +341,15 @@ def bwd_algo_flops_per_token(sh, block=KERNEL_BLOCK):
     time-reversed forward for dX (same flops as the forward), the dC and dB
     passes (the forward with headdim and state exchanged, the state split into
     64-wide sub-heads), the per-chunk states of the forward and of the reversed
-    problem, and the da kernel (per chunk Q: the lower triangle of 32x32 tiles
-    of dY X^T and C B^T per head, plus C S_in^T and B R^T)."""
+    problem, and the da stage (per chunk Q: the lower triangle of 32x32 tiles
+    of C B^T per group and of dY X^T per head, plus C S_in^T and B R^T)."""
     import dataclasses
-    P, N, H, Q = sh.headdim, sh.dstate, sh.nheads, sh.chunk
+    P, N, H, G, Q = sh.headdim, sh.dstate, sh.nheads, sh.ngroups, sh.chunk
     ns = N // 64
     swapped = dataclasses.replace(sh, nheads=H * ns, headdim=N // ns, dstate=P, ngroups=H)
     nI = Q // 32
-    da = H * ((nI * (nI + 1) // 2) * 32 * 32 * 2 * (P + N) + 2 * 2 * Q * P * N) / Q
+    tiles = nI * (nI + 1) // 2
+    da = (G * tiles * 32 * 32 * 2 * N + H * (tiles * 32 * 32 * 2 * P + 2 * 2 * Q * P * N)) / Q
     states = 2 * 2 * N * P * H   # chunk states of the forward and of the reversed problem
     return fwd_algo_flops_per_token(sh, block) + 2 * fwd_algo_flops_per_token(swapped, block) + da + states
 
@@ -376,28 +389,31 @@ def bench_backward(sh, steps, warmup, nbatch, seed0=100):
     Sin = 0.1 * torch.randn(st_shape, device="cuda")
     Adj = 0.1 * torch.randn(st_shape, device="cuda")
     da = torch.empty_like(g0["a"])
+    wsda = torch.empty(ssd.bwd_da_workspace_bytes(g0["X"], g0["B"], sh.chunk), dtype=torch.uint8, device="cuda")
 
     def da_step(i):
         g = batches[i % nbatch]
-        ssd.bwd_da(g["X"], g["a"], g["B"], g["C"], g["dY"], sh.chunk, Sin, Adj, da=da)
+        ssd.bwd_da(g["X"], g["a"], g["B"], g["C"], g["dY"], sh.chunk, Sin, Adj, da=da, workspace=wsda)
 
     for i in range(warmup):
         da_step(i)
     t_da = time_events(da_step, steps) / steps
-    del batches, ws, Sin, Adj, da
+    del batches, ws, Sin, Adj, da, wsda
     torch.cuda.empty_cache()
     return t, t_da
 
 
 def bwd_da_work(sh):
-    """(MFMA flops, algorithmic HBM bytes) of one da-kernel launch: per chunk
-    and head the lower-triangle 32x32 tiles of dY X^T (K = P) and C B^T (K = N)
-    plus C S_in^T and B R^T; X, dY, B, C, a and the two fp32 chunk-state
-    arrays in, da out."""
+    """(MFMA flops, algorithmic HBM bytes) of one call of the da stage (the
+    C B^T tile kernel and the da kernel): per chunk and group the
+    lower-triangle 32x32 tiles of C B^T (K = N), per chunk and head those of
+    dY X^T (K = P) plus C S_in^T and B R^T; X, dY, B, C, a and the two fp32
+    chunk-state arrays in, da out."""
     P, N, H, G, Q = sh.headdim, sh.dstate, sh.nheads, sh.ngroups, sh.chunk
     nc = (sh.seqlen + Q - 1) // Q
     nI = Q // 32
-    flops = sh.batch * nc * H * ((nI * (nI + 1) // 2) * 32 * 32 * 2 * (P + N) + 2 * 2 * Q * P * N)
+    tiles = nI * (nI + 1) // 2
+    flops = sh.batch * nc * (G * tiles * 32 * 32 * 2 * N + H * (tiles * 32 * 32 * 2 * P + 2 * 2 * Q * P * N))
     tok = sh.batch * sh.seqlen
     nbytes = tok * (2 * H * P * 2 + 2 * G * N * 2 + 2 * H * 4) + 2 * sh.batch * nc * H * P * N * 4
     return flops, nbytes
@@ -585,7 +601,7 @@ def main():
             "ms_per_step": tb * 1e3, "tokens_per_s": tokens130 / tb, "bwd_over_fwd": tb * 1e3 / fwd130,
             "mfma_frac": fl / tb / 1e12 / BF16_PEAK_TFLOPS, "algo_flops_per_step": fl,
             # its dominant kernel, timed alone with HIP events
-            "dominant_kernel": {"kernel": "k_bwd_da", "us": tda * 1e6,
+            "dominant_kernel": {"kernel": "k_bwd_da (with k_cb_tiles: the da stage)", "us": tda * 1e6,
                                 "mfma": {"achieved": dfl / tda / 1e12, "peak": BF16_PEAK_TFLOPS,
                                          "unit": "TFLOP/s", "frac": dfl / tda / 1e12 / BF16_PEAK_TFLOPS},
                                 "hbm": {"achieved": dby / tda / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -197,11 +197,16 @@ ssd_status ssd_chunk_scan_bwd(const ssd_fwd_desc* desc, const void* X, const flo
  *        + exp(Lam) <R, S_in>
  * over the chunk's steps (cs the chunk's prefix sums of a, Lam its total).
  * This equals da of ssd_chunk_scan_bwd when the states are the true ones.
- * Shapes and supported sizes as for ssd_chunk_scan_bwd; da must not overlap
- * an input. */
+ * Shapes and supported sizes as for ssd_chunk_scan_bwd (bf16 only).  The
+ * workspace (16-byte aligned, at least ssd_bwd_da_workspace_bytes bytes,
+ * contents on entry ignored) receives the chunks' C_i.B_j tiles, which the
+ * heads of a group share: batch * nchunks * ngroups * T(T+1)/2 * 4 KiB with
+ * T = chunk / 32.  da must not overlap an input or the workspace. */
+ssd_status ssd_bwd_da_workspace_bytes(const ssd_fwd_desc* desc, size_t* bytes);
 ssd_status ssd_bwd_da(const ssd_fwd_desc* desc, const void* X, const float* a, const void* B,
                       const void* C, const void* dY, const float* states_in,
-                      const float* adjoint_in, float* da, void* stream);
+                      const float* adjoint_in, float* da, void* workspace, size_t workspace_bytes,
+                      void* stream);
 
 /* ---- Stage entry points (the same kernels' building blocks, exposed so
  * each stage can be checked and timed on its own).  bf16 MFMA path only,

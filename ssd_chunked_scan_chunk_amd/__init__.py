@@ -23,7 +23,7 @@ from . import _lib
 from ._lib import (SSD_ALGO_AUTO, SSD_ALGO_MFMA, SSD_ALGO_VALU, SSD_BF16, SSD_F32,
                    SSDError)
 
-__all__ = ["chunk_scan_fwd", "chunk_scan_fwd_noalloc", "chunk_scan_bwd", "bwd_workspace_bytes", "bwd_da", "step", "stream_rmw", "chunk_cumsum", "chunk_state", "state_passing",
+__all__ = ["chunk_scan_fwd", "chunk_scan_fwd_noalloc", "chunk_scan_bwd", "bwd_workspace_bytes", "bwd_da_workspace_bytes", "bwd_da", "step", "stream_rmw", "chunk_cumsum", "chunk_state", "state_passing",
            "chunk_scan", "fwd_plan", "workspace_bytes", "SSDError", "SSD_ALGO_AUTO",
            "SSD_ALGO_MFMA", "SSD_ALGO_VALU", "library_path"]
 
@@ -232,10 +232,18 @@ def chunk_scan_bwd(X, a, B, C, dY, chunk, initial_state=None, dfinal_state=None,
     return {"dX": dX, "da": da, "dB": dB, "dC": dC, "dinitial_state": dS0}
 
 
-def bwd_da(X, a, B, C, dY, chunk, states_in, adjoint_in, da=None):
+def bwd_da_workspace_bytes(X, B, chunk) -> int:
+    d = _desc(X, B, chunk, SSD_ALGO_AUTO, 0)
+    n = ctypes.c_size_t()
+    _lib.check(_L().ssd_bwd_da_workspace_bytes(ctypes.byref(d), ctypes.byref(n)))
+    return n.value
+
+
+def bwd_da(X, a, B, C, dY, chunk, states_in, adjoint_in, da=None, workspace=None):
     """The backward's da stage alone, from the states entering each chunk and
     the adjoint dl/dS at the first step of each next chunk (dS_fin for the
-    last), both [Bz, nchunks, H, P, N] float32."""
+    last), both [Bz, nchunks, H, P, N] float32.  The workspace (uint8, at
+    least bwd_da_workspace_bytes) is allocated when not given."""
     Bz, L, H, P, G, N = _check_fwd_inputs(X, a, B, C)
     dev = X.device
     _check("dY", dY, X.shape, X.dtype, dev)
@@ -248,8 +256,15 @@ def bwd_da(X, a, B, C, dY, chunk, states_in, adjoint_in, da=None):
     d = _desc(X, B, chunk, SSD_ALGO_AUTO, 0)
     if da is None:
         da = torch.empty_like(a)
+    nws = ctypes.c_size_t()
+    _lib.check(_L().ssd_bwd_da_workspace_bytes(ctypes.byref(d), ctypes.byref(nws)))
+    _check_bytes("workspace", workspace, nws.value, dev)
+    if workspace is None and nws.value > 0:
+        workspace = torch.empty(nws.value, dtype=torch.uint8, device=dev)
+    wsz = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _lib.check(_L().ssd_bwd_da(ctypes.byref(d), _ptr(X), _ptr(a), _ptr(B), _ptr(C), _ptr(dY),
-                               _ptr(states_in), _ptr(adjoint_in), _ptr(da), _stream(X.device)))
+                               _ptr(states_in), _ptr(adjoint_in), _ptr(da), _ptr(workspace), wsz,
+                               _stream(X.device)))
     return da
 
 

@@ -332,6 +332,7 @@ enum BwdBuf {
     W_BEXP, W_AEXP, W_S0T, W_DCH,     // dC pass: B per head, a per sub-head, S0^T, output
     W_CREXP, W_XR, W_AREXP, W_DSFT, W_DBH,   // dB pass (reversed)
     W_INNER,              // workspace of the dC / dB passes
+    W_CBT,                // C B^T tiles of every chunk for the da kernel
     kBwdBufs
 };
 
@@ -371,10 +372,16 @@ ssd_status make_bwd_plan(const ssd_fwd_desc* d, BwdPlan* bp) {
                         (long long)s.Q, (long long)s.P, (long long)s.N);
     }
     // the chunk-state and dX passes launch up to batch*chunks*heads workgroups,
-    // the exchanged-dimension passes up to batch*chunks*(heads+groups), each of
-    // at most kMfmaThreads threads
-    if ((s.Bz * s.nc * (s.H + s.G) + 8) * kMfmaThreads >= ((int64_t)1 << 32) || s.nc > 0x7fffffff)
+    // the exchanged-dimension passes up to batch*chunks*(heads+groups), the
+    // paired chunk-state passes with the C B^T tiles up to
+    // batch*chunks*(2/3 heads + 7 groups) (plus XCD padding), each of at most
+    // kMfmaThreads threads
+    if ((s.Bz * s.nc * (s.H + 8 * s.G) + 24) * kMfmaThreads >= ((int64_t)1 << 32) || s.nc > 0x7fffffff)
         return fail(SSD_ERR_UNSUPPORTED, "batch*chunks*heads too large for one launch");
+    // the C B^T tile kernel launches batch * chunks * groups * ceil(T(T+1)/8)
+    // workgroups of 256 threads (T = chunk / 32, at most 8)
+    if (!bp->f32 && s.Bz * s.nc * s.G * 9 * 256 >= ((int64_t)1 << 32))
+        return fail(SSD_ERR_UNSUPPORTED, "batch*chunks*groups too large for the C B^T tile kernel");
     // the copy kernels launch (row blocks of up to 256 threads) x steps blocks
     const int64_t row_items = s.H * (s.N > s.P ? s.N : s.P) * bp->es / 16;
     if (s.nc * s.Q * (((row_items + 255) / 256) * 256) >= ((int64_t)1 << 31))
@@ -425,6 +432,7 @@ ssd_status make_bwd_plan(const ssd_fwd_desc* d, BwdPlan* bp) {
             bytes[W_DSFT] = bytes[W_S0T];
             bytes[W_INNER] = (int64_t)(bp->pc.ws > bp->pb.ws ? bp->pc.ws : bp->pb.ws);
         }
+        if (!bp->f32) bytes[W_CBT] = ssd::cb_tiles_bytes(s);
     }
     size_t o = 0;
     for (int i = 0; i < kBwdBufs; ++i) {
@@ -799,11 +807,15 @@ ssd_status ssd_chunk_scan_bwd(const ssd_fwd_desc* desc, const void* X, const flo
     // sequence of whole chunks needs no padding, and the kernels read (and
     // write) the reversed problem in place, both state passes in one launch;
     // otherwise it is copied out reversed.
+    // (the da kernel's C B^T tiles, shared by each group's heads, are formed
+    // in the same launch as the state passes or in one of their own)
+    const ssd::CbJob cbj{B, C, F(W_CBT), L, nc, (int)Bz, (int)G, (int)s.Q, (int)N};
     if (rin) {
         const ssd::StatePass pf{X, a, B, F(W_SFW), F(W_LAMFW), 0};
         const ssd::StatePass pr{dYr, ar, Cr, F(W_SREV), F(W_LAMREV), 1};
-        SSD_TRY(ssd::launch_mfma_state_pair(s, 1, nc - 1, nc, pf, pr, hs), "bwd: chunk states");
+        SSD_TRY(ssd::launch_mfma_state_pair(s, 1, nc - 1, nc, pf, pr, cbj, hs), "bwd: chunk states");
     } else {
+        SSD_TRY(ssd::launch_cb_tiles(cbj, hs), "bwd: C B^T tiles");
         SSD_TRY(ssd::launch_mfma_state(s, 1, nc - 1, nc, X, a, B, F(W_SFW), F(W_LAMFW), hs), "bwd: chunk states");
         SSD_TRY(ssd::launch_remap_rows(V(W_DYR), dY, Bz, Lp, L, Lp - 1, -1, H * P * es, hs), "bwd: reverse dY");
         SSD_TRY(ssd::launch_remap_rows(V(W_CR), C, Bz, Lp, L, Lp - 1, -1, G * N * es, hs), "bwd: reverse C");
@@ -835,7 +847,7 @@ ssd_status ssd_chunk_scan_bwd(const ssd_fwd_desc* desc, const void* X, const flo
     if (!rin)
         SSD_TRY(ssd::launch_remap_rows(dX, V(W_DXR), Bz, L, Lp, Lp - 1, -1, H * P * es, hs), "bwd: dX order");
     // 4. da from the chunk-local four-term form
-    SSD_TRY(ssd::launch_bwd_da(s, X, dY, a, B, C, F(W_SFW), F(W_SREV), true, da, hs), "bwd: da");
+    SSD_TRY(ssd::launch_bwd_da(s, X, dY, a, B, C, F(W_SFW), F(W_SREV), F(W_CBT), true, da, hs), "bwd: da");
     }
     if (bp.xg) {
         // 5-6. dC = S^T dy and dB = G^T x: the products with the state's two
@@ -885,9 +897,20 @@ ssd_status ssd_chunk_scan_bwd(const ssd_fwd_desc* desc, const void* X, const flo
     return ok();
 }
 
+ssd_status ssd_bwd_da_workspace_bytes(const ssd_fwd_desc* desc, size_t* bytes) {
+    if (!bytes) return fail(SSD_ERR_NULL, "bytes is NULL");
+    BwdPlan bp;
+    ssd_status st = make_bwd_plan(desc, &bp);
+    if (st != SSD_OK) return st;
+    if (bp.f32) return fail(SSD_ERR_UNSUPPORTED, "the da stage entry point runs the bf16 MFMA kernel");
+    *bytes = (size_t)ssd::cb_tiles_bytes(bp.s);
+    return ok();
+}
+
 ssd_status ssd_bwd_da(const ssd_fwd_desc* desc, const void* X, const float* a, const void* B,
                       const void* C, const void* dY, const float* states_in,
-                      const float* adjoint_in, float* da, void* stream) {
+                      const float* adjoint_in, float* da, void* workspace, size_t workspace_bytes,
+                      void* stream) {
     BwdPlan bp;
     ssd_status st = make_bwd_plan(desc, &bp);
     if (st != SSD_OK) return st;
@@ -900,16 +923,27 @@ ssd_status ssd_bwd_da(const ssd_fwd_desc* desc, const void* X, const float* a, c
     for (const void* q : v16)
         if (!aligned(q, 16)) return fail(SSD_ERR_ALIGN, "X, B, C, dY and the state arrays must be 16-byte aligned");
     if (!aligned(a, 4) || !aligned(da, 4)) return fail(SSD_ERR_ALIGN, "a / da misaligned");
+    const size_t need = (size_t)ssd::cb_tiles_bytes(s);
+    if (!workspace || workspace_bytes < need)
+        return fail(SSD_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need, workspace_bytes,
+                    workspace ? "" : ", NULL");
+    if (!aligned(workspace, 16)) return fail(SSD_ERR_ALIGN, "workspace is not 16-byte aligned");
     const int64_t nX = s.Bz * s.L * s.H * s.P * 2, nBC = s.Bz * s.L * s.G * s.N * 2;
     const int64_t nSt = s.Bz * s.nc * s.H * s.P * s.N * 4, nA = s.Bz * s.L * s.H * 4;
     const Range ins[] = {rng("X", X, nX), rng("a", a, nA), rng("B", B, nBC), rng("C", C, nBC),
                          rng("dY", dY, nX), rng("states_in", states_in, nSt),
                          rng("adjoint_in", adjoint_in, nSt)};
-    const Range o = rng("da", da, nA);
-    for (const Range& r : ins)
-        if (overlap(o, r)) return fail(SSD_ERR_ALIAS, "da overlaps %s", r.name);
-    hipError_t e = ssd::launch_bwd_da(s, X, dY, a, B, C, states_in, adjoint_in, false, da,
-                                      reinterpret_cast<hipStream_t>(stream));
+    const Range outs[] = {rng("da", da, nA), rng("workspace", workspace, (int64_t)need)};
+    for (const Range& o : outs)
+        for (const Range& r : ins)
+            if (overlap(o, r)) return fail(SSD_ERR_ALIAS, "%s overlaps %s", o.name, r.name);
+    if (overlap(outs[0], outs[1])) return fail(SSD_ERR_ALIAS, "da overlaps workspace");
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    float* cbt = static_cast<float*>(workspace);
+    const ssd::CbJob cbj{B, C, cbt, s.L, s.nc, (int)s.Bz, (int)s.G, (int)s.Q, (int)s.N};
+    hipError_t e = ssd::launch_cb_tiles(cbj, hs);
+    if (e != hipSuccess) return hip_fail(e, "C B^T tiles launch");
+    e = ssd::launch_bwd_da(s, X, dY, a, B, C, states_in, adjoint_in, cbt, false, da, hs);
     if (e != hipSuccess) return hip_fail(e, "da launch");
     return ok();
 }

@@ -351,8 +351,8 @@ template <int P, int N>
 __global__ __launch_bounds__(kDaThreads) void k_bwd_da(
     const u16* __restrict__ X, const u16* __restrict__ dY, const float* __restrict__ a,
     const u16* __restrict__ Bm, const u16* __restrict__ Cm, const float* __restrict__ Sin,
-    const float* __restrict__ Srev, float* __restrict__ da, int64_t L, int H, int G, int Q,
-    int64_t nc, int adj_reversed)
+    const float* __restrict__ Srev, const float* __restrict__ cbt, float* __restrict__ da, int64_t L,
+    int H, int G, int Q, int64_t nc, int adj_reversed)
 {
     constexpr int XPR = P / 8, BPR = N / 8;   // 16-byte pieces per row
     constexpr int PN = P * N;
@@ -418,7 +418,6 @@ __global__ __launch_bounds__(kDaThreads) void k_bwd_da(
         }
     };
     stage_rows(sX, X + (((int64_t)b * L + t0) * H + h) * P, (int64_t)H * P, std::integral_constant<int, XPR>{});
-    stage_rows(sB, Bm + (((int64_t)b * L + t0) * G + g) * N, (int64_t)G * N, std::integral_constant<int, BPR>{});
     __syncthreads();
 
     auto frag = [&](const u16* tile, auto pr, int row, int ks) {   // row `row`, k = 16ks + 8g2 .. +7
@@ -446,31 +445,60 @@ __global__ __launch_bounds__(kDaThreads) void k_bwd_da(
         }
     };
 
+    auto load_dy = [&](int I, u32x4_b (&dyu)[P / 16]) {
+        const int irow = 32 * I + l32;
+        const bool iok = irow < Lc;
+        const int64_t tr = (int64_t)b * L + t0 + irow;
+#pragma unroll
+        for (int ks = 0; ks < P / 16; ++ks) {
+            u32x4_b v = {0u, 0u, 0u, 0u};
+            if (iok) v = *reinterpret_cast<const u32x4_b*>(dY + (tr * H + h) * P + 16 * ks + 8 * g2);
+            dyu[ks] = v;
+        }
+    };
+
     // ================= the masked term =================
+    // C B^T tiles of the chunk (shared by the group's heads) in the MFMA
+    // accumulator layout (kernels_mfma.hip, cb_tile): tile (I, J) at index
+    // I(I+1)/2 + J, 16 floats per lane
+    // (the workgroup's tile offset is formed on the vector unit: as a 64-bit
+    // scalar product it cost the scalar file a spill slot)
+    int cbi;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(cbi) : "s"((int)(((int64_t)b * nc + c) * G + g)));
+    const float* cbase = cbt + (int64_t)cbi * (nI * (nI + 1) / 2 * 1024) + lane * 16;
+    auto load_cb = [&](int I, int J) {
+        const float4* q = reinterpret_cast<const float4*>(cbase + (int64_t)(I * (I + 1) / 2 + J) * 1024);
+        f32x16_b v;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float4 w = q[k];
+            v[4 * k] = w.x; v[4 * k + 1] = w.y; v[4 * k + 2] = w.z; v[4 * k + 3] = w.w;
+        }
+        return v;
+    };
     for (int pass = 0; pass < 2; ++pass) {
         const int I = pass == 0 ? wq : 7 - wq;   // (never the same tile twice: wq <= 3)
         if (I >= nI || 32 * I >= Lc) continue;
         u32x4_b dyu[P / 16];
-        bf16x8 cf[N / 16];
-        load_rows(I, dyu, cf);
+        load_dy(I, dyu);
+        f32x16_b CBn = par <= I ? load_cb(I, par) : zero16b();
         float csI[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) csI[r] = sCs[32 * I + acc_row(r, g2)] * kLog2e;
 
         f32x16_b Mrow = zero16b();
         for (int J = par; J <= I; J += 2) {
-            // the column tile's operand fragments, all read before the first MFMA
-            bf16x8 xb[P / 16], bb[N / 16];
+            // this tile's C B^T, the next one's requested a tile ahead; the
+            // column tile's X fragments, all read before the first MFMA
+            const f32x16_b CB = CBn;
+            if (J + 2 <= I) CBn = load_cb(I, J + 2);
+            bf16x8 xb[P / 16];
 #pragma unroll
             for (int ks = 0; ks < P / 16; ++ks) xb[ks] = frag(sX, XP{}, 32 * J + l32, ks);
-#pragma unroll
-            for (int ks = 0; ks < N / 16; ++ks) bb[ks] = frag(sB, BP{}, 32 * J + l32, ks);
             __builtin_amdgcn_sched_barrier(0);   // (keep the reads ahead of the MFMA chain)
-            f32x16_b DX = zero16b(), CB = zero16b();
+            f32x16_b DX = zero16b();
 #pragma unroll
             for (int ks = 0; ks < P / 16; ++ks) DX = mfma32b(__builtin_bit_cast(bf16x8, dyu[ks]), xb[ks], DX);
-#pragma unroll
-            for (int ks = 0; ks < N / 16; ++ks) CB = mfma32b(cf[ks], bb[ks], CB);
             const float csj = sCs[32 * J + l32] * kLog2e;
             f32x16_b M;
             if (J < I) {
@@ -527,7 +555,7 @@ __global__ __launch_bounds__(kDaThreads) void k_bwd_da(
         }
         wave_lds_sync();
     }
-    __syncthreads();   // B's LDS tile is free
+    __syncthreads();   // B's LDS tile (not used by the masked term) takes the split states
 
     // ---- entering state S_in and the adjoint entering from the right,
     // R = exp(a at the next chunk's first step) G there (dS_fin for the last
@@ -819,13 +847,13 @@ hipError_t launch_bwd_da_valu(const FwdShape& s, const float* X, const float* dY
 
 hipError_t launch_bwd_da(const FwdShape& s, const void* X, const void* dY, const float* a,
                          const void* B, const void* C, const float* Sin, const float* Srev,
-                         bool adj_reversed, float* da, hipStream_t st)
+                         const float* cbt, bool adj_reversed, float* da, hipStream_t st)
 {
     if (s.Bz == 0 || s.L == 0) return hipSuccess;
     const dim3 grid((unsigned)s.nc, (unsigned)s.H, (unsigned)s.Bz);
 #define SSD_LAUNCH_DA(PP, NN)                                                                    \
     hipLaunchKernelGGL((k_bwd_da<PP, NN>), grid, dim3(kDaThreads), 0, st, (const u16*)X,          \
-                       (const u16*)dY, a, (const u16*)B, (const u16*)C, Sin, Srev, da, s.L,      \
+                       (const u16*)dY, a, (const u16*)B, (const u16*)C, Sin, Srev, cbt, da, s.L, \
                        (int)s.H, (int)s.G, (int)s.Q, s.nc, adj_reversed ? 1 : 0);
     if (s.P == 64 && s.N == 128) SSD_LAUNCH_DA(64, 128)
     else if (s.P == 64 && s.N == 64) SSD_LAUNCH_DA(64, 64)

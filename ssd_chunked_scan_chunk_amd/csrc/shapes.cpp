@@ -30,4 +30,11 @@ bool bwd_da_supported(int64_t Q, int64_t P, int64_t N) {
     return (Q == 64 || Q == 128 || Q == 256) && (P == 32 || P == 64) && (N == 64 || N == 128);
 }
 
+// bytes of the da kernel's C B^T tiles: every (batch, chunk, group) holds the
+// T(T+1)/2 lower-triangle 32x32 fp32 tiles of its chunk, T = chunk / 32
+int64_t cb_tiles_bytes(const FwdShape& s) {
+    const int64_t nI = s.Q / 32;
+    return s.Bz * s.nc * s.G * (nI * (nI + 1) / 2) * 1024 * 4;
+}
+
 }  // namespace ssd

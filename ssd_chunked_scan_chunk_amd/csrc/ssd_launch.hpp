@@ -88,8 +88,21 @@ struct StatePass {
     float* lamseg;
     int rev;
 };
+// The C B^T tiles of the backward's da kernel: for every (batch, chunk,
+// group) the lower-triangle 32x32 fp32 tiles of C_I B_J^T (cb_tiles_bytes
+// bytes at cbt; N and Q as the layer's).
+struct CbJob {
+    const void* B;
+    const void* C;
+    float* cbt;
+    int64_t L, nc;
+    int Bz, G, Q, N;
+};
+hipError_t launch_cb_tiles(const CbJob& j, hipStream_t st);
+// ... and the two passes together with the C B^T tiles (of the same shape)
+// in the same launch.
 hipError_t launch_mfma_state_pair(const FwdShape& s, int64_t seg_chunks, int64_t nseg_run, int64_t nseg_total,
-                                  const StatePass& p0, const StatePass& p1, hipStream_t st);
+                                  const StatePass& p0, const StatePass& p1, const CbJob& cb, hipStream_t st);
 // The fused forward pass (kernels_fwd.hip): sw (4, 5 or 6) units -- 32-wide
 // head-dim slices of heads -- per workgroup, for every segment starting from
 // its entering state; writes Y and (last segment) the final state.  rev
@@ -177,9 +190,12 @@ bool bwd_da_supported(int64_t Q, int64_t P, int64_t N);
 hipError_t launch_bwd_da_valu(const FwdShape& s, const float* X, const float* dY, const float* a,
                               const float* B, const float* C, const float* Sin, const float* Srev,
                               float* da, hipStream_t st);
+// C B^T tiles of every (batch, chunk, group) for the da kernel:
+// cb_tiles_bytes(s) bytes of fp32 at cbt.
+int64_t cb_tiles_bytes(const FwdShape& s);
 hipError_t launch_bwd_da(const FwdShape& s, const void* X, const void* dY, const float* a,
                          const void* B, const void* C, const float* Sin, const float* Srev,
-                         bool adj_reversed, float* da, hipStream_t st);
+                         const float* cbt, bool adj_reversed, float* da, hipStream_t st);
 
 // The forward of the C ABI with a fixed workspace region of ws_cap bytes
 // (api.cpp): plans within the cap, validates every argument on the host, then

@@ -33,7 +33,7 @@ hipError_t launch_state_scan_pair(const FwdShape&, int64_t, int64_t, const ScanJ
 hipError_t launch_mfma_state(const FwdShape&, int64_t, int64_t, int64_t, const void*, const float*,
                              const void*, float*, float*, hipStream_t, bool) { SSD_STUB; }
 hipError_t launch_mfma_state_pair(const FwdShape&, int64_t, int64_t, int64_t, const StatePass&,
-                                  const StatePass&, hipStream_t) { SSD_STUB; }
+                                  const StatePass&, const CbJob&, hipStream_t) { SSD_STUB; }
 hipError_t launch_fwd(const FwdShape&, int, int64_t, int64_t, const void*, const float*, const void*,
                       const void*, StateSrc, void*, float*, hipStream_t, bool, const float*,
                       int64_t) { SSD_STUB; }
@@ -58,7 +58,9 @@ hipError_t launch_scale_state_by_a0(float*, const float*, int64_t, int64_t, int6
 hipError_t launch_bwd_da_valu(const FwdShape&, const float*, const float*, const float*, const float*,
                               const float*, const float*, const float*, float*, hipStream_t) { SSD_STUB; }
 hipError_t launch_bwd_da(const FwdShape&, const void*, const void*, const float*, const void*,
-                         const void*, const float*, const float*, bool, float*, hipStream_t) { SSD_STUB; }
+                         const void*, const float*, const float*, const float*, bool, float*,
+                         hipStream_t) { SSD_STUB; }
+hipError_t launch_cb_tiles(const CbJob&, hipStream_t) { SSD_STUB; }
 hipError_t launch_fill_zero(float*, int64_t, hipStream_t) { SSD_STUB; }
 hipError_t launch_copy_f32(float*, const float*, int64_t, hipStream_t) { SSD_STUB; }
 #undef SSD_STUB

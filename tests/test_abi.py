@@ -207,7 +207,11 @@ def test_bwd_validation(lib):
 
 
 def test_bwd_da_stage_validation(lib):
-    call = lambda d, *p: lib.ssd_bwd_da(ctypes.byref(d), *p, None)
+    n = ctypes.c_size_t()
+    assert lib.ssd_bwd_da_workspace_bytes(ctypes.byref(desc()), ctypes.byref(n)) == 0
+    assert n.value == 2 * 2 * 1 * 36 * 32 * 32 * 4    # batch x chunks x groups x 8*9/2 tiles of 32x32 fp32
+    WS = ctypes.c_void_p(1 << 38)
+    call = lambda d, *p, ws=WS, wsz=n.value: lib.ssd_bwd_da(ctypes.byref(d), *p, ws, wsz, None)
     F = [ctypes.c_void_p(1 << k) for k in (20, 24, 26, 28, 30, 32, 34)]
     out = ctypes.c_void_p(1 << 36)
     assert call(desc(dtype=_lib.SSD_F32), *F, out) == _lib.SSD_ERR_UNSUPPORTED
@@ -216,4 +220,12 @@ def test_bwd_da_stage_validation(lib):
     assert call(desc(), *F, None) == _lib.SSD_ERR_NULL
     assert call(desc(), *F[:5], ctypes.c_void_p((1 << 32) + 8), F[6], out) == _lib.SSD_ERR_ALIGN
     assert call(desc(), *F, F[6]) == _lib.SSD_ERR_ALIAS
-    assert call(desc(batch=0), None, None, None, None, None, None, None, None) == 0
+    # the workspace: missing, too small, misaligned, overlapping an input or da
+    assert call(desc(), *F, out, ws=None) == _lib.SSD_ERR_WORKSPACE
+    assert call(desc(), *F, out, wsz=n.value - 1) == _lib.SSD_ERR_WORKSPACE
+    assert call(desc(), *F, out, ws=ctypes.c_void_p((1 << 38) + 8)) == _lib.SSD_ERR_ALIGN
+    assert call(desc(), *F, out, ws=F[3]) == _lib.SSD_ERR_ALIAS
+    assert call(desc(), *F, out, ws=out) == _lib.SSD_ERR_ALIAS
+    assert call(desc(batch=0), None, None, None, None, None, None, None, None, ws=None, wsz=0) == 0
+    assert lib.ssd_bwd_da_workspace_bytes(ctypes.byref(desc(dtype=_lib.SSD_F32)),
+                                          ctypes.byref(n)) == _lib.SSD_ERR_UNSUPPORTED
