@@ -807,15 +807,11 @@ ssd_status ssd_chunk_scan_bwd(const ssd_fwd_desc* desc, const void* X, const flo
     // sequence of whole chunks needs no padding, and the kernels read (and
     // write) the reversed problem in place, both state passes in one launch;
     // otherwise it is copied out reversed.
-    // (the da kernel's C B^T tiles, shared by each group's heads, are formed
-    // in the same launch as the state passes or in one of their own)
-    const ssd::CbJob cbj{B, C, F(W_CBT), L, nc, (int)Bz, (int)G, (int)s.Q, (int)N};
     if (rin) {
         const ssd::StatePass pf{X, a, B, F(W_SFW), F(W_LAMFW), 0};
         const ssd::StatePass pr{dYr, ar, Cr, F(W_SREV), F(W_LAMREV), 1};
-        SSD_TRY(ssd::launch_mfma_state_pair(s, 1, nc - 1, nc, pf, pr, cbj, hs), "bwd: chunk states");
+        SSD_TRY(ssd::launch_mfma_state_pair(s, 1, nc - 1, nc, pf, pr, hs), "bwd: chunk states");
     } else {
-        SSD_TRY(ssd::launch_cb_tiles(cbj, hs), "bwd: C B^T tiles");
         SSD_TRY(ssd::launch_mfma_state(s, 1, nc - 1, nc, X, a, B, F(W_SFW), F(W_LAMFW), hs), "bwd: chunk states");
         SSD_TRY(ssd::launch_remap_rows(V(W_DYR), dY, Bz, Lp, L, Lp - 1, -1, H * P * es, hs), "bwd: reverse dY");
         SSD_TRY(ssd::launch_remap_rows(V(W_CR), C, Bz, Lp, L, Lp - 1, -1, G * N * es, hs), "bwd: reverse C");
@@ -832,7 +828,9 @@ ssd_status ssd_chunk_scan_bwd(const ssd_fwd_desc* desc, const void* X, const flo
                               F(W_SFW) + (nc - 1) * H * PN, nc * H * PN};
         const ssd::ScanJob jr{F(W_SREV), F(W_LAMREV), H * nc, nc, dfinal_state, F(W_SREV), 0,
                               F(W_SREV) + (nc - 1) * H * PN, nc * H * PN};
-        SSD_TRY(ssd::launch_state_scan_pair(s, nc - 1, nc, jf, jr, hs), "bwd: state scans");
+        // with them, the da kernel's C B^T tiles (shared by each group's heads)
+        const ssd::CbJob cbj{B, C, F(W_CBT), L, nc, (int)Bz, (int)G, (int)s.Q, (int)N};
+        SSD_TRY(ssd::launch_state_scan_pair(s, nc - 1, nc, jf, jr, &cbj, hs), "bwd: state scans");
     }
     {
         // the fused forward pass on the reversed problem, one chunk per segment

@@ -84,6 +84,7 @@
 // per-step output factor are fp32.
 #include <type_traits>
 
+#include "cb_tiles.hpp"
 #include "mfma_util.hpp"
 #include "ssd_launch.hpp"
 
@@ -669,58 +670,6 @@ __global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(3
                                           Bz, x_groups, wg, nwg, p.rev);
 }
 
-// C B^T tiles of every chunk, once per group (the head-independent factor of
-// the backward's da kernel, whose masked term is built from the products
-// (dY_i . X_j)(C_i . B_j)): tile (I, J), J <= I, of chunk c is C_I B_J^T
-// over the chunk's 32-row tiles (rows past a ragged end zero), formed on MFMA
-// from the bf16 inputs and stored in the accumulator layout, 16 floats per
-// lane: cbt[b][c][g][I(I+1)/2 + J][lane][16].  One wavefront per tile.
-template <int N>
-__device__ __forceinline__ void cb_tile(const CbJob& j, int b, int64_t c, int g, int t, int lane)
-{
-    const u16* Bm = static_cast<const u16*>(j.B);
-    const u16* Cm = static_cast<const u16*>(j.C);
-    const int nI = j.Q / 32, nt = nI * (nI + 1) / 2;
-    const int l32 = lane & 31, g2 = lane >> 5;
-    const int64_t t0 = c * j.Q;
-    const int Lc = (int)((j.L - t0 < j.Q) ? (j.L - t0) : j.Q);
-    int I = 0;
-    while ((I + 1) * (I + 2) / 2 <= t) ++I;
-    const int J = t - I * (I + 1) / 2;
-    const int irow = 32 * I + l32, jrow = 32 * J + l32;
-    bf16x8 cf[N / 16], bb[N / 16];
-#pragma unroll
-    for (int ks = 0; ks < N / 16; ++ks) {
-        u32x4 v = {0u, 0u, 0u, 0u}, w = {0u, 0u, 0u, 0u};
-        if (irow < Lc) v = *reinterpret_cast<const u32x4*>(Cm + (((int64_t)b * j.L + t0 + irow) * j.G + g) * N + 16 * ks + 8 * g2);
-        if (jrow < Lc) w = *reinterpret_cast<const u32x4*>(Bm + (((int64_t)b * j.L + t0 + jrow) * j.G + g) * N + 16 * ks + 8 * g2);
-        cf[ks] = as_bf16x8(v);
-        bb[ks] = as_bf16x8(w);
-    }
-    f32x16 CB = zero16();
-#pragma unroll
-    for (int ks = 0; ks < N / 16; ++ks) CB = mfma32(cf[ks], bb[ks], CB);
-    float4* o = reinterpret_cast<float4*>(j.cbt + ((((int64_t)b * j.nc + c) * j.G + g) * nt + t) * 1024 + lane * 16);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) o[k] = make_float4(CB[4 * k], CB[4 * k + 1], CB[4 * k + 2], CB[4 * k + 3]);
-}
-
-// workgroup wi of the cb tiles with W wavefronts per workgroup: ceil(tiles / W)
-// workgroups per (batch, chunk, group) item, wave w taking one tile
-template <int N, int W>
-__device__ __forceinline__ void cb_tiles_wg(const CbJob& j, int64_t wi, int wave, int lane)
-{
-    const int nI = j.Q / 32, nt = nI * (nI + 1) / 2;
-    const int tbs = (nt + W - 1) / W;
-    const int64_t item = wi / tbs;
-    const int t = (int)(wi - item * tbs) * W + wave;
-    if (t >= nt || item >= (int64_t)j.Bz * j.nc * j.G) return;
-    const int g = (int)(item % j.G);
-    const int64_t c = (item / j.G) % j.nc;
-    const int b = (int)(item / j.G / j.nc);
-    cb_tile<N>(j, b, c, g, t, lane);
-}
-
 constexpr int kCbWaves = 4;
 
 template <int N>
@@ -729,26 +678,14 @@ __global__ __launch_bounds__(64 * kCbWaves) void k_cb_tiles(CbJob j)
     cb_tiles_wg<N, kCbWaves>(j, blockIdx.x, threadIdx.x >> 6, threadIdx.x & 63);
 }
 
-static int64_t cb_workgroups(const CbJob& j, int waves) {
-    const int64_t nI = j.Q / 32, nt = nI * (nI + 1) / 2;
-    return (int64_t)j.Bz * j.nc * j.G * ((nt + waves - 1) / waves);
-}
-
 // Two state-only passes in one launch (the backward's forward-time and
-// reversed-time chunk states): workgroups [0, grid0) run the first, [grid0,
-// 2 grid0) the second (both share every size; grid0 is a multiple of the XCD
-// count), and the workgroups after them the C B^T tiles, eight per workgroup:
-// dispatched last, they fill the CUs the second round of state passes leaves
-// idle.
+// reversed-time chunk states): workgroups [0, grid0) run the first, the rest
+// the second.  Both share every size; grid0 is a multiple of the XCD count.
 template <int P, int N>
 __global__ __launch_bounds__(64 * (kStateWaves + 2)) __attribute__((amdgpu_waves_per_eu(2))) void k_mfma_state_pair(
-    StatePass p0, StatePass p1, unsigned grid0, CbJob cb, int64_t nseg_total, int64_t L, int H, int G,
+    StatePass p0, StatePass p1, unsigned grid0, int64_t nseg_total, int64_t L, int H, int G,
     int64_t blocks_per_seg, int nseg_grid, int Bz)
 {
-    if (blockIdx.x >= 2 * grid0) {
-        cb_tiles_wg<N, kStateWaves + 2>(cb, blockIdx.x - 2 * grid0, threadIdx.x >> 6, threadIdx.x & 63);
-        return;
-    }
     const bool second = blockIdx.x >= grid0;
     const StatePass& p = second ? p1 : p0;
     const unsigned wg = second ? blockIdx.x - grid0 : blockIdx.x;
@@ -804,19 +741,15 @@ hipError_t launch_cb_tiles(const CbJob& j, hipStream_t st)
 }
 
 hipError_t launch_mfma_state_pair(const FwdShape& s, int64_t seg_chunks, int64_t nseg_run, int64_t nseg_total,
-                                  const StatePass& p0, const StatePass& p1, const CbJob& cb, hipStream_t st)
+                                  const StatePass& p0, const StatePass& p1, hipStream_t st)
 {
+    if (nseg_run <= 0) return hipSuccess;
     if ((p0.rev || p1.rev) && s.L % kT != 0) return hipErrorInvalidValue;
-    if (cb.N != s.N || cb.Q != s.Q || cb.L != s.L || cb.nc != s.nc || cb.Bz != s.Bz || cb.G != s.G)
-        return hipErrorInvalidValue;
-    const unsigned grid0 = nseg_run > 0 ? grid_for(s, nseg_run) : 0;
-    const unsigned ncb = (unsigned)cb_workgroups(cb, kWaves);
-    if (grid0 + ncb == 0) return hipSuccess;
+    const unsigned grid0 = grid_for(s, nseg_run);
     const int64_t bps = seg_chunks * (s.Q / kT);
 #define SSD_LAUNCH_STATE_PAIR(PP, NN)                                                         \
-    hipLaunchKernelGGL((k_mfma_state_pair<PP, NN>), dim3(2 * grid0 + ncb), dim3(kThreads), 0, st, p0, p1, \
-                       grid0, cb, nseg_total, s.L, (int)s.H, (int)s.G, bps, (int)(nseg_run > 0 ? nseg_run : 1), \
-                       (int)s.Bz);
+    hipLaunchKernelGGL((k_mfma_state_pair<PP, NN>), dim3(2 * grid0), dim3(kThreads), 0, st, p0, p1, \
+                       grid0, nseg_total, s.L, (int)s.H, (int)s.G, bps, (int)nseg_run, (int)s.Bz);
     SSD_MFMA_DISPATCH(SSD_LAUNCH_STATE_PAIR)
 #undef SSD_LAUNCH_STATE_PAIR
     return hipGetLastError();

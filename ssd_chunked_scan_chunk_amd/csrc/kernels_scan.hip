@@ -11,6 +11,7 @@
 // concepts": semiseparable matrices and the block-decomposition SSD
 // algorithm): within a chunk of Q steps the output is the masked quadratic
 // form, across chunks it flows through the carried P x N state.
+#include "cb_tiles.hpp"
 #include "ssd_device.hpp"
 #include "ssd_launch.hpp"
 
@@ -419,13 +420,27 @@ hipError_t launch_chunk_cumsum(const FwdShape& s, const float* a, float* cs, flo
 // ---------------------------------------------------------------------------
 constexpr int kScanWin = 8;
 
+// NCB (the dstate of the C B^T tiles, 0 for none): the first zcb planes of
+// workgroups (blockIdx.z < zcb) form the da kernel's C B^T tiles instead
+// (four per workgroup); dispatched first, their MFMA and latency-bound work
+// overlaps the scan's streaming
+template <int NCB>
 __global__ __launch_bounds__(256) void k_state_scan(ScanJob j0, ScanJob j1, int Bz, int64_t nu,
-                                                    int64_t ustride, int H, int PN)
+                                                    int64_t ustride, int H, int PN, CbJob cb, int zcb)
 {
-    // blockIdx.z < Bz: job j0 for batch blockIdx.z; otherwise job j1 (a paired launch)
-    const bool second = (int)blockIdx.z >= Bz;
+    int z = (int)blockIdx.z;
+    if constexpr (NCB > 0) {
+        if (z < zcb) {
+            const int64_t wi = ((int64_t)z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
+            if (wi < cb_workgroups(cb, 4)) cb_tiles_wg<NCB, 4>(cb, wi, threadIdx.x >> 6, threadIdx.x & 63);
+            return;
+        }
+        z -= zcb;
+    }
+    // z < Bz: job j0 for batch z; otherwise job j1 (a paired launch)
+    const bool second = z >= Bz;
     const ScanJob j = second ? j1 : j0;
-    const int h = blockIdx.y, b = second ? (int)blockIdx.z - Bz : (int)blockIdx.z;
+    const int h = blockIdx.y, b = second ? z - Bz : z;
     const int q = blockIdx.x * blockDim.x + threadIdx.x;  // float4 index
     if (q * 4 >= PN) return;
     const int64_t bh = (int64_t)b * H + h;
@@ -460,11 +475,25 @@ __global__ __launch_bounds__(256) void k_state_scan(ScanJob j0, ScanJob j1, int 
 }
 
 static hipError_t launch_scan_jobs(const FwdShape& s, int64_t nu, int64_t ustride, const ScanJob& j0,
-                                   const ScanJob& j1, int njobs, hipStream_t st)
+                                   const ScanJob& j1, int njobs, const CbJob* cb, hipStream_t st)
 {
     const int PN = (int)(s.P * s.N);
-    dim3 grid((unsigned)((PN / 4 + 255) / 256), (unsigned)s.H, (unsigned)(njobs * s.Bz));
-    hipLaunchKernelGGL(k_state_scan, grid, dim3(256), 0, st, j0, j1, (int)s.Bz, nu, ustride, (int)s.H, PN);
+    const unsigned gx = (unsigned)((PN / 4 + 255) / 256), gy = (unsigned)s.H;
+    const int64_t ncb = cb ? cb_workgroups(*cb, 4) : 0;
+    const int zcb = (int)((ncb + (int64_t)gx * gy - 1) / ((int64_t)gx * gy));
+    const CbJob none{nullptr, nullptr, nullptr, 0, 0, 0, 0, 0, 0};
+    const dim3 grid(gx, gy, (unsigned)(njobs * s.Bz + zcb));
+    if (!cb)
+        hipLaunchKernelGGL(k_state_scan<0>, grid, dim3(256), 0, st, j0, j1, (int)s.Bz, nu, ustride, (int)s.H, PN,
+                           none, 0);
+    else if (cb->N == 128)
+        hipLaunchKernelGGL(k_state_scan<128>, grid, dim3(256), 0, st, j0, j1, (int)s.Bz, nu, ustride, (int)s.H,
+                           PN, *cb, zcb);
+    else if (cb->N == 64)
+        hipLaunchKernelGGL(k_state_scan<64>, grid, dim3(256), 0, st, j0, j1, (int)s.Bz, nu, ustride, (int)s.H,
+                           PN, *cb, zcb);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
@@ -475,17 +504,22 @@ hipError_t launch_state_scan(const FwdShape& s, int64_t nu, int64_t ustride, con
                              hipStream_t st)
 {
     const ScanJob j{D, lam, lam_bstride, lam_hstride, S0, Sout, u_write, final_, final_bstride};
-    return launch_scan_jobs(s, nu, ustride, j, j, 1, st);
+    return launch_scan_jobs(s, nu, ustride, j, j, 1, nullptr, st);
 }
 
 hipError_t launch_state_scan_pair(const FwdShape& s, int64_t nu, int64_t ustride, const ScanJob& j0,
-                                  const ScanJob& j1, hipStream_t st)
+                                  const ScanJob& j1, const CbJob* cb, hipStream_t st)
 {
-    if (2 * s.Bz > 65535) {   // keep grid.z within the 16-bit range: two launches
-        const hipError_t e = launch_scan_jobs(s, nu, ustride, j0, j0, 1, st);
-        return e != hipSuccess ? e : launch_scan_jobs(s, nu, ustride, j1, j1, 1, st);
+    // grid.z within the 16-bit range: otherwise two launches and the tiles on their own
+    const int64_t gxy = (int64_t)((s.P * s.N / 4 + 255) / 256) * s.H;
+    const int64_t zcb = cb ? (cb_workgroups(*cb, 4) + gxy - 1) / gxy : 0;
+    if (2 * s.Bz + zcb > 65535) {
+        hipError_t e = launch_scan_jobs(s, nu, ustride, j0, j0, 1, nullptr, st);
+        if (e == hipSuccess) e = launch_scan_jobs(s, nu, ustride, j1, j1, 1, nullptr, st);
+        if (e == hipSuccess && cb) e = launch_cb_tiles(*cb, st);
+        return e;
     }
-    return launch_scan_jobs(s, nu, ustride, j0, j1, 2, st);
+    return launch_scan_jobs(s, nu, ustride, j0, j1, 2, cb, st);
 }
 
 __global__ void k_fill_zero(float* p, int64_t n) {

@@ -61,8 +61,11 @@ struct ScanJob {
     float* fin;
     int64_t fin_bs;
 };
+struct CbJob;
+// cb (optional): the da kernel's C B^T tiles, formed by extra workgroups of the
+// same launch
 hipError_t launch_state_scan_pair(const FwdShape& s, int64_t nu, int64_t ustride, const ScanJob& j0,
-                                  const ScanJob& j1, hipStream_t st);
+                                  const ScanJob& j1, const CbJob* cb, hipStream_t st);
 
 // ---- MFMA segmented path (bf16) ----------------------------------------------------
 bool mfma_supported(int64_t Q, int64_t P, int64_t N);
@@ -99,10 +102,8 @@ struct CbJob {
     int Bz, G, Q, N;
 };
 hipError_t launch_cb_tiles(const CbJob& j, hipStream_t st);
-// ... and the two passes together with the C B^T tiles (of the same shape)
-// in the same launch.
 hipError_t launch_mfma_state_pair(const FwdShape& s, int64_t seg_chunks, int64_t nseg_run, int64_t nseg_total,
-                                  const StatePass& p0, const StatePass& p1, const CbJob& cb, hipStream_t st);
+                                  const StatePass& p0, const StatePass& p1, hipStream_t st);
 // The fused forward pass (kernels_fwd.hip): sw (4, 5 or 6) units -- 32-wide
 // head-dim slices of heads -- per workgroup, for every segment starting from
 // its entering state; writes Y and (last segment) the final state.  rev

@@ -29,11 +29,11 @@ hipError_t launch_chunk_cumsum(const FwdShape&, const float*, float*, float*, hi
 hipError_t launch_state_scan(const FwdShape&, int64_t, int64_t, const float*, const float*, int64_t,
                              int64_t, const float*, float*, int64_t, float*, int64_t, hipStream_t) { SSD_STUB; }
 hipError_t launch_state_scan_pair(const FwdShape&, int64_t, int64_t, const ScanJob&, const ScanJob&,
-                                  hipStream_t) { SSD_STUB; }
+                                  const CbJob*, hipStream_t) { SSD_STUB; }
 hipError_t launch_mfma_state(const FwdShape&, int64_t, int64_t, int64_t, const void*, const float*,
                              const void*, float*, float*, hipStream_t, bool) { SSD_STUB; }
 hipError_t launch_mfma_state_pair(const FwdShape&, int64_t, int64_t, int64_t, const StatePass&,
-                                  const StatePass&, const CbJob&, hipStream_t) { SSD_STUB; }
+                                  const StatePass&, hipStream_t) { SSD_STUB; }
 hipError_t launch_fwd(const FwdShape&, int, int64_t, int64_t, const void*, const float*, const void*,
                       const void*, StateSrc, void*, float*, hipStream_t, bool, const float*,
                       int64_t) { SSD_STUB; }
