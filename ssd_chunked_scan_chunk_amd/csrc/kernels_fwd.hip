@@ -606,10 +606,19 @@ __global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(2
                 u16* yblk = Y + ((int64_t)b * L + row_base(c)) * H * P;
                 const int yoff = (int)((row_loc((unsigned)(lane >> 2)) * H + h) * P + pc + 8 * (lane & 3));
                 const int ystep = rev ? -16 * H * P : 16 * H * P;   // step 16k + lane/4 of the block
+                if (last == kT - 1) {
+                    // a whole block: no per-lane conditions, so that the four
+                    // reads above stay ahead of the stores (under per-store
+                    // conditions the compiler moved them into the branches,
+                    // one read, wait and store after another)
 #pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    if (16 * k + (lane >> 2) <= last)
-                        *reinterpret_cast<u32x4*>(yblk + (yoff + k * ystep)) = Yr[k];
+                    for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x4*>(yblk + (yoff + k * ystep)) = Yr[k];
+                } else {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        if (16 * k + (lane >> 2) <= last)
+                            *reinterpret_cast<u32x4*>(yblk + (yoff + k * ystep)) = Yr[k];
+                }
             }
         };
         // ================= one instruction stream for both forms =================
