@@ -136,8 +136,10 @@ __global__ __launch_bounds__(256) void k_group_sum(GsJob j0, GsJob j1, int Bz, i
                 acc[2] += __uint_as_float(v.y << 16);
                 acc[3] += __uint_as_float(v.y & 0xffff0000u);
             } else {
-                const float4 v = *reinterpret_cast<const float4*>(p);
-                acc[0] += v.x; acc[1] += v.y; acc[2] += v.z; acc[3] += v.w;
+                // (read once: non-temporal, so the stream does not displace the cache)
+                typedef float f32x4_nt __attribute__((ext_vector_type(4)));
+                const f32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_nt*>(p));
+                acc[0] += v[0]; acc[1] += v[1]; acc[2] += v[2]; acc[3] += v[3];
             }
         }
     }

@@ -610,9 +610,15 @@ __global__ __launch_bounds__(64 * (SW + 2)) __attribute__((amdgpu_waves_per_eu(2
                     // a whole block: no per-lane conditions, so that the four
                     // reads above stay ahead of the stores (under per-store
                     // conditions the compiler moved them into the branches,
-                    // one read, wait and store after another)
+                    // one read, wait and store after another).  The backward's
+                    // dX (REV) is not read again: non-temporal stores
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x4*>(yblk + (yoff + k * ystep)) = Yr[k];
+                    for (int k = 0; k < 4; ++k) {
+                        if constexpr (REV)
+                            __builtin_nontemporal_store(Yr[k], reinterpret_cast<u32x4*>(yblk + (yoff + k * ystep)));
+                        else
+                            *reinterpret_cast<u32x4*>(yblk + (yoff + k * ystep)) = Yr[k];
+                    }
                 } else {
 #pragma unroll
                     for (int k = 0; k < 4; ++k)

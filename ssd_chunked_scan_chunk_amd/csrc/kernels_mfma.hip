@@ -575,16 +575,19 @@ __device__ __forceinline__ void mfma_seg_body(
             }
             // fp32 out, straight from the accumulators (lane = step, four
             // consecutive head-dim entries per register quad): the backward
-            // sums these over a group's heads before rounding
+            // sums these over a group's heads before rounding, reading them
+            // once (non-temporal stores: they do not stay in the caches)
             if (hvalid) {
+                typedef float f32x4_nt __attribute__((ext_vector_type(4)));
                 float* yrow = reinterpret_cast<float*>(Y) + (((int64_t)b * L + row_base(c)) * H + h) * P + pc + 4 * g2;
 #pragma unroll
                 for (int I = 0; I < 2; ++I)
                     if (32 * I + l32 <= last)
 #pragma unroll
                         for (int q = 0; q < 4; ++q)
-                            *reinterpret_cast<float4*>(yrow + (int64_t)row_loc((unsigned)(32 * I + l32)) * H * P + 8 * q) =
-                                make_float4(Yt[I][4 * q], Yt[I][4 * q + 1], Yt[I][4 * q + 2], Yt[I][4 * q + 3]);
+                            __builtin_nontemporal_store(
+                                f32x4_nt{Yt[I][4 * q], Yt[I][4 * q + 1], Yt[I][4 * q + 2], Yt[I][4 * q + 3]},
+                                reinterpret_cast<f32x4_nt*>(yrow + (int64_t)row_loc((unsigned)(32 * I + l32)) * H * P + 8 * q));
             }
         }
 
