@@ -174,10 +174,12 @@ ssd_status ssd_stream_rmw(float* data, int64_t n, float scale, int32_t per_threa
  * sums, dB and dC after summing the heads' fp32 contributions), da (fp32)
  * and, if dinitial_state != NULL, that gradient (fp32).  No output may
  * overlap an input, another output or the workspace.  The workspace holds
- * the per-chunk forward states and the adjoint's per-chunk states plus
+ * the per-chunk forward states and the adjoint's per-chunk states, the
+ * per-head dB and dC contributions in fp32, the chunks' C_i.B_j tiles of the
+ * da stage and, when the sequence is not a whole number of chunks,
  * time-reversed copies of the operands (about
  * 2 * batch * nchunks * nheads * headdim * dstate * 4 bytes plus a few
- * sequence-sized arrays in the inputs' dtype); its size comes from ssd_bwd_workspace_bytes
+ * sequence-sized arrays); its size comes from ssd_bwd_workspace_bytes
  * and its contents on entry are ignored.  Errors as for ssd_chunk_scan_fwd. */
 ssd_status ssd_bwd_workspace_bytes(const ssd_fwd_desc* desc, size_t* bytes);
 ssd_status ssd_chunk_scan_bwd(const ssd_fwd_desc* desc, const void* X, const float* a,
