@@ -10,6 +10,8 @@
 // (N/4)), so every wave-wide access is one contiguous 1 KiB run; all of a
 // thread's state loads are issued before any arithmetic, and the row sums over
 // n finish with lane shuffles inside groups of N/4 lanes.
+#include <type_traits>
+
 #include "ssd_device.hpp"
 #include "ssd_launch.hpp"
 
@@ -74,24 +76,53 @@ __global__ __launch_bounds__(256) void k_step(float* __restrict__ state, const T
     const Acc e = AccOf<T>::exp(a[bh]);
     const T* xb = x + (int64_t)bh * P;
     T* yb = y + (int64_t)bh * P;
+    // every row's x before any store (a store in flight would otherwise be
+    // waited for, as loads and stores share one counter)
+    Acc xp[ROWS];
+#pragma unroll
+    for (int k = 0; k < ROWS; ++k) xp[k] = Elem<T>::load(xb + r0 + k * RPP);
 
+    Acc acc[ROWS];
 #pragma unroll
     for (int k = 0; k < ROWS; ++k) {
         const int p = r0 + k * RPP;
-        const Acc xp = Elem<T>::load(xb + p);
         f32x4 v;
-        Acc acc = 0;
+        acc[k] = 0;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const Acc nv = e * (Acc)s[k][c] + xp * Bn[c];
+            const Acc nv = e * (Acc)s[k][c] + xp[k] * Bn[c];
             v[c] = (float)nv;
-            acc += nv * Cn[c];
+            acc[k] += nv * Cn[c];
         }
         __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(Sb + p * N) + nq);
-#pragma unroll
-        for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
-        if (nq == 0) Elem<T>::store(yb + p, (float)acc);
     }
+    // y_p: the sum over the row's LPR lanes (consecutive lanes), every row's
+    // reduction interleaved.  fp32: within 16 lanes by DPP moves (quad
+    // exchanges, then the half-row and row mirrors, each pairing a lane with
+    // one of the other half), across 16-lane rows by lane shuffles.
+#pragma unroll
+    for (int off = LPR / 2; off >= 1; off >>= 1) {
+#pragma unroll
+        for (int k = 0; k < ROWS; ++k) {
+            if constexpr (std::is_same<Acc, float>::value) {
+                if (off >= 16) {
+                    acc[k] += __shfl_xor(acc[k], off, 64);
+                } else {
+                    int t;   // row_mirror, row_half_mirror, quad_perm [2,3,0,1], quad_perm [1,0,3,2]
+                    if (off == 8) t = __builtin_amdgcn_update_dpp(0, __float_as_int(acc[k]), 0x140, 0xf, 0xf, false);
+                    else if (off == 4) t = __builtin_amdgcn_update_dpp(0, __float_as_int(acc[k]), 0x141, 0xf, 0xf, false);
+                    else if (off == 2) t = __builtin_amdgcn_update_dpp(0, __float_as_int(acc[k]), 0x4E, 0xf, 0xf, false);
+                    else t = __builtin_amdgcn_update_dpp(0, __float_as_int(acc[k]), 0xB1, 0xf, 0xf, false);
+                    acc[k] += __int_as_float(t);
+                }
+            } else {
+                acc[k] += __shfl_xor(acc[k], off, 64);
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < ROWS; ++k)
+        if (nq == 0) Elem<T>::store(yb + r0 + k * RPP, (float)acc[k]);
 }
 
 // General path: one thread per state row, any P and N.
