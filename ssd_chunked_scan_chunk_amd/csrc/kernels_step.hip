@@ -41,6 +41,34 @@ template <> struct AccOf<u16> {
     __device__ __forceinline__ static float exp(float a) { return expf(a); }
 };
 
+// The sum of v over each group of LPR consecutive lanes (LPR a power of two,
+// at most 64), in every lane of the group.  fp32: within 16 lanes by DPP
+// moves (quad exchanges, then the half-row and row mirrors, each pairing a
+// lane with one of the other half of its group), across 16-lane rows by lane
+// shuffles; fp64 by lane shuffles.
+template <typename Acc, int LPR>
+__device__ __forceinline__ Acc row_sum(Acc v)
+{
+#pragma unroll
+    for (int off = LPR / 2; off >= 1; off >>= 1) {
+        if constexpr (std::is_same<Acc, float>::value) {
+            if (off >= 16) {
+                v += __shfl_xor(v, off, 64);
+            } else {
+                int t;   // row_mirror, row_half_mirror, quad_perm [2,3,0,1], quad_perm [1,0,3,2]
+                if (off == 8) t = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xf, 0xf, false);
+                else if (off == 4) t = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xf, 0xf, false);
+                else if (off == 2) t = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xf, 0xf, false);
+                else t = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xf, 0xf, false);
+                v += __int_as_float(t);
+            }
+        } else {
+            v += __shfl_xor(v, off, 64);
+        }
+    }
+    return v;
+}
+
 // Fast path: N/4 lanes per state row (N in {16, 32, 64, 128, 256}); a
 // workgroup covers ROWS * 256 / (N/4) consecutive rows of one (b, h), so that
 // SPLIT = P / that workgroups share a (b, h) and each thread streams only ROWS
@@ -96,30 +124,8 @@ __global__ __launch_bounds__(256) void k_step(float* __restrict__ state, const T
         }
         __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(Sb + p * N) + nq);
     }
-    // y_p: the sum over the row's LPR lanes (consecutive lanes), every row's
-    // reduction interleaved.  fp32: within 16 lanes by DPP moves (quad
-    // exchanges, then the half-row and row mirrors, each pairing a lane with
-    // one of the other half), across 16-lane rows by lane shuffles.
 #pragma unroll
-    for (int off = LPR / 2; off >= 1; off >>= 1) {
-#pragma unroll
-        for (int k = 0; k < ROWS; ++k) {
-            if constexpr (std::is_same<Acc, float>::value) {
-                if (off >= 16) {
-                    acc[k] += __shfl_xor(acc[k], off, 64);
-                } else {
-                    int t;   // row_mirror, row_half_mirror, quad_perm [2,3,0,1], quad_perm [1,0,3,2]
-                    if (off == 8) t = __builtin_amdgcn_update_dpp(0, __float_as_int(acc[k]), 0x140, 0xf, 0xf, false);
-                    else if (off == 4) t = __builtin_amdgcn_update_dpp(0, __float_as_int(acc[k]), 0x141, 0xf, 0xf, false);
-                    else if (off == 2) t = __builtin_amdgcn_update_dpp(0, __float_as_int(acc[k]), 0x4E, 0xf, 0xf, false);
-                    else t = __builtin_amdgcn_update_dpp(0, __float_as_int(acc[k]), 0xB1, 0xf, 0xf, false);
-                    acc[k] += __int_as_float(t);
-                }
-            } else {
-                acc[k] += __shfl_xor(acc[k], off, 64);
-            }
-        }
-    }
+    for (int k = 0; k < ROWS; ++k) acc[k] = row_sum<Acc, LPR>(acc[k]);
 #pragma unroll
     for (int k = 0; k < ROWS; ++k)
         if (nq == 0) Elem<T>::store(yb + r0 + k * RPP, (float)acc[k]);
