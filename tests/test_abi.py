@@ -229,3 +229,14 @@ def test_bwd_da_stage_validation(lib):
     assert call(desc(batch=0), None, None, None, None, None, None, None, None, ws=None, wsz=0) == 0
     assert lib.ssd_bwd_da_workspace_bytes(ctypes.byref(desc(dtype=_lib.SSD_F32)),
                                           ctypes.byref(n)) == _lib.SSD_ERR_UNSUPPORTED
+    # other chunk lengths and groups: T = chunk/32 row tiles give T(T+1)/2 tiles per (batch, chunk, group);
+    # a ragged last chunk counts whole
+    for kw, tiles, chunks, groups in ((dict(chunk=64, seqlen=300), 3, 5, 1),
+                                      (dict(chunk=128, ngroups=2, seqlen=512), 10, 4, 2),
+                                      (dict(batch=3, seqlen=257), 36, 2, 1)):
+        assert lib.ssd_bwd_da_workspace_bytes(ctypes.byref(desc(**kw)), ctypes.byref(n)) == 0
+        assert n.value == kw.get("batch", 2) * chunks * groups * tiles * 32 * 32 * 4, (kw, n.value)
+    # the whole backward's workspace holds the same tiles among its regions
+    nb = ctypes.c_size_t()
+    assert lib.ssd_bwd_workspace_bytes(ctypes.byref(desc()), ctypes.byref(nb)) == 0
+    assert nb.value >= 2 * 2 * 1 * 36 * 32 * 32 * 4
